@@ -1,0 +1,204 @@
+"""CPU oracle for the half-precision GEMM path — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the CPU-baseline leg of ``bench.py`` load
+this package.  The product library never imports or links it, and it shares no
+code with the GPU path: the arithmetic lives in ``oracle.c`` (plain C, fp64),
+built by ``build()`` below with gcc into ``liboracle.so`` next to this file.
+
+What it computes (see the header of ``oracle.c`` for the passages it follows):
+
+* ``gemm``       D = alpha*op(A)*op(B) + beta*C_in (+ bias), out = RNE(D) to the
+                 16-bit type; optional per-row sum of squares of the written row,
+                 or the RMS row scale followed by SwiGLU (B then holds gate|up).
+* ``strassen``   the same product through 1 or 2 levels of the Strassen (1969) or
+                 Winograd 2x2 block recursion, in fp64 (identity check).
+* ``decode`` / ``encode``  exact 16-bit <-> fp64 conversions, RNE on encode.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against hand-worked
+products, exact integer identities, invariants and library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16 = 0, 1
+EPI_BIAS, EPI_ROWSUMSQ, EPI_RMS_SWIGLU = 1, 2, 4
+S69, WINOGRAD = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-pthread", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    i64, u16p, f64p, i64p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    lib.oracle_decode.restype = ctypes.c_double
+    lib.oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    lib.oracle_encode.restype = ctypes.c_uint16
+    lib.oracle_encode.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_decode_array.argtypes = [u16p, f64p, i64, ctypes.c_int]
+    lib.oracle_encode_array.argtypes = [f64p, u16p, i64, ctypes.c_int]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
+                                u16p, i64, u16p, i64, ctypes.c_double, u16p, i64, ctypes.c_int,
+                                ctypes.c_int, u16p, f64p, i64, ctypes.c_double, i64p, i64,
+                                f64p, u16p, f64p, ctypes.c_int]
+    lib.oracle_strassen.restype = ctypes.c_int
+    lib.oracle_strassen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, i64, u16p,
+                                    i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p]
+    lib.oracle_strassen_f64.restype = ctypes.c_int
+    lib.oracle_strassen_f64.argtypes = [i64, i64, i64, f64p, f64p, ctypes.c_int, ctypes.c_int, f64p]
+    lib.oracle_naive_f64.argtypes = [i64, i64, i64, f64p, f64p, f64p]
+    lib.oracle_s69_products.restype = ctypes.c_int
+    lib.oracle_s69_products.argtypes = [i64, f64p, f64p, f64p]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("16-bit inputs are passed as their uint16 bit patterns")
+    return a
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
+    bits = _u16(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_decode_array(_ptr(bits), _ptr(out), bits.size, dtype)
+    return out
+
+
+def encode(x: np.ndarray, dtype: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_encode_array(_ptr(x), _ptr(out), x.size, dtype)
+    return out
+
+
+def gemm(A, B, *, transA=False, transB=False, alpha=1.0, beta=0.0, C=None, dtype=BF16,
+         epi=0, bias=None, rms_ss=None, rms_n=0, rms_eps=1e-6, rows=None, threads=None):
+    """Reference GEMM on 16-bit bit patterns.
+
+    A is M x K (or K x M when transA), B is K x N (or N x K when transB), both
+    uint16 row-major.  Returns (D, Q, ss) for the selected rows: D the unrounded
+    fp64 result, Q its RNE 16-bit bits, ss the per-row sum of squares of the
+    written row (ROWSUMSQ only, else None).  For EPI_RMS_SWIGLU, rms_ss holds
+    the fp64 sums of squares of the selected rows.
+    """
+    A, B = _u16(A), _u16(B)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    Kb = B.shape[1] if transB else B.shape[0]
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    Nout = N // 2 if epi & EPI_RMS_SWIGLU else N
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = rows.size
+    if beta != 0.0:
+        C = _u16(C)
+        if C.shape[0] != M or C.shape[1] < Nout:
+            raise ValueError("C_in shape")
+    else:
+        C = None
+    if bias is not None:
+        bias = _u16(bias)
+    if epi & EPI_RMS_SWIGLU:
+        rms_ss = np.ascontiguousarray(rms_ss, dtype=np.float64)
+        if rms_ss.size != nrows:
+            raise ValueError("rms_ss must hold one value per selected row")
+    D = np.empty((nrows, Nout), dtype=np.float64)
+    Q = np.empty((nrows, Nout), dtype=np.uint16)
+    ss = np.empty(nrows, dtype=np.float64) if epi & EPI_ROWSUMSQ else None
+    rc = _load().oracle_gemm(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), A.shape[1],
+                             _ptr(B), B.shape[1], float(beta), _ptr(C),
+                             0 if C is None else C.shape[1], dtype, epi, _ptr(bias), _ptr(rms_ss),
+                             rms_n, float(rms_eps), _ptr(rows), nrows, _ptr(D), _ptr(Q), _ptr(ss),
+                             threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    return D, Q, ss
+
+
+def strassen(A, B, *, depth, variant, transA=False, transB=False, dtype=BF16):
+    """fp64 product through `depth` levels of the 2x2 recursion (no epilogue)."""
+    A, B = _u16(A), _u16(B)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    out = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_strassen(int(transA), int(transB), M, N, K, _ptr(A), A.shape[1], _ptr(B),
+                                 B.shape[1], dtype, depth, variant, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_strassen rejected its arguments")
+    return out
+
+
+def strassen_f64(A, B, *, depth, variant):
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    B = np.ascontiguousarray(B, dtype=np.float64)
+    M, K = A.shape
+    N = B.shape[1]
+    out = np.empty((M, N), dtype=np.float64)
+    if _load().oracle_strassen_f64(M, N, K, _ptr(A), _ptr(B), depth, variant, _ptr(out)) != 0:
+        raise ValueError("oracle_strassen_f64 rejected its arguments")
+    return out
+
+
+def naive_f64(A, B):
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    B = np.ascontiguousarray(B, dtype=np.float64)
+    out = np.empty((A.shape[0], B.shape[1]), dtype=np.float64)
+    _load().oracle_naive_f64(A.shape[0], B.shape[1], A.shape[1], _ptr(A), _ptr(B), _ptr(out))
+    return out
+
+
+def s69_products(A, B):
+    """The seven Strassen (1969) block products M1..M7 of one level (n x n, n even)."""
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    B = np.ascontiguousarray(B, dtype=np.float64)
+    n = A.shape[0]
+    out = np.empty((7, n // 2, n // 2), dtype=np.float64)
+    if _load().oracle_s69_products(n, _ptr(A), _ptr(B), _ptr(out)) != 0:
+        raise ValueError("n must be even")
+    return out
+
+
+def rel_fro(x, ref) -> float:
+    """Normwise relative error ||x - ref||_F / ||ref||_F, accumulated in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    return float(num / den) if den > 0 else float(num)

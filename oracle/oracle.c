@@ -1,0 +1,463 @@
+/*
+ * oracle.c — plain, slow, obviously-correct CPU reference for the half-precision
+ * GEMM path.  TEST INFRASTRUCTURE ONLY: it is loaded by the tests, by the smoke
+ * check and by the CPU-baseline leg of the benchmark, never by the product path.
+ * It shares no code, header, table or constant with the GPU library.
+ *
+ * What it computes (all in IEEE fp64, from the exact 16-bit input values):
+ *
+ *   D = alpha * op(A) * op(B) + beta * C_in  [+ bias_j]          (HGEMM, fp32+ acc)
+ *   out = Q(D)            Q = round-to-nearest-even to the output 16-bit type
+ *
+ *   Sources:
+ *   - "CUDA-L2: Surpassing cuBLAS Performance for Matrix Multiplication through
+ *     Reinforcement Learning" (chatpaper.ai), abstract: the operation is HGEMM,
+ *     half-precision general matrix multiply, in NN and TN layouts.
+ *   - CS336 Lecture 05 notes (jw9603.github.io), Page 26 "Low precision drives
+ *     faster matrix multiplies": 16-bit products accumulated in a wider type.
+ *   - tilnote.io PingPong GEMM note, opening section: a GEMM is a mainloop plus an
+ *     epilogue that scales and applies elementwise operations before the store.
+ *   - same note, section on CODA: the first GEMM's epilogue produces per-row norm
+ *     statistics, the second GEMM's epilogue applies the norm scaling, and SwiGLU
+ *     is fused into an epilogue.
+ *   - FalconGEMM (euno.news summary), Methodology items 1 and 4: Strassen-like and
+ *     Winograd-based low-complexity algorithms with a recursion depth; the
+ *     recursion reaches the same product with fewer multiplications.
+ *
+ * Accumulation: each element's k-sum runs in ascending k in fp64 (rows and
+ * columns may be blocked, k-order never changes, so the result is bitwise that of
+ * the naive triple loop).  Products of two 16-bit values are exact in fp64.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - epilogue order: D = alpha*acc + beta*C_in + bias, then Q, then statistics;
+ *   - the sum of squares is taken over the rounded (written) output row;
+ *   - RMS_SWIGLU: r_i = 1/sqrt(ss_i/n + eps); g = r_i*alpha*H[i][j],
+ *     u = r_i*alpha*H[i][j+Nout]; out = Q(silu(g)*u + beta*C_in[i][j]);
+ *     silu(x) = x/(1+exp(-x)); B then has 2*Nout columns (gate block, up block).
+ *   - Strassen recursion keeps fp64 temporaries (it is the exact identity check).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F16 0
+#define OR_BF16 1
+
+#define OR_EPI_BIAS 1
+#define OR_EPI_ROWSUMSQ 2
+#define OR_EPI_RMS_SWIGLU 4
+
+/* ---------------------------------------------------------------------------
+ * 16-bit decode: exact value of an IEEE binary16 or bfloat16 bit pattern.
+ * binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ * bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+ * ------------------------------------------------------------------------- */
+double oracle_decode(uint16_t h, int dtype) {
+    int sign = (h >> 15) & 1;
+    int ebits = dtype == OR_F16 ? 5 : 8;
+    int fbits = dtype == OR_F16 ? 10 : 7;
+    int bias = dtype == OR_F16 ? 15 : 127;
+    int emax = (1 << ebits) - 1;
+    int e = (h >> fbits) & emax;
+    int f = h & ((1 << fbits) - 1);
+    double v;
+    if (e == emax) {
+        v = f ? NAN : INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)f, 1 - bias - fbits); /* subnormal: f * 2^(1-bias-fbits) */
+    } else {
+        v = ldexp((double)((1 << fbits) | f), e - bias - fbits);
+    }
+    return sign ? -v : v;
+}
+
+/* ---------------------------------------------------------------------------
+ * 16-bit encode with round-to-nearest, ties to even, straight from fp64.
+ * The quantum (ulp) of the target format at |x| is a power of two; x/ulp is
+ * exact, rint() in the default rounding mode rounds half to even, and the
+ * product by ulp is exact again.  Overflow of the rounded value gives inf.
+ * ------------------------------------------------------------------------- */
+uint16_t oracle_encode(double x, int dtype) {
+    int fbits = dtype == OR_F16 ? 10 : 7;
+    int bias = dtype == OR_F16 ? 15 : 127;
+    int ebits = dtype == OR_F16 ? 5 : 8;
+    int emax_field = (1 << ebits) - 1;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return (uint16_t)(emax_field << fbits | (1 << (fbits - 1)));
+    double a = fabs(x);
+    int emin = 1 - bias;                 /* exponent of the smallest normal */
+    int emax = bias;                     /* exponent of the largest finite  */
+    double maxval = ldexp(2.0 - ldexp(1.0, -fbits), emax);
+    if (isinf(a)) return sign | (uint16_t)(emax_field << fbits);
+    int e2;
+    frexp(a, &e2);                       /* a = m * 2^e2, 0.5 <= m < 1 */
+    int ex = e2 - 1;                     /* a in [2^ex, 2^(ex+1)) */
+    if (a == 0.0) return sign;
+    if (ex < emin) ex = emin;            /* subnormal range shares emin's quantum */
+    double ulp = ldexp(1.0, ex - fbits);
+    double r = rint(a / ulp) * ulp;
+    if (r > maxval) return sign | (uint16_t)(emax_field << fbits);
+    if (r == 0.0) return sign;
+    /* pack the exact value r */
+    frexp(r, &e2);
+    ex = e2 - 1;
+    if (ex < emin) { /* subnormal */
+        uint16_t f = (uint16_t)(r / ldexp(1.0, emin - fbits));
+        return sign | f;
+    }
+    double mant = r / ldexp(1.0, ex) - 1.0;            /* in [0,1) */
+    uint16_t f = (uint16_t)(mant * (double)(1 << fbits));
+    uint16_t e = (uint16_t)(ex + bias);
+    return sign | (uint16_t)(e << fbits) | f;
+}
+
+void oracle_decode_array(const uint16_t* h, double* out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_decode(h[i], dtype);
+}
+
+void oracle_encode_array(const double* x, uint16_t* out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode(x[i], dtype);
+}
+
+/* ---------------------------------------------------------------------------
+ * Classical GEMM rows.
+ * op(A)[i][k] = transA ? A[k*lda + i] : A[i*lda + k]   (row-major storage)
+ * op(B)[k][j] = transB ? B[j*ldb + k] : B[k*ldb + j]
+ * The selected rows `rows[0..nrows)` of D (nrows x Ncols, Ncols = N) are computed.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int transA, transB;
+    int64_t M, N, K;
+    const uint16_t* A; int64_t lda;
+    const uint16_t* B; int64_t ldb;
+    int dtype;
+    const double* Bd;     /* decoded op(B), K x N row-major */
+    const int64_t* rows; int64_t nrows;
+    double* H;            /* nrows x N: the raw k-sums */
+    int64_t r0, r1;       /* this worker's slice of `rows` */
+} gemm_job_t;
+
+#define OR_JB 512
+
+static void* gemm_worker(void* p) {
+    gemm_job_t* J = (gemm_job_t*)p;
+    int64_t K = J->K, N = J->N;
+    double* arow = (double*)malloc(sizeof(double) * (K > 0 ? K : 1));
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        int64_t i = J->rows[r];
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t h = J->transA ? J->A[k * J->lda + i] : J->A[i * J->lda + k];
+            arow[k] = oracle_decode(h, J->dtype);
+        }
+        double* hrow = J->H + r * N;
+        for (int64_t j = 0; j < N; ++j) hrow[j] = 0.0;
+        /* ascending k for every element of the row: hrow[j] = sum_k a_k * b_kj */
+        for (int64_t jb = 0; jb < N; jb += OR_JB) {
+            int64_t je = jb + OR_JB < N ? jb + OR_JB : N;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = arow[k];
+                const double* brow = J->Bd + k * N;
+                for (int64_t j = jb; j < je; ++j) hrow[j] += a * brow[j];
+            }
+        }
+    }
+    free(arow);
+    return NULL;
+}
+
+static void decode_opB(int transB, int64_t K, int64_t N, const uint16_t* B, int64_t ldb,
+                       int dtype, double* Bd) {
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) {
+            uint16_t h = transB ? B[j * ldb + k] : B[k * ldb + j];
+            Bd[k * N + j] = oracle_decode(h, dtype);
+        }
+}
+
+/* H[r][j] = sum_k op(A)[rows[r]][k] * op(B)[k][j], fp64, ascending k. */
+static int raw_products(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                        int dtype, const int64_t* rows, int64_t nrows, double* H,
+                        int nthreads) {
+    (void)M;
+    double* Bd = (double*)malloc(sizeof(double) * (K * N > 0 ? K * N : 1));
+    if (!Bd) return -1;
+    decode_opB(transB, K, N, B, ldb, dtype, Bd);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    gemm_job_t jobs[256];
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    int launched = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t r0 = t * per, r1 = r0 + per < nrows ? r0 + per : nrows;
+        if (r0 >= r1) break;
+        gemm_job_t j = {transA, transB, M, N, K, A, lda, B, ldb, dtype, Bd, rows, nrows, H, r0, r1};
+        jobs[t] = j;
+        pthread_create(&th[t], NULL, gemm_worker, &jobs[t]);
+        ++launched;
+    }
+    for (int t = 0; t < launched; ++t) pthread_join(th[t], NULL);
+    free(Bd);
+    return 0;
+}
+
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
+/*
+ * oracle_gemm: classical reference with the epilogues.
+ *   N is the width of op(B) (for RMS_SWIGLU, N = 2*Nout and the output is Nout wide).
+ *   C_in, when beta != 0, is Mout x Nout with leading dimension ldc.
+ *   Outputs for the selected rows: D (nrows x Nout, unrounded fp64),
+ *   Q (nrows x Nout, 16-bit RNE bits), ss (nrows, only for ROWSUMSQ).
+ * Returns 0 on success, -1 on bad arguments.
+ */
+int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, double beta,
+                const uint16_t* Cin, int64_t ldc, int dtype, int epi, const uint16_t* bias,
+                const double* rms_ss, int64_t rms_n, double rms_eps, const int64_t* rows,
+                int64_t nrows, double* D, uint16_t* Q, double* ss, int nthreads) {
+    int swiglu = (epi & OR_EPI_RMS_SWIGLU) != 0;
+    if (swiglu && (epi & (OR_EPI_BIAS | OR_EPI_ROWSUMSQ))) return -1;
+    if (swiglu && (N % 2)) return -1;
+    int64_t Nout = swiglu ? N / 2 : N;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    double* H = (double*)malloc(sizeof(double) * (nrows * N > 0 ? nrows * N : 1));
+    if (!H) return -1;
+    if (raw_products(transA, transB, M, N, K, A, lda, B, ldb, dtype, rows, nrows, H, nthreads)) {
+        free(H);
+        return -1;
+    }
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows[r];
+        const double* h = H + r * N;
+        double sum_sq = 0.0;
+        double rscale = 1.0;
+        if (swiglu) rscale = 1.0 / sqrt(rms_ss[r] / (double)rms_n + rms_eps);
+        for (int64_t j = 0; j < Nout; ++j) {
+            double d;
+            if (swiglu) {
+                double g = rscale * (alpha * h[j]);
+                double u = rscale * (alpha * h[j + Nout]);
+                d = silu(g) * u;
+            } else {
+                d = alpha * h[j];
+            }
+            if (beta != 0.0) d += beta * oracle_decode(Cin[i * ldc + j], dtype);
+            if (epi & OR_EPI_BIAS) d += oracle_decode(bias[j], dtype);
+            uint16_t q = oracle_encode(d, dtype);
+            D[r * Nout + j] = d;
+            Q[r * Nout + j] = q;
+            if (epi & OR_EPI_ROWSUMSQ) {
+                double qv = oracle_decode(q, dtype);
+                sum_sq += qv * qv;
+            }
+        }
+        if ((epi & OR_EPI_ROWSUMSQ) && ss) ss[r] = sum_sq;
+    }
+    free(H);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Strassen / Winograd recursion in fp64 (identity check and diagnostic).
+ * Matrices here are dense row-major double blocks with their own stride.
+ * variant 0: Strassen (1969), seven products M1..M7 and 18 block additions.
+ * variant 1: Winograd's form, seven products P1..P7 and 15 block additions.
+ * depth 0 falls back to the classical loop (ascending k).
+ * ------------------------------------------------------------------------- */
+typedef struct { double* p; int64_t r, c, ld; } blk_t;
+
+static blk_t blk_alloc(int64_t r, int64_t c) {
+    blk_t b = {(double*)calloc((size_t)(r * c > 0 ? r * c : 1), sizeof(double)), r, c, c};
+    return b;
+}
+static blk_t blk_sub(blk_t m, int bi, int bj) {
+    blk_t b = {m.p + bi * (m.r / 2) * m.ld + bj * (m.c / 2), m.r / 2, m.c / 2, m.ld};
+    return b;
+}
+#define AT(b, i, j) ((b).p[(i) * (b).ld + (j)])
+
+/* out = x + sy*y  (sy = +1 or -1), elementwise */
+static void blk_axpy(blk_t out, blk_t x, blk_t y, double sy) {
+    for (int64_t i = 0; i < out.r; ++i)
+        for (int64_t j = 0; j < out.c; ++j) AT(out, i, j) = AT(x, i, j) + sy * AT(y, i, j);
+}
+static void blk_copy(blk_t out, blk_t x) {
+    for (int64_t i = 0; i < out.r; ++i)
+        for (int64_t j = 0; j < out.c; ++j) AT(out, i, j) = AT(x, i, j);
+}
+
+static void classical(blk_t C, blk_t A, blk_t B) {
+    for (int64_t i = 0; i < C.r; ++i) {
+        for (int64_t j = 0; j < C.c; ++j) AT(C, i, j) = 0.0;
+        for (int64_t k = 0; k < A.c; ++k) {
+            double a = AT(A, i, k);
+            for (int64_t j = 0; j < C.c; ++j) AT(C, i, j) += a * AT(B, k, j);
+        }
+    }
+}
+
+static void strassen_rec(blk_t C, blk_t A, blk_t B, int depth, int variant);
+
+static void s69(blk_t C, blk_t A, blk_t B, int depth) {
+    int64_t m = A.r / 2, k = A.c / 2, n = B.c / 2;
+    blk_t A11 = blk_sub(A, 0, 0), A12 = blk_sub(A, 0, 1), A21 = blk_sub(A, 1, 0), A22 = blk_sub(A, 1, 1);
+    blk_t B11 = blk_sub(B, 0, 0), B12 = blk_sub(B, 0, 1), B21 = blk_sub(B, 1, 0), B22 = blk_sub(B, 1, 1);
+    blk_t C11 = blk_sub(C, 0, 0), C12 = blk_sub(C, 0, 1), C21 = blk_sub(C, 1, 0), C22 = blk_sub(C, 1, 1);
+    blk_t L = blk_alloc(m, k), R = blk_alloc(k, n);
+    blk_t Mx[7];
+    for (int t = 0; t < 7; ++t) Mx[t] = blk_alloc(m, n);
+    /* M1 = (A11 + A22)(B11 + B22) */
+    blk_axpy(L, A11, A22, 1); blk_axpy(R, B11, B22, 1); strassen_rec(Mx[0], L, R, depth - 1, 0);
+    /* M2 = (A21 + A22) B11 */
+    blk_axpy(L, A21, A22, 1); strassen_rec(Mx[1], L, B11, depth - 1, 0);
+    /* M3 = A11 (B12 - B22) */
+    blk_axpy(R, B12, B22, -1); strassen_rec(Mx[2], A11, R, depth - 1, 0);
+    /* M4 = A22 (B21 - B11) */
+    blk_axpy(R, B21, B11, -1); strassen_rec(Mx[3], A22, R, depth - 1, 0);
+    /* M5 = (A11 + A12) B22 */
+    blk_axpy(L, A11, A12, 1); strassen_rec(Mx[4], L, B22, depth - 1, 0);
+    /* M6 = (A21 - A11)(B11 + B12) */
+    blk_axpy(L, A21, A11, -1); blk_axpy(R, B11, B12, 1); strassen_rec(Mx[5], L, R, depth - 1, 0);
+    /* M7 = (A12 - A22)(B21 + B22) */
+    blk_axpy(L, A12, A22, -1); blk_axpy(R, B21, B22, 1); strassen_rec(Mx[6], L, R, depth - 1, 0);
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double m1 = AT(Mx[0], i, j), m2 = AT(Mx[1], i, j), m3 = AT(Mx[2], i, j);
+            double m4 = AT(Mx[3], i, j), m5 = AT(Mx[4], i, j), m6 = AT(Mx[5], i, j);
+            double m7 = AT(Mx[6], i, j);
+            AT(C11, i, j) = m1 + m4 - m5 + m7;   /* C11 = M1 + M4 - M5 + M7 */
+            AT(C12, i, j) = m3 + m5;             /* C12 = M3 + M5 */
+            AT(C21, i, j) = m2 + m4;             /* C21 = M2 + M4 */
+            AT(C22, i, j) = m1 - m2 + m3 + m6;   /* C22 = M1 - M2 + M3 + M6 */
+        }
+    free(L.p); free(R.p);
+    for (int t = 0; t < 7; ++t) free(Mx[t].p);
+}
+
+static void winograd(blk_t C, blk_t A, blk_t B, int depth) {
+    int64_t m = A.r / 2, k = A.c / 2, n = B.c / 2;
+    blk_t A11 = blk_sub(A, 0, 0), A12 = blk_sub(A, 0, 1), A21 = blk_sub(A, 1, 0), A22 = blk_sub(A, 1, 1);
+    blk_t B11 = blk_sub(B, 0, 0), B12 = blk_sub(B, 0, 1), B21 = blk_sub(B, 1, 0), B22 = blk_sub(B, 1, 1);
+    blk_t C11 = blk_sub(C, 0, 0), C12 = blk_sub(C, 0, 1), C21 = blk_sub(C, 1, 0), C22 = blk_sub(C, 1, 1);
+    blk_t S1 = blk_alloc(m, k), S2 = blk_alloc(m, k), S3 = blk_alloc(m, k), S4 = blk_alloc(m, k);
+    blk_t T1 = blk_alloc(k, n), T2 = blk_alloc(k, n), T3 = blk_alloc(k, n), T4 = blk_alloc(k, n);
+    blk_axpy(S1, A21, A22, 1);   /* S1 = A21 + A22 */
+    blk_axpy(S2, S1, A11, -1);   /* S2 = S1 - A11  */
+    blk_axpy(S3, A11, A21, -1);  /* S3 = A11 - A21 */
+    blk_axpy(S4, A12, S2, -1);   /* S4 = A12 - S2  */
+    blk_axpy(T1, B12, B11, -1);  /* T1 = B12 - B11 */
+    blk_axpy(T2, B22, T1, -1);   /* T2 = B22 - T1  */
+    blk_axpy(T3, B22, B12, -1);  /* T3 = B22 - B12 */
+    blk_axpy(T4, T2, B21, -1);   /* T4 = T2 - B21  */
+    blk_t P[7];
+    for (int t = 0; t < 7; ++t) P[t] = blk_alloc(m, n);
+    strassen_rec(P[0], A11, B11, depth - 1, 1); /* P1 = A11 B11 */
+    strassen_rec(P[1], A12, B21, depth - 1, 1); /* P2 = A12 B21 */
+    strassen_rec(P[2], S4, B22, depth - 1, 1);  /* P3 = S4 B22  */
+    strassen_rec(P[3], A22, T4, depth - 1, 1);  /* P4 = A22 T4  */
+    strassen_rec(P[4], S1, T1, depth - 1, 1);   /* P5 = S1 T1   */
+    strassen_rec(P[5], S2, T2, depth - 1, 1);   /* P6 = S2 T2   */
+    strassen_rec(P[6], S3, T3, depth - 1, 1);   /* P7 = S3 T3   */
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double p1 = AT(P[0], i, j), p2 = AT(P[1], i, j), p3 = AT(P[2], i, j);
+            double p4 = AT(P[3], i, j), p5 = AT(P[4], i, j), p6 = AT(P[5], i, j);
+            double p7 = AT(P[6], i, j);
+            double u2 = p1 + p6;          /* U2 = P1 + P6 */
+            double u3 = u2 + p7;          /* U3 = U2 + P7 */
+            double u4 = u2 + p5;          /* U4 = U2 + P5 */
+            AT(C11, i, j) = p1 + p2;      /* C11 = P1 + P2 */
+            AT(C12, i, j) = u4 + p3;      /* C12 = U4 + P3 */
+            AT(C21, i, j) = u3 - p4;      /* C21 = U3 - P4 */
+            AT(C22, i, j) = u3 + p5;      /* C22 = U3 + P5 */
+        }
+    free(S1.p); free(S2.p); free(S3.p); free(S4.p);
+    free(T1.p); free(T2.p); free(T3.p); free(T4.p);
+    for (int t = 0; t < 7; ++t) free(P[t].p);
+}
+
+static void strassen_rec(blk_t C, blk_t A, blk_t B, int depth, int variant) {
+    if (depth <= 0) {
+        classical(C, A, B);
+        return;
+    }
+    if (variant == 0) s69(C, A, B, depth);
+    else winograd(C, A, B, depth);
+}
+
+/*
+ * oracle_strassen: C = op(A)*op(B) (fp64, no epilogue) through `depth` levels of
+ * the 2x2 block recursion.  M, N, K must be divisible by 2^depth.
+ * The 16-bit inputs are decoded exactly; out is M x N fp64 row-major.
+ */
+int oracle_strassen(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int dtype,
+                    int depth, int variant, double* out) {
+    if (depth < 0 || variant < 0 || variant > 1) return -1;
+    int64_t q = (int64_t)1 << depth;
+    if (M % q || N % q || K % q) return -1;
+    blk_t Ad = blk_alloc(M, K), Bd = blk_alloc(K, N);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            AT(Ad, i, k) = oracle_decode(transA ? A[k * lda + i] : A[i * lda + k], dtype);
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j)
+            AT(Bd, k, j) = oracle_decode(transB ? B[j * ldb + k] : B[k * ldb + j], dtype);
+    blk_t C = {out, M, N, N};
+    strassen_rec(C, Ad, Bd, depth, variant);
+    free(Ad.p); free(Bd.p);
+    return 0;
+}
+
+/* The same recursion on dense fp64 matrices (used for the integer identity pins). */
+int oracle_strassen_f64(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
+                        int depth, int variant, double* out) {
+    if (depth < 0 || variant < 0 || variant > 1) return -1;
+    int64_t q = (int64_t)1 << depth;
+    if (M % q || N % q || K % q) return -1;
+    blk_t Ad = blk_alloc(M, K), Bd = blk_alloc(K, N);
+    memcpy(Ad.p, A, sizeof(double) * M * K);
+    memcpy(Bd.p, B, sizeof(double) * K * N);
+    blk_t C = {out, M, N, N};
+    strassen_rec(C, Ad, Bd, depth, variant);
+    free(Ad.p); free(Bd.p);
+    return 0;
+}
+
+/* Naive triple loop on fp64 (used to pin the blocked, threaded loop above). */
+void oracle_naive_f64(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
+                      double* out) {
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += A[i * K + k] * B[k * N + j];
+            out[i * N + j] = s;
+        }
+}
+
+/* Seven S69 products of one 2x2-blocked level for inspection (M1..M7), fp64. */
+int oracle_s69_products(int64_t n, const double* A, const double* B, double* Mout) {
+    if (n % 2) return -1;
+    int64_t h = n / 2;
+    blk_t Ad = {(double*)A, n, n, n}, Bd = {(double*)B, n, n, n};
+    blk_t A11 = blk_sub(Ad, 0, 0), A12 = blk_sub(Ad, 0, 1), A21 = blk_sub(Ad, 1, 0), A22 = blk_sub(Ad, 1, 1);
+    blk_t B11 = blk_sub(Bd, 0, 0), B12 = blk_sub(Bd, 0, 1), B21 = blk_sub(Bd, 1, 0), B22 = blk_sub(Bd, 1, 1);
+    blk_t L = blk_alloc(h, h), R = blk_alloc(h, h), tmp = blk_alloc(h, h);
+    blk_t out[7];
+    for (int t = 0; t < 7; ++t) { blk_t b = {Mout + t * h * h, h, h, h}; out[t] = b; }
+    blk_axpy(L, A11, A22, 1); blk_axpy(R, B11, B22, 1); classical(out[0], L, R);
+    blk_axpy(L, A21, A22, 1); classical(out[1], L, B11);
+    blk_axpy(R, B12, B22, -1); classical(out[2], A11, R);
+    blk_axpy(R, B21, B11, -1); classical(out[3], A22, R);
+    blk_axpy(L, A11, A12, 1); classical(out[4], L, B22);
+    blk_axpy(L, A21, A11, -1); blk_axpy(R, B11, B12, 1); classical(out[5], L, R);
+    blk_axpy(L, A12, A22, -1); blk_axpy(R, B21, B22, 1); classical(out[6], L, R);
+    (void)blk_copy;
+    free(L.p); free(R.p); free(tmp.p);
+    return 0;
+}
