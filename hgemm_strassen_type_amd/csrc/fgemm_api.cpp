@@ -1,0 +1,604 @@
+// fgemm_api.cpp — the C ABI: handle, argument checks, plan selection and cache,
+// and the classical and Strassen/Winograd schedulers that enqueue the kernels.
+//
+// Run-time dispatch follows the FalconGEMM summary (euno.news), Methodology 5: the
+// model is queried with the actual shape, the chosen kernel runs with no further
+// input from the caller; a per-shape plan cache keeps the query cost far below the
+// kernels' own time (Results: model overhead under half a percent).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <unordered_map>
+
+#include "internal.h"
+#include "model.h"
+
+using namespace fgemm;
+
+namespace fgemm {
+
+int tile_m_of(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 : tile == 2 ? 64 : 32; }
+int tile_n_of(int tile) { return tile == 0 ? 256 : 128; }
+int waves_n_of(int tile) { return tile == 3 ? 4 : 2; }
+
+hipError_t launch_gemm(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
+#define FG_SEL(DT, AK, BK) \
+  if (k.dtype == DT && k.a_kcontig == AK && k.b_kcontig == BK) return launch_gemm_##DT##_##AK##BK(k, b, s);
+  FG_SEL(0, 0, 0) FG_SEL(0, 0, 1) FG_SEL(0, 1, 0) FG_SEL(0, 1, 1)
+  FG_SEL(1, 0, 0) FG_SEL(1, 0, 1) FG_SEL(1, 1, 0) FG_SEL(1, 1, 1)
+#undef FG_SEL
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fgemm
+
+namespace {
+
+struct PlanKey {
+  int64_t M, N, K;
+  int ta, tb, dtype, flags, vec;
+  bool operator==(const PlanKey& o) const {
+    return M == o.M && N == o.N && K == o.K && ta == o.ta && tb == o.tb && dtype == o.dtype &&
+           flags == o.flags && vec == o.vec;
+  }
+};
+struct PlanKeyHash {
+  size_t operator()(const PlanKey& k) const {
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&](uint64_t v) { h = (h ^ v) * 1099511628211ull; };
+    mix(k.M); mix(k.N); mix(k.K);
+    mix(((uint64_t)k.ta << 1 | k.tb) << 8 | (uint64_t)k.dtype << 4 | (uint64_t)k.vec);
+    mix(k.flags);
+    return (size_t)h;
+  }
+};
+
+}  // namespace
+
+struct fgemm_handle_s {
+  int device = 0;
+  fgemm_model_t model{};
+  std::unordered_map<PlanKey, fgemm_plan_t, PlanKeyHash> plans;
+  void* user_ws = nullptr;
+  size_t user_ws_bytes = 0;
+  void* own_ws = nullptr;
+  size_t own_ws_bytes = 0;
+};
+
+namespace {
+
+fgemm_status_t hip_status(hipError_t e) { return e == hipSuccess ? FGEMM_OK : FGEMM_ERR_HIP; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+uint32_t epi_flags(const fgemm_epilogue_t* e) { return e ? e->flags : 0u; }
+
+// Whether the 16-byte fast path applies.
+int vec_ok(fgemm_op_t ta, fgemm_op_t tb, int64_t N, const void* A, int64_t lda, const void* B,
+           int64_t ldb, const void* C, int64_t ldc, const fgemm_epilogue_t* e) {
+  (void)ta; (void)tb;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return 0;
+  if (lda % 8 || ldb % 8 || ldc % 8) return 0;
+  if ((epi_flags(e) & FGEMM_EPI_RMS_SWIGLU) && N % 8) return 0;
+  return 1;
+}
+
+fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int64_t K, int vec,
+                                uint32_t flags) {
+  if (p.path == FGEMM_PATH_CLASSICAL) return FGEMM_OK;
+  if (p.path != FGEMM_PATH_STRASSEN) return FGEMM_ERR_INVALID_VALUE;
+  if (p.depth < 1 || p.depth > 2) return FGEMM_ERR_INVALID_VALUE;
+  if (p.variant != FGEMM_VARIANT_S69 && p.variant != FGEMM_VARIANT_WINOGRAD)
+    return FGEMM_ERR_INVALID_VALUE;
+  const int64_t q = 8ll << p.depth;
+  if (M % q || N % q || K % q || M == 0 || N == 0 || K == 0) return FGEMM_ERR_NOT_SUPPORTED;
+  if (!vec) return FGEMM_ERR_NOT_SUPPORTED;
+  if (flags & ~(uint32_t)FGEMM_EPI_BIAS) return FGEMM_ERR_NOT_SUPPORTED;
+  return FGEMM_OK;
+}
+
+// Core of fgemm_select: classical tile choice, then Strassen candidates under guards.
+fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K,
+                           uint32_t flags, int beta_hint, int vec, size_t ws_limit,
+                           fgemm_plan_t* out) {
+  fgemm_plan_t p{};
+  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
+  double tc;
+  int tile = best_tile(md, M, N, K, swiglu, 1, 2.0, 2.0, beta_hint, &tc);
+  p.path = FGEMM_PATH_CLASSICAL;
+  p.depth = 0;
+  p.variant = FGEMM_VARIANT_WINOGRAD;
+  p.tile_m = tile_m_of(tile);
+  p.tile_n = tile_n_of(tile);
+  p.tile_k = 64;
+  p.split_k = 1;
+  p.workspace_bytes = 0;
+  if (flags & FGEMM_EPI_ROWSUMSQ)
+    p.workspace_bytes = (size_t)ceil_div(N, tile_n_of(tile)) * waves_n_of(tile) * (size_t)M * 4;
+  p.t_pred_us = tc;
+  p.t_classical_pred_us = tc;
+  for (int depth = 1; depth <= 2; ++depth) {
+    for (int variant = FGEMM_VARIANT_S69; variant <= FGEMM_VARIANT_WINOGRAD; ++variant) {
+      fgemm_plan_t c{};
+      c.path = FGEMM_PATH_STRASSEN;
+      c.depth = depth;
+      c.variant = variant;
+      if (check_plan_shape(c, M, N, K, vec, flags) != FGEMM_OK) continue;
+      // sub-problems below 512 never pay for their additions; keep them classical
+      if ((M >> depth) < 512 || (N >> depth) < 512 || (K >> depth) < 512) continue;
+      const size_t ws = strassen_workspace(M, N, K, depth, variant);
+      if ((double)ws > md.max_workspace_bytes || ws > ws_limit) continue;
+      int sub_tile = 0;
+      const double t = strassen_time_us(md, M, N, K, depth, variant, beta_hint, &sub_tile);
+      if (t < p.t_pred_us) {
+        c.tile_m = tile_m_of(sub_tile);
+        c.tile_n = tile_n_of(sub_tile);
+        c.tile_k = 64;
+        c.split_k = 1;
+        c.workspace_bytes = ws;
+        c.t_pred_us = t;
+        c.t_classical_pred_us = tc;
+        p = c;
+      }
+    }
+  }
+  *out = p;
+  return FGEMM_OK;
+}
+
+int tile_id(int tm, int tn) {
+  for (int i = 0; i < kNumTiles; ++i)
+    if (kTiles[i].bm == tm && kTiles[i].bn == tn) return kTiles[i].tile;
+  return -1;
+}
+
+fgemm_status_t ensure_workspace(fgemm_handle_t h, size_t bytes, void** ws) {
+  *ws = nullptr;
+  if (bytes == 0) return FGEMM_OK;
+  if (h->user_ws) {
+    if (h->user_ws_bytes < bytes) return FGEMM_ERR_WORKSPACE;
+    *ws = h->user_ws;
+    return FGEMM_OK;
+  }
+  if (h->own_ws_bytes < bytes) {
+    if (h->own_ws) {
+      // earlier launches may still read the old buffer
+      if (hipDeviceSynchronize() != hipSuccess) return FGEMM_ERR_HIP;
+      hipFree(h->own_ws);
+      h->own_ws = nullptr;
+      h->own_ws_bytes = 0;
+    }
+    if (hipMalloc(&h->own_ws, bytes) != hipSuccess) {
+      h->own_ws = nullptr;
+      return FGEMM_ERR_ALLOC;
+    }
+    h->own_ws_bytes = bytes;
+  }
+  *ws = h->own_ws;
+  return FGEMM_OK;
+}
+
+struct Call {
+  fgemm_op_t ta, tb;
+  int64_t M, N, K;
+  float alpha;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  float beta;
+  void* C; int64_t ldc;
+  fgemm_dtype_t dtype;
+  const fgemm_epilogue_t* epi;
+  hipStream_t stream;
+};
+
+fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c, int vec) {
+  const uint32_t flags = epi_flags(c.epi);
+  int tile = tile_id(plan.tile_m, plan.tile_n);
+  if (tile < 0) return FGEMM_ERR_INVALID_VALUE;
+  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
+  if (swiglu && tile == 3) return FGEMM_ERR_NOT_SUPPORTED;
+  GemmBatch b{};
+  b.count = 1;
+  GemmProblem& p = b.p[0];
+  p.A = c.A; p.B = c.B; p.C = c.C; p.Cin = c.C;
+  p.lda = c.lda; p.ldb = c.ldb; p.ldc = c.ldc;
+  p.M = (int)c.M; p.N = (int)c.N; p.K = (int)c.K;
+  p.alpha = c.alpha; p.beta = c.beta;
+  p.flags = (c.beta != 0.f ? kFlagBeta : 0u);
+  if (flags & FGEMM_EPI_BIAS) { p.flags |= kFlagBias; p.bias = c.epi->bias; }
+  int parts = 0;
+  if (flags & FGEMM_EPI_ROWSUMSQ) {
+    p.flags |= kFlagRowSumSq;
+    parts = (int)ceil_div(c.N, tile_n_of(tile)) * waves_n_of(tile);
+    void* ws;
+    fgemm_status_t st = ensure_workspace(h, (size_t)parts * (size_t)c.M * 4, &ws);
+    if (st != FGEMM_OK) return st;
+    p.ss_partial = static_cast<float*>(ws);
+  }
+  if (swiglu) {
+    p.rms_ss = c.epi->rms_rowsumsq;
+    p.rms_inv_n = 1.0f / (float)c.epi->rms_n;
+    p.rms_eps = c.epi->rms_eps;
+  }
+  KernelKey k{};
+  k.tile = tile;
+  k.a_kcontig = c.ta == FGEMM_OP_N;
+  k.b_kcontig = c.tb == FGEMM_OP_T;
+  k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
+  k.epi = swiglu ? kEpiSwiGLU : kEpiStore16;
+  k.vec = vec;
+  hipError_t e = launch_gemm(k, b, c.stream);
+  if (e != hipSuccess) return FGEMM_ERR_HIP;
+  if (parts) {
+    e = launch_rowsumsq_reduce(p.ss_partial, parts, (int)c.M, c.epi->rowsumsq, c.stream);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
+  }
+  return FGEMM_OK;
+}
+
+// ------------------------------------------------------------------ Strassen
+struct StrassenRun {
+  const Call* c;
+  int depth, variant, sub_tile;
+  int in_dtype;
+  float* scale_a; float* scale_b;
+  // per level l (1-based): S, T (fp16 sums) and P (fp32 products)
+  void* S[3][5];
+  void* T[3][5];
+  float* P[3][7];
+};
+
+// Logical sub-block (bi, bj) of a blocked operand with logical size rows x cols.
+BlockedOperand sub_block(const BlockedOperand& x, int64_t rows, int64_t cols, int bi, int bj) {
+  BlockedOperand r = x;
+  const uint16_t* base = static_cast<const uint16_t*>(x.ptr);
+  const int64_t hr = rows / 2, hc = cols / 2;
+  r.ptr = x.trans ? base + (int64_t)bj * hc * x.ld + bi * hr : base + (int64_t)bi * hr * x.ld + bj * hc;
+  return r;
+}
+
+BlockedOperand temp_op(void* p, int64_t rows, int64_t cols, int trans) {
+  BlockedOperand r;
+  r.ptr = p;
+  r.ld = trans ? rows : cols;  // stored (cols x rows) when transposed
+  r.trans = trans;
+  r.dtype = kF16;
+  r.scaled = 1;
+  return r;
+}
+
+// The seven operand pairs of one level.  L is the left operand (Ml x Kl), R the
+// right one (Kl x Nl); S/T are the pre-add outputs of this level.
+void product_operands(const StrassenRun& run, int level, const BlockedOperand& L,
+                      const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
+                      BlockedOperand (&left)[7], BlockedOperand (&right)[7]) {
+  const int64_t m = Ml / 2, k = Kl / 2, n = Nl / 2;
+  auto S = [&](int q) { return temp_op(run.S[level][q], m, k, L.trans); };
+  auto T = [&](int q) { return temp_op(run.T[level][q], k, n, R.trans); };
+  auto Lb = [&](int i, int j) { return sub_block(L, Ml, Kl, i, j); };
+  auto Rb = [&](int i, int j) { return sub_block(R, Kl, Nl, i, j); };
+  if (run.variant == FGEMM_VARIANT_WINOGRAD) {
+    left[0] = Lb(0, 0); right[0] = Rb(0, 0);  // P1 = A11 B11
+    left[1] = Lb(0, 1); right[1] = Rb(1, 0);  // P2 = A12 B21
+    left[2] = S(3);     right[2] = Rb(1, 1);  // P3 = S4 B22
+    left[3] = Lb(1, 1); right[3] = T(3);      // P4 = A22 T4
+    left[4] = S(0);     right[4] = T(0);      // P5 = S1 T1
+    left[5] = S(1);     right[5] = T(1);      // P6 = S2 T2
+    left[6] = S(2);     right[6] = T(2);      // P7 = S3 T3
+  } else {
+    left[0] = S(0);     right[0] = T(0);      // M1 = (A11+A22)(B11+B22)
+    left[1] = S(1);     right[1] = Rb(0, 0);  // M2 = (A21+A22) B11
+    left[2] = Lb(0, 0); right[2] = T(1);      // M3 = A11 (B12-B22)
+    left[3] = Lb(1, 1); right[3] = T(2);      // M4 = A22 (B21-B11)
+    left[4] = S(2);     right[4] = Rb(1, 1);  // M5 = (A11+A12) B22
+    left[5] = S(3);     right[5] = T(3);      // M6 = (A21-A11)(B11+B12)
+    left[6] = S(4);     right[6] = T(4);      // M7 = (A12-A22)(B21+B22)
+  }
+}
+
+fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOperand& L,
+                              const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
+                              float* out32, int64_t ld32) {
+  const Call& c = *run.c;
+  const int64_t m = Ml / 2, k = Kl / 2, n = Nl / 2;
+  hipError_t e = launch_preadd(L, Ml, Kl, run.variant, 0, run.scale_a, run.S[level], c.stream);
+  if (e != hipSuccess) return FGEMM_ERR_HIP;
+  e = launch_preadd(R, Kl, Nl, run.variant, 1, run.scale_b, run.T[level], c.stream);
+  if (e != hipSuccess) return FGEMM_ERR_HIP;
+  BlockedOperand left[7], right[7];
+  product_operands(run, level, L, R, Ml, Kl, Nl, left, right);
+  if (level == run.depth) {
+    GemmBatch b{};
+    b.count = 7;
+    for (int i = 0; i < 7; ++i) {
+      GemmProblem& p = b.p[i];
+      p.A = left[i].ptr; p.lda = left[i].ld;
+      p.B = right[i].ptr; p.ldb = right[i].ld;
+      p.C = run.P[level][i]; p.Cin = nullptr; p.ldc = n;
+      p.M = (int)m; p.N = (int)n; p.K = (int)k;
+      p.alpha = 1.f; p.beta = 0.f;
+      p.scale_a = run.scale_a; p.scale_b = run.scale_b;
+      p.cvt_a = !left[i].scaled; p.cvt_b = !right[i].scaled;
+    }
+    KernelKey key{};
+    key.tile = run.sub_tile;
+    key.a_kcontig = !L.trans;
+    key.b_kcontig = R.trans;
+    key.dtype = kF16;
+    key.epi = kEpiStore32;
+    key.vec = 1;
+    key.strassen = 1;
+    key.in_dtype = run.in_dtype;
+    e = launch_gemm(key, b, c.stream);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
+  } else {
+    for (int i = 0; i < 7; ++i) {
+      fgemm_status_t st = strassen_level(run, level + 1, left[i], right[i], m, k, n,
+                                         run.P[level][i], n);
+      if (st != FGEMM_OK) return st;
+    }
+  }
+  PostAddArgs pa{};
+  for (int i = 0; i < 7; ++i) pa.P[i] = run.P[level][i];
+  pa.m = m;
+  pa.n = n;
+  pa.variant = run.variant;
+  if (level > 1) {
+    pa.out32 = out32;
+    pa.ld32 = ld32;
+  } else {
+    pa.C = c.C;
+    pa.ldc = c.ldc;
+    pa.dtype = run.in_dtype;
+    pa.alpha = c.alpha;
+    pa.beta = c.beta;
+    pa.bias = (epi_flags(c.epi) & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr;
+    pa.scale_a = run.scale_a;
+    pa.scale_b = run.scale_b;
+  }
+  e = launch_postadd(pa, c.stream);
+  return hip_status(e);
+}
+
+fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
+  const size_t need = strassen_workspace(c.M, c.N, c.K, plan.depth, plan.variant);
+  void* ws;
+  fgemm_status_t st = ensure_workspace(h, need, &ws);
+  if (st != FGEMM_OK) return st;
+  StrassenRun run{};
+  run.c = &c;
+  run.depth = plan.depth;
+  run.variant = plan.variant;
+  run.sub_tile = tile_id(plan.tile_m, plan.tile_n);
+  if (run.sub_tile != 0 && run.sub_tile != 1) run.sub_tile = 0;
+  run.in_dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  unsigned* maxbits = reinterpret_cast<unsigned*>(base);
+  run.scale_a = reinterpret_cast<float*>(base + 64);
+  run.scale_b = reinterpret_cast<float*>(base + 128);
+  size_t off = kScaleHeaderBytes;
+  const int ns = plan.variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  for (int l = 1; l <= plan.depth; ++l) {
+    const int64_t m = c.M >> l, k = c.K >> l, n = c.N >> l;
+    for (int q = 0; q < ns; ++q) { run.S[l][q] = base + off; off += align256((size_t)(m * k * 2)); }
+    for (int q = 0; q < ns; ++q) { run.T[l][q] = base + off; off += align256((size_t)(k * n * 2)); }
+    for (int q = 0; q < 7; ++q) {
+      run.P[l][q] = reinterpret_cast<float*>(base + off);
+      off += align256((size_t)(m * n * 4));
+    }
+  }
+  // power-of-two scales keeping every fp16 sum in range: at most 4^depth terms
+  const float target = plan.depth == 1 ? 8192.f : 2048.f;
+  hipError_t e = launch_fill_u32(maxbits, 0u, 2, c.stream);
+  if (e == hipSuccess)
+    e = launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
+                      run.in_dtype, maxbits, c.stream);
+  if (e == hipSuccess)
+    e = launch_maxabs(c.B, c.ldb, c.tb == FGEMM_OP_T ? c.N : c.K, c.tb == FGEMM_OP_T ? c.K : c.N,
+                      run.in_dtype, maxbits + 1, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(maxbits, target, run.scale_a, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(maxbits + 1, target, run.scale_b, c.stream);
+  if (e != hipSuccess) return FGEMM_ERR_HIP;
+  BlockedOperand L{c.A, c.lda, c.ta == FGEMM_OP_T, run.in_dtype, 0};
+  BlockedOperand R{c.B, c.ldb, c.tb == FGEMM_OP_T, run.in_dtype, 0};
+  return strassen_level(run, 1, L, R, c.M, c.K, c.N, nullptr, 0);
+}
+
+fgemm_status_t execute(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
+  const int vec = vec_ok(c.ta, c.tb, c.N, c.A, c.lda, c.B, c.ldb, c.C, c.ldc, c.epi);
+  const uint32_t flags = epi_flags(c.epi);
+  fgemm_status_t st = check_plan_shape(plan, c.M, c.N, c.K, vec, flags);
+  if (st != FGEMM_OK) return st;
+  if (plan.path == FGEMM_PATH_STRASSEN) return run_strassen(h, plan, c);
+  return run_classical(h, plan, c, vec);
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* fgemm_status_string(fgemm_status_t s) {
+  switch (s) {
+    case FGEMM_OK: return "FGEMM_OK";
+    case FGEMM_ERR_INVALID_VALUE: return "FGEMM_ERR_INVALID_VALUE";
+    case FGEMM_ERR_NOT_SUPPORTED: return "FGEMM_ERR_NOT_SUPPORTED";
+    case FGEMM_ERR_WORKSPACE: return "FGEMM_ERR_WORKSPACE";
+    case FGEMM_ERR_ALLOC: return "FGEMM_ERR_ALLOC";
+    case FGEMM_ERR_HIP: return "FGEMM_ERR_HIP";
+  }
+  return "FGEMM_UNKNOWN_STATUS";
+}
+
+fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                float beta, const void* C, int64_t ldc, fgemm_dtype_t dtype,
+                                const fgemm_epilogue_t* epi) {
+  if (ta != FGEMM_OP_N && ta != FGEMM_OP_T) return FGEMM_ERR_INVALID_VALUE;
+  if (tb != FGEMM_OP_N && tb != FGEMM_OP_T) return FGEMM_ERR_INVALID_VALUE;
+  if (dtype != FGEMM_F16 && dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
+  if (M > INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX) return FGEMM_ERR_NOT_SUPPORTED;
+  const uint32_t flags = epi_flags(epi);
+  if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU))
+    return FGEMM_ERR_INVALID_VALUE;
+  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
+  if (swiglu && (flags & (FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ))) return FGEMM_ERR_NOT_SUPPORTED;
+  const int64_t Nb = swiglu ? 2 * N : N;
+  const int64_t a_cols = ta == FGEMM_OP_N ? K : M;   // stored row width of A
+  const int64_t b_cols = tb == FGEMM_OP_N ? Nb : K;  // stored row width of B
+  if (lda < (a_cols > 1 ? a_cols : 1)) return FGEMM_ERR_INVALID_VALUE;
+  if (ldb < (b_cols > 1 ? b_cols : 1)) return FGEMM_ERR_INVALID_VALUE;
+  if (ldc < (N > 1 ? N : 1)) return FGEMM_ERR_INVALID_VALUE;
+  const bool any_out = M > 0 && N > 0;
+  if (any_out && K > 0 && (A == nullptr || B == nullptr)) return FGEMM_ERR_INVALID_VALUE;
+  if (any_out && C == nullptr) return FGEMM_ERR_INVALID_VALUE;
+  (void)beta;
+  if ((flags & FGEMM_EPI_BIAS) && any_out && epi->bias == nullptr) return FGEMM_ERR_INVALID_VALUE;
+  if ((flags & FGEMM_EPI_ROWSUMSQ) && any_out && epi->rowsumsq == nullptr)
+    return FGEMM_ERR_INVALID_VALUE;
+  if (swiglu) {
+    if (any_out && epi->rms_rowsumsq == nullptr) return FGEMM_ERR_INVALID_VALUE;
+    if (epi->rms_n <= 0 || !(epi->rms_eps >= 0.f)) return FGEMM_ERR_INVALID_VALUE;
+  }
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
+  if (!handle) return FGEMM_ERR_INVALID_VALUE;
+  *handle = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return FGEMM_ERR_HIP;
+  if (device < 0 || device >= count) return FGEMM_ERR_INVALID_VALUE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FGEMM_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FGEMM_ERR_NOT_SUPPORTED;
+  fgemm_handle_s* h = new (std::nothrow) fgemm_handle_s();
+  if (!h) return FGEMM_ERR_ALLOC;
+  h->device = device;
+  double ghz = prop.clockRate > 0 ? prop.clockRate / 1e6 : 2.4;
+  model_defaults(&h->model, prop.multiProcessorCount, ghz);
+  *handle = h;
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_destroy(fgemm_handle_t h) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  if (h->own_ws) {
+    hipDeviceSynchronize();
+    hipFree(h->own_ws);
+  }
+  delete h;
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_set_workspace(fgemm_handle_t h, void* dptr, size_t bytes) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  if (dptr == nullptr && bytes != 0) return FGEMM_ERR_INVALID_VALUE;
+  if (dptr && !aligned16(dptr)) return FGEMM_ERR_INVALID_VALUE;
+  h->user_ws = dptr;
+  h->user_ws_bytes = dptr ? bytes : 0;
+  h->plans.clear();  // workspace guards depend on it
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_get_model(fgemm_handle_t h, fgemm_model_t* m) {
+  if (!h || !m) return FGEMM_ERR_INVALID_VALUE;
+  *m = h->model;
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_set_model(fgemm_handle_t h, const fgemm_model_t* m) {
+  if (!h || !m) return FGEMM_ERR_INVALID_VALUE;
+  if (m->compute_units <= 0 || !(m->peak_tflops > 0) || !(m->hbm_gbps > 0) ||
+      !(m->eta_mfma > 0) || !(m->eta_hbm > 0) || !(m->launch_us >= 0))
+    return FGEMM_ERR_INVALID_VALUE;
+  h->model = *m;
+  h->plans.clear();
+  return FGEMM_OK;
+}
+
+fgemm_status_t fgemm_select_model(const fgemm_model_t* md, fgemm_op_t ta, fgemm_op_t tb,
+                                  int64_t M, int64_t N, int64_t K, fgemm_dtype_t dtype,
+                                  const fgemm_epilogue_t* epi, fgemm_plan_t* plan) {
+  if (!md || !plan) return FGEMM_ERR_INVALID_VALUE;
+  if (ta != FGEMM_OP_N && ta != FGEMM_OP_T) return FGEMM_ERR_INVALID_VALUE;
+  if (tb != FGEMM_OP_N && tb != FGEMM_OP_T) return FGEMM_ERR_INVALID_VALUE;
+  if (dtype != FGEMM_F16 && dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
+  if (md->compute_units <= 0 || !(md->peak_tflops > 0) || !(md->hbm_gbps > 0))
+    return FGEMM_ERR_INVALID_VALUE;
+  // shapes only: assume the aligned fast path, no beta traffic, no workspace cap
+  // beyond the model's own
+  return select_plan(*md, M, N, K, epi_flags(epi), 0, 1, (size_t)-1, plan);
+}
+
+fgemm_status_t fgemm_select(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t N,
+                            int64_t K, fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
+                            fgemm_plan_t* plan) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  return fgemm_select_model(&h->model, ta, tb, M, N, K, dtype, epi, plan);
+}
+
+fgemm_status_t fgemm_gemm_plan(fgemm_handle_t h, const fgemm_plan_t* plan, fgemm_op_t ta,
+                               fgemm_op_t tb, int64_t M, int64_t N, int64_t K, float alpha,
+                               const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                               void* C, int64_t ldc, fgemm_dtype_t dtype,
+                               const fgemm_epilogue_t* epi, void* stream) {
+  if (!h || !plan) return FGEMM_ERR_INVALID_VALUE;
+  fgemm_status_t st = fgemm_check_args(ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype, epi);
+  if (st != FGEMM_OK) return st;
+  if (M == 0 || N == 0) return FGEMM_OK;
+  Call c{ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, epi,
+         static_cast<hipStream_t>(stream)};
+  fgemm_plan_t p = *plan;
+  if (p.path == FGEMM_PATH_CLASSICAL && (p.tile_m == 0 || p.tile_n == 0)) {
+    const int swiglu = (epi_flags(epi) & FGEMM_EPI_RMS_SWIGLU) != 0;
+    int t = best_tile(h->model, M, N, K, swiglu, 1, 2.0, 2.0, beta != 0.f, nullptr);
+    p.tile_m = tile_m_of(t);
+    p.tile_n = tile_n_of(t);
+  } else if (p.path == FGEMM_PATH_STRASSEN && (p.tile_m == 0 || p.tile_n == 0)) {
+    if (p.depth >= 1 && p.depth <= 2) {
+      int t = best_tile(h->model, M >> p.depth, N >> p.depth, K >> p.depth, 0, 7, 2.0, 4.0, 0,
+                        nullptr);
+      if (t > 1) t = 1;
+      p.tile_m = tile_m_of(t);
+      p.tile_n = tile_n_of(t);
+    }
+  }
+  if (p.path == FGEMM_PATH_STRASSEN && tile_id(p.tile_m, p.tile_n) > 1)
+    return FGEMM_ERR_NOT_SUPPORTED;
+  if (tile_id(p.tile_m, p.tile_n) < 0 && p.path == FGEMM_PATH_CLASSICAL)
+    return FGEMM_ERR_INVALID_VALUE;
+  return execute(h, p, c);
+}
+
+fgemm_status_t fgemm_gemm(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t N,
+                          int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, float beta, void* C, int64_t ldc, fgemm_dtype_t dtype,
+                          const fgemm_epilogue_t* epi, void* stream) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  fgemm_status_t st = fgemm_check_args(ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype, epi);
+  if (st != FGEMM_OK) return st;
+  if (M == 0 || N == 0) return FGEMM_OK;
+  const int vec = vec_ok(ta, tb, N, A, lda, B, ldb, C, ldc, epi);
+  PlanKey key{M, N, K, (int)ta, (int)tb, (int)dtype, (int)epi_flags(epi) | (beta != 0.f ? 8 : 0),
+              vec};
+  auto it = h->plans.find(key);
+  fgemm_plan_t plan;
+  if (it != h->plans.end()) {
+    plan = it->second;
+  } else {
+    size_t limit = h->user_ws ? h->user_ws_bytes : (size_t)-1;
+    st = select_plan(h->model, M, N, K, epi_flags(epi), beta != 0.f, vec, limit, &plan);
+    if (st != FGEMM_OK) return st;
+    h->plans.emplace(key, plan);
+  }
+  Call c{ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, epi,
+         static_cast<hipStream_t>(stream)};
+  return execute(h, plan, c);
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// gemm_inst.hip — instantiates the classical kernel for one (MFMA dtype, A layout,
+// B layout), chosen by -DFG_DT (0 fp16, 1 bf16), -DFG_AK, -DFG_BK at compile time.
+#include "gemm_mfma.h"
+
+#ifndef FG_DT
+#error "FG_DT, FG_AK and FG_BK select the instantiation"
+#endif
+
+#define FG_CAT2(a, b) a##b
+#define FG_CAT(a, b) FG_CAT2(a, b)
+#define FG_NAME FG_CAT(FG_CAT(FG_CAT(launch_gemm_, FG_DT), FG_CAT(_, FG_AK)), FG_BK)
+
+namespace fgemm {
+
+template <class CFG, int EPI, bool VEC>
+static hipError_t plain(const GemmBatch& b, hipStream_t s) {
+  return launch_t<CFG, FG_DT, FG_AK != 0, FG_BK != 0, EPI, VEC, false, 0>(b, s);
+}
+
+template <class CFG>
+static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
+  if (k.epi == kEpiStore16) return k.vec ? plain<CFG, kEpiStore16, true>(b, s)
+                                         : plain<CFG, kEpiStore16, false>(b, s);
+  if constexpr (CFG::FN % 2 == 0) {
+    if (k.epi == kEpiSwiGLU) return k.vec ? plain<CFG, kEpiSwiGLU, true>(b, s)
+                                          : plain<CFG, kEpiSwiGLU, false>(b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t FG_NAME(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
+  if (k.strassen) {
+#if FG_DT == 0
+    // Strassen sub-products: fp16 MFMA on fp16 temporaries and converted blocks,
+    // raw fp32 accumulators out.  Operands are always aligned here.
+    if (k.epi != kEpiStore32 || !k.vec) return hipErrorInvalidValue;
+    if (k.tile == 0)
+      return k.in_dtype == kBF16
+                 ? launch_t<Cfg256, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kBF16>(b, s)
+                 : launch_t<Cfg256, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kF16>(b, s);
+    if (k.tile == 1)
+      return k.in_dtype == kBF16
+                 ? launch_t<Cfg128, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kBF16>(b, s)
+                 : launch_t<Cfg128, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kF16>(b, s);
+#endif
+    return hipErrorInvalidValue;
+  }
+  switch (k.tile) {
+    case 0: return by_epilogue<Cfg256>(k, b, s);
+    case 1: return by_epilogue<Cfg128>(k, b, s);
+    case 2: return by_epilogue<Cfg64>(k, b, s);
+    case 3: return by_epilogue<Cfg32>(k, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fgemm

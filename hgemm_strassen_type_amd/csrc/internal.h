@@ -1,0 +1,123 @@
+// internal.h — declarations shared by the library's host code and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fgemm.h"
+
+namespace fgemm {
+
+// Element types of an operand as it sits in memory.
+enum ElemType : int { kF16 = 0, kBF16 = 1 };
+
+// Epilogue kinds the kernel template is instantiated for.
+enum EpiKind : int {
+  kEpiStore16 = 0,   // 16-bit output: alpha, beta*C, optional bias, optional row sum of squares
+  kEpiSwiGLU = 1,    // 16-bit output of silu(r*alpha*gate) * (r*alpha*up) + beta*C
+  kEpiStore32 = 2,   // fp32 output of the raw accumulators (Strassen sub-products)
+};
+
+// Runtime epilogue switches inside kEpiStore16.
+enum : uint32_t { kFlagBias = 1u, kFlagRowSumSq = 2u, kFlagBeta = 4u };
+
+// One GEMM problem as the classical kernel sees it.  Pointers are device pointers.
+// op(A) is M x K, op(B) is K x Nb (Nb = N, or 2N for SwiGLU), output M x N.
+struct GemmProblem {
+  const void* A;
+  const void* B;
+  void* C;              // output (16-bit or fp32)
+  const void* Cin;      // beta*C input, same type/layout as C (may equal C)
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  float alpha, beta;
+  uint32_t flags;       // kFlag* bits
+  const void* bias;     // [N] 16-bit
+  float* ss_partial;    // [tiles_n * 2][M] per-wave-column partial sums of squares
+  const float* rms_ss;  // [M] sums of squares for the RMS scale
+  float rms_inv_n, rms_eps;
+  const float* scale_a; // device scalar: multiply A by it while converting (Strassen)
+  const float* scale_b; // device scalar for B
+  int cvt_a, cvt_b;     // Strassen products: 1 = operand is in the input type and still
+                        // needs the scale and the conversion to fp16; 0 = fp16 temporary
+};
+
+// Up to 7 problems of one shape launched together (the Strassen sub-products).
+struct GemmBatch {
+  GemmProblem p[7];
+  int count;
+};
+
+// Kernel selection for one launch.
+struct KernelKey {
+  int tile;           // 0: 256x256, 1: 128x128, 2: 64x128 (skinny), 3: 32x128 (skinny)
+  int a_kcontig;      // 1: op(A) rows are K-contiguous (A not transposed)
+  int b_kcontig;      // 1: op(B) columns are K-contiguous (B transposed)
+  int dtype;          // ElemType of the MFMA inputs and of 16-bit outputs
+  int epi;            // EpiKind
+  int vec;            // 1: 16-byte aligned fast path
+  int strassen;       // 1: Strassen sub-products (fp16 MFMA, per-problem conversion)
+  int in_dtype;       // Strassen: ElemType of the caller's operands
+};
+
+// One instantiation unit per (MFMA dtype, A layout, B layout); each is compiled from
+// gemm_inst.hip with its own -D switches.
+#define FGEMM_INST_DECL(DT, AK, BK) \
+  hipError_t launch_gemm_##DT##_##AK##BK(const KernelKey& k, const GemmBatch& b, hipStream_t s);
+FGEMM_INST_DECL(0, 0, 0) FGEMM_INST_DECL(0, 0, 1) FGEMM_INST_DECL(0, 1, 0) FGEMM_INST_DECL(0, 1, 1)
+FGEMM_INST_DECL(1, 0, 0) FGEMM_INST_DECL(1, 0, 1) FGEMM_INST_DECL(1, 1, 0) FGEMM_INST_DECL(1, 1, 1)
+#undef FGEMM_INST_DECL
+
+int tile_m_of(int tile);
+int tile_n_of(int tile);
+int waves_n_of(int tile);
+
+// Launch the classical kernel over a batch of same-shape problems.
+hipError_t launch_gemm(const KernelKey& key, const GemmBatch& batch, hipStream_t stream);
+
+// Deterministic reduction of the per-wave partial sums of squares into ss[M].
+hipError_t launch_rowsumsq_reduce(const float* partial, int parts, int M, float* ss,
+                                  hipStream_t stream);
+
+// ---------------------------------------------------------------- Strassen kernels
+// A 2x2-blocked operand: base pointer, leading dimension, layout, element type and
+// whether its values still need the Strassen scale.  Sub-block (bi, bj) of the
+// logical (rows x cols) matrix starts at rows*bi/2, cols*bj/2.
+struct BlockedOperand {
+  const void* ptr;
+  int64_t ld;
+  int trans;          // stored transposed (logical row r, col c at ptr[c*ld + r])
+  int dtype;          // ElemType in memory
+  int scaled;         // 1: values already carry the scale (fp16 temporaries)
+};
+
+hipError_t launch_maxabs(const void* X, int64_t ld, int64_t rows, int64_t cols, int dtype,
+                         unsigned* max_bits, hipStream_t stream);
+hipError_t launch_fill_u32(unsigned* p, unsigned value, int64_t n, hipStream_t stream);
+hipError_t launch_scale_from_max(const unsigned* max_bits, float target, float* scale,
+                                 hipStream_t stream);
+
+// Pre-add: from the four sub-blocks of `src` (logical rows x cols), write the sum
+// operands of the variant into fp16 buffers out[0..count) (rows/2 x cols/2 each,
+// same layout as src, leading dimension = their own width), values times *scale
+// unless src.scaled.  side 0 = left operand (A), 1 = right operand (B).
+hipError_t launch_preadd(const BlockedOperand& src, int64_t rows, int64_t cols, int variant,
+                         int side, const float* scale, void* const* out, hipStream_t stream);
+
+// Post-add: combine seven fp32 products P[0..7) (m x n, ld = n) into the four
+// blocks of the output (2m x 2n).  out32 != null: fp32 output with ld_out (plain
+// combination).  Otherwise 16-bit output C (ldc) = RNE(alpha/(sa*sb) * comb
+// + beta*Cin + bias).
+struct PostAddArgs {
+  const float* P[7];
+  int64_t m, n;
+  int variant;
+  float* out32; int64_t ld32;
+  void* C; int64_t ldc; int dtype;
+  float alpha, beta;
+  const void* bias;
+  const float* scale_a; const float* scale_b;
+};
+hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
+
+}  // namespace fgemm

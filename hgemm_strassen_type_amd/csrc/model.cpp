@@ -1,0 +1,139 @@
+// model.cpp — the analytic decision model (pure host code, no device calls).
+//
+// FalconGEMM summary (euno.news), Methodology 4: the decision module estimates the
+// run time of every candidate from compute throughput, memory bandwidth and the
+// extra cost of each recursion level, and picks the algorithm and tiling of least
+// predicted time; Methodology 5: it is queried at run time with the actual sizes.
+// The time terms come from CS336 Lecture 05 notes:
+//   Page 21 (roofline): a kernel's time is about max(FLOPs / P_peak, bytes / B_mem);
+//   Page 43 (tile quantization): ceil-divided tile grids compute padded tiles;
+//   Page 48 (wave quantization): tiles run in waves of one tile per compute unit,
+//     the last wave possibly partly empty.
+// Strassen candidates add the traffic of their block additions per level and run
+// 7^d sub-products of (M/2^d, N/2^d, K/2^d) in batches of seven.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "model.h"
+
+namespace fgemm {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Macro-tiles of the classical kernel and the share of the per-CU MFMA rate each
+// reaches at steady state relative to the 256x256 tile (smaller tiles re-read
+// operands more often per FLOP and hide less latency).
+const TileInfo kTiles[kNumTiles] = {
+    {0, 256, 256, 1.00},
+    {1, 128, 128, 0.70},
+    {2, 64, 128, 0.45},
+    {3, 32, 128, 0.30},
+};
+
+void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
+  m->compute_units = cus;
+  // dense 16-bit MFMA: 4 SIMDs x 1024 FLOP per clock per CU on gfx950
+  m->peak_tflops = cus * 4096.0 * clock_ghz * 1e9 / 1e12;
+  m->hbm_gbps = 8000.0;
+  m->eta_mfma = 0.70;
+  m->eta_hbm = 0.80;
+  m->launch_us = 4.0;
+  m->max_workspace_bytes = 16.0 * (1ull << 30);
+}
+
+// Time of one classical launch of `count` same-shape problems on one tile config.
+double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
+                         int64_t K, int64_t Nb, int64_t out_bn, int count, double in_bytes,
+                         double out_bytes, int beta) {
+  const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, out_bn) * count;
+  const int64_t waves = ceil_div(tiles, md.compute_units);
+  const double per_cu = md.peak_tflops * 1e12 / md.compute_units;  // FLOP/s per CU
+  const double tile_flops = 2.0 * t.bm * t.bn * (double)(K > 0 ? K : 1);
+  const double t_compute = waves * tile_flops / (per_cu * md.eta_mfma * t.rel_eta);
+  const double bytes = count * ((double)M * K * in_bytes + (double)K * Nb * in_bytes +
+                                (double)M * N * out_bytes * (beta ? 2.0 : 1.0));
+  const double t_mem = bytes / (md.hbm_gbps * 1e9 * md.eta_hbm);
+  const double tt = t_compute > t_mem ? t_compute : t_mem;
+  return tt * 1e6 + md.launch_us;
+}
+
+int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
+              double in_bytes, double out_bytes, int beta, double* t_us) {
+  int best = -1;
+  double bt = 0;
+  for (int i = 0; i < kNumTiles; ++i) {
+    const TileInfo& t = kTiles[i];
+    if (swiglu && t.tile == 3) continue;  // the SwiGLU epilogue needs two column halves
+    const int64_t out_bn = swiglu ? t.bn / 2 : t.bn;
+    const int64_t Nb = swiglu ? 2 * N : N;
+    double tt = classical_time_us(md, t, M, N, K, Nb, out_bn, count, in_bytes, out_bytes, beta);
+    if (best < 0 || tt < bt) {
+      best = t.tile;
+      bt = tt;
+    }
+  }
+  if (t_us) *t_us = bt;
+  return best;
+}
+
+size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant) {
+  const int64_t ns = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  size_t total = kScaleHeaderBytes;
+  for (int l = 1; l <= depth; ++l) {
+    const int64_t m = M >> l, k = K >> l, n = N >> l;
+    total += align256((size_t)(m * k * 2)) * ns;
+    total += align256((size_t)(k * n * 2)) * ns;
+    total += align256((size_t)(m * n * 4)) * 7;
+  }
+  return total;
+}
+
+double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
+                        int variant, int beta, int* sub_tile) {
+  const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
+  const double ns = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  double t = 0, launches = 0;
+  // max|A|, max|B| for the fp16 scales
+  t += ((double)M * K + (double)K * N) * 2.0 / bw;
+  launches += 5;  // fills, two max passes, two scale kernels
+  double instances = 1;  // how many problems of this level run
+  for (int l = 1; l <= depth; ++l) {
+    const double m = (double)(M >> l), k = (double)(K >> l), n = (double)(N >> l);
+    const double pre = 4 * m * k * 2 + ns * m * k * 2 + 4 * k * n * 2 + ns * k * n * 2;
+    const double pwrite = 7 * m * n * 4;            // products written by the GEMMs
+    const double post = 7 * m * n * 4 + 4 * m * n * (l == 1 ? 2.0 : 4.0) +
+                        (l == 1 && beta ? 4 * m * n * 2.0 : 0.0);
+    t += instances * (pre + pwrite + post) / bw;
+    launches += instances * 3;
+    instances *= 7;
+  }
+  // sub-products: 7^d problems of the deepest size, seven per launch
+  const int64_t m = M >> depth, n = N >> depth, k = K >> depth;
+  double tp;
+  int tile = best_tile(md, m, n, k, 0, 7, 2.0, 4.0, 0, &tp);
+  if (sub_tile) *sub_tile = tile;
+  const double batches = instances / 7;
+  t += batches * (tp - md.launch_us) * 1e-6;
+  launches += batches;
+  return t * 1e6 + launches * md.launch_us;
+}
+
+}  // namespace fgemm
+
+using namespace fgemm;
+
+extern "C" int64_t fgemm_tile_count(int64_t M, int64_t N, int64_t tile_m, int64_t tile_n) {
+  if (M < 0 || N < 0 || tile_m <= 0 || tile_n <= 0) return -1;
+  return ceil_div(M, tile_m) * ceil_div(N, tile_n);
+}
+
+extern "C" int64_t fgemm_wave_count(int64_t tiles, int64_t units, double* tail_fraction) {
+  if (tiles < 0 || units <= 0) return -1;
+  const int64_t waves = ceil_div(tiles, units);
+  if (tail_fraction) {
+    const int64_t last = tiles - (waves > 0 ? (waves - 1) * units : 0);
+    *tail_fraction = waves > 0 ? (double)last / (double)units : 0.0;
+  }
+  return waves;
+}

@@ -1,0 +1,35 @@
+// model.h — the analytic time model shared by selection and dispatch (host only).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fgemm.h"
+
+namespace fgemm {
+
+struct TileInfo {
+  int tile;        // kernel tile id
+  int bm, bn;      // macro-tile (bn MFMA columns; SwiGLU writes bn/2 outputs)
+  double rel_eta;  // steady-state MFMA efficiency relative to the 256x256 tile
+};
+
+constexpr int kNumTiles = 4;
+extern const TileInfo kTiles[kNumTiles];
+constexpr size_t kScaleHeaderBytes = 256;
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+int64_t ceil_div(int64_t a, int64_t b);
+
+void model_defaults(fgemm_model_t* m, int cus, double clock_ghz);
+
+double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
+                         int64_t K, int64_t Nb, int64_t out_bn, int count, double in_bytes,
+                         double out_bytes, int beta);
+int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
+              double in_bytes, double out_bytes, int beta, double* t_us);
+size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant);
+double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
+                        int variant, int beta, int* sub_tile);
+
+}  // namespace fgemm

@@ -1,0 +1,360 @@
+// strassen_adds.hip — the memory-bound kernels of the Strassen/Winograd path.
+//
+// FalconGEMM summary (euno.news), Methodology 1 and 3: a low-complexity algorithm
+// replaces one product of 2x2 blocks by seven block products plus block sums, and
+// kernels are grouped so shared partial results stay on chip instead of being
+// fetched from DRAM again.  Here that grouping means:
+//   - one pre-add kernel per operand reads its four sub-blocks once and writes all
+//     of the variant's sums, chained sums (Winograd S2 from S1, S4 from S2, ...)
+//     staying in registers in fp32;
+//   - one post-add kernel reads the seven fp32 products once and writes all four
+//     output blocks, with alpha, beta*C and the bias fused in at the top level.
+// The limitation the same summary notes (temporary buffers cost memory) is why
+// the temporaries are 16-bit and the products are reused level by level.
+//
+// Precision: sums are formed in fp32 from the exact inputs and rounded once to
+// fp16.  bf16 (or large fp16) inputs are first multiplied by a power of two chosen
+// from max|x| so that every sum stays inside the fp16 range; the product of the two
+// scales is divided out in the final post-add.  Products accumulate in fp32.
+//
+// All kernels stream 16-byte vectors per lane with grid-stride loops over the
+// sub-block; they are bound by HBM bandwidth.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace fgemm {
+
+namespace {
+
+__device__ __forceinline__ float h2f(uint32_t h, int dt) {
+  return dt == kBF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t f2h16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t f2h(float f, int dt) {
+  return dt == kBF16 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f) : f2h16(f);
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, int dt, float* f) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    f[2 * p] = h2f(w[p] & 0xffffu, dt);
+    f[2 * p + 1] = h2f(w[p] >> 16, dt);
+  }
+}
+__device__ __forceinline__ uint4 pack8_f16(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) w[p] = f2h16(f[2 * p]) | (f2h16(f[2 * p + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ------------------------------------------------------------------ max |x|
+__global__ void fill_u32_kernel(unsigned* p, unsigned v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// max |x| over a stored rows x cols matrix (leading dimension ld), as the bit
+// pattern of a non-negative float (monotone as an unsigned integer).
+__global__ void maxabs_kernel(const uint16_t* __restrict__ X, int64_t ld, int64_t rows,
+                              int64_t cols, int dt, unsigned* max_bits) {
+  float m = 0.f;
+  const int64_t chunks = (cols + 7) / 8;
+  const int64_t total = rows * chunks;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = t / chunks, c = (t - r * chunks) * 8;
+    const uint16_t* p = X + r * ld + c;
+    if (c + 8 <= cols && ((ld & 7) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0)) {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(p), dt, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+    } else {
+      for (int e = 0; e < 8 && c + e < cols; ++e) m = fmaxf(m, fabsf(h2f(p[e], dt)));
+    }
+  }
+  // wave reduction, then one atomic per wave
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(max_bits, __float_as_uint(m));
+}
+
+// scale = 2^floor(log2(target / max)), 1 when max is 0 or not finite.
+__global__ void scale_from_max_kernel(const unsigned* max_bits, float target, float* scale) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  float m = __uint_as_float(*max_bits);
+  float s = 1.f;
+  if (m > 0.f && isfinite(m)) {
+    int e;
+    frexpf(target / m, &e);          // target/m = f * 2^e, 0.5 <= f < 1
+    e -= 1;
+    e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    s = ldexpf(1.f, e);
+  }
+  *scale = s;
+}
+
+// ------------------------------------------------------------------ pre-add
+struct PreAddArgs {
+  const uint16_t* blk[4];   // X11, X12, X21, X22 (logical blocks) in storage
+  int64_t ld;               // source leading dimension
+  int64_t srows, scols;     // stored sub-block shape (scols contiguous)
+  uint16_t* out[5];         // fp16 outputs, stored srows x scols, leading dim scols
+  int dt;                   // source element type
+  int scaled;               // source already carries the scale
+  const float* scale;
+  int variant, side;
+};
+
+__global__ void preadd_kernel(PreAddArgs a) {
+  const float s = a.scaled ? 1.f : *a.scale;
+  const int64_t chunks = a.scols / 8;
+  const int64_t total = a.srows * chunks;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = t / chunks, c = (t - r * chunks) * 8;
+    int64_t si = r * a.ld + c;
+    float x11[8], x12[8], x21[8], x22[8];
+    unpack8(*reinterpret_cast<const uint4*>(a.blk[0] + si), a.dt, x11);
+    unpack8(*reinterpret_cast<const uint4*>(a.blk[1] + si), a.dt, x12);
+    unpack8(*reinterpret_cast<const uint4*>(a.blk[2] + si), a.dt, x21);
+    unpack8(*reinterpret_cast<const uint4*>(a.blk[3] + si), a.dt, x22);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x11[e] *= s; x12[e] *= s; x21[e] *= s; x22[e] *= s;
+    }
+    const int64_t di = r * a.scols + c;
+    float o[5][8];
+    int n;
+    if (a.variant == FGEMM_VARIANT_WINOGRAD) {
+      n = 4;
+      if (a.side == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float s1 = x21[e] + x22[e];   // S1 = A21 + A22
+          float s2 = s1 - x11[e];       // S2 = S1 - A11
+          o[0][e] = s1;
+          o[1][e] = s2;
+          o[2][e] = x11[e] - x21[e];    // S3 = A11 - A21
+          o[3][e] = x12[e] - s2;        // S4 = A12 - S2
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float t1 = x12[e] - x11[e];   // T1 = B12 - B11
+          float t2 = x22[e] - t1;       // T2 = B22 - T1
+          o[0][e] = t1;
+          o[1][e] = t2;
+          o[2][e] = x22[e] - x12[e];    // T3 = B22 - B12
+          o[3][e] = t2 - x21[e];        // T4 = T2 - B21
+        }
+      }
+    } else {
+      n = 5;
+      if (a.side == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[0][e] = x11[e] + x22[e];    // M1: A11 + A22
+          o[1][e] = x21[e] + x22[e];    // M2: A21 + A22
+          o[2][e] = x11[e] + x12[e];    // M5: A11 + A12
+          o[3][e] = x21[e] - x11[e];    // M6: A21 - A11
+          o[4][e] = x12[e] - x22[e];    // M7: A12 - A22
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[0][e] = x11[e] + x22[e];    // M1: B11 + B22
+          o[1][e] = x12[e] - x22[e];    // M3: B12 - B22
+          o[2][e] = x21[e] - x11[e];    // M4: B21 - B11
+          o[3][e] = x11[e] + x12[e];    // M6: B11 + B12
+          o[4][e] = x21[e] + x22[e];    // M7: B21 + B22
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      if (q < n) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
+  }
+}
+
+// ------------------------------------------------------------------ post-add
+struct PostAddKArgs {
+  const float* P[7];
+  int64_t m, n;
+  int variant;
+  float* out32; int64_t ld32;
+  uint16_t* C; int64_t ldc; int dt;
+  float alpha, beta;
+  const uint16_t* bias;
+  const float* scale_a; const float* scale_b;
+};
+
+__device__ __forceinline__ void combine(int variant, const float (&p)[7], float* c) {
+  if (variant == FGEMM_VARIANT_WINOGRAD) {
+    float u2 = p[0] + p[5];             // U2 = P1 + P6
+    float u3 = u2 + p[6];               // U3 = U2 + P7
+    float u4 = u2 + p[4];               // U4 = U2 + P5
+    c[0] = p[0] + p[1];                 // C11 = P1 + P2
+    c[1] = u4 + p[2];                   // C12 = U4 + P3
+    c[2] = u3 - p[3];                   // C21 = U3 - P4
+    c[3] = u3 + p[4];                   // C22 = U3 + P5
+  } else {
+    c[0] = p[0] + p[3] - p[4] + p[6];   // C11 = M1 + M4 - M5 + M7
+    c[1] = p[2] + p[4];                 // C12 = M3 + M5
+    c[2] = p[1] + p[3];                 // C21 = M2 + M4
+    c[3] = p[0] - p[1] + p[2] + p[5];   // C22 = M1 - M2 + M3 + M6
+  }
+}
+
+__global__ void postadd_kernel(PostAddKArgs a) {
+  const int64_t chunks = a.n / 4;
+  const int64_t total = a.m * chunks;
+  float factor = 1.f;
+  if (!a.out32) factor = a.alpha / (*a.scale_a * *a.scale_b);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int64_t i = t / chunks, j = (t - i * chunks) * 4;
+    float p[4][7];
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      float4 v = *reinterpret_cast<const float4*>(a.P[q] + i * a.n + j);
+      p[0][q] = v.x; p[1][q] = v.y; p[2][q] = v.z; p[3][q] = v.w;
+    }
+    float c[4][4];  // [element][block]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) combine(a.variant, p[e], c[e]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t row = (b >> 1) * a.m + i, col = (b & 1) * a.n + j;
+      if (a.out32) {
+        *reinterpret_cast<float4*>(a.out32 + row * a.ld32 + col) =
+            make_float4(c[0][b], c[1][b], c[2][b], c[3][b]);
+      } else {
+        const int64_t off = row * a.ldc + col;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = factor * c[e][b];
+        if (a.beta != 0.f) {
+          uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+          v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
+          v[1] += a.beta * h2f(cv.x >> 16, a.dt);
+          v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
+          v[3] += a.beta * h2f(cv.y >> 16, a.dt);
+        }
+        if (a.bias) {
+          uint2 bv = *reinterpret_cast<const uint2*>(a.bias + col);
+          v[0] += h2f(bv.x & 0xffffu, a.dt);
+          v[1] += h2f(bv.x >> 16, a.dt);
+          v[2] += h2f(bv.y & 0xffffu, a.dt);
+          v[3] += h2f(bv.y >> 16, a.dt);
+        }
+        *reinterpret_cast<uint2*>(a.C + off) =
+            make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
+                       f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+      }
+    }
+  }
+}
+
+int stream_grid(int64_t work_items) {
+  // enough workgroups to cover every CU several times; grid-stride for the rest
+  int64_t g = (work_items + 255) / 256;
+  return (int)(g < 2048 ? (g > 0 ? g : 1) : 2048);
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(unsigned* p, unsigned value, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p,
+                     value, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_maxabs(const void* X, int64_t ld, int64_t rows, int64_t cols, int dtype,
+                         unsigned* max_bits, hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(maxabs_kernel, dim3(stream_grid(rows * ((cols + 7) / 8))), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(X), ld, rows, cols, dtype, max_bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_from_max(const unsigned* max_bits, float target, float* scale,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(scale_from_max_kernel, dim3(1), dim3(64), 0, stream, max_bits, target, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_preadd(const BlockedOperand& src, int64_t rows, int64_t cols, int variant,
+                         int side, const float* scale, void* const* out, hipStream_t stream) {
+  PreAddArgs a{};
+  const uint16_t* base = static_cast<const uint16_t*>(src.ptr);
+  const int64_t hr = rows / 2, hc = cols / 2;
+  for (int b = 0; b < 4; ++b) {
+    int bi = b >> 1, bj = b & 1;
+    // logical block (bi, bj) starts at logical (bi*hr, bj*hc)
+    a.blk[b] = src.trans ? base + (int64_t)bj * hc * src.ld + bi * hr
+                         : base + (int64_t)bi * hr * src.ld + bj * hc;
+  }
+  a.ld = src.ld;
+  a.srows = src.trans ? hc : hr;
+  a.scols = src.trans ? hr : hc;
+  int n = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  for (int q = 0; q < 5; ++q) a.out[q] = q < n ? static_cast<uint16_t*>(out[q]) : nullptr;
+  a.dt = src.dtype;
+  a.scaled = src.scaled;
+  a.scale = scale;
+  a.variant = variant;
+  a.side = side;
+  if (a.scols % 8 || a.ld % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(preadd_kernel, dim3(stream_grid(a.srows * (a.scols / 8))), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
+  PostAddKArgs a{};
+  for (int q = 0; q < 7; ++q) a.P[q] = in.P[q];
+  a.m = in.m;
+  a.n = in.n;
+  a.variant = in.variant;
+  a.out32 = in.out32;
+  a.ld32 = in.ld32;
+  a.C = static_cast<uint16_t*>(in.C);
+  a.ldc = in.ldc;
+  a.dt = in.dtype;
+  a.alpha = in.alpha;
+  a.beta = in.beta;
+  a.bias = static_cast<const uint16_t*>(in.bias);
+  a.scale_a = in.scale_a;
+  a.scale_b = in.scale_b;
+  if (a.n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(postadd_kernel, dim3(stream_grid(a.m * (a.n / 4))), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ row sum reduction
+namespace {
+__global__ void rowsumsq_reduce_kernel(const float* __restrict__ part, int parts, int M,
+                                       float* __restrict__ ss) {
+  int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= M) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += part[(int64_t)p * M + row];
+  ss[row] = s;
+}
+}  // namespace
+
+hipError_t launch_rowsumsq_reduce(const float* partial, int parts, int M, float* ss,
+                                  hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowsumsq_reduce_kernel, dim3((M + 255) / 256), dim3(256), 0, stream, partial,
+                     parts, M, ss);
+  return hipGetLastError();
+}
+
+}  // namespace fgemm

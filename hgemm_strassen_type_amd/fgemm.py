@@ -1,0 +1,269 @@
+"""ctypes binding of libfgemm (include/fgemm.h) — argument marshalling only.
+
+Every entry point of the C ABI has a function of the same name here.  All compute
+runs in the library's HIP kernels; this module never computes results itself and
+raises when the library is missing.  Torch tensors are accepted for convenience:
+their device pointers, leading dimensions and the current HIP stream are passed
+through unchanged.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfgemm.so")
+
+# enums of fgemm.h
+FGEMM_OK, FGEMM_ERR_INVALID_VALUE, FGEMM_ERR_NOT_SUPPORTED = 0, 1, 2
+FGEMM_ERR_WORKSPACE, FGEMM_ERR_ALLOC, FGEMM_ERR_HIP = 3, 4, 5
+FGEMM_OP_N, FGEMM_OP_T = 0, 1
+FGEMM_F16, FGEMM_BF16 = 0, 1
+FGEMM_EPI_NONE, FGEMM_EPI_BIAS, FGEMM_EPI_ROWSUMSQ, FGEMM_EPI_RMS_SWIGLU = 0, 1, 2, 4
+FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
+FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
+
+# every symbol include/fgemm.h declares
+EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
+           "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
+           "fgemm_gemm_plan", "fgemm_check_args", "fgemm_tile_count", "fgemm_wave_count",
+           "fgemm_status_string")
+
+
+class FgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_name(status)}")
+        self.status = status
+
+
+class fgemm_epilogue_t(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("bias", ctypes.c_void_p),
+                ("rowsumsq", ctypes.c_void_p), ("rms_rowsumsq", ctypes.c_void_p),
+                ("rms_n", ctypes.c_int64), ("rms_eps", ctypes.c_float)]
+
+
+class fgemm_plan_t(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("depth", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("t_pred_us", ctypes.c_double),
+                ("t_classical_pred_us", ctypes.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class fgemm_model_t(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("peak_tflops", ctypes.c_double),
+                ("hbm_gbps", ctypes.c_double), ("eta_mfma", ctypes.c_double),
+                ("eta_hbm", ctypes.c_double), ("launch_us", ctypes.c_double),
+                ("max_workspace_bytes", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfgemm.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m hgemm_strassen_type_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    st = ctypes.c_int
+    epi_p = ctypes.POINTER(fgemm_epilogue_t)
+    plan_p = ctypes.POINTER(fgemm_plan_t)
+    model_p = ctypes.POINTER(fgemm_model_t)
+    sig = {
+        "fgemm_create": (st, [ctypes.POINTER(vp), i32]),
+        "fgemm_destroy": (st, [vp]),
+        "fgemm_set_workspace": (st, [vp, vp, ctypes.c_size_t]),
+        "fgemm_get_model": (st, [vp, model_p]),
+        "fgemm_set_model": (st, [vp, model_p]),
+        "fgemm_select": (st, [vp, i32, i32, i64, i64, i64, i32, epi_p, plan_p]),
+        "fgemm_select_model": (st, [model_p, i32, i32, i64, i64, i64, i32, epi_p, plan_p]),
+        "fgemm_gemm": (st, [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                            i32, epi_p, vp]),
+        "fgemm_gemm_plan": (st, [vp, plan_p, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
+                                 vp, i64, i32, epi_p, vp]),
+        "fgemm_check_args": (st, [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64, i32,
+                                  epi_p]),
+        "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
+        "fgemm_wave_count": (i64, [i64, i64, ctypes.POINTER(ctypes.c_double)]),
+        "fgemm_status_string": (ctypes.c_char_p, [st]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_name(status: int) -> str:
+    return lib().fgemm_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != FGEMM_OK:
+        raise FgemmError(status, where)
+
+
+# ------------------------------------------------------------------ raw ABI calls
+def fgemm_create(device: int = 0) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().fgemm_create(ctypes.byref(h), device), "fgemm_create")
+    return h.value
+
+
+def fgemm_destroy(handle: int):
+    _check(lib().fgemm_destroy(handle), "fgemm_destroy")
+
+
+def fgemm_set_workspace(handle: int, dptr: int, nbytes: int):
+    _check(lib().fgemm_set_workspace(handle, dptr, nbytes), "fgemm_set_workspace")
+
+
+def fgemm_get_model(handle: int) -> fgemm_model_t:
+    m = fgemm_model_t()
+    _check(lib().fgemm_get_model(handle, ctypes.byref(m)), "fgemm_get_model")
+    return m
+
+
+def fgemm_set_model(handle: int, model: fgemm_model_t):
+    _check(lib().fgemm_set_model(handle, ctypes.byref(model)), "fgemm_set_model")
+
+
+def make_epilogue(flags=0, bias=0, rowsumsq=0, rms_rowsumsq=0, rms_n=0, rms_eps=0.0):
+    return fgemm_epilogue_t(flags, bias or None, rowsumsq or None, rms_rowsumsq or None, rms_n,
+                            rms_eps)
+
+
+def fgemm_select(handle, transA, transB, M, N, K, dtype, epilogue=None) -> fgemm_plan_t:
+    p = fgemm_plan_t()
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    _check(lib().fgemm_select(handle, transA, transB, M, N, K, dtype, e, ctypes.byref(p)),
+           "fgemm_select")
+    return p
+
+
+def fgemm_select_model(model, transA, transB, M, N, K, dtype, epilogue=None) -> fgemm_plan_t:
+    p = fgemm_plan_t()
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    _check(lib().fgemm_select_model(ctypes.byref(model), transA, transB, M, N, K, dtype, e,
+                                    ctypes.byref(p)), "fgemm_select_model")
+    return p
+
+
+def fgemm_gemm(handle, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,
+               epilogue=None, stream=0, check=True) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    s = lib().fgemm_gemm(handle, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         dtype, e, stream)
+    if check:
+        _check(s, "fgemm_gemm")
+    return s
+
+
+def fgemm_gemm_plan(handle, plan, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                    dtype, epilogue=None, stream=0, check=True) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    s = lib().fgemm_gemm_plan(handle, ctypes.byref(plan), transA, transB, M, N, K, alpha, A, lda,
+                              B, ldb, beta, C, ldc, dtype, e, stream)
+    if check:
+        _check(s, "fgemm_gemm_plan")
+    return s
+
+
+def fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype,
+                     epilogue=None) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    return lib().fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype, e)
+
+
+def fgemm_tile_count(M, N, tile_m, tile_n) -> int:
+    return lib().fgemm_tile_count(M, N, tile_m, tile_n)
+
+
+def fgemm_wave_count(tiles, units):
+    tail = ctypes.c_double()
+    w = lib().fgemm_wave_count(tiles, units, ctypes.byref(tail))
+    return w, tail.value
+
+
+# ------------------------------------------------------------ torch conveniences
+def torch_dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FGEMM_BF16
+    if t.dtype == torch.float16:
+        return FGEMM_F16
+    raise TypeError(f"fgemm takes fp16 or bf16 tensors, not {t.dtype}")
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("operands are 2-D row-major tensors (unit column stride)")
+    return t.stride(0)
+
+
+class Handle:
+    """Owns an fgemm handle on one device."""
+
+    def __init__(self, device: int = 0):
+        self.h = fgemm_create(device)
+
+    def close(self):
+        if self.h:
+            fgemm_destroy(self.h)
+            self.h = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def gemm(self, A, B, C, *, transA=False, transB=False, alpha=1.0, beta=0.0, epilogue=None,
+             plan=None, stream=None):
+        """C = alpha*op(A)*op(B) + beta*C on torch device tensors (C written in place)."""
+        ta = FGEMM_OP_T if transA else FGEMM_OP_N
+        tb = FGEMM_OP_T if transB else FGEMM_OP_N
+        M = A.shape[1] if transA else A.shape[0]
+        K = A.shape[0] if transA else A.shape[1]
+        N = C.shape[1]
+        dt = torch_dtype_code(C)
+        s = current_stream() if stream is None else stream
+        args = (ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                float(beta), C.data_ptr(), _ld(C), dt, epilogue, s)
+        if plan is None:
+            return fgemm_gemm(self.h, *args)
+        return fgemm_gemm_plan(self.h, plan, *args)
+
+    def select(self, M, N, K, *, transA=False, transB=False, dtype=FGEMM_BF16, epilogue=None):
+        return fgemm_select(self.h, FGEMM_OP_T if transA else FGEMM_OP_N,
+                            FGEMM_OP_T if transB else FGEMM_OP_N, M, N, K, dtype, epilogue)
+
+    def model(self) -> fgemm_model_t:
+        return fgemm_get_model(self.h)
+
+
+def strassen_plan(depth: int, variant: int, tile: int = 0) -> fgemm_plan_t:
+    p = fgemm_plan_t()
+    p.path, p.depth, p.variant = FGEMM_PATH_STRASSEN, depth, variant
+    p.tile_m = p.tile_n = tile
+    return p
+
+
+def classical_plan(tile_m: int = 0, tile_n: int = 0) -> fgemm_plan_t:
+    p = fgemm_plan_t()
+    p.path, p.tile_m, p.tile_n = FGEMM_PATH_CLASSICAL, tile_m, tile_n
+    return p

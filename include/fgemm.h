@@ -1,0 +1,191 @@
+/*
+ * fgemm.h — C ABI of libfgemm: half-precision GEMM for AMD MI355X (gfx950).
+ *
+ *   C = alpha * op(A) * op(B) + beta * C      fp16 or bf16 in, fp32 accumulate
+ *
+ * The operation is the HGEMM of the CUDA-L2 abstract (chatpaper.ai page, NN and TN
+ * layouts); 16-bit inputs with wider accumulation follow CS336 Lecture 05 notes,
+ * Page 26.  Two paths compute it:
+ *   - classical: a tiled MFMA GEMM whose epilogue (scale, beta*C, bias, row
+ *     statistics, activation) runs before the store (PingPong GEMM note on
+ *     tilnote.io: mainloop + epilogue; CODA section: RMSNorm statistics in the
+ *     first GEMM's epilogue, scaling and SwiGLU in the second's);
+ *   - Strassen/Winograd: one or two levels of the 2x2 block recursion with seven
+ *     sub-products per level (FalconGEMM summary on euno.news, Methodology 1, 3).
+ * An analytic model picks the path per shape from compute throughput, memory
+ * bandwidth and the per-level addition traffic (FalconGEMM summary, Methodology 4
+ * and 5; roofline of CS336 Lecture 05 notes, Page 21; tile and wave quantization,
+ * Pages 43 and 48).
+ *
+ * Conventions for every entry point:
+ *   - Storage is row-major.  op = N: A is M x K (lda >= K); op = T: A is stored
+ *     K x M (lda >= M).  op = N: B is K x Nb (ldb >= Nb); op = T: B is stored
+ *     Nb x K (ldb >= K).  Nb = N, or 2*N with FGEMM_EPI_RMS_SWIGLU.  C is M x N
+ *     with ldc >= N.  Leading dimensions are in elements.
+ *   - A, B, C, the epilogue vectors and the workspace are DEVICE pointers owned by
+ *     the caller; the library never frees them.  alpha and beta are host floats.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and the
+ *     call returns after the enqueue; nothing is synchronised.
+ *   - beta == 0: C is never read (NaN or Inf in C do not propagate).
+ *   - M == 0 or N == 0: nothing is done.  K == 0: C = beta*C (+ epilogue).
+ *   - C must not overlap A or B.  C may be read and written in place (beta*C).
+ *   - Arguments are validated before any device work; errors are returned
+ *     synchronously and nothing is enqueued.  No C++ exception crosses the ABI.
+ *   - A handle is not thread safe: use one per host thread.  Calls that overlap
+ *     on one handle's workspace must be on one stream.
+ *   - Fast path: 16-byte aligned pointers and leading dimensions that are
+ *     multiples of 8; anything else runs a correct element-wise path.
+ */
+#ifndef FGEMM_H
+#define FGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fgemm_handle_s* fgemm_handle_t;
+
+typedef enum {
+    FGEMM_OK = 0,
+    FGEMM_ERR_INVALID_VALUE = 1, /* a bad size, leading dimension, pointer or flag   */
+    FGEMM_ERR_NOT_SUPPORTED = 2, /* a valid request this library does not implement  */
+    FGEMM_ERR_WORKSPACE = 3,     /* a forced plan needs more workspace than is set   */
+    FGEMM_ERR_ALLOC = 4,         /* a device allocation failed                       */
+    FGEMM_ERR_HIP = 5            /* a HIP runtime or launch error                    */
+} fgemm_status_t;
+
+typedef enum { FGEMM_OP_N = 0, FGEMM_OP_T = 1 } fgemm_op_t;
+
+/* A, B and C share the type; accumulation is fp32. */
+typedef enum { FGEMM_F16 = 0, FGEMM_BF16 = 1 } fgemm_dtype_t;
+
+/* Epilogue flags (tilnote.io PingPong GEMM note: GEMM = mainloop + epilogue; CODA
+ * section: norm statistics in the first GEMM's epilogue, scaling and SwiGLU in the
+ * second's).  Per output element, in this order:
+ *   D = alpha*acc + beta*C + bias[j]             (BIAS adds bias[j])
+ *   C[i][j] = RNE16(D)
+ *   ROWSUMSQ: rowsumsq[i] = sum_j C[i][j]^2 of the rounded, written row (fp32).
+ * RMS_SWIGLU (alone): op(B) has 2N columns, gate = columns [0, N), up = [N, 2N):
+ *   r_i = 1/sqrt(rms_rowsumsq[i]/rms_n + rms_eps)
+ *   g = r_i*alpha*acc_gate, u = r_i*alpha*acc_up,
+ *   C[i][j] = RNE16(silu(g)*u + beta*C[i][j]),  silu(x) = x/(1+exp(-x)). */
+enum {
+    FGEMM_EPI_NONE = 0,
+    FGEMM_EPI_BIAS = 1,
+    FGEMM_EPI_ROWSUMSQ = 2,
+    FGEMM_EPI_RMS_SWIGLU = 4
+};
+
+typedef struct {
+    uint32_t flags;             /* FGEMM_EPI_* bits                                  */
+    const void* bias;           /* BIAS: device [N], same 16-bit type as C           */
+    float* rowsumsq;            /* ROWSUMSQ: device [M] fp32 output                  */
+    const float* rms_rowsumsq;  /* RMS_SWIGLU: device [M] fp32 input                 */
+    int64_t rms_n;              /* RMS_SWIGLU: width the statistics were taken over  */
+    float rms_eps;              /* RMS_SWIGLU: epsilon inside the square root        */
+} fgemm_epilogue_t;
+
+typedef enum {
+    FGEMM_PATH_CLASSICAL = 0,
+    FGEMM_PATH_STRASSEN = 1
+} fgemm_path_t;
+
+/* Strassen (1969): 7 products, 18 block additions.
+ * Winograd form: 7 products, 15 block additions (8 pre-add outputs instead of 10). */
+typedef enum { FGEMM_VARIANT_S69 = 0, FGEMM_VARIANT_WINOGRAD = 1 } fgemm_variant_t;
+
+/* A plan: what fgemm_select chose (or what a caller forces through fgemm_gemm_plan). */
+typedef struct {
+    int32_t path;               /* fgemm_path_t                                       */
+    int32_t depth;              /* Strassen recursion depth, 1 or 2 (0 = classical)  */
+    int32_t variant;            /* fgemm_variant_t                                    */
+    int32_t tile_m, tile_n, tile_k; /* macro-tile of the classical kernel (products) */
+    int32_t split_k;            /* K-splits of the classical kernel (1 = none)        */
+    size_t workspace_bytes;     /* device workspace the plan needs                    */
+    double t_pred_us;           /* model time of this plan                            */
+    double t_classical_pred_us; /* model time of the best classical plan              */
+} fgemm_plan_t;
+
+/* Constants of the analytic model.  fgemm_create fills them from the device and
+ * the built-in calibration; fgemm_set_model replaces them. */
+typedef struct {
+    int32_t compute_units;      /* CUs that run workgroups                            */
+    double peak_tflops;         /* dense 16-bit MFMA peak, TFLOP/s                    */
+    double hbm_gbps;            /* HBM bandwidth, GB/s                                */
+    double eta_mfma;            /* fraction of MFMA peak a full tile wave reaches     */
+    double eta_hbm;             /* fraction of HBM bandwidth streaming kernels reach  */
+    double launch_us;           /* per-kernel launch and drain cost, microseconds     */
+    double max_workspace_bytes; /* AUTO never plans above this workspace              */
+} fgemm_model_t;
+
+/* Handle: reads the device's CU count and architecture; fails with
+ * FGEMM_ERR_NOT_SUPPORTED on anything but gfx950 and FGEMM_ERR_HIP without a device. */
+fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device);
+fgemm_status_t fgemm_destroy(fgemm_handle_t handle);
+
+/* Caller-owned device workspace (for example a torch tensor).  Without one the
+ * handle allocates what a plan needs with hipMalloc and keeps it until destroyed. */
+fgemm_status_t fgemm_set_workspace(fgemm_handle_t handle, void* dptr, size_t bytes);
+
+fgemm_status_t fgemm_get_model(fgemm_handle_t handle, fgemm_model_t* model);
+fgemm_status_t fgemm_set_model(fgemm_handle_t handle, const fgemm_model_t* model);
+
+/* The model's pick for a shape: the plan of least predicted time among the
+ * classical kernel and Strassen/Winograd at depth 1 and 2, subject to the
+ * accuracy, divisibility, epilogue and workspace guards.  Host only; results
+ * are cached per shape in the handle. */
+fgemm_status_t fgemm_select(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
+                            int64_t M, int64_t N, int64_t K, fgemm_dtype_t dtype,
+                            const fgemm_epilogue_t* epilogue, fgemm_plan_t* plan);
+
+/* The same decision as a pure function of an explicit model (no handle, no GPU). */
+fgemm_status_t fgemm_select_model(const fgemm_model_t* model, fgemm_op_t transA,
+                                  fgemm_op_t transB, int64_t M, int64_t N, int64_t K,
+                                  fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                                  fgemm_plan_t* plan);
+
+/* C = alpha*op(A)*op(B) + beta*C with the epilogue (NULL = none), on the plan
+ * fgemm_select picks. */
+fgemm_status_t fgemm_gemm(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
+                          int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                          int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                          int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                          void* stream);
+
+/* The same on an explicit plan (path, depth, variant).  Tile fields of 0 let the
+ * library choose.  Strassen needs M, N and K divisible by 8*2^depth, aligned
+ * operands and an epilogue of NONE or BIAS, else FGEMM_ERR_NOT_SUPPORTED; too
+ * small a caller workspace gives FGEMM_ERR_WORKSPACE. */
+fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
+                               fgemm_op_t transA, fgemm_op_t transB, int64_t M, int64_t N,
+                               int64_t K, float alpha, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                               fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                               void* stream);
+
+/* Argument validation alone (pure; no handle, no device): the status fgemm_gemm
+ * would return before enqueuing anything. */
+fgemm_status_t fgemm_check_args(fgemm_op_t transA, fgemm_op_t transB, int64_t M, int64_t N,
+                                int64_t K, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, float beta, const void* C, int64_t ldc,
+                                fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue);
+
+/* Tile quantization: ceil(M/tile_m) * ceil(N/tile_n) output tiles (CS336 Lecture
+ * 05 notes, Page 43: 256/128 gives 2 tiles per dimension, 257/128 gives 3). */
+int64_t fgemm_tile_count(int64_t M, int64_t N, int64_t tile_m, int64_t tile_n);
+
+/* Wave quantization: waves = ceil(tiles/units); *tail_fraction = share of the
+ * units busy in the last wave (CS336 Lecture 05 notes, Page 48: 98 tiles on 108
+ * units is one wave; 120 tiles is two, the second 12/108 busy). */
+int64_t fgemm_wave_count(int64_t tiles, int64_t units, double* tail_fraction);
+
+const char* fgemm_status_string(fgemm_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGEMM_H */

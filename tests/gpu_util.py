@@ -1,0 +1,80 @@
+"""Helpers for the GPU parity tests: move 16-bit bit patterns to and from the
+device, call the library through its C ABI, and compare with the oracle."""
+import sys
+
+import numpy as np
+
+import oracle
+from hgemm_strassen_type_amd import fgemm
+from hgemm_strassen_type_amd import inputs
+
+F16, BF16 = inputs.F16, inputs.BF16
+
+CLASSICAL_TOL = 1e-3
+STRASSEN_TOL = 5e-3
+STATS_TOL = 1e-3
+
+
+def say(msg):
+    """Name the case before the GPU work starts (flushed, so it survives a crash)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.bfloat16 if dtype == BF16 else torch.float16
+
+
+def to_dev(bits, dtype, pad_cols=0):
+    """uint16 matrix -> device tensor; pad_cols > 0 gives a larger leading dimension."""
+    import torch
+    bits = np.ascontiguousarray(bits)
+    if pad_cols:
+        padded = np.full((bits.shape[0], bits.shape[1] + pad_cols), 0x7FC0, dtype=np.uint16)
+        padded[:, :bits.shape[1]] = bits
+        t = torch.from_numpy(padded.view(np.int16)).view(torch_dtype(dtype)).cuda()
+        return t[:, :bits.shape[1]]
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch_dtype(dtype)).cuda()
+
+
+def from_dev(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def empty_out(M, N, dtype, fill=0x7FC0):
+    """Output tensor pre-filled with NaN bits so unwritten elements are caught."""
+    import torch
+    return to_dev(np.full((M, N), fill, dtype=np.uint16), dtype)
+
+
+def rel_err(gpu_bits, ref_Q, dtype):
+    return oracle.rel_fro(oracle.decode(gpu_bits, dtype), oracle.decode(ref_Q, dtype))
+
+
+_handle = None
+
+
+def handle():
+    global _handle
+    if _handle is None:
+        _handle = fgemm.Handle(0)
+    return _handle
+
+
+def run(A_bits, B_bits, dtype, *, transA=False, transB=False, alpha=1.0, beta=0.0, C_bits=None,
+        M=None, N=None, plan=None, epilogue=None, pad=0):
+    """Run one GEMM on the device; returns the output bits."""
+    import torch
+    A = to_dev(A_bits, dtype, pad)
+    B = to_dev(B_bits, dtype, pad)
+    if M is None:
+        M = A_bits.shape[1] if transA else A_bits.shape[0]
+    if N is None:
+        N = B_bits.shape[0] if transB else B_bits.shape[1]
+    C = to_dev(C_bits, dtype, pad) if C_bits is not None else empty_out(M, N, dtype)
+    handle().gemm(A, B, C, transA=transA, transB=transB, alpha=alpha, beta=beta, plan=plan,
+                  epilogue=epilogue)
+    torch.cuda.synchronize()
+    return from_dev(C)

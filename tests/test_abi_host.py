@@ -1,0 +1,189 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol,
+argument validation, the quantization helpers against the worked examples of the
+CS336 Lecture 05 notes (Pages 43 and 48), and the decision model's properties."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hgemm_strassen_type_amd import fgemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+N_, T_ = fgemm.FGEMM_OP_N, fgemm.FGEMM_OP_T
+BF, HF = fgemm.FGEMM_BF16, fgemm.FGEMM_F16
+OK, INVAL, NOTSUP = fgemm.FGEMM_OK, fgemm.FGEMM_ERR_INVALID_VALUE, fgemm.FGEMM_ERR_NOT_SUPPORTED
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fgemm.lib()
+    names = declared_functions()
+    assert set(names) == set(fgemm.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert fgemm.status_name(OK) == "FGEMM_OK"
+    assert fgemm.status_name(fgemm.FGEMM_ERR_WORKSPACE) == "FGEMM_ERR_WORKSPACE"
+    assert fgemm.status_name(77) == "FGEMM_UNKNOWN_STATUS"
+
+
+# ---------------------------------------------------------------- quantization
+def test_tile_quantization_page_example():
+    # 256 / 128 -> 2 tiles per dimension, 257 / 128 -> 3
+    assert fgemm.fgemm_tile_count(256, 256, 128, 128) == 4
+    assert fgemm.fgemm_tile_count(257, 257, 128, 128) == 9
+    assert fgemm.fgemm_tile_count(256, 1, 128, 128) == 2
+    assert fgemm.fgemm_tile_count(257, 1, 128, 128) == 3
+
+
+def test_wave_quantization_page_example():
+    # N = 1792 with 256x128 tiles: 7 x 14 = 98 tiles, one wave on 108 units
+    tiles = fgemm.fgemm_tile_count(1792, 1792, 256, 128)
+    assert tiles == 98
+    waves, tail = fgemm.fgemm_wave_count(tiles, 108)
+    assert waves == 1 and tail == pytest.approx(98 / 108)
+    # N = 1793: 8 x 15 = 120 tiles, two waves, the second 12/108 busy
+    tiles = fgemm.fgemm_tile_count(1793, 1793, 256, 128)
+    assert tiles == 120
+    waves, tail = fgemm.fgemm_wave_count(tiles, 108)
+    assert waves == 2 and tail == pytest.approx(12 / 108)
+    assert round(tail * 100, 1) == 11.1
+
+
+def test_quantization_rejects_bad_input():
+    assert fgemm.fgemm_tile_count(-1, 4, 1, 1) == -1
+    assert fgemm.fgemm_tile_count(4, 4, 0, 1) == -1
+    assert fgemm.fgemm_wave_count(4, 0)[0] == -1
+
+
+# ------------------------------------------------------------ argument checks
+P = 0x10000  # a fake non-null device address (never dereferenced by the check)
+
+
+def chk(ta=N_, tb=N_, M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, beta=0.0, C=P, ldc=None,
+        dtype=BF, epi=None):
+    if lda is None:
+        lda = K if ta == N_ else M
+    if ldb is None:
+        nb = 2 * N if epi is not None and epi.flags & fgemm.FGEMM_EPI_RMS_SWIGLU else N
+        ldb = nb if tb == N_ else K
+    if ldc is None:
+        ldc = N
+    return fgemm.fgemm_check_args(ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype, epi)
+
+
+def test_check_args_accepts_valid_calls():
+    assert chk() == OK
+    for ta in (N_, T_):
+        for tb in (N_, T_):
+            assert chk(ta=ta, tb=tb, M=33, N=17, K=9) == OK
+    assert chk(M=0, A=None, B=None, C=None) == OK          # nothing to do
+    assert chk(K=0, A=None, B=None, lda=1) == OK           # C = beta*C
+    assert chk(dtype=HF) == OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(lda=63), dict(ldb=63), dict(ldc=63),
+    dict(ta=2), dict(tb=-1), dict(dtype=3),
+    dict(A=None), dict(B=None), dict(C=None),
+    dict(ta=T_, lda=63),                                     # A stored K x M: lda >= M
+    dict(tb=T_, ldb=63),                                     # B stored N x K: ldb >= K
+])
+def test_check_args_rejects(kw):
+    assert chk(**kw) == INVAL
+
+
+def test_check_args_epilogues():
+    E = fgemm.make_epilogue
+    assert chk(epi=E(fgemm.FGEMM_EPI_BIAS, bias=P)) == OK
+    assert chk(epi=E(fgemm.FGEMM_EPI_BIAS)) == INVAL                      # no bias pointer
+    assert chk(epi=E(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)) == OK
+    assert chk(epi=E(fgemm.FGEMM_EPI_ROWSUMSQ)) == INVAL
+    sw = E(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096, rms_eps=1e-6)
+    assert chk(epi=sw) == OK
+    assert chk(epi=sw, ldb=64) == INVAL                                    # B needs 2N columns
+    assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=0)) == INVAL
+    assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_n=4096)) == INVAL     # no statistics
+    assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU | fgemm.FGEMM_EPI_BIAS, bias=P, rms_rowsumsq=P,
+                     rms_n=4096)) == NOTSUP
+    assert chk(epi=E(64)) == INVAL                                         # unknown flag
+
+
+# ---------------------------------------------------------------- decision model
+def mi355x_model(**over):
+    m = fgemm.fgemm_model_t()
+    m.compute_units, m.peak_tflops, m.hbm_gbps = 256, 256 * 4096 * 2.4e9 / 1e12, 8000.0
+    m.eta_mfma, m.eta_hbm, m.launch_us, m.max_workspace_bytes = 0.7, 0.8, 4.0, 16 * 2.0 ** 30
+    for k, v in over.items():
+        setattr(m, k, v)
+    return m
+
+
+def select(M, N, K, model=None, epi=None, dtype=BF):
+    return fgemm.fgemm_select_model(model or mi355x_model(), N_, N_, M, N, K, dtype, epi)
+
+
+def test_select_never_picks_strassen_where_it_cannot_run():
+    for shape in [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (8191, 8192, 8192),
+                  (256, 256, 256), (8192, 8192, 8200)]:
+        assert select(*shape).path == fgemm.FGEMM_PATH_CLASSICAL, shape
+    # epilogues other than bias are classical only
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
+    assert select(32768, 32768, 32768, epi=epi).path == fgemm.FGEMM_PATH_CLASSICAL
+
+
+def test_select_predicted_time_is_monotone():
+    prev = 0.0
+    for n in (512, 1024, 2048, 4096, 8192, 16384):
+        t = select(n, n, n).t_classical_pred_us
+        assert t > prev
+        prev = t
+    assert select(8192, 8192, 8192).t_classical_pred_us < select(8192, 8192, 16384).t_classical_pred_us
+
+
+def test_select_roofline_bounds():
+    md = mi355x_model()
+    n = 8192
+    p = select(n, n, n, md)
+    flops = 2.0 * n ** 3
+    # never faster than the MFMA peak (roofline: min of peak and intensity x bandwidth)
+    assert p.t_classical_pred_us * 1e-6 >= flops / (md.peak_tflops * 1e12)
+    # decode: bandwidth term dominates, time >= weight bytes / bandwidth
+    p = select(1, 14336, 4096, md)
+    assert p.t_classical_pred_us * 1e-6 >= 4096 * 14336 * 2 / (md.hbm_gbps * 1e9)
+
+
+def test_select_takes_strassen_when_compute_is_slow_relative_to_memory():
+    # A machine with abundant bandwidth: the 7/8 multiply saving wins at large sizes.
+    fast_mem = mi355x_model(hbm_gbps=80000.0)
+    p = select(16384, 16384, 16384, fast_mem)
+    assert p.path == fgemm.FGEMM_PATH_STRASSEN
+    assert p.t_pred_us < p.t_classical_pred_us
+    assert p.workspace_bytes > 0
+    # Starved bandwidth: the addition traffic makes Strassen lose.
+    slow_mem = mi355x_model(hbm_gbps=800.0)
+    assert select(16384, 16384, 16384, slow_mem).path == fgemm.FGEMM_PATH_CLASSICAL
+    # A workspace cap below the need keeps it classical.
+    capped = mi355x_model(hbm_gbps=80000.0, max_workspace_bytes=1e6)
+    assert select(16384, 16384, 16384, capped).path == fgemm.FGEMM_PATH_CLASSICAL
+
+
+def test_select_tile_choice_follows_wave_quantization():
+    # 256 output tiles of 256x256 fill exactly one wave on 256 units
+    p = select(4096, 4096, 4096)
+    assert (p.tile_m, p.tile_n) == (256, 256)
+    # a single 256x256 tile would leave 255 units idle: smaller tiles win
+    p = select(256, 256, 4096)
+    assert p.tile_m * p.tile_n < 256 * 256
+    # skinny M uses a skinny tile
+    assert select(16, 14336, 4096).tile_m <= 64

@@ -1,0 +1,166 @@
+"""GPU parity of the classical MFMA path against the CPU oracle, through the C ABI.
+
+Exact cases use small-integer inputs whose products and sums are exact in fp32
+and in the 16-bit output, so the GPU must match the oracle bit for bit.  Random
+cases are held to the normwise bound ||C - Q(D)||_F / ||Q(D)||_F <= 1e-3."""
+import numpy as np
+import pytest
+
+import oracle
+from hgemm_strassen_type_amd import fgemm
+from hgemm_strassen_type_amd import inputs
+from gpu_util import (BF16, CLASSICAL_TOL, F16, from_dev, handle, rel_err, run, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [(False, False), (True, False), (False, True), (True, True)]
+TILES = [(256, 256), (128, 128), (64, 128), (32, 128)]
+
+
+def stored(M, N, K, transA, transB, A_lo, seedA, seedB, dtype, kind="int"):
+    shapeA = (K, M) if transA else (M, K)
+    shapeB = (N, K) if transB else (K, N)
+    if kind == "int":
+        lo = -1 if dtype == BF16 else -2
+        return (inputs.integers(shapeA, seedA, dtype, lo, -lo),
+                inputs.integers(shapeB, seedB, dtype, lo, -lo))
+    return inputs.normal(shapeA, seedA, dtype), inputs.normal(shapeB, seedB, dtype)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("transA,transB", LAYOUTS)
+def test_exact_integer_products(tile, dtype, transA, transB):
+    # |C| <= K*max|a|*max|b| = 256 (bf16) / 1024 (fp16): exact in the output type
+    for (M, N, K) in [(256, 256, 256), (300, 200, 130), (1, 264, 64), (67, 9, 1)]:
+        say(f"exact tile={tile} dtype={dtype} tA={transA} tB={transB} M={M} N={N} K={K}")
+        A, B = stored(M, N, K, transA, transB, 0, 11 + M, 12 + N, dtype)
+        _, Q, _ = oracle.gemm(A, B, transA=transA, transB=transB, dtype=dtype)
+        got = run(A, B, dtype, transA=transA, transB=transB, M=M, N=N,
+                  plan=fgemm.classical_plan(*tile))
+        assert np.array_equal(got, Q), (M, N, K)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("transA,transB", LAYOUTS)
+def test_random_ragged_with_alpha_beta(dtype, transA, transB):
+    M, N, K = 600, 520, 328   # several 256 tiles, ragged in every dimension
+    say(f"random dtype={dtype} tA={transA} tB={transB}")
+    A, B = stored(M, N, K, transA, transB, 0, 21, 22, dtype, kind="normal")
+    C = inputs.normal((M, N), 23, dtype)
+    _, Q, _ = oracle.gemm(A, B, transA=transA, transB=transB, alpha=0.75, beta=0.5, C=C,
+                          dtype=dtype)
+    for tile in TILES:
+        got = run(A, B, dtype, transA=transA, transB=transB, alpha=0.75, beta=0.5, C_bits=C,
+                  plan=fgemm.classical_plan(*tile))
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, tile
+    got = run(A, B, dtype, transA=transA, transB=transB, alpha=0.75, beta=0.5, C_bits=C)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+@pytest.mark.parametrize("transA,transB", LAYOUTS)
+def test_unaligned_leading_dimensions(transA, transB):
+    # leading dimensions not a multiple of 8 take the element-wise path
+    dtype = BF16
+    M, N, K = 133, 77, 91
+    say(f"unaligned tA={transA} tB={transB}")
+    A, B = stored(M, N, K, transA, transB, 0, 31, 32, dtype, kind="normal")
+    C = inputs.normal((M, N), 33, dtype)
+    _, Q, _ = oracle.gemm(A, B, transA=transA, transB=transB, beta=-1.0, C=C, dtype=dtype)
+    got = run(A, B, dtype, transA=transA, transB=transB, beta=-1.0, C_bits=C, pad=3)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+def test_k_zero_gives_beta_c():
+    dtype = BF16
+    M, N = 70, 90
+    say("K=0")
+    C = inputs.normal((M, N), 41, dtype)
+    import torch
+    Cd = to_dev(C, dtype)
+    A = torch.empty((M, 1), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+    st = fgemm.fgemm_gemm(handle().h, 0, 0, M, N, 0, 1.0, A.data_ptr(), 1, B.data_ptr(), N, 0.5,
+                          Cd.data_ptr(), N, fgemm.FGEMM_BF16, None, fgemm.current_stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = oracle.encode(0.5 * oracle.decode(C, dtype), dtype)
+    assert np.array_equal(from_dev(Cd), ref)
+
+
+def test_beta_zero_never_reads_c_and_alpha_zero():
+    dtype = F16
+    M, N, K = 96, 80, 64
+    say("beta=0 with NaN C; alpha=0")
+    A, B = stored(M, N, K, False, False, 0, 51, 52, dtype, kind="normal")
+    got = run(A, B, dtype, C_bits=np.full((M, N), 0x7E00, dtype=np.uint16))
+    assert np.isfinite(oracle.decode(got, dtype)).all()
+    C = inputs.normal((M, N), 53, dtype)
+    got = run(A, B, dtype, alpha=0.0, beta=2.0, C_bits=C)
+    assert np.array_equal(got, oracle.encode(2.0 * oracle.decode(C, dtype), dtype))
+
+
+def test_identity_and_transpose_invariants():
+    dtype = BF16
+    say("A*I = A and (AB)^T = B^T A^T")
+    A = inputs.normal((200, 136), 61, dtype)
+    I = inputs.to_bits(np.eye(136), dtype)
+    assert np.array_equal(run(A, I, dtype), A)
+    B = inputs.integers((136, 72), 62, dtype, -1, 1)
+    Ai = inputs.integers((200, 136), 63, dtype, -1, 1)
+    AB = run(Ai, B, dtype)
+    BtAt = run(B, Ai, dtype, transA=True, transB=True, M=72, N=200)
+    assert np.array_equal(BtAt, AB.T)
+
+
+def test_repeatable_bitwise():
+    dtype = BF16
+    say("repeatability 1024^3")
+    A = inputs.normal((1024, 1024), 71, dtype)
+    B = inputs.normal((1024, 1024), 72, dtype)
+    r1 = run(A, B, dtype)
+    r2 = run(A, B, dtype)
+    assert np.array_equal(r1, r2)
+
+
+# ------------------------------------------------------------ workload sizes
+def test_fp16_256_cube():
+    """fp16 NN row-major 256^3, U[-1,1] seeds 1001/1002, alpha=1 beta=0."""
+    dtype = F16
+    say("fp16 256^3")
+    A = inputs.uniform((256, 256), 1001, dtype)
+    B = inputs.uniform((256, 256), 1002, dtype)
+    _, Q, _ = oracle.gemm(A, B, dtype=dtype)
+    got = run(A, B, dtype)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+@pytest.mark.parametrize("transA", [False, True])
+def test_bf16_square_beta_half(n, transA):
+    """bf16 M=N=K in {4096, 8192}, NN and TN, N(0,1), alpha=1, beta=0.5, C N(0,1):
+    full-size run with the library's own plan, oracle on sampled rows."""
+    dtype = BF16
+    say(f"bf16 square n={n} transA={transA}")
+    A = inputs.normal((n, n), 2001, dtype)
+    B = inputs.normal((n, n), 2002, dtype)
+    C = inputs.normal((n, n), 2003, dtype)
+    got = run(A, B, dtype, transA=transA, beta=0.5, C_bits=C)
+    rows = inputs.sample_rows(n, 48, 7)
+    _, Q, _ = oracle.gemm(A, B, transA=transA, beta=0.5, C=C, dtype=dtype, rows=rows)
+    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+
+
+@pytest.mark.parametrize("M,N", [(16384, 4096), (16384, 14336), (1, 14336), (16, 14336),
+                                 (64, 14336)])
+def test_llm_shapes(M, N):
+    """bf16 NN, activations N(0,1), weights N(0,0.02), K=4096."""
+    dtype = BF16
+    K = 4096
+    say(f"llm M={M} N={N}")
+    X = inputs.normal((M, K), 3001, dtype)
+    W = inputs.normal((K, N), 3002, dtype, std=0.02)
+    got = run(X, W, dtype)
+    rows = inputs.sample_rows(M, 32, 8)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype, rows=rows)
+    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
