@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the half-precision GEMM path on one MI355X.
+
+Headline: effective TFLOP/s (2MNK/t) of bf16 C = alpha*A*B + beta*C with
+M = N = K = 8192, NN row-major, A, B, C ~ N(0,1), alpha = 1, beta = 0.5, fp32
+accumulate, through fgemm_gemm (the decision model picks the plan).  One step is
+one fgemm_gemm call on resident device inputs; warmup steps run first, then
+exactly --steps steps are timed between device synchronisations.
+
+The same JSON line carries
+  roofline      the dominant kernel (the MFMA GEMM) against the dense bf16 MFMA
+                peak: algorithmic FLOPs per launch / average launch time measured
+                here with HIP events on the launch stream; `traffic` is the HBM
+                bytes per launch from the committed rocprofv3 counter summary, or
+                null when the kernel sources changed after those counters;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+                (a seeded subset of output rows), with the threads it used;
+  workloads     the other shapes: 4096^3 and TN layouts, LLM projection/FFN and
+                decode shapes (decode as HBM GB/s), the fused two-GEMM chain, and
+                Strassen/Winograd vs classical at 16384^3 and 32768x8192x8192 with
+                the model's pick and its regret against the measured best.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_bf16_8192_traffic.json")
+KERNEL_SOURCES = ["hgemm_strassen_type_amd/csrc/gemm_mfma.h",
+                  "hgemm_strassen_type_amd/csrc/gemm_inst.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only-main", action="store_true",
+                    help="time the headline workload only (for profiler runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the GEMM path is a "
+              "single-device kernel; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hgemm_strassen_type_amd import fgemm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    h = fgemm.Handle(0)
+    timer = Timer(torch)
+    gen = torch.Generator(device=dev)
+
+    def normal(shape, seed, std=1.0, dtype=torch.bfloat16):
+        gen.manual_seed(seed)
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(dtype)
+
+    def uniform(shape, seed, dtype):
+        gen.manual_seed(seed)
+        return (torch.rand(shape, generator=gen, device=dev, dtype=torch.float32) * 2 - 1).to(dtype)
+
+    # ---------------------------------------------------------------- headline
+    n = 8192
+    A = normal((n, n), 2001)
+    B = normal((n, n), 2002)
+    C = normal((n, n), 2003)
+    plan = h.select(n, n, n)
+    log(f"headline bf16 {n}^3 NN beta=0.5, plan {plan.as_dict()}")
+    ms = timer.time(lambda: h.gemm(A, B, C, beta=0.5), args.steps, args.warmup)
+    flops = 2.0 * n * n * n
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"headline: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+
+    workloads = {}
+    if not args.only_main:
+        workloads = run_workloads(torch, h, fgemm, timer, normal, uniform, args)
+    del A, B, C
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": "effective TFLOP/s (2MNK/t) + % MFMA peak, bf16 GEMM",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 GEMM NN row-major M=N=K=8192, A,B,C ~ N(0,1), alpha=1, "
+                               "beta=0.5, fp32 accumulate, bf16 output",
+                   "M": n, "N": n, "K": n, "layout": "NN", "alpha": 1.0, "beta": 0.5,
+                   "plan": {k: v for k, v in plan.as_dict().items()
+                            if k in ("path", "depth", "variant", "tile_m", "tile_n")}},
+        "mfma_peak_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
+    W = {}
+    reps = max(5, args.steps // 5)
+
+    def gemm_case(name, M, N, K, transA=False, beta=0.0, dtype=torch.bfloat16, std_b=1.0,
+                  plan=None, seeds=(1, 2, 3), gen_fn=None, bytes_alg=None):
+        gen_fn = gen_fn or (lambda s, seed, std: normal(s, seed, std, dtype))
+        A = gen_fn((K, M) if transA else (M, K), seeds[0], 1.0)
+        B = gen_fn((K, N), seeds[1], std_b)
+        C = gen_fn((M, N), seeds[2], 1.0)
+        ms = timer.time(lambda: h.gemm(A, B, C, transA=transA, beta=beta, plan=plan), reps, 3)
+        r = {"ms": round(ms, 5), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+        if bytes_alg:
+            r["hbm_gbps"] = round(bytes_alg / (ms * 1e-3) / 1e9, 1)
+            r["hbm_frac"] = round(r["hbm_gbps"] / HBM_PEAK_GBPS, 4)
+        r["mfma_frac"] = round(r["tflops"] / MFMA_PEAK_TFLOPS, 4)
+        W[name] = r
+        log(f"{name}: {r}")
+        del A, B, C
+        return ms
+
+    gemm_case("bf16_4096_NN_beta0.5", 4096, 4096, 4096, beta=0.5, seeds=(2001, 2002, 2003))
+    gemm_case("bf16_4096_TN_beta0.5", 4096, 4096, 4096, transA=True, beta=0.5,
+              seeds=(2001, 2002, 2003))
+    gemm_case("bf16_8192_TN_beta0.5", 8192, 8192, 8192, transA=True, beta=0.5,
+              seeds=(2001, 2002, 2003))
+    for N in (4096, 14336):
+        gemm_case(f"bf16_prefill_16384x{N}x4096", 16384, N, 4096, std_b=0.02,
+                  seeds=(3001, 3002, 3003))
+    for M in (1, 16, 64):
+        K, N = 4096, 14336
+        gemm_case(f"bf16_decode_{M}x{N}x{K}", M, N, K, std_b=0.02, seeds=(3001, 3002, 3003),
+                  bytes_alg=2.0 * (K * N + M * K + M * N))
+
+    # fused chain: GEMM1 + row sums of squares, GEMM2 + RMS scale + SwiGLU
+    Mc, Hc, Fc = 8192, 4096, 11008
+    X = normal((Mc, Hc), 4001)
+    Wt = normal((Hc, Hc), 4002, 0.02)
+    W2 = normal((Hc, 2 * Fc), 4003, 0.02)
+    Y = torch.empty((Mc, Hc), dtype=torch.bfloat16, device="cuda")
+    O = torch.empty((Mc, Fc), dtype=torch.bfloat16, device="cuda")
+    ss = torch.empty(Mc, dtype=torch.float32, device="cuda")
+    e1 = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ss.data_ptr())
+    e2 = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
+                             rms_eps=1e-6)
+    t1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1), reps, 3)
+    t2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2), reps, 3)
+    f1, f2 = 2.0 * Mc * Hc * Hc, 2.0 * Mc * Hc * 2 * Fc
+    W["fused_chain_8192x4096_ffn11008"] = {
+        "gemm1_rowsumsq_ms": round(t1, 5), "gemm2_rms_swiglu_ms": round(t2, 5),
+        "gemm1_tflops": round(f1 / (t1 * 1e-3) / 1e12, 2),
+        "gemm2_tflops": round(f2 / (t2 * 1e-3) / 1e12, 2),
+        "chain_tflops": round((f1 + f2) / ((t1 + t2) * 1e-3) / 1e12, 2)}
+    log(f"chain: {W['fused_chain_8192x4096_ffn11008']}")
+    del X, Wt, W2, Y, O, ss
+
+    # Strassen / Winograd vs classical, and the model's pick
+    S69, WIN = fgemm.FGEMM_VARIANT_S69, fgemm.FGEMM_VARIANT_WINOGRAD
+    for (M, N, K) in [(16384, 16384, 16384), (32768, 8192, 8192)]:
+        for dname, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+            A = uniform((M, K), 5001, dt)
+            B = uniform((K, N), 5002, dt)
+            C = torch.empty((M, N), dtype=dt, device="cuda")
+            res = {}
+            cands = {"classical": fgemm.classical_plan()}
+            for d in (1, 2):
+                cands[f"s69_d{d}"] = fgemm.strassen_plan(d, S69)
+                cands[f"winograd_d{d}"] = fgemm.strassen_plan(d, WIN)
+            r2 = max(3, reps // 3)
+            for name, pl in cands.items():
+                ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), r2, 1)
+                res[name] = {"ms": round(ms, 4),
+                             "effective_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+            code = fgemm.FGEMM_BF16 if dt == torch.bfloat16 else fgemm.FGEMM_F16
+            pick = h.select(M, N, K, dtype=code)
+            pname = "classical" if pick.path == 0 else \
+                f"{'winograd' if pick.variant == WIN else 's69'}_d{pick.depth}"
+            best = min(res, key=lambda k: res[k]["ms"])
+            res["model_pick"] = pname
+            res["model_pred_us"] = round(pick.t_pred_us, 1)
+            res["measured_best"] = best
+            res["regret"] = round(res[pname]["ms"] / res[best]["ms"] - 1.0, 4)
+            key = f"strassen_{dname}_{M}x{N}x{K}"
+            W[key] = res
+            log(f"{key}: {res}")
+            del A, B, C
+            torch.cuda.empty_cache()
+    return W
+
+
+def cpu_baseline(target_s):
+    """The oracle as it stands, timed on a seeded sample of output rows of the
+    headline workload, scaled to TFLOP/s of that sample."""
+    import numpy as np
+    import oracle
+    from hgemm_strassen_type_amd import inputs
+    n = 8192
+    log("cpu baseline: generating the headline inputs on the host")
+    A = inputs.normal((n, n), 2001, inputs.BF16)
+    B = inputs.normal((n, n), 2002, inputs.BF16)
+    C = inputs.normal((n, n), 2003, inputs.BF16)
+    threads = oracle.default_threads()
+    rows = inputs.sample_rows(n, 8, 11)
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, beta=0.5, C=C, dtype=oracle.BF16, rows=rows, threads=threads)
+    t_probe = time.perf_counter() - t0
+    nrows = int(min(n, max(len(rows), len(rows) * target_s / max(t_probe, 1e-3))))
+    rows = inputs.sample_rows(n, nrows, 12)
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, beta=0.5, C=C, dtype=oracle.BF16, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * n * n
+    log(f"cpu baseline: {len(rows)} rows in {dt:.2f} s on {threads} threads")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} seeded output rows of the bf16 8192^3 NN beta=0.5 workload "
+                      f"(fp64 loop incl. decoding B), {dt:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

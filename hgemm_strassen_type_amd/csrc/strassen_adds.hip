@@ -92,7 +92,7 @@ __global__ void scale_from_max_kernel(const unsigned* max_bits, float target, fl
     int e;
     frexpf(target / m, &e);          // target/m = f * 2^e, 0.5 <= f < 1
     e -= 1;
-    e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    e = e < -126 ? -126 : (e > 126 ? 126 : e);  // a normal fp32 power of two
     s = ldexpf(1.f, e);
   }
   *scale = s;
@@ -214,7 +214,7 @@ __global__ void postadd_kernel(PostAddKArgs a) {
   const int64_t chunks = a.n / 4;
   const int64_t total = a.m * chunks;
   float factor = 1.f;
-  if (!a.out32) factor = a.alpha / (*a.scale_a * *a.scale_b);
+  if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
     int64_t i = t / chunks, j = (t - i * chunks) * 4;

@@ -1,0 +1,124 @@
+"""GPU parity of the fused epilogues (bias, per-row sum of squares, RMS row scale +
+SwiGLU) and of the two-GEMM chain that uses them, against the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from hgemm_strassen_type_amd import fgemm
+from hgemm_strassen_type_amd import inputs
+from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, from_dev, handle, rel_err, say,
+                      to_dev, empty_out)
+
+pytestmark = pytest.mark.gpu
+TILES = [(256, 256), (128, 128), (64, 128), (32, 128)]
+
+
+def dev_f32(n, fill=np.nan):
+    import torch
+    return torch.full((n,), fill, dtype=torch.float32, device="cuda")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("tile", TILES)
+def test_bias_and_rowsumsq(dtype, tile):
+    import torch
+    M, N, K = 300, 520, 200
+    say(f"bias+rowsumsq dtype={dtype} tile={tile}")
+    A = inputs.normal((M, K), 81, dtype)
+    B = inputs.normal((K, N), 82, dtype, std=0.1)
+    C = inputs.normal((M, N), 83, dtype)
+    bias = inputs.normal((N,), 84, dtype)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    _, Q, ss = oracle.gemm(A, B, beta=0.25, C=C, dtype=dtype, epi=flags, bias=bias)
+    Ad, Bd, Cd, bd = to_dev(A, dtype), to_dev(B, dtype), to_dev(C, dtype), to_dev(bias[None, :], dtype)
+    ssd = dev_f32(M)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ, bias=bd.data_ptr(),
+                              rowsumsq=ssd.data_ptr())
+    handle().gemm(Ad, Bd, Cd, beta=0.25, epilogue=epi, plan=fgemm.classical_plan(*tile))
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+    got = ssd.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ss) / ss) <= STATS_TOL
+
+
+def test_rowsumsq_exact_constant_rows():
+    # K = 1 and a row of ones: every output row is constant, ss = N * a_i^2 exactly
+    import torch
+    dtype = BF16
+    M, N = 130, 4096
+    say("rowsumsq constant rows")
+    a = inputs.integers((M, 1), 85, dtype, -3, 3)
+    ones = inputs.to_bits(np.ones((1, N)), dtype)
+    ssd = dev_f32(M)
+    Cd = empty_out(M, N, dtype)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
+    handle().gemm(to_dev(a, dtype), to_dev(ones, dtype), Cd, epilogue=epi)
+    torch.cuda.synchronize()
+    av = oracle.decode(a, dtype)[:, 0]
+    assert np.array_equal(ssd.cpu().numpy().astype(np.float64), N * av * av)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("transB", [False, True])
+@pytest.mark.parametrize("tile", TILES[:3])
+def test_rms_swiglu_ragged(dtype, transB, tile):
+    import torch
+    M, K, Nout = 300, 256, 264
+    say(f"rms_swiglu dtype={dtype} transB={transB} tile={tile}")
+    X = inputs.normal((M, K), 91, dtype)
+    W = inputs.normal((K, 2 * Nout), 92, dtype, std=0.1)
+    ss = (np.random.default_rng(93).uniform(0.5, 2.0, M) * 4096).astype(np.float32)
+    C = inputs.normal((M, Nout), 94, dtype)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_RMS_SWIGLU, rms_ss=ss.astype(np.float64),
+                          rms_n=4096, rms_eps=1e-6, beta=0.5, C=C, alpha=1.5)
+    Wst = np.ascontiguousarray(W.T) if transB else W
+    Xd, Wd, Cd = to_dev(X, dtype), to_dev(Wst, dtype), to_dev(C, dtype)
+    ssd = torch.from_numpy(ss).cuda()
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(), rms_n=4096,
+                              rms_eps=1e-6)
+    handle().gemm(Xd, Wd, Cd, transB=transB, alpha=1.5, beta=0.5, epilogue=epi,
+                  plan=fgemm.classical_plan(*tile))
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+
+
+def run_chain(M, H, F, seed0, dtype=BF16):
+    """GEMM1 X[M x H] W[H x H] + row sums of squares; GEMM2 Y W2[H x 2F] + RMS + SwiGLU."""
+    import torch
+    X = inputs.normal((M, H), seed0, dtype)
+    W = inputs.normal((H, H), seed0 + 1, dtype, std=0.02)
+    W2 = inputs.normal((H, 2 * F), seed0 + 2, dtype, std=0.02)
+    Xd, Wd, W2d = to_dev(X, dtype), to_dev(W, dtype), to_dev(W2, dtype)
+    Yd = empty_out(M, H, dtype)
+    ssd = dev_f32(M)
+    Od = empty_out(M, F, dtype)
+    e1 = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
+    e2 = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(), rms_n=H,
+                             rms_eps=1e-6)
+    handle().gemm(Xd, Wd, Yd, epilogue=e1)
+    handle().gemm(Yd, W2d, Od, epilogue=e2)
+    torch.cuda.synchronize()
+    return X, W, W2, from_dev(Yd), ssd.cpu().numpy().astype(np.float64), from_dev(Od)
+
+
+def check_chain(X, W, W2, Y, ss, O, rows, H, dtype=BF16):
+    _, Yq, ssr = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_ROWSUMSQ, rows=rows)
+    assert rel_err(Y[rows], Yq, dtype) <= CLASSICAL_TOL
+    assert np.max(np.abs(ss[rows] - ssr) / ssr) <= STATS_TOL
+    # GEMM2 on the oracle's own Y rows and statistics
+    _, Oq, _ = oracle.gemm(Yq, W2, dtype=dtype, epi=oracle.EPI_RMS_SWIGLU, rms_ss=ssr, rms_n=H,
+                           rms_eps=1e-6)
+    assert rel_err(O[rows], Oq, dtype) <= CLASSICAL_TOL
+
+
+def test_chain_small_full_check():
+    say("chain 520x384 -> 2x264")
+    X, W, W2, Y, ss, O = run_chain(520, 384, 264, 4100)
+    check_chain(X, W, W2, Y, ss, O, np.arange(520), 384)
+
+
+def test_chain_llm_size():
+    """M=8192, hidden 4096, FFN 11008: X N(0,1), W and W2 N(0,0.02); sampled rows."""
+    say("chain 8192x4096 -> 2x11008")
+    X, W, W2, Y, ss, O = run_chain(8192, 4096, 11008, 4001)
+    check_chain(X, W, W2, Y, ss, O, inputs.sample_rows(8192, 24, 9), 4096)
