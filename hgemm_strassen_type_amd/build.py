@@ -39,33 +39,35 @@ def _units():
     return units
 
 
-def _compile(unit):
+def _compile(unit, extra=(), build_dir=BUILD):
     src, obj, defs = unit
-    out = os.path.join(BUILD, obj)
-    cmd = [HIPCC, *FLAGS, *defs, "-c", src, "-o", out]
+    out = os.path.join(build_dir, obj)
+    cmd = [HIPCC, *FLAGS, *extra, *defs, "-c", src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return out
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = True, extra=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile and link; `extra` adds compiler switches, `out` names the library."""
+    os.makedirs(build_dir, exist_ok=True)
     units = _units()
     jobs = jobs or min(len(units), max(1, len(os.sched_getaffinity(0))))
     if verbose:
         print(f"[fgemm build] {len(units)} units, {jobs} jobs, {HIPCC}", flush=True)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, units))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda u: _compile(u, extra, build_dir), units))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"[fgemm build] wrote {LIB}", flush=True)
-    return LIB
+        print(f"[fgemm build] wrote {out}", flush=True)
+    return out
 
 
 if __name__ == "__main__":

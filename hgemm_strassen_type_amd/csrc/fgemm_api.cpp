@@ -244,20 +244,12 @@ struct StrassenRun {
   int depth, variant, sub_tile;
   int in_dtype;
   float* scale_a; float* scale_b;
-  // per level l (1-based): S, T (fp16 sums) and P (fp32 products)
-  void* S[3][5];
-  void* T[3][5];
+  // per level l (1-based): the seven left and right product operands (fp16) and
+  // the seven products (fp32)
+  void* S[3][7];
+  void* T[3][7];
   float* P[3][7];
 };
-
-// Logical sub-block (bi, bj) of a blocked operand with logical size rows x cols.
-BlockedOperand sub_block(const BlockedOperand& x, int64_t rows, int64_t cols, int bi, int bj) {
-  BlockedOperand r = x;
-  const uint16_t* base = static_cast<const uint16_t*>(x.ptr);
-  const int64_t hr = rows / 2, hc = cols / 2;
-  r.ptr = x.trans ? base + (int64_t)bj * hc * x.ld + bi * hr : base + (int64_t)bi * hr * x.ld + bj * hc;
-  return r;
-}
 
 BlockedOperand temp_op(void* p, int64_t rows, int64_t cols, int trans) {
   BlockedOperand r;
@@ -269,35 +261,9 @@ BlockedOperand temp_op(void* p, int64_t rows, int64_t cols, int trans) {
   return r;
 }
 
-// The seven operand pairs of one level.  L is the left operand (Ml x Kl), R the
-// right one (Kl x Nl); S/T are the pre-add outputs of this level.
-void product_operands(const StrassenRun& run, int level, const BlockedOperand& L,
-                      const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
-                      BlockedOperand (&left)[7], BlockedOperand (&right)[7]) {
-  const int64_t m = Ml / 2, k = Kl / 2, n = Nl / 2;
-  auto S = [&](int q) { return temp_op(run.S[level][q], m, k, L.trans); };
-  auto T = [&](int q) { return temp_op(run.T[level][q], k, n, R.trans); };
-  auto Lb = [&](int i, int j) { return sub_block(L, Ml, Kl, i, j); };
-  auto Rb = [&](int i, int j) { return sub_block(R, Kl, Nl, i, j); };
-  if (run.variant == FGEMM_VARIANT_WINOGRAD) {
-    left[0] = Lb(0, 0); right[0] = Rb(0, 0);  // P1 = A11 B11
-    left[1] = Lb(0, 1); right[1] = Rb(1, 0);  // P2 = A12 B21
-    left[2] = S(3);     right[2] = Rb(1, 1);  // P3 = S4 B22
-    left[3] = Lb(1, 1); right[3] = T(3);      // P4 = A22 T4
-    left[4] = S(0);     right[4] = T(0);      // P5 = S1 T1
-    left[5] = S(1);     right[5] = T(1);      // P6 = S2 T2
-    left[6] = S(2);     right[6] = T(2);      // P7 = S3 T3
-  } else {
-    left[0] = S(0);     right[0] = T(0);      // M1 = (A11+A22)(B11+B22)
-    left[1] = S(1);     right[1] = Rb(0, 0);  // M2 = (A21+A22) B11
-    left[2] = Lb(0, 0); right[2] = T(1);      // M3 = A11 (B12-B22)
-    left[3] = Lb(1, 1); right[3] = T(2);      // M4 = A22 (B21-B11)
-    left[4] = S(2);     right[4] = Rb(1, 1);  // M5 = (A11+A12) B22
-    left[5] = S(3);     right[5] = T(3);      // M6 = (A21-A11)(B11+B12)
-    left[6] = S(4);     right[6] = T(4);      // M7 = (A12-A22)(B21+B22)
-  }
-}
-
+// One level of the recursion on the left operand L (Ml x Kl) and the right
+// operand R (Kl x Nl): pre-adds, seven sub-products (batched, or recursed into the
+// next level), post-add into `out32` (inner levels) or the caller's C (top level).
 fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOperand& L,
                               const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
                               float* out32, int64_t ld32) {
@@ -307,20 +273,18 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
   if (e != hipSuccess) return FGEMM_ERR_HIP;
   e = launch_preadd(R, Kl, Nl, run.variant, 1, run.scale_b, run.T[level], c.stream);
   if (e != hipSuccess) return FGEMM_ERR_HIP;
-  BlockedOperand left[7], right[7];
-  product_operands(run, level, L, R, Ml, Kl, Nl, left, right);
   if (level == run.depth) {
     GemmBatch b{};
     b.count = 7;
     for (int i = 0; i < 7; ++i) {
+      BlockedOperand lo = temp_op(run.S[level][i], m, k, L.trans);
+      BlockedOperand ro = temp_op(run.T[level][i], k, n, R.trans);
       GemmProblem& p = b.p[i];
-      p.A = left[i].ptr; p.lda = left[i].ld;
-      p.B = right[i].ptr; p.ldb = right[i].ld;
+      p.A = lo.ptr; p.lda = lo.ld;
+      p.B = ro.ptr; p.ldb = ro.ld;
       p.C = run.P[level][i]; p.Cin = nullptr; p.ldc = n;
       p.M = (int)m; p.N = (int)n; p.K = (int)k;
       p.alpha = 1.f; p.beta = 0.f;
-      p.scale_a = run.scale_a; p.scale_b = run.scale_b;
-      p.cvt_a = !left[i].scaled; p.cvt_b = !right[i].scaled;
     }
     KernelKey key{};
     key.tile = run.sub_tile;
@@ -329,13 +293,12 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
     key.dtype = kF16;
     key.epi = kEpiStore32;
     key.vec = 1;
-    key.strassen = 1;
-    key.in_dtype = run.in_dtype;
     e = launch_gemm(key, b, c.stream);
     if (e != hipSuccess) return FGEMM_ERR_HIP;
   } else {
     for (int i = 0; i < 7; ++i) {
-      fgemm_status_t st = strassen_level(run, level + 1, left[i], right[i], m, k, n,
+      fgemm_status_t st = strassen_level(run, level + 1, temp_op(run.S[level][i], m, k, L.trans),
+                                         temp_op(run.T[level][i], k, n, R.trans), m, k, n,
                                          run.P[level][i], n);
       if (st != FGEMM_OK) return st;
     }
@@ -379,11 +342,10 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   run.scale_a = reinterpret_cast<float*>(base + 64);
   run.scale_b = reinterpret_cast<float*>(base + 128);
   size_t off = kScaleHeaderBytes;
-  const int ns = plan.variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
   for (int l = 1; l <= plan.depth; ++l) {
     const int64_t m = c.M >> l, k = c.K >> l, n = c.N >> l;
-    for (int q = 0; q < ns; ++q) { run.S[l][q] = base + off; off += align256((size_t)(m * k * 2)); }
-    for (int q = 0; q < ns; ++q) { run.T[l][q] = base + off; off += align256((size_t)(k * n * 2)); }
+    for (int q = 0; q < 7; ++q) { run.S[l][q] = base + off; off += align256((size_t)(m * k * 2)); }
+    for (int q = 0; q < 7; ++q) { run.T[l][q] = base + off; off += align256((size_t)(k * n * 2)); }
     for (int q = 0; q < 7; ++q) {
       run.P[l][q] = reinterpret_cast<float*>(base + off);
       off += align256((size_t)(m * n * 4));

@@ -14,7 +14,7 @@ namespace fgemm {
 
 template <class CFG, int EPI, bool VEC>
 static hipError_t plain(const GemmBatch& b, hipStream_t s) {
-  return launch_t<CFG, FG_DT, FG_AK != 0, FG_BK != 0, EPI, VEC, false, 0>(b, s);
+  return launch_t<CFG, FG_DT, FG_AK != 0, FG_BK != 0, EPI, VEC>(b, s);
 }
 
 template <class CFG>
@@ -25,26 +25,14 @@ static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_
     if (k.epi == kEpiSwiGLU) return k.vec ? plain<CFG, kEpiSwiGLU, true>(b, s)
                                           : plain<CFG, kEpiSwiGLU, false>(b, s);
   }
+#if FG_DT == 0
+  // fp32 accumulators out: the Strassen sub-products (fp16 temporaries, aligned)
+  if (k.epi == kEpiStore32 && k.vec && CFG::BM >= 128) return plain<CFG, kEpiStore32, true>(b, s);
+#endif
   return hipErrorInvalidValue;
 }
 
 hipError_t FG_NAME(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
-  if (k.strassen) {
-#if FG_DT == 0
-    // Strassen sub-products: fp16 MFMA on fp16 temporaries and converted blocks,
-    // raw fp32 accumulators out.  Operands are always aligned here.
-    if (k.epi != kEpiStore32 || !k.vec) return hipErrorInvalidValue;
-    if (k.tile == 0)
-      return k.in_dtype == kBF16
-                 ? launch_t<Cfg256, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kBF16>(b, s)
-                 : launch_t<Cfg256, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kF16>(b, s);
-    if (k.tile == 1)
-      return k.in_dtype == kBF16
-                 ? launch_t<Cfg128, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kBF16>(b, s)
-                 : launch_t<Cfg128, kF16, FG_AK != 0, FG_BK != 0, kEpiStore32, true, true, kF16>(b, s);
-#endif
-    return hipErrorInvalidValue;
-  }
   switch (k.tile) {
     case 0: return by_epilogue<Cfg256>(k, b, s);
     case 1: return by_epilogue<Cfg128>(k, b, s);

@@ -1,27 +1,31 @@
-// gemm_mfma.hip — classical tiled MFMA GEMM for gfx950 with fused epilogues.
+// gemm_mfma.h — classical tiled MFMA GEMM for gfx950 with fused epilogues.
 //
 // Method (CS336 Lecture 05 notes, Pages 40-42 "tiling"): every workgroup owns one
-// BM x BN output tile and walks K in BK = 64 phases, staging an A and a B tile in
+// BM x BN output tile and walks K in BK-deep phases, staging an A and a B tile in
 // LDS per phase, so each input element is fetched from HBM about N/BN (M/BM) times
 // instead of N times.  The epilogue (tilnote.io PingPong GEMM note, mainloop +
 // epilogue; CODA section for the RMSNorm statistics and SwiGLU) runs on the fp32
 // accumulators in registers before the only store of the tile.
 //
 // gfx950 mapping:
-//   - 256 threads = 4 wave64s in a WAVES_M x WAVES_N grid; each wave owns a
-//     (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA blocks;
-//   - v_mfma_f32_32x32x16_{bf16,f16}: every lane feeds 8 consecutive k of one row
-//     of each operand, so both operands sit in LDS with K contiguous (128 bytes per
-//     row for BK = 64) and a fragment is one 16-byte LDS read;
+//   - NT = 64 * WAVES_M * WAVES_N threads; each wave64 owns a (BM/WAVES_M) x
+//     (BN/WAVES_N) sub-tile of 32x32 blocks of v_mfma_f32_32x32x16_{bf16,f16};
 //   - the B fragment is passed as the MFMA's first operand and the A fragment as
 //     its second, so the accumulator layout gives each lane 4 consecutive output
 //     columns of one row (8-byte stores, in-lane row statistics);
-//   - operands that are M- or N-contiguous in memory (A transposed, B not) are
-//     loaded as 8 x KB blocks and transposed in registers before the LDS store;
-//   - LDS rows are XOR-swizzled on 16-byte chunks so fragment reads and both kinds
-//     of LDS stores spread over the banks;
-//   - two LDS buffers: the global loads of phase k+1 are in flight while phase k
-//     runs on the MFMA units, one barrier per phase;
+//   - tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane straight
+//     into LDS, no registers, asynchronous): a ring of STAGES phase buffers keeps
+//     the loads of STAGES-1 phases in flight while one phase feeds the MFMAs;
+//   - LDS keeps each operand in its memory layout.  K-contiguous operands (A not
+//     transposed, B transposed) are rows of BK values read as one 16-byte fragment
+//     per lane; M/N-contiguous operands (A transposed, B not) are BK rows of BM or
+//     BN values read with ds_read_b64_tr_b16, whose 16-lane groups hand every lane
+//     one column of four consecutive rows, i.e. four consecutive k;
+//   - 16-byte chunks are XOR-swizzled per row so that the fragment reads of both
+//     kinds hit 64 distinct banks; the direct loads fetch each lane's chunk from
+//     the swizzled source position, so LDS is written densely in 1 KB blocks;
+//   - edge tiles (partial M, N or K) load the same slots through registers with
+//     bounds tests and zero fill, and store them to the same LDS positions;
 //   - workgroup ids are remapped so that each XCD (ids are dealt round-robin over
 //     the 8 XCDs) works on a contiguous, L2-friendly group of tiles.
 #pragma once
@@ -35,20 +39,31 @@ namespace fgemm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native vectors, not HIP's uint4/uint2 structs: struct copies are lowered through
+// private memory and lose their place in the schedule.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;
-constexpr int kRowBytes = kBK * 2;  // one LDS row: 64 16-bit values
+#define FGEMM_LDS __attribute__((address_space(3)))
+#define FGEMM_GLOBAL __attribute__((address_space(1)))
+
+// Phase boundary: neither the IR optimizer (memory clobber) nor the machine
+// scheduler (sched_barrier) moves instructions across it.
+#define FGEMM_PHASE_FENCE()            \
+  do {                                 \
+    asm volatile("" ::: "memory");     \
+    __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
 
 // ------------------------------------------------------------------ scalar codecs
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
-  return __uint_as_float(h << 16);
-}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, RNE
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // RNE
 }
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);    // RNE
@@ -62,56 +77,52 @@ __device__ __forceinline__ uint32_t from_f32(float f) {
   return DT == kBF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
 }
 
-// LDS chunk swizzle: 16-byte chunk c of row r lives at chunk c ^ swz(r).
-// Consecutive rows (fragment reads) and rows 8 apart (transposed stores) both land
-// on distinct chunk positions.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 4)) & 7; }
-
-// --------------------------------------------------------------- configuration
-template <int BM_, int BN_, int WAVES_M_>
-struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M_;
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int VA = BM / 32;  // 16-byte vectors per thread for the A tile
-  static constexpr int VB = BN / 32;  // ... and for the B tile
-  static constexpr int LDS_A = BM * kRowBytes, LDS_B = BN * kRowBytes;
-  static constexpr int LDS_STAGE = LDS_A + LDS_B;
-  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
-};
-
-// ------------------------------------------------------------ operand loading
-// Converts 8 packed 16-bit values of type IN to fp16 times `scale` (Strassen
-// operands kept as fp16 temporaries).
-template <int IN>
-__device__ __forceinline__ uint4 convert8(uint4 v, float scale) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    float lo = to_f32<IN>(w[p] & 0xffffu) * scale;
-    float hi = to_f32<IN>(w[p] >> 16) * scale;
-    o[p] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+// s_waitcnt immediate for "vector memory count <= n", other counters unconstrained
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Load 8 consecutive 16-bit values starting at p, of which the first `n` exist.
-template <bool VEC>
-__device__ __forceinline__ uint4 load8(const uint16_t* p, int n) {
-  if (VEC && n >= 8) return *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < n) w[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// --------------------------------------------------------------- configuration
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int STEPS = BK / 16;  // MFMA k-steps per phase
+  static constexpr int LDS_A = BM * BK * 2, LDS_B = BN * BK * 2;
+  static constexpr int LDS_STAGE = LDS_A + LDS_B;
+  static constexpr int QA = LDS_A / 1024, QB = LDS_B / 1024;  // 1 KB load slots per phase
+  static constexpr int QAW = (QA + NW - 1) / NW, QBW = (QB + NW - 1) / NW;  // per wave
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(BK == 32 || BK == 64, "phase depth");
+  static_assert(LDS_A % 1024 == 0 && LDS_B % 1024 == 0, "1 KB load slots");
+  static_assert(STAGES >= 2 && STAGES * LDS_STAGE <= 160 * 1024, "LDS budget");
+};
+
+// ------------------------------------------------------------------ LDS layout
+// K-contiguous operand: R rows of BK values (BK*2 bytes), chunk c of row r at
+// chunk c ^ swz_k(r).  Fragment reads take 16 consecutive rows per bank cycle.
+template <int BK>
+__device__ __forceinline__ int swz_k(int r) {
+  return BK == 32 ? ((r >> 2) & 3) : (((r >> 1) ^ (r >> 4)) & 7);
+}
+// M/N-contiguous operand: BK rows of R values (R*2 bytes), chunk c of row k at
+// chunk c ^ swz_mn(k); a transposed read takes rows k..k+3 (k % 4 == 0) of four
+// consecutive chunks per 16 lanes.
+template <int R>
+__device__ __forceinline__ int swz_mn(int k) {
+  return (4 * (k & 3)) & (R / 8 - 1);
 }
 
 // Column map of the B tile.  Plain GEMM: tile column c is global column n0 + c.
 // SwiGLU: each wave column of WN tile columns holds WN/2 gate columns followed by
-// the WN/2 up columns of the same outputs; `out` is the output column, `g` the
-// column of op(B).  Returns the number of valid columns from c on (<= 8 needed).
+// the WN/2 up columns of the same outputs; `*g` is the column of op(B).  Returns
+// the number of valid columns from c on.
 template <bool SWIGLU, int WN>
 __device__ __forceinline__ int bcol_map(int c, int n0, int N, int* g) {
   if (!SWIGLU) {
@@ -125,160 +136,372 @@ __device__ __forceinline__ int bcol_map(int c, int n0, int N, int* g) {
   return N - out;
 }
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, bool STR, int INDT>
-struct GemmTile {
-  static constexpr int BM = CFG::BM, BN = CFG::BN;
-  static constexpr bool SWIGLU = EPI == kEpiSwiGLU;
+// Load 8 consecutive 16-bit values starting at p, of which the first `n` exist.
+__device__ __forceinline__ v4u load8_checked(const uint16_t* p, int n, bool vec) {
+  if (vec && n >= 8) return *reinterpret_cast<const v4u*>(p);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < n) w[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
+  return v4u{w[0], w[1], w[2], w[3]};
+}
 
-  // ---- A: op(A) is M x K.  AK: stored M x K (K contiguous); else stored K x M.
-  __device__ __forceinline__ static void load_a(const GemmProblem& P, int m0, int k0, int tid,
-                                                float sa, uint4 (&r)[CFG::VA]) {
-    const uint16_t* A = static_cast<const uint16_t*>(P.A);
-    if (AK) {
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+struct GemmTile {
+  static constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
+  static constexpr bool SWIGLU = EPI == kEpiSwiGLU;
+  static constexpr int OUT_BN = SWIGLU ? BN / 2 : BN;
+
+  // ============================================================ load slots
+  // Slot q of an operand is the 1 KB block [q*1024, q*1024 + 1024) of its LDS region;
+  // lane l of the wave that owns it moves the 16 bytes at q*1024 + 16*l.  slot_src
+  // gives the source of that chunk: `row` (operand row for K-contiguous, k for
+  // M/N-contiguous) and the logical 16-byte chunk `c` inside the row.
+  template <bool KCONTIG, int R>
+  __device__ __forceinline__ static void slot_src(int q, int lane, int* row, int* c) {
+    constexpr int CPR = KCONTIG ? BK / 8 : R / 8;  // chunks per LDS row
+    const int e = q * 64 + lane;
+    const int r = e / CPR, p = e % CPR;
+    *row = r;
+    *c = p ^ (KCONTIG ? swz_k<BK>(r) : swz_mn<R>(r));
+  }
+
+  // Per-lane byte offsets of the fast path (relative to a per-phase uniform base).
+  struct LoadAddr {
+    uint32_t a[CFG::QAW];
+    uint32_t b[CFG::QBW];
+  };
+
+  __device__ __forceinline__ static void load_addr(const GemmProblem& P, int n0, int wave,
+                                                   int lane, LoadAddr& la) {
 #pragma unroll
-      for (int i = 0; i < CFG::VA; ++i) {
-        int idx = tid + i * kThreads, row = idx >> 3, c = idx & 7;
-        int gm = m0 + row, gk = k0 + c * 8;
-        int n = (gm < P.M) ? P.K - gk : 0;
-        r[i] = n > 0 ? load8<VEC>(A + (int64_t)gm * P.lda + gk, n) : make_uint4(0, 0, 0, 0);
-        if (STR && P.cvt_a) r[i] = convert8<INDT>(r[i], sa);
-      }
-    } else {
-      constexpr int KB = CFG::VA, CHUNKS = BM / 8;
-      int cm = tid % CHUNKS, kg = tid / CHUNKS;
+    for (int i = 0; i < CFG::QAW; ++i) {
+      int q = wave + CFG::NW * i, row, c;
+      slot_src<AK, BM>(q < CFG::QA ? q : 0, lane, &row, &c);
+      // AK: base = A + m0 rows + k0, row = m; else base = A + k0 rows + m0, row = k
+      la.a[i] = (uint32_t)((int64_t)row * P.lda * 2 + c * 16);
+    }
 #pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        int gk = k0 + kg * KB + j, gm = m0 + cm * 8;
-        int n = (gk < P.K) ? P.M - gm : 0;
-        r[j] = n > 0 ? load8<VEC>(A + (int64_t)gk * P.lda + gm, n) : make_uint4(0, 0, 0, 0);
-        if (STR && P.cvt_a) r[j] = convert8<INDT>(r[j], sa);
+    for (int i = 0; i < CFG::QBW; ++i) {
+      int q = wave + CFG::NW * i, row, c;
+      slot_src<BKC, BN>(q < CFG::QB ? q : 0, lane, &row, &c);
+      int g;
+      if (BKC) {  // row = tile column n: global row g of B (stored Nb x K)
+        bcol_map<SWIGLU, CFG::WN>(row, n0, P.N, &g);
+        la.b[i] = (uint32_t)((int64_t)g * P.ldb * 2 + c * 16);
+      } else {    // row = k, chunk c = tile columns 8c..8c+7
+        bcol_map<SWIGLU, CFG::WN>(c * 8, n0, P.N, &g);
+        la.b[i] = (uint32_t)((int64_t)row * P.ldb * 2 + (int64_t)g * 2);
       }
     }
   }
 
-  // ---- B: op(B) is K x Nb.  BKC: stored Nb x K (K contiguous); else stored K x Nb.
-  __device__ __forceinline__ static void load_b(const GemmProblem& P, int n0, int k0, int tid,
-                                                float sb, uint4 (&r)[CFG::VB]) {
-    const uint16_t* B = static_cast<const uint16_t*>(P.B);
-    if (BKC) {
+  // Uniform byte base of phase kt.
+  __device__ __forceinline__ static const char* a_base(const GemmProblem& P, int m0, int kt) {
+    const char* A = static_cast<const char*>(P.A);
+    return AK ? A + ((int64_t)m0 * P.lda + (int64_t)kt * BK) * 2
+              : A + ((int64_t)kt * BK * P.lda + m0) * 2;
+  }
+  __device__ __forceinline__ static const char* b_base(const GemmProblem& P, int kt) {
+    const char* B = static_cast<const char*>(P.B);
+    return BKC ? B + (int64_t)kt * BK * 2 : B + (int64_t)kt * BK * P.ldb * 2;
+  }
+
+  // One global_load_lds_dwordx4: 64 lanes x 16 bytes from gbase + voff (per lane)
+  // to LDS [lds, lds + 1 KB).  Written as assembly so that the compiler does not see
+  // an LDS write it cannot disambiguate from the fragment reads (it would wait for
+  // every load in flight before each of them); the ring's own vmcnt waits order
+  // them instead.  M0 carries the LDS address; one wait state after writing it.
+  __device__ __forceinline__ static void lds_dma(const char* gbase, uint32_t voff, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+
+  __device__ __forceinline__ static uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const FGEMM_LDS uint8_t*)p;
+  }
+
+  // Fast path: issue this wave's direct-to-LDS loads of phase kt into `stage`.
+  __device__ __forceinline__ static void issue_loads(const GemmProblem& P, int m0, int kt,
+                                                     int wave, const LoadAddr& la,
+                                                     uint8_t* stage) {
+    const char* ab = a_base(P, m0, kt);
+    const char* bb = b_base(P, kt);
+    const uint32_t ls = lds_addr(stage);
 #pragma unroll
-      for (int i = 0; i < CFG::VB; ++i) {
-        int idx = tid + i * kThreads, row = idx >> 3, c = idx & 7;
-        int g;
+    for (int i = 0; i < CFG::QAW; ++i) {
+      const int q = wave + CFG::NW * i;
+      if (CFG::QA % CFG::NW == 0 || q < CFG::QA) lds_dma(ab, la.a[i], ls + q * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < CFG::QBW; ++i) {
+      const int q = wave + CFG::NW * i;
+      if (CFG::QB % CFG::NW == 0 || q < CFG::QB) lds_dma(bb, la.b[i], ls + CFG::LDS_A + q * 1024);
+    }
+  }
+
+  // Edge path: the same slots through registers, bounds-tested, zero-filled.
+  __device__ __forceinline__ static void load_checked(const GemmProblem& P, int m0, int n0,
+                                                      int kt, int wave, int lane,
+                                                      v4u (&ra)[CFG::QAW], v4u (&rb)[CFG::QBW]) {
+    const uint16_t* A = static_cast<const uint16_t*>(P.A);
+    const uint16_t* B = static_cast<const uint16_t*>(P.B);
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < CFG::QAW; ++i) {
+      int q = wave + CFG::NW * i, row, c;
+      ra[i] = v4u{0u, 0u, 0u, 0u};
+      if (q >= CFG::QA) continue;
+      slot_src<AK, BM>(q, lane, &row, &c);
+      if (AK) {
+        int gm = m0 + row, gk = k0 + c * 8;
+        int n = gm < P.M ? P.K - gk : 0;
+        if (n > 0) ra[i] = load8_checked(A + (int64_t)gm * P.lda + gk, n, VEC);
+      } else {
+        int gk = k0 + row, gm = m0 + c * 8;
+        int n = gk < P.K ? P.M - gm : 0;
+        if (n > 0) ra[i] = load8_checked(A + (int64_t)gk * P.lda + gm, n, VEC);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CFG::QBW; ++i) {
+      int q = wave + CFG::NW * i, row, c;
+      rb[i] = v4u{0u, 0u, 0u, 0u};
+      if (q >= CFG::QB) continue;
+      slot_src<BKC, BN>(q, lane, &row, &c);
+      int g;
+      if (BKC) {
         int valid = bcol_map<SWIGLU, CFG::WN>(row, n0, P.N, &g);
         int gk = k0 + c * 8;
         int n = valid > 0 ? P.K - gk : 0;
-        r[i] = n > 0 ? load8<VEC>(B + (int64_t)g * P.ldb + gk, n) : make_uint4(0, 0, 0, 0);
-        if (STR && P.cvt_b) r[i] = convert8<INDT>(r[i], sb);
-      }
-    } else {
-      constexpr int KB = CFG::VB, CHUNKS = BN / 8;
-      int cn = tid % CHUNKS, kg = tid / CHUNKS;
-      int g;
-      int valid = bcol_map<SWIGLU, CFG::WN>(cn * 8, n0, P.N, &g);
-#pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        int gk = k0 + kg * KB + j;
-        int n = (gk < P.K) ? valid : 0;
-        r[j] = n > 0 ? load8<VEC>(B + (int64_t)gk * P.ldb + g, n) : make_uint4(0, 0, 0, 0);
-        if (STR && P.cvt_b) r[j] = convert8<INDT>(r[j], sb);
-      }
-    }
-  }
-
-  // ---- LDS stores.  K-contiguous operand: one 16-byte chunk per vector.
-  template <int ROWS, int V>
-  __device__ __forceinline__ static void store_kcontig(uint8_t* lds, int tid, const uint4 (&r)[V]) {
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      int idx = tid + i * kThreads, row = idx >> 3, c = idx & 7;
-      *reinterpret_cast<uint4*>(lds + row * kRowBytes + ((c ^ swz(row)) << 4)) = r[i];
-    }
-  }
-
-  // MN-contiguous operand: KB rows of 8 values -> 8 LDS rows of KB values.
-  template <int ROWS, int KB>
-  __device__ __forceinline__ static void store_transposed(uint8_t* lds, int tid,
-                                                          const uint4 (&r)[KB]) {
-    constexpr int CHUNKS = ROWS / 8;
-    int cm = tid % CHUNKS, kg = tid / CHUNKS;
-    int kel = kg * KB;                 // first k (element) this thread holds
-    int chunk = kel >> 3, within = (kel & 7) * 2;
-    uint32_t w[KB][4];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      w[j][0] = r[j].x; w[j][1] = r[j].y; w[j][2] = r[j].z; w[j][3] = r[j].w;
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      int row = cm * 8 + n;
-      uint8_t* dst = lds + row * kRowBytes + ((chunk ^ swz(row)) << 4) + within;
-      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-      if constexpr (KB == 1) {
-        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w[0][n >> 1] >> (16 * (n & 1)));
+        if (n > 0) rb[i] = load8_checked(B + (int64_t)g * P.ldb + gk, n, VEC);
       } else {
-        uint32_t o[KB / 2];
+        int valid = bcol_map<SWIGLU, CFG::WN>(c * 8, n0, P.N, &g);
+        int gk = k0 + row;
+        int n = gk < P.K ? valid : 0;
+        if (n > 0) rb[i] = load8_checked(B + (int64_t)gk * P.ldb + g, n, VEC);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store_checked(uint8_t* stage, int wave, int lane,
+                                                       const v4u (&ra)[CFG::QAW],
+                                                       const v4u (&rb)[CFG::QBW]) {
 #pragma unroll
-        for (int q = 0; q < KB / 2; ++q)
-          o[q] = __builtin_amdgcn_perm(w[2 * q + 1][n >> 1], w[2 * q][n >> 1], sel);
-        if constexpr (KB == 2) {
-          *reinterpret_cast<uint32_t*>(dst) = o[0];
-        } else if constexpr (KB == 4) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+    for (int i = 0; i < CFG::QAW; ++i) {
+      int q = wave + CFG::NW * i;
+      if (q < CFG::QA) *reinterpret_cast<v4u*>(stage + q * 1024 + lane * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CFG::QBW; ++i) {
+      int q = wave + CFG::NW * i;
+      if (q < CFG::QB)
+        *reinterpret_cast<v4u*>(stage + CFG::LDS_A + q * 1024 + lane * 16) = rb[i];
+    }
+  }
+
+  // ============================================================ fragments
+  struct Frags {
+    v4u a[CFG::FM];
+    v4u b[CFG::FN];
+  };
+
+  // Per-lane LDS byte offsets of the fragments at MFMA step 0 (stage-relative).
+  //   K-contiguous: row r = base + 32f + (lane & 31), chunk 2s + (lane >> 5).
+  //   M/N-contiguous: two transposed 8-byte reads per fragment (k 0-3 and 4-7 of
+  //   the lane's 8-k slot); in a 16-lane group, lane j reads row kb + j/4 at the
+  //   four columns from 4*(j%4) of the group's 16 columns.
+  struct FragAddr {
+    int a[CFG::FM];
+    int b[CFG::FN];
+  };
+
+  template <bool KCONTIG, int R, int F>
+  __device__ __forceinline__ static void frag_base(int wbase, int lane, int base_off,
+                                                   int (&out)[F]) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      if (KCONTIG) {
+        int r = wbase + f * 32 + (lane & 31);
+        out[f] = base_off + r * (BK * 2) + (((lane >> 5) ^ swz_k<BK>(r)) << 4);
+      } else {
+        int g = lane >> 4, j = lane & 15;
+        int kr = 8 * (g >> 1) + (j >> 2);              // row within the k-step
+        int col = wbase + f * 32 + 16 * (g & 1) + 4 * (j & 3);
+        out[f] = base_off + kr * (R * 2) + (((col >> 3) ^ swz_mn<R>(kr)) << 4) + (col & 7) * 2;
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void frag_addr(int wm, int wn, int lane, FragAddr& fa) {
+    frag_base<AK, BM, CFG::FM>(wm * CFG::WM, lane, 0, fa.a);
+    frag_base<BKC, BN, CFG::FN>(wn * CFG::WN, lane, CFG::LDS_A, fa.b);
+  }
+
+  // Offset of step s from step 0.  K-contiguous: chunk 2s + h, and 2s only flips
+  // bits 5 and up of the chunk offset inside the row, so it is an XOR.  M/N-contiguous:
+  // 16 rows further down (the swizzle depends on k mod 4 only).
+  template <bool KCONTIG, int R>
+  __device__ __forceinline__ static int step_addr(int base, int s) {
+    return KCONTIG ? (base ^ (32 * s)) : base + s * 16 * (R * 2);
+  }
+
+  template <bool KCONTIG, int R>
+  __device__ __forceinline__ static v4u read_frag(const uint8_t* stage, int addr) {
+    if constexpr (KCONTIG) {
+      return *reinterpret_cast<const v4u*>(stage + addr);
+    } else {
+      const uint8_t* p = stage + addr;
+      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s FGEMM_LDS*)(p));
+      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s FGEMM_LDS*)(p + 4 * (R * 2)));
+      v2u l2 = __builtin_bit_cast(v2u, lo), h2 = __builtin_bit_cast(v2u, hi);
+      return v4u{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+
+  __device__ __forceinline__ static void read_frags(const uint8_t* stage, const FragAddr& fa,
+                                                    int s, Frags& fr) {
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+      fr.a[f] = read_frag<AK, BM>(stage, step_addr<AK, BM>(fa.a[f], s));
+#pragma unroll
+    for (int f = 0; f < CFG::FN; ++f)
+      fr.b[f] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s));
+  }
+
+  __device__ __forceinline__ static void mfma_step(const Frags& fr,
+                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+#pragma unroll
+    for (int i = 0; i < CFG::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CFG::FN; ++j) {
+        if constexpr (DT == kBF16) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fr.b[j]), __builtin_bit_cast(bf16x8_t, fr.a[i]),
+              acc[i][j], 0, 0, 0);
         } else {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8_t, fr.b[j]), __builtin_bit_cast(f16x8_t, fr.a[i]),
+              acc[i][j], 0, 0, 0);
         }
       }
+  }
+
+  // one MFMA, then one instruction of OTHER_MASK, while both last (I counts MFMAs)
+  template <int I, int MFMA, int OTHER_MASK, int OTHERS>
+  __device__ __forceinline__ static void interleave() {
+    if constexpr (I < MFMA) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (I < OTHERS) __builtin_amdgcn_sched_group_barrier(OTHER_MASK, 1, 0);
+      interleave<I + 1, MFMA, OTHER_MASK, OTHERS>();
+    }
+  }
+  static constexpr int kMfmaPerStep = CFG::FM * CFG::FN;
+  static constexpr int kReadsPerStep = CFG::FM * (AK ? 1 : 2) + CFG::FN * (BKC ? 1 : 2);
+
+  // MFMA step s of the phase in `cur` on fragments `now`, reading step s+1 into `next`.
+  __device__ __forceinline__ static void step(const uint8_t* cur, const FragAddr& fa, int s,
+                                              const Frags& now, Frags& next,
+                                              f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    read_frags(cur, fa, s + 1, next);
+    mfma_step(now, acc);
+    interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
+    FGEMM_PHASE_FENCE();
+  }
+
+  // ============================================================ main loops
+  // Interior tiles: STAGES-deep ring of direct-to-LDS phases.  Per phase kt: issue
+  // the loads of phase kt+STAGES-1 (into the stage freed by the last barrier), run
+  // the MFMA steps while reading the next step's fragments, then wait for phase
+  // kt+1's loads, barrier, and read its first fragments under the last MFMA step.
+  template <int VMC>
+  __device__ __forceinline__ static void wait_phase(bool steady) {
+    if (steady) wait_vmcnt<VMC>();
+    else wait_vmcnt<0>();
+  }
+
+  __device__ __forceinline__ static void loop_fast(const GemmProblem& P, int m0, int n0,
+                                                   uint8_t* smem, int wave, int wm, int wn,
+                                                   int lane, int ktiles,
+                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    constexpr int S = CFG::STAGES;
+    // every wave issues the same number of loads per phase, so one vmcnt bound fits all
+    static_assert(CFG::QA % CFG::NW == 0 && CFG::QB % CFG::NW == 0, "even load slots");
+    constexpr int QW = CFG::QAW + CFG::QBW;  // loads this wave issues per phase
+    LoadAddr la;
+    load_addr(P, n0, wave, lane, la);
+    FragAddr fa;
+    frag_addr(wm, wn, lane, fa);
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+      if (t < ktiles) issue_loads(P, m0, t, wave, la, smem + t * CFG::LDS_STAGE);
+    // phase 0 ready: at most the later prologue phases still in flight
+    wait_phase<(S - 2) * QW>(ktiles >= S - 1);
+    __syncthreads();
+    Frags f0, f1;
+    read_frags(smem, fa, 0, f0);
+    int st = 0;  // stage of phase kt
+    for (int kt = 0; kt < ktiles; ++kt) {
+      FGEMM_PHASE_FENCE();
+      const uint8_t* cur = smem + st * CFG::LDS_STAGE;
+      int st_ahead = st + S - 1;
+      if (st_ahead >= S) st_ahead -= S;
+      if (kt + S - 1 < ktiles)
+        issue_loads(P, m0, kt + S - 1, wave, la, smem + st_ahead * CFG::LDS_STAGE);
+      FGEMM_PHASE_FENCE();
+      // all but the last step; the last step's fragments end up in f1
+      step(cur, fa, 0, f0, f1, acc);
+      if constexpr (CFG::STEPS == 4) {
+        step(cur, fa, 1, f1, f0, acc);
+        step(cur, fa, 2, f0, f1, acc);
+      }
+      // phase kt+1 must have landed; loads of later phases may still fly
+      wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
+      __syncthreads();
+      const int st_next = st + 1 == S ? 0 : st + 1;
+      if (kt + 1 < ktiles) read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
+      mfma_step(f1, acc);
+      interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
+      st = st_next;
+    }
+    FGEMM_PHASE_FENCE();
+  }
+
+  // Edge tiles: bounds-tested register loads into two stages, one barrier a phase.
+  __device__ __forceinline__ static void loop_checked(const GemmProblem& P, int m0, int n0,
+                                                      uint8_t* smem, int wave, int wm, int wn,
+                                                      int lane, int ktiles,
+                                                      f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    FragAddr fa;
+    frag_addr(wm, wn, lane, fa);
+    v4u ra[CFG::QAW], rb[CFG::QBW];
+    load_checked(P, m0, n0, 0, wave, lane, ra, rb);
+    store_checked(smem, wave, lane, ra, rb);
+    __syncthreads();
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const uint8_t* cur = smem + (kt & 1) * CFG::LDS_STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * CFG::LDS_STAGE;
+      const bool more = kt + 1 < ktiles;
+      if (more) load_checked(P, m0, n0, kt + 1, wave, lane, ra, rb);
+#pragma unroll
+      for (int s = 0; s < CFG::STEPS; ++s) {
+        Frags fr;
+        read_frags(cur, fa, s, fr);
+        mfma_step(fr, acc);
+      }
+      if (more) store_checked(nxt, wave, lane, ra, rb);
+      __syncthreads();
     }
   }
 
-  __device__ __forceinline__ static void store_a(uint8_t* lds, int tid, const uint4 (&r)[CFG::VA]) {
-    if (AK) store_kcontig<BM, CFG::VA>(lds, tid, r);
-    else store_transposed<BM, CFG::VA>(lds, tid, r);
-  }
-  __device__ __forceinline__ static void store_b(uint8_t* lds, int tid, const uint4 (&r)[CFG::VB]) {
-    if (BKC) store_kcontig<BN, CFG::VB>(lds, tid, r);
-    else store_transposed<BN, CFG::VB>(lds, tid, r);
-  }
-
-  // ---- one BK = 64 phase on the MFMA units
-  __device__ __forceinline__ static void compute(const uint8_t* la, const uint8_t* lb, int wm,
-                                                 int wn, int lane,
-                                                 f32x16_t (&acc)[CFG::FM][CFG::FN]) {
-    const int lr = lane & 31, hk = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int chunk = 2 * s + hk;
-      uint4 af[CFG::FM], bfr[CFG::FN];
-#pragma unroll
-      for (int f = 0; f < CFG::FM; ++f) {
-        int row = wm * CFG::WM + f * 32 + lr;
-        af[f] = *reinterpret_cast<const uint4*>(la + row * kRowBytes + ((chunk ^ swz(row)) << 4));
-      }
-#pragma unroll
-      for (int f = 0; f < CFG::FN; ++f) {
-        int row = wn * CFG::WN + f * 32 + lr;
-        bfr[f] = *reinterpret_cast<const uint4*>(lb + row * kRowBytes + ((chunk ^ swz(row)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < CFG::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < CFG::FN; ++j) {
-          if constexpr (DT == kBF16) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, bfr[j]), __builtin_bit_cast(bf16x8_t, af[i]),
-                acc[i][j], 0, 0, 0);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8_t, bfr[j]), __builtin_bit_cast(f16x8_t, af[i]),
-                acc[i][j], 0, 0, 0);
-          }
-        }
-    }
-  }
-
-  // ---- epilogues.  Lane layout of acc[i][j][4q+s]: row = wave row base + 32i +
-  // (lane & 31), column = wave column base + 32j + 8q + 4*(lane >> 5) + s.
+  // ============================================================ epilogues
+  // Lane layout of acc[i][j][4q+s]: row = wave row base + 32i + (lane & 31),
+  // column = wave column base + 32j + 8q + 4*(lane >> 5) + s.
   __device__ __forceinline__ static void epilogue(const GemmProblem& P, int m0, int n0, int tn,
                                                   int wm, int wn, int lane,
                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
@@ -296,8 +519,8 @@ struct GemmTile {
             int col = n0 + wn * CFG::WN + j * 32 + 8 * q + 4 * h;
             float* dst = C + (int64_t)row * P.ldc + col;
             if (VEC && col + 4 <= P.N) {
-              *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              *reinterpret_cast<v4f*>(dst) = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s)
@@ -333,7 +556,7 @@ struct GemmTile {
             if (use_beta) {
               uint32_t c[4];
               if (VEC && nv >= 4) {
-                uint2 cv = *reinterpret_cast<const uint2*>(Cin + off);
+                v2u cv = *reinterpret_cast<const v2u*>(Cin + off);
                 c[0] = cv.x & 0xffff; c[1] = cv.x >> 16; c[2] = cv.y & 0xffff; c[3] = cv.y >> 16;
               } else {
 #pragma unroll
@@ -354,7 +577,7 @@ struct GemmTile {
               if (s < nv) ss += r * r;
             }
             if (VEC && nv >= 4) {
-              *reinterpret_cast<uint2*>(C + off) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+              *reinterpret_cast<v2u*>(C + off) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s)
@@ -397,7 +620,7 @@ struct GemmTile {
 #pragma unroll
             for (int s = 0; s < 4; ++s) o[s] = from_f32<DT>(v[s]);
             if (VEC && nv >= 4) {
-              *reinterpret_cast<uint2*>(C + off) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+              *reinterpret_cast<v2u*>(C + off) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s)
@@ -427,22 +650,20 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
   *tn = in / gsz;
 }
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, bool STR, int INDT>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmBatch batch) {
-  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC, STR, INDT>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * CFG::LDS_STAGE];
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+__global__ __launch_bounds__(CFG::NT) void gemm_mfma_kernel(GemmBatch batch) {
+  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[CFG::STAGES * CFG::LDS_STAGE];
   const GemmProblem& P = batch.p[blockIdx.z];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
-  const int out_bn = EPI == kEpiSwiGLU ? CFG::BN / 2 : CFG::BN;
   const int tiles_m = (P.M + CFG::BM - 1) / CFG::BM;
-  const int tiles_n = (P.N + out_bn - 1) / out_bn;
+  const int tiles_n = (P.N + T::OUT_BN - 1) / T::OUT_BN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
   if (tm >= tiles_m || tn >= tiles_n) return;
-  const int m0 = tm * CFG::BM, n0 = tn * out_bn;
-  const float sa = (STR && P.cvt_a) ? *P.scale_a : 1.f;
-  const float sb = (STR && P.cvt_b) ? *P.scale_b : 1.f;
+  const int m0 = tm * CFG::BM, n0 = tn * T::OUT_BN;
 
   f32x16_t acc[CFG::FM][CFG::FN];
 #pragma unroll
@@ -452,40 +673,28 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmBatch batch) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int ktiles = (P.K + kBK - 1) / kBK;
+  const int ktiles = (P.K + CFG::BK - 1) / CFG::BK;
+  // Interior tiles with no K tail take the direct-load ring.  Per-lane offsets are
+  // 32-bit, which bounds the leading dimensions there.
+  const int64_t b_rows = BKC ? (EPI == kEpiSwiGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
+  const bool fast = VEC && (P.K % CFG::BK == 0) && (m0 + CFG::BM <= P.M) &&
+                    (n0 + T::OUT_BN <= P.N) &&
+                    (int64_t)(AK ? CFG::BM : CFG::BK) * P.lda < (1ll << 31) &&
+                    b_rows * P.ldb < (1ll << 31);
   if (ktiles > 0) {
-    uint4 ra[CFG::VA], rb[CFG::VB];
-    T::load_a(P, m0, 0, tid, sa, ra);
-    T::load_b(P, n0, 0, tid, sb, rb);
-    T::store_a(smem, tid, ra);
-    T::store_b(smem + CFG::LDS_A, tid, rb);
-    __syncthreads();
-    for (int kt = 0; kt < ktiles; ++kt) {
-      uint8_t* cur = smem + (kt & 1) * CFG::LDS_STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * CFG::LDS_STAGE;
-      const bool more = kt + 1 < ktiles;
-      if (more) {
-        T::load_a(P, m0, (kt + 1) * kBK, tid, sa, ra);
-        T::load_b(P, n0, (kt + 1) * kBK, tid, sb, rb);
-      }
-      T::compute(cur, cur + CFG::LDS_A, wm, wn, lane, acc);
-      if (more) {
-        T::store_a(nxt, tid, ra);
-        T::store_b(nxt + CFG::LDS_A, tid, rb);
-      }
-      __syncthreads();
-    }
+    if (fast) T::loop_fast(P, m0, n0, smem, wave, wm, wn, lane, ktiles, acc);
+    else T::loop_checked(P, m0, n0, smem, wave, wm, wn, lane, ktiles, acc);
   }
   T::epilogue(P, m0, n0, tn, wm, wn, lane, acc);
 }
 
 // ------------------------------------------------------------------ launching
-using Cfg256 = TileCfg<256, 256, 2>;
-using Cfg128 = TileCfg<128, 128, 2>;
-using Cfg64 = TileCfg<64, 128, 2>;
-using Cfg32 = TileCfg<32, 128, 1>;
+using Cfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
+using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
+using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, bool STR, int INDT>
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
   int maxtiles = 0;
   for (int i = 0; i < b.count; ++i) {
@@ -495,8 +704,8 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
   }
   if (maxtiles == 0) return hipSuccess;
   dim3 grid(maxtiles, 1, b.count);
-  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC, STR, INDT>), grid,
-                     dim3(kThreads), 0, s, b);
+  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), grid, dim3(CFG::NT), 0, s,
+                     b);
   return hipGetLastError();
 }
 

@@ -36,10 +36,6 @@ struct GemmProblem {
   float* ss_partial;    // [tiles_n * 2][M] per-wave-column partial sums of squares
   const float* rms_ss;  // [M] sums of squares for the RMS scale
   float rms_inv_n, rms_eps;
-  const float* scale_a; // device scalar: multiply A by it while converting (Strassen)
-  const float* scale_b; // device scalar for B
-  int cvt_a, cvt_b;     // Strassen products: 1 = operand is in the input type and still
-                        // needs the scale and the conversion to fp16; 0 = fp16 temporary
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).
@@ -56,8 +52,6 @@ struct KernelKey {
   int dtype;          // ElemType of the MFMA inputs and of 16-bit outputs
   int epi;            // EpiKind
   int vec;            // 1: 16-byte aligned fast path
-  int strassen;       // 1: Strassen sub-products (fp16 MFMA, per-problem conversion)
-  int in_dtype;       // Strassen: ElemType of the caller's operands
 };
 
 // One instantiation unit per (MFMA dtype, A layout, B layout); each is compiled from
@@ -97,10 +91,11 @@ hipError_t launch_fill_u32(unsigned* p, unsigned value, int64_t n, hipStream_t s
 hipError_t launch_scale_from_max(const unsigned* max_bits, float target, float* scale,
                                  hipStream_t stream);
 
-// Pre-add: from the four sub-blocks of `src` (logical rows x cols), write the sum
-// operands of the variant into fp16 buffers out[0..count) (rows/2 x cols/2 each,
-// same layout as src, leading dimension = their own width), values times *scale
-// unless src.scaled.  side 0 = left operand (A), 1 = right operand (B).
+// Pre-add: from the four sub-blocks of `src` (logical rows x cols), write the seven
+// operands of the variant's products on that side into fp16 buffers out[0..7)
+// (rows/2 x cols/2 each, same layout as src, leading dimension = their own width):
+// the block sums and the plain blocks the products use, values times *scale unless
+// src.scaled.  side 0 = left operand (A), 1 = right operand (B).
 hipError_t launch_preadd(const BlockedOperand& src, int64_t rows, int64_t cols, int variant,
                          int side, const float* scale, void* const* out, hipStream_t stream);
 

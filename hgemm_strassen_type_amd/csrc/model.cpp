@@ -59,10 +59,10 @@ double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, 
 }
 
 int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
-              double in_bytes, double out_bytes, int beta, double* t_us) {
+              double in_bytes, double out_bytes, int beta, double* t_us, int max_tile) {
   int best = -1;
   double bt = 0;
-  for (int i = 0; i < kNumTiles; ++i) {
+  for (int i = 0; i < kNumTiles && kTiles[i].tile <= max_tile; ++i) {
     const TileInfo& t = kTiles[i];
     if (swiglu && t.tile == 3) continue;  // the SwiGLU epilogue needs two column halves
     const int64_t out_bn = swiglu ? t.bn / 2 : t.bn;
@@ -78,7 +78,8 @@ int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swig
 }
 
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant) {
-  const int64_t ns = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  (void)variant;
+  const int64_t ns = 7;  // the seven fp16 operands of each side's products
   size_t total = kScaleHeaderBytes;
   for (int l = 1; l <= depth; ++l) {
     const int64_t m = M >> l, k = K >> l, n = N >> l;
@@ -92,7 +93,8 @@ size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int varian
 double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
                         int variant, int beta, int* sub_tile) {
   const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
-  const double ns = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
+  (void)variant;
+  const double ns = 7;  // fp16 operands written per side (sums and plain blocks)
   double t = 0, launches = 0;
   // max|A|, max|B| for the fp16 scales
   t += ((double)M * K + (double)K * N) * 2.0 / bw;
@@ -111,7 +113,7 @@ double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K
   // sub-products: 7^d problems of the deepest size, seven per launch
   const int64_t m = M >> depth, n = N >> depth, k = K >> depth;
   double tp;
-  int tile = best_tile(md, m, n, k, 0, 7, 2.0, 4.0, 0, &tp);
+  int tile = best_tile(md, m, n, k, 0, 7, 2.0, 4.0, 0, &tp, 1);
   if (sub_tile) *sub_tile = tile;
   const double batches = instances / 7;
   t += batches * (tp - md.launch_us) * 1e-6;

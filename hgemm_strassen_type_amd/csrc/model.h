@@ -26,8 +26,9 @@ void model_defaults(fgemm_model_t* m, int cus, double clock_ghz);
 double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
                          int64_t K, int64_t Nb, int64_t out_bn, int count, double in_bytes,
                          double out_bytes, int beta);
+// Tile of least predicted time among tile ids 0..max_tile.
 int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
-              double in_bytes, double out_bytes, int beta, double* t_us);
+              double in_bytes, double out_bytes, int beta, double* t_us, int max_tile = 3);
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant);
 double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
                         int variant, int beta, int* sub_tile);

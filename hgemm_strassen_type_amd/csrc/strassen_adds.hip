@@ -4,9 +4,10 @@
 // replaces one product of 2x2 blocks by seven block products plus block sums, and
 // kernels are grouped so shared partial results stay on chip instead of being
 // fetched from DRAM again.  Here that grouping means:
-//   - one pre-add kernel per operand reads its four sub-blocks once and writes all
-//     of the variant's sums, chained sums (Winograd S2 from S1, S4 from S2, ...)
-//     staying in registers in fp32;
+//   - one pre-add kernel per operand reads its four sub-blocks once and writes the
+//     seven operands of that side's products (the variant's sums and the plain
+//     blocks, all as scaled fp16), chained sums (Winograd S2 from S1, S4 from S2,
+//     ...) staying in registers in fp32;
 //   - one post-add kernel reads the seven fp32 products once and writes all four
 //     output blocks, with alpha, beta*C and the bias fused in at the top level.
 // The limitation the same summary notes (temporary buffers cost memory) is why
@@ -99,11 +100,15 @@ __global__ void scale_from_max_kernel(const unsigned* max_bits, float target, fl
 }
 
 // ------------------------------------------------------------------ pre-add
+// One pass over the four sub-blocks of an operand writes the seven operands of
+// that side's products, in product order, as scaled fp16: the block sums (chained
+// Winograd sums stay in fp32 registers) and the plain blocks, so that every
+// sub-product is a plain fp16 GEMM.
 struct PreAddArgs {
   const uint16_t* blk[4];   // X11, X12, X21, X22 (logical blocks) in storage
   int64_t ld;               // source leading dimension
   int64_t srows, scols;     // stored sub-block shape (scols contiguous)
-  uint16_t* out[5];         // fp16 outputs, stored srows x scols, leading dim scols
+  uint16_t* out[7];         // fp16 outputs, stored srows x scols, leading dim scols
   int dt;                   // source element type
   int scaled;               // source already carries the scale
   const float* scale;
@@ -128,56 +133,62 @@ __global__ void preadd_kernel(PreAddArgs a) {
       x11[e] *= s; x12[e] *= s; x21[e] *= s; x22[e] *= s;
     }
     const int64_t di = r * a.scols + c;
-    float o[5][8];
-    int n;
+    float o[7][8];
     if (a.variant == FGEMM_VARIANT_WINOGRAD) {
-      n = 4;
       if (a.side == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float s1 = x21[e] + x22[e];   // S1 = A21 + A22
           float s2 = s1 - x11[e];       // S2 = S1 - A11
-          o[0][e] = s1;
-          o[1][e] = s2;
-          o[2][e] = x11[e] - x21[e];    // S3 = A11 - A21
-          o[3][e] = x12[e] - s2;        // S4 = A12 - S2
+          o[0][e] = x11[e];             // P1: A11
+          o[1][e] = x12[e];             // P2: A12
+          o[2][e] = x12[e] - s2;        // P3: S4 = A12 - S2
+          o[3][e] = x22[e];             // P4: A22
+          o[4][e] = s1;                 // P5: S1
+          o[5][e] = s2;                 // P6: S2
+          o[6][e] = x11[e] - x21[e];    // P7: S3 = A11 - A21
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float t1 = x12[e] - x11[e];   // T1 = B12 - B11
           float t2 = x22[e] - t1;       // T2 = B22 - T1
-          o[0][e] = t1;
-          o[1][e] = t2;
-          o[2][e] = x22[e] - x12[e];    // T3 = B22 - B12
-          o[3][e] = t2 - x21[e];        // T4 = T2 - B21
+          o[0][e] = x11[e];             // P1: B11
+          o[1][e] = x21[e];             // P2: B21
+          o[2][e] = x22[e];             // P3: B22
+          o[3][e] = t2 - x21[e];        // P4: T4 = T2 - B21
+          o[4][e] = t1;                 // P5: T1
+          o[5][e] = t2;                 // P6: T2
+          o[6][e] = x22[e] - x12[e];    // P7: T3 = B22 - B12
         }
       }
     } else {
-      n = 5;
       if (a.side == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           o[0][e] = x11[e] + x22[e];    // M1: A11 + A22
           o[1][e] = x21[e] + x22[e];    // M2: A21 + A22
-          o[2][e] = x11[e] + x12[e];    // M5: A11 + A12
-          o[3][e] = x21[e] - x11[e];    // M6: A21 - A11
-          o[4][e] = x12[e] - x22[e];    // M7: A12 - A22
+          o[2][e] = x11[e];             // M3: A11
+          o[3][e] = x22[e];             // M4: A22
+          o[4][e] = x11[e] + x12[e];    // M5: A11 + A12
+          o[5][e] = x21[e] - x11[e];    // M6: A21 - A11
+          o[6][e] = x12[e] - x22[e];    // M7: A12 - A22
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           o[0][e] = x11[e] + x22[e];    // M1: B11 + B22
-          o[1][e] = x12[e] - x22[e];    // M3: B12 - B22
-          o[2][e] = x21[e] - x11[e];    // M4: B21 - B11
-          o[3][e] = x11[e] + x12[e];    // M6: B11 + B12
-          o[4][e] = x21[e] + x22[e];    // M7: B21 + B22
+          o[1][e] = x11[e];             // M2: B11
+          o[2][e] = x12[e] - x22[e];    // M3: B12 - B22
+          o[3][e] = x21[e] - x11[e];    // M4: B21 - B11
+          o[4][e] = x22[e];             // M5: B22
+          o[5][e] = x11[e] + x12[e];    // M6: B11 + B12
+          o[6][e] = x21[e] + x22[e];    // M7: B21 + B22
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < 5; ++q)
-      if (q < n) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
+    for (int q = 0; q < 7; ++q) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
   }
 }
 
@@ -303,8 +314,7 @@ hipError_t launch_preadd(const BlockedOperand& src, int64_t rows, int64_t cols, 
   a.ld = src.ld;
   a.srows = src.trans ? hc : hr;
   a.scols = src.trans ? hr : hc;
-  int n = variant == FGEMM_VARIANT_WINOGRAD ? 4 : 5;
-  for (int q = 0; q < 5; ++q) a.out[q] = q < n ? static_cast<uint16_t*>(out[q]) : nullptr;
+  for (int q = 0; q < 7; ++q) a.out[q] = static_cast<uint16_t*>(out[q]);
   a.dt = src.dtype;
   a.scaled = src.scaled;
   a.scale = scale;
