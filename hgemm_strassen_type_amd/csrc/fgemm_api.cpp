@@ -85,9 +85,22 @@ int vec_ok(fgemm_op_t ta, fgemm_op_t tb, int64_t N, const void* A, int64_t lda, 
   return 1;
 }
 
+int tile_id(int tm, int tn);
+
 fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int64_t K, int vec,
                                 uint32_t flags) {
-  if (p.path == FGEMM_PATH_CLASSICAL) return FGEMM_OK;
+  if (p.path == FGEMM_PATH_CLASSICAL) {
+    if (p.split_k <= 1) return FGEMM_OK;
+    // split K: fp32 slices and a finalize pass; epilogue NONE or BIAS, aligned, and
+    // a whole number of pipeline phases per slice
+    const int t = tile_id(p.tile_m, p.tile_n);
+    if (t < 0) return FGEMM_ERR_INVALID_VALUE;
+    const int64_t ktiles = ceil_div(K, kTiles[t].bk);
+    if (!vec || (flags & ~(uint32_t)FGEMM_EPI_BIAS) || K == 0 || ktiles % p.split_k ||
+        p.split_k > 64)
+      return FGEMM_ERR_NOT_SUPPORTED;
+    return FGEMM_OK;
+  }
   if (p.path != FGEMM_PATH_STRASSEN) return FGEMM_ERR_INVALID_VALUE;
   if (p.depth < 1 || p.depth > 2) return FGEMM_ERR_INVALID_VALUE;
   if (p.variant != FGEMM_VARIANT_S69 && p.variant != FGEMM_VARIANT_WINOGRAD)
@@ -117,6 +130,28 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
   p.workspace_bytes = 0;
   if (flags & FGEMM_EPI_ROWSUMSQ)
     p.workspace_bytes = (size_t)ceil_div(N, tile_n_of(tile)) * waves_n_of(tile) * (size_t)M * 4;
+  // skinny shapes leave CUs idle: split K over extra workgroups when the model
+  // says the finalize pass costs less than the idle bandwidth (tile and split
+  // count are chosen together)
+  if (!(flags & ~(uint32_t)FGEMM_EPI_BIAS) && vec && K > 0) {
+    for (int i = 0; i < kNumTiles; ++i) {
+      const TileInfo& ti = kTiles[i];
+      const int64_t tiles = ceil_div(M, ti.bm) * ceil_div(N, ti.bn);
+      const int64_t ktiles = ceil_div(K, ti.bk);
+      for (int sk = 2; sk <= 16 && tiles < md.compute_units; sk *= 2) {
+        if (ktiles % sk || ktiles / sk < 4) continue;
+        const double t = splitk_time_us(md, ti, M, N, K, sk, beta_hint);
+        if (t < tc) {
+          tc = t;
+          tile = ti.tile;
+          p.tile_m = ti.bm;
+          p.tile_n = ti.bn;
+          p.split_k = sk;
+          p.workspace_bytes = (size_t)sk * (size_t)M * (size_t)N * 4;
+        }
+      }
+    }
+  }
   p.t_pred_us = tc;
   p.t_classical_pred_us = tc;
   for (int depth = 1; depth <= 2; ++depth) {
@@ -229,6 +264,24 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
   k.epi = swiglu ? kEpiSwiGLU : kEpiStore16;
   k.vec = vec;
+  if (plan.split_k > 1) {
+    // fp32 K slices into the workspace, then the epilogue in the finalize pass
+    void* ws;
+    fgemm_status_t st =
+        ensure_workspace(h, (size_t)plan.split_k * (size_t)c.M * (size_t)c.N * 4, &ws);
+    if (st != FGEMM_OK) return st;
+    p.C = ws;
+    p.ldc = c.N;
+    b.k_splits = plan.split_k;
+    k.epi = kEpiStore32;
+    hipError_t e = launch_gemm(k, b, c.stream);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
+    e = launch_splitk_finalize(static_cast<const float*>(ws), plan.split_k, c.M, c.N, c.alpha,
+                               c.beta, c.C, c.ldc,
+                               (flags & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr,
+                               k.dtype, c.stream);
+    return hip_status(e);
+  }
   hipError_t e = launch_gemm(k, b, c.stream);
   if (e != hipSuccess) return FGEMM_ERR_HIP;
   if (parts) {

@@ -25,10 +25,8 @@ static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_
     if (k.epi == kEpiSwiGLU) return k.vec ? plain<CFG, kEpiSwiGLU, true>(b, s)
                                           : plain<CFG, kEpiSwiGLU, false>(b, s);
   }
-#if FG_DT == 0
-  // fp32 accumulators out: the Strassen sub-products (fp16 temporaries, aligned)
-  if (k.epi == kEpiStore32 && k.vec && CFG::BM >= 128) return plain<CFG, kEpiStore32, true>(b, s);
-#endif
+  // fp32 accumulators out: Strassen sub-products and split-K partial slices
+  if (k.epi == kEpiStore32 && k.vec) return plain<CFG, kEpiStore32, true>(b, s);
   return hipErrorInvalidValue;
 }
 

@@ -86,9 +86,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // --------------------------------------------------------------- configuration
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int OCC = OCC_;  // workgroups per CU the register budget is sized for
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -172,14 +173,22 @@ struct GemmTile {
     uint32_t b[CFG::QBW];
   };
 
-  __device__ __forceinline__ static void load_addr(const GemmProblem& P, int n0, int wave,
-                                                   int lane, LoadAddr& la) {
+  // Rows and columns beyond M or N (edge tiles) are clamped onto the last valid
+  // ones: they load real memory, feed MFMA rows/columns the epilogue never stores,
+  // and keep the fast path open for partial tiles whose K is a whole number of phases.
+  __device__ __forceinline__ static void load_addr(const GemmProblem& P, int m0, int n0,
+                                                   int wave, int lane, LoadAddr& la) {
 #pragma unroll
     for (int i = 0; i < CFG::QAW; ++i) {
       int q = wave + CFG::NW * i, row, c;
       slot_src<AK, BM>(q < CFG::QA ? q : 0, lane, &row, &c);
-      // AK: base = A + m0 rows + k0, row = m; else base = A + k0 rows + m0, row = k
-      la.a[i] = (uint32_t)((int64_t)row * P.lda * 2 + c * 16);
+      if (AK) {  // base = A + m0 rows + k0; row = m - m0
+        int r = m0 + row < P.M ? row : P.M - 1 - m0;
+        la.a[i] = (uint32_t)((int64_t)r * P.lda * 2 + c * 16);
+      } else {   // base = A + k0 rows + m0; row = k, columns m0 + 8c .. +7
+        int mc = m0 + 8 * c + 8 <= P.M ? 8 * c : P.M - 8 - m0;
+        la.a[i] = (uint32_t)((int64_t)row * P.lda * 2 + (int64_t)mc * 2);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CFG::QBW; ++i) {
@@ -187,10 +196,12 @@ struct GemmTile {
       slot_src<BKC, BN>(q < CFG::QB ? q : 0, lane, &row, &c);
       int g;
       if (BKC) {  // row = tile column n: global row g of B (stored Nb x K)
-        bcol_map<SWIGLU, CFG::WN>(row, n0, P.N, &g);
+        int valid = bcol_map<SWIGLU, CFG::WN>(row, n0, P.N, &g);
+        if (valid <= 0) g = SWIGLU ? 0 : P.N - 1;
         la.b[i] = (uint32_t)((int64_t)g * P.ldb * 2 + c * 16);
       } else {    // row = k, chunk c = tile columns 8c..8c+7
-        bcol_map<SWIGLU, CFG::WN>(c * 8, n0, P.N, &g);
+        int valid = bcol_map<SWIGLU, CFG::WN>(c * 8, n0, P.N, &g);
+        if (valid < 8) g -= 8 - valid;  // shift the chunk back inside its column block
         la.b[i] = (uint32_t)((int64_t)row * P.ldb * 2 + (int64_t)g * 2);
       }
     }
@@ -427,19 +438,19 @@ struct GemmTile {
 
   __device__ __forceinline__ static void loop_fast(const GemmProblem& P, int m0, int n0,
                                                    uint8_t* smem, int wave, int wm, int wn,
-                                                   int lane, int ktiles,
+                                                   int lane, int kt0, int ktiles,
                                                    f32x16_t (&acc)[CFG::FM][CFG::FN]) {
     constexpr int S = CFG::STAGES;
     // every wave issues the same number of loads per phase, so one vmcnt bound fits all
     static_assert(CFG::QA % CFG::NW == 0 && CFG::QB % CFG::NW == 0, "even load slots");
     constexpr int QW = CFG::QAW + CFG::QBW;  // loads this wave issues per phase
     LoadAddr la;
-    load_addr(P, n0, wave, lane, la);
+    load_addr(P, m0, n0, wave, lane, la);
     FragAddr fa;
     frag_addr(wm, wn, lane, fa);
 #pragma unroll
     for (int t = 0; t < S - 1; ++t)
-      if (t < ktiles) issue_loads(P, m0, t, wave, la, smem + t * CFG::LDS_STAGE);
+      if (t < ktiles) issue_loads(P, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
     // phase 0 ready: at most the later prologue phases still in flight
     wait_phase<(S - 2) * QW>(ktiles >= S - 1);
     __syncthreads();
@@ -452,7 +463,7 @@ struct GemmTile {
       int st_ahead = st + S - 1;
       if (st_ahead >= S) st_ahead -= S;
       if (kt + S - 1 < ktiles)
-        issue_loads(P, m0, kt + S - 1, wave, la, smem + st_ahead * CFG::LDS_STAGE);
+        issue_loads(P, m0, kt0 + kt + S - 1, wave, la, smem + st_ahead * CFG::LDS_STAGE);
       FGEMM_PHASE_FENCE();
       // all but the last step; the last step's fragments end up in f1
       step(cur, fa, 0, f0, f1, acc);
@@ -475,19 +486,19 @@ struct GemmTile {
   // Edge tiles: bounds-tested register loads into two stages, one barrier a phase.
   __device__ __forceinline__ static void loop_checked(const GemmProblem& P, int m0, int n0,
                                                       uint8_t* smem, int wave, int wm, int wn,
-                                                      int lane, int ktiles,
+                                                      int lane, int kt0, int ktiles,
                                                       f32x16_t (&acc)[CFG::FM][CFG::FN]) {
     FragAddr fa;
     frag_addr(wm, wn, lane, fa);
     v4u ra[CFG::QAW], rb[CFG::QBW];
-    load_checked(P, m0, n0, 0, wave, lane, ra, rb);
+    load_checked(P, m0, n0, kt0, wave, lane, ra, rb);
     store_checked(smem, wave, lane, ra, rb);
     __syncthreads();
     for (int kt = 0; kt < ktiles; ++kt) {
       const uint8_t* cur = smem + (kt & 1) * CFG::LDS_STAGE;
       uint8_t* nxt = smem + ((kt + 1) & 1) * CFG::LDS_STAGE;
       const bool more = kt + 1 < ktiles;
-      if (more) load_checked(P, m0, n0, kt + 1, wave, lane, ra, rb);
+      if (more) load_checked(P, m0, n0, kt0 + kt + 1, wave, lane, ra, rb);
 #pragma unroll
       for (int s = 0; s < CFG::STEPS; ++s) {
         Frags fr;
@@ -502,12 +513,12 @@ struct GemmTile {
   // ============================================================ epilogues
   // Lane layout of acc[i][j][4q+s]: row = wave row base + 32i + (lane & 31),
   // column = wave column base + 32j + 8q + 4*(lane >> 5) + s.
-  __device__ __forceinline__ static void epilogue(const GemmProblem& P, int m0, int n0, int tn,
-                                                  int wm, int wn, int lane,
+  __device__ __forceinline__ static void epilogue(const GemmProblem& P, void* Cout, int m0,
+                                                  int n0, int tn, int wm, int wn, int lane,
                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
     const int lr = lane & 31, h = lane >> 5;
     if constexpr (EPI == kEpiStore32) {
-      float* C = static_cast<float*>(P.C);
+      float* C = static_cast<float*>(Cout);
 #pragma unroll
       for (int i = 0; i < CFG::FM; ++i) {
         int row = m0 + wm * CFG::WM + i * 32 + lr;
@@ -530,7 +541,7 @@ struct GemmTile {
       }
       return;
     }
-    uint16_t* C = static_cast<uint16_t*>(P.C);
+    uint16_t* C = static_cast<uint16_t*>(Cout);
     const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
     const bool use_beta = (P.flags & kFlagBeta) != 0;
     if constexpr (EPI == kEpiStore16) {
@@ -651,7 +662,7 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tile
 }
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
-__global__ __launch_bounds__(CFG::NT) void gemm_mfma_kernel(GemmBatch batch) {
+__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
   using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[CFG::STAGES * CFG::LDS_STAGE];
   const GemmProblem& P = batch.p[blockIdx.z];
@@ -673,23 +684,34 @@ __global__ __launch_bounds__(CFG::NT) void gemm_mfma_kernel(GemmBatch batch) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int ktiles = (P.K + CFG::BK - 1) / CFG::BK;
-  // Interior tiles with no K tail take the direct-load ring.  Per-lane offsets are
-  // 32-bit, which bounds the leading dimensions there.
+  // Split K over gridDim.y (fp32 partial slices, EPI = kEpiStore32): the host
+  // makes the phase count a multiple of the split count.
+  const int ktiles_all = (P.K + CFG::BK - 1) / CFG::BK;
+  const int ktiles = ktiles_all / gridDim.y;
+  const int kt0 = blockIdx.y * ktiles;
+  void* Cout = P.C;
+  if (EPI == kEpiStore32 && gridDim.y > 1)
+    Cout = static_cast<float*>(P.C) + (int64_t)blockIdx.y * P.M * P.ldc;
+  // Phases with no K tail take the direct-load ring, also on M/N edge tiles
+  // (clamped rows; transposed operands need 8 valid columns from the tile start).
+  // Per-lane offsets are 32-bit, which bounds the leading dimensions there.
   const int64_t b_rows = BKC ? (EPI == kEpiSwiGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
-  const bool fast = VEC && (P.K % CFG::BK == 0) && (m0 + CFG::BM <= P.M) &&
-                    (n0 + T::OUT_BN <= P.N) &&
-                    (int64_t)(AK ? CFG::BM : CFG::BK) * P.lda < (1ll << 31) &&
-                    b_rows * P.ldb < (1ll << 31);
+  const bool fast = VEC && (P.K % CFG::BK == 0) && (AK || P.M - m0 >= 8) &&
+                    (BKC || P.N - n0 >= 8) &&
+                    (int64_t)(AK ? CFG::BM : CFG::BK + 1) * P.lda < (1ll << 31) &&
+                    (b_rows + 1) * P.ldb < (1ll << 31);
   if (ktiles > 0) {
-    if (fast) T::loop_fast(P, m0, n0, smem, wave, wm, wn, lane, ktiles, acc);
-    else T::loop_checked(P, m0, n0, smem, wave, wm, wn, lane, ktiles, acc);
+    if (fast) T::loop_fast(P, m0, n0, smem, wave, wm, wn, lane, kt0, ktiles, acc);
+    else T::loop_checked(P, m0, n0, smem, wave, wm, wn, lane, kt0, ktiles, acc);
   }
-  T::epilogue(P, m0, n0, tn, wm, wn, lane, acc);
+  T::epilogue(P, Cout, m0, n0, tn, wm, wn, lane, acc);
 }
 
 // ------------------------------------------------------------------ launching
-using Cfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+// 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages; measured on the
+// 8192^3 bf16 shapes against 4-wave 128x128 waves, BK = 32 with 3-4 stages, and
+// 256x128 / 128x256 tiles at two workgroups per CU.
+using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
@@ -703,7 +725,8 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
     if (t > maxtiles) maxtiles = t;
   }
   if (maxtiles == 0) return hipSuccess;
-  dim3 grid(maxtiles, 1, b.count);
+  const int splits = EPI == kEpiStore32 && b.k_splits > 1 ? b.k_splits : 1;
+  dim3 grid(maxtiles, splits, b.count);
   hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), grid, dim3(CFG::NT), 0, s,
                      b);
   return hipGetLastError();

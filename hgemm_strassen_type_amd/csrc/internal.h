@@ -42,6 +42,7 @@ struct GemmProblem {
 struct GemmBatch {
   GemmProblem p[7];
   int count;
+  int k_splits;   // kEpiStore32 only: K split over gridDim.y into fp32 slices of M x ldc
 };
 
 // Kernel selection for one launch.
@@ -114,5 +115,11 @@ struct PostAddArgs {
   const float* scale_a; const float* scale_b;
 };
 hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
+
+// Split-K finalize: C = RNE16(alpha * sum_s part[s] + beta*C + bias), part[s] is
+// M x N fp32 (leading dimension N), C is 16-bit with leading dimension ldc.
+hipError_t launch_splitk_finalize(const float* part, int splits, int64_t M, int64_t N,
+                                  float alpha, float beta, void* C, int64_t ldc,
+                                  const void* bias, int dtype, hipStream_t stream);
 
 }  // namespace fgemm

@@ -21,14 +21,21 @@ namespace fgemm {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute and memory time of one kernel: they overlap, but not perfectly; the
+// shorter one still shows a little (this also breaks ties toward less padding).
+double overlap(double a, double b) {
+  const double hi = a > b ? a : b, lo = a > b ? b : a;
+  return hi + 0.05 * lo;
+}
+
 // Macro-tiles of the classical kernel and the share of the per-CU MFMA rate each
 // reaches at steady state relative to the 256x256 tile (smaller tiles re-read
 // operands more often per FLOP and hide less latency).
 const TileInfo kTiles[kNumTiles] = {
-    {0, 256, 256, 1.00},
-    {1, 128, 128, 0.70},
-    {2, 64, 128, 0.45},
-    {3, 32, 128, 0.30},
+    {0, 256, 256, 64, 1.00},
+    {1, 128, 128, 32, 0.70},
+    {2, 64, 128, 32, 0.45},
+    {3, 32, 128, 64, 0.30},
 };
 
 void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
@@ -53,9 +60,11 @@ double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, 
   const double t_compute = waves * tile_flops / (per_cu * md.eta_mfma * t.rel_eta);
   const double bytes = count * ((double)M * K * in_bytes + (double)K * Nb * in_bytes +
                                 (double)M * N * out_bytes * (beta ? 2.0 : 1.0));
-  const double t_mem = bytes / (md.hbm_gbps * 1e9 * md.eta_hbm);
-  const double tt = t_compute > t_mem ? t_compute : t_mem;
-  return tt * 1e6 + md.launch_us;
+  // streaming from HBM needs enough workgroups in flight: fewer than one per CU
+  // leaves bandwidth unused
+  const double occ = tiles < md.compute_units ? (double)tiles / md.compute_units : 1.0;
+  const double t_mem = bytes / (md.hbm_gbps * 1e9 * md.eta_hbm * occ);
+  return overlap(t_compute, t_mem) * 1e6 + md.launch_us;
 }
 
 int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
@@ -75,6 +84,23 @@ int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swig
   }
   if (t_us) *t_us = bt;
   return best;
+}
+
+double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
+                      int64_t K, int splits, int beta) {
+  // `splits` slices of K/splits each, fp32 partials out, then one finalize pass
+  const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+  const int64_t blocks = tiles * splits;
+  const int64_t waves = ceil_div(blocks, md.compute_units);
+  const double per_cu = md.peak_tflops * 1e12 / md.compute_units;
+  const double t_compute =
+      waves * 2.0 * t.bm * t.bn * (double)(K / splits) / (per_cu * md.eta_mfma * t.rel_eta);
+  const double bytes = (double)M * K * 2 + (double)K * N * 2 + (double)splits * M * N * 4;
+  const double occ = blocks < md.compute_units ? (double)blocks / md.compute_units : 1.0;
+  const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
+  const double t_mem = bytes / (bw * occ);
+  const double fin = ((double)splits * M * N * 4 + (double)M * N * 2 * (beta ? 2.0 : 1.0)) / bw;
+  return (overlap(t_compute, t_mem) + fin) * 1e6 + 2 * md.launch_us;
 }
 
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant) {

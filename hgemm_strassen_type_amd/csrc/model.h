@@ -11,6 +11,7 @@ namespace fgemm {
 struct TileInfo {
   int tile;        // kernel tile id
   int bm, bn;      // macro-tile (bn MFMA columns; SwiGLU writes bn/2 outputs)
+  int bk;          // K depth of one pipeline phase
   double rel_eta;  // steady-state MFMA efficiency relative to the 256x256 tile
 };
 
@@ -20,6 +21,7 @@ constexpr size_t kScaleHeaderBytes = 256;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 int64_t ceil_div(int64_t a, int64_t b);
+double overlap(double a, double b);
 
 void model_defaults(fgemm_model_t* m, int cus, double clock_ghz);
 
@@ -29,6 +31,9 @@ double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, 
 // Tile of least predicted time among tile ids 0..max_tile.
 int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
               double in_bytes, double out_bytes, int beta, double* t_us, int max_tile = 3);
+// Split-K plan of `splits` K slices with an fp32 finalize pass.
+double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
+                      int64_t K, int splits, int beta);
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant);
 double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
                         int variant, int beta, int* sub_tile);

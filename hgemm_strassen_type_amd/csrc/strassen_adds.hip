@@ -347,6 +347,51 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ split-K finalize
+namespace {
+// Sums the fp32 K slices of a skinny GEMM in a fixed order and applies the
+// epilogue; four consecutive columns per lane where the row allows it.
+__global__ void splitk_finalize_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                       int64_t N, float alpha, float beta, uint16_t* C,
+                                       int64_t ldc, const uint16_t* bias, int dt) {
+  const int64_t chunks = (N + 3) / 4;
+  const int64_t total = M * chunks;
+  const int64_t slice = M * N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / chunks, j = (t - i * chunks) * 4;
+    const int nv = N - j < 4 ? (int)(N - j) : 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sidx = 0; sidx < splits; ++sidx) {
+      const float* p = part + sidx * slice + i * N + j;
+      if (nv == 4 && (N & 3) == 0) {
+        float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+      } else {
+        for (int e = 0; e < nv; ++e) v[e] += p[e];
+      }
+    }
+    uint16_t* c = C + i * ldc + j;
+    for (int e = 0; e < nv; ++e) {
+      float r = alpha * v[e];
+      if (beta != 0.f) r += beta * h2f(c[e], dt);
+      if (bias) r += h2f(bias[j + e], dt);
+      c[e] = (uint16_t)f2h(r, dt);
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_splitk_finalize(const float* part, int splits, int64_t M, int64_t N,
+                                  float alpha, float beta, void* C, int64_t ldc,
+                                  const void* bias, int dtype, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_finalize_kernel, dim3(stream_grid(M * ((N + 3) / 4))), dim3(256), 0,
+                     stream, part, splits, M, N, alpha, beta, static_cast<uint16_t*>(C), ldc,
+                     static_cast<const uint16_t*>(bias), dtype);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ row sum reduction
 namespace {
 __global__ void rowsumsq_reduce_kernel(const float* __restrict__ part, int parts, int M,

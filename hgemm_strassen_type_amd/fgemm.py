@@ -263,7 +263,7 @@ def strassen_plan(depth: int, variant: int, tile: int = 0) -> fgemm_plan_t:
     return p
 
 
-def classical_plan(tile_m: int = 0, tile_n: int = 0) -> fgemm_plan_t:
+def classical_plan(tile_m: int = 0, tile_n: int = 0, split_k: int = 1) -> fgemm_plan_t:
     p = fgemm_plan_t()
-    p.path, p.tile_m, p.tile_n = FGEMM_PATH_CLASSICAL, tile_m, tile_n
+    p.path, p.tile_m, p.tile_n, p.split_k = FGEMM_PATH_CLASSICAL, tile_m, tile_n, split_k
     return p

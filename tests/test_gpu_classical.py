@@ -32,7 +32,9 @@ def stored(M, N, K, transA, transB, A_lo, seedA, seedB, dtype, kind="int"):
 @pytest.mark.parametrize("transA,transB", LAYOUTS)
 def test_exact_integer_products(tile, dtype, transA, transB):
     # |C| <= K*max|a|*max|b| = 256 (bf16) / 1024 (fp16): exact in the output type
-    for (M, N, K) in [(256, 256, 256), (300, 200, 130), (1, 264, 64), (67, 9, 1)]:
+    # whole-phase K with ragged M/N (clamped fast path), K tails (checked path), tiny
+    for (M, N, K) in [(256, 256, 256), (300, 200, 256), (33, 136, 128), (300, 200, 130),
+                      (1, 264, 64), (67, 9, 1)]:
         say(f"exact tile={tile} dtype={dtype} tA={transA} tB={transB} M={M} N={N} K={K}")
         A, B = stored(M, N, K, transA, transB, 0, 11 + M, 12 + N, dtype)
         _, Q, _ = oracle.gemm(A, B, transA=transA, transB=transB, dtype=dtype)
@@ -164,3 +166,46 @@ def test_llm_shapes(M, N):
     rows = inputs.sample_rows(M, 32, 8)
     _, Q, _ = oracle.gemm(X, W, dtype=dtype, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+
+
+@pytest.mark.parametrize("tile", [(32, 128), (64, 128), (128, 128), (256, 256)])
+@pytest.mark.parametrize("split", [2, 4])
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_split_k_exact_and_random(tile, split, dtype):
+    # exact: integer inputs, K = 256; random: beta and bias through the finalize pass
+    for (M, N) in [(1, 264), (16, 520), (100, 136)]:
+        K = 256
+        say(f"split-K tile={tile} split={split} dtype={dtype} M={M} N={N}")
+        A, B = stored(M, N, K, False, False, 0, 81 + M, 82 + N, dtype)
+        _, Q, _ = oracle.gemm(A, B, dtype=dtype)
+        got = run(A, B, dtype, M=M, N=N, plan=fgemm.classical_plan(*tile, split_k=split))
+        assert np.array_equal(got, Q), (M, N)
+    M, N, K = 48, 392, 512
+    A, B = stored(M, N, K, False, True, 0, 91, 92, dtype, kind="normal")
+    C = inputs.normal((M, N), 93, dtype)
+    _, Q, _ = oracle.gemm(A, B, transB=True, alpha=0.5, beta=-0.75, C=C, dtype=dtype)
+    got = run(A, B, dtype, transB=True, alpha=0.5, beta=-0.75, C_bits=C,
+              plan=fgemm.classical_plan(*tile, split_k=split))
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+def test_split_k_refusals():
+    import torch
+    dtype = BF16
+    say("split-K refusals")
+    A = to_dev(inputs.normal((16, 96), 1, dtype), dtype)
+    B = to_dev(inputs.normal((96, 64), 2, dtype), dtype)
+    C = to_dev(np.zeros((16, 64), dtype=np.uint16), dtype)
+    ssd = torch.zeros(16, dtype=torch.float32, device="cuda")
+    # 96 = 3 phases of 32: not divisible into 2 slices
+    st = fgemm.fgemm_gemm_plan(handle().h, fgemm.classical_plan(128, 128, split_k=2), 0, 0, 16,
+                               64, 96, 1.0, A.data_ptr(), 96, B.data_ptr(), 64, 0.0, C.data_ptr(),
+                               64, fgemm.FGEMM_BF16, None, fgemm.current_stream(), check=False)
+    assert st == fgemm.FGEMM_ERR_NOT_SUPPORTED
+    # the row-statistics epilogue needs the unsplit kernel
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
+    st = fgemm.fgemm_gemm_plan(handle().h, fgemm.classical_plan(32, 128, split_k=2), 0, 0, 16, 64,
+                               96, 1.0, A.data_ptr(), 96, B.data_ptr(), 64, 0.0, C.data_ptr(), 64,
+                               fgemm.FGEMM_BF16, epi, fgemm.current_stream(), check=False)
+    assert st == fgemm.FGEMM_ERR_NOT_SUPPORTED
+    torch.cuda.synchronize()
