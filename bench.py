@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -131,6 +133,15 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic}
+
+    if args.copy_calib:
+        # a plain copy of known size: 1 GiB read and 1 GiB written per launch
+        src = torch.ones(512 * 1024 * 1024, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     workloads = {}
     if not args.only_main:
@@ -270,15 +281,20 @@ def cpu_baseline(target_s):
     B = inputs.normal((n, n), 2002, inputs.BF16)
     C = inputs.normal((n, n), 2003, inputs.BF16)
     threads = oracle.default_threads()
-    rows = inputs.sample_rows(n, 8, 11)
-    t0 = time.perf_counter()
-    oracle.gemm(A, B, beta=0.5, C=C, dtype=oracle.BF16, rows=rows, threads=threads)
-    t_probe = time.perf_counter() - t0
-    nrows = int(min(n, max(len(rows), len(rows) * target_s / max(t_probe, 1e-3))))
-    rows = inputs.sample_rows(n, nrows, 12)
-    t0 = time.perf_counter()
-    oracle.gemm(A, B, beta=0.5, C=C, dtype=oracle.BF16, rows=rows, threads=threads)
-    dt = time.perf_counter() - t0
+
+    def timed(nrows, seed):
+        rows = inputs.sample_rows(n, nrows, seed)
+        t0 = time.perf_counter()
+        oracle.gemm(A, B, beta=0.5, C=C, dtype=oracle.BF16, rows=rows, threads=threads)
+        return rows, time.perf_counter() - t0
+
+    # two probes separate the fixed cost (decoding B) from the per-row cost
+    _, t_a = timed(8, 11)
+    _, t_b = timed(32, 12)
+    per_row = max((t_b - t_a) / 24.0, 1e-4)
+    fixed = max(t_a - 8 * per_row, 0.0)
+    nrows = int(min(n, max(32, (target_s - fixed) / per_row)))
+    rows, dt = timed(nrows, 13)
     flops = 2.0 * len(rows) * n * n
     log(f"cpu baseline: {len(rows)} rows in {dt:.2f} s on {threads} threads")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,

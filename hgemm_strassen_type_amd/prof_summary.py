@@ -1,0 +1,116 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m hgemm_strassen_type_amd.prof_summary stats <kernel_stats.csv> <out.md> "<command>"
+        [<kernel_trace.csv> "<kernel substring>" <warmup dispatches> <bench stdout log>]
+    python -m hgemm_strassen_type_amd.prof_summary traffic <fetch.csv> <write.csv> <out.json>
+        "<kernel substring>" "<command>"
+
+`stats` keeps the per-kernel call count and average/min/max duration of a
+`--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
+`--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of the
+named kernel, each scaled by what the same counter reads for the 1 GiB device
+copy that `bench.py --copy-calib` runs in the same process (read 1 GiB, write
+1 GiB), and records the GEMM kernel sources' hash so a stale record is ignored.
+"""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GIB = 1024 ** 3
+
+
+def _short(name: str, width: int = 120) -> str:
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def stats(csv_path: str, out_md: str, command: str, trace_csv: str | None = None,
+          kernel: str | None = None, skip: int = 0, bench_log: str | None = None) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    if trace_csv and kernel:
+        # the launches of bench.py's timed region: all dispatches after the warmup ones
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+        timed = d[skip:]
+        lines += ["", f"Timed region ({len(timed)} dispatches after {skip} warmup ones) of "
+                      f"`{kernel}`: average {statistics.mean(timed):.2f} us "
+                      f"(min {min(timed):.2f}, max {max(timed):.2f})."]
+        if bench_log:
+            for line in open(bench_log):
+                if line.startswith("{"):
+                    ms = json.loads(line)["ms_per_step"]
+                    lines.append(f"bench.py's own HIP-event timing of the same launches in that "
+                                 f"run: {ms * 1e3:.2f} us per step.")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(csv_path: str, counter: str):
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def _kernel_hash() -> str:
+    sys.path.insert(0, ROOT)
+    import bench  # noqa: E402  (the hash bench.py compares against)
+    return bench.kernel_hash()
+
+
+def traffic(fetch_csv: str, write_csv: str, out_json: str, kernel: str, command: str) -> None:
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, sub):
+        keys = [k for k in d if sub in k]
+        if not keys:
+            raise SystemExit(f"no kernel matching {sub!r}")
+        return statistics.mean(d[keys[0]]), keys[0]
+
+    f_k, name = pick(fetch, kernel)
+    w_k, _ = pick(write, kernel)
+    f_c, _ = pick(fetch, "copyBuffer")
+    w_c, _ = pick(write, "copyBuffer")
+    f_scale = GIB / (f_c * 1024.0)   # true bytes per counted byte
+    w_scale = GIB / (w_c * 1024.0)
+    rec = {"kernel": name, "kernel_hash": _kernel_hash(),
+           "fetch_kib_raw": f_k, "write_kib_raw": w_k,
+           "copy_fetch_kib_raw": f_c, "copy_write_kib_raw": w_c,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_bytes": f_k * 1024.0 * f_scale, "write_bytes": w_k * 1024.0 * w_scale,
+           "command": command}
+    rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    json.dump(rec, open(out_json, "w"), indent=1)
+    md = os.path.splitext(out_json)[0] + ".md"
+    open(md, "w").write(
+        "# HBM traffic of the GEMM kernel (rocprofv3 --pmc)\n\n"
+        f"Kernel: `{_short(name)}`\n\nCommands:\n\n```\n{command}\n```\n\n"
+        "| counter | kernel KiB/launch (raw) | 1 GiB copy KiB (raw) | scale | bytes/launch |\n"
+        "|---|---|---|---|---|\n"
+        f"| FETCH_SIZE | {f_k:.0f} | {f_c:.0f} | {f_scale:.3f} | {rec['fetch_bytes']:.4g} |\n"
+        f"| WRITE_SIZE | {w_k:.0f} | {w_c:.0f} | {w_scale:.3f} | {rec['write_bytes']:.4g} |\n\n"
+        f"Total HBM bytes per launch: {rec['bytes_per_launch']:.4g}\n")
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        extra = sys.argv[5:]
+        stats(sys.argv[2], sys.argv[3], sys.argv[4], *(extra[:2]),
+              *([int(extra[2])] if len(extra) > 2 else []), *(extra[3:4]))
+    elif sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+    else:
+        raise SystemExit(__doc__)
