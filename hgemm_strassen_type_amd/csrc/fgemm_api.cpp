@@ -59,6 +59,7 @@ struct PlanKeyHash {
 
 struct fgemm_handle_s {
   int device = 0;
+  int cus = 0;  // compute units of the device (the model's count may be set otherwise)
   fgemm_model_t model{};
   std::unordered_map<PlanKey, fgemm_plan_t, PlanKeyHash> plans;
   void* user_ws = nullptr;
@@ -236,6 +237,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   if (swiglu && tile == 3) return FGEMM_ERR_NOT_SUPPORTED;
   GemmBatch b{};
   b.count = 1;
+  b.cus = h->cus;
   GemmProblem& p = b.p[0];
   p.A = c.A; p.B = c.B; p.C = c.C; p.Cin = c.C;
   p.lda = c.lda; p.ldb = c.ldb; p.ldc = c.ldc;
@@ -294,6 +296,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
 // ------------------------------------------------------------------ Strassen
 struct StrassenRun {
   const Call* c;
+  int cus;
   int depth, variant, sub_tile;
   int in_dtype;
   float* scale_a; float* scale_b;
@@ -329,6 +332,7 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
   if (level == run.depth) {
     GemmBatch b{};
     b.count = 7;
+    b.cus = run.cus;
     for (int i = 0; i < 7; ++i) {
       BlockedOperand lo = temp_op(run.S[level][i], m, k, L.trans);
       BlockedOperand ro = temp_op(run.T[level][i], k, n, R.trans);
@@ -385,6 +389,7 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   if (st != FGEMM_OK) return st;
   StrassenRun run{};
   run.c = &c;
+  run.cus = h->cus;
   run.depth = plan.depth;
   run.variant = plan.variant;
   run.sub_tile = tile_id(plan.tile_m, plan.tile_n);
@@ -493,6 +498,7 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
   fgemm_handle_s* h = new (std::nothrow) fgemm_handle_s();
   if (!h) return FGEMM_ERR_ALLOC;
   h->device = device;
+  h->cus = prop.multiProcessorCount;
   double ghz = prop.clockRate > 0 ? prop.clockRate / 1e6 : 2.4;
   model_defaults(&h->model, prop.multiProcessorCount, ghz);
   *handle = h;

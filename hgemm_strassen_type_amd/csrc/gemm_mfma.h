@@ -102,7 +102,17 @@ struct TileCfg {
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
   static_assert(BK == 32 || BK == 64, "phase depth");
   static_assert(LDS_A % 1024 == 0 && LDS_B % 1024 == 0, "1 KB load slots");
-  static_assert(STAGES >= 2 && STAGES * LDS_STAGE <= 160 * 1024, "LDS budget");
+  // Epilogue staging: each wave transposes 32 x EPI_CW fp32 blocks through its own
+  // EPI_CW*128-byte region of the last stage (free at the end of a tile; the first
+  // STAGES-1 stages may already hold the next tile's first phases).
+  static constexpr int EPI_CW = (WN % 64 == 0 && NW * 32 * 64 * 4 <= LDS_STAGE) ? 64 : 32;
+  static constexpr int EPI_WAVE_BYTES = 32 * EPI_CW * 4;
+  static constexpr int EPI_OFF = (STAGES - 1) * LDS_STAGE;
+  static constexpr int SMEM = STAGES * LDS_STAGE > EPI_OFF + NW * EPI_WAVE_BYTES
+                                  ? STAGES * LDS_STAGE
+                                  : EPI_OFF + NW * EPI_WAVE_BYTES;
+  static_assert(STAGES >= 2 && SMEM <= 160 * 1024, "LDS budget");
+  static_assert(WN % EPI_CW == 0, "epilogue blocks");
 };
 
 // ------------------------------------------------------------------ LDS layout
@@ -177,7 +187,11 @@ struct GemmTile {
   // ones: they load real memory, feed MFMA rows/columns the epilogue never stores,
   // and keep the fast path open for partial tiles whose K is a whole number of phases.
   __device__ __forceinline__ static void load_addr(const GemmProblem& P, int m0, int n0,
-                                                   int wave, int lane, LoadAddr& la) {
+                                                   int wave, int lane_in, LoadAddr& la) {
+    // recomputed per tile: an opaque lane id keeps the lane-only parts from being
+    // hoisted out of the tile loop and held in registers across the main loop
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int i = 0; i < CFG::QAW; ++i) {
       int q = wave + CFG::NW * i, row, c;
@@ -436,9 +450,28 @@ struct GemmTile {
     else wait_vmcnt<0>();
   }
 
+  // Next tile's first phases, issued by the last phase of the current tile (after
+  // its final barrier every stage is free) so that they fly during the epilogue.
+  struct Next {
+    int m0, n0, kt0, ktiles;
+  };
+
+  __device__ __forceinline__ static void issue_prologue(const GemmProblem& P, int m0, int kt0,
+                                                        int ktiles, int wave, const LoadAddr& la,
+                                                        uint8_t* smem) {
+#pragma unroll
+    for (int t = 0; t < CFG::STAGES - 1; ++t)
+      if (t < ktiles) issue_loads(P, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
+  }
+
+  // `pre`: this tile's prologue was issued by the previous tile (before its
+  // epilogue stores, which share the wait counter).  `chain`: issue the prologue of
+  // `nx` (a tile of problem `Pn`) at the end.
   __device__ __forceinline__ static void loop_fast(const GemmProblem& P, int m0, int n0,
                                                    uint8_t* smem, int wave, int wm, int wn,
-                                                   int lane, int kt0, int ktiles,
+                                                   int lane, int kt0, int ktiles, bool pre,
+                                                   bool chain, const GemmProblem& Pn,
+                                                   const Next& nx,
                                                    f32x16_t (&acc)[CFG::FM][CFG::FN]) {
     constexpr int S = CFG::STAGES;
     // every wave issues the same number of loads per phase, so one vmcnt bound fits all
@@ -446,13 +479,14 @@ struct GemmTile {
     constexpr int QW = CFG::QAW + CFG::QBW;  // loads this wave issues per phase
     LoadAddr la;
     load_addr(P, m0, n0, wave, lane, la);
+    int flane = lane;  // opaque: fragment offsets are rebuilt per tile, not held across it
+    asm volatile("" : "+v"(flane));
     FragAddr fa;
-    frag_addr(wm, wn, lane, fa);
-#pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-      if (t < ktiles) issue_loads(P, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
-    // phase 0 ready: at most the later prologue phases still in flight
-    wait_phase<(S - 2) * QW>(ktiles >= S - 1);
+    frag_addr(wm, wn, flane, fa);
+    if (!pre) issue_prologue(P, m0, kt0, ktiles, wave, la, smem);
+    // phase 0 ready: at most the later prologue phases still in flight (all of
+    // them when stores were issued after them)
+    wait_phase<(S - 2) * QW>(!pre && ktiles >= S - 1);
     __syncthreads();
     Frags f0, f1;
     read_frags(smem, fa, 0, f0);
@@ -475,7 +509,13 @@ struct GemmTile {
       wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
       __syncthreads();
       const int st_next = st + 1 == S ? 0 : st + 1;
-      if (kt + 1 < ktiles) read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
+      if (kt + 1 < ktiles) {
+        read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
+      } else if (chain) {
+        LoadAddr ln;  // computed here, where the next fragments are dead
+        load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);
+        issue_prologue(Pn, nx.m0, nx.kt0, nx.ktiles, wave, ln, smem);
+      }
       mfma_step(f1, acc);
       interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
       st = st_next;
@@ -486,8 +526,10 @@ struct GemmTile {
   // Edge tiles: bounds-tested register loads into two stages, one barrier a phase.
   __device__ __forceinline__ static void loop_checked(const GemmProblem& P, int m0, int n0,
                                                       uint8_t* smem, int wave, int wm, int wn,
-                                                      int lane, int kt0, int ktiles,
+                                                      int lane_in, int kt0, int ktiles,
                                                       f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    int lane = lane_in;  // opaque: per-tile recomputation instead of hoisted registers
+    asm volatile("" : "+v"(lane));
     FragAddr fa;
     frag_addr(wm, wn, lane, fa);
     v4u ra[CFG::QAW], rb[CFG::QBW];
@@ -511,6 +553,152 @@ struct GemmTile {
   }
 
   // ============================================================ epilogues
+  // Row-contiguous epilogue (plain stores, 16-byte aligned operands): every 32-row,
+  // EPI_CW-column block of the wave's accumulators goes to LDS in the MFMA layout and
+  // comes back as 8 consecutive columns of one row per lane, so that beta*C is read
+  // and the result written in whole 128-byte lines.  The arithmetic per element is
+  // that of the register epilogue below: alpha*acc, + beta*C, + bias, one rounding.
+  __device__ __forceinline__ static void epilogue_rows(const GemmProblem& P, void* Cout, int m0,
+                                                       int n0, int tn, int wave, int wm, int wn,
+                                                       int lane_in, uint8_t* smem,
+                                                       f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    int lane = lane_in;  // opaque: recomputed per tile rather than held across the loop
+    asm volatile("" : "+v"(lane));
+    constexpr int CW = CFG::EPI_CW;
+    constexpr int NCH = CW / 4;          // 16-byte chunks per staged row
+    constexpr int LPR = NCH / 2;         // lanes per row on the way out (8 columns each)
+    constexpr int RPT = 64 / LPR;        // rows per pass
+    constexpr int JC = CW / 32;          // accumulator blocks per staged block
+    uint8_t* region = smem + CFG::EPI_OFF + wave * CFG::EPI_WAVE_BYTES;
+    // chunk swizzle: 16 consecutive rows of one logical chunk hit distinct banks
+    auto swz = [](int r) { return NCH == 16 ? (r & 15) : ((r >> 1) & 7); };
+    const int lr = lane & 31, h = lane >> 5;
+    const int orow = lane / LPR, oc = lane % LPR;
+    const bool use_beta = EPI == kEpiStore16 && (P.flags & kFlagBeta) != 0;
+    const bool use_bias = EPI == kEpiStore16 && (P.flags & kFlagBias) != 0;
+    const bool use_ss = EPI == kEpiStore16 && (P.flags & kFlagRowSumSq) != 0;
+    const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
+    const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
+    // beta*C: every whole 8-column piece of the wave's tile is requested up front so
+    // that the reads overlap the staging instead of waiting once per piece
+    constexpr int NPASS = 32 / RPT, NJC = CFG::WN / CW;
+    v4u cpre[EPI == kEpiStore16 ? CFG::FM : 1][EPI == kEpiStore16 ? NJC : 1]
+            [EPI == kEpiStore16 ? NPASS : 1];
+    if constexpr (EPI == kEpiStore16) {
+      if (use_beta) {
+#pragma unroll
+        for (int i = 0; i < CFG::FM; ++i)
+#pragma unroll
+          for (int jc = 0; jc < NJC; ++jc)
+#pragma unroll
+            for (int t = 0; t < NPASS; ++t) {
+              const int row = m0 + wm * CFG::WM + i * 32 + t * RPT + orow;
+              const int col = n0 + wn * CFG::WN + jc * CW + 8 * oc;
+              cpre[i][jc][t] = v4u{0u, 0u, 0u, 0u};
+              if (row < P.M && P.N - col >= 8)
+                cpre[i][jc][t] = *reinterpret_cast<const v4u*>(Cin + (int64_t)row * P.ldc + col);
+            }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CFG::FM; ++i) {
+      const int row_base = m0 + wm * CFG::WM + i * 32;
+      float ss[32 / RPT];
+#pragma unroll
+      for (int t = 0; t < 32 / RPT; ++t) ss[t] = 0.f;
+#pragma unroll
+      for (int jc = 0; jc < CFG::WN / CW; ++jc) {
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& a = acc[i][jc * JC + jj];
+            const float sc = EPI == kEpiStore16 ? P.alpha : 1.f;
+            v4f v = v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            if (EPI == kEpiStore16) v = v * sc;
+            const int c = jj * 8 + 2 * q + h;
+            *reinterpret_cast<v4f*>(region + lr * (CW * 4) + ((c ^ swz(lr)) << 4)) = v;
+          }
+        const int col = n0 + wn * CFG::WN + jc * CW + 8 * oc;
+        const int nv = P.N - col;
+#pragma unroll
+        for (int t = 0; t < 32 / RPT; ++t) {
+          const int r = t * RPT + orow;
+          const uint8_t* src = region + r * (CW * 4);
+          v4f lo = *reinterpret_cast<const v4f*>(src + (((2 * oc) ^ swz(r)) << 4));
+          v4f hi = *reinterpret_cast<const v4f*>(src + (((2 * oc + 1) ^ swz(r)) << 4));
+          const int row = row_base + r;
+          if (row >= P.M || nv <= 0) continue;
+          float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          const int64_t off = (int64_t)row * P.ldc + col;
+          if constexpr (EPI == kEpiStore32) {
+            float* C = static_cast<float*>(Cout);
+            if (nv >= 8) {
+              *reinterpret_cast<v4f*>(C + off) = lo;
+              *reinterpret_cast<v4f*>(C + off + 4) = hi;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (e < nv) C[off + e] = v[e];
+            }
+          } else {
+            uint16_t* C = static_cast<uint16_t*>(Cout);
+            if (use_beta) {
+              uint32_t cb[8];
+              if (nv >= 8) {
+                const v4u cv = cpre[i][jc][t];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  cb[2 * e] = cv[e] & 0xffff;
+                  cb[2 * e + 1] = cv[e] >> 16;
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cb[e] = e < nv ? Cin[off + e] : 0;
+              }
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += P.beta * to_f32<DT>(cb[e]);
+            }
+            if (use_bias) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
+            }
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              o[e] = from_f32<DT>(v[e]);
+              if (use_ss) {
+                const float rr = to_f32<DT>(o[e]);
+                if (e < nv) ss[t] += rr * rr;
+              }
+            }
+            if (nv >= 8) {
+              *reinterpret_cast<v4u*>(C + off) =
+                  v4u{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+                      o[6] | (o[7] << 16)};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (e < nv) C[off + e] = (uint16_t)o[e];
+            }
+          }
+        }
+      }
+      if (use_ss) {
+#pragma unroll
+        for (int t = 0; t < 32 / RPT; ++t) {
+          float x = ss[t];
+#pragma unroll
+          for (int d = 1; d < LPR; d <<= 1) x += __shfl_xor(x, d);
+          const int row = row_base + t * RPT + orow;
+          if (oc == 0 && row < P.M)
+            P.ss_partial[(int64_t)(tn * CFG::WAVES_N + wn) * P.M + row] = x;
+        }
+      }
+    }
+  }
+
+
   // Lane layout of acc[i][j][4q+s]: row = wave row base + 32i + (lane & 31),
   // column = wave column base + 32j + 8q + 4*(lane >> 5) + s.
   __device__ __forceinline__ static void epilogue(const GemmProblem& P, void* Cout, int m0,
@@ -643,68 +831,127 @@ struct GemmTile {
   }
 };
 
-// Workgroup id -> tile.  Ids are dealt round-robin over the 8 XCDs; renumber so
-// each XCD gets a contiguous range, then walk tiles in groups of 8 tile-rows so
-// that tiles running together share A rows and B columns in L2.
-__device__ __forceinline__ void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int* tm,
-                                        int* tn) {
+// Position of a workgroup inside one round of `G` items.  Ids are dealt
+// round-robin over the 8 XCDs; renumber so that the workgroups of one XCD take a
+// contiguous range of the round.
+__device__ __forceinline__ int xcd_slot(int bid, int G) {
   int xcd = bid & 7, idx = bid >> 3;
-  int base = nblk >> 3, rem = nblk & 7;
-  int pid = xcd * base + (xcd < rem ? xcd : rem) + idx;
+  int base = G >> 3, rem = G & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + idx;
+}
+
+// Tile index -> (tile row, tile column), walking groups of 8 tile rows column by
+// column, so that the tiles of one XCD share A rows and B columns in L2.
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
   constexpr int G = 8;
   int per_group = G * tiles_n;
-  int group = pid / per_group;
+  int group = t / per_group;
   int first = group * G;
   int gsz = tiles_m - first < G ? tiles_m - first : G;
-  int in = pid - group * per_group;
+  int in = t - group * per_group;
   *tm = first + in % gsz;
   *tn = in / gsz;
 }
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
-__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
-  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[CFG::STAGES * CFG::LDS_STAGE];
-  const GemmProblem& P = batch.p[blockIdx.z];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+// One work item: problem z, K slice y, tile (tm, tn).
+struct Work {
+  int z, y, tm, tn, m0, n0, kt0, ktiles;
+  bool fast;
+};
+
+template <class T, class CFG, int EPI, bool VEC, bool AK, bool BKC>
+__device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits, Work* w) {
+  const int t = item % b.tiles;
+  const int zy = item / b.tiles;
+  w->z = zy % b.count;
+  w->y = zy / b.count;
+  const GemmProblem& P = b.p[w->z];
   const int tiles_m = (P.M + CFG::BM - 1) / CFG::BM;
   const int tiles_n = (P.N + T::OUT_BN - 1) / T::OUT_BN;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  if (tm >= tiles_m || tn >= tiles_n) return;
-  const int m0 = tm * CFG::BM, n0 = tn * T::OUT_BN;
-
-  f32x16_t acc[CFG::FM][CFG::FN];
-#pragma unroll
-  for (int i = 0; i < CFG::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < CFG::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // Split K over gridDim.y (fp32 partial slices, EPI = kEpiStore32): the host
-  // makes the phase count a multiple of the split count.
+  if (t >= tiles_m * tiles_n) return false;
+  raster(t, tiles_m, tiles_n, &w->tm, &w->tn);
+  w->m0 = w->tm * CFG::BM;
+  w->n0 = w->tn * T::OUT_BN;
+  // split K: the host makes the phase count a multiple of the split count
   const int ktiles_all = (P.K + CFG::BK - 1) / CFG::BK;
-  const int ktiles = ktiles_all / gridDim.y;
-  const int kt0 = blockIdx.y * ktiles;
-  void* Cout = P.C;
-  if (EPI == kEpiStore32 && gridDim.y > 1)
-    Cout = static_cast<float*>(P.C) + (int64_t)blockIdx.y * P.M * P.ldc;
+  w->ktiles = ktiles_all / splits;
+  w->kt0 = w->y * w->ktiles;
   // Phases with no K tail take the direct-load ring, also on M/N edge tiles
   // (clamped rows; transposed operands need 8 valid columns from the tile start).
   // Per-lane offsets are 32-bit, which bounds the leading dimensions there.
   const int64_t b_rows = BKC ? (EPI == kEpiSwiGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
-  const bool fast = VEC && (P.K % CFG::BK == 0) && (AK || P.M - m0 >= 8) &&
-                    (BKC || P.N - n0 >= 8) &&
-                    (int64_t)(AK ? CFG::BM : CFG::BK + 1) * P.lda < (1ll << 31) &&
-                    (b_rows + 1) * P.ldb < (1ll << 31);
-  if (ktiles > 0) {
-    if (fast) T::loop_fast(P, m0, n0, smem, wave, wm, wn, lane, kt0, ktiles, acc);
-    else T::loop_checked(P, m0, n0, smem, wave, wm, wn, lane, kt0, ktiles, acc);
+  w->fast = VEC && (P.K % CFG::BK == 0) && (AK || P.M - w->m0 >= 8) &&
+            (BKC || P.N - w->n0 >= 8) &&
+            (int64_t)(AK ? CFG::BM : CFG::BK + 1) * P.lda < (1ll << 31) &&
+            (b_rows + 1) * P.ldb < (1ll << 31);
+  return true;
+}
+
+// Persistent: gridDim.x workgroups (at most what the device holds at once) take
+// items in rounds of gridDim.x.  A tile that follows a direct-load tile has its
+// first phases loaded during that tile's epilogue.
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
+  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[CFG::SMEM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+  const int G = gridDim.x;
+  const int splits = EPI == kEpiStore32 && batch.k_splits > 1 ? batch.k_splits : 1;
+  const int items = batch.count * splits * batch.tiles;
+
+  int item = xcd_slot(blockIdx.x, G);
+  Work cur;
+  bool have = false;
+  for (; item < items && !have; item += G)
+    have = work_of<T, CFG, EPI, VEC, AK, BKC>(batch, item, splits, &cur);
+  bool pre = false;
+  while (have) {
+    Work nxt;
+    bool have_next = false;
+    for (; item < items && !have_next; item += G)
+      have_next = work_of<T, CFG, EPI, VEC, AK, BKC>(batch, item, splits, &nxt);
+    const GemmProblem& P = batch.p[cur.z];
+
+    f32x16_t acc[CFG::FM][CFG::FN];
+#pragma unroll
+    for (int i = 0; i < CFG::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CFG::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    bool issued = false;
+    if (cur.ktiles > 0) {
+      if (cur.fast) {
+        typename T::Next nx{};
+        const bool chain = have_next && nxt.fast && nxt.ktiles > 0;
+        const GemmProblem& Pn = batch.p[chain ? nxt.z : cur.z];
+        if (chain) {
+          nx.m0 = nxt.m0;
+          nx.n0 = nxt.n0;
+          nx.kt0 = nxt.kt0;
+          nx.ktiles = nxt.ktiles;
+        }
+        T::loop_fast(P, cur.m0, cur.n0, smem, wave, wm, wn, lane, cur.kt0, cur.ktiles, pre,
+                     chain, Pn, nx, acc);
+        issued = chain;
+      } else {
+        T::loop_checked(P, cur.m0, cur.n0, smem, wave, wm, wn, lane, cur.kt0, cur.ktiles, acc);
+      }
+    }
+    void* Cout = P.C;
+    if (EPI == kEpiStore32 && splits > 1)
+      Cout = static_cast<float*>(P.C) + (int64_t)cur.y * P.M * P.ldc;
+    if constexpr (VEC && EPI != kEpiSwiGLU)
+      T::epilogue_rows(P, Cout, cur.m0, cur.n0, cur.tn, wave, wm, wn, lane, smem, acc);
+    else
+      T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, acc);
+    pre = issued;
+    cur = nxt;
+    have = have_next;
   }
-  T::epilogue(P, Cout, m0, n0, tn, wm, wn, lane, acc);
 }
 
 // ------------------------------------------------------------------ launching
@@ -717,7 +964,8 @@ using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
-static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
+static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
+  GemmBatch b = b0;
   int maxtiles = 0;
   for (int i = 0; i < b.count; ++i) {
     int out_bn = EPI == kEpiSwiGLU ? CFG::BN / 2 : CFG::BN;
@@ -725,10 +973,24 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
     if (t > maxtiles) maxtiles = t;
   }
   if (maxtiles == 0) return hipSuccess;
+  b.tiles = maxtiles;
   const int splits = EPI == kEpiStore32 && b.k_splits > 1 ? b.k_splits : 1;
-  dim3 grid(maxtiles, splits, b.count);
-  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), grid, dim3(CFG::NT), 0, s,
-                     b);
+  const int64_t items = (int64_t)maxtiles * splits * b.count;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  // workgroups resident per CU, asked of the runtime once per instantiation
+  static int occ = 0;
+  if (occ <= 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &o, gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>, CFG::NT, 0) != hipSuccess ||
+        o < 1)
+      o = 1;
+    occ = o;
+  }
+  int64_t groups = items;
+  if (b.cus > 0 && (int64_t)b.cus * occ < groups) groups = (int64_t)b.cus * occ;
+  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), dim3((unsigned)groups),
+                     dim3(CFG::NT), 0, s, b);
   return hipGetLastError();
 }
 

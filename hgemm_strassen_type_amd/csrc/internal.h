@@ -39,10 +39,15 @@ struct GemmProblem {
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).
+// Work items are (problem, K slice, output tile) triples.  The launcher starts as
+// many workgroups as the device holds at once (compute units x occupancy, capped
+// by the item count); each loops over its share of the items.
 struct GemmBatch {
   GemmProblem p[7];
   int count;
-  int k_splits;   // kEpiStore32 only: K split over gridDim.y into fp32 slices of M x ldc
+  int k_splits;   // kEpiStore32 only: K split into fp32 slices of M x ldc
+  int cus;        // compute units of the device (0: one workgroup per item)
+  int tiles;      // output tiles of the largest problem (set by the launcher)
 };
 
 // Kernel selection for one launch.
