@@ -251,12 +251,20 @@ struct GemmTile {
     return (uint32_t)(uintptr_t)(const FGEMM_LDS uint8_t*)p;
   }
 
+  // A wave-uniform pointer, held in scalar registers (the load's base operand).
+  __device__ __forceinline__ static const char* uniform_ptr(const char* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+  }
+
   // Fast path: issue this wave's direct-to-LDS loads of phase kt into `stage`.
   __device__ __forceinline__ static void issue_loads(const GemmProblem& P, int m0, int kt,
                                                      int wave, const LoadAddr& la,
                                                      uint8_t* stage) {
-    const char* ab = a_base(P, m0, kt);
-    const char* bb = b_base(P, kt);
+    const char* ab = uniform_ptr(a_base(P, m0, kt));
+    const char* bb = uniform_ptr(b_base(P, kt));
     const uint32_t ls = lds_addr(stage);
 #pragma unroll
     for (int i = 0; i < CFG::QAW; ++i) {

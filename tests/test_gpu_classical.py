@@ -209,3 +209,26 @@ def test_split_k_refusals():
                                fgemm.FGEMM_BF16, epi, fgemm.current_stream(), check=False)
     assert st == fgemm.FGEMM_ERR_NOT_SUPPORTED
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("tile,bk", [((256, 256), 64), ((128, 128), 32), ((64, 128), 32),
+                                     ((32, 128), 64)])
+@pytest.mark.parametrize("phases", [3, 5])
+def test_persistent_chains_odd_and_even_phases(tile, bk, phases):
+    """More tiles than the device holds at once, so every workgroup runs several tiles
+    back to back (each tile's first loads issued by its predecessor); odd and even
+    phase counts.  Integer inputs: exact."""
+    dtype = BF16
+    M = N = 4352
+    K = phases * bk
+    say(f"persistent chains tile={tile} K={K}")
+    A, B = stored(M, N, K, False, False, 0, 101 + phases, 102 + phases, dtype)
+    _, Q, _ = oracle.gemm(A, B, dtype=dtype)
+    got = run(A, B, dtype, plan=fgemm.classical_plan(*tile))
+    assert np.array_equal(got, Q)
+    if tile == (256, 256):
+        At, Bt = stored(M, N, K, True, True, 0, 103 + phases, 104 + phases, dtype)
+        _, Qt, _ = oracle.gemm(At, Bt, transA=True, transB=True, dtype=dtype)
+        got = run(At, Bt, dtype, transA=True, transB=True, M=M, N=N,
+                  plan=fgemm.classical_plan(*tile))
+        assert np.array_equal(got, Qt)
