@@ -221,15 +221,30 @@ struct GemmTile {
     }
   }
 
-  // Uniform byte base of phase kt.
-  __device__ __forceinline__ static const char* a_base(const GemmProblem& P, int m0, int kt) {
-    const char* A = static_cast<const char*>(P.A);
-    return AK ? A + ((int64_t)m0 * P.lda + (int64_t)kt * BK) * 2
-              : A + ((int64_t)kt * BK * P.lda + m0) * 2;
+  // The operand pointers and leading dimensions the direct loads use, read once per
+  // tile into (scalar) registers: the phase fences would otherwise make the
+  // compiler fetch them from the argument block again in every phase.
+  struct Src {
+    const char* A;
+    const char* B;
+    int64_t lda, ldb;
+  };
+  __device__ __forceinline__ static Src src_of(const GemmProblem& P) {
+    Src r;
+    r.A = static_cast<const char*>(P.A);
+    r.B = static_cast<const char*>(P.B);
+    r.lda = P.lda;
+    r.ldb = P.ldb;
+    return r;
   }
-  __device__ __forceinline__ static const char* b_base(const GemmProblem& P, int kt) {
-    const char* B = static_cast<const char*>(P.B);
-    return BKC ? B + (int64_t)kt * BK * 2 : B + (int64_t)kt * BK * P.ldb * 2;
+
+  // Uniform byte base of phase kt.
+  __device__ __forceinline__ static const char* a_base(const Src& S, int m0, int kt) {
+    return AK ? S.A + ((int64_t)m0 * S.lda + (int64_t)kt * BK) * 2
+              : S.A + ((int64_t)kt * BK * S.lda + m0) * 2;
+  }
+  __device__ __forceinline__ static const char* b_base(const Src& S, int kt) {
+    return BKC ? S.B + (int64_t)kt * BK * 2 : S.B + (int64_t)kt * BK * S.ldb * 2;
   }
 
   // One global_load_lds_dwordx4: 64 lanes x 16 bytes from gbase + voff (per lane)
@@ -260,11 +275,10 @@ struct GemmTile {
   }
 
   // Fast path: issue this wave's direct-to-LDS loads of phase kt into `stage`.
-  __device__ __forceinline__ static void issue_loads(const GemmProblem& P, int m0, int kt,
-                                                     int wave, const LoadAddr& la,
-                                                     uint8_t* stage) {
-    const char* ab = uniform_ptr(a_base(P, m0, kt));
-    const char* bb = uniform_ptr(b_base(P, kt));
+  __device__ __forceinline__ static void issue_loads(const Src& S, int m0, int kt, int wave,
+                                                     const LoadAddr& la, uint8_t* stage) {
+    const char* ab = uniform_ptr(a_base(S, m0, kt));
+    const char* bb = uniform_ptr(b_base(S, kt));
     const uint32_t ls = lds_addr(stage);
 #pragma unroll
     for (int i = 0; i < CFG::QAW; ++i) {
@@ -437,6 +451,96 @@ struct GemmTile {
   static constexpr int kMfmaPerStep = CFG::FM * CFG::FN;
   static constexpr int kReadsPerStep = CFG::FM * (AK ? 1 : 2) + CFG::FN * (BKC ? 1 : 2);
 
+  // ---- step 0 with the phase's direct loads slotted between its MFMAs
+  static constexpr int kRA = AK ? 1 : 2, kRB = BKC ? 1 : 2;  // read instructions a fragment
+  static constexpr int kLoadsPerPhase = CFG::QAW + CFG::QBW;
+
+  // Read instruction r of step s into `next`: A fragments first, then B.
+  template <int R>
+  __device__ __forceinline__ static void read_job(const uint8_t* cur, const FragAddr& fa, int s,
+                                                  Frags& next) {
+    if constexpr (R < CFG::FM * kRA) {
+      constexpr int f = R / kRA, part = R % kRA;
+      const int addr = step_addr<AK, BM>(fa.a[f], s);
+      if constexpr (AK) {
+        next.a[f] = *reinterpret_cast<const v4u*>(cur + addr);
+      } else {
+        v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BM * 2)));
+        v2u t2 = __builtin_bit_cast(v2u, t);
+        if (part == 0) { next.a[f].x = t2.x; next.a[f].y = t2.y; }
+        else { next.a[f].z = t2.x; next.a[f].w = t2.y; }
+      }
+    } else {
+      constexpr int r = R - CFG::FM * kRA;
+      constexpr int f = r / kRB, part = r % kRB;
+      const int addr = step_addr<BKC, BN>(fa.b[f], s);
+      if constexpr (BKC) {
+        next.b[f] = *reinterpret_cast<const v4u*>(cur + addr);
+      } else {
+        v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BN * 2)));
+        v2u t2 = __builtin_bit_cast(v2u, t);
+        if (part == 0) { next.b[f].x = t2.x; next.b[f].y = t2.y; }
+        else { next.b[f].z = t2.x; next.b[f].w = t2.y; }
+      }
+    }
+  }
+
+  // Direct load L of this wave's share of a phase (A slots, then B slots).
+  template <int L>
+  __device__ __forceinline__ static void load_job(const char* ab, const char* bb,
+                                                  const LoadAddr& la, int wave, uint32_t ls) {
+    if constexpr (L < CFG::QAW) {
+      const int q = wave + CFG::NW * L;
+      if (CFG::QA % CFG::NW == 0 || q < CFG::QA) lds_dma(ab, la.a[L], ls + q * 1024);
+    } else {
+      constexpr int i = L - CFG::QAW;
+      const int q = wave + CFG::NW * i;
+      if (CFG::QB % CFG::NW == 0 || q < CFG::QB) lds_dma(bb, la.b[i], ls + CFG::LDS_A + q * 1024);
+    }
+  }
+
+  // MFMA M of step 0, then read instruction M of step 1, then load M (when LD); a
+  // scheduling fence after each group keeps the order.  Leftover reads and loads
+  // follow the last MFMA.
+  template <int M, bool LD>
+  __device__ __forceinline__ static void emit0(const uint8_t* cur, const FragAddr& fa,
+                                               const Frags& now, Frags& next,
+                                               f32x16_t (&acc)[CFG::FM][CFG::FN],
+                                               const char* ab, const char* bb,
+                                               const LoadAddr& la, int wave, uint32_t ls) {
+    constexpr int NM = kMfmaPerStep, NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
+    if constexpr (M < NM) {
+      constexpr int i = M / CFG::FN, j = M % CFG::FN;
+      if constexpr (DT == kBF16)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, now.b[j]), __builtin_bit_cast(bf16x8_t, now.a[i]),
+            acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8_t, now.b[j]), __builtin_bit_cast(f16x8_t, now.a[i]),
+            acc[i][j], 0, 0, 0);
+      if constexpr (M < NR) read_job<M>(cur, fa, 1, next);
+      if constexpr (M < NL) load_job<M>(ab, bb, la, wave, ls);
+      __builtin_amdgcn_sched_barrier(0);
+      emit0<M + 1, LD>(cur, fa, now, next, acc, ab, bb, la, wave, ls);
+    } else {
+      emit0_rest<NM, LD>(cur, fa, next, ab, bb, la, wave, ls);
+    }
+  }
+  template <int X, bool LD>
+  __device__ __forceinline__ static void emit0_rest(const uint8_t* cur, const FragAddr& fa,
+                                                    Frags& next, const char* ab, const char* bb,
+                                                    const LoadAddr& la, int wave, uint32_t ls) {
+    constexpr int NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
+    if constexpr (X < NR || X < NL) {
+      if constexpr (X < NR) read_job<X>(cur, fa, 1, next);
+      if constexpr (X < NL) load_job<X>(ab, bb, la, wave, ls);
+      emit0_rest<X + 1, LD>(cur, fa, next, ab, bb, la, wave, ls);
+    }
+  }
+
   // MFMA step s of the phase in `cur` on fragments `now`, reading step s+1 into `next`.
   __device__ __forceinline__ static void step(const uint8_t* cur, const FragAddr& fa, int s,
                                               const Frags& now, Frags& next,
@@ -464,12 +568,12 @@ struct GemmTile {
     int m0, n0, kt0, ktiles;
   };
 
-  __device__ __forceinline__ static void issue_prologue(const GemmProblem& P, int m0, int kt0,
+  __device__ __forceinline__ static void issue_prologue(const Src& S, int m0, int kt0,
                                                         int ktiles, int wave, const LoadAddr& la,
                                                         uint8_t* smem) {
 #pragma unroll
     for (int t = 0; t < CFG::STAGES - 1; ++t)
-      if (t < ktiles) issue_loads(P, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
+      if (t < ktiles) issue_loads(S, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
   }
 
   // `pre`: this tile's prologue was issued by the previous tile (before its
@@ -485,13 +589,14 @@ struct GemmTile {
     // every wave issues the same number of loads per phase, so one vmcnt bound fits all
     static_assert(CFG::QA % CFG::NW == 0 && CFG::QB % CFG::NW == 0, "even load slots");
     constexpr int QW = CFG::QAW + CFG::QBW;  // loads this wave issues per phase
+    const Src src = src_of(P);
     LoadAddr la;
     load_addr(P, m0, n0, wave, lane, la);
     int flane = lane;  // opaque: fragment offsets are rebuilt per tile, not held across it
     asm volatile("" : "+v"(flane));
     FragAddr fa;
     frag_addr(wm, wn, flane, fa);
-    if (!pre) issue_prologue(P, m0, kt0, ktiles, wave, la, smem);
+    if (!pre) issue_prologue(src, m0, kt0, ktiles, wave, la, smem);
     // phase 0 ready: at most the later prologue phases still in flight (all of
     // them when stores were issued after them)
     wait_phase<(S - 2) * QW>(!pre && ktiles >= S - 1);
@@ -499,36 +604,60 @@ struct GemmTile {
     Frags f0, f1;
     read_frags(smem, fa, 0, f0);
     int st = 0;  // stage of phase kt
-    for (int kt = 0; kt < ktiles; ++kt) {
-      FGEMM_PHASE_FENCE();
-      const uint8_t* cur = smem + st * CFG::LDS_STAGE;
-      int st_ahead = st + S - 1;
-      if (st_ahead >= S) st_ahead -= S;
-      if (kt + S - 1 < ktiles)
-        issue_loads(P, m0, kt0 + kt + S - 1, wave, la, smem + st_ahead * CFG::LDS_STAGE);
-      FGEMM_PHASE_FENCE();
-      // all but the last step; the last step's fragments end up in f1
-      step(cur, fa, 0, f0, f1, acc);
-      if constexpr (CFG::STEPS == 4) {
-        step(cur, fa, 1, f1, f0, acc);
-        step(cur, fa, 2, f0, f1, acc);
-      }
-      // phase kt+1 must have landed; loads of later phases may still fly
-      wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
-      __syncthreads();
-      const int st_next = st + 1 == S ? 0 : st + 1;
-      if (kt + 1 < ktiles) {
-        read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
-      } else if (chain) {
-        LoadAddr ln;  // computed here, where the next fragments are dead
-        load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);
-        issue_prologue(Pn, nx.m0, nx.kt0, nx.ktiles, wave, ln, smem);
-      }
-      mfma_step(f1, acc);
-      interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
-      st = st_next;
-    }
+    // phases that still load a later phase, then the last S-1 that do not: two
+    // straight loop bodies
+    int kt = 0;
+    for (; kt + S - 1 < ktiles; ++kt)
+      phase<true>(src, m0, smem, wave, lane, fa, la, kt0, kt, ktiles, st, chain, Pn, nx, f0, f1,
+                  acc);
+    for (; kt < ktiles; ++kt)
+      phase<false>(src, m0, smem, wave, lane, fa, la, kt0, kt, ktiles, st, chain, Pn, nx, f0, f1,
+                   acc);
     FGEMM_PHASE_FENCE();
+  }
+
+  // Phase kt of the ring (stage st): step 0 with the loads of phase kt+S-1 when LD,
+  // the middle steps, the wait for phase kt+1 and the barrier, then the last step
+  // under the first reads of phase kt+1 (or, after the last phase, the next tile's
+  // first loads).
+  template <bool LD>
+  __device__ __forceinline__ static void phase(const Src& src, int m0, uint8_t* smem, int wave,
+                                               int lane, const FragAddr& fa, const LoadAddr& la,
+                                               int kt0, int kt, int ktiles, int& st, bool chain,
+                                               const GemmProblem& Pn, const Next& nx, Frags& f0,
+                                               Frags& f1, f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+    constexpr int S = CFG::STAGES;
+    constexpr int QW = CFG::QAW + CFG::QBW;
+    FGEMM_PHASE_FENCE();
+    const uint8_t* cur = smem + st * CFG::LDS_STAGE;
+    int st_ahead = st + S - 1;
+    if (st_ahead >= S) st_ahead -= S;
+    const int kl = kt0 + kt + S - 1;
+    const char* ab = LD ? uniform_ptr(a_base(src, m0, kl)) : nullptr;
+    const char* bb = LD ? uniform_ptr(b_base(src, kl)) : nullptr;
+    const uint32_t ls = lds_addr(smem + st_ahead * CFG::LDS_STAGE);
+    emit0<0, LD>(cur, fa, f0, f1, acc, ab, bb, la, wave, ls);
+    FGEMM_PHASE_FENCE();
+    // the other steps but the last; the last step's fragments end up in f1
+    if constexpr (CFG::STEPS == 4) {
+      step(cur, fa, 1, f1, f0, acc);
+      step(cur, fa, 2, f0, f1, acc);
+    }
+    // phase kt+1 must have landed; loads of later phases may still fly
+    if constexpr (LD) wait_vmcnt<(S - 2) * QW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const int st_next = st + 1 == S ? 0 : st + 1;
+    if (kt + 1 < ktiles) {
+      read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
+    } else if (chain) {
+      LoadAddr ln;  // computed here, where the next fragments are dead
+      load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);
+      issue_prologue(src_of(Pn), nx.m0, nx.kt0, nx.ktiles, wave, ln, smem);
+    }
+    mfma_step(f1, acc);
+    interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
+    st = st_next;
   }
 
   // Edge tiles: bounds-tested register loads into two stages, one barrier a phase.
