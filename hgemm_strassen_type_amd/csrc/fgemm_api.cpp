@@ -396,9 +396,11 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   if (run.sub_tile != 0 && run.sub_tile != 1) run.sub_tile = 0;
   run.in_dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  unsigned* maxbits = reinterpret_cast<unsigned*>(base);
+  static_assert(kScaleHeaderBytes >= 256 + 2 * kMaxPartials * sizeof(float), "header");
   run.scale_a = reinterpret_cast<float*>(base + 64);
   run.scale_b = reinterpret_cast<float*>(base + 128);
+  float* part_a = reinterpret_cast<float*>(base + 256);
+  float* part_b = part_a + kMaxPartials;
   size_t off = kScaleHeaderBytes;
   for (int l = 1; l <= plan.depth; ++l) {
     const int64_t m = c.M >> l, k = c.K >> l, n = c.N >> l;
@@ -411,15 +413,15 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   }
   // power-of-two scales keeping every fp16 sum in range: at most 4^depth terms
   const float target = plan.depth == 1 ? 8192.f : 2048.f;
-  hipError_t e = launch_fill_u32(maxbits, 0u, 2, c.stream);
-  if (e == hipSuccess)
-    e = launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
-                      run.in_dtype, maxbits, c.stream);
+  int na = 0, nb = 0;
+  hipError_t e =
+      launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
+                    run.in_dtype, part_a, &na, c.stream);
   if (e == hipSuccess)
     e = launch_maxabs(c.B, c.ldb, c.tb == FGEMM_OP_T ? c.N : c.K, c.tb == FGEMM_OP_T ? c.K : c.N,
-                      run.in_dtype, maxbits + 1, c.stream);
-  if (e == hipSuccess) e = launch_scale_from_max(maxbits, target, run.scale_a, c.stream);
-  if (e == hipSuccess) e = launch_scale_from_max(maxbits + 1, target, run.scale_b, c.stream);
+                      run.in_dtype, part_b, &nb, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(part_a, na, target, run.scale_a, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(part_b, nb, target, run.scale_b, c.stream);
   if (e != hipSuccess) return FGEMM_ERR_HIP;
   BlockedOperand L{c.A, c.lda, c.ta == FGEMM_OP_T, run.in_dtype, 0};
   BlockedOperand R{c.B, c.ldb, c.tb == FGEMM_OP_T, run.in_dtype, 0};

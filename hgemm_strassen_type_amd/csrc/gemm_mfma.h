@@ -32,6 +32,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace fgemm {
@@ -39,6 +41,7 @@ namespace fgemm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Native vectors, not HIP's uint4/uint2 structs: struct copies are lowered through
 // private memory and lose their place in the schedule.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -86,20 +89,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // --------------------------------------------------------------- configuration
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1,
+          int MI_ = 32>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int OCC = OCC_;  // workgroups per CU the register budget is sized for
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int STEPS = BK / 16;  // MFMA k-steps per phase
+  // MFMA shape: MI x MI output blocks, KSTEP-deep (v_mfma_f32_32x32x16 or _16x16x32);
+  // either way a lane feeds 8 consecutive k of one row/column per operand and holds
+  // ACC accumulators, in groups of 4 consecutive output columns of one row.
+  static constexpr int MI = MI_;
+  static constexpr int KSTEP = MI == 32 ? 16 : 32;
+  static constexpr int ACC = MI * MI / 64;
+  using AccT = typename std::conditional<MI == 32, f32x16_t, f32x4_t>::type;
+  static constexpr int FM = WM / MI, FN = WN / MI;
+  static constexpr int STEPS = BK / KSTEP;  // MFMA k-steps per phase
+  static_assert(MI == 32 || MI == 16, "MFMA shape");
+  static_assert(STEPS == 2 || STEPS == 4, "k-steps per phase");
   static constexpr int LDS_A = BM * BK * 2, LDS_B = BN * BK * 2;
   static constexpr int LDS_STAGE = LDS_A + LDS_B;
   static constexpr int QA = LDS_A / 1024, QB = LDS_B / 1024;  // 1 KB load slots per phase
   static constexpr int QAW = (QA + NW - 1) / NW, QBW = (QB + NW - 1) / NW;  // per wave
-  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0, "wave tile: whole MFMA blocks, 32-row bands");
   static_assert(BK == 32 || BK == 64, "phase depth");
   static_assert(LDS_A % 1024 == 0 && LDS_B % 1024 == 0, "1 KB load slots");
   // Epilogue staging: each wave transposes 32 x EPI_CW fp32 blocks through its own
@@ -123,11 +136,13 @@ __device__ __forceinline__ int swz_k(int r) {
   return BK == 32 ? ((r >> 2) & 3) : (((r >> 1) ^ (r >> 4)) & 7);
 }
 // M/N-contiguous operand: BK rows of R values (R*2 bytes), chunk c of row k at
-// chunk c ^ swz_mn(k); a transposed read takes rows k..k+3 (k % 4 == 0) of four
-// consecutive chunks per 16 lanes.
+// chunk c ^ swz_mn(k); a transposed read takes rows k..k+3 (k % 4 == 0) of two
+// consecutive chunks per 16 lanes, and the 32 lanes served together read either
+// 4 more chunks of the same rows (32x32 blocks) or the same 2 chunks of rows
+// k+8..k+11 (16x16 blocks): bit 3 of k moves those by 2 chunks.
 template <int R>
 __device__ __forceinline__ int swz_mn(int k) {
-  return (4 * (k & 3)) & (R / 8 - 1);
+  return (4 * (k & 3) + 2 * ((k >> 3) & 1)) & (R / 8 - 1);
 }
 
 // Column map of the B tile.  Plain GEMM: tile column c is global column n0 + c.
@@ -161,6 +176,7 @@ template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 struct GemmTile {
   static constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
   static constexpr bool SWIGLU = EPI == kEpiSwiGLU;
+  using Acc = typename CFG::AccT;
   static constexpr int OUT_BN = SWIGLU ? BN / 2 : BN;
 
   // ============================================================ load slots
@@ -359,7 +375,8 @@ struct GemmTile {
   };
 
   // Per-lane LDS byte offsets of the fragments at MFMA step 0 (stage-relative).
-  //   K-contiguous: row r = base + 32f + (lane & 31), chunk 2s + (lane >> 5).
+  // A lane feeds row (lane % MI) of its fragment with k slot lane / MI (8 k each).
+  //   K-contiguous: row r = base + MI*f + (lane % MI), chunk (KSTEP/8)*s + lane/MI.
   //   M/N-contiguous: two transposed 8-byte reads per fragment (k 0-3 and 4-7 of
   //   the lane's 8-k slot); in a 16-lane group, lane j reads row kb + j/4 at the
   //   four columns from 4*(j%4) of the group's 16 columns.
@@ -373,13 +390,15 @@ struct GemmTile {
                                                    int (&out)[F]) {
 #pragma unroll
     for (int f = 0; f < F; ++f) {
+      constexpr int MI = CFG::MI;
       if (KCONTIG) {
-        int r = wbase + f * 32 + (lane & 31);
-        out[f] = base_off + r * (BK * 2) + (((lane >> 5) ^ swz_k<BK>(r)) << 4);
+        int r = wbase + f * MI + lane % MI;
+        out[f] = base_off + r * (BK * 2) + (((lane / MI) ^ swz_k<BK>(r)) << 4);
       } else {
+        // 16-lane group g: k slot g / (MI/16), columns 16 * (g % (MI/16)) ..
         int g = lane >> 4, j = lane & 15;
-        int kr = 8 * (g >> 1) + (j >> 2);              // row within the k-step
-        int col = wbase + f * 32 + 16 * (g & 1) + 4 * (j & 3);
+        int kr = 8 * (g / (MI / 16)) + (j >> 2);  // row within the k-step
+        int col = wbase + f * MI + 16 * (g % (MI / 16)) + 4 * (j & 3);
         out[f] = base_off + kr * (R * 2) + (((col >> 3) ^ swz_mn<R>(kr)) << 4) + (col & 7) * 2;
       }
     }
@@ -390,12 +409,12 @@ struct GemmTile {
     frag_base<BKC, BN, CFG::FN>(wn * CFG::WN, lane, CFG::LDS_A, fa.b);
   }
 
-  // Offset of step s from step 0.  K-contiguous: chunk 2s + h, and 2s only flips
-  // bits 5 and up of the chunk offset inside the row, so it is an XOR.  M/N-contiguous:
-  // 16 rows further down (the swizzle depends on k mod 4 only).
+  // Offset of step s from step 0.  K-contiguous: chunk (KSTEP/8)*s + slot, and the
+  // step only flips chunk bits above the slot's, so it is an XOR of 2*KSTEP*s bytes.
+  // M/N-contiguous: KSTEP rows further down (the swizzle depends on k mod 16 only).
   template <bool KCONTIG, int R>
   __device__ __forceinline__ static int step_addr(int base, int s) {
-    return KCONTIG ? (base ^ (32 * s)) : base + s * 16 * (R * 2);
+    return KCONTIG ? (base ^ (2 * CFG::KSTEP * s)) : base + s * CFG::KSTEP * (R * 2);
   }
 
   template <bool KCONTIG, int R>
@@ -421,22 +440,31 @@ struct GemmTile {
       fr.b[f] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s));
   }
 
-  __device__ __forceinline__ static void mfma_step(const Frags& fr,
-                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+  // One MFMA: the B fragment first, so that a lane's accumulators are consecutive
+  // columns of one output row.
+  __device__ __forceinline__ static Acc mfma(const v4u& b, const v4u& a, const Acc& c) {
+    if constexpr (CFG::MI == 32) {
+      if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                       __builtin_bit_cast(bf16x8_t, a), c, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, b),
+                                                      __builtin_bit_cast(f16x8_t, a), c, 0, 0, 0);
+    } else {
+      if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                       __builtin_bit_cast(bf16x8_t, a), c, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, b),
+                                                      __builtin_bit_cast(f16x8_t, a), c, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ static void mfma_step(const Frags& fr, Acc (&acc)[CFG::FM][CFG::FN]) {
 #pragma unroll
     for (int i = 0; i < CFG::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < CFG::FN; ++j) {
-        if constexpr (DT == kBF16) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, fr.b[j]), __builtin_bit_cast(bf16x8_t, fr.a[i]),
-              acc[i][j], 0, 0, 0);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8_t, fr.b[j]), __builtin_bit_cast(f16x8_t, fr.a[i]),
-              acc[i][j], 0, 0, 0);
-        }
-      }
+      for (int j = 0; j < CFG::FN; ++j) acc[i][j] = mfma(fr.b[j], fr.a[i], acc[i][j]);
   }
 
   // one MFMA, then one instruction of OTHER_MASK, while both last (I counts MFMAs)
@@ -507,20 +535,13 @@ struct GemmTile {
   template <int M, bool LD>
   __device__ __forceinline__ static void emit0(const uint8_t* cur, const FragAddr& fa,
                                                const Frags& now, Frags& next,
-                                               f32x16_t (&acc)[CFG::FM][CFG::FN],
+                                               Acc (&acc)[CFG::FM][CFG::FN],
                                                const char* ab, const char* bb,
                                                const LoadAddr& la, int wave, uint32_t ls) {
     constexpr int NM = kMfmaPerStep, NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
     if constexpr (M < NM) {
       constexpr int i = M / CFG::FN, j = M % CFG::FN;
-      if constexpr (DT == kBF16)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, now.b[j]), __builtin_bit_cast(bf16x8_t, now.a[i]),
-            acc[i][j], 0, 0, 0);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(f16x8_t, now.b[j]), __builtin_bit_cast(f16x8_t, now.a[i]),
-            acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma(now.b[j], now.a[i], acc[i][j]);
       if constexpr (M < NR) read_job<M>(cur, fa, 1, next);
       if constexpr (M < NL) load_job<M>(ab, bb, la, wave, ls);
       __builtin_amdgcn_sched_barrier(0);
@@ -544,7 +565,7 @@ struct GemmTile {
   // MFMA step s of the phase in `cur` on fragments `now`, reading step s+1 into `next`.
   __device__ __forceinline__ static void step(const uint8_t* cur, const FragAddr& fa, int s,
                                               const Frags& now, Frags& next,
-                                              f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+                                              Acc (&acc)[CFG::FM][CFG::FN]) {
     read_frags(cur, fa, s + 1, next);
     mfma_step(now, acc);
     interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
@@ -584,7 +605,7 @@ struct GemmTile {
                                                    int lane, int kt0, int ktiles, bool pre,
                                                    bool chain, const GemmProblem& Pn,
                                                    const Next& nx,
-                                                   f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+                                                   Acc (&acc)[CFG::FM][CFG::FN]) {
     constexpr int S = CFG::STAGES;
     // every wave issues the same number of loads per phase, so one vmcnt bound fits all
     static_assert(CFG::QA % CFG::NW == 0 && CFG::QB % CFG::NW == 0, "even load slots");
@@ -625,7 +646,7 @@ struct GemmTile {
                                                int lane, const FragAddr& fa, const LoadAddr& la,
                                                int kt0, int kt, int ktiles, int& st, bool chain,
                                                const GemmProblem& Pn, const Next& nx, Frags& f0,
-                                               Frags& f1, f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+                                               Frags& f1, Acc (&acc)[CFG::FM][CFG::FN]) {
     constexpr int S = CFG::STAGES;
     constexpr int QW = CFG::QAW + CFG::QBW;
     FGEMM_PHASE_FENCE();
@@ -664,7 +685,7 @@ struct GemmTile {
   __device__ __forceinline__ static void loop_checked(const GemmProblem& P, int m0, int n0,
                                                       uint8_t* smem, int wave, int wm, int wn,
                                                       int lane_in, int kt0, int ktiles,
-                                                      f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+                                                      Acc (&acc)[CFG::FM][CFG::FN]) {
     int lane = lane_in;  // opaque: per-tile recomputation instead of hoisted registers
     asm volatile("" : "+v"(lane));
     FragAddr fa;
@@ -698,18 +719,22 @@ struct GemmTile {
   __device__ __forceinline__ static void epilogue_rows(const GemmProblem& P, void* Cout, int m0,
                                                        int n0, int tn, int wave, int wm, int wn,
                                                        int lane_in, uint8_t* smem,
-                                                       f32x16_t (&acc)[CFG::FM][CFG::FN]) {
+                                                       Acc (&acc)[CFG::FM][CFG::FN]) {
     int lane = lane_in;  // opaque: recomputed per tile rather than held across the loop
     asm volatile("" : "+v"(lane));
     constexpr int CW = CFG::EPI_CW;
     constexpr int NCH = CW / 4;          // 16-byte chunks per staged row
     constexpr int LPR = NCH / 2;         // lanes per row on the way out (8 columns each)
     constexpr int RPT = 64 / LPR;        // rows per pass
-    constexpr int JC = CW / 32;          // accumulator blocks per staged block
+    constexpr int MI = CFG::MI;
+    constexpr int JC = CW / MI;          // accumulator block columns per staged block
+    constexpr int BPB = 32 / MI;         // accumulator block rows per 32-row band
+    constexpr int NB = CFG::WM / 32;     // 32-row bands of the wave tile
+    constexpr int G4 = CFG::ACC / 4;     // groups of 4 columns a lane holds per block
     uint8_t* region = smem + CFG::EPI_OFF + wave * CFG::EPI_WAVE_BYTES;
     // chunk swizzle: 16 consecutive rows of one logical chunk hit distinct banks
     auto swz = [](int r) { return NCH == 16 ? (r & 15) : ((r >> 1) & 7); };
-    const int lr = lane & 31, h = lane >> 5;
+    const int lr = lane % MI, lc = lane / MI;  // lane's row and column slot in a block
     const int orow = lane / LPR, oc = lane % LPR;
     const bool use_beta = EPI == kEpiStore16 && (P.flags & kFlagBeta) != 0;
     const bool use_bias = EPI == kEpiStore16 && (P.flags & kFlagBias) != 0;
@@ -719,12 +744,12 @@ struct GemmTile {
     // beta*C: every whole 8-column piece of the wave's tile is requested up front so
     // that the reads overlap the staging instead of waiting once per piece
     constexpr int NPASS = 32 / RPT, NJC = CFG::WN / CW;
-    v4u cpre[EPI == kEpiStore16 ? CFG::FM : 1][EPI == kEpiStore16 ? NJC : 1]
+    v4u cpre[EPI == kEpiStore16 ? NB : 1][EPI == kEpiStore16 ? NJC : 1]
             [EPI == kEpiStore16 ? NPASS : 1];
     if constexpr (EPI == kEpiStore16) {
       if (use_beta) {
 #pragma unroll
-        for (int i = 0; i < CFG::FM; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int jc = 0; jc < NJC; ++jc)
 #pragma unroll
@@ -738,7 +763,7 @@ struct GemmTile {
       }
     }
 #pragma unroll
-    for (int i = 0; i < CFG::FM; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int row_base = m0 + wm * CFG::WM + i * 32;
       float ss[32 / RPT];
 #pragma unroll
@@ -746,16 +771,21 @@ struct GemmTile {
 #pragma unroll
       for (int jc = 0; jc < CFG::WN / CW; ++jc) {
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj)
+        for (int ib = 0; ib < BPB; ++ib)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x16_t& a = acc[i][jc * JC + jj];
-            const float sc = EPI == kEpiStore16 ? P.alpha : 1.f;
-            v4f v = v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-            if (EPI == kEpiStore16) v = v * sc;
-            const int c = jj * 8 + 2 * q + h;
-            *reinterpret_cast<v4f*>(region + lr * (CW * 4) + ((c ^ swz(lr)) << 4)) = v;
-          }
+          for (int jj = 0; jj < JC; ++jj)
+#pragma unroll
+            for (int g = 0; g < G4; ++g) {
+              const Acc& a = acc[i * BPB + ib][jc * JC + jj];
+              const float sc = EPI == kEpiStore16 ? P.alpha : 1.f;
+              v4f v = v4f{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+              if (EPI == kEpiStore16) v = v * sc;
+              // row ib*MI + lr of the band; 16-byte chunk of columns
+              // jj*MI + g*(256/MI) + 4*lc
+              const int r = ib * MI + lr;
+              const int c = jj * (MI / 4) + g * (64 / MI) + lc;
+              *reinterpret_cast<v4f*>(region + r * (CW * 4) + ((c ^ swz(r)) << 4)) = v;
+            }
         const int col = n0 + wn * CFG::WN + jc * CW + 8 * oc;
         const int nv = P.N - col;
 #pragma unroll
@@ -836,23 +866,24 @@ struct GemmTile {
   }
 
 
-  // Lane layout of acc[i][j][4q+s]: row = wave row base + 32i + (lane & 31),
-  // column = wave column base + 32j + 8q + 4*(lane >> 5) + s.
+  // Lane layout of acc[i][j][4g+s]: row = wave row base + MI*i + lane % MI,
+  // column = wave column base + MI*j + g*(256/MI) + 4*(lane / MI) + s.
   __device__ __forceinline__ static void epilogue(const GemmProblem& P, void* Cout, int m0,
                                                   int n0, int tn, int wm, int wn, int lane,
-                                                  f32x16_t (&acc)[CFG::FM][CFG::FN]) {
-    const int lr = lane & 31, h = lane >> 5;
+                                                  Acc (&acc)[CFG::FM][CFG::FN]) {
+    constexpr int MI = CFG::MI, G4 = CFG::ACC / 4;
+    const int lr = lane % MI, lc = lane / MI;
     if constexpr (EPI == kEpiStore32) {
       float* C = static_cast<float*>(Cout);
 #pragma unroll
       for (int i = 0; i < CFG::FM; ++i) {
-        int row = m0 + wm * CFG::WM + i * 32 + lr;
+        int row = m0 + wm * CFG::WM + i * MI + lr;
         if (row >= P.M) continue;
 #pragma unroll
         for (int j = 0; j < CFG::FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            int col = n0 + wn * CFG::WN + j * 32 + 8 * q + 4 * h;
+          for (int q = 0; q < G4; ++q) {
+            int col = n0 + wn * CFG::WN + j * MI + q * (256 / MI) + 4 * lc;
             float* dst = C + (int64_t)row * P.ldc + col;
             if (VEC && col + 4 <= P.N) {
               *reinterpret_cast<v4f*>(dst) = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1],
@@ -875,14 +906,14 @@ struct GemmTile {
       const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
 #pragma unroll
       for (int i = 0; i < CFG::FM; ++i) {
-        int row = m0 + wm * CFG::WM + i * 32 + lr;
+        int row = m0 + wm * CFG::WM + i * MI + lr;
         bool rv = row < P.M;
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < CFG::FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            int col = n0 + wn * CFG::WN + j * 32 + 8 * q + 4 * h;
+          for (int q = 0; q < G4; ++q) {
+            int col = n0 + wn * CFG::WN + j * MI + q * (256 / MI) + 4 * lc;
             int nv = P.N - col;
             if (!rv || nv <= 0) continue;
             float v[4];
@@ -921,8 +952,9 @@ struct GemmTile {
             }
           }
         if (use_ss) {
-          ss += __shfl_xor(ss, 32);
-          if (h == 0 && rv) P.ss_partial[(int64_t)(tn * CFG::WAVES_N + wn) * P.M + row] = ss;
+#pragma unroll
+          for (int d = MI; d < 64; d <<= 1) ss += __shfl_xor(ss, d);
+          if (lc == 0 && rv) P.ss_partial[(int64_t)(tn * CFG::WAVES_N + wn) * P.M + row] = ss;
         }
       }
     } else {  // kEpiSwiGLU: output tile is BM x BN/2
@@ -930,14 +962,14 @@ struct GemmTile {
       const int out0 = n0 + wn * (CFG::WN / 2);
 #pragma unroll
       for (int i = 0; i < CFG::FM; ++i) {
-        int row = m0 + wm * CFG::WM + i * 32 + lr;
+        int row = m0 + wm * CFG::WM + i * MI + lr;
         if (row >= P.M) continue;
         float r = rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps) * P.alpha;
 #pragma unroll
         for (int j = 0; j < HF; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            int col = out0 + j * 32 + 8 * q + 4 * h;
+          for (int q = 0; q < G4; ++q) {
+            int col = out0 + j * MI + q * (256 / MI) + 4 * lc;
             int nv = P.N - col;
             if (nv <= 0) continue;
             float v[4];
@@ -1051,13 +1083,13 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
       have_next = work_of<T, CFG, EPI, VEC, AK, BKC>(batch, item, splits, &nxt);
     const GemmProblem& P = batch.p[cur.z];
 
-    f32x16_t acc[CFG::FM][CFG::FN];
+    typename T::Acc acc[CFG::FM][CFG::FN];
 #pragma unroll
     for (int i = 0; i < CFG::FM; ++i)
 #pragma unroll
       for (int j = 0; j < CFG::FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int e = 0; e < CFG::ACC; ++e) acc[i][j][e] = 0.f;
 
     bool issued = false;
     if (cur.ktiles > 0) {
@@ -1092,9 +1124,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
 }
 
 // ------------------------------------------------------------------ launching
-// 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages; measured on the
-// 8192^3 bf16 shapes against 4-wave 128x128 waves, BK = 32 with 3-4 stages, and
-// 256x128 / 128x256 tiles at two workgroups per CU.
+// 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages, 32x32x16 MFMAs;
+// measured on the 8192^3 bf16 shapes against 4-wave 128x128 waves, 2x4 waves of
+// 128x64, 16x16x32 MFMAs, BK = 32 with 3-5 stages, and 256x128 / 128x256 tiles at
+// two workgroups per CU.
 using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;

@@ -91,10 +91,13 @@ struct BlockedOperand {
   int scaled;         // 1: values already carry the scale (fp16 temporaries)
 };
 
+// max |x| of a stored rows x cols matrix as per-workgroup partial maxima (at most
+// kMaxPartials of them; *count receives how many), and the power-of-two scale
+// 2^floor(log2(target / max)) reduced from them.
+constexpr int kMaxPartials = 4096;
 hipError_t launch_maxabs(const void* X, int64_t ld, int64_t rows, int64_t cols, int dtype,
-                         unsigned* max_bits, hipStream_t stream);
-hipError_t launch_fill_u32(unsigned* p, unsigned value, int64_t n, hipStream_t stream);
-hipError_t launch_scale_from_max(const unsigned* max_bits, float target, float* scale,
+                         float* partial, int* count, hipStream_t stream);
+hipError_t launch_scale_from_max(const float* partial, int count, float target, float* scale,
                                  hipStream_t stream);
 
 // Pre-add: from the four sub-blocks of `src` (logical rows x cols), write the seven

@@ -43,8 +43,11 @@ void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
   // dense 16-bit MFMA: 4 SIMDs x 1024 FLOP per clock per CU on gfx950
   m->peak_tflops = cus * 4096.0 * clock_ghz * 1e9 / 1e12;
   m->hbm_gbps = 8000.0;
-  m->eta_mfma = 0.70;
-  m->eta_hbm = 0.80;
+  // measured on MI355X (bf16 8192^3 and LLM shapes, 256x256 tile): ~1.2-1.26
+  // PFLOP/s against 2.5 at the nominal clock (the chip holds ~1.4-1.7 GHz under
+  // this load); the streaming add kernels move ~5.2-5.3 TB/s
+  m->eta_mfma = 0.49;
+  m->eta_hbm = 0.66;
   m->launch_us = 4.0;
   m->max_workspace_bytes = 16.0 * (1ull << 30);
 }
@@ -124,25 +127,29 @@ double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K
   double t = 0, launches = 0;
   // max|A|, max|B| for the fp16 scales
   t += ((double)M * K + (double)K * N) * 2.0 / bw;
-  launches += 5;  // fills, two max passes, two scale kernels
+  launches += 4;  // two max passes, two scale kernels
   double instances = 1;  // how many problems of this level run
   for (int l = 1; l <= depth; ++l) {
     const double m = (double)(M >> l), k = (double)(K >> l), n = (double)(N >> l);
     const double pre = 4 * m * k * 2 + ns * m * k * 2 + 4 * k * n * 2 + ns * k * n * 2;
-    const double pwrite = 7 * m * n * 4;            // products written by the GEMMs
+    // (the fp32 products are written by the MFMA-bound sub-product kernels, under
+    // their compute time)
     const double post = 7 * m * n * 4 + 4 * m * n * (l == 1 ? 2.0 : 4.0) +
                         (l == 1 && beta ? 4 * m * n * 2.0 : 0.0);
-    t += instances * (pre + pwrite + post) / bw;
+    t += instances * (pre + post) / bw;
     launches += instances * 3;
     instances *= 7;
   }
-  // sub-products: 7^d problems of the deepest size, seven per launch
+  // sub-products: 7^d problems of the deepest size, seven per launch.  They run on
+  // fp16 operands with fp32 outputs, measured at ~0.93 of the bf16 rate of the
+  // same kernel (the chip clocks lower on fp16 MFMA work under its power limit).
+  constexpr double kProductRate = 0.93;
   const int64_t m = M >> depth, n = N >> depth, k = K >> depth;
   double tp;
   int tile = best_tile(md, m, n, k, 0, 7, 2.0, 4.0, 0, &tp, 1);
   if (sub_tile) *sub_tile = tile;
   const double batches = instances / 7;
-  t += batches * (tp - md.launch_us) * 1e-6;
+  t += batches * (tp - md.launch_us) / kProductRate * 1e-6;
   launches += batches;
   return t * 1e6 + launches * md.launch_us;
 }

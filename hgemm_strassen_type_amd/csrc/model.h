@@ -17,7 +17,8 @@ struct TileInfo {
 
 constexpr int kNumTiles = 4;
 extern const TileInfo kTiles[kNumTiles];
-constexpr size_t kScaleHeaderBytes = 256;
+// Strassen workspace header: the two scales, then the partial maxima of A and B.
+constexpr size_t kScaleHeaderBytes = 256 + 2 * 4096 * 4;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 int64_t ceil_div(int64_t a, int64_t b);

@@ -18,8 +18,11 @@
 // from max|x| so that every sum stays inside the fp16 range; the product of the two
 // scales is divided out in the final post-add.  Products accumulate in fp32.
 //
-// All kernels stream 16-byte vectors per lane with grid-stride loops over the
-// sub-block; they are bound by HBM bandwidth.
+// All kernels are bound by HBM bandwidth.  They stream 16-byte vectors on a 2-D
+// grid: blockIdx.x walks 256 consecutive 16-byte chunks of a row (coalesced),
+// blockIdx.y rows (with a stride loop when there are more rows than grid rows), so
+// no lane divides an index, and every lane has several independent loads in
+// flight (the four sub-blocks, the seven products, or four rows).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -54,40 +57,63 @@ __device__ __forceinline__ uint4 pack8_f16(const float* f) {
 }
 
 // ------------------------------------------------------------------ max |x|
-__global__ void fill_u32_kernel(unsigned* p, unsigned v, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
 
-// max |x| over a stored rows x cols matrix (leading dimension ld), as the bit
-// pattern of a non-negative float (monotone as an unsigned integer).
+// max |x| over a stored rows x cols matrix (leading dimension ld): every
+// workgroup writes the max of its share to partial[workgroup] (no atomics; the
+// scale kernel reduces the partials).  A lane reads kMaxRows rows of its chunk per
+// round, independently.
+constexpr int kMaxRows = 4;
+
 __global__ void maxabs_kernel(const uint16_t* __restrict__ X, int64_t ld, int64_t rows,
-                              int64_t cols, int dt, unsigned* max_bits) {
+                              int64_t cols, int dt, int vec, float* partial) {
   float m = 0.f;
   const int64_t chunks = (cols + 7) / 8;
-  const int64_t total = rows * chunks;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = t / chunks, c = (t - r * chunks) * 8;
-    const uint16_t* p = X + r * ld + c;
-    if (c + 8 <= cols && ((ld & 7) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0)) {
-      float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(p), dt, f);
+  for (int64_t cx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; cx < chunks;
+       cx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = cx * 8;
+    const bool full = vec && c + 8 <= cols;
+    for (int64_t r0 = (int64_t)blockIdx.y * kMaxRows; r0 < rows;
+         r0 += (int64_t)gridDim.y * kMaxRows) {
+      if (full && r0 + kMaxRows <= rows) {
+        uint4 v[kMaxRows];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
-    } else {
-      for (int e = 0; e < 8 && c + e < cols; ++e) m = fmaxf(m, fabsf(h2f(p[e], dt)));
+        for (int u = 0; u < kMaxRows; ++u)
+          v[u] = *reinterpret_cast<const uint4*>(X + (r0 + u) * ld + c);
+#pragma unroll
+        for (int u = 0; u < kMaxRows; ++u) {
+          float f[8];
+          unpack8(v[u], dt, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+        }
+      } else {
+        for (int64_t r = r0; r < r0 + kMaxRows && r < rows; ++r)
+          for (int e = 0; e < 8 && c + e < cols; ++e) m = fmaxf(m, fabsf(h2f(X[r * ld + c + e], dt)));
+      }
     }
   }
-  // wave reduction, then one atomic per wave
+  __shared__ float wmax[4];
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(max_bits, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    partial[blockIdx.y * gridDim.x + blockIdx.x] = b;
+  }
 }
 
-// scale = 2^floor(log2(target / max)), 1 when max is 0 or not finite.
-__global__ void scale_from_max_kernel(const unsigned* max_bits, float target, float* scale) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  float m = __uint_as_float(*max_bits);
+// scale = 2^floor(log2(target / max)) over the partial maxima, 1 when the max is
+// 0 or not finite.
+__global__ void scale_from_max_kernel(const float* partial, int count, float target,
+                                      float* scale) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < count; i += blockDim.x) m = fmaxf(m, partial[i]);
+  __shared__ float wmax[4];
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float s = 1.f;
   if (m > 0.f && isfinite(m)) {
     int e;
@@ -117,11 +143,9 @@ struct PreAddArgs {
 
 __global__ void preadd_kernel(PreAddArgs a) {
   const float s = a.scaled ? 1.f : *a.scale;
-  const int64_t chunks = a.scols / 8;
-  const int64_t total = a.srows * chunks;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = t / chunks, c = (t - r * chunks) * 8;
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (c >= a.scols) return;
+  for (int64_t r = blockIdx.y; r < a.srows; r += gridDim.y) {
     int64_t si = r * a.ld + c;
     float x11[8], x12[8], x21[8], x22[8];
     unpack8(*reinterpret_cast<const uint4*>(a.blk[0] + si), a.dt, x11);
@@ -222,13 +246,11 @@ __device__ __forceinline__ void combine(int variant, const float (&p)[7], float*
 }
 
 __global__ void postadd_kernel(PostAddKArgs a) {
-  const int64_t chunks = a.n / 4;
-  const int64_t total = a.m * chunks;
+  const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (j >= a.n) return;
   float factor = 1.f;
   if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    int64_t i = t / chunks, j = (t - i * chunks) * 4;
+  for (int64_t i = blockIdx.y; i < a.m; i += gridDim.y) {
     float p[4][7];
 #pragma unroll
     for (int q = 0; q < 7; ++q) {
@@ -277,26 +299,37 @@ int stream_grid(int64_t work_items) {
   return (int)(g < 2048 ? (g > 0 ? g : 1) : 2048);
 }
 
+// 2-D streaming grid: 256 lanes of `per_lane`-element pieces across a row, one
+// grid row per matrix row (at most 65535; the kernels loop over the rest).
+dim3 rows_grid(int64_t rows, int64_t cols, int64_t per_lane) {
+  int64_t gx = (cols / per_lane + 255) / 256;
+  int64_t gy = rows < 65535 ? rows : 65535;
+  return dim3((unsigned)(gx > 0 ? gx : 1), (unsigned)(gy > 0 ? gy : 1));
+}
+
 }  // namespace
 
-hipError_t launch_fill_u32(unsigned* p, unsigned value, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p,
-                     value, n);
-  return hipGetLastError();
-}
 
 hipError_t launch_maxabs(const void* X, int64_t ld, int64_t rows, int64_t cols, int dtype,
-                         unsigned* max_bits, hipStream_t stream) {
+                         float* partial, int* count, hipStream_t stream) {
+  *count = 0;
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  hipLaunchKernelGGL(maxabs_kernel, dim3(stream_grid(rows * ((cols + 7) / 8))), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(X), ld, rows, cols, dtype, max_bits);
+  const int64_t chunks = (cols + 7) / 8;
+  int64_t gx = (chunks + 255) / 256;
+  if (gx > kMaxPartials) gx = kMaxPartials;
+  int64_t gy = (rows + kMaxRows - 1) / kMaxRows;
+  if (gy > kMaxPartials / gx) gy = kMaxPartials / gx;
+  const int vec = (ld % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
+  hipLaunchKernelGGL(maxabs_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(X), ld, rows, cols, dtype, vec, partial);
+  *count = (int)(gx * gy);
   return hipGetLastError();
 }
 
-hipError_t launch_scale_from_max(const unsigned* max_bits, float target, float* scale,
+hipError_t launch_scale_from_max(const float* partial, int count, float target, float* scale,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(scale_from_max_kernel, dim3(1), dim3(64), 0, stream, max_bits, target, scale);
+  hipLaunchKernelGGL(scale_from_max_kernel, dim3(1), dim3(256), 0, stream, partial, count, target,
+                     scale);
   return hipGetLastError();
 }
 
@@ -321,8 +354,7 @@ hipError_t launch_preadd(const BlockedOperand& src, int64_t rows, int64_t cols, 
   a.variant = variant;
   a.side = side;
   if (a.scols % 8 || a.ld % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(preadd_kernel, dim3(stream_grid(a.srows * (a.scols / 8))), dim3(256), 0,
-                     stream, a);
+  hipLaunchKernelGGL(preadd_kernel, rows_grid(a.srows, a.scols, 8), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -343,7 +375,7 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
   a.scale_a = in.scale_a;
   a.scale_b = in.scale_b;
   if (a.n % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(postadd_kernel, dim3(stream_grid(a.m * (a.n / 4))), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(postadd_kernel, rows_grid(a.m, a.n, 4), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
