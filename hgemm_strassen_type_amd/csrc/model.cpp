@@ -28,6 +28,16 @@ double overlap(double a, double b) {
   return hi + 0.05 * lo;
 }
 
+// Bandwidth `blocks` workgroups can pull: each keeps a few tile phases in flight,
+// measured at ~50 GB/s per workgroup (112 workgroups of the 32x128 tile stream
+// 5.6 TB/s), capped by HBM.
+double stream_bw(const fgemm_model_t& md, int64_t blocks) {
+  constexpr double kWgBytesPerSec = 50e9;
+  const double hbm = md.hbm_gbps * 1e9 * md.eta_hbm;
+  const double wg = (double)blocks * kWgBytesPerSec;
+  return wg < hbm ? wg : hbm;
+}
+
 // Macro-tiles of the classical kernel and the share of the per-CU MFMA rate each
 // reaches at steady state relative to the 256x256 tile (smaller tiles re-read
 // operands more often per FLOP and hide less latency).
@@ -63,10 +73,7 @@ double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, 
   const double t_compute = waves * tile_flops / (per_cu * md.eta_mfma * t.rel_eta);
   const double bytes = count * ((double)M * K * in_bytes + (double)K * Nb * in_bytes +
                                 (double)M * N * out_bytes * (beta ? 2.0 : 1.0));
-  // streaming from HBM needs enough workgroups in flight: fewer than one per CU
-  // leaves bandwidth unused
-  const double occ = tiles < md.compute_units ? (double)tiles / md.compute_units : 1.0;
-  const double t_mem = bytes / (md.hbm_gbps * 1e9 * md.eta_hbm * occ);
+  const double t_mem = bytes / stream_bw(md, tiles);
   return overlap(t_compute, t_mem) * 1e6 + md.launch_us;
 }
 
@@ -99,9 +106,8 @@ double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int
   const double t_compute =
       waves * 2.0 * t.bm * t.bn * (double)(K / splits) / (per_cu * md.eta_mfma * t.rel_eta);
   const double bytes = (double)M * K * 2 + (double)K * N * 2 + (double)splits * M * N * 4;
-  const double occ = blocks < md.compute_units ? (double)blocks / md.compute_units : 1.0;
   const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
-  const double t_mem = bytes / (bw * occ);
+  const double t_mem = bytes / stream_bw(md, blocks);
   const double fin = ((double)splits * M * N * 4 + (double)M * N * 2 * (beta ? 2.0 : 1.0)) / bw;
   return (overlap(t_compute, t_mem) + fin) * 1e6 + 2 * md.launch_us;
 }

@@ -23,6 +23,8 @@ constexpr size_t kScaleHeaderBytes = 256 + 2 * 4096 * 4;
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 int64_t ceil_div(int64_t a, int64_t b);
 double overlap(double a, double b);
+// HBM bandwidth (bytes/s) that `blocks` concurrently streaming workgroups reach.
+double stream_bw(const fgemm_model_t& md, int64_t blocks);
 
 void model_defaults(fgemm_model_t* m, int cus, double clock_ghz);
 
