@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,10 +41,15 @@ KERNEL_SOURCES = ["hgemm_strassen_type_amd/csrc/gemm_mfma.h",
 
 
 def kernel_hash() -> str:
+    """Hash of the GEMM kernel sources' code: comments and layout do not count, so a
+    traffic record stays valid across edits that cannot change the kernel."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,13 +9,15 @@
 //
 // gfx950 mapping:
 //   - NT = 64 * WAVES_M * WAVES_N threads; each wave64 owns a (BM/WAVES_M) x
-//     (BN/WAVES_N) sub-tile of 32x32 blocks of v_mfma_f32_32x32x16_{bf16,f16};
+//     (BN/WAVES_N) sub-tile of MI x MI blocks of v_mfma_f32_32x32x16 (MI = 32) or
+//     v_mfma_f32_16x16x32 (MI = 16), bf16 or f16;
 //   - the B fragment is passed as the MFMA's first operand and the A fragment as
-//     its second, so the accumulator layout gives each lane 4 consecutive output
-//     columns of one row (8-byte stores, in-lane row statistics);
+//     its second, so the accumulator layout gives each lane groups of 4
+//     consecutive output columns of one row (in-lane row statistics);
 //   - tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane straight
 //     into LDS, no registers, asynchronous): a ring of STAGES phase buffers keeps
-//     the loads of STAGES-1 phases in flight while one phase feeds the MFMAs;
+//     the loads of STAGES-1 phases in flight while one phase feeds the MFMAs; a
+//     phase's loads are issued one after each MFMA of its first k-step;
 //   - LDS keeps each operand in its memory layout.  K-contiguous operands (A not
 //     transposed, B transposed) are rows of BK values read as one 16-byte fragment
 //     per lane; M/N-contiguous operands (A transposed, B not) are BK rows of BM or
@@ -26,8 +28,12 @@
 //     the swizzled source position, so LDS is written densely in 1 KB blocks;
 //   - edge tiles (partial M, N or K) load the same slots through registers with
 //     bounds tests and zero fill, and store them to the same LDS positions;
-//   - workgroup ids are remapped so that each XCD (ids are dealt round-robin over
-//     the 8 XCDs) works on a contiguous, L2-friendly group of tiles.
+//   - the grid is persistent (as many workgroups as the device holds), each
+//     looping over tiles; workgroups of one XCD (ids are dealt round-robin over
+//     the 8 XCDs) take a contiguous, L2-friendly run of tiles per round, and a
+//     tile's first loads are issued by its predecessor before that one's epilogue;
+//   - plain and fp32 epilogues stage the accumulators through LDS so that every
+//     lane stores (and reads beta*C as) 8 consecutive columns: whole 128-byte lines.
 #pragma once
 
 #include <hip/hip_runtime.h>
