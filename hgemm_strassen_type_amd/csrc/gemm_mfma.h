@@ -717,11 +717,12 @@ struct GemmTile {
   }
 
   // ============================================================ epilogues
-  // Row-contiguous epilogue (plain stores, 16-byte aligned operands): every 32-row,
-  // EPI_CW-column block of the wave's accumulators goes to LDS in the MFMA layout and
-  // comes back as 8 consecutive columns of one row per lane, so that beta*C is read
-  // and the result written in whole 128-byte lines.  The arithmetic per element is
-  // that of the register epilogue below: alpha*acc, + beta*C, + bias, one rounding.
+  // Row-contiguous epilogue (16-byte aligned operands): every 32-row, EPI_CW-column
+  // block of the wave's results goes to LDS in the MFMA layout and comes back as 8
+  // consecutive columns of one row per lane, so that beta*C is read and the result
+  // written in whole 128-byte lines.  The arithmetic per element is that of the
+  // register epilogue below: alpha*acc (SwiGLU: silu(g)*u of the row-scaled gate and
+  // up accumulators), + beta*C, + bias, one rounding.
   __device__ __forceinline__ static void epilogue_rows(const GemmProblem& P, void* Cout, int m0,
                                                        int n0, int tn, int wave, int wm, int wn,
                                                        int lane_in, uint8_t* smem,
@@ -742,17 +743,20 @@ struct GemmTile {
     auto swz = [](int r) { return NCH == 16 ? (r & 15) : ((r >> 1) & 7); };
     const int lr = lane % MI, lc = lane / MI;  // lane's row and column slot in a block
     const int orow = lane / LPR, oc = lane % LPR;
-    const bool use_beta = EPI == kEpiStore16 && (P.flags & kFlagBeta) != 0;
+    const bool use_beta = EPI != kEpiStore32 && (P.flags & kFlagBeta) != 0;
     const bool use_bias = EPI == kEpiStore16 && (P.flags & kFlagBias) != 0;
     const bool use_ss = EPI == kEpiStore16 && (P.flags & kFlagRowSumSq) != 0;
     const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
     const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
     // beta*C: every whole 8-column piece of the wave's tile is requested up front so
     // that the reads overlap the staging instead of waiting once per piece
-    constexpr int NPASS = 32 / RPT, NJC = CFG::WN / CW;
-    v4u cpre[EPI == kEpiStore16 ? NB : 1][EPI == kEpiStore16 ? NJC : 1]
-            [EPI == kEpiStore16 ? NPASS : 1];
-    if constexpr (EPI == kEpiStore16) {
+    constexpr int WO = SWIGLU ? CFG::WN / 2 : CFG::WN;  // output columns of the wave
+    constexpr int HF = CFG::FN / 2;                       // SwiGLU: up blocks follow gate ones
+    static_assert(WO % CW == 0, "epilogue blocks");
+    constexpr int NPASS = 32 / RPT, NJC = WO / CW;
+    constexpr bool HAS_C = EPI != kEpiStore32;
+    v4u cpre[HAS_C ? NB : 1][HAS_C ? NJC : 1][HAS_C ? NPASS : 1];
+    if constexpr (HAS_C) {
       if (use_beta) {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
@@ -761,7 +765,7 @@ struct GemmTile {
 #pragma unroll
             for (int t = 0; t < NPASS; ++t) {
               const int row = m0 + wm * CFG::WM + i * 32 + t * RPT + orow;
-              const int col = n0 + wn * CFG::WN + jc * CW + 8 * oc;
+              const int col = n0 + wn * WO + jc * CW + 8 * oc;
               cpre[i][jc][t] = v4u{0u, 0u, 0u, 0u};
               if (row < P.M && P.N - col >= 8)
                 cpre[i][jc][t] = *reinterpret_cast<const v4u*>(Cin + (int64_t)row * P.ldc + col);
@@ -775,24 +779,41 @@ struct GemmTile {
 #pragma unroll
       for (int t = 0; t < 32 / RPT; ++t) ss[t] = 0.f;
 #pragma unroll
-      for (int jc = 0; jc < CFG::WN / CW; ++jc) {
+      for (int jc = 0; jc < NJC; ++jc) {
 #pragma unroll
-        for (int ib = 0; ib < BPB; ++ib)
+        for (int ib = 0; ib < BPB; ++ib) {
+          // SwiGLU row scale of this lane's row (alpha folded in)
+          float rs = 0.f;
+          if constexpr (SWIGLU) {
+            const int row = row_base + ib * MI + lr;
+            if (row < P.M) rs = rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps) * P.alpha;
+          }
 #pragma unroll
           for (int jj = 0; jj < JC; ++jj)
 #pragma unroll
             for (int g = 0; g < G4; ++g) {
               const Acc& a = acc[i * BPB + ib][jc * JC + jj];
-              const float sc = EPI == kEpiStore16 ? P.alpha : 1.f;
-              v4f v = v4f{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-              if (EPI == kEpiStore16) v = v * sc;
+              v4f v;
+              if constexpr (SWIGLU) {
+                const Acc& ua = acc[i * BPB + ib][jc * JC + jj + HF];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float gg = rs * a[4 * g + e];
+                  const float uu = rs * ua[4 * g + e];
+                  v[e] = gg / (1.f + __expf(-gg)) * uu;
+                }
+              } else {
+                v = v4f{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+                if (EPI == kEpiStore16) v = v * P.alpha;
+              }
               // row ib*MI + lr of the band; 16-byte chunk of columns
               // jj*MI + g*(256/MI) + 4*lc
               const int r = ib * MI + lr;
               const int c = jj * (MI / 4) + g * (64 / MI) + lc;
               *reinterpret_cast<v4f*>(region + r * (CW * 4) + ((c ^ swz(r)) << 4)) = v;
             }
-        const int col = n0 + wn * CFG::WN + jc * CW + 8 * oc;
+        }
+        const int col = n0 + wn * WO + jc * CW + 8 * oc;
         const int nv = P.N - col;
 #pragma unroll
         for (int t = 0; t < 32 / RPT; ++t) {
@@ -1119,7 +1140,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
     void* Cout = P.C;
     if (EPI == kEpiStore32 && splits > 1)
       Cout = static_cast<float*>(P.C) + (int64_t)cur.y * P.M * P.ldc;
-    if constexpr (VEC && EPI != kEpiSwiGLU)
+    if constexpr (VEC)
       T::epilogue_rows(P, Cout, cur.m0, cur.n0, cur.tn, wave, wm, wn, lane, smem, acc);
     else
       T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, acc);
