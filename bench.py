@@ -97,7 +97,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the GEMM path is a "
-              "single-device kernel; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "single-device kernel with no collectives; it shards by splitting M or N across "
+              "GPUs, which is not built here.", file=sys.stderr)
         sys.exit(2)
     import torch
     from hgemm_strassen_type_amd import fgemm
