@@ -428,7 +428,24 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   return strassen_level(run, 1, L, R, c.M, c.K, c.N, nullptr, 0);
 }
 
+// Makes the handle's device current for the scope of a call and restores the
+// caller's afterwards.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int device) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != device && hipSetDevice(device) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
 fgemm_status_t execute(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return FGEMM_ERR_HIP;
   const int vec = vec_ok(c.ta, c.tb, c.N, c.A, c.lda, c.B, c.ldb, c.C, c.ldc, c.epi);
   const uint32_t flags = epi_flags(c.epi);
   fgemm_status_t st = check_plan_shape(plan, c.M, c.N, c.K, vec, flags);
@@ -510,6 +527,7 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
 fgemm_status_t fgemm_destroy(fgemm_handle_t h) {
   if (!h) return FGEMM_ERR_INVALID_VALUE;
   if (h->own_ws) {
+    DeviceGuard guard(h->device);
     hipDeviceSynchronize();
     hipFree(h->own_ws);
   }

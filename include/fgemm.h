@@ -122,7 +122,9 @@ typedef struct {
 } fgemm_model_t;
 
 /* Handle: reads the device's CU count and architecture; fails with
- * FGEMM_ERR_NOT_SUPPORTED on anything but gfx950 and FGEMM_ERR_HIP without a device. */
+ * FGEMM_ERR_NOT_SUPPORTED on anything but gfx950 and FGEMM_ERR_HIP without a device.
+ * Calls through a handle run on its device (made current for the call, the caller's
+ * current device restored on return); their streams and pointers must belong to it. */
 fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device);
 fgemm_status_t fgemm_destroy(fgemm_handle_t handle);
 
