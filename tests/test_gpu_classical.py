@@ -232,3 +232,17 @@ def test_persistent_chains_odd_and_even_phases(tile, bk, phases):
         got = run(At, Bt, dtype, transA=True, transB=True, M=M, N=N,
                   plan=fgemm.classical_plan(*tile))
         assert np.array_equal(got, Qt)
+
+
+@pytest.mark.parametrize("transA", [False, True])
+def test_persistent_chains_through_edge_tiles(transA):
+    """Chains of tiles per workgroup that cross clamped edge tiles (fast path) and
+    tiles narrower than 8 in the contiguous dimension of a transposed operand
+    (bounds-checked path) in one launch.  Integer inputs: exact."""
+    dtype = BF16
+    M, N, K = (4452, 4356, 320) if not transA else (4356, 4452, 320)
+    say(f"persistent chains with edge tiles transA={transA} M={M} N={N} K={K}")
+    A, B = stored(M, N, K, transA, False, 0, 111, 112, dtype)
+    _, Q, _ = oracle.gemm(A, B, transA=transA, dtype=dtype)
+    got = run(A, B, dtype, transA=transA, M=M, N=N, plan=fgemm.classical_plan(256, 256))
+    assert np.array_equal(got, Q)
