@@ -16,8 +16,9 @@
 //     consecutive output columns of one row (in-lane row statistics);
 //   - tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane straight
 //     into LDS, no registers, asynchronous): a ring of STAGES phase buffers keeps
-//     the loads of STAGES-1 phases in flight while one phase feeds the MFMAs; a
-//     phase's loads are issued one after each MFMA of its first k-step;
+//     the loads of STAGES-1 phases in flight while one phase feeds the MFMAs; the
+//     loads into a stage are issued as soon as the barrier that frees it has
+//     passed, one after each MFMA of the last k-step of the phase that read it;
 //   - LDS keeps each operand in its memory layout.  K-contiguous operands (A not
 //     transposed, B transposed) are rows of BK values read as one 16-byte fragment
 //     per lane; M/N-contiguous operands (A transposed, B not) are BK rows of BM or
@@ -32,8 +33,9 @@
 //     looping over tiles; workgroups of one XCD (ids are dealt round-robin over
 //     the 8 XCDs) take a contiguous, L2-friendly run of tiles per round, and a
 //     tile's first loads are issued by its predecessor before that one's epilogue;
-//   - plain and fp32 epilogues stage the accumulators through LDS so that every
-//     lane stores (and reads beta*C as) 8 consecutive columns: whole 128-byte lines.
+//   - with aligned operands the epilogues (plain, fp32 slices, SwiGLU) stage their
+//     results through LDS so that every lane stores (and reads beta*C as) 8
+//     consecutive columns: whole 128-byte lines.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -535,11 +537,11 @@ struct GemmTile {
     }
   }
 
-  // MFMA M of step 0, then read instruction M of step 1, then load M (when LD); a
-  // scheduling fence after each group keeps the order.  Leftover reads and loads
-  // follow the last MFMA.
+  // MFMA M of the step on `now`, then read instruction M of step `rs` of stage `rd`
+  // into `next`, then load M (when LD); a scheduling fence after each group keeps
+  // the order.  Leftover reads and loads follow the last MFMA.
   template <int M, bool LD>
-  __device__ __forceinline__ static void emit0(const uint8_t* cur, const FragAddr& fa,
+  __device__ __forceinline__ static void emit0(const uint8_t* rd, int rs, const FragAddr& fa,
                                                const Frags& now, Frags& next,
                                                Acc (&acc)[CFG::FM][CFG::FN],
                                                const char* ab, const char* bb,
@@ -548,23 +550,23 @@ struct GemmTile {
     if constexpr (M < NM) {
       constexpr int i = M / CFG::FN, j = M % CFG::FN;
       acc[i][j] = mfma(now.b[j], now.a[i], acc[i][j]);
-      if constexpr (M < NR) read_job<M>(cur, fa, 1, next);
+      if constexpr (M < NR) read_job<M>(rd, fa, rs, next);
       if constexpr (M < NL) load_job<M>(ab, bb, la, wave, ls);
       __builtin_amdgcn_sched_barrier(0);
-      emit0<M + 1, LD>(cur, fa, now, next, acc, ab, bb, la, wave, ls);
+      emit0<M + 1, LD>(rd, rs, fa, now, next, acc, ab, bb, la, wave, ls);
     } else {
-      emit0_rest<NM, LD>(cur, fa, next, ab, bb, la, wave, ls);
+      emit0_rest<NM, LD>(rd, rs, fa, next, ab, bb, la, wave, ls);
     }
   }
   template <int X, bool LD>
-  __device__ __forceinline__ static void emit0_rest(const uint8_t* cur, const FragAddr& fa,
+  __device__ __forceinline__ static void emit0_rest(const uint8_t* rd, int rs, const FragAddr& fa,
                                                     Frags& next, const char* ab, const char* bb,
                                                     const LoadAddr& la, int wave, uint32_t ls) {
     constexpr int NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
     if constexpr (X < NR || X < NL) {
-      if constexpr (X < NR) read_job<X>(cur, fa, 1, next);
+      if constexpr (X < NR) read_job<X>(rd, fa, rs, next);
       if constexpr (X < NL) load_job<X>(ab, bb, la, wave, ls);
-      emit0_rest<X + 1, LD>(cur, fa, next, ab, bb, la, wave, ls);
+      emit0_rest<X + 1, LD>(rd, rs, fa, next, ab, bb, la, wave, ls);
     }
   }
 
@@ -579,10 +581,11 @@ struct GemmTile {
   }
 
   // ============================================================ main loops
-  // Interior tiles: STAGES-deep ring of direct-to-LDS phases.  Per phase kt: issue
-  // the loads of phase kt+STAGES-1 (into the stage freed by the last barrier), run
-  // the MFMA steps while reading the next step's fragments, then wait for phase
-  // kt+1's loads, barrier, and read its first fragments under the last MFMA step.
+  // Interior tiles: STAGES-deep ring of direct-to-LDS phases.  Per phase kt: run
+  // the MFMA steps but the last while reading the next step's fragments, wait for
+  // phase kt+1's loads, barrier, then run the last step while reading phase kt+1's
+  // first fragments and issuing the loads of phase kt+STAGES into the stage that
+  // the barrier has just freed (so a phase's loads have a whole phase to land).
   template <int VMC>
   __device__ __forceinline__ static void wait_phase(bool steady) {
     if (steady) wait_vmcnt<VMC>();
@@ -628,13 +631,16 @@ struct GemmTile {
     // them when stores were issued after them)
     wait_phase<(S - 2) * QW>(!pre && ktiles >= S - 1);
     __syncthreads();
+    // the last stage is free now (it held the previous tile's epilogue staging)
+    if (S - 1 < ktiles)
+      issue_loads(src, m0, kt0 + S - 1, wave, la, smem + (S - 1) * CFG::LDS_STAGE);
     Frags f0, f1;
     read_frags(smem, fa, 0, f0);
     int st = 0;  // stage of phase kt
-    // phases that still load a later phase, then the last S-1 that do not: two
+    // phases that still load a later phase, then the last S that do not: two
     // straight loop bodies
     int kt = 0;
-    for (; kt + S - 1 < ktiles; ++kt)
+    for (; kt + S < ktiles; ++kt)
       phase<true>(src, m0, smem, wave, lane, fa, la, kt0, kt, ktiles, st, chain, Pn, nx, f0, f1,
                   acc);
     for (; kt < ktiles; ++kt)
@@ -643,10 +649,10 @@ struct GemmTile {
     FGEMM_PHASE_FENCE();
   }
 
-  // Phase kt of the ring (stage st): step 0 with the loads of phase kt+S-1 when LD,
-  // the middle steps, the wait for phase kt+1 and the barrier, then the last step
-  // under the first reads of phase kt+1 (or, after the last phase, the next tile's
-  // first loads).
+  // Phase kt of the ring (stage st): the steps but the last, the wait for phase kt+1
+  // and the barrier, then the last step under the first reads of phase kt+1 and,
+  // when LD, the loads of phase kt+S into stage st (after the last phase: the next
+  // tile's first loads instead).
   template <bool LD>
   __device__ __forceinline__ static void phase(const Src& src, int m0, uint8_t* smem, int wave,
                                                int lane, const FragAddr& fa, const LoadAddr& la,
@@ -656,27 +662,32 @@ struct GemmTile {
     constexpr int S = CFG::STAGES;
     constexpr int QW = CFG::QAW + CFG::QBW;
     FGEMM_PHASE_FENCE();
-    const uint8_t* cur = smem + st * CFG::LDS_STAGE;
-    int st_ahead = st + S - 1;
-    if (st_ahead >= S) st_ahead -= S;
-    const int kl = kt0 + kt + S - 1;
+    uint8_t* cur = smem + st * CFG::LDS_STAGE;
+    const int kl = kt0 + kt + S;
     const char* ab = LD ? uniform_ptr(a_base(src, m0, kl)) : nullptr;
     const char* bb = LD ? uniform_ptr(b_base(src, kl)) : nullptr;
-    const uint32_t ls = lds_addr(smem + st_ahead * CFG::LDS_STAGE);
-    emit0<0, LD>(cur, fa, f0, f1, acc, ab, bb, la, wave, ls);
-    FGEMM_PHASE_FENCE();
-    // the other steps but the last; the last step's fragments end up in f1
+    // every step but the last; the last step's fragments end up in f1
+    step(cur, fa, 0, f0, f1, acc);
     if constexpr (CFG::STEPS == 4) {
       step(cur, fa, 1, f1, f0, acc);
       step(cur, fa, 2, f0, f1, acc);
     }
-    // phase kt+1 must have landed; loads of later phases may still fly
-    if constexpr (LD) wait_vmcnt<(S - 2) * QW>();
-    else wait_vmcnt<0>();
+    // phase kt+1 must have landed; the S-2 phases after it may still fly when
+    // they have all been issued
+    wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
     __syncthreads();
     const int st_next = st + 1 == S ? 0 : st + 1;
+    const uint8_t* nxt = smem + st_next * CFG::LDS_STAGE;
     if (kt + 1 < ktiles) {
-      read_frags(smem + st_next * CFG::LDS_STAGE, fa, 0, f0);
+      if constexpr (LD) {
+        // stage st is free once every wave has passed the barrier: phase kt+S goes
+        // there, its loads slotted between the last step's MFMAs
+        emit0<0, true>(nxt, 0, fa, f1, f0, acc, ab, bb, la, wave, lds_addr(cur));
+        FGEMM_PHASE_FENCE();
+        st = st_next;
+        return;
+      }
+      read_frags(nxt, fa, 0, f0);
     } else if (chain) {
       LoadAddr ln;  // computed here, where the next fragments are dead
       load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);

@@ -53,10 +53,10 @@ void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
   // dense 16-bit MFMA: 4 SIMDs x 1024 FLOP per clock per CU on gfx950
   m->peak_tflops = cus * 4096.0 * clock_ghz * 1e9 / 1e12;
   m->hbm_gbps = 8000.0;
-  // measured on MI355X (bf16 8192^3 and LLM shapes, 256x256 tile): ~1.2-1.26
-  // PFLOP/s against 2.5 at the nominal clock (the chip holds ~1.4-1.7 GHz under
+  // measured on MI355X (bf16 8192^3 and LLM shapes, 256x256 tile): ~1.27-1.33
+  // PFLOP/s against 2.5 at the nominal clock (the chip holds ~1.3-1.5 GHz under
   // this load); the streaming add kernels move ~5.2-5.3 TB/s
-  m->eta_mfma = 0.49;
+  m->eta_mfma = 0.52;
   m->eta_hbm = 0.66;
   m->launch_us = 4.0;
   m->max_workspace_bytes = 16.0 * (1ull << 30);
