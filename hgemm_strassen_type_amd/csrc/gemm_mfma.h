@@ -1162,11 +1162,14 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
 }
 
 // ------------------------------------------------------------------ launching
-// 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages, 32x32x16 MFMAs;
-// measured on the 8192^3 bf16 shapes against 4-wave 128x128 waves, 2x4 waves of
-// 128x64, 16x16x32 MFMAs, BK = 32 with 3-5 stages, and 256x128 / 128x256 tiles at
-// two workgroups per CU.
+// 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages; measured on the
+// 8192^3 bf16 shapes against 4-wave 128x128 waves, 2x4 waves of 128x64, BK = 32
+// with 3-5 stages, and 256x128 / 128x256 tiles at two workgroups per CU.  With B
+// N-contiguous the 16x16x32 MFMAs are 2-5 % faster (the chip holds a higher clock
+// on them); with B K-contiguous their twice as many fragment registers spill inside
+// the loop, so that layout keeps 32x32x16.
 using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2>;
+using Cfg256n = TileCfg<256, 256, 4, 2, 64, 2, 1, 16>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
