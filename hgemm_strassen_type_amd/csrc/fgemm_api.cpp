@@ -19,9 +19,9 @@ using namespace fgemm;
 
 namespace fgemm {
 
-int tile_m_of(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 : tile == 2 ? 64 : 32; }
-int tile_n_of(int tile) { return tile == 0 ? 256 : 128; }
-int waves_n_of(int tile) { return tile == 3 ? 4 : 2; }
+int tile_m_of(int tile) { return kTiles[tile].bm; }
+int tile_n_of(int tile) { return kTiles[tile].bn; }
+int waves_n_of(int tile) { return kTiles[tile].waves_n; }
 
 hipError_t launch_gemm(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
 #define FG_SEL(DT, AK, BK) \
@@ -137,6 +137,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
   if (!(flags & ~(uint32_t)FGEMM_EPI_BIAS) && vec && K > 0) {
     for (int i = 0; i < kNumTiles; ++i) {
       const TileInfo& ti = kTiles[i];
+      if (ti.one_row && M > ti.bm) continue;
       const int64_t tiles = ceil_div(M, ti.bm) * ceil_div(N, ti.bn);
       const int64_t ktiles = ceil_div(K, ti.bk);
       for (int sk = 2; sk <= 16 && tiles < md.compute_units; sk *= 2) {
@@ -234,7 +235,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   int tile = tile_id(plan.tile_m, plan.tile_n);
   if (tile < 0) return FGEMM_ERR_INVALID_VALUE;
   const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
-  if (swiglu && tile == 3) return FGEMM_ERR_NOT_SUPPORTED;
+  if (swiglu && !kTiles[tile].swiglu) return FGEMM_ERR_NOT_SUPPORTED;
   GemmBatch b{};
   b.count = 1;
   b.cus = h->cus;

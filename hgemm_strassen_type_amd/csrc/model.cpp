@@ -42,10 +42,14 @@ double stream_bw(const fgemm_model_t& md, int64_t blocks) {
 // reaches at steady state relative to the 256x256 tile (smaller tiles re-read
 // operands more often per FLOP and hide less latency).
 const TileInfo kTiles[kNumTiles] = {
-    {0, 256, 256, 64, 1.00},
-    {1, 128, 128, 32, 0.70},
-    {2, 64, 128, 32, 0.45},
-    {3, 32, 128, 64, 0.30},
+    {0, 256, 256, 64, 1.00, 2, 1, 0},
+    {1, 128, 128, 32, 0.70, 2, 1, 0},
+    {2, 64, 128, 32, 0.45, 2, 1, 0},
+    {3, 32, 128, 64, 0.30, 4, 0, 0},
+    // twice the workgroups of the 32x128 tile on one-row (decode) shapes: 6 % more
+    // bandwidth at M = 1 and 16 on N = 14336, K = 4096; with two tile rows (M = 64)
+    // the extra workgroups re-read B and it is 25 % slower, hence one row only
+    {4, 32, 64, 64, 0.30, 2, 0, 1},
 };
 
 void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
@@ -83,7 +87,8 @@ int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swig
   double bt = 0;
   for (int i = 0; i < kNumTiles && kTiles[i].tile <= max_tile; ++i) {
     const TileInfo& t = kTiles[i];
-    if (swiglu && t.tile == 3) continue;  // the SwiGLU epilogue needs two column halves
+    if (swiglu && !t.swiglu) continue;  // the SwiGLU epilogue needs two column halves
+    if (t.one_row && M > t.bm) continue;
     const int64_t out_bn = swiglu ? t.bn / 2 : t.bn;
     const int64_t Nb = swiglu ? 2 * N : N;
     double tt = classical_time_us(md, t, M, N, K, Nb, out_bn, count, in_bytes, out_bytes, beta);

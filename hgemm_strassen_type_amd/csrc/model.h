@@ -9,13 +9,16 @@
 namespace fgemm {
 
 struct TileInfo {
-  int tile;        // kernel tile id
+  int tile;        // kernel tile id (its index in kTiles)
   int bm, bn;      // macro-tile (bn MFMA columns; SwiGLU writes bn/2 outputs)
   int bk;          // K depth of one pipeline phase
   double rel_eta;  // steady-state MFMA efficiency relative to the 256x256 tile
+  int waves_n;     // waves across the tile's columns (row-sum partials per tile)
+  int swiglu;      // the SwiGLU epilogue runs on it (each wave holds both halves)
+  int one_row;     // offered only when M fits one tile row (decode shapes)
 };
 
-constexpr int kNumTiles = 4;
+constexpr int kNumTiles = 5;
 extern const TileInfo kTiles[kNumTiles];
 // Strassen workspace header: the two scales, then the partial maxima of A and B.
 constexpr size_t kScaleHeaderBytes = 256 + 2 * 4096 * 4;
@@ -33,7 +36,8 @@ double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, 
                          double out_bytes, int beta);
 // Tile of least predicted time among tile ids 0..max_tile.
 int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swiglu, int count,
-              double in_bytes, double out_bytes, int beta, double* t_us, int max_tile = 3);
+              double in_bytes, double out_bytes, int beta, double* t_us,
+              int max_tile = kNumTiles - 1);
 // Split-K plan of `splits` K slices with an fp32 finalize pass.
 double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
                       int64_t K, int splits, int beta);
