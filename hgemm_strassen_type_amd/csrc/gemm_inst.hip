@@ -42,7 +42,7 @@ hipError_t FG_NAME(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
     case 1: return by_epilogue<Cfg128>(k, b, s);
     case 2: return by_epilogue<Cfg64>(k, b, s);
     case 3: return by_epilogue<Cfg32>(k, b, s);
-    case 4: return by_epilogue<Cfg32n>(k, b, s);
+    case 4: return by_epilogue<Cfg64n>(k, b, s);
   }
   return hipErrorInvalidValue;
 }

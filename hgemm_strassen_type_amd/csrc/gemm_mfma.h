@@ -1173,7 +1173,7 @@ using Cfg256n = TileCfg<256, 256, 4, 2, 64, 2, 1, 16>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
-using Cfg32n = TileCfg<32, 64, 1, 2, 64, 4>;
+using Cfg64n = TileCfg<64, 64, 2, 2, 64, 4>;
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {

@@ -46,10 +46,10 @@ const TileInfo kTiles[kNumTiles] = {
     {1, 128, 128, 32, 0.70, 2, 1, 0},
     {2, 64, 128, 32, 0.45, 2, 1, 0},
     {3, 32, 128, 64, 0.30, 4, 0, 0},
-    // twice the workgroups of the 32x128 tile on one-row (decode) shapes: 6 % more
-    // bandwidth at M = 1 and 16 on N = 14336, K = 4096; with two tile rows (M = 64)
-    // the extra workgroups re-read B and it is 25 % slower, hence one row only
-    {4, 32, 64, 64, 0.30, 2, 0, 1},
+    // twice the workgroups of the 32x128 tile on one-row (decode) shapes: 7 % more
+    // bandwidth at M = 1 and 16 on N = 14336, K = 4096 and 3 % at M = 64 (where the
+    // 32x128 tile reads B twice); with more rows it would re-read B, hence one row
+    {4, 64, 64, 64, 0.30, 2, 0, 1},
 };
 
 void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
@@ -92,7 +92,14 @@ int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swig
     const int64_t out_bn = swiglu ? t.bn / 2 : t.bn;
     const int64_t Nb = swiglu ? 2 * N : N;
     double tt = classical_time_us(md, t, M, N, K, Nb, out_bn, count, in_bytes, out_bytes, beta);
-    if (best < 0 || tt < bt) {
+    // on a tie prefer fewer tile rows (every tile row reads B again, from L2 at
+    // best), then more tiles (more workgroups keep more loads in flight)
+    const TileInfo* b = best < 0 ? nullptr : &kTiles[best];
+    const int64_t rows = ceil_div(M, t.bm), brows = b ? ceil_div(M, b->bm) : 0;
+    const int64_t cols = ceil_div(N, out_bn);
+    const int64_t bcols = b ? ceil_div(N, swiglu ? b->bn / 2 : b->bn) : 0;
+    if (!b || tt < bt ||
+        (tt == bt && (rows < brows || (rows == brows && cols > bcols)))) {
       best = t.tile;
       bt = tt;
     }

@@ -10,7 +10,7 @@ from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, from_dev, handle, rel
                       to_dev, empty_out)
 
 pytestmark = pytest.mark.gpu
-TILES = [(256, 256), (128, 128), (64, 128), (32, 128), (32, 64)]
+TILES = [(256, 256), (128, 128), (64, 128), (32, 128), (64, 64)]
 
 
 def dev_f32(n, fill=np.nan):
