@@ -676,6 +676,10 @@ struct GemmTile {
     // they have all been issued
     wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
     __syncthreads();
+    // raised issue priority for the last step: a wave still in it is served ahead of
+    // its SIMD partner that has moved on, so the pair reaches the next barrier
+    // together (measured 0.5-1 % faster)
+    __builtin_amdgcn_s_setprio(1);
     const int st_next = st + 1 == S ? 0 : st + 1;
     const uint8_t* nxt = smem + st_next * CFG::LDS_STAGE;
     if (kt + 1 < ktiles) {
@@ -683,6 +687,7 @@ struct GemmTile {
         // stage st is free once every wave has passed the barrier: phase kt+S goes
         // there, its loads slotted between the last step's MFMAs
         emit0<0, true>(nxt, 0, fa, f1, f0, acc, ab, bb, la, wave, lds_addr(cur));
+        __builtin_amdgcn_s_setprio(0);
         FGEMM_PHASE_FENCE();
         st = st_next;
         return;
@@ -695,6 +700,7 @@ struct GemmTile {
     }
     mfma_step(f1, acc);
     interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
+    __builtin_amdgcn_s_setprio(0);
     st = st_next;
   }
 
