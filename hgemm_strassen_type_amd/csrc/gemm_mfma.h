@@ -138,10 +138,12 @@ struct TileCfg {
 
 // ------------------------------------------------------------------ LDS layout
 // K-contiguous operand: R rows of BK values (BK*2 bytes), chunk c of row r at
-// chunk c ^ swz_k(r).  Fragment reads take 16 consecutive rows per bank cycle.
+// chunk c ^ swz_k(r).  Fragment reads take 16 consecutive rows per bank cycle; the
+// swizzle depends on r mod 16 only, so fragments 16 or 32 rows apart share it and
+// their addresses differ by a constant (one base register per operand).
 template <int BK>
 __device__ __forceinline__ int swz_k(int r) {
-  return BK == 32 ? ((r >> 2) & 3) : (((r >> 1) ^ (r >> 4)) & 7);
+  return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 // M/N-contiguous operand: BK rows of R values (R*2 bytes), chunk c of row k at
 // chunk c ^ swz_mn(k); a transposed read takes rows k..k+3 (k % 4 == 0) of two
@@ -422,7 +424,13 @@ struct GemmTile {
   // M/N-contiguous: KSTEP rows further down (the swizzle depends on k mod 16 only).
   template <bool KCONTIG, int R>
   __device__ __forceinline__ static int step_addr(int base, int s) {
-    return KCONTIG ? (base ^ (2 * CFG::KSTEP * s)) : base + s * CFG::KSTEP * (R * 2);
+    if constexpr (KCONTIG) {
+      if (s == 0) return base;
+      int b = base;  // opaque: the XORed address is formed at its use, not held
+      asm volatile("" : "+v"(b));
+      return b ^ (2 * CFG::KSTEP * s);
+    }
+    return base + s * CFG::KSTEP * (R * 2);
   }
 
   template <bool KCONTIG, int R>
@@ -1170,12 +1178,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
 // ------------------------------------------------------------------ launching
 // 256x256: 8 waves (two per SIMD) of 64x128, BK = 64, two stages; measured on the
 // 8192^3 bf16 shapes against 4-wave 128x128 waves, 2x4 waves of 128x64, BK = 32
-// with 3-5 stages, and 256x128 / 128x256 tiles at two workgroups per CU.  With B
-// N-contiguous the 16x16x32 MFMAs are 2-5 % faster (the chip holds a higher clock
-// on them); with B K-contiguous their twice as many fragment registers spill inside
-// the loop, so that layout keeps 32x32x16.
-using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2>;
-using Cfg256n = TileCfg<256, 256, 4, 2, 64, 2, 1, 16>;
+// with 3-5 stages, and 256x128 / 128x256 tiles at two workgroups per CU.  The
+// 16x16x32 MFMAs are faster than 32x32x16 (the chip holds a higher clock on them)
+// except under the SwiGLU epilogue.
+using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2, 1, 16>;
+using Cfg256s = TileCfg<256, 256, 4, 2, 64, 2>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
