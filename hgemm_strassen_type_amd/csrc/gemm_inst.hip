@@ -32,11 +32,7 @@ static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_
 
 hipError_t FG_NAME(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
   switch (k.tile) {
-    case 0:
-      // the SwiGLU epilogue keeps 32x32x16 MFMAs (16x16x32 measured 5 % slower on the
-      // 8192 x 22016 x 4096 product)
-      if (k.epi == kEpiSwiGLU) return by_epilogue<Cfg256s>(k, b, s);
-      return by_epilogue<Cfg256>(k, b, s);
+    case 0: return by_epilogue<Cfg256>(k, b, s);
     case 1: return by_epilogue<Cfg128>(k, b, s);
     case 2: return by_epilogue<Cfg64>(k, b, s);
     case 3: return by_epilogue<Cfg32>(k, b, s);
