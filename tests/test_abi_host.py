@@ -187,3 +187,18 @@ def test_select_tile_choice_follows_wave_quantization():
     assert p.tile_m * p.tile_n < 256 * 256
     # skinny M uses a skinny tile
     assert select(16, 14336, 4096).tile_m <= 64
+
+
+def test_select_one_row_decode_tile():
+    # the 64x64 tile is offered only while M fits one tile row; on the decode shapes
+    # it ties with 32x128 in the model and wins the tie (one tile row, more tiles)
+    for m in (1, 16, 64):
+        p = select(m, 14336, 4096)
+        assert (p.tile_m, p.tile_n, p.split_k) == (64, 64, 1), m
+    for m in (65, 128, 1000):
+        p = select(m, 14336, 4096)
+        assert (p.tile_m, p.tile_n) != (64, 64), m
+    # the SwiGLU epilogue needs both column halves in one wave: never the 64x64 tile
+    e = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=1, rms_n=4096)
+    p = select(16, 14336, 4096, epi=e)
+    assert (p.tile_m, p.tile_n) not in ((64, 64), (32, 128))
