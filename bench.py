@@ -240,6 +240,18 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
         "gemm2_tflops": round(f2 / (t2 * 1e-3) / 1e12, 2),
         "chain_tflops": round((f1 + f2) / ((t1 + t2) * 1e-3) / 1e12, 2)}
     log(f"chain: {W['fused_chain_8192x4096_ffn11008']}")
+    # the same chain with both GEMMs forced onto the Strassen path (epilogues in the
+    # top-level post-add), for comparison with the model's classical pick
+    chain_sk = {}
+    for depth in (1, 2):
+        plan = fgemm.strassen_plan(depth, fgemm.FGEMM_VARIANT_WINOGRAD)
+        s1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1, plan=plan), reps, 2)
+        s2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2, plan=plan), reps, 2)
+        chain_sk[f"winograd_d{depth}"] = {
+            "gemm1_rowsumsq_ms": round(s1, 5), "gemm2_rms_swiglu_ms": round(s2, 5),
+            "chain_effective_tflops": round((f1 + f2) / ((s1 + s2) * 1e-3) / 1e12, 2)}
+    W["fused_chain_8192x4096_ffn11008"]["strassen"] = chain_sk
+    log(f"chain on the Strassen path: {chain_sk}")
     del X, Wt, W2, Y, O, ss
 
     # Strassen / Winograd vs classical, and the model's pick

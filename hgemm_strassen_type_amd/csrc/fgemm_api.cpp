@@ -106,11 +106,19 @@ fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int
   if (p.depth < 1 || p.depth > 2) return FGEMM_ERR_INVALID_VALUE;
   if (p.variant != FGEMM_VARIANT_S69 && p.variant != FGEMM_VARIANT_WINOGRAD)
     return FGEMM_ERR_INVALID_VALUE;
+  // the recursion runs on op(B)'s Nb columns (2N with SwiGLU: its top split is the
+  // gate/up boundary); every epilogue is applied in the top-level post-add
   const int64_t q = 8ll << p.depth;
-  if (M % q || N % q || K % q || M == 0 || N == 0 || K == 0) return FGEMM_ERR_NOT_SUPPORTED;
+  const int64_t Nb = (flags & FGEMM_EPI_RMS_SWIGLU) ? 2 * N : N;
+  if (M % q || Nb % q || K % q || M == 0 || N == 0 || K == 0) return FGEMM_ERR_NOT_SUPPORTED;
   if (!vec) return FGEMM_ERR_NOT_SUPPORTED;
-  if (flags & ~(uint32_t)FGEMM_EPI_BIAS) return FGEMM_ERR_NOT_SUPPORTED;
   return FGEMM_OK;
+}
+
+// Row-sum partials of the Strassen path's top-level post-add (ROWSUMSQ only).
+size_t strassen_stats_bytes(int64_t M, int64_t Nb, uint32_t flags) {
+  if (!(flags & FGEMM_EPI_ROWSUMSQ)) return 0;
+  return align256((size_t)postadd_ss_parts(Nb / 2) * (size_t)M * 4);
 }
 
 // Core of fgemm_select: classical tile choice, then Strassen candidates under guards.
@@ -164,11 +172,14 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       c.variant = variant;
       if (check_plan_shape(c, M, N, K, vec, flags) != FGEMM_OK) continue;
       // sub-problems below 512 never pay for their additions; keep them classical
-      if ((M >> depth) < 512 || (N >> depth) < 512 || (K >> depth) < 512) continue;
-      const size_t ws = strassen_workspace(M, N, K, depth, variant);
+      if ((M >> depth) < 512 || ((swiglu ? 2 * N : N) >> depth) < 512 || (K >> depth) < 512)
+        continue;
+      const int64_t Nb = swiglu ? 2 * N : N;
+      const size_t ws = strassen_workspace(M, Nb, K, depth, variant) +
+                        strassen_stats_bytes(M, Nb, flags);
       if ((double)ws > md.max_workspace_bytes || ws > ws_limit) continue;
       int sub_tile = 0;
-      const double t = strassen_time_us(md, M, N, K, depth, variant, beta_hint, &sub_tile);
+      const double t = strassen_time_us(md, M, Nb, K, depth, variant, beta_hint, &sub_tile);
       if (t < p.t_pred_us) {
         c.tile_m = tile_m_of(sub_tile);
         c.tile_n = tile_n_of(sub_tile);
@@ -306,6 +317,7 @@ struct StrassenRun {
   void* S[3][7];
   void* T[3][7];
   float* P[3][7];
+  float* ss_partial;  // ROWSUMSQ: the top-level post-add's row-sum partials
 };
 
 BlockedOperand temp_op(void* p, int64_t rows, int64_t cols, int trans) {
@@ -375,16 +387,30 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
     pa.dtype = run.in_dtype;
     pa.alpha = c.alpha;
     pa.beta = c.beta;
-    pa.bias = (epi_flags(c.epi) & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr;
+    const uint32_t flags = epi_flags(c.epi);
+    pa.bias = (flags & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr;
     pa.scale_a = run.scale_a;
     pa.scale_b = run.scale_b;
+    if (flags & FGEMM_EPI_ROWSUMSQ) {
+      pa.rowsumsq = c.epi->rowsumsq;
+      pa.ss_partial = run.ss_partial;
+    }
+    if (flags & FGEMM_EPI_RMS_SWIGLU) {
+      pa.swiglu = 1;
+      pa.rms_ss = c.epi->rms_rowsumsq;
+      pa.rms_inv_n = 1.0f / (float)c.epi->rms_n;
+      pa.rms_eps = c.epi->rms_eps;
+    }
   }
   e = launch_postadd(pa, c.stream);
   return hip_status(e);
 }
 
 fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
-  const size_t need = strassen_workspace(c.M, c.N, c.K, plan.depth, plan.variant);
+  const uint32_t flags = epi_flags(c.epi);
+  const int64_t Nb = (flags & FGEMM_EPI_RMS_SWIGLU) ? 2 * c.N : c.N;  // columns of op(B)
+  const size_t body = strassen_workspace(c.M, Nb, c.K, plan.depth, plan.variant);
+  const size_t need = body + strassen_stats_bytes(c.M, Nb, flags);
   void* ws;
   fgemm_status_t st = ensure_workspace(h, need, &ws);
   if (st != FGEMM_OK) return st;
@@ -397,6 +423,7 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   if (run.sub_tile != 0 && run.sub_tile != 1) run.sub_tile = 0;
   run.in_dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
+  run.ss_partial = (flags & FGEMM_EPI_ROWSUMSQ) ? reinterpret_cast<float*>(base + body) : nullptr;
   static_assert(kScaleHeaderBytes >= 256 + 2 * kMaxPartials * sizeof(float), "header");
   run.scale_a = reinterpret_cast<float*>(base + 64);
   run.scale_b = reinterpret_cast<float*>(base + 128);
@@ -404,7 +431,7 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   float* part_b = part_a + kMaxPartials;
   size_t off = kScaleHeaderBytes;
   for (int l = 1; l <= plan.depth; ++l) {
-    const int64_t m = c.M >> l, k = c.K >> l, n = c.N >> l;
+    const int64_t m = c.M >> l, k = c.K >> l, n = Nb >> l;
     for (int q = 0; q < 7; ++q) { run.S[l][q] = base + off; off += align256((size_t)(m * k * 2)); }
     for (int q = 0; q < 7; ++q) { run.T[l][q] = base + off; off += align256((size_t)(k * n * 2)); }
     for (int q = 0; q < 7; ++q) {
@@ -419,14 +446,14 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
       launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
                     run.in_dtype, part_a, &na, c.stream);
   if (e == hipSuccess)
-    e = launch_maxabs(c.B, c.ldb, c.tb == FGEMM_OP_T ? c.N : c.K, c.tb == FGEMM_OP_T ? c.K : c.N,
+    e = launch_maxabs(c.B, c.ldb, c.tb == FGEMM_OP_T ? Nb : c.K, c.tb == FGEMM_OP_T ? c.K : Nb,
                       run.in_dtype, part_b, &nb, c.stream);
   if (e == hipSuccess) e = launch_scale_from_max(part_a, na, target, run.scale_a, c.stream);
   if (e == hipSuccess) e = launch_scale_from_max(part_b, nb, target, run.scale_b, c.stream);
   if (e != hipSuccess) return FGEMM_ERR_HIP;
   BlockedOperand L{c.A, c.lda, c.ta == FGEMM_OP_T, run.in_dtype, 0};
   BlockedOperand R{c.B, c.ldb, c.tb == FGEMM_OP_T, run.in_dtype, 0};
-  return strassen_level(run, 1, L, R, c.M, c.K, c.N, nullptr, 0);
+  return strassen_level(run, 1, L, R, c.M, c.K, Nb, nullptr, 0);
 }
 
 // Makes the handle's device current for the scope of a call and restores the

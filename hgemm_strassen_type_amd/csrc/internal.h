@@ -121,8 +121,18 @@ struct PostAddArgs {
   float alpha, beta;
   const void* bias;
   const float* scale_a; const float* scale_b;
+  // Top level only.  rowsumsq != null: rowsumsq[r] = sum over the written row r of
+  // C^2, from per-workgroup partials in ss_partial ([postadd_ss_parts(n)][2m]).
+  // swiglu: op(B) had 2n columns split at the gate/up boundary, so output blocks
+  // 11/21 hold gate and 12/22 up; C (2m x n) = RNE(silu(r*f*gate) * (r*f*up)
+  // + beta*C) with r = 1/sqrt(rms_ss[row]*rms_inv_n + rms_eps), f = alpha/(sa*sb).
+  float* rowsumsq; float* ss_partial;
+  int swiglu;
+  const float* rms_ss; float rms_inv_n, rms_eps;
 };
 hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
+// Row-sum partials per output row the post-add writes for sub-block width n.
+int64_t postadd_ss_parts(int64_t n);
 
 // Split-K finalize: C = RNE16(alpha * sum_s part[s] + beta*C + bias), part[s] is
 // M x N fp32 (leading dimension N), C is 16-bit with leading dimension ldc.

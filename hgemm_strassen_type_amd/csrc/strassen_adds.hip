@@ -226,6 +226,9 @@ struct PostAddKArgs {
   float alpha, beta;
   const uint16_t* bias;
   const float* scale_a; const float* scale_b;
+  float* ss_partial;   // [gridDim.x][2m] row-sum partials (null: no statistics)
+  int swiglu;
+  const float* rms_ss; float rms_inv_n, rms_eps;
 };
 
 __device__ __forceinline__ void combine(int variant, const float (&p)[7], float* c) {
@@ -245,49 +248,108 @@ __device__ __forceinline__ void combine(int variant, const float (&p)[7], float*
   }
 }
 
-__global__ void postadd_kernel(PostAddKArgs a) {
+// Sum of x over the workgroup's 256 lanes in a fixed order (wave64 butterfly, then
+// the four waves in order); every lane gets the result.
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // the previous round's readers are done
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
+  __shared__ float red[2][4];
   const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (j >= a.n) return;
+  // lanes past the row still take part in the row-sum reductions
+  const bool active = j < a.n;
   float factor = 1.f;
   if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
+  const bool stats = a.ss_partial != nullptr;
   for (int64_t i = blockIdx.y; i < a.m; i += gridDim.y) {
-    float p[4][7];
+    float ss[2] = {0.f, 0.f};  // top row i, bottom row m + i
+    if (active) {
+      float p[4][7];
 #pragma unroll
-    for (int q = 0; q < 7; ++q) {
-      float4 v = *reinterpret_cast<const float4*>(a.P[q] + i * a.n + j);
-      p[0][q] = v.x; p[1][q] = v.y; p[2][q] = v.z; p[3][q] = v.w;
-    }
-    float c[4][4];  // [element][block]
+      for (int q = 0; q < 7; ++q) {
+        float4 v = *reinterpret_cast<const float4*>(a.P[q] + i * a.n + j);
+        p[0][q] = v.x; p[1][q] = v.y; p[2][q] = v.z; p[3][q] = v.w;
+      }
+      float c[4][4];  // [element][block]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) combine(a.variant, p[e], c[e]);
+      for (int e = 0; e < 4; ++e) combine(a.variant, p[e], c[e]);
+      if (a.swiglu) {
+        // blocks 0/1 (rows i) and 2/3 (rows m + i): gate, then up
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t row = (b >> 1) * a.m + i, col = (b & 1) * a.n + j;
-      if (a.out32) {
-        *reinterpret_cast<float4*>(a.out32 + row * a.ld32 + col) =
-            make_float4(c[0][b], c[1][b], c[2][b], c[3][b]);
+        for (int h = 0; h < 2; ++h) {
+          const int64_t row = h * a.m + i;
+          const float r = rsqrtf(a.rms_ss[row] * a.rms_inv_n + a.rms_eps) * factor;
+          const int64_t off = row * a.ldc + j;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = r * c[e][2 * h], u = r * c[e][2 * h + 1];
+            v[e] = g / (1.f + __expf(-g)) * u;
+          }
+          if (a.beta != 0.f) {
+            uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+            v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
+            v[1] += a.beta * h2f(cv.x >> 16, a.dt);
+            v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
+            v[3] += a.beta * h2f(cv.y >> 16, a.dt);
+          }
+          *reinterpret_cast<uint2*>(a.C + off) =
+              make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
+                         f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+        }
       } else {
-        const int64_t off = row * a.ldc + col;
-        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = factor * c[e][b];
-        if (a.beta != 0.f) {
-          uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
-          v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
-          v[1] += a.beta * h2f(cv.x >> 16, a.dt);
-          v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
-          v[3] += a.beta * h2f(cv.y >> 16, a.dt);
+        for (int b = 0; b < 4; ++b) {
+          const int64_t row = (b >> 1) * a.m + i, col = (b & 1) * a.n + j;
+          if (a.out32) {
+            *reinterpret_cast<float4*>(a.out32 + row * a.ld32 + col) =
+                make_float4(c[0][b], c[1][b], c[2][b], c[3][b]);
+          } else {
+            const int64_t off = row * a.ldc + col;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = factor * c[e][b];
+            if (a.beta != 0.f) {
+              uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+              v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
+              v[1] += a.beta * h2f(cv.x >> 16, a.dt);
+              v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
+              v[3] += a.beta * h2f(cv.y >> 16, a.dt);
+            }
+            if (a.bias) {
+              uint2 bv = *reinterpret_cast<const uint2*>(a.bias + col);
+              v[0] += h2f(bv.x & 0xffffu, a.dt);
+              v[1] += h2f(bv.x >> 16, a.dt);
+              v[2] += h2f(bv.y & 0xffffu, a.dt);
+              v[3] += h2f(bv.y >> 16, a.dt);
+            }
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = f2h(v[e], a.dt);
+              // statistics of the rounded, written values
+              const float w = h2f(o[e], a.dt);
+              ss[b >> 1] += w * w;
+            }
+            *reinterpret_cast<uint2*>(a.C + off) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+          }
         }
-        if (a.bias) {
-          uint2 bv = *reinterpret_cast<const uint2*>(a.bias + col);
-          v[0] += h2f(bv.x & 0xffffu, a.dt);
-          v[1] += h2f(bv.x >> 16, a.dt);
-          v[2] += h2f(bv.y & 0xffffu, a.dt);
-          v[3] += h2f(bv.y >> 16, a.dt);
-        }
-        *reinterpret_cast<uint2*>(a.C + off) =
-            make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
-                       f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+      }
+    }
+    if (stats) {  // uniform over the workgroup
+      const float top = block_sum256(ss[0], red[0]);
+      const float bot = block_sum256(ss[1], red[1]);
+      if (threadIdx.x == 0) {
+        float* part = a.ss_partial + (int64_t)blockIdx.x * 2 * a.m;
+        part[i] = top;
+        part[a.m + i] = bot;
       }
     }
   }
@@ -374,10 +436,24 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
   a.bias = static_cast<const uint16_t*>(in.bias);
   a.scale_a = in.scale_a;
   a.scale_b = in.scale_b;
+  a.swiglu = in.swiglu;
+  a.rms_ss = in.rms_ss;
+  a.rms_inv_n = in.rms_inv_n;
+  a.rms_eps = in.rms_eps;
   if (a.n % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(postadd_kernel, rows_grid(a.m, a.n, 4), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  const bool stats = in.rowsumsq != nullptr;
+  if ((stats || a.swiglu) && (a.out32 || !in.C)) return hipErrorInvalidValue;
+  if (stats && (a.swiglu || !in.ss_partial || 2 * a.m > 0x7fffffff)) return hipErrorInvalidValue;
+  a.ss_partial = stats ? in.ss_partial : nullptr;
+  const dim3 grid = rows_grid(a.m, a.n, 4);
+  hipLaunchKernelGGL(postadd_kernel, grid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && stats)
+    e = launch_rowsumsq_reduce(in.ss_partial, (int)grid.x, (int)(2 * a.m), in.rowsumsq, stream);
+  return e;
 }
+
+int64_t postadd_ss_parts(int64_t n) { return rows_grid(1, n, 4).x; }
 
 // ------------------------------------------------------------ split-K finalize
 namespace {

@@ -158,9 +158,12 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t t
                           void* stream);
 
 /* The same on an explicit plan (path, depth, variant).  Tile fields of 0 let the
- * library choose.  Strassen needs M, N and K divisible by 8*2^depth, aligned
- * operands and an epilogue of NONE or BIAS, else FGEMM_ERR_NOT_SUPPORTED; too
- * small a caller workspace gives FGEMM_ERR_WORKSPACE. */
+ * library choose.  Strassen needs M, K and the column count of op(B) (N, or 2N
+ * with RMS_SWIGLU) divisible by 8*2^depth and aligned operands, else
+ * FGEMM_ERR_NOT_SUPPORTED; too small a caller workspace gives FGEMM_ERR_WORKSPACE.
+ * On the Strassen path every epilogue runs in the top-level block post-add: with
+ * RMS_SWIGLU the 2x2 split of op(B)'s 2N columns is exactly the gate/up boundary,
+ * so gate and up of one output meet in the same post-add lane. */
 fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
                                fgemm_op_t transA, fgemm_op_t transB, int64_t M, int64_t N,
                                int64_t K, float alpha, const void* A, int64_t lda,

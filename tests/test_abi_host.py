@@ -137,9 +137,30 @@ def test_select_never_picks_strassen_where_it_cannot_run():
     for shape in [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (8191, 8192, 8192),
                   (256, 256, 256), (8192, 8192, 8200)]:
         assert select(*shape).path == fgemm.FGEMM_PATH_CLASSICAL, shape
-    # epilogues other than bias are classical only
-    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
-    assert select(32768, 32768, 32768, epi=epi).path == fgemm.FGEMM_PATH_CLASSICAL
+    # SwiGLU: the recursion runs on op(B)'s 2N columns, which must divide by 8*2^depth
+    fast_mem = mi355x_model(hbm_gbps=80000.0)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096,
+                              rms_eps=1e-6)
+    assert select(16384, 16380, 16384, fast_mem, epi=epi).path == fgemm.FGEMM_PATH_CLASSICAL
+
+
+def test_select_strassen_with_epilogues():
+    # every epilogue runs in the Strassen post-add: where the multiply saving wins,
+    # the row statistics and RMS + SwiGLU epilogues take the Strassen path too, and
+    # the statistics' partials are counted in the workspace
+    fast_mem = mi355x_model(hbm_gbps=80000.0)
+    base = select(16384, 16384, 16384, fast_mem)
+    ss = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
+    p = select(16384, 16384, 16384, fast_mem, epi=ss)
+    assert p.path == fgemm.FGEMM_PATH_STRASSEN
+    assert p.workspace_bytes > base.workspace_bytes
+    sw = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096, rms_eps=1e-6)
+    p = select(16384, 8192, 16384, fast_mem, epi=sw)
+    assert p.path == fgemm.FGEMM_PATH_STRASSEN
+    assert p.workspace_bytes == base.workspace_bytes  # op(B) is 16384 wide
+    # on the MI355X constants the configured fused chain stays classical
+    for (M, N, K, e) in [(8192, 4096, 4096, ss), (8192, 11008, 4096, sw)]:
+        assert select(M, N, K, epi=e).path == fgemm.FGEMM_PATH_CLASSICAL
 
 
 def test_select_predicted_time_is_monotone():

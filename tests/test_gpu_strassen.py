@@ -8,7 +8,8 @@ import pytest
 import oracle
 from hgemm_strassen_type_amd import fgemm
 from hgemm_strassen_type_amd import inputs
-from gpu_util import BF16, F16, STRASSEN_TOL, rel_err, run, say
+from gpu_util import (BF16, F16, STATS_TOL, STRASSEN_TOL, empty_out, from_dev, handle, rel_err,
+                      run, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,12 +89,15 @@ def test_unsupported_shapes_and_epilogues_are_refused():
                                A.data_ptr(), 96, B.data_ptr(), 64, 0.0, C.data_ptr(), 64,
                                fgemm.FGEMM_BF16, None, fgemm.current_stream(), check=False)
     assert st == fgemm.FGEMM_ERR_NOT_SUPPORTED          # 200 is not a multiple of 32
+    # SwiGLU recurses on op(B)'s 2N columns: 2 * 100 is not a multiple of 16
     A2 = to_dev(inputs.uniform((256, 256), 1, dtype), dtype)
-    C2 = empty_out(256, 256, dtype)
-    ssd = torch.zeros(256, dtype=torch.float32, device="cuda")
-    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
-    st = fgemm.fgemm_gemm_plan(handle().h, fgemm.strassen_plan(1, WIN), 0, 0, 256, 256, 256, 1.0,
-                               A2.data_ptr(), 256, A2.data_ptr(), 256, 0.0, C2.data_ptr(), 256,
+    B2 = to_dev(inputs.uniform((256, 200), 2, dtype), dtype)
+    C2 = empty_out(256, 100, dtype)
+    ssd = torch.ones(256, dtype=torch.float32, device="cuda")
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(), rms_n=256,
+                              rms_eps=1e-6)
+    st = fgemm.fgemm_gemm_plan(handle().h, fgemm.strassen_plan(1, WIN), 0, 0, 256, 100, 256, 1.0,
+                               A2.data_ptr(), 256, B2.data_ptr(), 200, 0.0, C2.data_ptr(), 100,
                                fgemm.FGEMM_BF16, epi, fgemm.current_stream(), check=False)
     assert st == fgemm.FGEMM_ERR_NOT_SUPPORTED
     torch.cuda.synchronize()
@@ -130,3 +134,141 @@ def test_large_shapes_sampled(dtype, M, N, K, depth, variant):
     rows = inputs.sample_rows(M, 16, 10)
     _, Q, _ = oracle.gemm(A, B, dtype=dtype, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= STRASSEN_TOL
+
+
+# ------------------------------------------------------------ epilogues in the post-add
+def check_row_stats(ss_gpu, C_bits, ss_ref, Q_bits, dtype):
+    """Row sums of squares of the Strassen path.  They are of the rounded, written
+    rows, so (1) they must match the fp64 sums of squares of the GPU's own output
+    rows within the statistics bound, and (2) they may differ from the oracle's
+    statistics (of Q(D)) only as far as the row itself differs: for y' = y + d,
+    |sum y'^2 - sum y^2| / sum y^2 <= 2 e + e^2 with e = ||d|| / ||y|| (Cauchy-Schwarz),
+    and e is what the Strassen output bound already allows."""
+    y = oracle.decode(C_bits, dtype)
+    own = np.sum(y * y, axis=1)
+    assert np.max(np.abs(ss_gpu - own) / own) <= STATS_TOL
+    yr = oracle.decode(Q_bits, dtype)
+    e = np.sqrt(np.sum((y - yr) ** 2, axis=1) / np.sum(yr * yr, axis=1))
+    assert np.all(np.abs(ss_gpu - ss_ref) / ss_ref <= 2 * e + e * e + STATS_TOL * 1e-2)
+
+
+def dev_f32(values):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("variant", [S69, WIN])
+@pytest.mark.parametrize("depth", [1, 2])
+def test_rowsumsq_and_bias_exact_integers(dtype, variant, depth):
+    """Integer A, B and bias: the output and every row sum of squares (integers
+    below 2^24) are exact, so both must equal the oracle's bit for bit."""
+    import torch
+    M, N, K = 128, 192, 64
+    say(f"strassen rowsumsq+bias exact dtype={dtype} v={variant} d={depth}")
+    A, B = operands(M, N, K, False, False, 611, dtype, "int")
+    bias = inputs.integers((N,), 613, dtype, -3, 3)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    _, Q, ss = oracle.gemm(A, B, dtype=dtype, epi=flags, bias=bias)
+    Ad, Bd, bd = to_dev(A, dtype), to_dev(B, dtype), to_dev(bias[None, :], dtype)
+    Cd = empty_out(M, N, dtype)
+    ssd = dev_f32(np.full(M, np.nan))
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ, bias=bd.data_ptr(),
+                              rowsumsq=ssd.data_ptr())
+    handle().gemm(Ad, Bd, Cd, epilogue=epi, plan=fgemm.strassen_plan(depth, variant))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(Cd), Q)
+    assert np.array_equal(ssd.cpu().numpy().astype(np.float64), ss)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("variant", [S69, WIN])
+@pytest.mark.parametrize("depth", [1, 2])
+def test_rowsumsq_bias_beta_random(dtype, variant, depth):
+    import torch
+    M, N, K = 256, 320, 512
+    say(f"strassen rowsumsq+bias+beta dtype={dtype} v={variant} d={depth}")
+    A, B = operands(M, N, K, True, False, 621, dtype, "uniform")
+    C = inputs.uniform((M, N), 623, dtype)
+    bias = inputs.uniform((N,), 624, dtype)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    _, Q, ss = oracle.gemm(A, B, transA=True, alpha=0.75, beta=0.5, C=C, dtype=dtype, epi=flags,
+                           bias=bias)
+    Ad, Bd, Cd, bd = to_dev(A, dtype), to_dev(B, dtype), to_dev(C, dtype), to_dev(bias[None, :], dtype)
+    ssd = dev_f32(np.full(M, np.nan))
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ, bias=bd.data_ptr(),
+                              rowsumsq=ssd.data_ptr())
+    handle().gemm(Ad, Bd, Cd, transA=True, alpha=0.75, beta=0.5, epilogue=epi,
+                  plan=fgemm.strassen_plan(depth, variant))
+    torch.cuda.synchronize()
+    got = from_dev(Cd)
+    assert rel_err(got, Q, dtype) <= STRASSEN_TOL
+    check_row_stats(ssd.cpu().numpy().astype(np.float64), got, ss, Q, dtype)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("variant", [S69, WIN])
+@pytest.mark.parametrize("depth", [1, 2])
+@pytest.mark.parametrize("transB", [False, True])
+def test_rms_swiglu(dtype, variant, depth, transB):
+    """op(B) = [gate | up] with 2N columns; the Strassen split of those columns is the
+    gate/up boundary, so the post-add forms silu(r*g)*(r*u) + beta*C."""
+    import torch
+    M, K, N = 256, 256, 192
+    say(f"strassen rms_swiglu dtype={dtype} v={variant} d={depth} tB={transB}")
+    X = inputs.normal((M, K), 631, dtype)
+    W = inputs.normal((K, 2 * N), 632, dtype, std=0.1)
+    ss = (np.random.default_rng(633).uniform(0.5, 2.0, M) * 4096).astype(np.float32)
+    C = inputs.normal((M, N), 634, dtype)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_RMS_SWIGLU,
+                          rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6, beta=0.5, C=C,
+                          alpha=1.5)
+    Wst = np.ascontiguousarray(W.T) if transB else W
+    Xd, Wd, Cd = to_dev(X, dtype), to_dev(Wst, dtype), to_dev(C, dtype)
+    ssd = dev_f32(ss)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(), rms_n=4096,
+                              rms_eps=1e-6)
+    handle().gemm(Xd, Wd, Cd, transB=transB, alpha=1.5, beta=0.5, epilogue=epi,
+                  plan=fgemm.strassen_plan(depth, variant))
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= STRASSEN_TOL
+
+
+@pytest.mark.parametrize("depth", [1, 2])
+def test_fused_chain_llm_size_on_strassen(depth):
+    """The fused chain at its configured size, both GEMMs forced onto Winograd: X
+    [8192 x 4096] N(0,1), W [4096 x 4096] and W2 [4096 x 2*11008] N(0,0.02); GEMM1
+    writes Y and its row sums of squares, GEMM2 applies the RMS scale and SwiGLU.
+    Sampled rows against the oracle, each GEMM on the inputs it was given."""
+    import torch
+    dtype, M, H, F = BF16, 8192, 4096, 11008
+    say(f"strassen chain 8192x4096 -> 2x11008 d={depth}")
+    X = inputs.normal((M, H), 4001, dtype)
+    W = inputs.normal((H, H), 4002, dtype, std=0.02)
+    W2 = inputs.normal((H, 2 * F), 4003, dtype, std=0.02)
+    Xd, Wd, W2d = to_dev(X, dtype), to_dev(W, dtype), to_dev(W2, dtype)
+    Yd = empty_out(M, H, dtype)
+    ssd = dev_f32(np.full(M, np.nan))
+    Od = empty_out(M, F, dtype)
+    e1 = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
+    e2 = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(), rms_n=H,
+                             rms_eps=1e-6)
+    plan = fgemm.strassen_plan(depth, WIN)
+    handle().gemm(Xd, Wd, Yd, epilogue=e1, plan=plan)
+    handle().gemm(Yd, W2d, Od, epilogue=e2, plan=plan)
+    torch.cuda.synchronize()
+    Y, ss, O = from_dev(Yd), ssd.cpu().numpy().astype(np.float64), from_dev(Od)
+    rows = inputs.sample_rows(M, 24, 9)
+    _, Yq, ssr = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_ROWSUMSQ, rows=rows)
+    assert rel_err(Y[rows], Yq, dtype) <= STRASSEN_TOL
+    check_row_stats(ss[rows], Y[rows], ssr, Yq, dtype)
+    # GEMM2 against the oracle on the inputs it was given (the GPU's Y rows and
+    # statistics): each Strassen GEMM is held to its own bound; the chain end to end
+    # compounds two of them and is reported only
+    _, Oq, _ = oracle.gemm(Y[rows], W2, dtype=dtype, epi=oracle.EPI_RMS_SWIGLU, rms_ss=ss[rows],
+                           rms_n=H, rms_eps=1e-6)
+    assert rel_err(O[rows], Oq, dtype) <= STRASSEN_TOL
+    _, Oe, _ = oracle.gemm(Yq, W2, dtype=dtype, epi=oracle.EPI_RMS_SWIGLU, rms_ss=ssr, rms_n=H,
+                           rms_eps=1e-6)
+    print(f"[chain d={depth}] end-to-end rel err vs the oracle's chain: "
+          f"{rel_err(O[rows], Oe, dtype):.3e}")
