@@ -9,7 +9,9 @@ What it computes (see the header of ``oracle.c`` for the passages it follows):
 
 * ``gemm``       D = alpha*op(A)*op(B) + beta*C_in (+ bias), out = RNE(D) to the
                  16-bit type; optional per-row sum of squares of the written row,
-                 or the RMS row scale followed by SwiGLU (B then holds gate|up).
+                 or the RMS row scale followed by SwiGLU (B then holds gate|up), or
+                 an activation (ReLU, SiLU, tanh-form GELU) or the interleaved-pair
+                 rotary position embedding applied before the rounding.
 * ``strassen``   the same product through 1 or 2 levels of the Strassen (1969) or
                  Winograd 2x2 block recursion, in fp64 (identity check).
 * ``decode`` / ``encode``  exact 16-bit <-> fp64 conversions, RNE on encode.
@@ -30,7 +32,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F16, BF16 = 0, 1
-EPI_BIAS, EPI_ROWSUMSQ, EPI_RMS_SWIGLU = 1, 2, 4
+EPI_BIAS, EPI_ROWSUMSQ, EPI_RMS_SWIGLU, EPI_ACT, EPI_ROPE = 1, 2, 4, 8, 16
+ACT_RELU, ACT_SILU, ACT_GELU_TANH = 1, 2, 3
 S69, WINOGRAD = 0, 1
 
 _lib = None
@@ -65,6 +68,12 @@ def _load():
                                 u16p, i64, u16p, i64, ctypes.c_double, u16p, i64, ctypes.c_int,
                                 ctypes.c_int, u16p, f64p, i64, ctypes.c_double, i64p, i64,
                                 f64p, u16p, f64p, ctypes.c_int]
+    lib.oracle_gemm_ex.restype = ctypes.c_int
+    lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
+                                   u16p, i64, u16p, i64, ctypes.c_double, u16p, i64, ctypes.c_int,
+                                   ctypes.c_int, u16p, f64p, i64, ctypes.c_double, ctypes.c_int,
+                                   i64p, i64, ctypes.c_double, i64p, i64, f64p, u16p, f64p,
+                                   ctypes.c_int]
     lib.oracle_strassen.restype = ctypes.c_int
     lib.oracle_strassen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, i64, u16p,
                                     i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p]
@@ -107,14 +116,18 @@ def encode(x: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def gemm(A, B, *, transA=False, transB=False, alpha=1.0, beta=0.0, C=None, dtype=BF16,
-         epi=0, bias=None, rms_ss=None, rms_n=0, rms_eps=1e-6, rows=None, threads=None):
+         epi=0, bias=None, rms_ss=None, rms_n=0, rms_eps=1e-6, act=0, rope_pos=None,
+         rope_head_dim=0, rope_theta=10000.0, rows=None, threads=None):
     """Reference GEMM on 16-bit bit patterns.
 
     A is M x K (or K x M when transA), B is K x N (or N x K when transB), both
     uint16 row-major.  Returns (D, Q, ss) for the selected rows: D the unrounded
     fp64 result, Q its RNE 16-bit bits, ss the per-row sum of squares of the
     written row (ROWSUMSQ only, else None).  For EPI_RMS_SWIGLU, rms_ss holds
-    the fp64 sums of squares of the selected rows.
+    the fp64 sums of squares of the selected rows.  EPI_ACT applies activation
+    `act` (ACT_RELU, ACT_SILU, ACT_GELU_TANH) and EPI_ROPE the rotary embedding
+    with positions rope_pos (one per row of the output, all M rows), head width
+    rope_head_dim and base rope_theta, both to alpha*acc + beta*C + bias.
     """
     A, B = _u16(A), _u16(B)
     M = A.shape[1] if transA else A.shape[0]
@@ -138,14 +151,18 @@ def gemm(A, B, *, transA=False, transB=False, alpha=1.0, beta=0.0, C=None, dtype
         rms_ss = np.ascontiguousarray(rms_ss, dtype=np.float64)
         if rms_ss.size != nrows:
             raise ValueError("rms_ss must hold one value per selected row")
+    pos = None
+    if epi & EPI_ROPE:
+        pos = np.ascontiguousarray(np.asarray(rope_pos, dtype=np.int64)[rows])
     D = np.empty((nrows, Nout), dtype=np.float64)
     Q = np.empty((nrows, Nout), dtype=np.uint16)
     ss = np.empty(nrows, dtype=np.float64) if epi & EPI_ROWSUMSQ else None
-    rc = _load().oracle_gemm(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), A.shape[1],
-                             _ptr(B), B.shape[1], float(beta), _ptr(C),
-                             0 if C is None else C.shape[1], dtype, epi, _ptr(bias), _ptr(rms_ss),
-                             rms_n, float(rms_eps), _ptr(rows), nrows, _ptr(D), _ptr(Q), _ptr(ss),
-                             threads or default_threads())
+    rc = _load().oracle_gemm_ex(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
+                                A.shape[1], _ptr(B), B.shape[1], float(beta), _ptr(C),
+                                0 if C is None else C.shape[1], dtype, epi, _ptr(bias),
+                                _ptr(rms_ss), rms_n, float(rms_eps), int(act), _ptr(pos),
+                                int(rope_head_dim), float(rope_theta), _ptr(rows), nrows, _ptr(D),
+                                _ptr(Q), _ptr(ss), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return D, Q, ss

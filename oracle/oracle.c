@@ -34,6 +34,16 @@
  *   - RMS_SWIGLU: r_i = 1/sqrt(ss_i/n + eps); g = r_i*alpha*H[i][j],
  *     u = r_i*alpha*H[i][j+Nout]; out = Q(silu(g)*u + beta*C_in[i][j]);
  *     silu(x) = x/(1+exp(-x)); B then has 2*Nout columns (gate block, up block).
+ *   - ACT and ROPE (the same note's opening and CODA sections: elementwise work and
+ *     RoPE run in the epilogue) transform the full linear result before rounding:
+ *     out = Q(T(alpha*acc + beta*C_in + bias)).
+ *     ACT: relu(x) = max(x, 0); silu as above; gelu = the tanh approximation of
+ *     Hendrycks and Gimpel, 0.5*x*(1 + tanh(sqrt(2/pi)*(x + 0.044715*x^3))).
+ *     ROPE: rotary position embedding of Su et al. (RoFormer) on interleaved pairs:
+ *     column j lies in head j / hd at offset d = j % hd, pair p = d / 2 rotates by
+ *     theta_ij = pos_i * base^(-2p/hd):
+ *       y[2p] = x[2p] cos(theta) - x[2p+1] sin(theta)
+ *       y[2p+1] = x[2p] sin(theta) + x[2p+1] cos(theta).
  *   - Strassen recursion keeps fp64 temporaries (it is the exact identity check).
  */
 #include <math.h>
@@ -48,6 +58,12 @@
 #define OR_EPI_BIAS 1
 #define OR_EPI_ROWSUMSQ 2
 #define OR_EPI_RMS_SWIGLU 4
+#define OR_EPI_ACT 8
+#define OR_EPI_ROPE 16
+
+#define OR_ACT_RELU 1
+#define OR_ACT_SILU 2
+#define OR_ACT_GELU_TANH 3
 
 /* ---------------------------------------------------------------------------
  * 16-bit decode: exact value of an IEEE binary16 or bfloat16 bit pattern.
@@ -206,6 +222,16 @@ static int raw_products(int transA, int transB, int64_t M, int64_t N, int64_t K,
 
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 
+static double activation(int act, double x) {
+    const double pi = 3.14159265358979323846;
+    switch (act) {
+        case OR_ACT_RELU: return x > 0.0 ? x : 0.0;
+        case OR_ACT_SILU: return silu(x);
+        case OR_ACT_GELU_TANH: return 0.5 * x * (1.0 + tanh(sqrt(2.0 / pi) * (x + 0.044715 * x * x * x)));
+    }
+    return x;
+}
+
 /*
  * oracle_gemm: classical reference with the epilogues.
  *   N is the width of op(B) (for RMS_SWIGLU, N = 2*Nout and the output is Nout wide).
@@ -214,13 +240,20 @@ static double silu(double x) { return x / (1.0 + exp(-x)); }
  *   Q (nrows x Nout, 16-bit RNE bits), ss (nrows, only for ROWSUMSQ).
  * Returns 0 on success, -1 on bad arguments.
  */
-int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
-                const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, double beta,
-                const uint16_t* Cin, int64_t ldc, int dtype, int epi, const uint16_t* bias,
-                const double* rms_ss, int64_t rms_n, double rms_eps, const int64_t* rows,
-                int64_t nrows, double* D, uint16_t* Q, double* ss, int nthreads) {
+int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, double beta,
+                   const uint16_t* Cin, int64_t ldc, int dtype, int epi, const uint16_t* bias,
+                   const double* rms_ss, int64_t rms_n, double rms_eps, int act,
+                   const int64_t* rope_pos, int64_t rope_hd, double rope_base,
+                   const int64_t* rows, int64_t nrows, double* D, uint16_t* Q, double* ss,
+                   int nthreads) {
     int swiglu = (epi & OR_EPI_RMS_SWIGLU) != 0;
-    if (swiglu && (epi & (OR_EPI_BIAS | OR_EPI_ROWSUMSQ))) return -1;
+    int rope = (epi & OR_EPI_ROPE) != 0;
+    if (swiglu && (epi & (OR_EPI_BIAS | OR_EPI_ROWSUMSQ | OR_EPI_ACT | OR_EPI_ROPE))) return -1;
+    if ((epi & OR_EPI_ACT) && rope) return -1;
+    if ((epi & OR_EPI_ACT) && (act < OR_ACT_RELU || act > OR_ACT_GELU_TANH)) return -1;
+    if (rope && (rope_hd <= 0 || rope_hd % 2 || N % rope_hd || !rope_pos || !(rope_base > 0.0)))
+        return -1;
     if (swiglu && (N % 2)) return -1;
     int64_t Nout = swiglu ? N / 2 : N;
     for (int64_t r = 0; r < nrows; ++r)
@@ -248,8 +281,21 @@ int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double 
             }
             if (beta != 0.0) d += beta * oracle_decode(Cin[i * ldc + j], dtype);
             if (epi & OR_EPI_BIAS) d += oracle_decode(bias[j], dtype);
-            uint16_t q = oracle_encode(d, dtype);
+            if (epi & OR_EPI_ACT) d = activation(act, d);
             D[r * Nout + j] = d;
+        }
+        if (rope) {
+            /* rotate each interleaved pair of the row's linear results */
+            for (int64_t j = 0; j < Nout; j += 2) {
+                int64_t p = (j % rope_hd) / 2;
+                double theta = (double)rope_pos[r] * pow(rope_base, -2.0 * (double)p / (double)rope_hd);
+                double x0 = D[r * Nout + j], x1 = D[r * Nout + j + 1];
+                D[r * Nout + j] = x0 * cos(theta) - x1 * sin(theta);
+                D[r * Nout + j + 1] = x0 * sin(theta) + x1 * cos(theta);
+            }
+        }
+        for (int64_t j = 0; j < Nout; ++j) {
+            uint16_t q = oracle_encode(D[r * Nout + j], dtype);
             Q[r * Nout + j] = q;
             if (epi & OR_EPI_ROWSUMSQ) {
                 double qv = oracle_decode(q, dtype);
@@ -260,6 +306,17 @@ int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double 
     }
     free(H);
     return 0;
+}
+
+int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, double beta,
+                const uint16_t* Cin, int64_t ldc, int dtype, int epi, const uint16_t* bias,
+                const double* rms_ss, int64_t rms_n, double rms_eps, const int64_t* rows,
+                int64_t nrows, double* D, uint16_t* Q, double* ss, int nthreads) {
+    if (epi & (OR_EPI_ACT | OR_EPI_ROPE)) return -1;
+    return oracle_gemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, Cin, ldc, dtype,
+                          epi, bias, rms_ss, rms_n, rms_eps, 0, NULL, 0, 0.0, rows, nrows, D, Q,
+                          ss, nthreads);
 }
 
 /* ---------------------------------------------------------------------------

@@ -284,3 +284,104 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.strassen(inputs.normal((6, 6), 1, BF16), inputs.normal((6, 6), 2, BF16),
                         depth=2, variant=0)
+
+
+# ---------------------------------------------------------------- activation and RoPE
+def identity_gemm(values, dtype, **kw):
+    """A = I (n x n): D = alpha * B + ..., so the epilogue sees B's values directly."""
+    B = inputs.to_bits(np.asarray(values, dtype=np.float64), dtype)
+    n = B.shape[0]
+    A = ints_to_bits(np.eye(n), dtype)
+    return oracle.gemm(A, B, dtype=dtype, **kw)
+
+
+def test_activation_closed_forms_and_identities():
+    xs = np.array([[-3.0, -1.0, -0.5, 0.0, 0.5, 1.0, 3.0, 8.0]])
+    x = np.vstack([xs, -xs])                       # row 1 holds -x
+    # ReLU: max(x, 0) exactly
+    D, _, _ = identity_gemm(x, BF16, epi=oracle.EPI_ACT, act=oracle.ACT_RELU)
+    assert np.array_equal(D, np.where(x > 0, x, 0.0))
+    # SiLU: silu(0) = 0 and silu(x) - silu(-x) = x (x*s(x) + x*s(-x) = x)
+    D, _, _ = identity_gemm(x, BF16, epi=oracle.EPI_ACT, act=oracle.ACT_SILU)
+    assert D[0, 3] == 0.0
+    assert np.allclose(D[0] - D[1], x[0], rtol=0, atol=1e-15)
+    assert D[0, 7] == pytest.approx(8.0 / (1.0 + np.exp(-8.0)), rel=1e-15)
+    # GELU (tanh form): gelu(x) - gelu(-x) = x, gelu(0) = 0, and within the
+    # approximation's error of the exact x * Phi(x)
+    D, _, _ = identity_gemm(x, BF16, epi=oracle.EPI_ACT, act=oracle.ACT_GELU_TANH)
+    assert D[0, 3] == 0.0
+    assert np.allclose(D[0] - D[1], x[0], rtol=0, atol=1e-14)
+    from math import erf, sqrt
+    exact = np.array([v * 0.5 * (1.0 + erf(v / sqrt(2.0))) for v in x[0]])
+    assert np.max(np.abs(D[0] - exact)) < 5e-4
+    assert not np.array_equal(D[0], exact)         # it is the approximation, not erf
+    # the activation acts on alpha*acc + beta*C + bias: with alpha = -1 ReLU clips the
+    # other half; with a bias the argument shifts
+    D, _, _ = identity_gemm(x, BF16, alpha=-1.0, epi=oracle.EPI_ACT, act=oracle.ACT_RELU)
+    assert np.array_equal(D, np.where(-x > 0, -x, 0.0))
+    bias = inputs.to_bits(np.full(8, 0.5), BF16)
+    D, _, _ = identity_gemm(x, BF16, epi=oracle.EPI_ACT | oracle.EPI_BIAS, act=oracle.ACT_RELU,
+                            bias=bias)
+    assert np.array_equal(D, np.where(x + 0.5 > 0, x + 0.5, 0.0))
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(7)
+    M, hd, heads = 6, 8, 3
+    N = hd * heads
+    vals = rng.integers(-8, 9, size=(M, N)).astype(np.float64)
+    pos = np.array([0, 1, 5, 2, 13, 10])
+    plain, _, _ = identity_gemm(vals, F16)
+    D, Q, _ = identity_gemm(vals, F16, epi=oracle.EPI_ROPE, rope_pos=pos, rope_head_dim=hd)
+    # position 0 rotates nothing
+    assert np.array_equal(D[0], plain[0])
+    # every interleaved pair keeps its length
+    n_in = plain[:, 0::2] ** 2 + plain[:, 1::2] ** 2
+    n_out = D[:, 0::2] ** 2 + D[:, 1::2] ** 2
+    assert np.allclose(n_out, n_in, rtol=1e-13, atol=1e-12)
+    # the first pair of every head turns by exactly `pos` radians: (1, 0) -> (cos, sin)
+    e = np.zeros((M, N))
+    e[:, 0::hd] = 1.0
+    De, _, _ = identity_gemm(e, F16, epi=oracle.EPI_ROPE, rope_pos=pos, rope_head_dim=hd)
+    for h in range(heads):
+        assert np.allclose(De[:, h * hd], np.cos(pos), atol=1e-15)
+        assert np.allclose(De[:, h * hd + 1], np.sin(pos), atol=1e-15)
+    # heads repeat the same frequencies: identical inputs rotate identically
+    same = np.tile(vals[:, :hd], (1, heads))
+    Ds, _, _ = identity_gemm(same, F16, epi=oracle.EPI_ROPE, rope_pos=pos, rope_head_dim=hd)
+    for h in range(1, heads):
+        assert np.array_equal(Ds[:, h * hd:(h + 1) * hd], Ds[:, :hd])
+    # relative positions: the pairwise dot products of rows 1 and 2 rotated to
+    # positions (5, 2) and to (13, 10) agree (they depend on the difference only)
+    two = np.vstack([vals[1], vals[2], vals[1], vals[2]])
+    Dr, _, _ = identity_gemm(two, F16, epi=oracle.EPI_ROPE, rope_pos=np.array([5, 2, 13, 10]),
+                             rope_head_dim=hd)
+    dots_a = Dr[0, 0::2] * Dr[1, 0::2] + Dr[0, 1::2] * Dr[1, 1::2]
+    dots_b = Dr[2, 0::2] * Dr[3, 0::2] + Dr[2, 1::2] * Dr[3, 1::2]
+    assert np.allclose(dots_a, dots_b, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_hand_worked_angle():
+    # head width 4, base 10000: pair 1 turns by pos * 10000^(-1/2) = pos / 100, so
+    # position 100 turns (1, 0) by one radian and (0, 1) to (-sin 1, cos 1)
+    x = np.array([[0.0, 0.0, 1.0, 0.0], [0.0, 0.0, 0.0, 1.0]])
+    D, _, _ = identity_gemm(x, F16, epi=oracle.EPI_ROPE, rope_pos=np.array([100, 100]),
+                            rope_head_dim=4, rope_theta=10000.0)
+    assert D[0, 2:] == pytest.approx([0.5403023058681398, 0.8414709848078965], abs=1e-15)
+    assert D[1, 2:] == pytest.approx([-0.8414709848078965, 0.5403023058681398], abs=1e-15)
+    # pair 0 of the same rows turns by 100 rad
+    y = np.array([[1.0, 0.0, 0.0, 0.0]])
+    D, _, _ = identity_gemm(y, F16, epi=oracle.EPI_ROPE, rope_pos=np.array([100]),
+                            rope_head_dim=4)
+    assert D[0, :2] == pytest.approx([0.8623188722876839, -0.5063656411097588], abs=1e-15)
+
+
+def test_act_and_rope_argument_checks():
+    x = np.ones((2, 8))
+    with pytest.raises(ValueError):
+        identity_gemm(x, BF16, epi=oracle.EPI_ACT, act=7)
+    with pytest.raises(ValueError):   # head width must divide N and be even
+        identity_gemm(x, BF16, epi=oracle.EPI_ROPE, rope_pos=[0, 1], rope_head_dim=3)
+    with pytest.raises(ValueError):   # one transform at a time
+        identity_gemm(x, BF16, epi=oracle.EPI_ROPE | oracle.EPI_ACT, act=1, rope_pos=[0, 1],
+                      rope_head_dim=4)
