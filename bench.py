@@ -16,7 +16,9 @@ The same JSON line carries
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (a seeded subset of output rows), with the threads it used;
   workloads     the other shapes: 4096^3 and TN layouts, LLM projection/FFN and
-                decode shapes (decode as HBM GB/s), the fused two-GEMM chain, and
+                decode shapes (decode as HBM GB/s), the projection with RoPE and the
+                FFN up projection with bias + GELU, the fused two-GEMM chain (also on
+                the Strassen path), and
                 Strassen/Winograd vs classical at 16384^3 and 32768x8192x8192 with
                 the model's pick and its regret against the measured best.
 """
@@ -191,12 +193,13 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     reps = max(5, args.steps // 5)
 
     def gemm_case(name, M, N, K, transA=False, beta=0.0, dtype=torch.bfloat16, std_b=1.0,
-                  plan=None, seeds=(1, 2, 3), gen_fn=None, bytes_alg=None):
+                  plan=None, seeds=(1, 2, 3), gen_fn=None, bytes_alg=None, epilogue=None):
         gen_fn = gen_fn or (lambda s, seed, std: normal(s, seed, std, dtype))
         A = gen_fn((K, M) if transA else (M, K), seeds[0], 1.0)
         B = gen_fn((K, N), seeds[1], std_b)
         C = gen_fn((M, N), seeds[2], 1.0)
-        ms = timer.time(lambda: h.gemm(A, B, C, transA=transA, beta=beta, plan=plan), reps, 3)
+        ms = timer.time(lambda: h.gemm(A, B, C, transA=transA, beta=beta, plan=plan,
+                                       epilogue=epilogue), reps, 3)
         r = {"ms": round(ms, 5), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
         if bytes_alg:
             r["hbm_gbps"] = round(bytes_alg / (ms * 1e-3) / 1e9, 1)
@@ -219,6 +222,19 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
         K, N = 4096, 14336
         gemm_case(f"bf16_decode_{M}x{N}x{K}", M, N, K, std_b=0.02, seeds=(3001, 3002, 3003),
                   bytes_alg=2.0 * (K * N + M * K + M * N))
+    # prefill shapes with the transform epilogues: RoPE on the projection (32 heads of
+    # 128, four sequences of 4096 positions) and bias + GELU on the FFN up projection
+    pos = (torch.arange(16384, device="cuda", dtype=torch.int32) % 4096).contiguous()
+    gemm_case("bf16_prefill_16384x4096x4096_rope", 16384, 4096, 4096, std_b=0.02,
+              seeds=(3001, 3002, 3003),
+              epilogue=fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE, rope_positions=pos.data_ptr(),
+                                           rope_head_dim=128, rope_theta=10000.0))
+    bias = normal((14336,), 3004, 0.02)
+    gemm_case("bf16_prefill_16384x14336x4096_bias_gelu", 16384, 14336, 4096, std_b=0.02,
+              seeds=(3001, 3002, 3003),
+              epilogue=fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT | fgemm.FGEMM_EPI_BIAS,
+                                           bias=bias.data_ptr(), act=fgemm.FGEMM_ACT_GELU_TANH))
+    del pos, bias
 
     # fused chain: GEMM1 + row sums of squares, GEMM2 + RMS scale + SwiGLU
     Mc, Hc, Fc = 8192, 4096, 11008

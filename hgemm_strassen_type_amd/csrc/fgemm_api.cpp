@@ -6,6 +6,7 @@
 // input from the caller; a per-shape plan cache keeps the query cost far below the
 // kernels' own time (Results: model overhead under half a percent).
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string.h>
 
 #include <mutex>
@@ -241,6 +242,17 @@ struct Call {
   hipStream_t stream;
 };
 
+// Activation or rotary-embedding parameters of an epilogue, as the kernels take them.
+void set_transform(const fgemm_epilogue_t* e, int* act, int* rope_hd, const int32_t** rope_pos,
+                   int64_t* rope_off, double* rope_log2_base) {
+  const uint32_t flags = epi_flags(e);
+  *act = (flags & FGEMM_EPI_ACT) ? e->act : 0;
+  *rope_hd = (flags & FGEMM_EPI_ROPE) ? (int)e->rope_head_dim : 0;
+  *rope_pos = (flags & FGEMM_EPI_ROPE) ? e->rope_positions : nullptr;
+  *rope_off = (flags & FGEMM_EPI_ROPE) ? e->rope_offset : 0;
+  *rope_log2_base = (flags & FGEMM_EPI_ROPE) ? log2((double)e->rope_theta) : 0.0;
+}
+
 fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c, int vec) {
   const uint32_t flags = epi_flags(c.epi);
   int tile = tile_id(plan.tile_m, plan.tile_n);
@@ -271,12 +283,14 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     p.rms_inv_n = 1.0f / (float)c.epi->rms_n;
     p.rms_eps = c.epi->rms_eps;
   }
+  const bool xform = (flags & (FGEMM_EPI_ACT | FGEMM_EPI_ROPE)) != 0;
+  if (xform) set_transform(c.epi, &p.act, &p.rope_hd, &p.rope_pos, &p.rope_off, &p.rope_log2_base);
   KernelKey k{};
   k.tile = tile;
   k.a_kcontig = c.ta == FGEMM_OP_N;
   k.b_kcontig = c.tb == FGEMM_OP_T;
   k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
-  k.epi = swiglu ? kEpiSwiGLU : kEpiStore16;
+  k.epi = swiglu ? kEpiSwiGLU : xform ? kEpiTransform : kEpiStore16;
   k.vec = vec;
   if (plan.split_k > 1) {
     // fp32 K slices into the workspace, then the epilogue in the finalize pass
@@ -395,6 +409,8 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
       pa.rowsumsq = c.epi->rowsumsq;
       pa.ss_partial = run.ss_partial;
     }
+    if (flags & (FGEMM_EPI_ACT | FGEMM_EPI_ROPE))
+      set_transform(c.epi, &pa.act, &pa.rope_hd, &pa.rope_pos, &pa.rope_off, &pa.rope_log2_base);
     if (flags & FGEMM_EPI_RMS_SWIGLU) {
       pa.swiglu = 1;
       pa.rms_ss = c.epi->rms_rowsumsq;
@@ -509,10 +525,22 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
   if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
   if (M > INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX) return FGEMM_ERR_NOT_SUPPORTED;
   const uint32_t flags = epi_flags(epi);
-  if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU))
+  if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU |
+                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE))
     return FGEMM_ERR_INVALID_VALUE;
   const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
-  if (swiglu && (flags & (FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ))) return FGEMM_ERR_NOT_SUPPORTED;
+  if (swiglu && (flags & (FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_ACT | FGEMM_EPI_ROPE)))
+    return FGEMM_ERR_NOT_SUPPORTED;
+  // one transform before the rounding: an activation or the rotary embedding
+  if ((flags & FGEMM_EPI_ACT) && (flags & FGEMM_EPI_ROPE)) return FGEMM_ERR_NOT_SUPPORTED;
+  if ((flags & FGEMM_EPI_ACT) &&
+      (epi->act != FGEMM_ACT_RELU && epi->act != FGEMM_ACT_SILU && epi->act != FGEMM_ACT_GELU_TANH))
+    return FGEMM_ERR_INVALID_VALUE;
+  if (flags & FGEMM_EPI_ROPE) {
+    const int64_t hd = epi->rope_head_dim;
+    if (hd <= 0 || hd % 2 || hd > INT32_MAX || N % hd || !(epi->rope_theta > 0.f))
+      return FGEMM_ERR_INVALID_VALUE;
+  }
   const int64_t Nb = swiglu ? 2 * N : N;
   const int64_t a_cols = ta == FGEMM_OP_N ? K : M;   // stored row width of A
   const int64_t b_cols = tb == FGEMM_OP_N ? Nb : K;  // stored row width of B

@@ -42,6 +42,7 @@
 
 #include <type_traits>
 
+#include "epilogue_ops.h"
 #include "internal.h"
 
 namespace fgemm {
@@ -769,8 +770,9 @@ struct GemmTile {
     const int lr = lane % MI, lc = lane / MI;  // lane's row and column slot in a block
     const int orow = lane / LPR, oc = lane % LPR;
     const bool use_beta = EPI != kEpiStore32 && (P.flags & kFlagBeta) != 0;
-    const bool use_bias = EPI == kEpiStore16 && (P.flags & kFlagBias) != 0;
-    const bool use_ss = EPI == kEpiStore16 && (P.flags & kFlagRowSumSq) != 0;
+    constexpr bool STORE16 = EPI == kEpiStore16 || EPI == kEpiTransform;
+    const bool use_bias = STORE16 && (P.flags & kFlagBias) != 0;
+    const bool use_ss = STORE16 && (P.flags & kFlagRowSumSq) != 0;
     const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
     const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
     // beta*C: every whole 8-column piece of the wave's tile is requested up front so
@@ -829,7 +831,7 @@ struct GemmTile {
                 }
               } else {
                 v = v4f{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-                if (EPI == kEpiStore16) v = v * P.alpha;
+                if (STORE16) v = v * P.alpha;
               }
               // row ib*MI + lr of the band; 16-byte chunk of columns
               // jj*MI + g*(256/MI) + 4*lc
@@ -882,6 +884,9 @@ struct GemmTile {
 #pragma unroll
               for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
             }
+            if constexpr (EPI == kEpiTransform)
+              apply_transform<8>(P.act, P.rope_pos, P.rope_off, P.rope_hd, P.rope_log2_base, row,
+                                 col, v);
             uint32_t o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -952,7 +957,7 @@ struct GemmTile {
     uint16_t* C = static_cast<uint16_t*>(Cout);
     const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
     const bool use_beta = (P.flags & kFlagBeta) != 0;
-    if constexpr (EPI == kEpiStore16) {
+    if constexpr (EPI == kEpiStore16 || EPI == kEpiTransform) {
       const bool use_bias = (P.flags & kFlagBias) != 0;
       const bool use_ss = (P.flags & kFlagRowSumSq) != 0;
       const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
@@ -988,6 +993,9 @@ struct GemmTile {
 #pragma unroll
               for (int s = 0; s < 4; ++s) v[s] += s < nv ? to_f32<DT>(bias[col + s]) : 0.f;
             }
+            if constexpr (EPI == kEpiTransform)
+              apply_transform<4>(P.act, P.rope_pos, P.rope_off, P.rope_hd, P.rope_log2_base, row,
+                                 col, v);
             uint32_t o[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {

@@ -16,6 +16,7 @@ enum EpiKind : int {
   kEpiStore16 = 0,   // 16-bit output: alpha, beta*C, optional bias, optional row sum of squares
   kEpiSwiGLU = 1,    // 16-bit output of silu(r*alpha*gate) * (r*alpha*up) + beta*C
   kEpiStore32 = 2,   // fp32 output of the raw accumulators (Strassen sub-products)
+  kEpiTransform = 3, // kEpiStore16 plus an activation or the rotary embedding before rounding
 };
 
 // Runtime epilogue switches inside kEpiStore16.
@@ -36,6 +37,12 @@ struct GemmProblem {
   float* ss_partial;    // [tiles_n * 2][M] per-wave-column partial sums of squares
   const float* rms_ss;  // [M] sums of squares for the RMS scale
   float rms_inv_n, rms_eps;
+  // kEpiTransform: act != 0 applies that activation, else the rotary embedding
+  int act;
+  int rope_hd;
+  const int32_t* rope_pos;  // [M] positions, or null: row + rope_off
+  int64_t rope_off;
+  double rope_log2_base;
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).
@@ -129,6 +136,9 @@ struct PostAddArgs {
   float* rowsumsq; float* ss_partial;
   int swiglu;
   const float* rms_ss; float rms_inv_n, rms_eps;
+  // act != 0 or rope_hd != 0: the activation or the rotary embedding before rounding
+  int act; int rope_hd;
+  const int32_t* rope_pos; int64_t rope_off; double rope_log2_base;
 };
 hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
 // Row-sum partials per output row the post-add writes for sub-block width n.

@@ -25,6 +25,7 @@
 // flight (the four sub-blocks, the seven products, or four rows).
 #include <hip/hip_runtime.h>
 
+#include "epilogue_ops.h"
 #include "internal.h"
 
 namespace fgemm {
@@ -229,6 +230,8 @@ struct PostAddKArgs {
   float* ss_partial;   // [gridDim.x][2m] row-sum partials (null: no statistics)
   int swiglu;
   const float* rms_ss; float rms_inv_n, rms_eps;
+  int act; int rope_hd;
+  const int32_t* rope_pos; int64_t rope_off; double rope_log2_base;
 };
 
 __device__ __forceinline__ void combine(int variant, const float (&p)[7], float* c) {
@@ -330,6 +333,9 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
               v[2] += h2f(bv.y & 0xffffu, a.dt);
               v[3] += h2f(bv.y >> 16, a.dt);
             }
+            if (a.act || a.rope_hd)
+              apply_transform<4>(a.act, a.rope_pos, a.rope_off, a.rope_hd, a.rope_log2_base,
+                                 (int)row, (int)col, v);
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -440,6 +446,12 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
   a.rms_ss = in.rms_ss;
   a.rms_inv_n = in.rms_inv_n;
   a.rms_eps = in.rms_eps;
+  a.act = in.act;
+  a.rope_hd = in.rope_hd;
+  a.rope_pos = in.rope_pos;
+  a.rope_off = in.rope_off;
+  a.rope_log2_base = in.rope_log2_base;
+  if ((a.act || a.rope_hd) && (a.out32 || !in.C || a.swiglu)) return hipErrorInvalidValue;
   if (a.n % 4) return hipErrorInvalidValue;
   const bool stats = in.rowsumsq != nullptr;
   if ((stats || a.swiglu) && (a.out32 || !in.C)) return hipErrorInvalidValue;

@@ -20,6 +20,8 @@ FGEMM_ERR_WORKSPACE, FGEMM_ERR_ALLOC, FGEMM_ERR_HIP = 3, 4, 5
 FGEMM_OP_N, FGEMM_OP_T = 0, 1
 FGEMM_F16, FGEMM_BF16 = 0, 1
 FGEMM_EPI_NONE, FGEMM_EPI_BIAS, FGEMM_EPI_ROWSUMSQ, FGEMM_EPI_RMS_SWIGLU = 0, 1, 2, 4
+FGEMM_EPI_ACT, FGEMM_EPI_ROPE = 8, 16
+FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
 FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
 
@@ -39,7 +41,10 @@ class FgemmError(RuntimeError):
 class fgemm_epilogue_t(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("bias", ctypes.c_void_p),
                 ("rowsumsq", ctypes.c_void_p), ("rms_rowsumsq", ctypes.c_void_p),
-                ("rms_n", ctypes.c_int64), ("rms_eps", ctypes.c_float)]
+                ("rms_n", ctypes.c_int64), ("rms_eps", ctypes.c_float),
+                ("act", ctypes.c_int32), ("rope_positions", ctypes.c_void_p),
+                ("rope_offset", ctypes.c_int64), ("rope_head_dim", ctypes.c_int64),
+                ("rope_theta", ctypes.c_float)]
 
 
 class fgemm_plan_t(ctypes.Structure):
@@ -137,9 +142,11 @@ def fgemm_set_model(handle: int, model: fgemm_model_t):
     _check(lib().fgemm_set_model(handle, ctypes.byref(model)), "fgemm_set_model")
 
 
-def make_epilogue(flags=0, bias=0, rowsumsq=0, rms_rowsumsq=0, rms_n=0, rms_eps=0.0):
+def make_epilogue(flags=0, bias=0, rowsumsq=0, rms_rowsumsq=0, rms_n=0, rms_eps=0.0, act=0,
+                  rope_positions=0, rope_offset=0, rope_head_dim=0, rope_theta=10000.0):
     return fgemm_epilogue_t(flags, bias or None, rowsumsq or None, rms_rowsumsq or None, rms_n,
-                            rms_eps)
+                            rms_eps, act, rope_positions or None, rope_offset, rope_head_dim,
+                            rope_theta)
 
 
 def fgemm_select(handle, transA, transB, M, N, K, dtype, epilogue=None) -> fgemm_plan_t:

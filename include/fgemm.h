@@ -71,13 +71,28 @@ typedef enum { FGEMM_F16 = 0, FGEMM_BF16 = 1 } fgemm_dtype_t;
  * RMS_SWIGLU (alone): op(B) has 2N columns, gate = columns [0, N), up = [N, 2N):
  *   r_i = 1/sqrt(rms_rowsumsq[i]/rms_n + rms_eps)
  *   g = r_i*alpha*acc_gate, u = r_i*alpha*acc_up,
- *   C[i][j] = RNE16(silu(g)*u + beta*C[i][j]),  silu(x) = x/(1+exp(-x)). */
+ *   C[i][j] = RNE16(silu(g)*u + beta*C[i][j]),  silu(x) = x/(1+exp(-x)).
+ * ACT (with BIAS and ROWSUMSQ, not with ROPE): D = act(D) before the rounding;
+ *   act is ReLU, SiLU, or GELU in the tanh form of Hendrycks and Gimpel,
+ *   0.5x(1 + tanh(sqrt(2/pi)(x + 0.044715x^3))).
+ * ROPE (with BIAS and ROWSUMSQ, not with ACT; same note, CODA section: RoPE in the
+ *   epilogue): the rotary embedding of Su et al. (RoFormer) on interleaved pairs
+ *   before the rounding.  Column j is at d = j % rope_head_dim of its head; pair
+ *   (2p, 2p+1), p = d/2, of row i turns by theta = pos_i * rope_theta^(-2p/rope_head_dim):
+ *     D[i][2p] <- D[i][2p] cos(theta) - D[i][2p+1] sin(theta)
+ *     D[i][2p+1] <- D[i][2p] sin(theta) + D[i][2p+1] cos(theta)
+ *   with pos_i = rope_positions[i], or i + rope_offset when rope_positions is NULL.
+ *   (The half-split pairing (d, d + hd/2) is this one after a fixed permutation
+ *   of op(B)'s columns within each head.) */
 enum {
     FGEMM_EPI_NONE = 0,
     FGEMM_EPI_BIAS = 1,
     FGEMM_EPI_ROWSUMSQ = 2,
-    FGEMM_EPI_RMS_SWIGLU = 4
+    FGEMM_EPI_RMS_SWIGLU = 4,
+    FGEMM_EPI_ACT = 8,
+    FGEMM_EPI_ROPE = 16
 };
+typedef enum { FGEMM_ACT_RELU = 1, FGEMM_ACT_SILU = 2, FGEMM_ACT_GELU_TANH = 3 } fgemm_act_t;
 
 typedef struct {
     uint32_t flags;             /* FGEMM_EPI_* bits                                  */
@@ -86,6 +101,11 @@ typedef struct {
     const float* rms_rowsumsq;  /* RMS_SWIGLU: device [M] fp32 input                 */
     int64_t rms_n;              /* RMS_SWIGLU: width the statistics were taken over  */
     float rms_eps;              /* RMS_SWIGLU: epsilon inside the square root        */
+    int32_t act;                /* ACT: fgemm_act_t                                   */
+    const int32_t* rope_positions; /* ROPE: device [M] positions, or NULL            */
+    int64_t rope_offset;        /* ROPE: position of row 0 when rope_positions is NULL */
+    int64_t rope_head_dim;      /* ROPE: even, divides N                              */
+    float rope_theta;           /* ROPE: frequency base (> 0), e.g. 10000             */
 } fgemm_epilogue_t;
 
 typedef enum {

@@ -117,6 +117,21 @@ def test_check_args_epilogues():
     assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU | fgemm.FGEMM_EPI_BIAS, bias=P, rms_rowsumsq=P,
                      rms_n=4096)) == NOTSUP
     assert chk(epi=E(64)) == INVAL                                         # unknown flag
+    # activation and rotary embedding: one of them, with bias and statistics
+    ACT, ROPE = fgemm.FGEMM_EPI_ACT, fgemm.FGEMM_EPI_ROPE
+    for a in (fgemm.FGEMM_ACT_RELU, fgemm.FGEMM_ACT_SILU, fgemm.FGEMM_ACT_GELU_TANH):
+        assert chk(epi=E(ACT | fgemm.FGEMM_EPI_BIAS, bias=P, act=a)) == OK
+    assert chk(epi=E(ACT, act=0)) == INVAL
+    assert chk(epi=E(ACT, act=4)) == INVAL
+    assert chk(epi=E(ROPE | fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P, rope_head_dim=16)) == OK
+    assert chk(epi=E(ROPE, rope_positions=P, rope_head_dim=64)) == OK
+    assert chk(epi=E(ROPE, rope_head_dim=0)) == INVAL
+    assert chk(epi=E(ROPE, rope_head_dim=7)) == INVAL                      # odd
+    assert chk(epi=E(ROPE, rope_head_dim=48)) == INVAL                     # does not divide N
+    assert chk(epi=E(ROPE, rope_head_dim=16, rope_theta=0.0)) == INVAL
+    assert chk(epi=E(ACT | ROPE, act=1, rope_head_dim=16)) == NOTSUP
+    assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU | ACT, rms_rowsumsq=P, rms_n=4096,
+                     act=1)) == NOTSUP
 
 
 # ---------------------------------------------------------------- decision model

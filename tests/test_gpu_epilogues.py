@@ -122,3 +122,149 @@ def test_chain_llm_size():
     say("chain 8192x4096 -> 2x11008")
     X, W, W2, Y, ss, O = run_chain(8192, 4096, 11008, 4001)
     check_chain(X, W, W2, Y, ss, O, inputs.sample_rows(8192, 24, 9), 4096)
+
+
+# ------------------------------------------------------------ activation and RoPE
+ACTS = [fgemm.FGEMM_ACT_RELU, fgemm.FGEMM_ACT_SILU, fgemm.FGEMM_ACT_GELU_TANH]
+ORACLE_ACT = {fgemm.FGEMM_ACT_RELU: oracle.ACT_RELU, fgemm.FGEMM_ACT_SILU: oracle.ACT_SILU,
+              fgemm.FGEMM_ACT_GELU_TANH: oracle.ACT_GELU_TANH}
+
+
+def run_transform(A, B, C, dtype, epi, plan=None, transB=False, alpha=1.0, beta=0.0, pad=0,
+                  M=None):
+    import torch
+    Ad, Bd = to_dev(A, dtype, pad), to_dev(B, dtype, pad)
+    Cd = to_dev(C, dtype, pad) if C is not None else empty_out(M, B.shape[0] if transB else B.shape[1], dtype)
+    handle().gemm(Ad, Bd, Cd, transB=transB, alpha=alpha, beta=beta, epilogue=epi, plan=plan)
+    torch.cuda.synchronize()
+    return from_dev(Cd)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("tile", TILES)
+def test_activation_bias_rowsumsq(dtype, act, tile):
+    """D = act(alpha*acc + beta*C + bias) before the rounding, statistics of the
+    written rows; ragged in every dimension."""
+    import torch
+    M, N, K = 300, 520, 200
+    say(f"activation dtype={dtype} act={act} tile={tile}")
+    A = inputs.normal((M, K), 701, dtype)
+    B = inputs.normal((K, N), 702, dtype, std=0.1)
+    C = inputs.normal((M, N), 703, dtype)
+    bias = inputs.normal((N,), 704, dtype)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ | oracle.EPI_ACT
+    _, Q, ss = oracle.gemm(A, B, alpha=1.25, beta=0.25, C=C, dtype=dtype, epi=flags, bias=bias,
+                           act=ORACLE_ACT[act])
+    Ad, Bd, Cd, bd = to_dev(A, dtype), to_dev(B, dtype), to_dev(C, dtype), to_dev(bias[None, :], dtype)
+    ssd = dev_f32(M)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ | fgemm.FGEMM_EPI_ACT,
+                              bias=bd.data_ptr(), rowsumsq=ssd.data_ptr(), act=act)
+    handle().gemm(Ad, Bd, Cd, alpha=1.25, beta=0.25, epilogue=epi, plan=fgemm.classical_plan(*tile))
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+    got = ssd.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ss) / ss) <= STATS_TOL
+
+
+def test_relu_exact_integers():
+    # integer products: ReLU of exact integers is exact, bit for bit on every tile
+    dtype = BF16
+    M, N, K = 130, 264, 64
+    A = inputs.integers((M, K), 711, dtype, -1, 1)
+    B = inputs.integers((K, N), 712, dtype, -1, 1)
+    _, Q, _ = oracle.gemm(A, B, dtype=dtype, epi=oracle.EPI_ACT, act=oracle.ACT_RELU)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT, act=fgemm.FGEMM_ACT_RELU)
+    for tile in TILES:
+        say(f"relu exact tile={tile}")
+        got = run_transform(A, B, None, dtype, epi, plan=fgemm.classical_plan(*tile), M=M)
+        assert np.array_equal(got, Q), tile
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("transB", [False, True])
+def test_rope_positions_and_offset(dtype, tile, transB):
+    """Interleaved-pair rotary embedding of alpha*acc + bias, head width 64, with a
+    position array (values up to 8191) and with row index + offset."""
+    import torch
+    M, K, hd, heads = 300, 256, 64, 6
+    N = hd * heads
+    say(f"rope dtype={dtype} tile={tile} tB={transB}")
+    X = inputs.normal((M, K), 721, dtype)
+    W = inputs.normal((K, N), 722, dtype, std=0.05)
+    bias = inputs.normal((N,), 723, dtype)
+    pos = np.random.default_rng(724).integers(0, 8192, size=M).astype(np.int32)
+    Wst = np.ascontiguousarray(W.T) if transB else W
+    bd = to_dev(bias[None, :], dtype)
+    posd = torch.from_numpy(pos).cuda()
+    for mode in ("array", "offset"):
+        if mode == "array":
+            opos, epi = pos, fgemm.make_epilogue(
+                fgemm.FGEMM_EPI_ROPE | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(),
+                rope_positions=posd.data_ptr(), rope_head_dim=hd, rope_theta=10000.0)
+        else:
+            opos, epi = np.arange(M) + 5000, fgemm.make_epilogue(
+                fgemm.FGEMM_EPI_ROPE | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(), rope_offset=5000,
+                rope_head_dim=hd, rope_theta=10000.0)
+        _, Q, _ = oracle.gemm(X, W, alpha=0.5, dtype=dtype, epi=oracle.EPI_ROPE | oracle.EPI_BIAS,
+                              bias=bias, rope_pos=opos, rope_head_dim=hd, rope_theta=10000.0)
+        got = run_transform(X, Wst, None, dtype, epi, plan=fgemm.classical_plan(*tile),
+                            transB=transB, alpha=0.5, M=M)
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, mode
+
+
+def test_transforms_unaligned_operands():
+    # leading dimensions that are not multiples of 8: the register epilogue
+    dtype = F16
+    M, K, N = 70, 96, 128
+    X = inputs.normal((M, K), 731, dtype)
+    W = inputs.normal((K, N), 732, dtype, std=0.1)
+    say("transforms unaligned")
+    for epi_f, okw, gkw in (
+            (oracle.EPI_ACT, dict(act=oracle.ACT_GELU_TANH),
+             dict(act=fgemm.FGEMM_ACT_GELU_TANH)),
+            (oracle.EPI_ROPE, dict(rope_pos=np.arange(M) + 77, rope_head_dim=32),
+             dict(rope_offset=77, rope_head_dim=32))):
+        _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=epi_f, **okw)
+        flag = fgemm.FGEMM_EPI_ACT if epi_f == oracle.EPI_ACT else fgemm.FGEMM_EPI_ROPE
+        got = run_transform(X, W, None, dtype, fgemm.make_epilogue(flag, **gkw), pad=3, M=M)
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, epi_f
+
+
+def test_rope_llm_projection_size():
+    """The projection shape 16384 tokens x 4096 -> 4096 with RoPE over 32 heads of
+    128 (four sequences of 4096 positions), as the model picks the plan; sampled rows."""
+    import torch
+    dtype, M, K, N, hd = BF16, 16384, 4096, 4096, 128
+    say("rope 16384x4096x4096")
+    X = inputs.normal((M, K), 3001, dtype)
+    W = inputs.normal((K, N), 3002, dtype, std=0.02)
+    pos = (np.arange(M) % 4096).astype(np.int32)
+    posd = torch.from_numpy(pos).cuda()
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE, rope_positions=posd.data_ptr(),
+                              rope_head_dim=hd, rope_theta=10000.0)
+    got = run_transform(X, W, None, dtype, epi, M=M)
+    rows = inputs.sample_rows(M, 32, 11)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_ROPE, rope_pos=pos, rope_head_dim=hd,
+                          rows=rows)
+    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+
+
+def test_gelu_llm_ffn_up_size():
+    """FFN up projection 16384 x 4096 -> 14336 with bias + GELU, as the model picks
+    the plan; sampled rows."""
+    import torch
+    dtype, M, K, N = BF16, 16384, 4096, 14336
+    say("gelu 16384x4096x14336")
+    X = inputs.normal((M, K), 3001, dtype)
+    W = inputs.normal((K, N), 3002, dtype, std=0.02)
+    bias = inputs.normal((N,), 3003, dtype, std=0.02)
+    bd = to_dev(bias[None, :], dtype)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(),
+                              act=fgemm.FGEMM_ACT_GELU_TANH)
+    got = run_transform(X, W, None, dtype, epi, M=M)
+    rows = inputs.sample_rows(M, 32, 12)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_ACT | oracle.EPI_BIAS, bias=bias,
+                          act=oracle.ACT_GELU_TANH, rows=rows)
+    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL

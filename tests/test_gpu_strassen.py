@@ -272,3 +272,35 @@ def test_fused_chain_llm_size_on_strassen(depth):
                            rms_eps=1e-6)
     print(f"[chain d={depth}] end-to-end rel err vs the oracle's chain: "
           f"{rel_err(O[rows], Oe, dtype):.3e}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("variant", [S69, WIN])
+@pytest.mark.parametrize("depth", [1, 2])
+def test_activation_and_rope_in_post_add(dtype, variant, depth):
+    """GELU + bias and the rotary embedding (positions up to 8191, head width 64)
+    applied by the top-level post-add to alpha*acc + beta*C + bias."""
+    import torch
+    M, N, K = 256, 384, 512
+    say(f"strassen act/rope dtype={dtype} v={variant} d={depth}")
+    A, B = operands(M, N, K, False, True, 641, dtype, "uniform")
+    C = inputs.uniform((M, N), 643, dtype)
+    bias = inputs.uniform((N,), 644, dtype)
+    pos = np.random.default_rng(645).integers(0, 8192, size=M).astype(np.int32)
+    Ad, Bd, bd = to_dev(A, dtype), to_dev(B, dtype), to_dev(bias[None, :], dtype)
+    posd = torch.from_numpy(pos).cuda()
+    plan = fgemm.strassen_plan(depth, variant)
+    cases = [
+        (oracle.EPI_ACT | oracle.EPI_BIAS, dict(act=oracle.ACT_GELU_TANH),
+         fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(),
+                             act=fgemm.FGEMM_ACT_GELU_TANH)),
+        (oracle.EPI_ROPE | oracle.EPI_BIAS, dict(rope_pos=pos, rope_head_dim=64),
+         fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(),
+                             rope_positions=posd.data_ptr(), rope_head_dim=64))]
+    for epi_o, okw, epi_g in cases:
+        _, Q, _ = oracle.gemm(A, B, transB=True, alpha=0.75, beta=0.5, C=C, dtype=dtype,
+                              epi=epi_o, bias=bias, **okw)
+        Cd = to_dev(C, dtype)
+        handle().gemm(Ad, Bd, Cd, transB=True, alpha=0.75, beta=0.5, epilogue=epi_g, plan=plan)
+        torch.cuda.synchronize()
+        assert rel_err(from_dev(Cd), Q, dtype) <= STRASSEN_TOL, epi_o
