@@ -290,7 +290,10 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   k.a_kcontig = c.ta == FGEMM_OP_N;
   k.b_kcontig = c.tb == FGEMM_OP_T;
   k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
-  k.epi = swiglu ? kEpiSwiGLU : xform ? kEpiTransform : kEpiStore16;
+  k.epi = swiglu                        ? kEpiSwiGLU
+          : (flags & FGEMM_EPI_ACT)     ? kEpiAct
+          : (flags & FGEMM_EPI_ROPE)    ? kEpiRope
+                                        : kEpiStore16;
   k.vec = vec;
   if (plan.split_k > 1) {
     // fp32 K slices into the workspace, then the epilogue in the finalize pass
@@ -540,6 +543,9 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
     const int64_t hd = epi->rope_head_dim;
     if (hd <= 0 || hd % 2 || hd > INT32_MAX || N % hd || !(epi->rope_theta > 0.f))
       return FGEMM_ERR_INVALID_VALUE;
+    // the kernels rotate runs of 4 or 8 columns inside one head, and keep the pair
+    // frequencies of one head in a table
+    if (hd % 8 || hd > 1024) return FGEMM_ERR_NOT_SUPPORTED;
   }
   const int64_t Nb = swiglu ? 2 * N : N;
   const int64_t a_cols = ta == FGEMM_OP_N ? K : M;   // stored row width of A

@@ -21,9 +21,11 @@ template <class CFG>
 static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
   if (k.epi == kEpiStore16) return k.vec ? plain<CFG, kEpiStore16, true>(b, s)
                                          : plain<CFG, kEpiStore16, false>(b, s);
-  // activation or rotary embedding before the rounding
-  if (k.epi == kEpiTransform) return k.vec ? plain<CFG, kEpiTransform, true>(b, s)
-                                           : plain<CFG, kEpiTransform, false>(b, s);
+  // an activation or the rotary embedding before the rounding
+  if (k.epi == kEpiAct) return k.vec ? plain<CFG, kEpiAct, true>(b, s)
+                                     : plain<CFG, kEpiAct, false>(b, s);
+  if (k.epi == kEpiRope) return k.vec ? plain<CFG, kEpiRope, true>(b, s)
+                                      : plain<CFG, kEpiRope, false>(b, s);
   if constexpr (CFG::FN % 2 == 0) {
     if (k.epi == kEpiSwiGLU) return k.vec ? plain<CFG, kEpiSwiGLU, true>(b, s)
                                           : plain<CFG, kEpiSwiGLU, false>(b, s);

@@ -33,9 +33,9 @@
 //     looping over tiles; workgroups of one XCD (ids are dealt round-robin over
 //     the 8 XCDs) take a contiguous, L2-friendly run of tiles per round, and a
 //     tile's first loads are issued by its predecessor before that one's epilogue;
-//   - with aligned operands the epilogues (plain, fp32 slices, SwiGLU) stage their
-//     results through LDS so that every lane stores (and reads beta*C as) 8
-//     consecutive columns: whole 128-byte lines.
+//   - with aligned operands the epilogues (plain, fp32 slices, SwiGLU, activation or
+//     rotary embedding) stage their results through LDS so that every lane stores
+//     (and reads beta*C as) 8 consecutive columns: whole 128-byte lines.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -770,7 +770,7 @@ struct GemmTile {
     const int lr = lane % MI, lc = lane / MI;  // lane's row and column slot in a block
     const int orow = lane / LPR, oc = lane % LPR;
     const bool use_beta = EPI != kEpiStore32 && (P.flags & kFlagBeta) != 0;
-    constexpr bool STORE16 = EPI == kEpiStore16 || EPI == kEpiTransform;
+    constexpr bool STORE16 = EPI == kEpiStore16 || EPI == kEpiAct || EPI == kEpiRope;
     const bool use_bias = STORE16 && (P.flags & kFlagBias) != 0;
     const bool use_ss = STORE16 && (P.flags & kFlagRowSumSq) != 0;
     const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
@@ -884,9 +884,14 @@ struct GemmTile {
 #pragma unroll
               for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
             }
-            if constexpr (EPI == kEpiTransform)
-              apply_transform<8>(P.act, P.rope_pos, P.rope_off, P.rope_hd, P.rope_log2_base, row,
-                                 col, v);
+            if constexpr (EPI == kEpiAct) apply_act_run<8>(P.act, v);
+            if constexpr (EPI == kEpiRope) {
+              // pair frequencies of this run from the table after the stages
+              const double* ft = reinterpret_cast<const double*>(smem + CFG::SMEM) +
+                                 ((col % P.rope_hd) >> 1);
+              rope_run<8>(rope_pos_of(P.rope_pos, P.rope_off, row),
+                          [&](int q) { return ft[q]; }, v);
+            }
             uint32_t o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -927,6 +932,7 @@ struct GemmTile {
   // column = wave column base + MI*j + g*(256/MI) + 4*(lane / MI) + s.
   __device__ __forceinline__ static void epilogue(const GemmProblem& P, void* Cout, int m0,
                                                   int n0, int tn, int wm, int wn, int lane,
+                                                  const uint8_t* smem,
                                                   Acc (&acc)[CFG::FM][CFG::FN]) {
     constexpr int MI = CFG::MI, G4 = CFG::ACC / 4;
     const int lr = lane % MI, lc = lane / MI;
@@ -957,7 +963,7 @@ struct GemmTile {
     uint16_t* C = static_cast<uint16_t*>(Cout);
     const uint16_t* Cin = static_cast<const uint16_t*>(P.Cin);
     const bool use_beta = (P.flags & kFlagBeta) != 0;
-    if constexpr (EPI == kEpiStore16 || EPI == kEpiTransform) {
+    if constexpr (EPI == kEpiStore16 || EPI == kEpiAct || EPI == kEpiRope) {
       const bool use_bias = (P.flags & kFlagBias) != 0;
       const bool use_ss = (P.flags & kFlagRowSumSq) != 0;
       const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
@@ -993,9 +999,13 @@ struct GemmTile {
 #pragma unroll
               for (int s = 0; s < 4; ++s) v[s] += s < nv ? to_f32<DT>(bias[col + s]) : 0.f;
             }
-            if constexpr (EPI == kEpiTransform)
-              apply_transform<4>(P.act, P.rope_pos, P.rope_off, P.rope_hd, P.rope_log2_base, row,
-                                 col, v);
+            if constexpr (EPI == kEpiAct) apply_act_run<4>(P.act, v);
+            if constexpr (EPI == kEpiRope) {
+              const double* ft = reinterpret_cast<const double*>(smem + CFG::SMEM) +
+                                 ((col % P.rope_hd) >> 1);
+              rope_run<4>(rope_pos_of(P.rope_pos, P.rope_off, row),
+                          [&](int q) { return ft[q]; }, v);
+            }
             uint32_t o[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -1122,8 +1132,17 @@ __device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
   using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[CFG::SMEM];
+  // the rotary embedding keeps its pair frequencies in a table after the stages
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t smem[CFG::SMEM + (EPI == kEpiRope ? kRopeMaxPairs * sizeof(double) : 0)];
   const int tid = threadIdx.x, lane = tid & 63;
+  if constexpr (EPI == kEpiRope) {
+    double* ft = reinterpret_cast<double*>(smem + CFG::SMEM);
+    const GemmProblem& P0 = batch.p[0];
+    for (int t = tid; t < P0.rope_hd / 2; t += CFG::NT)
+      ft[t] = rope_freq(t, P0.rope_hd, P0.rope_log2_base);
+    __syncthreads();
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
   const int G = gridDim.x;
@@ -1176,7 +1195,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
     if constexpr (VEC)
       T::epilogue_rows(P, Cout, cur.m0, cur.n0, cur.tn, wave, wm, wn, lane, smem, acc);
     else
-      T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, acc);
+      T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, smem, acc);
     pre = issued;
     cur = nxt;
     have = have_next;

@@ -16,7 +16,8 @@ enum EpiKind : int {
   kEpiStore16 = 0,   // 16-bit output: alpha, beta*C, optional bias, optional row sum of squares
   kEpiSwiGLU = 1,    // 16-bit output of silu(r*alpha*gate) * (r*alpha*up) + beta*C
   kEpiStore32 = 2,   // fp32 output of the raw accumulators (Strassen sub-products)
-  kEpiTransform = 3, // kEpiStore16 plus an activation or the rotary embedding before rounding
+  kEpiAct = 3,       // kEpiStore16 plus an activation before rounding
+  kEpiRope = 4,      // kEpiStore16 plus the rotary position embedding before rounding
 };
 
 // Runtime epilogue switches inside kEpiStore16.
@@ -37,9 +38,8 @@ struct GemmProblem {
   float* ss_partial;    // [tiles_n * 2][M] per-wave-column partial sums of squares
   const float* rms_ss;  // [M] sums of squares for the RMS scale
   float rms_inv_n, rms_eps;
-  // kEpiTransform: act != 0 applies that activation, else the rotary embedding
-  int act;
-  int rope_hd;
+  int act;                  // kEpiAct: the activation
+  int rope_hd;              // kEpiRope: head width (a multiple of 8, at most 1024)
   const int32_t* rope_pos;  // [M] positions, or null: row + rope_off
   int64_t rope_off;
   double rope_log2_base;

@@ -271,6 +271,17 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
   float factor = 1.f;
   if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
   const bool stats = a.ss_partial != nullptr;
+  // rotary embedding: the frequencies of this lane's two pairs in each column block
+  // (a lane keeps its columns for every row)
+  double rf[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  if (a.rope_hd && active) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int d0 = (int)((cb * a.n + j) % a.rope_hd);
+      rf[cb][0] = rope_freq(d0 >> 1, a.rope_hd, a.rope_log2_base);
+      rf[cb][1] = rope_freq((d0 >> 1) + 1, a.rope_hd, a.rope_log2_base);
+    }
+  }
   for (int64_t i = blockIdx.y; i < a.m; i += gridDim.y) {
     float ss[2] = {0.f, 0.f};  // top row i, bottom row m + i
     if (active) {
@@ -333,9 +344,11 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
               v[2] += h2f(bv.y & 0xffffu, a.dt);
               v[3] += h2f(bv.y >> 16, a.dt);
             }
-            if (a.act || a.rope_hd)
-              apply_transform<4>(a.act, a.rope_pos, a.rope_off, a.rope_hd, a.rope_log2_base,
-                                 (int)row, (int)col, v);
+            if (a.act)
+              apply_act_run<4>(a.act, v);
+            else if (a.rope_hd)
+              rope_run<4>(rope_pos_of(a.rope_pos, a.rope_off, row),
+                          [&](int q) { return rf[b & 1][q]; }, v);
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

@@ -129,6 +129,8 @@ def test_check_args_epilogues():
     assert chk(epi=E(ROPE, rope_head_dim=7)) == INVAL                      # odd
     assert chk(epi=E(ROPE, rope_head_dim=48)) == INVAL                     # does not divide N
     assert chk(epi=E(ROPE, rope_head_dim=16, rope_theta=0.0)) == INVAL
+    assert chk(epi=E(ROPE, rope_head_dim=4)) == NOTSUP                     # kernels: hd % 8 == 0
+    assert chk(N=2048, epi=E(ROPE, rope_head_dim=2048)) == NOTSUP           # table of 512 pairs
     assert chk(epi=E(ACT | ROPE, act=1, rope_head_dim=16)) == NOTSUP
     assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU | ACT, rms_rowsumsq=P, rms_n=4096,
                      act=1)) == NOTSUP
