@@ -9,9 +9,9 @@
 //     1.5957691216057308 below is 2*sqrt(2/pi);
 //   RoPE: the rotary position embedding of Su et al. (RoFormer) on interleaved
 //     pairs: in each head of hd columns, pair p = (2p, 2p+1) turns by
-//     pos * base^(-2p/hd).  The pair frequencies base^(-2p/hd) are computed once
-//     in fp64; the angle is formed and reduced to [-pi, pi] in fp64 (at positions
-//     in the thousands an fp32 angle is off by ~1e-3 rad), and its sine and cosine
+//     pos * base^(-2p/hd).  The pair rates base^(-2p/hd)/(2 pi) are computed once
+//     in fp64; the angle is formed in turns and reduced in fp64 (at positions in
+//     the thousands an fp32 angle is off by ~1e-3 rad), and its sine and cosine
 //     are taken in fp32 by the hardware instructions.  The GPU path needs hd to be a
 //     multiple of 8, so the 4 or 8 consecutive columns a lane transforms never
 //     leave their head.
@@ -40,23 +40,25 @@ __device__ __forceinline__ void apply_act_run(int act, float (&v)[W]) {
   for (int e = 0; e < W; ++e) v[e] = apply_act(act, v[e]);
 }
 
-// Frequency of pair p of a head of hd columns: base^(-2p/hd).
-__device__ __forceinline__ double rope_freq(int p, int hd, double log2_base) {
-  return exp2(-(double)(2 * p) / (double)hd * log2_base);
+// Rotation rate of pair p of a head of hd columns in turns per position:
+// base^(-2p/hd) / (2 pi).
+__device__ __forceinline__ double rope_turns(int p, int hd, double log2_base) {
+  const double inv_two_pi = 0.15915494309189535;
+  return exp2(-(double)(2 * p) / (double)hd * log2_base) * inv_two_pi;
 }
 
-// Rotate the pairs of W consecutive values at position `pos`; freq[q] is the
-// frequency of pair q of the run.
+// Rotate the pairs of W consecutive values at position `pos`; turns(q) is the
+// rotation rate of pair q of the run.  The angle in turns is reduced to
+// [-1/2, 1/2] in fp64 and handed to the hardware sine and cosine, which take
+// their argument in turns (absolute error ~1e-6).
 template <int W, class F>
-__device__ __forceinline__ void rope_run(double pos, const F& freq, float (&v)[W]) {
+__device__ __forceinline__ void rope_run(double pos, const F& turns, float (&v)[W]) {
   static_assert(W % 2 == 0, "whole pairs");
-  const double two_pi = 6.283185307179586;
 #pragma unroll
   for (int q = 0; q < W / 2; ++q) {
-    const double th = pos * freq(q);
-    const float r = (float)(th - two_pi * rint(th / two_pi));
-    // hardware sine/cosine: absolute error ~1e-6 on [-pi, pi]
-    const float s = __sinf(r), c = __cosf(r);
+    const double t = pos * turns(q);
+    const float r = (float)(t - rint(t));
+    const float s = __builtin_amdgcn_sinf(r), c = __builtin_amdgcn_cosf(r);
     const float x0 = v[2 * q], x1 = v[2 * q + 1];
     v[2 * q] = x0 * c - x1 * s;
     v[2 * q + 1] = x0 * s + x1 * c;

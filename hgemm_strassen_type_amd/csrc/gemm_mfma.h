@@ -881,12 +881,22 @@ struct GemmTile {
               for (int e = 0; e < 8; ++e) v[e] += P.beta * to_f32<DT>(cb[e]);
             }
             if (use_bias) {
+              // one 16-byte load where the bias vector is aligned
+              if (nv >= 8 && (reinterpret_cast<uintptr_t>(bias + col) & 15) == 0) {
+                const v4u b4 = *reinterpret_cast<const v4u*>(bias + col);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                  v[2 * e] += to_f32<DT>(b4[e] & 0xffff);
+                  v[2 * e + 1] += to_f32<DT>(b4[e] >> 16);
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
+              }
             }
             if constexpr (EPI == kEpiAct) apply_act_run<8>(P.act, v);
             if constexpr (EPI == kEpiRope) {
-              // pair frequencies of this run from the table after the stages
+              // pair rates of this run from the table after the stages
               const double* ft = reinterpret_cast<const double*>(smem + CFG::SMEM) +
                                  ((col % P.rope_hd) >> 1);
               rope_run<8>(rope_pos_of(P.rope_pos, P.rope_off, row),
@@ -1132,7 +1142,7 @@ __device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
   using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
-  // the rotary embedding keeps its pair frequencies in a table after the stages
+  // the rotary embedding keeps its pair rates in a table after the stages
   __shared__ __attribute__((aligned(1024)))
   uint8_t smem[CFG::SMEM + (EPI == kEpiRope ? kRopeMaxPairs * sizeof(double) : 0)];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1140,7 +1150,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
     double* ft = reinterpret_cast<double*>(smem + CFG::SMEM);
     const GemmProblem& P0 = batch.p[0];
     for (int t = tid; t < P0.rope_hd / 2; t += CFG::NT)
-      ft[t] = rope_freq(t, P0.rope_hd, P0.rope_log2_base);
+      ft[t] = rope_turns(t, P0.rope_hd, P0.rope_log2_base);
     __syncthreads();
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

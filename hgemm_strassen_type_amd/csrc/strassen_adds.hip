@@ -271,15 +271,15 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
   float factor = 1.f;
   if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
   const bool stats = a.ss_partial != nullptr;
-  // rotary embedding: the frequencies of this lane's two pairs in each column block
+  // rotary embedding: the rates of this lane's two pairs in each column block
   // (a lane keeps its columns for every row)
   double rf[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
   if (a.rope_hd && active) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int d0 = (int)((cb * a.n + j) % a.rope_hd);
-      rf[cb][0] = rope_freq(d0 >> 1, a.rope_hd, a.rope_log2_base);
-      rf[cb][1] = rope_freq((d0 >> 1) + 1, a.rope_hd, a.rope_log2_base);
+      rf[cb][0] = rope_turns(d0 >> 1, a.rope_hd, a.rope_log2_base);
+      rf[cb][1] = rope_turns((d0 >> 1) + 1, a.rope_hd, a.rope_log2_base);
     }
   }
   for (int64_t i = blockIdx.y; i < a.m; i += gridDim.y) {

@@ -268,3 +268,27 @@ def test_gelu_llm_ffn_up_size():
     _, Q, _ = oracle.gemm(X, W, dtype=dtype, epi=oracle.EPI_ACT | oracle.EPI_BIAS, bias=bias,
                           act=oracle.ACT_GELU_TANH, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+
+
+def test_rope_backward_is_negated_positions():
+    """The backward of RoPE is the rotation by the opposite angle: running the
+    rotated output through an identity GEMM with negated positions gives back the
+    unrotated product (to two roundings), and matches the oracle at -pos."""
+    import torch
+    dtype, M, K, hd, heads = F16, 256, 192, 64, 4
+    N = hd * heads
+    say("rope backward")
+    X = inputs.normal((M, K), 741, dtype)
+    W = inputs.normal((K, N), 742, dtype, std=0.1)
+    pos = np.random.default_rng(743).integers(0, 4096, size=M).astype(np.int32)
+    posd, negd = torch.from_numpy(pos).cuda(), torch.from_numpy(-pos).cuda()
+    fwd = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE, rope_positions=posd.data_ptr(), rope_head_dim=hd)
+    bwd = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE, rope_positions=negd.data_ptr(), rope_head_dim=hd)
+    Y = run_transform(X, W, None, dtype, fwd, M=M)
+    eye = inputs.to_bits(np.eye(N), dtype)
+    back = run_transform(Y, eye, None, dtype, bwd, M=M)
+    _, Q, _ = oracle.gemm(X, W, dtype=dtype)
+    assert rel_err(back, Q, dtype) <= 2 * CLASSICAL_TOL
+    _, Qb, _ = oracle.gemm(Y, eye, dtype=dtype, epi=oracle.EPI_ROPE, rope_pos=-pos.astype(np.int64),
+                           rope_head_dim=hd)
+    assert rel_err(back, Qb, dtype) <= CLASSICAL_TOL

@@ -385,3 +385,24 @@ def test_act_and_rope_argument_checks():
     with pytest.raises(ValueError):   # one transform at a time
         identity_gemm(x, BF16, epi=oracle.EPI_ROPE | oracle.EPI_ACT, act=1, rope_pos=[0, 1],
                       rope_head_dim=4)
+
+
+def test_rope_negative_positions_invert_it():
+    # the backward of a rotation is the rotation by the opposite angle: at -pos every
+    # pair keeps its length and turns by exactly the opposite angle, and rotating the
+    # 16-bit result of +pos by -pos gives the input back to that rounding
+    rng = np.random.default_rng(11)
+    M, hd = 5, 16
+    vals = rng.uniform(-1, 1, size=(M, 2 * hd))
+    pos = np.array([0, 3, 77, 1000, 8191])
+    plain, _, _ = identity_gemm(vals, F16)
+    Y, Yq, _ = identity_gemm(vals, F16, epi=oracle.EPI_ROPE, rope_pos=pos, rope_head_dim=hd)
+    Yn, _, _ = identity_gemm(vals, F16, epi=oracle.EPI_ROPE, rope_pos=-pos, rope_head_dim=hd)
+    length = lambda D: np.hypot(D[:, 0::2], D[:, 1::2])
+    ang = lambda D: np.arctan2(D[:, 1::2], D[:, 0::2])
+    assert np.allclose(length(Yn), length(Y), rtol=1e-13)
+    turn = lambda D: np.angle(np.exp(1j * (ang(D) - ang(plain))))
+    assert np.allclose(turn(Y), -turn(Yn), atol=1e-9)
+    A = ints_to_bits(np.eye(M), F16)
+    back, _, _ = oracle.gemm(A, Yq, dtype=F16, epi=oracle.EPI_ROPE, rope_pos=-pos, rope_head_dim=hd)
+    assert np.max(np.abs(back - plain)) <= 2 * 2.0 ** -11
