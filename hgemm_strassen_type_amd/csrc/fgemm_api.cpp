@@ -124,8 +124,8 @@ size_t strassen_stats_bytes(int64_t M, int64_t Nb, uint32_t flags) {
 
 // Core of fgemm_select: classical tile choice, then Strassen candidates under guards.
 fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K,
-                           uint32_t flags, int beta_hint, int vec, size_t ws_limit,
-                           fgemm_plan_t* out) {
+                           fgemm_dtype_t dtype, uint32_t flags, int beta_hint, int vec,
+                           size_t ws_limit, fgemm_plan_t* out) {
   fgemm_plan_t p{};
   const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
   double tc;
@@ -165,6 +165,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
   }
   p.t_pred_us = tc;
   p.t_classical_pred_us = tc;
+  p.pred_rel_err = predicted_rel_err(dtype, 0, 0);
   for (int depth = 1; depth <= 2; ++depth) {
     for (int variant = FGEMM_VARIANT_S69; variant <= FGEMM_VARIANT_WINOGRAD; ++variant) {
       fgemm_plan_t c{};
@@ -172,6 +173,9 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       c.depth = depth;
       c.variant = variant;
       if (check_plan_shape(c, M, N, K, vec, flags) != FGEMM_OK) continue;
+      // accuracy guard: the calibrated error of this variant and depth within budget
+      const double err = predicted_rel_err(dtype, variant, depth);
+      if (err > md.max_rel_err) continue;
       // sub-problems below 512 never pay for their additions; keep them classical
       if ((M >> depth) < 512 || ((swiglu ? 2 * N : N) >> depth) < 512 || (K >> depth) < 512)
         continue;
@@ -189,6 +193,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
         c.workspace_bytes = ws;
         c.t_pred_us = t;
         c.t_classical_pred_us = tc;
+        c.pred_rel_err = err;
         p = c;
       }
     }
@@ -616,7 +621,7 @@ fgemm_status_t fgemm_get_model(fgemm_handle_t h, fgemm_model_t* m) {
 fgemm_status_t fgemm_set_model(fgemm_handle_t h, const fgemm_model_t* m) {
   if (!h || !m) return FGEMM_ERR_INVALID_VALUE;
   if (m->compute_units <= 0 || !(m->peak_tflops > 0) || !(m->hbm_gbps > 0) ||
-      !(m->eta_mfma > 0) || !(m->eta_hbm > 0) || !(m->launch_us >= 0))
+      !(m->eta_mfma > 0) || !(m->eta_hbm > 0) || !(m->launch_us >= 0) || !(m->max_rel_err > 0))
     return FGEMM_ERR_INVALID_VALUE;
   h->model = *m;
   h->plans.clear();
@@ -631,11 +636,12 @@ fgemm_status_t fgemm_select_model(const fgemm_model_t* md, fgemm_op_t ta, fgemm_
   if (tb != FGEMM_OP_N && tb != FGEMM_OP_T) return FGEMM_ERR_INVALID_VALUE;
   if (dtype != FGEMM_F16 && dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
-  if (md->compute_units <= 0 || !(md->peak_tflops > 0) || !(md->hbm_gbps > 0))
+  if (md->compute_units <= 0 || !(md->peak_tflops > 0) || !(md->hbm_gbps > 0) ||
+      !(md->max_rel_err > 0))
     return FGEMM_ERR_INVALID_VALUE;
   // shapes only: assume the aligned fast path, no beta traffic, no workspace cap
   // beyond the model's own
-  return select_plan(*md, M, N, K, epi_flags(epi), 0, 1, (size_t)-1, plan);
+  return select_plan(*md, M, N, K, dtype, epi_flags(epi), 0, 1, (size_t)-1, plan);
 }
 
 fgemm_status_t fgemm_select(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t N,
@@ -695,7 +701,7 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_
     plan = it->second;
   } else {
     size_t limit = h->user_ws ? h->user_ws_bytes : (size_t)-1;
-    st = select_plan(h->model, M, N, K, epi_flags(epi), beta != 0.f, vec, limit, &plan);
+    st = select_plan(h->model, M, N, K, dtype, epi_flags(epi), beta != 0.f, vec, limit, &plan);
     if (st != FGEMM_OK) return st;
     h->plans.emplace(key, plan);
   }

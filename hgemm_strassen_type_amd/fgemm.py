@@ -29,7 +29,7 @@ FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
 EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
            "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
            "fgemm_gemm_plan", "fgemm_check_args", "fgemm_tile_count", "fgemm_wave_count",
-           "fgemm_status_string")
+           "fgemm_plan_rel_err", "fgemm_status_string")
 
 
 class FgemmError(RuntimeError):
@@ -52,7 +52,7 @@ class fgemm_plan_t(ctypes.Structure):
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("t_pred_us", ctypes.c_double),
-                ("t_classical_pred_us", ctypes.c_double)]
+                ("t_classical_pred_us", ctypes.c_double), ("pred_rel_err", ctypes.c_double)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -62,7 +62,7 @@ class fgemm_model_t(ctypes.Structure):
     _fields_ = [("compute_units", ctypes.c_int32), ("peak_tflops", ctypes.c_double),
                 ("hbm_gbps", ctypes.c_double), ("eta_mfma", ctypes.c_double),
                 ("eta_hbm", ctypes.c_double), ("launch_us", ctypes.c_double),
-                ("max_workspace_bytes", ctypes.c_double)]
+                ("max_workspace_bytes", ctypes.c_double), ("max_rel_err", ctypes.c_double)]
 
 
 _lib = None
@@ -98,6 +98,7 @@ def lib():
                                   epi_p]),
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
         "fgemm_wave_count": (i64, [i64, i64, ctypes.POINTER(ctypes.c_double)]),
+        "fgemm_plan_rel_err": (ctypes.c_double, [i32, plan_p]),
         "fgemm_status_string": (ctypes.c_char_p, [st]),
     }
     for name, (res, args) in sig.items():
@@ -199,6 +200,10 @@ def fgemm_wave_count(tiles, units):
     tail = ctypes.c_double()
     w = lib().fgemm_wave_count(tiles, units, ctypes.byref(tail))
     return w, tail.value
+
+
+def fgemm_plan_rel_err(dtype, plan) -> float:
+    return lib().fgemm_plan_rel_err(dtype, ctypes.byref(plan))
 
 
 # ------------------------------------------------------------ torch conveniences

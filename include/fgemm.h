@@ -127,6 +127,11 @@ typedef struct {
     size_t workspace_bytes;     /* device workspace the plan needs                    */
     double t_pred_us;           /* model time of this plan                            */
     double t_classical_pred_us; /* model time of the best classical plan              */
+    double pred_rel_err;        /* predicted normwise error of the plan against the
+                                   exactly rounded result, from calibrated per-path
+                                   figures on i.i.d. inputs (FalconGEMM summary,
+                                   Methodology 4: accuracy guides the choice); not a
+                                   worst-case bound                                  */
 } fgemm_plan_t;
 
 /* Constants of the analytic model.  fgemm_create fills them from the device and
@@ -139,6 +144,9 @@ typedef struct {
     double eta_hbm;             /* fraction of HBM bandwidth streaming kernels reach  */
     double launch_us;           /* per-kernel launch and drain cost, microseconds     */
     double max_workspace_bytes; /* AUTO never plans above this workspace              */
+    double max_rel_err;         /* AUTO never plans a path whose predicted normwise
+                                   error ||C - RNE(D)||_F / ||RNE(D)||_F exceeds this
+                                   (default 5e-3); see fgemm_plan_t.pred_rel_err     */
 } fgemm_model_t;
 
 /* Handle: reads the device's CU count and architecture; fails with
@@ -157,7 +165,9 @@ fgemm_status_t fgemm_set_model(fgemm_handle_t handle, const fgemm_model_t* model
 
 /* The model's pick for a shape: the plan of least predicted time among the
  * classical kernel and Strassen/Winograd at depth 1 and 2, subject to the
- * accuracy, divisibility, epilogue and workspace guards.  Host only; results
+ * accuracy (model.max_rel_err against the plan's pred_rel_err), divisibility,
+ * epilogue and workspace guards; a tighter error budget lowers the depth or keeps
+ * the classical path.  Host only; results
  * are cached per shape in the handle. */
 fgemm_status_t fgemm_select(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
                             int64_t M, int64_t N, int64_t K, fgemm_dtype_t dtype,
@@ -207,6 +217,12 @@ int64_t fgemm_tile_count(int64_t M, int64_t N, int64_t tile_m, int64_t tile_n);
  * units is one wave; 120 tiles is two, the second 12/108 busy). */
 int64_t fgemm_wave_count(int64_t tiles, int64_t units, double* tail_fraction);
 
+/* The error model behind the accuracy guard (pure): the predicted normwise error
+ * ||C - RNE(D)||_F / ||RNE(D)||_F of `plan` (classical, or Strassen/Winograd at its
+ * depth and variant) for 16-bit inputs of type `dtype`; negative for an invalid
+ * dtype, path, depth or variant.  Calibrated on MI355X with i.i.d. inputs; not a
+ * worst-case bound. */
+double fgemm_plan_rel_err(fgemm_dtype_t dtype, const fgemm_plan_t* plan);
 const char* fgemm_status_string(fgemm_status_t status);
 
 #ifdef __cplusplus

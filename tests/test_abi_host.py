@@ -141,6 +141,7 @@ def mi355x_model(**over):
     m = fgemm.fgemm_model_t()
     m.compute_units, m.peak_tflops, m.hbm_gbps = 256, 256 * 4096 * 2.4e9 / 1e12, 8000.0
     m.eta_mfma, m.eta_hbm, m.launch_us, m.max_workspace_bytes = 0.7, 0.8, 4.0, 16 * 2.0 ** 30
+    m.max_rel_err = 5e-3
     for k, v in over.items():
         setattr(m, k, v)
     return m
@@ -240,3 +241,53 @@ def test_select_one_row_decode_tile():
     e = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=1, rms_n=4096)
     p = select(16, 14336, 4096, epi=e)
     assert (p.tile_m, p.tile_n) not in ((64, 64), (32, 128))
+
+
+def test_select_error_budget_sets_the_depth():
+    """The accuracy guard: with bandwidth to spare (the multiply saving wins), the
+    calibrated error of each variant and depth against the error budget decides how
+    deep AUTO goes; a budget below every Strassen figure keeps the classical path."""
+    def pick(budget, dtype):
+        p = select(16384, 16384, 16384, mi355x_model(hbm_gbps=80000.0, max_rel_err=budget),
+                   dtype=dtype)
+        return p.path, p.depth, p.variant, p.pred_rel_err
+    # default budget (the Strassen tolerance): the deepest, fastest candidate
+    path, depth, variant, err = pick(5e-3, BF)
+    assert (path, depth) == (fgemm.FGEMM_PATH_STRASSEN, 2) and err <= 5e-3
+    # bf16 figures: S69 d1 < Winograd d1 < S69 d2 < Winograd d2
+    path, depth, variant, err = pick(2e-3, BF)
+    assert (path, depth, variant) == (fgemm.FGEMM_PATH_STRASSEN, 2, fgemm.FGEMM_VARIANT_S69)
+    path, depth, variant, err = pick(1.5e-3, BF)
+    assert (path, depth) == (fgemm.FGEMM_PATH_STRASSEN, 1) and err <= 1.5e-3
+    path, depth, variant, err = pick(1e-3, BF)
+    assert (path, depth, variant) == (fgemm.FGEMM_PATH_STRASSEN, 1, fgemm.FGEMM_VARIANT_S69)
+    path, depth, variant, err = pick(5e-4, BF)
+    assert path == fgemm.FGEMM_PATH_CLASSICAL and err <= 5e-4
+    # fp16 carries less error through the same fp16 temporaries: 1e-3 still allows
+    # Winograd at depth 1
+    path, depth, variant, err = pick(1e-3, HF)
+    assert (path, depth) == (fgemm.FGEMM_PATH_STRASSEN, 1) and err <= 1e-3
+    # a model without a budget is refused
+    m = mi355x_model()
+    m.max_rel_err = 0.0
+    with pytest.raises(fgemm.FgemmError):
+        fgemm.fgemm_select_model(m, N_, N_, 1024, 1024, 1024, BF, None)
+
+
+def test_plan_rel_err_model():
+    cl = fgemm.classical_plan()
+    assert 0 < fgemm.fgemm_plan_rel_err(BF, cl) <= 1e-4
+    figs = {}
+    for dt in (BF, HF):
+        for v in (fgemm.FGEMM_VARIANT_S69, fgemm.FGEMM_VARIANT_WINOGRAD):
+            for d in (1, 2):
+                figs[dt, v, d] = fgemm.fgemm_plan_rel_err(dt, fgemm.strassen_plan(d, v))
+    for key, e in figs.items():
+        assert 1e-4 < e < 5e-3, key
+    for dt in (BF, HF):
+        for v in (fgemm.FGEMM_VARIANT_S69, fgemm.FGEMM_VARIANT_WINOGRAD):
+            assert figs[dt, v, 2] > figs[dt, v, 1]                   # a level adds error
+        for d in (1, 2):                                             # Winograd's chained sums
+            assert figs[dt, fgemm.FGEMM_VARIANT_WINOGRAD, d] > figs[dt, fgemm.FGEMM_VARIANT_S69, d]
+    assert fgemm.fgemm_plan_rel_err(7, cl) < 0
+    assert fgemm.fgemm_plan_rel_err(BF, fgemm.strassen_plan(3, 0)) < 0

@@ -304,3 +304,26 @@ def test_activation_and_rope_in_post_add(dtype, variant, depth):
         handle().gemm(Ad, Bd, Cd, transB=True, alpha=0.75, beta=0.5, epilogue=epi_g, plan=plan)
         torch.cuda.synchronize()
         assert rel_err(from_dev(Cd), Q, dtype) <= STRASSEN_TOL, epi_o
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("dist", ["uniform", "normal"])
+def test_error_model_calibration(dtype, dist):
+    """The accuracy guard's figures (fgemm_plan_rel_err) against measurement: on
+    i.i.d. 1024^3 inputs every path's normwise error against RNE(D) is at most its
+    predicted figure and at least half of it (the model is neither violated nor
+    vacuous)."""
+    n = 1024
+    say(f"error model dtype={dtype} dist={dist}")
+    gen = inputs.uniform if dist == "uniform" else inputs.normal
+    A, B = gen((n, n), 661, dtype), gen((n, n), 662, dtype)
+    rows = inputs.sample_rows(n, 96, 13)
+    _, Q, _ = oracle.gemm(A, B, dtype=dtype, rows=rows)
+    got = run(A, B, dtype, plan=fgemm.classical_plan())
+    assert rel_err(got[rows], Q, dtype) <= fgemm.fgemm_plan_rel_err(dtype, fgemm.classical_plan())
+    for variant in (S69, WIN):
+        for depth in (1, 2):
+            plan = fgemm.strassen_plan(depth, variant)
+            pred = fgemm.fgemm_plan_rel_err(dtype, plan)
+            err = rel_err(run(A, B, dtype, plan=plan)[rows], Q, dtype)
+            assert 0.5 * pred <= err <= pred, (variant, depth, err, pred)
