@@ -74,6 +74,10 @@ def _load():
                                    ctypes.c_int, u16p, f64p, i64, ctypes.c_double, ctypes.c_int,
                                    i64p, i64, ctypes.c_double, i64p, i64, f64p, u16p, f64p,
                                    ctypes.c_int]
+    lib.oracle_swiglu_bwd.restype = ctypes.c_int
+    lib.oracle_swiglu_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
+                                      u16p, i64, u16p, i64, ctypes.c_int, f64p, f64p, i64,
+                                      ctypes.c_double, i64p, i64, f64p, u16p, ctypes.c_int]
     lib.oracle_strassen.restype = ctypes.c_int
     lib.oracle_strassen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, i64, u16p,
                                     i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p]
@@ -166,6 +170,35 @@ def gemm(A, B, *, transA=False, transB=False, alpha=1.0, beta=0.0, C=None, dtype
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return D, Q, ss
+
+
+def swiglu_bwd(A, B, dO, *, rms_ss, rms_n, rms_eps=1e-6, alpha=1.0, transA=False,
+               transB=False, dtype=BF16, rows=None, threads=None):
+    """Backward of the RMS + SwiGLU epilogue with the row scale held fixed.
+
+    op(B) has 2*Nout columns (gate | up); dO (M x Nout, 16-bit bits) is the incoming
+    gradient and rms_ss the fp64 sums of squares of the selected rows.  Returns
+    (D, Q): the gradient with respect to op(A)op(B) for the selected rows,
+    unrounded and RNE 16-bit bits, both nrows x 2*Nout.
+    """
+    A, B = _u16(A), _u16(B)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    d = np.ascontiguousarray(decode(_u16(dO)[rows], dtype), dtype=np.float64)
+    rms_ss = np.ascontiguousarray(rms_ss, dtype=np.float64)
+    if d.shape != (rows.size, N // 2) or rms_ss.size != rows.size:
+        raise ValueError("dO or rms_ss shape")
+    D = np.empty((rows.size, N), dtype=np.float64)
+    Q = np.empty((rows.size, N), dtype=np.uint16)
+    rc = _load().oracle_swiglu_bwd(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
+                                   A.shape[1], _ptr(B), B.shape[1], dtype, _ptr(d), _ptr(rms_ss),
+                                   rms_n, float(rms_eps), _ptr(rows), rows.size, _ptr(D), _ptr(Q),
+                                   threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_swiglu_bwd rejected its arguments")
+    return D, Q
 
 
 def strassen(A, B, *, depth, variant, transA=False, transB=False, dtype=BF16):

@@ -44,6 +44,13 @@
  *     theta_ij = pos_i * base^(-2p/hd):
  *       y[2p] = x[2p] cos(theta) - x[2p+1] sin(theta)
  *       y[2p+1] = x[2p] sin(theta) + x[2p+1] cos(theta).
+ *   - SWIGLU_BWD, the backward of RMS_SWIGLU with the row scale r_i held fixed (the
+ *     same note's CODA section: backward passes of SwiGLU can run in the epilogue):
+ *     recompute H = op(A)op(B) (gate | up, 2*Nout columns) and, with g, u as in the
+ *     forward and dO the incoming gradient, write the gradient with respect to H:
+ *       out[i][j]        = Q(dO[i][j] * u * silu'(g) * r_i * alpha)
+ *       out[i][Nout + j] = Q(dO[i][j] * silu(g) * r_i * alpha)
+ *     silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)).
  *   - Strassen recursion keeps fp64 temporaries (it is the exact identity check).
  */
 #include <math.h>
@@ -303,6 +310,44 @@ int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, doub
             }
         }
         if ((epi & OR_EPI_ROWSUMSQ) && ss) ss[r] = sum_sq;
+    }
+    free(H);
+    return 0;
+}
+
+/*
+ * oracle_swiglu_bwd: N is the width of op(B) (2*Nout).  dO holds the incoming
+ * gradient of the selected rows (nrows x Nout, fp64), rms_ss their sums of squares.
+ * Outputs D (nrows x N, unrounded) and Q (nrows x N, 16-bit RNE bits).
+ */
+int oracle_swiglu_bwd(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                      const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int dtype,
+                      const double* dO, const double* rms_ss, int64_t rms_n, double rms_eps,
+                      const int64_t* rows, int64_t nrows, double* D, uint16_t* Q, int nthreads) {
+    if (N % 2 || rms_n <= 0) return -1;
+    int64_t Nout = N / 2;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    double* H = (double*)malloc(sizeof(double) * (nrows * N > 0 ? nrows * N : 1));
+    if (!H) return -1;
+    if (raw_products(transA, transB, M, N, K, A, lda, B, ldb, dtype, rows, nrows, H, nthreads)) {
+        free(H);
+        return -1;
+    }
+    for (int64_t r = 0; r < nrows; ++r) {
+        const double* h = H + r * N;
+        double rs = alpha / sqrt(rms_ss[r] / (double)rms_n + rms_eps);
+        for (int64_t j = 0; j < Nout; ++j) {
+            double g = rs * h[j], u = rs * h[j + Nout];
+            double s = 1.0 / (1.0 + exp(-g));
+            double d = dO[r * Nout + j];
+            double dg = d * u * s * (1.0 + g * (1.0 - s)) * rs;
+            double du = d * g * s * rs;
+            D[r * N + j] = dg;
+            D[r * N + Nout + j] = du;
+            Q[r * N + j] = oracle_encode(dg, dtype);
+            Q[r * N + Nout + j] = oracle_encode(du, dtype);
+        }
     }
     free(H);
     return 0;

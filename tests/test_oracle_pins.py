@@ -406,3 +406,40 @@ def test_rope_negative_positions_invert_it():
     A = ints_to_bits(np.eye(M), F16)
     back, _, _ = oracle.gemm(A, Yq, dtype=F16, epi=oracle.EPI_ROPE, rope_pos=-pos, rope_head_dim=hd)
     assert np.max(np.abs(back - plain)) <= 2 * 2.0 ** -11
+
+
+def test_swiglu_backward_is_the_gradient_of_the_forward():
+    # with A = I the recomputed product is B itself; the oracle's backward must be
+    # the gradient of f(H) = sum dO * silu(r a g) * (r a u) by central differences
+    rng = np.random.default_rng(21)
+    M, Nout = 4, 6
+    H = rng.uniform(-2, 2, size=(M, 2 * Nout))
+    Hb = inputs.to_bits(H, F16)
+    H = oracle.decode(Hb, F16)
+    dO = inputs.to_bits(rng.uniform(-1, 1, size=(M, Nout)), F16)
+    d = oracle.decode(dO, F16)
+    ss = rng.uniform(0.5, 2.0, M) * 8
+    alpha, n = 1.5, 8
+    A = ints_to_bits(np.eye(M), F16)
+    D, _ = oracle.swiglu_bwd(A, Hb, dO, rms_ss=ss, rms_n=n, rms_eps=1e-6, alpha=alpha, dtype=F16)
+    rs = alpha / np.sqrt(ss / n + 1e-6)
+
+    def f(Hx):
+        g, u = rs[:, None] * Hx[:, :Nout], rs[:, None] * Hx[:, Nout:]
+        return np.sum(d * g / (1 + np.exp(-g)) * u)
+    num = np.zeros_like(H)
+    h = 1e-6
+    for i in range(M):
+        for j in range(2 * Nout):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, j] += h
+            Hm[i, j] -= h
+            num[i, j] = (f(Hp) - f(Hm)) / (2 * h)
+    assert np.allclose(D, num, rtol=1e-6, atol=1e-8)
+    # closed forms: gate 0 -> silu'(0) = 1/2 and silu(0) = 0
+    Z = H.copy()
+    Z[:, :Nout] = 0.0
+    D0, _ = oracle.swiglu_bwd(A, inputs.to_bits(Z, F16), dO, rms_ss=ss, rms_n=n, rms_eps=1e-6,
+                              alpha=alpha, dtype=F16)
+    assert np.array_equal(D0[:, Nout:], np.zeros((M, Nout)))
+    assert np.allclose(D0[:, :Nout], d * rs[:, None] * Z[:, Nout:] * 0.5 * rs[:, None], rtol=1e-15)
