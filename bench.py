@@ -268,6 +268,16 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
             "chain_effective_tflops": round((f1 + f2) / ((s1 + s2) * 1e-3) / 1e12, 2)}
     W["fused_chain_8192x4096_ffn11008"]["strassen"] = chain_sk
     log(f"chain on the Strassen path: {chain_sk}")
+    # backward of GEMM2's epilogue: recompute Y W2 and write the gate|up gradient
+    dO = normal((Mc, Fc), 4004)
+    dH = torch.empty((Mc, 2 * Fc), dtype=torch.bfloat16, device="cuda")
+    eb = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
+                             rms_eps=1e-6, swiglu_dout=dO.data_ptr(), swiglu_ldd=Fc)
+    tb = timer.time(lambda: h.gemm(Y, W2, dH, epilogue=eb), reps, 2)
+    W["fused_chain_8192x4096_ffn11008"]["gemm2_swiglu_backward"] = {
+        "ms": round(tb, 5), "tflops": round(f2 / (tb * 1e-3) / 1e12, 2)}
+    log(f"chain GEMM2 backward: {W['fused_chain_8192x4096_ffn11008']['gemm2_swiglu_backward']}")
+    del dO, dH
     del X, Wt, W2, Y, O, ss
 
     # Strassen / Winograd vs classical, and the model's pick

@@ -77,13 +77,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 uint32_t epi_flags(const fgemm_epilogue_t* e) { return e ? e->flags : 0u; }
 
+// Epilogues on gate/up column pairs of a 2N-wide op(B).
+constexpr uint32_t kSwiGLUFlags = FGEMM_EPI_RMS_SWIGLU | FGEMM_EPI_SWIGLU_BWD;
+
 // Whether the 16-byte fast path applies.
 int vec_ok(fgemm_op_t ta, fgemm_op_t tb, int64_t N, const void* A, int64_t lda, const void* B,
            int64_t ldb, const void* C, int64_t ldc, const fgemm_epilogue_t* e) {
   (void)ta; (void)tb;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return 0;
   if (lda % 8 || ldb % 8 || ldc % 8) return 0;
-  if ((epi_flags(e) & FGEMM_EPI_RMS_SWIGLU) && N % 8) return 0;
+  if ((epi_flags(e) & kSwiGLUFlags) && N % 8) return 0;
   return 1;
 }
 
@@ -111,6 +114,7 @@ fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int
   // gate/up boundary); every epilogue is applied in the top-level post-add
   const int64_t q = 8ll << p.depth;
   const int64_t Nb = (flags & FGEMM_EPI_RMS_SWIGLU) ? 2 * N : N;
+  if (flags & FGEMM_EPI_SWIGLU_BWD) return FGEMM_ERR_NOT_SUPPORTED;  // classical path only
   if (M % q || Nb % q || K % q || M == 0 || N == 0 || K == 0) return FGEMM_ERR_NOT_SUPPORTED;
   if (!vec) return FGEMM_ERR_NOT_SUPPORTED;
   return FGEMM_OK;
@@ -127,7 +131,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
                            fgemm_dtype_t dtype, uint32_t flags, int beta_hint, int vec,
                            size_t ws_limit, fgemm_plan_t* out) {
   fgemm_plan_t p{};
-  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
+  const int swiglu = (flags & kSwiGLUFlags) != 0;
   double tc;
   int tile = best_tile(md, M, N, K, swiglu, 1, 2.0, 2.0, beta_hint, &tc);
   p.path = FGEMM_PATH_CLASSICAL;
@@ -262,7 +266,8 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   const uint32_t flags = epi_flags(c.epi);
   int tile = tile_id(plan.tile_m, plan.tile_n);
   if (tile < 0) return FGEMM_ERR_INVALID_VALUE;
-  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
+  const int swiglu = (flags & kSwiGLUFlags) != 0;
+  const int swiglu_bwd = (flags & FGEMM_EPI_SWIGLU_BWD) != 0;
   if (swiglu && !kTiles[tile].swiglu) return FGEMM_ERR_NOT_SUPPORTED;
   GemmBatch b{};
   b.count = 1;
@@ -283,6 +288,10 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     if (st != FGEMM_OK) return st;
     p.ss_partial = static_cast<float*>(ws);
   }
+  if (swiglu_bwd) {
+    p.dout = c.epi->swiglu_dout;
+    p.ldd = c.epi->swiglu_ldd;
+  }
   if (swiglu) {
     p.rms_ss = c.epi->rms_rowsumsq;
     p.rms_inv_n = 1.0f / (float)c.epi->rms_n;
@@ -295,7 +304,8 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   k.a_kcontig = c.ta == FGEMM_OP_N;
   k.b_kcontig = c.tb == FGEMM_OP_T;
   k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
-  k.epi = swiglu                        ? kEpiSwiGLU
+  k.epi = swiglu_bwd                    ? kEpiSwiGLUBwd
+          : swiglu                      ? kEpiSwiGLU
           : (flags & FGEMM_EPI_ACT)     ? kEpiAct
           : (flags & FGEMM_EPI_ROPE)    ? kEpiRope
                                         : kEpiStore16;
@@ -534,11 +544,13 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
   if (M > INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX) return FGEMM_ERR_NOT_SUPPORTED;
   const uint32_t flags = epi_flags(epi);
   if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU |
-                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE))
+                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE | FGEMM_EPI_SWIGLU_BWD))
     return FGEMM_ERR_INVALID_VALUE;
-  const int swiglu = (flags & FGEMM_EPI_RMS_SWIGLU) != 0;
-  if (swiglu && (flags & (FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_ACT | FGEMM_EPI_ROPE)))
-    return FGEMM_ERR_NOT_SUPPORTED;
+  const int swiglu = (flags & kSwiGLUFlags) != 0;
+  const int swiglu_bwd = (flags & FGEMM_EPI_SWIGLU_BWD) != 0;
+  if (swiglu && (flags & ~kSwiGLUFlags)) return FGEMM_ERR_NOT_SUPPORTED;
+  if ((flags & kSwiGLUFlags) == kSwiGLUFlags) return FGEMM_ERR_NOT_SUPPORTED;
+  if (swiglu_bwd && beta != 0.f) return FGEMM_ERR_NOT_SUPPORTED;
   // one transform before the rounding: an activation or the rotary embedding
   if ((flags & FGEMM_EPI_ACT) && (flags & FGEMM_EPI_ROPE)) return FGEMM_ERR_NOT_SUPPORTED;
   if ((flags & FGEMM_EPI_ACT) &&
@@ -557,11 +569,13 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
   const int64_t b_cols = tb == FGEMM_OP_N ? Nb : K;  // stored row width of B
   if (lda < (a_cols > 1 ? a_cols : 1)) return FGEMM_ERR_INVALID_VALUE;
   if (ldb < (b_cols > 1 ? b_cols : 1)) return FGEMM_ERR_INVALID_VALUE;
-  if (ldc < (N > 1 ? N : 1)) return FGEMM_ERR_INVALID_VALUE;
+  const int64_t Nc = swiglu_bwd ? 2 * N : N;  // output width
+  if (ldc < (Nc > 1 ? Nc : 1)) return FGEMM_ERR_INVALID_VALUE;
   const bool any_out = M > 0 && N > 0;
   if (any_out && K > 0 && (A == nullptr || B == nullptr)) return FGEMM_ERR_INVALID_VALUE;
   if (any_out && C == nullptr) return FGEMM_ERR_INVALID_VALUE;
-  (void)beta;
+  if (swiglu_bwd && ((any_out && epi->swiglu_dout == nullptr) || epi->swiglu_ldd < (N > 1 ? N : 1)))
+    return FGEMM_ERR_INVALID_VALUE;
   if ((flags & FGEMM_EPI_BIAS) && any_out && epi->bias == nullptr) return FGEMM_ERR_INVALID_VALUE;
   if ((flags & FGEMM_EPI_ROWSUMSQ) && any_out && epi->rowsumsq == nullptr)
     return FGEMM_ERR_INVALID_VALUE;
@@ -664,7 +678,7 @@ fgemm_status_t fgemm_gemm_plan(fgemm_handle_t h, const fgemm_plan_t* plan, fgemm
          static_cast<hipStream_t>(stream)};
   fgemm_plan_t p = *plan;
   if (p.path == FGEMM_PATH_CLASSICAL && (p.tile_m == 0 || p.tile_n == 0)) {
-    const int swiglu = (epi_flags(epi) & FGEMM_EPI_RMS_SWIGLU) != 0;
+    const int swiglu = (epi_flags(epi) & kSwiGLUFlags) != 0;
     int t = best_tile(h->model, M, N, K, swiglu, 1, 2.0, 2.0, beta != 0.f, nullptr);
     p.tile_m = tile_m_of(t);
     p.tile_n = tile_n_of(t);

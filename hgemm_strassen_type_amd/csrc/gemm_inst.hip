@@ -29,6 +29,8 @@ static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_
   if constexpr (CFG::FN % 2 == 0) {
     if (k.epi == kEpiSwiGLU) return k.vec ? plain<CFG, kEpiSwiGLU, true>(b, s)
                                           : plain<CFG, kEpiSwiGLU, false>(b, s);
+    if (k.epi == kEpiSwiGLUBwd) return k.vec ? plain<CFG, kEpiSwiGLUBwd, true>(b, s)
+                                             : plain<CFG, kEpiSwiGLUBwd, false>(b, s);
   }
   // fp32 accumulators out: Strassen sub-products and split-K partial slices
   if (k.epi == kEpiStore32 && k.vec) return plain<CFG, kEpiStore32, true>(b, s);

@@ -186,7 +186,8 @@ __device__ __forceinline__ v4u load8_checked(const uint16_t* p, int n, bool vec)
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
 struct GemmTile {
   static constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
-  static constexpr bool SWIGLU = EPI == kEpiSwiGLU;
+  // gate/up column pairs: the SwiGLU epilogue and its backward
+  static constexpr bool SWIGLU = EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd;
   using Acc = typename CFG::AccT;
   static constexpr int OUT_BN = SWIGLU ? BN / 2 : BN;
 
@@ -1037,6 +1038,43 @@ struct GemmTile {
           if (lc == 0 && rv) P.ss_partial[(int64_t)(tn * CFG::WAVES_N + wn) * P.M + row] = ss;
         }
       }
+    } else if constexpr (EPI == kEpiSwiGLUBwd) {
+      // gradient of silu(g)*u with respect to the gate and up accumulators (row scale
+      // fixed): columns out and N + out of a 2N-wide output
+      constexpr int HF = CFG::FN / 2;
+      const int out0 = n0 + wn * (CFG::WN / 2);
+      const uint16_t* dO = static_cast<const uint16_t*>(P.dout);
+#pragma unroll
+      for (int i = 0; i < CFG::FM; ++i) {
+        int row = m0 + wm * CFG::WM + i * MI + lr;
+        if (row >= P.M) continue;
+        const float r = rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps) * P.alpha;
+#pragma unroll
+        for (int j = 0; j < HF; ++j)
+#pragma unroll
+          for (int q = 0; q < G4; ++q) {
+            const int col = out0 + j * MI + q * (256 / MI) + 4 * lc;
+            const int nv = P.N - col;
+            if (nv <= 0) continue;
+            uint32_t og[4], ou[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const float d = s < nv ? to_f32<DT>(dO[(int64_t)row * P.ldd + col + s]) : 0.f;
+              const float g = r * acc[i][j][4 * q + s];
+              const float u = r * acc[i][j + HF][4 * q + s];
+              const float sg = 1.f / (1.f + __expf(-g));
+              og[s] = from_f32<DT>(d * u * sg * (1.f + g * (1.f - sg)) * r);
+              ou[s] = from_f32<DT>(d * g * sg * r);
+            }
+            const int64_t off = (int64_t)row * P.ldc + col;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              if (s < nv) {
+                C[off + s] = (uint16_t)og[s];
+                C[off + P.N + s] = (uint16_t)ou[s];
+              }
+          }
+      }
     } else {  // kEpiSwiGLU: output tile is BM x BN/2
       constexpr int HF = CFG::FN / 2;
       const int out0 = n0 + wn * (CFG::WN / 2);
@@ -1128,7 +1166,7 @@ __device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits
   // Phases with no K tail take the direct-load ring, also on M/N edge tiles
   // (clamped rows; transposed operands need 8 valid columns from the tile start).
   // Per-lane offsets are 32-bit, which bounds the leading dimensions there.
-  const int64_t b_rows = BKC ? (EPI == kEpiSwiGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
+  const int64_t b_rows = BKC ? (T::SWIGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
   w->fast = VEC && (P.K % CFG::BK == 0) && (AK || P.M - w->m0 >= 8) &&
             (BKC || P.N - w->n0 >= 8) &&
             (int64_t)(AK ? CFG::BM : CFG::BK + 1) * P.lda < (1ll << 31) &&
@@ -1202,7 +1240,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
     void* Cout = P.C;
     if (EPI == kEpiStore32 && splits > 1)
       Cout = static_cast<float*>(P.C) + (int64_t)cur.y * P.M * P.ldc;
-    if constexpr (VEC)
+    // the SwiGLU backward writes both halves from registers
+    if constexpr (VEC && EPI != kEpiSwiGLUBwd)
       T::epilogue_rows(P, Cout, cur.m0, cur.n0, cur.tn, wave, wm, wn, lane, smem, acc);
     else
       T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, smem, acc);
@@ -1229,7 +1268,7 @@ static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
   GemmBatch b = b0;
   int maxtiles = 0;
   for (int i = 0; i < b.count; ++i) {
-    int out_bn = EPI == kEpiSwiGLU ? CFG::BN / 2 : CFG::BN;
+    int out_bn = (EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd) ? CFG::BN / 2 : CFG::BN;
     int t = ((b.p[i].M + CFG::BM - 1) / CFG::BM) * ((b.p[i].N + out_bn - 1) / out_bn);
     if (t > maxtiles) maxtiles = t;
   }

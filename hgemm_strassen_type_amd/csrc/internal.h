@@ -18,6 +18,7 @@ enum EpiKind : int {
   kEpiStore32 = 2,   // fp32 output of the raw accumulators (Strassen sub-products)
   kEpiAct = 3,       // kEpiStore16 plus an activation before rounding
   kEpiRope = 4,      // kEpiStore16 plus the rotary position embedding before rounding
+  kEpiSwiGLUBwd = 5, // 16-bit gradient of the SwiGLU epilogue's input (2N columns)
 };
 
 // Runtime epilogue switches inside kEpiStore16.
@@ -43,6 +44,8 @@ struct GemmProblem {
   const int32_t* rope_pos;  // [M] positions, or null: row + rope_off
   int64_t rope_off;
   double rope_log2_base;
+  const void* dout;         // kEpiSwiGLUBwd: [M][ldd] incoming 16-bit gradient
+  int64_t ldd;
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).

@@ -20,7 +20,7 @@ FGEMM_ERR_WORKSPACE, FGEMM_ERR_ALLOC, FGEMM_ERR_HIP = 3, 4, 5
 FGEMM_OP_N, FGEMM_OP_T = 0, 1
 FGEMM_F16, FGEMM_BF16 = 0, 1
 FGEMM_EPI_NONE, FGEMM_EPI_BIAS, FGEMM_EPI_ROWSUMSQ, FGEMM_EPI_RMS_SWIGLU = 0, 1, 2, 4
-FGEMM_EPI_ACT, FGEMM_EPI_ROPE = 8, 16
+FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD = 8, 16, 32
 FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
 FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
@@ -44,7 +44,8 @@ class fgemm_epilogue_t(ctypes.Structure):
                 ("rms_n", ctypes.c_int64), ("rms_eps", ctypes.c_float),
                 ("act", ctypes.c_int32), ("rope_positions", ctypes.c_void_p),
                 ("rope_offset", ctypes.c_int64), ("rope_head_dim", ctypes.c_int64),
-                ("rope_theta", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("swiglu_dout", ctypes.c_void_p),
+                ("swiglu_ldd", ctypes.c_int64)]
 
 
 class fgemm_plan_t(ctypes.Structure):
@@ -144,10 +145,11 @@ def fgemm_set_model(handle: int, model: fgemm_model_t):
 
 
 def make_epilogue(flags=0, bias=0, rowsumsq=0, rms_rowsumsq=0, rms_n=0, rms_eps=0.0, act=0,
-                  rope_positions=0, rope_offset=0, rope_head_dim=0, rope_theta=10000.0):
+                  rope_positions=0, rope_offset=0, rope_head_dim=0, rope_theta=10000.0,
+                  swiglu_dout=0, swiglu_ldd=0):
     return fgemm_epilogue_t(flags, bias or None, rowsumsq or None, rms_rowsumsq or None, rms_n,
                             rms_eps, act, rope_positions or None, rope_offset, rope_head_dim,
-                            rope_theta)
+                            rope_theta, swiglu_dout or None, swiglu_ldd)
 
 
 def fgemm_select(handle, transA, transB, M, N, K, dtype, epilogue=None) -> fgemm_plan_t:
@@ -252,6 +254,8 @@ class Handle:
         M = A.shape[1] if transA else A.shape[0]
         K = A.shape[0] if transA else A.shape[1]
         N = C.shape[1]
+        if epilogue is not None and epilogue.flags & FGEMM_EPI_SWIGLU_BWD:
+            N //= 2  # the backward writes the gate and up gradients: C is M x 2N
         dt = torch_dtype_code(C)
         s = current_stream() if stream is None else stream
         args = (ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),

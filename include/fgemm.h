@@ -83,14 +83,24 @@ typedef enum { FGEMM_F16 = 0, FGEMM_BF16 = 1 } fgemm_dtype_t;
  *     D[i][2p+1] <- D[i][2p] sin(theta) + D[i][2p+1] cos(theta)
  *   with pos_i = rope_positions[i], or i + rope_offset when rope_positions is NULL.
  *   (The half-split pairing (d, d + hd/2) is this one after a fixed permutation
- *   of op(B)'s columns within each head.) */
+ *   of op(B)'s columns within each head.)
+ * SWIGLU_BWD (alone; same note, CODA section: backward passes of SwiGLU in the
+ *   epilogue): the backward of RMS_SWIGLU with the row scale held fixed.  op(B)
+ *   has the forward's 2N columns [gate | up]; g, u and r_i are as in RMS_SWIGLU;
+ *   dO = swiglu_dout[i][j] (device, M x N, leading dimension swiglu_ldd) is the
+ *   incoming gradient.  C is M x 2N (ldc >= 2N), the gradient with respect to
+ *   op(A)op(B):
+ *     C[i][j]     = RNE16(dO * u * silu'(g) * r_i * alpha)
+ *     C[i][N + j] = RNE16(dO * silu(g) * r_i * alpha),
+ *   silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)); beta must be 0. */
 enum {
     FGEMM_EPI_NONE = 0,
     FGEMM_EPI_BIAS = 1,
     FGEMM_EPI_ROWSUMSQ = 2,
     FGEMM_EPI_RMS_SWIGLU = 4,
     FGEMM_EPI_ACT = 8,
-    FGEMM_EPI_ROPE = 16
+    FGEMM_EPI_ROPE = 16,
+    FGEMM_EPI_SWIGLU_BWD = 32
 };
 typedef enum { FGEMM_ACT_RELU = 1, FGEMM_ACT_SILU = 2, FGEMM_ACT_GELU_TANH = 3 } fgemm_act_t;
 
@@ -106,6 +116,8 @@ typedef struct {
     int64_t rope_offset;        /* ROPE: position of row 0 when rope_positions is NULL */
     int64_t rope_head_dim;      /* ROPE: even, divides N                              */
     float rope_theta;           /* ROPE: frequency base (> 0), e.g. 10000             */
+    const void* swiglu_dout;    /* SWIGLU_BWD: device [M][swiglu_ldd] 16-bit gradient */
+    int64_t swiglu_ldd;         /* SWIGLU_BWD: leading dimension of swiglu_dout (>= N) */
 } fgemm_epilogue_t;
 
 typedef enum {

@@ -74,7 +74,8 @@ def chk(ta=N_, tb=N_, M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, beta=0.0, 
     if lda is None:
         lda = K if ta == N_ else M
     if ldb is None:
-        nb = 2 * N if epi is not None and epi.flags & fgemm.FGEMM_EPI_RMS_SWIGLU else N
+        pair = fgemm.FGEMM_EPI_RMS_SWIGLU | fgemm.FGEMM_EPI_SWIGLU_BWD
+        nb = 2 * N if epi is not None and epi.flags & pair else N
         ldb = nb if tb == N_ else K
     if ldc is None:
         ldc = N
@@ -134,6 +135,18 @@ def test_check_args_epilogues():
     assert chk(epi=E(ACT | ROPE, act=1, rope_head_dim=16)) == NOTSUP
     assert chk(epi=E(fgemm.FGEMM_EPI_RMS_SWIGLU | ACT, rms_rowsumsq=P, rms_n=4096,
                      act=1)) == NOTSUP
+    # SwiGLU backward: 2N-wide output, the incoming gradient, beta 0, alone
+    BWD = fgemm.FGEMM_EPI_SWIGLU_BWD
+    bw = E(BWD, rms_rowsumsq=P, rms_n=4096, rms_eps=1e-6, swiglu_dout=P, swiglu_ldd=64)
+    assert chk(epi=bw, ldc=128) == OK
+    assert chk(epi=bw, ldc=64) == INVAL                                    # output is 2N wide
+    assert chk(epi=bw, ldc=128, beta=0.5) == NOTSUP
+    assert chk(epi=E(BWD, rms_rowsumsq=P, rms_n=4096, swiglu_ldd=64), ldc=128) == INVAL  # no dO
+    assert chk(epi=E(BWD, rms_rowsumsq=P, rms_n=4096, swiglu_dout=P, swiglu_ldd=32), ldc=128) == INVAL
+    assert chk(epi=E(BWD | fgemm.FGEMM_EPI_BIAS, bias=P, rms_rowsumsq=P, rms_n=4096,
+                     swiglu_dout=P, swiglu_ldd=64), ldc=128) == NOTSUP
+    assert chk(epi=E(BWD | fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096,
+                     swiglu_dout=P, swiglu_ldd=64), ldc=128) == NOTSUP
 
 
 # ---------------------------------------------------------------- decision model

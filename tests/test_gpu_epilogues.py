@@ -292,3 +292,70 @@ def test_rope_backward_is_negated_positions():
     _, Qb, _ = oracle.gemm(Y, eye, dtype=dtype, epi=oracle.EPI_ROPE, rope_pos=-pos.astype(np.int64),
                            rope_head_dim=hd)
     assert rel_err(back, Qb, dtype) <= CLASSICAL_TOL
+
+
+
+# ------------------------------------------------------------ SwiGLU backward
+def run_swiglu_bwd(X, W, dO, ss, dtype, transB=False, tile=None, alpha=1.0, pad=0):
+    import torch
+    M, Nout = dO.shape
+    Xd, dOd = to_dev(X, dtype, pad), to_dev(dO, dtype, pad)
+    Wst = np.ascontiguousarray(W.T) if transB else W
+    Wd = to_dev(Wst, dtype, pad)
+    Cd = empty_out(M, 2 * Nout, dtype)
+    ssd = torch.from_numpy(np.asarray(ss, dtype=np.float32)).cuda()
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ssd.data_ptr(), rms_n=4096,
+                              rms_eps=1e-6, swiglu_dout=dOd.data_ptr(), swiglu_ldd=dOd.stride(0))
+    handle().gemm(Xd, Wd, Cd, transB=transB, alpha=alpha, epilogue=epi,
+                  plan=fgemm.classical_plan(*tile) if tile else None)
+    torch.cuda.synchronize()
+    return from_dev(Cd)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("transB", [False, True])
+@pytest.mark.parametrize("tile", TILES[:3])
+def test_swiglu_backward_ragged(dtype, transB, tile):
+    """Gradient of the RMS + SwiGLU epilogue with respect to the recomputed gate|up
+    product (row scale fixed), ragged M and N, against the oracle."""
+    M, K, Nout = 300, 256, 264
+    say(f"swiglu bwd dtype={dtype} transB={transB} tile={tile}")
+    X = inputs.normal((M, K), 751, dtype)
+    W = inputs.normal((K, 2 * Nout), 752, dtype, std=0.1)
+    dO = inputs.normal((M, Nout), 753, dtype)
+    ss = (np.random.default_rng(754).uniform(0.5, 2.0, M) * 4096).astype(np.float32)
+    _, Q = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
+                             alpha=1.5, dtype=dtype)
+    got = run_swiglu_bwd(X, W, dO, ss, dtype, transB=transB, tile=tile, alpha=1.5)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+def test_swiglu_backward_unaligned():
+    # leading dimensions that are not multiples of 8 take the bounds-checked loads
+    dtype = BF16
+    M, K, Nout = 70, 96, 64
+    say("swiglu bwd unaligned")
+    X = inputs.normal((M, K), 761, dtype)
+    W = inputs.normal((K, 2 * Nout), 762, dtype, std=0.1)
+    dO = inputs.normal((M, Nout), 763, dtype)
+    ss = np.full(M, 4096.0, dtype=np.float32)
+    _, Q = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
+                             dtype=dtype)
+    got = run_swiglu_bwd(X, W, dO, ss, dtype, pad=3)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+
+
+def test_swiglu_backward_llm_size():
+    """The chain's second GEMM backward at its configured size: Y [8192 x 4096] N(0,1),
+    W2 [4096 x 2*11008] N(0,0.02), dO N(0,1), as the model picks the plan; sampled rows."""
+    dtype, M, K, Nout = BF16, 8192, 4096, 11008
+    say("swiglu bwd 8192x4096 -> 2x11008")
+    Y = inputs.normal((M, K), 4101, dtype)
+    W2 = inputs.normal((K, 2 * Nout), 4102, dtype, std=0.02)
+    dO = inputs.normal((M, Nout), 4103, dtype)
+    ss = (np.random.default_rng(4104).uniform(0.5, 2.0, M) * K).astype(np.float32)
+    got = run_swiglu_bwd(Y, W2, dO, ss, dtype)
+    rows = inputs.sample_rows(M, 24, 14)
+    _, Q = oracle.swiglu_bwd(Y, W2, dO, rms_ss=ss[rows].astype(np.float64), rms_n=4096,
+                             rms_eps=1e-6, dtype=dtype, rows=rows)
+    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
