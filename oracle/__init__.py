@@ -77,7 +77,11 @@ def _load():
     lib.oracle_swiglu_bwd.restype = ctypes.c_int
     lib.oracle_swiglu_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
                                       u16p, i64, u16p, i64, ctypes.c_int, f64p, f64p, i64,
-                                      ctypes.c_double, i64p, i64, f64p, u16p, ctypes.c_int]
+                                      ctypes.c_double, i64p, i64, f64p, u16p, f64p, ctypes.c_int]
+    lib.oracle_rms_bwd.restype = ctypes.c_int
+    lib.oracle_rms_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
+                                   u16p, i64, u16p, i64, ctypes.c_int, f64p, f64p, f64p, i64,
+                                   ctypes.c_double, i64p, i64, f64p, u16p, ctypes.c_int]
     lib.oracle_strassen.restype = ctypes.c_int
     lib.oracle_strassen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, i64, u16p,
                                     i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p]
@@ -179,7 +183,8 @@ def swiglu_bwd(A, B, dO, *, rms_ss, rms_n, rms_eps=1e-6, alpha=1.0, transA=False
     op(B) has 2*Nout columns (gate | up); dO (M x Nout, 16-bit bits) is the incoming
     gradient and rms_ss the fp64 sums of squares of the selected rows.  Returns
     (D, Q): the gradient with respect to op(A)op(B) for the selected rows,
-    unrounded and RNE 16-bit bits, both nrows x 2*Nout.
+    unrounded and RNE 16-bit bits, both nrows x 2*Nout, and rgrad, the gradient
+    with respect to each selected row's scale r_i.
     """
     A, B = _u16(A), _u16(B)
     M = A.shape[1] if transA else A.shape[0]
@@ -192,12 +197,39 @@ def swiglu_bwd(A, B, dO, *, rms_ss, rms_n, rms_eps=1e-6, alpha=1.0, transA=False
         raise ValueError("dO or rms_ss shape")
     D = np.empty((rows.size, N), dtype=np.float64)
     Q = np.empty((rows.size, N), dtype=np.uint16)
+    rg = np.empty(rows.size, dtype=np.float64)
     rc = _load().oracle_swiglu_bwd(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
                                    A.shape[1], _ptr(B), B.shape[1], dtype, _ptr(d), _ptr(rms_ss),
                                    rms_n, float(rms_eps), _ptr(rows), rows.size, _ptr(D), _ptr(Q),
-                                   threads or default_threads())
+                                   _ptr(rg), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_swiglu_bwd rejected its arguments")
+    return D, Q, rg
+
+
+def rms_bwd(A, B, X, *, rms_ss, rgrad, rms_n, rms_eps=1e-6, alpha=1.0, transA=False,
+            transB=False, dtype=BF16, rows=None, threads=None):
+    """alpha*op(A)op(B) + c_i X with c_i = -r_i^3 rgrad_i / n: the gradient of the
+    RMS-normalised layer's input X (M x N, 16-bit bits).  rms_ss and rgrad hold one
+    fp64 value per selected row.  Returns (D, Q) for the selected rows."""
+    A, B = _u16(A), _u16(B)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    x = np.ascontiguousarray(decode(_u16(X)[rows], dtype), dtype=np.float64)
+    rms_ss = np.ascontiguousarray(rms_ss, dtype=np.float64)
+    rgrad = np.ascontiguousarray(rgrad, dtype=np.float64)
+    if x.shape != (rows.size, N) or rms_ss.size != rows.size or rgrad.size != rows.size:
+        raise ValueError("X, rms_ss or rgrad shape")
+    D = np.empty((rows.size, N), dtype=np.float64)
+    Q = np.empty((rows.size, N), dtype=np.uint16)
+    rc = _load().oracle_rms_bwd(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
+                                A.shape[1], _ptr(B), B.shape[1], dtype, _ptr(x), _ptr(rms_ss),
+                                _ptr(rgrad), rms_n, float(rms_eps), _ptr(rows), rows.size, _ptr(D),
+                                _ptr(Q), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_rms_bwd rejected its arguments")
     return D, Q
 
 

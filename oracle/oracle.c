@@ -50,7 +50,13 @@
  *     forward and dO the incoming gradient, write the gradient with respect to H:
  *       out[i][j]        = Q(dO[i][j] * u * silu'(g) * r_i * alpha)
  *       out[i][Nout + j] = Q(dO[i][j] * silu(g) * r_i * alpha)
- *     silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)).
+ *     silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)).  It also gives the
+ *     gradient with respect to the row scale, rgrad_i = sum_j dO (silu'(g) g u +
+ *     silu(g) u) / r_i.
+ *   - RMS_BWD, the rest of the RMSNorm backward (r_i = 1/sqrt(ss_i/n + eps),
+ *     ss_i = sum_k X_ik^2, so dr_i/dX_ik = -r_i^3 X_ik / n): a GEMM's epilogue adds
+ *     the scale's contribution to the gradient of X,
+ *       out = Q(alpha*acc + c_i * X_ij),  c_i = -r_i^3 * rgrad_i / n.
  *   - Strassen recursion keeps fp64 temporaries (it is the exact identity check).
  */
 #include <math.h>
@@ -323,7 +329,8 @@ int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, doub
 int oracle_swiglu_bwd(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
                       const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int dtype,
                       const double* dO, const double* rms_ss, int64_t rms_n, double rms_eps,
-                      const int64_t* rows, int64_t nrows, double* D, uint16_t* Q, int nthreads) {
+                      const int64_t* rows, int64_t nrows, double* D, uint16_t* Q, double* rgrad,
+                      int nthreads) {
     if (N % 2 || rms_n <= 0) return -1;
     int64_t Nout = N / 2;
     for (int64_t r = 0; r < nrows; ++r)
@@ -336,17 +343,53 @@ int oracle_swiglu_bwd(int transA, int transB, int64_t M, int64_t N, int64_t K, d
     }
     for (int64_t r = 0; r < nrows; ++r) {
         const double* h = H + r * N;
-        double rs = alpha / sqrt(rms_ss[r] / (double)rms_n + rms_eps);
+        double rr = 1.0 / sqrt(rms_ss[r] / (double)rms_n + rms_eps);
+        double rs = alpha * rr;
+        double acc_r = 0.0;
         for (int64_t j = 0; j < Nout; ++j) {
             double g = rs * h[j], u = rs * h[j + Nout];
             double s = 1.0 / (1.0 + exp(-g));
             double d = dO[r * Nout + j];
             double dg = d * u * s * (1.0 + g * (1.0 - s)) * rs;
             double du = d * g * s * rs;
+            acc_r += d * (s * (1.0 + g * (1.0 - s)) * g * u + g * s * u);
             D[r * N + j] = dg;
             D[r * N + Nout + j] = du;
             Q[r * N + j] = oracle_encode(dg, dtype);
             Q[r * N + Nout + j] = oracle_encode(du, dtype);
+        }
+        if (rgrad) rgrad[r] = acc_r / rr;
+    }
+    free(H);
+    return 0;
+}
+
+/*
+ * oracle_rms_bwd: out = Q(alpha*op(A)op(B) + c_i * X_ij), c_i = -r_i^3 * rgrad_i / n,
+ * r_i = 1/sqrt(ss_i/n + eps).  X (the normalised layer's input, decoded, selected
+ * rows, nrows x N), rms_ss and rgrad are per selected row.
+ */
+int oracle_rms_bwd(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int dtype,
+                   const double* X, const double* rms_ss, const double* rgrad, int64_t rms_n,
+                   double rms_eps, const int64_t* rows, int64_t nrows, double* D, uint16_t* Q,
+                   int nthreads) {
+    if (rms_n <= 0) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    double* H = (double*)malloc(sizeof(double) * (nrows * N > 0 ? nrows * N : 1));
+    if (!H) return -1;
+    if (raw_products(transA, transB, M, N, K, A, lda, B, ldb, dtype, rows, nrows, H, nthreads)) {
+        free(H);
+        return -1;
+    }
+    for (int64_t r = 0; r < nrows; ++r) {
+        double rr = 1.0 / sqrt(rms_ss[r] / (double)rms_n + rms_eps);
+        double c = -rr * rr * rr * rgrad[r] / (double)rms_n;
+        for (int64_t j = 0; j < N; ++j) {
+            double d = alpha * H[r * N + j] + c * X[r * N + j];
+            D[r * N + j] = d;
+            Q[r * N + j] = oracle_encode(d, dtype);
         }
     }
     free(H);

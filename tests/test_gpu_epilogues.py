@@ -324,7 +324,7 @@ def test_swiglu_backward_ragged(dtype, transB, tile):
     W = inputs.normal((K, 2 * Nout), 752, dtype, std=0.1)
     dO = inputs.normal((M, Nout), 753, dtype)
     ss = (np.random.default_rng(754).uniform(0.5, 2.0, M) * 4096).astype(np.float32)
-    _, Q = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
+    _, Q, _ = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
                              alpha=1.5, dtype=dtype)
     got = run_swiglu_bwd(X, W, dO, ss, dtype, transB=transB, tile=tile, alpha=1.5)
     assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
@@ -339,7 +339,7 @@ def test_swiglu_backward_unaligned():
     W = inputs.normal((K, 2 * Nout), 762, dtype, std=0.1)
     dO = inputs.normal((M, Nout), 763, dtype)
     ss = np.full(M, 4096.0, dtype=np.float32)
-    _, Q = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
+    _, Q, _ = oracle.swiglu_bwd(X, W, dO, rms_ss=ss.astype(np.float64), rms_n=4096, rms_eps=1e-6,
                              dtype=dtype)
     got = run_swiglu_bwd(X, W, dO, ss, dtype, pad=3)
     assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
@@ -356,6 +356,6 @@ def test_swiglu_backward_llm_size():
     ss = (np.random.default_rng(4104).uniform(0.5, 2.0, M) * K).astype(np.float32)
     got = run_swiglu_bwd(Y, W2, dO, ss, dtype)
     rows = inputs.sample_rows(M, 24, 14)
-    _, Q = oracle.swiglu_bwd(Y, W2, dO, rms_ss=ss[rows].astype(np.float64), rms_n=4096,
+    _, Q, _ = oracle.swiglu_bwd(Y, W2, dO, rms_ss=ss[rows].astype(np.float64), rms_n=4096,
                              rms_eps=1e-6, dtype=dtype, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL

@@ -421,7 +421,7 @@ def test_swiglu_backward_is_the_gradient_of_the_forward():
     ss = rng.uniform(0.5, 2.0, M) * 8
     alpha, n = 1.5, 8
     A = ints_to_bits(np.eye(M), F16)
-    D, _ = oracle.swiglu_bwd(A, Hb, dO, rms_ss=ss, rms_n=n, rms_eps=1e-6, alpha=alpha, dtype=F16)
+    D, _, _ = oracle.swiglu_bwd(A, Hb, dO, rms_ss=ss, rms_n=n, rms_eps=1e-6, alpha=alpha, dtype=F16)
     rs = alpha / np.sqrt(ss / n + 1e-6)
 
     def f(Hx):
@@ -439,7 +439,58 @@ def test_swiglu_backward_is_the_gradient_of_the_forward():
     # closed forms: gate 0 -> silu'(0) = 1/2 and silu(0) = 0
     Z = H.copy()
     Z[:, :Nout] = 0.0
-    D0, _ = oracle.swiglu_bwd(A, inputs.to_bits(Z, F16), dO, rms_ss=ss, rms_n=n, rms_eps=1e-6,
+    D0, _, _ = oracle.swiglu_bwd(A, inputs.to_bits(Z, F16), dO, rms_ss=ss, rms_n=n, rms_eps=1e-6,
                               alpha=alpha, dtype=F16)
     assert np.array_equal(D0[:, Nout:], np.zeros((M, Nout)))
     assert np.allclose(D0[:, :Nout], d * rs[:, None] * Z[:, Nout:] * 0.5 * rs[:, None], rtol=1e-15)
+
+
+def test_rmsnorm_backward_chain_by_central_differences():
+    # L = sum dO * silu(r a (Y W2)_gate) * (r a (Y W2)_up) with r_i = 1/sqrt(sum_k Y_ik^2/n
+    # + eps): the oracle's two backward pieces (the SwiGLU backward's dH and row-scale
+    # gradient, then dY = dH W2^T + c_i Y) must give dL/dY by central differences
+    rng = np.random.default_rng(31)
+    M, Hd, F = 3, 8, 5
+    Yb = inputs.to_bits(rng.uniform(-1, 1, (M, Hd)), F16)
+    W2b = inputs.to_bits(rng.uniform(-0.5, 0.5, (Hd, 2 * F)), F16)
+    dOb = inputs.to_bits(rng.uniform(-1, 1, (M, F)), F16)
+    Y, W2, dO = oracle.decode(Yb, F16), oracle.decode(W2b, F16), oracle.decode(dOb, F16)
+    alpha, eps = 1.25, 1e-6
+
+    def loss(Yx):
+        r = 1.0 / np.sqrt(np.sum(Yx * Yx, axis=1) / Hd + eps)
+        H = Yx @ W2
+        g, u = (alpha * r)[:, None] * H[:, :F], (alpha * r)[:, None] * H[:, F:]
+        return np.sum(dO * g / (1 + np.exp(-g)) * u)
+    num = np.zeros_like(Y)
+    for i in range(M):
+        for k in range(Hd):
+            Yp, Ym = Y.copy(), Y.copy()
+            Yp[i, k] += 1e-6
+            Ym[i, k] -= 1e-6
+            num[i, k] = (loss(Yp) - loss(Ym)) / 2e-6
+    ss = np.sum(Y * Y, axis=1)
+    dH, _, rgrad = oracle.swiglu_bwd(Yb, W2b, dOb, rms_ss=ss, rms_n=Hd, rms_eps=eps, alpha=alpha,
+                                     dtype=F16)
+    r = 1.0 / np.sqrt(ss / Hd + eps)
+    dY = dH @ W2.T + (-(r ** 3) * rgrad / Hd)[:, None] * Y
+    assert np.allclose(dY, num, rtol=1e-6, atol=1e-8)
+
+
+def test_rms_bwd_closed_forms():
+    rng = np.random.default_rng(41)
+    M, K, N = 4, 6, 8
+    A = inputs.to_bits(rng.uniform(-1, 1, (M, K)), BF16)
+    B = inputs.to_bits(rng.uniform(-1, 1, (K, N)), BF16)
+    X = inputs.to_bits(rng.uniform(-1, 1, (M, N)), BF16)
+    ss = rng.uniform(1, 3, M)
+    # no row-scale gradient: the plain product
+    D, _ = oracle.rms_bwd(A, B, X, rms_ss=ss, rgrad=np.zeros(M), rms_n=N, alpha=0.5, dtype=BF16)
+    D0, _, _ = oracle.gemm(A, B, alpha=0.5, dtype=BF16)
+    assert np.array_equal(D, D0)
+    # no product: exactly c_i * X with c_i = -r_i^3 rgrad_i / n
+    Z = inputs.to_bits(np.zeros((M, K)), BF16)
+    rg = rng.uniform(-2, 2, M)
+    D, _ = oracle.rms_bwd(Z, B, X, rms_ss=ss, rgrad=rg, rms_n=N, rms_eps=0.0, dtype=BF16)
+    c = -(ss / N) ** -1.5 * rg / N
+    assert np.allclose(D, c[:, None] * oracle.decode(X, BF16), rtol=1e-15, atol=0)
