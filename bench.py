@@ -271,13 +271,22 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     # backward of GEMM2's epilogue: recompute Y W2 and write the gate|up gradient
     dO = normal((Mc, Fc), 4004)
     dH = torch.empty((Mc, 2 * Fc), dtype=torch.bfloat16, device="cuda")
+    rg = torch.empty(Mc, dtype=torch.float32, device="cuda")
     eb = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
-                             rms_eps=1e-6, swiglu_dout=dO.data_ptr(), swiglu_ldd=Fc)
+                             rms_eps=1e-6, swiglu_dout=dO.data_ptr(), swiglu_ldd=Fc,
+                             rms_grad=rg.data_ptr())
     tb = timer.time(lambda: h.gemm(Y, W2, dH, epilogue=eb), reps, 2)
-    W["fused_chain_8192x4096_ffn11008"]["gemm2_swiglu_backward"] = {
-        "ms": round(tb, 5), "tflops": round(f2 / (tb * 1e-3) / 1e12, 2)}
-    log(f"chain GEMM2 backward: {W['fused_chain_8192x4096_ffn11008']['gemm2_swiglu_backward']}")
-    del dO, dH
+    # then dY = dH W2^T plus the RMS scale's share (the RMSNorm backward)
+    dY = torch.empty((Mc, Hc), dtype=torch.bfloat16, device="cuda")
+    er = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_BWD, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
+                             rms_eps=1e-6, rms_grad=rg.data_ptr(), rms_x=Y.data_ptr(), rms_ldx=Hc)
+    tr = timer.time(lambda: h.gemm(dH, W2, dY, transB=True, epilogue=er), reps, 2)
+    W["fused_chain_8192x4096_ffn11008"]["backward"] = {
+        "gemm2_swiglu_backward_ms": round(tb, 5), "gemm2_swiglu_backward_tflops":
+        round(f2 / (tb * 1e-3) / 1e12, 2), "dY_rms_backward_ms": round(tr, 5),
+        "dY_rms_backward_tflops": round(f2 / (tr * 1e-3) / 1e12, 2)}
+    log(f"chain backward: {W['fused_chain_8192x4096_ffn11008']['backward']}")
+    del dO, dH, dY, rg
     del X, Wt, W2, Y, O, ss
 
     # Strassen / Winograd vs classical, and the model's pick

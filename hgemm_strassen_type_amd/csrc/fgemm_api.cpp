@@ -114,7 +114,8 @@ fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int
   // gate/up boundary); every epilogue is applied in the top-level post-add
   const int64_t q = 8ll << p.depth;
   const int64_t Nb = (flags & FGEMM_EPI_RMS_SWIGLU) ? 2 * N : N;
-  if (flags & FGEMM_EPI_SWIGLU_BWD) return FGEMM_ERR_NOT_SUPPORTED;  // classical path only
+  if (flags & (FGEMM_EPI_SWIGLU_BWD | FGEMM_EPI_RMS_BWD))
+    return FGEMM_ERR_NOT_SUPPORTED;  // classical path only
   if (M % q || Nb % q || K % q || M == 0 || N == 0 || K == 0) return FGEMM_ERR_NOT_SUPPORTED;
   if (!vec) return FGEMM_ERR_NOT_SUPPORTED;
   return FGEMM_OK;
@@ -288,9 +289,27 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     if (st != FGEMM_OK) return st;
     p.ss_partial = static_cast<float*>(ws);
   }
+  const int rms_bwd = (flags & FGEMM_EPI_RMS_BWD) != 0;
   if (swiglu_bwd) {
     p.dout = c.epi->swiglu_dout;
     p.ldd = c.epi->swiglu_ldd;
+    if (c.epi->rms_grad) {
+      // per-wave partials of the row-scale gradient, one per (output tile column, wave column)
+      p.rms_grad_out = 1;
+      parts = (int)ceil_div(c.N, tile_n_of(tile) / 2) * waves_n_of(tile);
+      void* ws;
+      fgemm_status_t st = ensure_workspace(h, (size_t)parts * (size_t)c.M * 4, &ws);
+      if (st != FGEMM_OK) return st;
+      p.ss_partial = static_cast<float*>(ws);
+    }
+  }
+  if (rms_bwd) {
+    p.rms_ss = c.epi->rms_rowsumsq;
+    p.rms_inv_n = 1.0f / (float)c.epi->rms_n;
+    p.rms_eps = c.epi->rms_eps;
+    p.rms_grad = c.epi->rms_grad;
+    p.rms_x = c.epi->rms_x;
+    p.ldx = c.epi->rms_ldx;
   }
   if (swiglu) {
     p.rms_ss = c.epi->rms_rowsumsq;
@@ -304,7 +323,8 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   k.a_kcontig = c.ta == FGEMM_OP_N;
   k.b_kcontig = c.tb == FGEMM_OP_T;
   k.dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
-  k.epi = swiglu_bwd                    ? kEpiSwiGLUBwd
+  k.epi = rms_bwd                       ? kEpiRmsBwd
+          : swiglu_bwd                  ? kEpiSwiGLUBwd
           : swiglu                      ? kEpiSwiGLU
           : (flags & FGEMM_EPI_ACT)     ? kEpiAct
           : (flags & FGEMM_EPI_ROPE)    ? kEpiRope
@@ -331,7 +351,8 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
   hipError_t e = launch_gemm(k, b, c.stream);
   if (e != hipSuccess) return FGEMM_ERR_HIP;
   if (parts) {
-    e = launch_rowsumsq_reduce(p.ss_partial, parts, (int)c.M, c.epi->rowsumsq, c.stream);
+    e = launch_rowsumsq_reduce(p.ss_partial, parts, (int)c.M,
+                               swiglu_bwd ? c.epi->rms_grad : c.epi->rowsumsq, c.stream);
     if (e != hipSuccess) return FGEMM_ERR_HIP;
   }
   return FGEMM_OK;
@@ -544,8 +565,13 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
   if (M > INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX) return FGEMM_ERR_NOT_SUPPORTED;
   const uint32_t flags = epi_flags(epi);
   if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU |
-                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE | FGEMM_EPI_SWIGLU_BWD))
+                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE | FGEMM_EPI_SWIGLU_BWD |
+                          FGEMM_EPI_RMS_BWD))
     return FGEMM_ERR_INVALID_VALUE;
+  // the RMS backward epilogue runs alone, without beta
+  const int rms_bwd = (flags & FGEMM_EPI_RMS_BWD) != 0;
+  if (rms_bwd && (flags != (uint32_t)FGEMM_EPI_RMS_BWD || beta != 0.f))
+    return FGEMM_ERR_NOT_SUPPORTED;
   const int swiglu = (flags & kSwiGLUFlags) != 0;
   const int swiglu_bwd = (flags & FGEMM_EPI_SWIGLU_BWD) != 0;
   if (swiglu && (flags & ~kSwiGLUFlags)) return FGEMM_ERR_NOT_SUPPORTED;
@@ -576,6 +602,13 @@ fgemm_status_t fgemm_check_args(fgemm_op_t ta, fgemm_op_t tb, int64_t M, int64_t
   if (any_out && C == nullptr) return FGEMM_ERR_INVALID_VALUE;
   if (swiglu_bwd && ((any_out && epi->swiglu_dout == nullptr) || epi->swiglu_ldd < (N > 1 ? N : 1)))
     return FGEMM_ERR_INVALID_VALUE;
+  if (rms_bwd) {
+    if (any_out && (epi->rms_x == nullptr || epi->rms_grad == nullptr ||
+                    epi->rms_rowsumsq == nullptr))
+      return FGEMM_ERR_INVALID_VALUE;
+    if (epi->rms_ldx < (N > 1 ? N : 1) || epi->rms_n <= 0 || !(epi->rms_eps >= 0.f))
+      return FGEMM_ERR_INVALID_VALUE;
+  }
   if ((flags & FGEMM_EPI_BIAS) && any_out && epi->bias == nullptr) return FGEMM_ERR_INVALID_VALUE;
   if ((flags & FGEMM_EPI_ROWSUMSQ) && any_out && epi->rowsumsq == nullptr)
     return FGEMM_ERR_INVALID_VALUE;

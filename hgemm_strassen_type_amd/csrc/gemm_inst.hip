@@ -21,6 +21,9 @@ template <class CFG>
 static hipError_t by_epilogue(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
   if (k.epi == kEpiStore16) return k.vec ? plain<CFG, kEpiStore16, true>(b, s)
                                          : plain<CFG, kEpiStore16, false>(b, s);
+  // the RMS scale's share of an input gradient
+  if (k.epi == kEpiRmsBwd) return k.vec ? plain<CFG, kEpiRmsBwd, true>(b, s)
+                                        : plain<CFG, kEpiRmsBwd, false>(b, s);
   // an activation or the rotary embedding before the rounding
   if (k.epi == kEpiAct) return k.vec ? plain<CFG, kEpiAct, true>(b, s)
                                      : plain<CFG, kEpiAct, false>(b, s);

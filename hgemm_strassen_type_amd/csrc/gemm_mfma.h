@@ -1047,15 +1047,16 @@ struct GemmTile {
 #pragma unroll
       for (int i = 0; i < CFG::FM; ++i) {
         int row = m0 + wm * CFG::WM + i * MI + lr;
-        if (row >= P.M) continue;
-        const float r = rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps) * P.alpha;
+        const bool rv = row < P.M;
+        const float r = rv ? rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps) * P.alpha : 0.f;
+        float rsum = 0.f;  // this lane's share of the row-scale gradient (times r)
 #pragma unroll
         for (int j = 0; j < HF; ++j)
 #pragma unroll
           for (int q = 0; q < G4; ++q) {
             const int col = out0 + j * MI + q * (256 / MI) + 4 * lc;
             const int nv = P.N - col;
-            if (nv <= 0) continue;
+            if (!rv || nv <= 0) continue;
             uint32_t og[4], ou[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -1063,8 +1064,10 @@ struct GemmTile {
               const float g = r * acc[i][j][4 * q + s];
               const float u = r * acc[i][j + HF][4 * q + s];
               const float sg = 1.f / (1.f + __expf(-g));
-              og[s] = from_f32<DT>(d * u * sg * (1.f + g * (1.f - sg)) * r);
+              const float dsilu = sg * (1.f + g * (1.f - sg));
+              og[s] = from_f32<DT>(d * u * dsilu * r);
               ou[s] = from_f32<DT>(d * g * sg * r);
+              rsum += d * (dsilu * g * u + g * sg * u);
             }
             const int64_t off = (int64_t)row * P.ldc + col;
 #pragma unroll
@@ -1073,6 +1076,39 @@ struct GemmTile {
                 C[off + s] = (uint16_t)og[s];
                 C[off + P.N + s] = (uint16_t)ou[s];
               }
+          }
+        if (P.rms_grad_out) {
+          // lanes of one row in a fixed butterfly; the partial carries alpha/r so the
+          // partials of a row sum to the row-scale gradient
+#pragma unroll
+          for (int d = MI; d < 64; d <<= 1) rsum += __shfl_xor(rsum, d);
+          if (lc == 0 && rv)
+            P.ss_partial[(int64_t)(tn * CFG::WAVES_N + wn) * P.M + row] = rsum * P.alpha / r;
+        }
+      }
+    } else if constexpr (EPI == kEpiRmsBwd) {
+      // alpha*acc + c_i*X with c_i = -r_i^3 * grad_i / n (beta is 0)
+      const uint16_t* X = static_cast<const uint16_t*>(P.rms_x);
+#pragma unroll
+      for (int i = 0; i < CFG::FM; ++i) {
+        const int row = m0 + wm * CFG::WM + i * MI + lr;
+        if (row >= P.M) continue;
+        const float rr = rsqrtf(P.rms_ss[row] * P.rms_inv_n + P.rms_eps);
+        const float c = -rr * rr * rr * P.rms_grad[row] * P.rms_inv_n;
+#pragma unroll
+        for (int j = 0; j < CFG::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < G4; ++q) {
+            const int col = n0 + wn * CFG::WN + j * MI + q * (256 / MI) + 4 * lc;
+            const int nv = P.N - col;
+            if (nv <= 0) continue;
+            const int64_t off = (int64_t)row * P.ldc + col;
+            const int64_t xo = (int64_t)row * P.ldx + col;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              if (s < nv)
+                C[off + s] = (uint16_t)from_f32<DT>(P.alpha * acc[i][j][4 * q + s] +
+                                                    c * to_f32<DT>(X[xo + s]));
           }
       }
     } else {  // kEpiSwiGLU: output tile is BM x BN/2
@@ -1241,7 +1277,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
     if (EPI == kEpiStore32 && splits > 1)
       Cout = static_cast<float*>(P.C) + (int64_t)cur.y * P.M * P.ldc;
     // the SwiGLU backward writes both halves from registers
-    if constexpr (VEC && EPI != kEpiSwiGLUBwd)
+    if constexpr (VEC && EPI != kEpiSwiGLUBwd && EPI != kEpiRmsBwd)
       T::epilogue_rows(P, Cout, cur.m0, cur.n0, cur.tn, wave, wm, wn, lane, smem, acc);
     else
       T::epilogue(P, Cout, cur.m0, cur.n0, cur.tn, wm, wn, lane, smem, acc);

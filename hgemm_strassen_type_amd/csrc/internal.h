@@ -19,6 +19,7 @@ enum EpiKind : int {
   kEpiAct = 3,       // kEpiStore16 plus an activation before rounding
   kEpiRope = 4,      // kEpiStore16 plus the rotary position embedding before rounding
   kEpiSwiGLUBwd = 5, // 16-bit gradient of the SwiGLU epilogue's input (2N columns)
+  kEpiRmsBwd = 6,    // alpha*acc + c_i*X: the RMS scale's share of the input gradient
 };
 
 // Runtime epilogue switches inside kEpiStore16.
@@ -46,6 +47,12 @@ struct GemmProblem {
   double rope_log2_base;
   const void* dout;         // kEpiSwiGLUBwd: [M][ldd] incoming 16-bit gradient
   int64_t ldd;
+  // kEpiSwiGLUBwd: per-wave partials of the row-scale gradient (into ss_partial) when
+  // set; kEpiRmsBwd: the row-scale gradient [M] (input) and X [M][ldx]
+  int rms_grad_out;
+  const float* rms_grad;
+  const void* rms_x;
+  int64_t ldx;
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).

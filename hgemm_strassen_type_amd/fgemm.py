@@ -20,7 +20,7 @@ FGEMM_ERR_WORKSPACE, FGEMM_ERR_ALLOC, FGEMM_ERR_HIP = 3, 4, 5
 FGEMM_OP_N, FGEMM_OP_T = 0, 1
 FGEMM_F16, FGEMM_BF16 = 0, 1
 FGEMM_EPI_NONE, FGEMM_EPI_BIAS, FGEMM_EPI_ROWSUMSQ, FGEMM_EPI_RMS_SWIGLU = 0, 1, 2, 4
-FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD = 8, 16, 32
+FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD, FGEMM_EPI_RMS_BWD = 8, 16, 32, 64
 FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
 FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
@@ -45,7 +45,8 @@ class fgemm_epilogue_t(ctypes.Structure):
                 ("act", ctypes.c_int32), ("rope_positions", ctypes.c_void_p),
                 ("rope_offset", ctypes.c_int64), ("rope_head_dim", ctypes.c_int64),
                 ("rope_theta", ctypes.c_float), ("swiglu_dout", ctypes.c_void_p),
-                ("swiglu_ldd", ctypes.c_int64)]
+                ("swiglu_ldd", ctypes.c_int64), ("rms_grad", ctypes.c_void_p),
+                ("rms_x", ctypes.c_void_p), ("rms_ldx", ctypes.c_int64)]
 
 
 class fgemm_plan_t(ctypes.Structure):
@@ -146,10 +147,11 @@ def fgemm_set_model(handle: int, model: fgemm_model_t):
 
 def make_epilogue(flags=0, bias=0, rowsumsq=0, rms_rowsumsq=0, rms_n=0, rms_eps=0.0, act=0,
                   rope_positions=0, rope_offset=0, rope_head_dim=0, rope_theta=10000.0,
-                  swiglu_dout=0, swiglu_ldd=0):
+                  swiglu_dout=0, swiglu_ldd=0, rms_grad=0, rms_x=0, rms_ldx=0):
     return fgemm_epilogue_t(flags, bias or None, rowsumsq or None, rms_rowsumsq or None, rms_n,
                             rms_eps, act, rope_positions or None, rope_offset, rope_head_dim,
-                            rope_theta, swiglu_dout or None, swiglu_ldd)
+                            rope_theta, swiglu_dout or None, swiglu_ldd, rms_grad or None,
+                            rms_x or None, rms_ldx)
 
 
 def fgemm_select(handle, transA, transB, M, N, K, dtype, epilogue=None) -> fgemm_plan_t:

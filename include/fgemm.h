@@ -92,7 +92,15 @@ typedef enum { FGEMM_F16 = 0, FGEMM_BF16 = 1 } fgemm_dtype_t;
  *   op(A)op(B):
  *     C[i][j]     = RNE16(dO * u * silu'(g) * r_i * alpha)
  *     C[i][N + j] = RNE16(dO * silu(g) * r_i * alpha),
- *   silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)); beta must be 0. */
+ *   silu'(x) = s(x)(1 + x(1 - s(x))), s(x) = 1/(1+exp(-x)); beta must be 0.
+ *   With rms_grad != NULL it also writes the gradient with respect to each row's
+ *   scale: rms_grad[i] = sum_j dO (silu'(g) g u + silu(g) u) / r_i  (fp32, [M]).
+ * RMS_BWD (alone; the rest of the RMSNorm backward): with r_i = 1/sqrt(ss_i/n + eps)
+ *   from rms_rowsumsq, rms_n, rms_eps and the scale gradient rms_grad[i] (input),
+ *   C[i][j] = RNE16(alpha*acc + c_i * X[i][j]),  c_i = -r_i^3 * rms_grad[i] / n,
+ *   X = rms_x (device, M x N 16-bit, leading dimension rms_ldx), the normalised
+ *   layer's input; beta must be 0.  For the chain Y -> RMS scale -> Y W2 -> SwiGLU:
+ *   dH from SWIGLU_BWD, then dY = dH W2^T with RMS_BWD and X = Y. */
 enum {
     FGEMM_EPI_NONE = 0,
     FGEMM_EPI_BIAS = 1,
@@ -100,7 +108,8 @@ enum {
     FGEMM_EPI_RMS_SWIGLU = 4,
     FGEMM_EPI_ACT = 8,
     FGEMM_EPI_ROPE = 16,
-    FGEMM_EPI_SWIGLU_BWD = 32
+    FGEMM_EPI_SWIGLU_BWD = 32,
+    FGEMM_EPI_RMS_BWD = 64
 };
 typedef enum { FGEMM_ACT_RELU = 1, FGEMM_ACT_SILU = 2, FGEMM_ACT_GELU_TANH = 3 } fgemm_act_t;
 
@@ -118,6 +127,10 @@ typedef struct {
     float rope_theta;           /* ROPE: frequency base (> 0), e.g. 10000             */
     const void* swiglu_dout;    /* SWIGLU_BWD: device [M][swiglu_ldd] 16-bit gradient */
     int64_t swiglu_ldd;         /* SWIGLU_BWD: leading dimension of swiglu_dout (>= N) */
+    float* rms_grad;            /* SWIGLU_BWD: device [M] output, or NULL;
+                                   RMS_BWD: device [M] input                          */
+    const void* rms_x;          /* RMS_BWD: device [M][rms_ldx] 16-bit                */
+    int64_t rms_ldx;            /* RMS_BWD: leading dimension of rms_x (>= N)         */
 } fgemm_epilogue_t;
 
 typedef enum {

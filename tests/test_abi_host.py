@@ -147,6 +147,16 @@ def test_check_args_epilogues():
                      swiglu_dout=P, swiglu_ldd=64), ldc=128) == NOTSUP
     assert chk(epi=E(BWD | fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096,
                      swiglu_dout=P, swiglu_ldd=64), ldc=128) == NOTSUP
+    # RMS backward: alone, beta 0, the input X, the scale gradient and the statistics
+    RB = fgemm.FGEMM_EPI_RMS_BWD
+    rb = dict(rms_rowsumsq=P, rms_n=4096, rms_eps=1e-6, rms_grad=P, rms_x=P, rms_ldx=64)
+    assert chk(epi=E(RB, **rb)) == OK
+    assert chk(epi=E(RB, **rb), beta=1.0) == NOTSUP
+    assert chk(epi=E(RB | fgemm.FGEMM_EPI_BIAS, bias=P, **rb)) == NOTSUP
+    assert chk(epi=E(RB, **{**rb, "rms_x": 0})) == INVAL
+    assert chk(epi=E(RB, **{**rb, "rms_grad": 0})) == INVAL
+    assert chk(epi=E(RB, **{**rb, "rms_ldx": 32})) == INVAL
+    assert chk(epi=E(RB, **{**rb, "rms_n": 0})) == INVAL
 
 
 # ---------------------------------------------------------------- decision model

@@ -359,3 +359,65 @@ def test_swiglu_backward_llm_size():
     _, Q, _ = oracle.swiglu_bwd(Y, W2, dO, rms_ss=ss[rows].astype(np.float64), rms_n=4096,
                              rms_eps=1e-6, dtype=dtype, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+
+
+
+# ------------------------------------------------------------ RMSNorm backward
+def run_rmsnorm_backward(Y, W2, dO, ss, dtype, tile=None):
+    """SWIGLU_BWD with the row-scale gradient, then dY = dH W2^T + c_i Y (RMS_BWD)."""
+    import torch
+    M, H = Y.shape
+    F = dO.shape[1]
+    Yd, W2d, dOd = to_dev(Y, dtype), to_dev(W2, dtype), to_dev(dO, dtype)
+    ssd = torch.from_numpy(np.asarray(ss, dtype=np.float32)).cuda()
+    rg = dev_f32(M)
+    dH = empty_out(M, 2 * F, dtype)
+    e1 = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ssd.data_ptr(), rms_n=H,
+                             rms_eps=1e-6, swiglu_dout=dOd.data_ptr(), swiglu_ldd=F,
+                             rms_grad=rg.data_ptr())
+    plan = fgemm.classical_plan(*tile) if tile else None
+    handle().gemm(Yd, W2d, dH, epilogue=e1, plan=plan)
+    dY = empty_out(M, H, dtype)
+    e2 = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_BWD, rms_rowsumsq=ssd.data_ptr(), rms_n=H,
+                             rms_eps=1e-6, rms_grad=rg.data_ptr(), rms_x=Yd.data_ptr(), rms_ldx=H)
+    handle().gemm(dH, W2d, dY, transB=True, epilogue=e2, plan=plan if tile != (64, 64) else None)
+    torch.cuda.synchronize()
+    return from_dev(dH), rg.cpu().numpy().astype(np.float64), from_dev(dY)
+
+
+def check_rmsnorm_backward(Y, W2, dO, ss, dH, rg, dY, rows, dtype):
+    H = Y.shape[1]
+    _, Qh, rgr = oracle.swiglu_bwd(Y, W2, dO, rms_ss=ss[rows], rms_n=H, rms_eps=1e-6, dtype=dtype,
+                                   rows=rows)
+    assert rel_err(dH[rows], Qh, dtype) <= CLASSICAL_TOL
+    assert np.linalg.norm(rg[rows] - rgr) <= STATS_TOL * np.linalg.norm(rgr)
+    # dY against the oracle on the inputs it was given (the GPU's dH and scale gradient)
+    _, Qy = oracle.rms_bwd(dH, W2, Y, rms_ss=ss[rows], rgrad=rg[rows], rms_n=H, rms_eps=1e-6,
+                           transB=True, dtype=dtype, rows=rows)
+    assert rel_err(dY[rows], Qy, dtype) <= CLASSICAL_TOL
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("tile", TILES[:3])
+def test_rmsnorm_backward_ragged(dtype, tile):
+    M, H, F = 300, 264, 136
+    say(f"rmsnorm bwd dtype={dtype} tile={tile}")
+    Y = inputs.normal((M, H), 771, dtype)
+    W2 = inputs.normal((H, 2 * F), 772, dtype, std=0.1)
+    dO = inputs.normal((M, F), 773, dtype)
+    ss = np.sum(oracle.decode(Y, dtype) ** 2, axis=1)
+    dH, rg, dY = run_rmsnorm_backward(Y, W2, dO, ss, dtype, tile=tile)
+    check_rmsnorm_backward(Y, W2, dO, ss, dH, rg, dY, np.arange(M), dtype)
+
+
+def test_rmsnorm_backward_llm_size():
+    """The chain's backward at its configured size: Y [8192 x 4096], W2 [4096 x
+    2*11008] N(0,0.02), dO N(0,1); both GEMMs as the model picks; sampled rows."""
+    dtype, M, H, F = BF16, 8192, 4096, 11008
+    say("rmsnorm bwd 8192x4096 / 2x11008")
+    Y = inputs.normal((M, H), 4201, dtype)
+    W2 = inputs.normal((H, 2 * F), 4202, dtype, std=0.02)
+    dO = inputs.normal((M, F), 4203, dtype)
+    ss = np.sum(oracle.decode(Y, dtype) ** 2, axis=1)
+    dH, rg, dY = run_rmsnorm_backward(Y, W2, dO, ss, dtype)
+    check_rmsnorm_backward(Y, W2, dO, ss, dH, rg, dY, inputs.sample_rows(M, 16, 15), dtype)
