@@ -1057,10 +1057,19 @@ struct GemmTile {
             const int col = out0 + j * MI + q * (256 / MI) + 4 * lc;
             const int nv = P.N - col;
             if (!rv || nv <= 0) continue;
-            uint32_t og[4], ou[4];
+            uint32_t og[4], ou[4], dv[4];
+            const int64_t doff = (int64_t)row * P.ldd + col;
+            if (VEC && nv >= 4 && P.ldd % 4 == 0 &&
+                (reinterpret_cast<uintptr_t>(dO) & 7) == 0) {  // 8-byte aligned group of 4
+              const v2u w = *reinterpret_cast<const v2u*>(dO + doff);
+              dv[0] = w.x & 0xffff; dv[1] = w.x >> 16; dv[2] = w.y & 0xffff; dv[3] = w.y >> 16;
+            } else {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) dv[s] = s < nv ? dO[doff + s] : 0u;
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const float d = s < nv ? to_f32<DT>(dO[(int64_t)row * P.ldd + col + s]) : 0.f;
+              const float d = to_f32<DT>(dv[s]);
               const float g = r * acc[i][j][4 * q + s];
               const float u = r * acc[i][j + HF][4 * q + s];
               const float sg = 1.f / (1.f + __expf(-g));
@@ -1070,12 +1079,18 @@ struct GemmTile {
               rsum += d * (dsilu * g * u + g * sg * u);
             }
             const int64_t off = (int64_t)row * P.ldc + col;
+            if (VEC && nv >= 4 && P.N % 4 == 0) {
+              *reinterpret_cast<v2u*>(C + off) = v2u{og[0] | (og[1] << 16), og[2] | (og[3] << 16)};
+              *reinterpret_cast<v2u*>(C + off + P.N) =
+                  v2u{ou[0] | (ou[1] << 16), ou[2] | (ou[3] << 16)};
+            } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-              if (s < nv) {
-                C[off + s] = (uint16_t)og[s];
-                C[off + P.N + s] = (uint16_t)ou[s];
-              }
+              for (int s = 0; s < 4; ++s)
+                if (s < nv) {
+                  C[off + s] = (uint16_t)og[s];
+                  C[off + P.N + s] = (uint16_t)ou[s];
+                }
+            }
           }
         if (P.rms_grad_out) {
           // lanes of one row in a fixed butterfly; the partial carries alpha/r so the
@@ -1104,11 +1119,26 @@ struct GemmTile {
             if (nv <= 0) continue;
             const int64_t off = (int64_t)row * P.ldc + col;
             const int64_t xo = (int64_t)row * P.ldx + col;
+            uint32_t xv[4], o[4];
+            const bool v4 = VEC && nv >= 4 && P.ldx % 4 == 0 &&
+                            (reinterpret_cast<uintptr_t>(X) & 7) == 0;  // 8-byte aligned groups
+            if (v4) {
+              const v2u w = *reinterpret_cast<const v2u*>(X + xo);
+              xv[0] = w.x & 0xffff; xv[1] = w.x >> 16; xv[2] = w.y & 0xffff; xv[3] = w.y >> 16;
+            } else {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) xv[s] = s < nv ? X[xo + s] : 0u;
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-              if (s < nv)
-                C[off + s] = (uint16_t)from_f32<DT>(P.alpha * acc[i][j][4 * q + s] +
-                                                    c * to_f32<DT>(X[xo + s]));
+              o[s] = from_f32<DT>(P.alpha * acc[i][j][4 * q + s] + c * to_f32<DT>(xv[s]));
+            if (v4) {
+              *reinterpret_cast<v2u*>(C + off) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+            } else {
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                if (s < nv) C[off + s] = (uint16_t)o[s];
+            }
           }
       }
     } else {  // kEpiSwiGLU: output tile is BM x BN/2
