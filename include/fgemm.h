@@ -117,13 +117,15 @@ typedef struct {
     uint32_t flags;             /* FGEMM_EPI_* bits                                  */
     const void* bias;           /* BIAS: device [N], same 16-bit type as C           */
     float* rowsumsq;            /* ROWSUMSQ: device [M] fp32 output                  */
-    const float* rms_rowsumsq;  /* RMS_SWIGLU: device [M] fp32 input                 */
-    int64_t rms_n;              /* RMS_SWIGLU: width the statistics were taken over  */
-    float rms_eps;              /* RMS_SWIGLU: epsilon inside the square root        */
+    const float* rms_rowsumsq;  /* RMS_SWIGLU, SWIGLU_BWD, RMS_BWD: device [M] fp32
+                                   sums of squares of the normalised rows (input)    */
+    int64_t rms_n;              /* the same: width the statistics were taken over    */
+    float rms_eps;              /* the same: epsilon inside the square root          */
     int32_t act;                /* ACT: fgemm_act_t                                   */
     const int32_t* rope_positions; /* ROPE: device [M] positions, or NULL            */
     int64_t rope_offset;        /* ROPE: position of row 0 when rope_positions is NULL */
-    int64_t rope_head_dim;      /* ROPE: even, divides N                              */
+    int64_t rope_head_dim;      /* ROPE: divides N; a multiple of 8, at most 1024
+                                   (other even widths: FGEMM_ERR_NOT_SUPPORTED)     */
     float rope_theta;           /* ROPE: frequency base (> 0), e.g. 10000             */
     const void* swiglu_dout;    /* SWIGLU_BWD: device [M][swiglu_ldd] 16-bit gradient */
     int64_t swiglu_ldd;         /* SWIGLU_BWD: leading dimension of swiglu_dout (>= N) */
@@ -216,9 +218,10 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t t
  * library choose.  Strassen needs M, K and the column count of op(B) (N, or 2N
  * with RMS_SWIGLU) divisible by 8*2^depth and aligned operands, else
  * FGEMM_ERR_NOT_SUPPORTED; too small a caller workspace gives FGEMM_ERR_WORKSPACE.
- * On the Strassen path every epilogue runs in the top-level block post-add: with
- * RMS_SWIGLU the 2x2 split of op(B)'s 2N columns is exactly the gate/up boundary,
- * so gate and up of one output meet in the same post-add lane. */
+ * On the Strassen path the epilogues run in the top-level block post-add (all but
+ * SWIGLU_BWD and RMS_BWD, which are classical only): with RMS_SWIGLU the 2x2 split
+ * of op(B)'s 2N columns is exactly the gate/up boundary, so gate and up of one
+ * output meet in the same post-add lane. */
 fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
                                fgemm_op_t transA, fgemm_op_t transB, int64_t M, int64_t N,
                                int64_t K, float alpha, const void* A, int64_t lda,
