@@ -226,7 +226,11 @@ def current_stream() -> int:
 
 
 def _ld(t) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2:
+        raise ValueError("operands are 2-D row-major tensors (unit column stride)")
+    if t.numel() == 0:  # an empty operand (K = 0): any leading dimension >= its width
+        return max(t.shape[1], 1)
+    if t.stride(1) != 1 and t.shape[1] > 1:
         raise ValueError("operands are 2-D row-major tensors (unit column stride)")
     return t.stride(0)
 

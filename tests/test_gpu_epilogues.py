@@ -421,3 +421,53 @@ def test_rmsnorm_backward_llm_size():
     ss = np.sum(oracle.decode(Y, dtype) ** 2, axis=1)
     dH, rg, dY = run_rmsnorm_backward(Y, W2, dO, ss, dtype)
     check_rmsnorm_backward(Y, W2, dO, ss, dH, rg, dY, inputs.sample_rows(M, 16, 15), dtype)
+
+
+# ------------------------------------------------------------ degenerate shapes
+def test_new_epilogues_degenerate_shapes():
+    """K = 0 (the transforms act on beta*C + bias alone; the backward epilogues see
+    a zero product), a single row, and tiny ragged shapes with K tails."""
+    import torch
+    dtype = BF16
+    for (M, N, K) in [(5, 16, 0), (1, 24, 40), (3, 8, 3), (67, 40, 130)]:
+        say(f"degenerate M={M} N={N} K={K}")
+        A = inputs.normal((M, K), 781, dtype)
+        B = inputs.normal((K, N), 782, dtype, std=0.2)
+        C = inputs.normal((M, N), 783, dtype)
+        bias = inputs.normal((N,), 784, dtype)
+        bd = to_dev(bias[None, :], dtype)
+        # activation with bias and beta
+        _, Q, _ = oracle.gemm(A, B, beta=0.5, C=C, dtype=dtype, epi=oracle.EPI_ACT | oracle.EPI_BIAS,
+                              bias=bias, act=oracle.ACT_GELU_TANH)
+        got = run_transform(A, B, C, dtype, fgemm.make_epilogue(
+            fgemm.FGEMM_EPI_ACT | fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr(),
+            act=fgemm.FGEMM_ACT_GELU_TANH), beta=0.5)
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, (M, N, K)
+        # RoPE with head width 8 and an offset
+        _, Q, _ = oracle.gemm(A, B, beta=0.5, C=C, dtype=dtype, epi=oracle.EPI_ROPE,
+                              rope_pos=np.arange(M) + 3, rope_head_dim=8)
+        got = run_transform(A, B, C, dtype, fgemm.make_epilogue(
+            fgemm.FGEMM_EPI_ROPE, rope_offset=3, rope_head_dim=8), beta=0.5)
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, (M, N, K)
+        if N % 16:
+            continue
+        # SwiGLU backward with the row-scale gradient (op(B) is 2 * (N/2) wide)
+        F = N // 2
+        dO = inputs.normal((M, F), 785, dtype)
+        ss = np.random.default_rng(786).uniform(1, 3, M).astype(np.float32)
+        _, Qh, rgr = oracle.swiglu_bwd(A, B, dO, rms_ss=ss.astype(np.float64), rms_n=8,
+                                       rms_eps=1e-6, dtype=dtype)
+        Ad, Bd, dOd = to_dev(A, dtype), to_dev(B, dtype), to_dev(dO, dtype)
+        ssd = torch.from_numpy(ss).cuda()
+        rg = dev_f32(M)
+        dH = empty_out(M, N, dtype)
+        handle().gemm(Ad, Bd, dH, epilogue=fgemm.make_epilogue(
+            fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ssd.data_ptr(), rms_n=8, rms_eps=1e-6,
+            swiglu_dout=dOd.data_ptr(), swiglu_ldd=F, rms_grad=rg.data_ptr()))
+        torch.cuda.synchronize()
+        got = from_dev(dH)
+        if K == 0:
+            assert not np.any(oracle.decode(got, dtype)) and not np.any(rg.cpu().numpy())
+        else:
+            assert rel_err(got, Qh, dtype) <= CLASSICAL_TOL, (M, N, K)
+            assert np.linalg.norm(rg.cpu().numpy() - rgr) <= STATS_TOL * np.linalg.norm(rgr)
