@@ -156,6 +156,8 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       const int64_t ktiles = ceil_div(K, ti.bk);
       for (int sk = 2; sk <= 16 && tiles < md.compute_units; sk *= 2) {
         if (ktiles % sk || ktiles / sk < 4) continue;
+        const size_t ws = (size_t)sk * (size_t)M * (size_t)N * 4;
+        if ((double)ws > md.max_workspace_bytes || ws > ws_limit) continue;
         const double t = splitk_time_us(md, ti, M, N, K, sk, beta_hint);
         if (t < tc) {
           tc = t;
@@ -163,7 +165,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
           p.tile_m = ti.bm;
           p.tile_n = ti.bn;
           p.split_k = sk;
-          p.workspace_bytes = (size_t)sk * (size_t)M * (size_t)N * 4;
+          p.workspace_bytes = ws;
         }
       }
     }
@@ -230,6 +232,7 @@ fgemm_status_t ensure_workspace(fgemm_handle_t h, size_t bytes, void** ws) {
       h->own_ws_bytes = 0;
     }
     if (hipMalloc(&h->own_ws, bytes) != hipSuccess) {
+      (void)hipGetLastError();  // leave no error behind for the caller's next check
       h->own_ws = nullptr;
       return FGEMM_ERR_ALLOC;
     }
@@ -633,7 +636,7 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
   h->device = device;
   h->cus = prop.multiProcessorCount;
   double ghz = prop.clockRate > 0 ? prop.clockRate / 1e6 : 2.4;
-  model_defaults(&h->model, prop.multiProcessorCount, ghz);
+  model_defaults(&h->model, prop.multiProcessorCount, ghz, (double)prop.totalGlobalMem);
   *handle = h;
   return FGEMM_OK;
 }
@@ -740,8 +743,9 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_
   if (st != FGEMM_OK) return st;
   if (M == 0 || N == 0) return FGEMM_OK;
   const int vec = vec_ok(ta, tb, N, A, lda, B, ldb, C, ldc, epi);
-  PlanKey key{M, N, K, (int)ta, (int)tb, (int)dtype, (int)epi_flags(epi) | (beta != 0.f ? 8 : 0),
-              vec};
+  // beta != 0 sits above every epilogue flag bit
+  PlanKey key{M, N, K, (int)ta, (int)tb, (int)dtype,
+              (int)epi_flags(epi) | (beta != 0.f ? 1 << 30 : 0), vec};
   auto it = h->plans.find(key);
   fgemm_plan_t plan;
   if (it != h->plans.end()) {
@@ -754,7 +758,19 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_
   }
   Call c{ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, epi,
          static_cast<hipStream_t>(stream)};
-  return execute(h, plan, c);
+  st = execute(h, plan, c);
+  if (st == FGEMM_ERR_ALLOC && !h->user_ws && plan.workspace_bytes > 0) {
+    // the device could not hold the planned workspace (nothing was launched): plan
+    // again within what the handle holds now, which at worst is the classical path
+    fgemm_plan_t alt;
+    if (select_plan(h->model, M, N, K, dtype, epi_flags(epi), beta != 0.f, vec,
+                    h->own_ws_bytes, &alt) == FGEMM_OK &&
+        alt.workspace_bytes < plan.workspace_bytes) {
+      h->plans[key] = alt;
+      st = execute(h, alt, c);
+    }
+  }
+  return st;
 }
 
 }  // extern "C"

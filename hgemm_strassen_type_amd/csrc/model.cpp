@@ -52,7 +52,7 @@ const TileInfo kTiles[kNumTiles] = {
     {4, 64, 64, 64, 0.30, 2, 0, 1},
 };
 
-void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
+void model_defaults(fgemm_model_t* m, int cus, double clock_ghz, double device_bytes) {
   m->compute_units = cus;
   // dense 16-bit MFMA: 4 SIMDs x 1024 FLOP per clock per CU on gfx950
   m->peak_tflops = cus * 4096.0 * clock_ghz * 1e9 / 1e12;
@@ -63,7 +63,10 @@ void model_defaults(fgemm_model_t* m, int cus, double clock_ghz) {
   m->eta_mfma = 0.52;
   m->eta_hbm = 0.66;
   m->launch_us = 4.0;
-  m->max_workspace_bytes = 16.0 * (1ull << 30);
+  // a third of device memory (96 GB on a 288 GB MI355X): Strassen workspace grows as
+  // (M*K + K*N + M*N) * (2/4 + ...) bytes, and its crossover on this chip sits near
+  // 49152^3, whose two-level plan needs 42 GB (75 GB at 65536^3)
+  m->max_workspace_bytes = device_bytes > 0 ? device_bytes / 3.0 : 16.0 * (1ull << 30);
   m->max_rel_err = 5e-3;
 }
 

@@ -29,7 +29,7 @@ double overlap(double a, double b);
 // HBM bandwidth (bytes/s) that `blocks` concurrently streaming workgroups reach.
 double stream_bw(const fgemm_model_t& md, int64_t blocks);
 
-void model_defaults(fgemm_model_t* m, int cus, double clock_ghz);
+void model_defaults(fgemm_model_t* m, int cus, double clock_ghz, double device_bytes);
 
 double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
                          int64_t K, int64_t Nb, int64_t out_bn, int count, double in_bytes,

@@ -170,7 +170,8 @@ typedef struct {
     double eta_mfma;            /* fraction of MFMA peak a full tile wave reaches     */
     double eta_hbm;             /* fraction of HBM bandwidth streaming kernels reach  */
     double launch_us;           /* per-kernel launch and drain cost, microseconds     */
-    double max_workspace_bytes; /* AUTO never plans above this workspace              */
+    double max_workspace_bytes; /* AUTO never plans above this workspace (default a
+                                   third of the device's memory)                     */
     double max_rel_err;         /* AUTO never plans a path whose predicted normwise
                                    error ||C - RNE(D)||_F / ||RNE(D)||_F exceeds this
                                    (default 5e-3); see fgemm_plan_t.pred_rel_err     */
@@ -207,7 +208,11 @@ fgemm_status_t fgemm_select_model(const fgemm_model_t* model, fgemm_op_t transA,
                                   fgemm_plan_t* plan);
 
 /* C = alpha*op(A)*op(B) + beta*C with the epilogue (NULL = none), on the plan
- * fgemm_select picks. */
+ * fgemm_select picks.  Without a caller workspace, if hipMalloc cannot hold the
+ * workspace that plan needs, the call plans again within what the handle already
+ * holds (at worst the classical path) and keeps that plan for the shape;
+ * FGEMM_ERR_ALLOC only when even that fails.  Nothing is enqueued before the
+ * workspace is in hand. */
 fgemm_status_t fgemm_gemm(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
                           int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                           int64_t lda, const void* B, int64_t ldb, float beta, void* C,

@@ -471,3 +471,31 @@ def test_new_epilogues_degenerate_shapes():
         else:
             assert rel_err(got, Qh, dtype) <= CLASSICAL_TOL, (M, N, K)
             assert np.linalg.norm(rg.cpu().numpy() - rgr) <= STATS_TOL * np.linalg.norm(rgr)
+
+
+def test_plan_cache_keeps_beta_and_epilogue_apart():
+    """64 x 1024 x 16384 is a shape where the model splits K when there is no
+    epilogue.  A call with beta != 0 and no epilogue, then one with SiLU and beta = 0,
+    on one fresh handle: the second must get a plan of its own (the split-K path has
+    no activation), and both must match the oracle."""
+    import torch
+    M, N, K, dtype = 64, 1024, 16384, BF16
+    say(f"plan cache beta/epilogue {M}x{N}x{K}")
+    A = inputs.normal((M, K), 731, dtype)
+    B = inputs.normal((K, N), 732, dtype, std=0.02)
+    C = inputs.normal((M, N), 733, dtype)
+    _, Q1, _ = oracle.gemm(A, B, beta=0.5, C=C, dtype=dtype)
+    _, Q2, _ = oracle.gemm(A, B, dtype=dtype, epi=oracle.EPI_ACT, act=oracle.ACT_SILU)
+    h = fgemm.Handle(0)
+    try:
+        assert h.select(M, N, K).split_k > 1
+        Ad, Bd, Cd = to_dev(A, dtype), to_dev(B, dtype), to_dev(C, dtype)
+        h.gemm(Ad, Bd, Cd, beta=0.5)
+        Od = empty_out(M, N, dtype)
+        h.gemm(Ad, Bd, Od, epilogue=fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT,
+                                                          act=fgemm.FGEMM_ACT_SILU))
+        torch.cuda.synchronize()
+        assert rel_err(from_dev(Cd), Q1, dtype) <= CLASSICAL_TOL
+        assert rel_err(from_dev(Od), Q2, dtype) <= CLASSICAL_TOL
+    finally:
+        h.close()

@@ -327,3 +327,44 @@ def test_error_model_calibration(dtype, dist):
             pred = fgemm.fgemm_plan_rel_err(dtype, plan)
             err = rel_err(run(A, B, dtype, plan=plan)[rows], Q, dtype)
             assert 0.5 * pred <= err <= pred, (variant, depth, err, pred)
+
+
+# ------------------------------------------------------------ the model's own Strassen pick
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_default_model_picks_strassen_at_49152_cube(dtype):
+    """At 49152^3 (where Strassen measures 5-10 % faster than the classical kernel on
+    MI355X) the default model, whose workspace cap is a third of device memory, picks
+    a Strassen plan, and fgemm_gemm runs it: 24 sampled rows x 256 sampled columns of
+    the output against the oracle.  Inputs are U[-1,1] from torch's seeded device
+    generator (seed 4915), too large to draw on the host in a test."""
+    import torch
+    n = 49152
+    say(f"default-model strassen {n}^3 dtype={dtype}")
+    h = fgemm.Handle(0)
+    try:
+        total = torch.cuda.get_device_properties(0).total_memory
+        assert abs(h.model().max_workspace_bytes - total / 3) <= 1.0
+        pick = h.select(n, n, n, dtype=dtype)
+        assert pick.path == fgemm.FGEMM_PATH_STRASSEN, (pick.path, pick.depth)
+        assert pick.workspace_bytes <= total / 3
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4915)
+        td = torch.bfloat16 if dtype == BF16 else torch.float16
+        A = (torch.rand(n, n, device="cuda", generator=g) * 2 - 1).to(td)
+        B = (torch.rand(n, n, device="cuda", generator=g) * 2 - 1).to(td)
+        C = torch.full((n, n), float("nan"), device="cuda", dtype=td)
+        h.gemm(A, B, C)
+        torch.cuda.synchronize()
+        rows = inputs.sample_rows(n, 24, 21)
+        cols = inputs.sample_rows(n, 256, 22)
+        r, c = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+        A_s = from_dev(A.index_select(0, r))
+        B_s = from_dev(B.index_select(1, c))
+        got = from_dev(C.index_select(0, r).index_select(1, c))
+        del A, B, C
+        _, Q, _ = oracle.gemm(A_s, B_s, dtype=dtype)
+        err = rel_err(got, Q, dtype)
+        assert err <= pick.pred_rel_err <= STRASSEN_TOL, (err, pick.pred_rel_err)
+    finally:
+        h.close()
+        torch.cuda.empty_cache()
