@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--only-adds", action="store_true",
+                    help="time Winograd depth 1 at bf16 16384^3 only and print the add kernels' "
+                         "algorithmic bytes (for profiler runs of the add kernels)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (byte-counter calibration)")
     return ap.parse_args()
@@ -122,6 +125,19 @@ def main():
         gen.manual_seed(seed)
         return (torch.rand(shape, generator=gen, device=dev, dtype=torch.float32) * 2 - 1).to(dtype)
 
+    if args.copy_calib:
+        # a plain copy of known size: 1 GiB read and 1 GiB written per launch
+        src = torch.ones(512 * 1024 * 1024, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.only_adds:
+        print(json.dumps(adds_workload(torch, h, fgemm, timer, uniform, args)), flush=True)
+        return
+
     # ---------------------------------------------------------------- headline
     n = 8192
     A = normal((n, n), 2001)
@@ -143,15 +159,6 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic}
-
-    if args.copy_calib:
-        # a plain copy of known size: 1 GiB read and 1 GiB written per launch
-        src = torch.ones(512 * 1024 * 1024, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     workloads = {}
     if not args.only_main:
@@ -187,6 +194,30 @@ def main():
         "workloads": workloads,
     }
     print(json.dumps(out), flush=True)
+
+
+def adds_workload(torch, h, fgemm, timer, uniform, args):
+    """Winograd depth 1 on bf16 16384^3 (U[-1,1], beta 0): one step is one
+    fgemm_gemm call, which launches max|x| twice (A, B), the pre-add twice (A side,
+    B side), the batched sub-products once and the post-add once.  Algorithmic
+    bytes per launch with 8192^2 sub-blocks (m = k = n = 8192), 2-byte inputs and
+    outputs: pre-add 4*m*k*2 read + 7*m*k*2 written; post-add 7*m*n*4 read +
+    4*m*n*2 written; max|x| 2*M*K read."""
+    n = 16384
+    m = n // 2
+    A = uniform((n, n), 5001, torch.bfloat16)
+    B = uniform((n, n), 5002, torch.bfloat16)
+    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    plan = fgemm.strassen_plan(1, fgemm.FGEMM_VARIANT_WINOGRAD)
+    ms = timer.time(lambda: h.gemm(A, B, C, plan=plan), args.steps, args.warmup)
+    log(f"adds workload: Winograd d1 bf16 {n}^3, {ms:.4f} ms/step")
+    return {"workload": f"Winograd depth 1, bf16 {n}^3 NN, U[-1,1], beta 0",
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "effective_tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 2),
+            "launches_per_step": {"preadd_kernel": 2, "postadd_kernel": 1, "maxabs_kernel": 2},
+            "alg_bytes_per_launch": {"preadd_kernel": 4 * m * m * 2 + 7 * m * m * 2,
+                                     "postadd_kernel": 7 * m * m * 4 + 4 * m * m * 2,
+                                     "maxabs_kernel": 2 * n * n}}
 
 
 def run_workloads(torch, h, fgemm, timer, normal, uniform, args):

@@ -5,12 +5,19 @@
     python -m hgemm_strassen_type_amd.prof_summary traffic <fetch.csv> <write.csv> <out.json>
         "<kernel substring>" "<command>"
 
+    python -m hgemm_strassen_type_amd.prof_summary adds <kernel_trace.csv> <fetch.csv>
+        <write.csv> <bench stdout log> <out.md> "<commands>"
+
 `stats` keeps the per-kernel call count and average/min/max duration of a
 `--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
 `--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of the
 named kernel, each scaled by what the same counter reads for the 1 GiB device
 copy that `bench.py --copy-calib` runs in the same process (read 1 GiB, write
 1 GiB), and records the GEMM kernel sources' hash so a stale record is ignored.
+`adds` does the same for the Strassen add kernels of `bench.py --only-adds`: per
+kernel, the average duration of the timed dispatches, the algorithmic bytes that
+bench.py states, the GB/s they make against the 8 TB/s HBM peak, and the
+counters' bytes per launch next to the algorithmic ones.
 """
 from __future__ import annotations
 
@@ -105,6 +112,49 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, kernel: str, command:
         f"Total HBM bytes per launch: {rec['bytes_per_launch']:.4g}\n")
 
 
+def adds(trace_csv: str, fetch_csv: str, write_csv: str, bench_log: str, out_md: str,
+         command: str, peak_gbps: float = 8000.0) -> None:
+    info = None
+    for line in open(bench_log):
+        if line.startswith("{"):
+            info = json.loads(line)
+    if info is None:
+        raise SystemExit("no JSON line in " + bench_log)
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+
+    def mean_of(d, sub):
+        keys = [k for k in d if sub in k]
+        if not keys:
+            raise SystemExit(f"no kernel matching {sub!r}")
+        return statistics.mean(v for k in keys for v in d[k])
+
+    f_scale = GIB / (mean_of(fetch, "copyBuffer") * 1024.0)
+    w_scale = GIB / (mean_of(write, "copyBuffer") * 1024.0)
+    trace = list(csv.DictReader(open(trace_csv)))
+    lines = ["# HBM rate of the Strassen add kernels (rocprofv3)", "",
+             f"Workload: {info['workload']}; {info['steps']} timed steps after "
+             f"{info['warmup']} warmup ones, {info['ms_per_step']} ms per step "
+             f"({info['effective_tflops']} effective TFLOP/s).", "", "Commands:", "", "```",
+             command, "```", "",
+             "| kernel | timed launches | avg us | algorithmic bytes | GB/s | of 8 TB/s "
+             "| counter bytes/launch | counter / algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, alg in info["alg_bytes_per_launch"].items():
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in trace if k in r["Kernel_Name"]]
+        timed = d[info["warmup"] * info["launches_per_step"][k]:]
+        us = statistics.mean(timed)
+        gbps = alg / (us * 1e-6) / 1e9
+        hbm = mean_of(fetch, k) * 1024.0 * f_scale + mean_of(write, k) * 1024.0 * w_scale
+        lines.append(f"| `{k}` | {len(timed)} | {us:.2f} | {alg:.4g} | {gbps:.0f} | "
+                     f"{gbps / peak_gbps:.3f} | {hbm:.4g} | {hbm / alg:.3f} |")
+    lines += ["", f"Counter scale from the 1 GiB copy in the same process: FETCH_SIZE x{f_scale:.3f}, "
+                  f"WRITE_SIZE x{w_scale:.3f}. Both counter runs average over every dispatch of a "
+                  "kernel (the two pre-add launches move the same bytes on this square shape)."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         extra = sys.argv[5:]
@@ -112,5 +162,7 @@ if __name__ == "__main__":
               *([int(extra[2])] if len(extra) > 2 else []), *(extra[3:4]))
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+    elif sys.argv[1] == "adds":
+        adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7])
     else:
         raise SystemExit(__doc__)
