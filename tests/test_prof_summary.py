@@ -1,0 +1,85 @@
+"""Host logic of the rocprofv3 summarizer on small hand-made CSV files: durations
+of the timed dispatches, counter scaling by the 1 GiB copy, and the add kernels'
+GB/s against their algorithmic bytes."""
+import csv
+import json
+
+import pytest
+
+from hgemm_strassen_type_amd import prof_summary
+
+GIB = 1024 ** 3
+
+
+def write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def trace_rows(spec):
+    """spec: list of (kernel name, duration in ns); consecutive timestamps."""
+    rows, t = [], 1000
+    for name, ns in spec:
+        rows.append([name, t, t + ns])
+        t += ns + 100
+    return rows
+
+
+def counter_rows(counter, spec):
+    return [[name, counter, v] for name, v in spec]
+
+
+def test_adds_summary(tmp_path):
+    # 2 warmup steps + 2 timed steps; per step: two pre-adds, one post-add
+    spec = []
+    for step, (pre_ns, post_ns) in enumerate([(9e6, 9e6), (9e6, 9e6), (250e3, 500e3),
+                                             (270e3, 500e3)]):
+        spec += [("preadd_kernel(x)", int(pre_ns)), ("preadd_kernel(x)", int(pre_ns)),
+                 ("gemm_mfma_kernel<...>", 5000000), ("postadd_kernel(y)", int(post_ns))]
+    write_csv(tmp_path / "trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+              trace_rows(spec))
+    # the copy reads half its bytes per counted byte (scale 2) and writes 1:1
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    write_csv(tmp_path / "fetch.csv", hdr, counter_rows("FETCH_SIZE", [
+        ("__amd_rocclr_copyBuffer", GIB / 1024 / 2), ("preadd_kernel(x)", 200000.0),
+        ("preadd_kernel(x)", 200000.0), ("postadd_kernel(y)", 700000.0)]))
+    write_csv(tmp_path / "write.csv", hdr, counter_rows("WRITE_SIZE", [
+        ("__amd_rocclr_copyBuffer", GIB / 1024), ("preadd_kernel(x)", 100000.0),
+        ("preadd_kernel(x)", 100000.0), ("postadd_kernel(y)", 200000.0)]))
+    info = {"workload": "w", "steps": 2, "warmup": 2, "ms_per_step": 1.0,
+            "effective_tflops": 1.0, "launches_per_step": {"preadd_kernel": 2, "postadd_kernel": 1},
+            "alg_bytes_per_launch": {"preadd_kernel": 512000000, "postadd_kernel": 1638400000}}
+    (tmp_path / "bench.log").write_text("[bench] x\n" + json.dumps(info) + "\n")
+    out = tmp_path / "out.md"
+    prof_summary.adds(str(tmp_path / "trace.csv"), str(tmp_path / "fetch.csv"),
+                      str(tmp_path / "write.csv"), str(tmp_path / "bench.log"), str(out), "cmd")
+    rows = {line.split("|")[1].strip(): [c.strip() for c in line.split("|")[2:-1]]
+            for line in out.read_text().splitlines() if line.startswith("| `")}
+    pre, post = rows["`preadd_kernel`"], rows["`postadd_kernel`"]
+    # timed pre-adds: 250, 250, 270, 270 us -> 260 us; 512 MB / 260 us = 1969 GB/s
+    assert pre[0] == "4" and float(pre[1]) == pytest.approx(260.0)
+    assert float(pre[3]) == pytest.approx(512e6 / 260e-6 / 1e9, abs=1)
+    assert float(post[1]) == pytest.approx(500.0) and float(post[3]) == pytest.approx(3277, abs=1)
+    # counters: pre-add 2*200000 KiB read + 100000 KiB written = 500000 KiB
+    assert float(pre[5]) == pytest.approx(500000 * 1024, rel=1e-3)
+    assert float(post[5]) == pytest.approx(1600000 * 1024, rel=1e-3)
+    assert float(post[6]) == pytest.approx(1600000 * 1024 / 1638400000, abs=1e-3)
+
+
+def test_traffic_record(tmp_path):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    write_csv(tmp_path / "fetch.csv", hdr, counter_rows("FETCH_SIZE", [
+        ("__amd_rocclr_copyBuffer", GIB / 1024 / 2), ("gemm_mfma_kernel<A>", 1000.0),
+        ("gemm_mfma_kernel<A>", 3000.0)]))
+    write_csv(tmp_path / "write.csv", hdr, counter_rows("WRITE_SIZE", [
+        ("__amd_rocclr_copyBuffer", GIB / 1024), ("gemm_mfma_kernel<A>", 500.0)]))
+    out = tmp_path / "t.json"
+    prof_summary.traffic(str(tmp_path / "fetch.csv"), str(tmp_path / "write.csv"), str(out),
+                         "gemm_mfma_kernel", "cmd")
+    rec = json.loads(out.read_text())
+    assert rec["fetch_scale"] == pytest.approx(2.0)
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["bytes_per_launch"] == pytest.approx(2000 * 1024 * 2 + 500 * 1024)
+    assert len(rec["kernel_hash"]) == 16
