@@ -19,9 +19,10 @@ The same JSON line carries
                 decode shapes (decode as HBM GB/s), the projection with RoPE and the
                 FFN up projection with bias + GELU, the fused two-GEMM chain (also on
                 the Strassen path), and
-                Strassen/Winograd vs classical at 16384^3, 32768x8192x8192 and
-                49152^3 (past the crossover, where the model picks Strassen) with
-                the model's pick and its regret against the measured best.
+                Strassen/Winograd vs classical at 16384^3, 32768x8192x8192, 40960^3
+                and 49152^3 (around and past the crossover, where the model picks
+                Strassen) with the model's pick and its regret against the measured
+                best.
 """
 from __future__ import annotations
 
@@ -323,7 +324,8 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
 
     # Strassen / Winograd vs classical, and the model's pick
     S69, WIN = fgemm.FGEMM_VARIANT_S69, fgemm.FGEMM_VARIANT_WINOGRAD
-    for (M, N, K) in [(16384, 16384, 16384), (32768, 8192, 8192), (49152, 49152, 49152)]:
+    for (M, N, K) in [(16384, 16384, 16384), (32768, 8192, 8192), (40960, 40960, 40960),
+                      (49152, 49152, 49152)]:
         for dname, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
             A = uniform((M, K), 5001, dt)
             B = uniform((K, N), 5002, dt)

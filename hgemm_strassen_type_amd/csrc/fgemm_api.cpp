@@ -170,6 +170,11 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       }
     }
   }
+  {
+    // fp16 MFMA work runs at a lower clock (the launch cost does not scale)
+    const double launch = (p.split_k > 1 ? 2 : 1) * md.launch_us;
+    tc = launch + (tc - launch) / classical_dtype_rate(dtype);
+  }
   p.t_pred_us = tc;
   p.t_classical_pred_us = tc;
   p.pred_rel_err = predicted_rel_err(dtype, 0, 0);

@@ -85,6 +85,12 @@ double predicted_rel_err(int dtype, int variant, int depth) {
   return s69 ? (bf ? 1.64e-3 : 1.33e-3) : (bf ? 2.6e-3 : 2.26e-3);
 }
 
+// Rate of the classical kernel on fp16 inputs relative to bf16 ones: the chip holds a
+// lower clock on fp16 MFMA work under its power limit.  Measured fp16/bf16 time ratios
+// at 16384^3, 32768x8192x8192, 40960^3, 49152^3 and 65536^3 were 0.99-1.09, 1.03 on
+// average.
+double classical_dtype_rate(int dtype) { return dtype == FGEMM_F16 ? 0.97 : 1.0; }
+
 // Time of one classical launch of `count` same-shape problems on one tile config.
 double classical_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
                          int64_t K, int64_t Nb, int64_t out_bn, int count, double in_bytes,

@@ -44,6 +44,7 @@ double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant);
 // Predicted normwise error against the exactly rounded result (depth 0: classical).
 double predicted_rel_err(int dtype, int variant, int depth);
+double classical_dtype_rate(int dtype);
 double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
                         int variant, int beta, int* sub_tile);
 
