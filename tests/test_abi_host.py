@@ -314,3 +314,28 @@ def test_plan_rel_err_model():
             assert figs[dt, fgemm.FGEMM_VARIANT_WINOGRAD, d] > figs[dt, fgemm.FGEMM_VARIANT_S69, d]
     assert fgemm.fgemm_plan_rel_err(7, cl) < 0
     assert fgemm.fgemm_plan_rel_err(BF, fgemm.strassen_plan(3, 0)) < 0
+
+
+def test_select_crossover_with_calibrated_constants():
+    """The decision at the sizes where Strassen starts to win on MI355X, under the
+    constants a handle gets on that chip (eta_mfma 0.52, eta_hbm 0.66, workspace cap a
+    third of 288 GB): classical at and below 40960^3 for bf16 inputs, at 32768^3 for
+    fp16 ones (which run the classical kernel at a lower clock), two-level S69 from
+    49152^3 on; a 16 GiB cap keeps classical (the plans need 42 and 75 GB)."""
+    md = mi355x_model(eta_mfma=0.52, eta_hbm=0.66, max_workspace_bytes=288e9 / 3)
+    path = lambda n, dt, m=md: (lambda p: (p.path, p.depth, p.variant))(select(n, n, n, m, dtype=dt))
+    CL, S = fgemm.FGEMM_PATH_CLASSICAL, fgemm.FGEMM_PATH_STRASSEN
+    S69 = fgemm.FGEMM_VARIANT_S69
+    for n in (16384, 24576, 32768, 40960):
+        assert path(n, BF)[0] == CL, n
+    for n in (16384, 32768):
+        assert path(n, HF)[0] == CL, n
+    assert path(40960, HF) == (S, 1, S69)
+    for n in (49152, 65536):
+        for dt in (BF, HF):
+            assert path(n, dt) == (S, 2, S69), (n, dt)
+            p = select(n, n, n, md, dtype=dt)
+            assert p.workspace_bytes <= md.max_workspace_bytes
+            assert p.t_pred_us < p.t_classical_pred_us
+    small_cap = mi355x_model(eta_mfma=0.52, eta_hbm=0.66)
+    assert path(65536, BF, small_cap)[0] == CL
