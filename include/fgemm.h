@@ -185,7 +185,10 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device);
 fgemm_status_t fgemm_destroy(fgemm_handle_t handle);
 
 /* Caller-owned device workspace (for example a torch tensor).  Without one the
- * handle allocates what a plan needs with hipMalloc and keeps it until destroyed. */
+ * handle allocates what a plan needs with hipMalloc and keeps it until destroyed:
+ * for automatic plans up to model.max_workspace_bytes (by default a third of the
+ * device's memory; Strassen at 49152^3 takes 42 GB).  With one, automatic plans
+ * stay within its size and NULL (bytes 0) returns to the handle's own. */
 fgemm_status_t fgemm_set_workspace(fgemm_handle_t handle, void* dptr, size_t bytes);
 
 fgemm_status_t fgemm_get_model(fgemm_handle_t handle, fgemm_model_t* model);
