@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--only-adds", action="store_true",
                     help="time Winograd depth 1 at bf16 16384^3 only and print the add kernels' "
                          "algorithmic bytes (for profiler runs of the add kernels)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time the 16x14336x4096 decode shape only and print its kernel's "
+                         "algorithmic bytes (for profiler runs of the decode kernel)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (byte-counter calibration)")
     return ap.parse_args()
@@ -137,6 +140,9 @@ def main():
 
     if args.only_adds:
         print(json.dumps(adds_workload(torch, h, fgemm, timer, uniform, args)), flush=True)
+        return
+    if args.only_decode:
+        print(json.dumps(decode_workload(torch, h, fgemm, timer, normal, args)), flush=True)
         return
 
     # ---------------------------------------------------------------- headline
@@ -219,6 +225,25 @@ def adds_workload(torch, h, fgemm, timer, uniform, args):
             "alg_bytes_per_launch": {"preadd_kernel": 4 * m * m * 2 + 7 * m * m * 2,
                                      "postadd_kernel": 7 * m * m * 4 + 4 * m * m * 2,
                                      "maxabs_kernel": 2 * n * n}}
+
+
+def decode_workload(torch, h, fgemm, timer, normal, args):
+    """bf16 decode shape M = 16, N = 14336, K = 4096 (activations N(0,1), weights
+    N(0,0.02), beta 0), one fgemm_gemm call per step on the model's plan (the 64x64
+    tile, one launch).  Algorithmic bytes per launch: 2*(K*N + M*K + M*N)."""
+    M, N, K = 16, 14336, 4096
+    A = normal((M, K), 3001)
+    B = normal((K, N), 3002, 0.02)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    plan = h.select(M, N, K)
+    ms = timer.time(lambda: h.gemm(A, B, C), args.steps, args.warmup)
+    log(f"decode workload: bf16 {M}x{N}x{K}, plan {plan.as_dict()}, {ms * 1e3:.2f} us/step")
+    name = f"TileCfg<{plan.tile_m}, {plan.tile_n},"
+    return {"workload": f"bf16 decode {M}x{N}x{K} NN, A N(0,1), B N(0,0.02), beta 0",
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "effective_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
+            "launches_per_step": {name: 1},
+            "alg_bytes_per_launch": {name: 2 * (K * N + M * K + M * N)}}
 
 
 def run_workloads(torch, h, fgemm, timer, normal, uniform, args):

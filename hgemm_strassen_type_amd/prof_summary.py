@@ -14,7 +14,8 @@
 named kernel, each scaled by what the same counter reads for the 1 GiB device
 copy that `bench.py --copy-calib` runs in the same process (read 1 GiB, write
 1 GiB), and records the GEMM kernel sources' hash so a stale record is ignored.
-`adds` does the same for the Strassen add kernels of `bench.py --only-adds`: per
+`adds` does the same for the Strassen add kernels of `bench.py --only-adds` (and
+for the decode kernel of `bench.py --only-decode`, whose JSON line has the same keys): per
 kernel, the average duration of the timed dispatches, the algorithmic bytes that
 bench.py states, the GB/s they make against the 8 TB/s HBM peak, and the
 counters' bytes per launch next to the algorithmic ones.
@@ -113,7 +114,8 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, kernel: str, command:
 
 
 def adds(trace_csv: str, fetch_csv: str, write_csv: str, bench_log: str, out_md: str,
-         command: str, peak_gbps: float = 8000.0) -> None:
+         command: str, peak_gbps: float = 8000.0,
+         title: str = "the Strassen add kernels") -> None:
     info = None
     for line in open(bench_log):
         if line.startswith("{"):
@@ -132,7 +134,7 @@ def adds(trace_csv: str, fetch_csv: str, write_csv: str, bench_log: str, out_md:
     f_scale = GIB / (mean_of(fetch, "copyBuffer") * 1024.0)
     w_scale = GIB / (mean_of(write, "copyBuffer") * 1024.0)
     trace = list(csv.DictReader(open(trace_csv)))
-    lines = ["# HBM rate of the Strassen add kernels (rocprofv3)", "",
+    lines = [f"# HBM rate of {title} (rocprofv3)", "",
              f"Workload: {info['workload']}; {info['steps']} timed steps after "
              f"{info['warmup']} warmup ones, {info['ms_per_step']} ms per step "
              f"({info['effective_tflops']} effective TFLOP/s).", "", "Commands:", "", "```",
@@ -147,11 +149,21 @@ def adds(trace_csv: str, fetch_csv: str, write_csv: str, bench_log: str, out_md:
         us = statistics.mean(timed)
         gbps = alg / (us * 1e-6) / 1e9
         hbm = mean_of(fetch, k) * 1024.0 * f_scale + mean_of(write, k) * 1024.0 * w_scale
-        lines.append(f"| `{k}` | {len(timed)} | {us:.2f} | {alg:.4g} | {gbps:.0f} | "
+        lines.append(f"| `{k.rstrip(',')}` | {len(timed)} | {us:.2f} | {alg:.4g} | {gbps:.0f} | "
                      f"{gbps / peak_gbps:.3f} | {hbm:.4g} | {hbm / alg:.3f} |")
     lines += ["", f"Counter scale from the 1 GiB copy in the same process: FETCH_SIZE x{f_scale:.3f}, "
                   f"WRITE_SIZE x{w_scale:.3f}. Both counter runs average over every dispatch of a "
-                  "kernel (the two pre-add launches move the same bytes on this square shape)."]
+                  "kernel" + (" (the two pre-add launches move the same bytes on this square shape)."
+                              if "preadd_kernel" in info["alg_bytes_per_launch"] else ".")]
+    # the copy's own rate in the counter runs (2 GiB moved per launch), where timed
+    copy_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+               for path in (fetch_csv, write_csv) for r in csv.DictReader(open(path))
+               if "copyBuffer" in r["Kernel_Name"] and r.get("Start_Timestamp")]
+    if copy_us:
+        rates = [2 * GIB / (u * 1e-6) / 1e12 for u in copy_us]
+        lines += ["", f"For comparison, the runtime's 1 GiB device copy (2 GiB moved per launch) in "
+                      f"the same counter runs: {min(copy_us):.0f}-{max(copy_us):.0f} us, "
+                      f"{min(rates):.1f}-{max(rates):.1f} TB/s."]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -163,6 +175,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
     elif sys.argv[1] == "adds":
-        adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7])
+        adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
+             title=sys.argv[8] if len(sys.argv) > 8 else "the Strassen add kernels")
     else:
         raise SystemExit(__doc__)
