@@ -63,6 +63,30 @@ def test_random_with_beta_and_bias(dtype, variant, depth):
     assert rel_err(from_dev(Cd), Q, dtype) <= STRASSEN_TOL
 
 
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("variant", [S69, WIN])
+@pytest.mark.parametrize("depth", [1, 2])
+@pytest.mark.parametrize("transA,transB", LAYOUTS[1:])
+def test_transposed_layouts_with_beta_bias_and_padding(dtype, variant, depth, transA, transB):
+    """The transposed operand views (NT, TN, TT) on random inputs with alpha, beta*C and
+    bias, every operand with a leading dimension 8 wider than its rows."""
+    import torch
+    M, N, K = 384, 512, 640
+    say(f"strassen layouts tA={transA} tB={transB} d={depth} v={variant} dtype={dtype}")
+    A, B = operands(M, N, K, transA, transB, 210, dtype, "uniform")
+    C = inputs.normal((M, N), 212, dtype)
+    bias = inputs.normal((N,), 213, dtype)
+    _, Q, _ = oracle.gemm(A, B, transA=transA, transB=transB, alpha=0.75, beta=-0.5, C=C,
+                          dtype=dtype, epi=oracle.EPI_BIAS, bias=bias)
+    Ad, Bd, Cd = to_dev(A, dtype, 8), to_dev(B, dtype, 8), to_dev(C, dtype, 8)
+    bd = to_dev(bias[None, :], dtype)
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr())
+    handle().gemm(Ad, Bd, Cd, transA=transA, transB=transB, alpha=0.75, beta=-0.5, epilogue=epi,
+                  plan=fgemm.strassen_plan(depth, variant))
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= STRASSEN_TOL
+
+
 def test_large_magnitudes_are_scaled_into_fp16():
     # bf16 values far outside the fp16 range: the power-of-two scale keeps the
     # fp16 temporaries finite and is divided out again
