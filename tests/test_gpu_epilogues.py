@@ -499,3 +499,90 @@ def test_plan_cache_keeps_beta_and_epilogue_apart():
         assert rel_err(from_dev(Od), Q2, dtype) <= CLASSICAL_TOL
     finally:
         h.close()
+
+
+# ------------------------------------------------------------ A stored K x M (transA)
+EPI_KINDS = ["bias_rowsumsq", "act", "rope", "rms_swiglu", "swiglu_bwd", "rms_bwd"]
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+@pytest.mark.parametrize("tile", [(256, 256), (64, 128)])
+@pytest.mark.parametrize("transB", [False, True])
+@pytest.mark.parametrize("kind", EPI_KINDS)
+def test_every_epilogue_with_transposed_a(dtype, tile, transB, kind):
+    """Each epilogue kind with A stored K x M (the transposed-A load path has its own
+    kernel instances), ragged M, against the oracle: output within 1e-3, row
+    statistics and the row-scale gradient within 1e-3."""
+    import torch
+    M, K, N = 264, 192, 256  # N: output width (gate|up take 2N columns of op(B))
+    say(f"transA epilogue {kind} dtype={dtype} tile={tile} tB={transB}")
+    At = inputs.normal((K, M), 781, dtype)
+    two = kind in ("rms_swiglu", "swiglu_bwd")
+    W = inputs.normal((K, 2 * N if two else N), 782, dtype, std=0.1)
+    Wst = np.ascontiguousarray(W.T) if transB else W
+    Ad, Wd = to_dev(At, dtype), to_dev(Wst, dtype)
+    plan = fgemm.classical_plan(*tile)
+    ss = (np.random.default_rng(783).uniform(0.5, 2.0, M) * 4096).astype(np.float32)
+    ssd = torch.from_numpy(ss).cuda()
+    common = dict(transA=True, transB=transB, dtype=dtype)
+    if kind == "swiglu_bwd":
+        dO = inputs.normal((M, N), 784, dtype)
+        dOd = to_dev(dO, dtype)
+        rg = dev_f32(M)
+        Cd = empty_out(M, 2 * N, dtype)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ssd.data_ptr(),
+                                  rms_n=4096, rms_eps=1e-6, swiglu_dout=dOd.data_ptr(),
+                                  swiglu_ldd=N, rms_grad=rg.data_ptr())
+        handle().gemm(Ad, Wd, Cd, transA=True, transB=transB, alpha=1.5, epilogue=epi, plan=plan)
+        torch.cuda.synchronize()
+        _, Q, rgr = oracle.swiglu_bwd(At, Wst, dO, rms_ss=ss.astype(np.float64), rms_n=4096,
+                                      alpha=1.5, **common)
+        assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+        got = rg.cpu().numpy().astype(np.float64)
+        assert np.linalg.norm(got - rgr) <= STATS_TOL * np.linalg.norm(rgr)
+        return
+    if kind == "rms_bwd":
+        X = inputs.normal((M, N), 785, dtype)
+        rgrad = np.random.default_rng(786).normal(size=M).astype(np.float32)
+        Xd, rgd = to_dev(X, dtype), torch.from_numpy(rgrad).cuda()
+        Cd = empty_out(M, N, dtype)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_BWD, rms_rowsumsq=ssd.data_ptr(), rms_n=4096,
+                                  rms_eps=1e-6, rms_grad=rgd.data_ptr(), rms_x=Xd.data_ptr(),
+                                  rms_ldx=N)
+        handle().gemm(Ad, Wd, Cd, transA=True, transB=transB, alpha=0.75, epilogue=epi, plan=plan)
+        torch.cuda.synchronize()
+        _, Q = oracle.rms_bwd(At, Wst, X, rms_ss=ss.astype(np.float64),
+                              rgrad=rgrad.astype(np.float64), rms_n=4096, alpha=0.75, **common)
+        assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+        return
+    C = inputs.normal((M, N), 787, dtype)
+    bias = inputs.normal((N,), 788, dtype)
+    Cd, bd = to_dev(C, dtype), to_dev(bias[None, :], dtype)
+    ssout = dev_f32(M)
+    pos = np.random.default_rng(789).integers(0, 4096, size=M).astype(np.int32)
+    posd = torch.from_numpy(pos).cuda()
+    if kind == "bias_rowsumsq":
+        flags, oflags, extra = (fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ,
+                                oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ, {})
+        epi = fgemm.make_epilogue(flags, bias=bd.data_ptr(), rowsumsq=ssout.data_ptr())
+    elif kind == "act":
+        oflags, extra = oracle.EPI_BIAS | oracle.EPI_ACT, dict(act=oracle.ACT_GELU_TANH)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ACT, bias=bd.data_ptr(),
+                                  act=fgemm.FGEMM_ACT_GELU_TANH)
+    elif kind == "rope":
+        oflags, extra = oracle.EPI_ROPE, dict(rope_pos=pos, rope_head_dim=64)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROPE, rope_positions=posd.data_ptr(),
+                                  rope_head_dim=64, rope_theta=10000.0)
+    else:  # rms_swiglu
+        oflags, extra = oracle.EPI_RMS_SWIGLU, dict(rms_ss=ss.astype(np.float64), rms_n=4096)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ssd.data_ptr(),
+                                  rms_n=4096, rms_eps=1e-6)
+    _, Q, ssr = oracle.gemm(At, Wst, alpha=1.25, beta=0.5, C=C, epi=oflags,
+                            bias=bias if oflags & oracle.EPI_BIAS else None, **extra, **common)
+    handle().gemm(Ad, Wd, Cd, transA=True, transB=transB, alpha=1.25, beta=0.5, epilogue=epi,
+                  plan=plan)
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(Cd), Q, dtype) <= CLASSICAL_TOL
+    if kind == "bias_rowsumsq":
+        got = ssout.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got - ssr) / ssr) <= STATS_TOL
