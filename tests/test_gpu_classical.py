@@ -189,6 +189,27 @@ def test_split_k_exact_and_random(tile, split, dtype):
     assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
 
 
+@pytest.mark.parametrize("tile", [(64, 64), (32, 128), (256, 256)])
+@pytest.mark.parametrize("transB", [False, True])
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_split_k_transposed_a_with_bias_and_beta(tile, transB, dtype):
+    """Split K with A stored K x M: alpha, beta*C and bias applied once, in the
+    finalize pass, after the fp32 slices are summed."""
+    M, N, K = 40, 264, 512
+    say(f"split-K transA tile={tile} tB={transB} dtype={dtype}")
+    A, B = stored(M, N, K, True, transB, 0, 95, 96, dtype, kind="normal")
+    C = inputs.normal((M, N), 97, dtype)
+    bias = inputs.normal((N,), 98, dtype)
+    _, Q, _ = oracle.gemm(A, B, transA=True, transB=transB, alpha=1.5, beta=0.25, C=C,
+                          dtype=dtype, epi=oracle.EPI_BIAS, bias=bias)
+    bd = to_dev(bias[None, :], dtype)
+    for split in (2, 4):
+        got = run(A, B, dtype, transA=True, transB=transB, alpha=1.5, beta=0.25, C_bits=C,
+                  plan=fgemm.classical_plan(*tile, split_k=split),
+                  epilogue=fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS, bias=bd.data_ptr()))
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL, split
+
+
 def test_split_k_refusals():
     import torch
     dtype = BF16
