@@ -215,7 +215,9 @@ fgemm_status_t fgemm_select_model(const fgemm_model_t* model, fgemm_op_t transA,
  * workspace that plan needs, the call plans again within what the handle already
  * holds (at worst the classical path) and keeps that plan for the shape;
  * FGEMM_ERR_ALLOC only when even that fails.  Nothing is enqueued before the
- * workspace is in hand. */
+ * workspace is in hand.  Once a call of the same shape has sized the workspace, a
+ * call only enqueues kernels (no allocation, memset or synchronisation), so it can
+ * be captured into a HIP graph. */
 fgemm_status_t fgemm_gemm(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
                           int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                           int64_t lda, const void* B, int64_t ldb, float beta, void* C,
