@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_bf16_8192_traffic.json")
+WARM_MS = 30.0              # least untimed load before each secondary workload is timed
 KERNEL_SOURCES = ["hgemm_strassen_type_amd/csrc/gemm_mfma.h",
                   "hgemm_strassen_type_amd/csrc/gemm_inst.hip"]
 
@@ -61,7 +62,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only-main", action="store_true",
                     help="time the headline workload only (for profiler runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -88,11 +89,19 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def time(self, fn, steps, warmup):
+    def time(self, fn, steps, warmup, min_warm_ms=0.0):
+        """Mean ms per call of `steps` calls after `warmup` untimed ones; with
+        min_warm_ms, untimed calls continue until that much wall time has passed
+        (the chip needs some milliseconds of load to reach its working clock after
+        lighter work: the first calls of a case ran up to 25 % slow)."""
         torch = self.torch
+        t0 = time.perf_counter()
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        while (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+            fn()
+            torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -257,7 +266,7 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
         B = gen_fn((K, N), seeds[1], std_b)
         C = gen_fn((M, N), seeds[2], 1.0)
         ms = timer.time(lambda: h.gemm(A, B, C, transA=transA, beta=beta, plan=plan,
-                                       epilogue=epilogue), reps, 3)
+                                       epilogue=epilogue), reps, 3, WARM_MS)
         r = {"ms": round(ms, 5), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
         if bytes_alg:
             r["hbm_gbps"] = round(bytes_alg / (ms * 1e-3) / 1e9, 1)
@@ -305,8 +314,8 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     e1 = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ss.data_ptr())
     e2 = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
                              rms_eps=1e-6)
-    t1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1), reps, 3)
-    t2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2), reps, 3)
+    t1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1), reps, 3, WARM_MS)
+    t2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2), reps, 3, WARM_MS)
     f1, f2 = 2.0 * Mc * Hc * Hc, 2.0 * Mc * Hc * 2 * Fc
     W["fused_chain_8192x4096_ffn11008"] = {
         "gemm1_rowsumsq_ms": round(t1, 5), "gemm2_rms_swiglu_ms": round(t2, 5),
@@ -319,8 +328,8 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     chain_sk = {}
     for depth in (1, 2):
         plan = fgemm.strassen_plan(depth, fgemm.FGEMM_VARIANT_WINOGRAD)
-        s1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1, plan=plan), reps, 2)
-        s2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2, plan=plan), reps, 2)
+        s1 = timer.time(lambda: h.gemm(X, Wt, Y, epilogue=e1, plan=plan), reps, 2, WARM_MS)
+        s2 = timer.time(lambda: h.gemm(Y, W2, O, epilogue=e2, plan=plan), reps, 2, WARM_MS)
         chain_sk[f"winograd_d{depth}"] = {
             "gemm1_rowsumsq_ms": round(s1, 5), "gemm2_rms_swiglu_ms": round(s2, 5),
             "chain_effective_tflops": round((f1 + f2) / ((s1 + s2) * 1e-3) / 1e12, 2)}
@@ -333,12 +342,12 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     eb = fgemm.make_epilogue(fgemm.FGEMM_EPI_SWIGLU_BWD, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
                              rms_eps=1e-6, swiglu_dout=dO.data_ptr(), swiglu_ldd=Fc,
                              rms_grad=rg.data_ptr())
-    tb = timer.time(lambda: h.gemm(Y, W2, dH, epilogue=eb), reps, 2)
+    tb = timer.time(lambda: h.gemm(Y, W2, dH, epilogue=eb), reps, 2, WARM_MS)
     # then dY = dH W2^T plus the RMS scale's share (the RMSNorm backward)
     dY = torch.empty((Mc, Hc), dtype=torch.bfloat16, device="cuda")
     er = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_BWD, rms_rowsumsq=ss.data_ptr(), rms_n=Hc,
                              rms_eps=1e-6, rms_grad=rg.data_ptr(), rms_x=Y.data_ptr(), rms_ldx=Hc)
-    tr = timer.time(lambda: h.gemm(dH, W2, dY, transB=True, epilogue=er), reps, 2)
+    tr = timer.time(lambda: h.gemm(dH, W2, dY, transB=True, epilogue=er), reps, 2, WARM_MS)
     W["fused_chain_8192x4096_ffn11008"]["backward"] = {
         "gemm2_swiglu_backward_ms": round(tb, 5), "gemm2_swiglu_backward_tflops":
         round(f2 / (tb * 1e-3) / 1e12, 2), "dY_rms_backward_ms": round(tr, 5),
@@ -362,7 +371,7 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
                 cands[f"winograd_d{d}"] = fgemm.strassen_plan(d, WIN)
             r2 = max(3, reps // 3)
             for name, pl in cands.items():
-                ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), r2, 1)
+                ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), r2, 1, WARM_MS)
                 res[name] = {"ms": round(ms, 4),
                              "effective_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
             code = fgemm.FGEMM_BF16 if dt == torch.bfloat16 else fgemm.FGEMM_F16
