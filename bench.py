@@ -22,7 +22,7 @@ The same JSON line carries
                 Strassen/Winograd vs classical at 16384^3, 32768x8192x8192, 40960^3
                 and 49152^3 (around and past the crossover, where the model picks
                 Strassen) with the model's pick and its regret against the measured
-                best.
+                best, and 49152^3 again with padded leading dimensions.
 """
 from __future__ import annotations
 
@@ -388,6 +388,27 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
             log(f"{key}: {res}")
             del A, B, C
             torch.cuda.empty_cache()
+    # the same 49152^3 comparison with every leading dimension 64 elements wider: rows
+    # 96 KB apart cost the classical kernel ~11 %, padded rows do not
+    n, pad = 49152, 64
+    for dname, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        A = uniform((n, n + pad), 5001, dt)[:, :n]
+        B = uniform((n, n + pad), 5002, dt)[:, :n]
+        C = torch.empty((n, n + pad), dtype=dt, device="cuda")[:, :n]
+        code = fgemm.FGEMM_BF16 if dt == torch.bfloat16 else fgemm.FGEMM_F16
+        pick = h.select(n, n, n, dtype=code)
+        res = {}
+        for name, pl in (("classical", fgemm.classical_plan()), ("model_pick", None)):
+            ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), 3, 1, WARM_MS)
+            res[name] = {"ms": round(ms, 4),
+                         "effective_tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 2)}
+        res["model_pick_plan"] = "classical" if pick.path == 0 else \
+            f"{'winograd' if pick.variant == WIN else 's69'}_d{pick.depth}"
+        key = f"strassen_{dname}_{n}x{n}x{n}_ld+{pad}"
+        W[key] = res
+        log(f"{key}: {res}")
+        del A, B, C
+        torch.cuda.empty_cache()
     return W
 
 
