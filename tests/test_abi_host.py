@@ -339,3 +339,18 @@ def test_select_crossover_with_calibrated_constants():
             assert p.t_pred_us < p.t_classical_pred_us
     small_cap = mi355x_model(eta_mfma=0.52, eta_hbm=0.66)
     assert path(65536, BF, small_cap)[0] == CL
+
+
+def test_split_k_respects_the_workspace_cap():
+    """Split K needs slices*M*N*4 bytes of fp32 partials: a skinny shape that splits
+    under the default cap stays unsplit when the cap is below the smallest split's
+    need, and splits less when the cap admits only two slices."""
+    md = mi355x_model(eta_mfma=0.52, eta_hbm=0.66)
+    M, N, K = 64, 1024, 16384
+    p = select(M, N, K, md)
+    assert p.split_k > 2 and p.workspace_bytes == p.split_k * M * N * 4
+    tight = mi355x_model(eta_mfma=0.52, eta_hbm=0.66, max_workspace_bytes=2 * M * N * 4 - 1)
+    assert select(M, N, K, tight).split_k == 1
+    two = mi355x_model(eta_mfma=0.52, eta_hbm=0.66, max_workspace_bytes=2 * M * N * 4)
+    q = select(M, N, K, two)
+    assert q.split_k == 2 and q.workspace_bytes <= two.max_workspace_bytes
