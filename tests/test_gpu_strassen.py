@@ -354,15 +354,14 @@ def test_error_model_calibration(dtype, dist):
 
 
 # ------------------------------------------------------------ the model's own Strassen pick
-@pytest.mark.parametrize("dtype", [BF16, F16])
-def test_default_model_picks_strassen_at_49152_cube(dtype):
-    """At 49152^3 (where Strassen measures 5-10 % faster than the classical kernel on
-    MI355X) the default model, whose workspace cap is a third of device memory, picks
-    a Strassen plan, and fgemm_gemm runs it: 24 sampled rows x 256 sampled columns of
-    the output against the oracle.  Inputs are U[-1,1] from torch's seeded device
-    generator (seed 4915), too large to draw on the host in a test."""
+@pytest.mark.parametrize("dtype,n", [(BF16, 49152), (F16, 49152), (BF16, 65536)])
+def test_default_model_picks_strassen_at_large_cubes(dtype, n):
+    """At 49152^3 and 65536^3 (2^32 elements per operand, 75 GB of workspace) the
+    default model, whose workspace cap is a third of device memory, picks a Strassen
+    plan, and fgemm_gemm runs it: 24 sampled rows x 256 sampled columns of the output
+    against the oracle.  Inputs are U[-1,1] from torch's seeded device generator
+    (seed 4915), too large to draw on the host in a test."""
     import torch
-    n = 49152
     say(f"default-model strassen {n}^3 dtype={dtype}")
     h = fgemm.Handle(0)
     try:
@@ -374,8 +373,12 @@ def test_default_model_picks_strassen_at_49152_cube(dtype):
         g = torch.Generator(device="cuda")
         g.manual_seed(4915)
         td = torch.bfloat16 if dtype == BF16 else torch.float16
-        A = (torch.rand(n, n, device="cuda", generator=g) * 2 - 1).to(td)
-        B = (torch.rand(n, n, device="cuda", generator=g) * 2 - 1).to(td)
+        A = torch.empty(n, n, device="cuda", dtype=td)
+        B = torch.empty(n, n, device="cuda", dtype=td)
+        for X in (A, B):  # in row blocks: no full-size fp32 temporary
+            for r in range(0, n, 8192):
+                X[r:r + 8192] = (torch.rand(min(8192, n - r), n, device="cuda",
+                                            generator=g) * 2 - 1).to(td)
         C = torch.full((n, n), float("nan"), device="cuda", dtype=td)
         h.gemm(A, B, C)
         torch.cuda.synchronize()
