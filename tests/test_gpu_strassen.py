@@ -8,7 +8,7 @@ import pytest
 import oracle
 from hgemm_strassen_type_amd import fgemm
 from hgemm_strassen_type_amd import inputs
-from gpu_util import (BF16, F16, STATS_TOL, STRASSEN_TOL, empty_out, from_dev, handle, rel_err,
+from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, STRASSEN_TOL, empty_out, from_dev, handle, rel_err,
                       run, say, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -359,7 +359,7 @@ def test_default_model_picks_strassen_at_large_cubes(dtype, n):
     """At 49152^3 and 65536^3 (2^32 elements per operand, 75 GB of workspace) the
     default model, whose workspace cap is a third of device memory, picks a Strassen
     plan, and fgemm_gemm runs it: 24 sampled rows x 256 sampled columns of the output
-    against the oracle.  Inputs are U[-1,1] from torch's seeded device generator
+    against the oracle; the classical kernel on the same inputs too.  Inputs are U[-1,1] from torch's seeded device generator
     (seed 4915), too large to draw on the host in a test."""
     import torch
     say(f"default-model strassen {n}^3 dtype={dtype}")
@@ -388,10 +388,16 @@ def test_default_model_picks_strassen_at_large_cubes(dtype, n):
         A_s = from_dev(A.index_select(0, r))
         B_s = from_dev(B.index_select(1, c))
         got = from_dev(C.index_select(0, r).index_select(1, c))
+        # the classical kernel on the same inputs, for the same entries
+        C.fill_(float("nan"))
+        h.gemm(A, B, C, plan=fgemm.classical_plan())
+        torch.cuda.synchronize()
+        got_c = from_dev(C.index_select(0, r).index_select(1, c))
         del A, B, C
         _, Q, _ = oracle.gemm(A_s, B_s, dtype=dtype)
         err = rel_err(got, Q, dtype)
         assert err <= pick.pred_rel_err <= STRASSEN_TOL, (err, pick.pred_rel_err)
+        assert rel_err(got_c, Q, dtype) <= CLASSICAL_TOL
     finally:
         h.close()
         torch.cuda.empty_cache()
