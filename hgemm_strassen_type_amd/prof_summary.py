@@ -5,6 +5,8 @@
     python -m hgemm_strassen_type_amd.prof_summary traffic <fetch.csv> <write.csv> <out.json>
         "<kernel substring>" "<command>"
 
+    python -m hgemm_strassen_type_amd.prof_summary clock <pmc.csv> <out.md> "<command>"
+        "<kernel substring>" <FLOP per launch>
     python -m hgemm_strassen_type_amd.prof_summary adds <kernel_trace.csv> <fetch.csv>
         <write.csv> <bench stdout log> <out.md> "<commands>"
 
@@ -167,6 +169,38 @@ def adds(trace_csv: str, fetch_csv: str, write_csv: str, bench_log: str, out_md:
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def clock(pmc_csv: str, out_md: str, command: str, kernel: str, flops: float, cus: int = 256,
+          xcds: int = 8, flop_per_clk_cu: float = 4096.0) -> None:
+    """Clock held and MFMA occupancy of a GEMM kernel from GRBM_GUI_ACTIVE (GPU cycles
+    while busy, summed over the XCDs): per dispatch, cycles per XCD / duration is the
+    clock; the cycles the MFMA work needs at full rate (flops / (cus * flop_per_clk_cu))
+    over the cycles taken is the fraction of cycles the MFMA pipes had work."""
+    per = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not per:
+        raise SystemExit(f"no kernel matching {kernel!r}")
+    need = flops / (cus * flop_per_clk_cu)
+    name = next(iter(per.values()))["name"]
+    lines = ["# Clock and MFMA occupancy of the GEMM kernel (rocprofv3 --pmc)", "",
+             f"Kernel: `{_short(name)}`", "", "Command:", "", "```", command, "```", "",
+             f"MFMA work per launch: {flops:.4g} FLOP = {need / 1e6:.3f} M cycles per CU at "
+             f"{flop_per_clk_cu:.0f} FLOP/clock/CU (dense 16-bit) on {cus} CUs.", "",
+             "| dispatch | us | GRBM_GUI_ACTIVE (sum of XCDs) | cycles per XCD | clock GHz "
+             "| MFMA busy | TFLOP/s |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(per, key=int):
+        d = per[k]
+        cyc = d["GRBM_GUI_ACTIVE"] / xcds
+        lines.append(f"| {k} | {d['us']:.1f} | {d['GRBM_GUI_ACTIVE']:.4g} | {cyc / 1e6:.3f} M | "
+                     f"{cyc / (d['us'] * 1e3):.2f} | {need / cyc:.3f} | "
+                     f"{flops / (d['us'] * 1e-6) / 1e12:.0f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         extra = sys.argv[5:]
@@ -174,6 +208,8 @@ if __name__ == "__main__":
               *([int(extra[2])] if len(extra) > 2 else []), *(extra[3:4]))
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+    elif sys.argv[1] == "clock":
+        clock(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], float(sys.argv[6]))
     elif sys.argv[1] == "adds":
         adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
              title=sys.argv[8] if len(sys.argv) > 8 else "the Strassen add kernels")
