@@ -83,3 +83,23 @@ def test_traffic_record(tmp_path):
     assert rec["write_scale"] == pytest.approx(1.0)
     assert rec["bytes_per_launch"] == pytest.approx(2000 * 1024 * 2 + 500 * 1024)
     assert len(rec["kernel_hash"]) == 16
+
+
+def test_clock_summary(tmp_path):
+    # 8 XCDs summing 8 * 1.5e6 cycles over 1000 us: 1.5 GHz; 1.05e12 FLOP on 256 CUs at
+    # 4096 FLOP/clock/CU needs ~1.0014e6 cycles, so the MFMA pipes are busy ~0.668
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+           "End_Timestamp"]
+    rows = [["7", "gemm_mfma_kernel<TileCfg<256, 256,...>", "GRBM_GUI_ACTIVE", 12.0e6, 1000, 1001000],
+            ["7", "gemm_mfma_kernel<TileCfg<256, 256,...>", "SQ_WAVES", 2048, 1000, 1001000],
+            ["8", "other_kernel", "GRBM_GUI_ACTIVE", 1.0, 0, 10]]
+    write_csv(tmp_path / "pmc.csv", hdr, rows)
+    out = tmp_path / "c.md"
+    prof_summary.clock(str(tmp_path / "pmc.csv"), str(out), "cmd", "TileCfg<256, 256", 1.05e12)
+    line = [l for l in out.read_text().splitlines() if l.startswith("| 7 |")][0]
+    cells = [c.strip() for c in line.split("|")[1:-1]]
+    assert float(cells[1]) == pytest.approx(1000.0)
+    assert float(cells[4]) == pytest.approx(1.5)
+    assert float(cells[5]) == pytest.approx(1.05e12 / (256 * 4096) / 1.5e6, abs=1e-3)
+    assert float(cells[6]) == pytest.approx(1050, abs=1)
+    assert "| 8 |" not in out.read_text()
