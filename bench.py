@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--main-dtype", choices=("bf16", "fp16"), default="bf16",
+                    help="input type of the 8192^3 workload; fp16 only with --only-main "
+                         "(for profiler runs that compare the two types on one box)")
     ap.add_argument("--only-adds", action="store_true",
                     help="time Winograd depth 1 at bf16 16384^3 only and print the add kernels' "
                          "algorithmic bytes (for profiler runs of the add kernels)")
@@ -156,10 +159,14 @@ def main():
 
     # ---------------------------------------------------------------- headline
     n = 8192
-    A = normal((n, n), 2001)
-    B = normal((n, n), 2002)
-    C = normal((n, n), 2003)
-    plan = h.select(n, n, n)
+    if args.main_dtype != "bf16" and not args.only_main:
+        print("--main-dtype fp16 needs --only-main (the headline metric is bf16)", file=sys.stderr)
+        sys.exit(2)
+    mdt = torch.float16 if args.main_dtype == "fp16" else torch.bfloat16
+    A = normal((n, n), 2001, dtype=mdt)
+    B = normal((n, n), 2002, dtype=mdt)
+    C = normal((n, n), 2003, dtype=mdt)
+    plan = h.select(n, n, n, dtype=fgemm.FGEMM_F16 if args.main_dtype == "fp16" else fgemm.FGEMM_BF16)
     log(f"headline bf16 {n}^3 NN beta=0.5, plan {plan.as_dict()}")
     ms = timer.time(lambda: h.gemm(A, B, C, beta=0.5), args.steps, args.warmup)
     flops = 2.0 * n * n * n
@@ -197,10 +204,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.main_dtype,
         "data": "synthetic",
-        "config": {"workload": "bf16 GEMM NN row-major M=N=K=8192, A,B,C ~ N(0,1), alpha=1, "
-                               "beta=0.5, fp32 accumulate, bf16 output",
+        "config": {"workload": f"{args.main_dtype} GEMM NN row-major M=N=K=8192, A,B,C ~ N(0,1), alpha=1, "
+                               f"beta=0.5, fp32 accumulate, {args.main_dtype} output",
                    "M": n, "N": n, "K": n, "layout": "NN", "alpha": 1.0, "beta": 0.5,
                    "plan": {k: v for k, v in plan.as_dict().items()
                             if k in ("path", "depth", "variant", "tile_m", "tile_n")}},
