@@ -15,7 +15,7 @@ The same JSON line carries
                 null when the kernel sources changed after those counters;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (a seeded subset of output rows), with the threads it used;
-  workloads     the other shapes: 4096^3 and TN layouts, LLM projection/FFN and
+  workloads     the other shapes: 4096^3 and TN layouts, 8192^3 on fp16 inputs, LLM projection/FFN and
                 decode shapes (decode as HBM GB/s), the projection with RoPE and the
                 FFN up projection with bias + GELU, the fused two-GEMM chain (also on
                 the Strassen path), and
@@ -288,6 +288,9 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     gemm_case("bf16_4096_TN_beta0.5", 4096, 4096, 4096, transA=True, beta=0.5,
               seeds=(2001, 2002, 2003))
     gemm_case("bf16_8192_TN_beta0.5", 8192, 8192, 8192, transA=True, beta=0.5,
+              seeds=(2001, 2002, 2003))
+    # the same shape on fp16 inputs (the chip holds a lower clock on fp16 MFMA work)
+    gemm_case("fp16_8192_NN_beta0.5", 8192, 8192, 8192, beta=0.5, dtype=torch.float16,
               seeds=(2001, 2002, 2003))
     for N in (4096, 14336):
         gemm_case(f"bf16_prefill_16384x{N}x4096", 16384, N, 4096, std_b=0.02,
