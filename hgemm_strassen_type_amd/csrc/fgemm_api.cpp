@@ -80,6 +80,11 @@ uint32_t epi_flags(const fgemm_epilogue_t* e) { return e ? e->flags : 0u; }
 // Epilogues on gate/up column pairs of a 2N-wide op(B).
 constexpr uint32_t kSwiGLUFlags = FGEMM_EPI_RMS_SWIGLU | FGEMM_EPI_SWIGLU_BWD;
 
+// Relative error the row statistics (ROWSUMSQ) of an automatic plan are held to.
+// In the CODA split (tilnote.io PingPong GEMM note, CODA section) these sums set the
+// next GEMM's RMS row scale.
+constexpr double kStatsRelErr = 1e-3;
+
 // Whether the 16-byte fast path applies.
 int vec_ok(fgemm_op_t ta, fgemm_op_t tb, int64_t N, const void* A, int64_t lda, const void* B,
            int64_t ldb, const void* C, int64_t ldc, const fgemm_epilogue_t* e) {
@@ -188,6 +193,11 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       // accuracy guard: the calibrated error of this variant and depth within budget
       const double err = predicted_rel_err(dtype, variant, depth);
       if (err > md.max_rel_err) continue;
+      // statistics guard: a row's sum of squares of the written output moves by up
+      // to about twice the output's relative error (for y' = y + d, |sum y'^2 -
+      // sum y^2| / sum y^2 <= 2e + e^2 with e = ||d|| / ||y||); row statistics are
+      // held to kStatsRelErr, so they stay classical unless 2e fits in it
+      if ((flags & FGEMM_EPI_ROWSUMSQ) && 2.0 * err > kStatsRelErr) continue;
       // sub-problems below 512 never pay for their additions; keep them classical
       if ((M >> depth) < 512 || ((swiglu ? 2 * N : N) >> depth) < 512 || (K >> depth) < 512)
         continue;

@@ -214,6 +214,9 @@ struct GemmTile {
   // Rows and columns beyond M or N (edge tiles) are clamped onto the last valid
   // ones: they load real memory, feed MFMA rows/columns the epilogue never stores,
   // and keep the fast path open for partial tiles whose K is a whole number of phases.
+  // For M/N-contiguous operands the caller guarantees that the edge dimension is a
+  // multiple of 8 on such tiles, so a chunk is either wholly valid (never moved) or
+  // wholly past the edge (moved onto the last 8 valid values, never stored).
   __device__ __forceinline__ static void load_addr(const GemmProblem& P, int m0, int n0,
                                                    int wave, int lane_in, LoadAddr& la) {
     // recomputed per tile: an opaque lane id keeps the lane-only parts from being
@@ -1230,11 +1233,17 @@ __device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits
   w->ktiles = ktiles_all / splits;
   w->kt0 = w->y * w->ktiles;
   // Phases with no K tail take the direct-load ring, also on M/N edge tiles
-  // (clamped rows; transposed operands need 8 valid columns from the tile start).
+  // (rows and columns past the edge are clamped onto valid memory).  An operand
+  // stored M- or N-contiguous moves 8 consecutive rows/columns per 16-byte chunk,
+  // and a clamped chunk is moved whole: on an edge tile every chunk must be either
+  // wholly inside the matrix or wholly outside, i.e. that edge dimension must be a
+  // multiple of 8 (a chunk straddling the edge would land its valid values in the
+  // wrong tile positions).  Other edge tiles take the bounds-checked path.
   // Per-lane offsets are 32-bit, which bounds the leading dimensions there.
   const int64_t b_rows = BKC ? (T::SWIGLU ? 2 * (int64_t)P.N : P.N) : CFG::BK;
-  w->fast = VEC && (P.K % CFG::BK == 0) && (AK || P.M - w->m0 >= 8) &&
-            (BKC || P.N - w->n0 >= 8) &&
+  w->fast = VEC && (P.K % CFG::BK == 0) &&
+            (AK || P.M % 8 == 0 || P.M - w->m0 >= CFG::BM) &&
+            (BKC || P.N % 8 == 0 || P.N - w->n0 >= T::OUT_BN) &&
             (int64_t)(AK ? CFG::BM : CFG::BK + 1) * P.lda < (1ll << 31) &&
             (b_rows + 1) * P.ldb < (1ll << 31);
   return true;

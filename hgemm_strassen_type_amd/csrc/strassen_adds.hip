@@ -118,7 +118,8 @@ __global__ void scale_from_max_kernel(const float* partial, int count, float tar
   float s = 1.f;
   if (m > 0.f && isfinite(m)) {
     int e;
-    frexpf(target / m, &e);          // target/m = f * 2^e, 0.5 <= f < 1
+    // in fp64: for the smallest bf16 magnitudes target/m leaves the fp32 range
+    frexp((double)target / (double)m, &e);  // target/m = f * 2^e, 0.5 <= f < 1
     e -= 1;
     e = e < -126 ? -126 : (e > 126 ? 126 : e);  // a normal fp32 power of two
     s = ldexpf(1.f, e);
@@ -268,8 +269,12 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
   const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   // lanes past the row still take part in the row-sum reductions
   const bool active = j < a.n;
-  float factor = 1.f;
-  if (!a.out32) factor = a.alpha / *a.scale_a / *a.scale_b;  // the scales' product may leave fp32
+  // alpha / (sa*sb) in fp64: each scale may reach 2^126, so the factor can lie far
+  // below the fp32 range while the scaled products times it are ordinary values.
+  // Both scales are powers of two, so an fp32 value times the factor is exact in
+  // fp64 and its one rounding is the one to fp32, as in an fp32 product.
+  double factor = 1.0;
+  if (!a.out32) factor = (double)a.alpha / (double)*a.scale_a / (double)*a.scale_b;
   const bool stats = a.ss_partial != nullptr;
   // rotary embedding: the rates of this lane's two pairs in each column block
   // (a lane keeps its columns for every row)
@@ -299,12 +304,12 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int64_t row = h * a.m + i;
-          const float r = rsqrtf(a.rms_ss[row] * a.rms_inv_n + a.rms_eps) * factor;
+          const double r = (double)rsqrtf(a.rms_ss[row] * a.rms_inv_n + a.rms_eps) * factor;
           const int64_t off = row * a.ldc + j;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float g = r * c[e][2 * h], u = r * c[e][2 * h + 1];
+            const float g = (float)(r * c[e][2 * h]), u = (float)(r * c[e][2 * h + 1]);
             v[e] = g / (1.f + __expf(-g)) * u;
           }
           if (a.beta != 0.f) {
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
             const int64_t off = row * a.ldc + col;
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = factor * c[e][b];
+            for (int e = 0; e < 4; ++e) v[e] = (float)(factor * c[e][b]);
             if (a.beta != 0.f) {
               uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
               v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);

@@ -198,8 +198,11 @@ fgemm_status_t fgemm_set_model(fgemm_handle_t handle, const fgemm_model_t* model
  * classical kernel and Strassen/Winograd at depth 1 and 2, subject to the
  * accuracy (model.max_rel_err against the plan's pred_rel_err), divisibility,
  * epilogue and workspace guards; a tighter error budget lowers the depth or keeps
- * the classical path.  Host only; it caches nothing (fgemm_gemm keeps its own
- * pick per shape in the handle). */
+ * the classical path.  With ROWSUMSQ a statistics guard also applies: a row's sum
+ * of squares moves by up to about twice the output's relative error, so such calls
+ * go to Strassen only where 2*pred_rel_err <= 1e-3 (with the built-in error table:
+ * never; the statistics then stay within 1e-3 on every automatic plan).  Host only;
+ * it caches nothing (fgemm_gemm keeps its own pick per shape in the handle). */
 fgemm_status_t fgemm_select(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
                             int64_t M, int64_t N, int64_t K, fgemm_dtype_t dtype,
                             const fgemm_epilogue_t* epilogue, fgemm_plan_t* plan);

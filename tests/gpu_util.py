@@ -65,15 +65,20 @@ def handle():
 
 def run(A_bits, B_bits, dtype, *, transA=False, transB=False, alpha=1.0, beta=0.0, C_bits=None,
         M=None, N=None, plan=None, epilogue=None, pad=0):
-    """Run one GEMM on the device; returns the output bits."""
+    """Run one GEMM on the device; returns the output bits.  `pad` widens the
+    leading dimension of every operand by that many elements, or of A, B and C
+    separately when it is a triple."""
     import torch
-    A = to_dev(A_bits, dtype, pad)
-    B = to_dev(B_bits, dtype, pad)
+    pa, pb, pc = pad if isinstance(pad, tuple) else (pad, pad, pad)
+    A = to_dev(A_bits, dtype, pa)
+    B = to_dev(B_bits, dtype, pb)
     if M is None:
         M = A_bits.shape[1] if transA else A_bits.shape[0]
     if N is None:
         N = B_bits.shape[0] if transB else B_bits.shape[1]
-    C = to_dev(C_bits, dtype, pad) if C_bits is not None else empty_out(M, N, dtype)
+    if C_bits is None:
+        C_bits = np.full((M, N), 0x7FC0, dtype=np.uint16)  # NaN: unwritten elements show
+    C = to_dev(C_bits, dtype, pc)
     handle().gemm(A, B, C, transA=transA, transB=transB, alpha=alpha, beta=beta, plan=plan,
                   epilogue=epilogue)
     torch.cuda.synchronize()

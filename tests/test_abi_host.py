@@ -187,21 +187,45 @@ def test_select_never_picks_strassen_where_it_cannot_run():
 
 def test_select_strassen_with_epilogues():
     # every epilogue runs in the Strassen post-add: where the multiply saving wins,
-    # the row statistics and RMS + SwiGLU epilogues take the Strassen path too, and
-    # the statistics' partials are counted in the workspace
+    # the bias and RMS + SwiGLU epilogues take the Strassen path too
     fast_mem = mi355x_model(hbm_gbps=80000.0)
     base = select(16384, 16384, 16384, fast_mem)
-    ss = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
-    p = select(16384, 16384, 16384, fast_mem, epi=ss)
+    bias = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS, bias=P)
+    p = select(16384, 16384, 16384, fast_mem, epi=bias)
     assert p.path == fgemm.FGEMM_PATH_STRASSEN
-    assert p.workspace_bytes > base.workspace_bytes
+    assert p.workspace_bytes == base.workspace_bytes
     sw = fgemm.make_epilogue(fgemm.FGEMM_EPI_RMS_SWIGLU, rms_rowsumsq=P, rms_n=4096, rms_eps=1e-6)
     p = select(16384, 8192, 16384, fast_mem, epi=sw)
     assert p.path == fgemm.FGEMM_PATH_STRASSEN
     assert p.workspace_bytes == base.workspace_bytes  # op(B) is 16384 wide
     # on the MI355X constants the configured fused chain stays classical
+    ss = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
     for (M, N, K, e) in [(8192, 4096, 4096, ss), (8192, 11008, 4096, sw)]:
         assert select(M, N, K, epi=e).path == fgemm.FGEMM_PATH_CLASSICAL
+
+
+def test_select_statistics_guard_keeps_row_sums_within_1e3():
+    """A row's sum of squares of the written output moves by up to 2e + e^2 for an
+    output relative error e, so row statistics (ROWSUMSQ) go to Strassen only where
+    twice the plan's predicted error is within 1e-3.  No Strassen figure is that low,
+    so every automatic ROWSUMSQ plan is classical, also where Strassen wins without
+    statistics: with bandwidth to spare, and at 49152^3 and 65536^3 under the
+    calibrated MI355X constants."""
+    ss = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=P)
+    ssb = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ | fgemm.FGEMM_EPI_BIAS, rowsumsq=P, bias=P)
+    fast_mem = mi355x_model(hbm_gbps=80000.0)
+    cal = mi355x_model(eta_mfma=0.52, eta_hbm=0.66, max_workspace_bytes=288e9 / 3)
+    for (n, md) in [(16384, fast_mem), (49152, cal), (65536, cal)]:
+        for dt in (BF, HF):
+            assert select(n, n, n, md, dtype=dt).path == fgemm.FGEMM_PATH_STRASSEN, (n, dt)
+            for e in (ss, ssb):
+                p = select(n, n, n, md, epi=e, dtype=dt)
+                assert p.path == fgemm.FGEMM_PATH_CLASSICAL, (n, dt)
+                assert 2 * p.pred_rel_err <= 1e-3
+    for dt in (BF, HF):
+        for v in (fgemm.FGEMM_VARIANT_S69, fgemm.FGEMM_VARIANT_WINOGRAD):
+            for d in (1, 2):
+                assert 2 * fgemm.fgemm_plan_rel_err(dt, fgemm.strassen_plan(d, v)) > 1e-3
 
 
 def test_select_predicted_time_is_monotone():

@@ -43,6 +43,27 @@ def test_exact_integer_products(tile, dtype, transA, transB):
         assert np.array_equal(got, Q), (M, N, K)
 
 
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_edge_chunk_straddling_the_matrix_edge(tile, dtype):
+    """Aligned leading dimensions, but an M/N-contiguous operand whose edge dimension
+    is not a multiple of 8: a 16-byte chunk of the edge tile straddles the edge and
+    must not be moved (NN: B stored K x N with N = 77 and ldb = ldc = 80; TN: A
+    stored K x M with M = 70 and lda = 72).  Integer inputs and an integer C with
+    beta = 1: every output is exact, so the comparison is bitwise."""
+    for (transA, M, N, K, pad) in [(False, 64, 77, 64, (0, 3, 3)), (True, 70, 64, 64, (2, 0, 0)),
+                                   (False, 300, 205, 128, (0, 3, 3)),
+                                   (True, 270, 136, 128, (2, 0, 0)),
+                                   (True, 70, 77, 64, (2, 3, 3))]:
+        say(f"edge chunk tile={tile} dtype={dtype} tA={transA} M={M} N={N} K={K} pad={pad}")
+        A, B = stored(M, N, K, transA, False, 0, 15 + M, 16 + N, dtype)
+        C = inputs.integers((M, N), 17 + K, dtype, -4, 4)
+        _, Q, _ = oracle.gemm(A, B, transA=transA, beta=1.0, C=C, dtype=dtype)
+        got = run(A, B, dtype, transA=transA, M=M, N=N, beta=1.0, C_bits=C, pad=pad,
+                  plan=fgemm.classical_plan(*tile))
+        assert np.array_equal(got, Q), (transA, M, N, K)
+
+
 @pytest.mark.parametrize("dtype", [BF16, F16])
 @pytest.mark.parametrize("transA,transB", LAYOUTS)
 def test_random_ragged_with_alpha_beta(dtype, transA, transB):
@@ -256,14 +277,22 @@ def test_persistent_chains_odd_and_even_phases(tile, bk, phases):
 
 
 @pytest.mark.parametrize("transA", [False, True])
-def test_persistent_chains_through_edge_tiles(transA):
-    """Chains of tiles per workgroup that cross clamped edge tiles (fast path) and
-    tiles narrower than 8 in the contiguous dimension of a transposed operand
-    (bounds-checked path) in one launch.  Integer inputs: exact."""
+@pytest.mark.parametrize("edge8", [True, False])
+def test_persistent_chains_through_edge_tiles(transA, edge8):
+    """Chains of tiles per workgroup that cross edge tiles in one launch, with every
+    leading dimension a multiple of 8 (the aligned kernel).  edge8: the M/N-contiguous
+    operand's edge dimension is a multiple of 8, so its edge tiles stay on the
+    direct-load path with clamped chunks; otherwise they take the bounds-checked
+    path between direct-load tiles.  Integer inputs: exact."""
     dtype = BF16
-    M, N, K = (4452, 4356, 320) if not transA else (4356, 4452, 320)
+    ragged = 4360 if edge8 else 4356  # 17 tiles of 256 plus 8 (or 4) rows or columns
+    M, N, K = (4452, ragged, 320) if not transA else (ragged, 4452, 320)
     say(f"persistent chains with edge tiles transA={transA} M={M} N={N} K={K}")
     A, B = stored(M, N, K, transA, False, 0, 111, 112, dtype)
     _, Q, _ = oracle.gemm(A, B, transA=transA, dtype=dtype)
-    got = run(A, B, dtype, transA=transA, M=M, N=N, plan=fgemm.classical_plan(256, 256))
+    # pad every operand to a leading dimension that is a multiple of 8
+    pa = (-(M if transA else K)) % 8
+    pb = (-N) % 8
+    got = run(A, B, dtype, transA=transA, M=M, N=N, pad=(pa, pb, pb),
+              plan=fgemm.classical_plan(256, 256))
     assert np.array_equal(got, Q)

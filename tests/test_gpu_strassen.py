@@ -101,6 +101,25 @@ def test_large_magnitudes_are_scaled_into_fp16():
         assert rel_err(got, Q, dtype) <= STRASSEN_TOL
 
 
+def test_tiny_magnitudes_keep_their_unscale_factor():
+    """bf16 inputs near the bottom of the exponent range: max|A| * max|B| = 2^-124,
+    so each fp16 scale is 2^74 and alpha / (sa * sb) = 2^-148 lies below the fp32
+    normal range; the outputs (about 1e-37) are ordinary bf16 values and must come
+    out as accurately as at unit scale."""
+    dtype = BF16
+    M = N = K = 256
+    say("strassen bf16 tiny magnitudes")
+    sc = 2.0 ** -62
+    A = inputs.to_bits(oracle.decode(inputs.uniform((M, K), 303, dtype), dtype) * sc, dtype)
+    B = inputs.to_bits(oracle.decode(inputs.uniform((K, N), 304, dtype), dtype) * sc, dtype)
+    _, Q, _ = oracle.gemm(A, B, alpha=1.5, dtype=dtype)
+    assert np.abs(oracle.decode(Q, dtype)).max() < 1e-35
+    for variant in (S69, WIN):
+        for depth in (1, 2):
+            got = run(A, B, dtype, alpha=1.5, plan=fgemm.strassen_plan(depth, variant))
+            assert rel_err(got, Q, dtype) <= STRASSEN_TOL, (variant, depth)
+
+
 def test_unsupported_shapes_and_epilogues_are_refused():
     import torch
     from gpu_util import to_dev, handle, empty_out
@@ -398,6 +417,48 @@ def test_default_model_picks_strassen_at_large_cubes(dtype, n):
         err = rel_err(got, Q, dtype)
         assert err <= pick.pred_rel_err <= STRASSEN_TOL, (err, pick.pred_rel_err)
         assert rel_err(got_c, Q, dtype) <= CLASSICAL_TOL
+    finally:
+        h.close()
+        torch.cuda.empty_cache()
+
+
+def test_row_statistics_stay_classical_and_within_1e3_at_49152():
+    """ROWSUMSQ under the default model at 49152^3, where the same call without
+    statistics goes to Strassen: the statistics guard keeps it classical, and the
+    row sums of squares of 8 sampled rows (whole rows, against the oracle's of the
+    exactly rounded rows) are within 1e-3.  Inputs are U[-1,1] from torch's seeded
+    device generator (seed 4916)."""
+    import torch
+    dtype, n = BF16, 49152
+    say(f"rowsumsq auto {n}^3")
+    h = fgemm.Handle(0)
+    try:
+        assert h.select(n, n, n, dtype=dtype).path == fgemm.FGEMM_PATH_STRASSEN
+        ssd = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_ROWSUMSQ, rowsumsq=ssd.data_ptr())
+        assert h.select(n, n, n, dtype=dtype, epilogue=epi).path == fgemm.FGEMM_PATH_CLASSICAL
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4916)
+        A = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        B = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        for X in (A, B):  # in row blocks: no full-size fp32 temporary
+            for r in range(0, n, 8192):
+                X[r:r + 8192] = (torch.rand(min(8192, n - r), n, device="cuda",
+                                            generator=g) * 2 - 1).to(torch.bfloat16)
+        C = torch.full((n, n), float("nan"), device="cuda", dtype=torch.bfloat16)
+        h.gemm(A, B, C, epilogue=epi)
+        torch.cuda.synchronize()
+        rows = inputs.sample_rows(n, 8, 23)
+        r = torch.from_numpy(rows).cuda()
+        A_s = from_dev(A.index_select(0, r))
+        got = from_dev(C.index_select(0, r))
+        ss = ssd.index_select(0, r).cpu().numpy().astype(np.float64)
+        del C, A
+        B_h = from_dev(B)
+        del B
+        _, Q, ssr = oracle.gemm(A_s, B_h, dtype=dtype, epi=oracle.EPI_ROWSUMSQ)
+        assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+        assert np.max(np.abs(ss - ssr) / ssr) <= STATS_TOL
     finally:
         h.close()
         torch.cuda.empty_cache()

@@ -277,6 +277,61 @@ def test_rms_swiglu_closed_forms():
     assert oracle.rel_fro(D, g / (1 + np.exp(-g)) * h) < 1e-12
 
 
+def test_rms_swiglu_alpha_and_beta_placement():
+    """alpha scales the GEMM result before the epilogue (C = alpha*op(A)op(B) + beta*C
+    with the epilogue on the first term), so it sits inside silu and scales both
+    halves; beta*C is added after the SwiGLU.  Closed forms at alpha != 1 and
+    beta != 0 that a misplaced alpha or beta would fail."""
+    dtype = BF16
+    M, K, Nout = 12, 16, 20
+    X = inputs.normal((M, K), 24, dtype)
+    W = inputs.normal((K, Nout), 25, dtype, std=0.5)
+    C = inputs.normal((M, Nout), 26, dtype)
+    ssin = np.abs(np.random.default_rng(4).standard_normal(M)) * 100 + 1
+    h = oracle.decode(X, dtype) @ oracle.decode(W, dtype)
+    r = 1.0 / np.sqrt(ssin / 4096.0 + 1e-6)
+    Wgu = np.concatenate([W, W], axis=1)
+    # gate == up, alpha = 2: out = silu(2 r h) * (2 r h), not 2 * silu(r h) * (r h)
+    D, _, _ = oracle.gemm(X, Wgu, dtype=dtype, alpha=2.0, epi=oracle.EPI_RMS_SWIGLU, rms_ss=ssin,
+                          rms_n=4096, rms_eps=1e-6)
+    g = 2.0 * r[:, None] * h
+    assert oracle.rel_fro(D, g / (1.0 + np.exp(-g)) * g) < 1e-14
+    g1 = r[:, None] * h
+    assert oracle.rel_fro(D, 2.0 * g1 / (1.0 + np.exp(-g1)) * g1) > 1e-2
+    # up == 0, beta = 0.5: the SwiGLU term vanishes and exactly 0.5*C is left
+    Wu = np.concatenate([W, np.zeros_like(W)], axis=1)
+    D, Q, _ = oracle.gemm(X, Wu, dtype=dtype, alpha=1.5, beta=0.5, C=C,
+                          epi=oracle.EPI_RMS_SWIGLU, rms_ss=ssin, rms_n=4096, rms_eps=1e-6)
+    assert np.array_equal(D, 0.5 * oracle.decode(C, dtype))
+    assert np.array_equal(Q, oracle.encode(0.5 * oracle.decode(C, dtype), dtype))
+    # both at once: silu(1.5 r h) * (1.5 r h) + 0.25 * C
+    D, _, _ = oracle.gemm(X, Wgu, dtype=dtype, alpha=1.5, beta=0.25, C=C,
+                          epi=oracle.EPI_RMS_SWIGLU, rms_ss=ssin, rms_n=4096, rms_eps=1e-6)
+    g = 1.5 * r[:, None] * h
+    ref = g / (1.0 + np.exp(-g)) * g + 0.25 * oracle.decode(C, dtype)
+    assert oracle.rel_fro(D, ref) < 1e-14
+
+
+def test_tiny_magnitudes_scale_exactly():
+    """bf16 shares fp32's exponent range: A * 2^-60 and B * 2^-60 are exact and the
+    exact product scales by 2^-120 (results around 1e-36), so the oracle's fp64
+    result, and its rounding wherever the scaled result is still a normal bf16
+    value, are the ones at unit scale times 2^-120."""
+    dtype = BF16
+    A = inputs.uniform((48, 40), 27, dtype)
+    B = inputs.uniform((40, 56), 28, dtype)
+    sc = 2.0 ** -60
+    At = inputs.to_bits(oracle.decode(A, dtype) * sc, dtype)
+    Bt = inputs.to_bits(oracle.decode(B, dtype) * sc, dtype)
+    assert np.array_equal(oracle.decode(At, dtype), oracle.decode(A, dtype) * sc)
+    D, Q, _ = oracle.gemm(A, B, dtype=dtype)
+    Dt, Qt, _ = oracle.gemm(At, Bt, dtype=dtype)
+    assert np.array_equal(Dt, D * sc * sc)
+    nz = np.abs(D) >= 2.0 ** -6  # results whose scaled value (>= 2^-126) is normal
+    assert nz.mean() > 0.9
+    assert np.array_equal(oracle.decode(Qt, dtype)[nz], (oracle.decode(Q, dtype) * sc * sc)[nz])
+
+
 def test_rejects_bad_arguments():
     A = inputs.normal((4, 4), 1, BF16)
     with pytest.raises(ValueError):
