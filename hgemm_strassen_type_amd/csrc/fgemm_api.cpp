@@ -58,11 +58,21 @@ struct PlanKeyHash {
 
 }  // namespace
 
+// A fixed, direct-mapped plan table for fgemm_gemm_noalloc (no allocation on a miss:
+// the entry is overwritten).
+struct NoAllocSlot {
+  PlanKey key;
+  fgemm_plan_t plan;
+  bool valid;
+};
+constexpr int kNoAllocSlots = 64;
+
 struct fgemm_handle_s {
   int device = 0;
   int cus = 0;  // compute units of the device (the model's count may be set otherwise)
   fgemm_model_t model{};
   std::unordered_map<PlanKey, fgemm_plan_t, PlanKeyHash> plans;
+  NoAllocSlot noalloc_plans[kNoAllocSlots] = {};
   void* user_ws = nullptr;
   size_t user_ws_bytes = 0;
   void* own_ws = nullptr;
@@ -135,7 +145,7 @@ size_t strassen_stats_bytes(int64_t M, int64_t Nb, uint32_t flags) {
 // Core of fgemm_select: classical tile choice, then Strassen candidates under guards.
 fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K,
                            fgemm_dtype_t dtype, uint32_t flags, int beta_hint, int vec,
-                           size_t ws_limit, fgemm_plan_t* out) {
+                           size_t ws_limit, fgemm_plan_t* out, bool classical_only = false) {
   fgemm_plan_t p{};
   const int swiglu = (flags & kSwiGLUFlags) != 0;
   double tc;
@@ -183,7 +193,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
   p.t_pred_us = tc;
   p.t_classical_pred_us = tc;
   p.pred_rel_err = predicted_rel_err(dtype, 0, 0);
-  for (int depth = 1; depth <= 2; ++depth) {
+  for (int depth = 1; depth <= (classical_only ? 0 : 2); ++depth) {
     for (int variant = FGEMM_VARIANT_S69; variant <= FGEMM_VARIANT_WINOGRAD; ++variant) {
       fgemm_plan_t c{};
       c.path = FGEMM_PATH_STRASSEN;
@@ -230,9 +240,21 @@ int tile_id(int tm, int tn) {
   return -1;
 }
 
-fgemm_status_t ensure_workspace(fgemm_handle_t h, size_t bytes, void** ws) {
+// Where a call's scratch memory comes from: the handle's workspace (the caller's,
+// or one the handle allocates), or a fixed device array that is never allocated.
+struct WsSource {
+  void* fixed = nullptr;
+  size_t fixed_bytes = 0;
+};
+
+fgemm_status_t ensure_workspace(fgemm_handle_t h, const WsSource& src, size_t bytes, void** ws) {
   *ws = nullptr;
   if (bytes == 0) return FGEMM_OK;
+  if (src.fixed) {
+    if (bytes > src.fixed_bytes) return FGEMM_ERR_WORKSPACE;
+    *ws = src.fixed;
+    return FGEMM_OK;
+  }
   if (h->user_ws) {
     if (h->user_ws_bytes < bytes) return FGEMM_ERR_WORKSPACE;
     *ws = h->user_ws;
@@ -281,7 +303,8 @@ void set_transform(const fgemm_epilogue_t* e, int* act, int* rope_hd, const int3
   *rope_log2_base = (flags & FGEMM_EPI_ROPE) ? log2((double)e->rope_theta) : 0.0;
 }
 
-fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c, int vec) {
+fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c, int vec,
+                             const WsSource& wsrc) {
   const uint32_t flags = epi_flags(c.epi);
   int tile = tile_id(plan.tile_m, plan.tile_n);
   if (tile < 0) return FGEMM_ERR_INVALID_VALUE;
@@ -303,7 +326,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     p.flags |= kFlagRowSumSq;
     parts = (int)ceil_div(c.N, tile_n_of(tile)) * waves_n_of(tile);
     void* ws;
-    fgemm_status_t st = ensure_workspace(h, (size_t)parts * (size_t)c.M * 4, &ws);
+    fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, &ws);
     if (st != FGEMM_OK) return st;
     p.ss_partial = static_cast<float*>(ws);
   }
@@ -316,7 +339,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
       p.rms_grad_out = 1;
       parts = (int)ceil_div(c.N, tile_n_of(tile) / 2) * waves_n_of(tile);
       void* ws;
-      fgemm_status_t st = ensure_workspace(h, (size_t)parts * (size_t)c.M * 4, &ws);
+      fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, &ws);
       if (st != FGEMM_OK) return st;
       p.ss_partial = static_cast<float*>(ws);
     }
@@ -352,7 +375,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     // fp32 K slices into the workspace, then the epilogue in the finalize pass
     void* ws;
     fgemm_status_t st =
-        ensure_workspace(h, (size_t)plan.split_k * (size_t)c.M * (size_t)c.N * 4, &ws);
+        ensure_workspace(h, wsrc, (size_t)plan.split_k * (size_t)c.M * (size_t)c.N * 4, &ws);
     if (st != FGEMM_OK) return st;
     p.C = ws;
     p.ldc = c.N;
@@ -485,7 +508,7 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   const size_t body = strassen_workspace(c.M, Nb, c.K, plan.depth, plan.variant);
   const size_t need = body + strassen_stats_bytes(c.M, Nb, flags);
   void* ws;
-  fgemm_status_t st = ensure_workspace(h, need, &ws);
+  fgemm_status_t st = ensure_workspace(h, WsSource{}, need, &ws);
   if (st != FGEMM_OK) return st;
   StrassenRun run{};
   run.c = &c;
@@ -544,15 +567,19 @@ struct DeviceGuard {
   }
 };
 
-fgemm_status_t execute(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
+fgemm_status_t execute(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c,
+                       const WsSource& wsrc = WsSource{}) {
   DeviceGuard guard(h->device);
   if (!guard.ok) return FGEMM_ERR_HIP;
   const int vec = vec_ok(c.ta, c.tb, c.N, c.A, c.lda, c.B, c.ldb, c.C, c.ldc, c.epi);
   const uint32_t flags = epi_flags(c.epi);
   fgemm_status_t st = check_plan_shape(plan, c.M, c.N, c.K, vec, flags);
   if (st != FGEMM_OK) return st;
-  if (plan.path == FGEMM_PATH_STRASSEN) return run_strassen(h, plan, c);
-  return run_classical(h, plan, c, vec);
+  if (plan.path == FGEMM_PATH_STRASSEN) {
+    if (wsrc.fixed) return FGEMM_ERR_NOT_SUPPORTED;  // its workspace is not fixed-size
+    return run_strassen(h, plan, c);
+  }
+  return run_classical(h, plan, c, vec, wsrc);
 }
 
 }  // namespace
@@ -646,6 +673,12 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FGEMM_ERR_HIP;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FGEMM_ERR_NOT_SUPPORTED;
+  {
+    // the fixed scratch of fgemm_gemm_noalloc: its device address on this device,
+    // asked once, with the device current
+    DeviceGuard guard(device);
+    if (!guard.ok || noalloc_scratch_init(device) != hipSuccess) return FGEMM_ERR_HIP;
+  }
   fgemm_handle_s* h = new (std::nothrow) fgemm_handle_s();
   if (!h) return FGEMM_ERR_ALLOC;
   h->device = device;
@@ -786,6 +819,37 @@ fgemm_status_t fgemm_gemm(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_
     }
   }
   return st;
+}
+
+fgemm_status_t fgemm_gemm_noalloc(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb, int64_t M,
+                                  int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                  const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                                  fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
+                                  void* stream) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  fgemm_status_t st = fgemm_check_args(ta, tb, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype, epi);
+  if (st != FGEMM_OK) return st;
+  if (M == 0 || N == 0) return FGEMM_OK;
+  WsSource wsrc;
+  wsrc.fixed = noalloc_scratch(h->device);
+  wsrc.fixed_bytes = kNoAllocScratchBytes;
+  if (!wsrc.fixed) return FGEMM_ERR_HIP;  // fgemm_create sets it up on the handle's device
+  const int vec = vec_ok(ta, tb, N, A, lda, B, ldb, C, ldc, epi);
+  PlanKey key{M, N, K, (int)ta, (int)tb, (int)dtype,
+              (int)epi_flags(epi) | (beta != 0.f ? 1 << 30 : 0), vec};
+  NoAllocSlot& slot = h->noalloc_plans[PlanKeyHash()(key) % kNoAllocSlots];
+  if (!slot.valid || !(slot.key == key)) {
+    fgemm_plan_t plan;
+    st = select_plan(h->model, M, N, K, dtype, epi_flags(epi), beta != 0.f, vec,
+                     kNoAllocScratchBytes, &plan, /*classical_only=*/true);
+    if (st != FGEMM_OK) return st;
+    slot.key = key;
+    slot.plan = plan;
+    slot.valid = true;
+  }
+  Call c{ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, epi,
+         static_cast<hipStream_t>(stream)};
+  return execute(h, slot.plan, c, wsrc);
 }
 
 }  // extern "C"

@@ -92,6 +92,13 @@ int waves_n_of(int tile);
 // Launch the classical kernel over a batch of same-shape problems.
 hipError_t launch_gemm(const KernelKey& key, const GemmBatch& batch, hipStream_t stream);
 
+// The fixed device scratch of fgemm_gemm_noalloc (noalloc.hip): its size, its
+// set-up (once per device, with that device current; fgemm_create calls it) and
+// its device address on a device (null before the set-up).
+constexpr size_t kNoAllocScratchBytes = FGEMM_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch_init(int device);
+void* noalloc_scratch(int device);
+
 // Deterministic reduction of the per-wave partial sums of squares into ss[M].
 hipError_t launch_rowsumsq_reduce(const float* partial, int parts, int M, float* ss,
                                   hipStream_t stream);

@@ -28,8 +28,11 @@ FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
 # every symbol include/fgemm.h declares
 EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
            "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
-           "fgemm_gemm_plan", "fgemm_check_args", "fgemm_tile_count", "fgemm_wave_count",
-           "fgemm_plan_rel_err", "fgemm_status_string")
+           "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_check_args", "fgemm_tile_count",
+           "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_status_string")
+
+# FGEMM_NOALLOC_SCRATCH_BYTES of fgemm.h
+FGEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class FgemmError(RuntimeError):
@@ -96,6 +99,8 @@ def lib():
                             i32, epi_p, vp]),
         "fgemm_gemm_plan": (st, [vp, plan_p, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
                                  vp, i64, i32, epi_p, vp]),
+        "fgemm_gemm_noalloc": (st, [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
+                                    i64, i32, epi_p, vp]),
         "fgemm_check_args": (st, [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64, i32,
                                   epi_p]),
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
@@ -190,6 +195,16 @@ def fgemm_gemm_plan(handle, plan, transA, transB, M, N, K, alpha, A, lda, B, ldb
     return s
 
 
+def fgemm_gemm_noalloc(handle, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       dtype, epilogue=None, stream=0, check=True) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    s = lib().fgemm_gemm_noalloc(handle, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                 ldc, dtype, e, stream)
+    if check:
+        _check(s, "fgemm_gemm_noalloc")
+    return s
+
+
 def fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype,
                      epilogue=None) -> int:
     e = ctypes.byref(epilogue) if epilogue is not None else None
@@ -253,8 +268,9 @@ class Handle:
             pass
 
     def gemm(self, A, B, C, *, transA=False, transB=False, alpha=1.0, beta=0.0, epilogue=None,
-             plan=None, stream=None):
-        """C = alpha*op(A)*op(B) + beta*C on torch device tensors (C written in place)."""
+             plan=None, stream=None, noalloc=False):
+        """C = alpha*op(A)*op(B) + beta*C on torch device tensors (C written in place);
+        noalloc: through fgemm_gemm_noalloc (fixed device scratch, no allocation)."""
         ta = FGEMM_OP_T if transA else FGEMM_OP_N
         tb = FGEMM_OP_T if transB else FGEMM_OP_N
         M = A.shape[1] if transA else A.shape[0]
@@ -266,6 +282,10 @@ class Handle:
         s = current_stream() if stream is None else stream
         args = (ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                 float(beta), C.data_ptr(), _ld(C), dt, epilogue, s)
+        if noalloc:
+            if plan is not None:
+                raise ValueError("fgemm_gemm_noalloc takes no plan")
+            return fgemm_gemm_noalloc(self.h, *args)
         if plan is None:
             return fgemm_gemm(self.h, *args)
         return fgemm_gemm_plan(self.h, plan, *args)

@@ -242,6 +242,29 @@ fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
                                fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
                                void* stream);
 
+/* Size of the fixed per-device scratch array behind fgemm_gemm_noalloc. */
+#define FGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The arguments, results
+ * and errors of fgemm_gemm, on the classical path only (the model's classical
+ * pick, split K included), with every scratch buffer its kernels use (the
+ * row-statistics partials of ROWSUMSQ and SWIGLU_BWD, the fp32 split-K slices) in
+ * a fixed device array of FGEMM_NOALLOC_SCRATCH_BYTES.  Each device holds its own
+ * array from the first fgemm_create on it until the process ends.  The call makes
+ * no device or host allocation: no hipMalloc or hipFree, and the handle's
+ * workspace is never used or grown; its plans are kept in a fixed table in the
+ * handle.  A call whose plan needs more scratch than the array holds returns
+ * FGEMM_ERR_WORKSPACE before anything is enqueued.  Every call on a device shares
+ * that device's array and leaves its contents there (no part of it needs to start
+ * at zero): calls that may overlap in time on one device (different streams,
+ * handles or host threads) race on it and must be serialised by the caller. */
+fgemm_status_t fgemm_gemm_noalloc(fgemm_handle_t handle, fgemm_op_t transA, fgemm_op_t transB,
+                                  int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                                  int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                                  int64_t ldc, fgemm_dtype_t dtype,
+                                  const fgemm_epilogue_t* epilogue, void* stream);
+
 /* Argument validation alone (pure; no handle, no device): the status fgemm_gemm
  * would return before enqueuing anything. */
 fgemm_status_t fgemm_check_args(fgemm_op_t transA, fgemm_op_t transB, int64_t M, int64_t N,
