@@ -186,6 +186,9 @@ def main():
     workloads = {}
     if not args.only_main:
         workloads = run_workloads(torch, h, fgemm, timer, normal, uniform, args)
+        d = workloads.get("dispatch")
+        if d:
+            d["select_frac_of_8192_headline"] = round(d["fgemm_select_uncached_us"] / (ms * 1e3), 6)
     del A, B, C
     torch.cuda.empty_cache()
 
@@ -262,6 +265,95 @@ def decode_workload(torch, h, fgemm, timer, normal, args):
             "alg_bytes_per_launch": {name: 2 * (K * N + M * K + M * N)}}
 
 
+def decode_cold(torch, h, normal, M, N, K, reps):
+    """The decode shape with the 256 MB Infinity Cache and the L2s evicted before
+    every call: a 1 GiB buffer is read (a reduction, so the evicting lines stay
+    clean and no write-back competes with the GEMM) between calls, outside the
+    timed events, so the 117 MB weight matrix streams from HBM.  Mean of per-call
+    HIP event times on the launch stream."""
+    A = normal((M, K), 3001)
+    B = normal((K, N), 3002, 0.02)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(20, reps))]
+    for _ in range(5):
+        h.gemm(A, B, C)
+    for e0, e1 in ev:
+        torch.sum(scratch, out=sink)
+        e0.record()
+        h.gemm(A, B, C)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    alg = 2.0 * (K * N + M * K + M * N)
+    r = {"ms": round(ms, 5), "hbm_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "warm": False,
+         "eviction": "1 GiB device read between calls"}
+    log(f"bf16_decode_{M}x{N}x{K}_cold: {r}")
+    del A, B, C, scratch, sink
+    return r
+
+
+def dispatch_overhead(torch, h, fgemm, normal):
+    """Host cost of the run-time decision (FalconGEMM summary, Results: the decision
+    module costs under half a percent of run time).  Host microseconds per call,
+    each the median of 9 batches of 100 calls enqueued without waiting:
+    fgemm_gemm (plan-cache hit, then the launch), fgemm_gemm_plan on the same plan
+    (the same checks and launch, no plan lookup), and fgemm_select (the model run
+    from scratch, no cache); against the GPU time of the same call."""
+    import statistics
+    M, N, K = 16, 14336, 4096
+    A = normal((M, K), 3001)
+    B = normal((K, N), 3002, 0.02)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    plan = h.select(M, N, K)
+
+    # the same ctypes marshalling for both entry points, so their difference is the
+    # library's plan lookup (argument conversion and launch are common to both)
+    L = fgemm.lib()
+    s = fgemm.current_stream()
+    common = (fgemm.FGEMM_OP_N, fgemm.FGEMM_OP_N, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N,
+              0.0, C.data_ptr(), N, fgemm.FGEMM_BF16, None, s)
+    pref = fgemm.ctypes.byref(plan)
+    call_gemm = lambda: L.fgemm_gemm(h.h, *common)
+    call_plan = lambda: L.fgemm_gemm_plan(h.h, pref, *common)
+
+    def per_call_us(fn, n=100):
+        ts = []
+        for _ in range(9):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            ts.append((time.perf_counter() - t0) / n * 1e6)
+        torch.cuda.synchronize()
+        return statistics.median(ts)
+
+    assert call_gemm() == 0 and call_plan() == 0
+    gemm_us = per_call_us(call_gemm)
+    plan_us = per_call_us(call_plan)
+    select_us = per_call_us(lambda: h.select(M, N, K), 2000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(200):
+        h.gemm(A, B, C)
+    e1.record()
+    torch.cuda.synchronize()
+    kernel_us = e0.elapsed_time(e1) / 200 * 1e3
+    lookup_us = max(gemm_us - plan_us, 0.0)
+    r = {"shape": f"bf16 {M}x{N}x{K}", "fgemm_gemm_host_us": round(gemm_us, 3),
+         "fgemm_gemm_plan_host_us": round(plan_us, 3), "plan_lookup_us": round(lookup_us, 3),
+         "fgemm_select_uncached_us": round(select_us, 3), "gpu_us_per_call": round(kernel_us, 2),
+         "lookup_frac_of_gpu_time": round(lookup_us / kernel_us, 5),
+         "select_frac_of_gpu_time": round(select_us / kernel_us, 5),
+         "select_frac_of_8192_headline": None}
+    log(f"dispatch: {r}")
+    del A, B, C
+    return r
+
+
 def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     W = {}
     reps = max(5, args.steps // 5)
@@ -299,6 +391,9 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
         K, N = 4096, 14336
         gemm_case(f"bf16_decode_{M}x{N}x{K}", M, N, K, std_b=0.02, seeds=(3001, 3002, 3003),
                   bytes_alg=2.0 * (K * N + M * K + M * N))
+        W[f"bf16_decode_{M}x{N}x{K}"]["warm"] = True
+        W[f"bf16_decode_{M}x{N}x{K}_cold"] = decode_cold(torch, h, normal, M, N, K, reps)
+    W["dispatch"] = dispatch_overhead(torch, h, fgemm, normal)
     # prefill shapes with the transform epilogues: RoPE on the projection (32 heads of
     # 128, four sequences of 4096 positions) and bias + GELU on the FFN up projection
     pos = (torch.arange(16384, device="cuda", dtype=torch.int32) % 4096).contiguous()
@@ -422,6 +517,18 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     return W
 
 
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(target_s):
     """The oracle as it stands, timed on a seeded sample of output rows of the
     headline workload, scaled to TFLOP/s of that sample."""
@@ -451,7 +558,7 @@ def cpu_baseline(target_s):
     flops = 2.0 * len(rows) * n * n
     log(f"cpu baseline: {len(rows)} rows in {dt:.2f} s on {threads} threads")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{len(rows)} seeded output rows of the bf16 8192^3 NN beta=0.5 workload "
                       f"(fp64 loop incl. decoding B), {dt:.1f} s wall"}
 

@@ -77,6 +77,7 @@ struct fgemm_handle_s {
   size_t user_ws_bytes = 0;
   void* own_ws = nullptr;
   size_t own_ws_bytes = 0;
+  int pools = 0;  // the device supports stream-ordered allocation
 };
 
 namespace {
@@ -247,7 +248,8 @@ struct WsSource {
   size_t fixed_bytes = 0;
 };
 
-fgemm_status_t ensure_workspace(fgemm_handle_t h, const WsSource& src, size_t bytes, void** ws) {
+fgemm_status_t ensure_workspace(fgemm_handle_t h, const WsSource& src, size_t bytes,
+                                hipStream_t stream, void** ws) {
   *ws = nullptr;
   if (bytes == 0) return FGEMM_OK;
   if (src.fixed) {
@@ -261,14 +263,26 @@ fgemm_status_t ensure_workspace(fgemm_handle_t h, const WsSource& src, size_t by
     return FGEMM_OK;
   }
   if (h->own_ws_bytes < bytes) {
+    // Regrowth in stream order where the device has memory pools: the old buffer is
+    // released after the work already enqueued on this stream (calls that share the
+    // workspace run on one stream, or the caller orders them), and the new one is
+    // usable from there on; no other stream of the device waits.  Without pools,
+    // the device drains first.
     if (h->own_ws) {
-      // earlier launches may still read the old buffer
-      if (hipDeviceSynchronize() != hipSuccess) return FGEMM_ERR_HIP;
-      hipFree(h->own_ws);
+      hipError_t e;
+      if (h->pools) {
+        e = hipFreeAsync(h->own_ws, stream);
+      } else {
+        e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(h->own_ws);
+      }
+      if (e != hipSuccess) return FGEMM_ERR_HIP;
       h->own_ws = nullptr;
       h->own_ws_bytes = 0;
     }
-    if (hipMalloc(&h->own_ws, bytes) != hipSuccess) {
+    const hipError_t e = h->pools ? hipMallocAsync(&h->own_ws, bytes, stream)
+                                  : hipMalloc(&h->own_ws, bytes);
+    if (e != hipSuccess) {
       (void)hipGetLastError();  // leave no error behind for the caller's next check
       h->own_ws = nullptr;
       return FGEMM_ERR_ALLOC;
@@ -326,7 +340,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     p.flags |= kFlagRowSumSq;
     parts = (int)ceil_div(c.N, tile_n_of(tile)) * waves_n_of(tile);
     void* ws;
-    fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, &ws);
+    fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, c.stream, &ws);
     if (st != FGEMM_OK) return st;
     p.ss_partial = static_cast<float*>(ws);
   }
@@ -339,7 +353,7 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
       p.rms_grad_out = 1;
       parts = (int)ceil_div(c.N, tile_n_of(tile) / 2) * waves_n_of(tile);
       void* ws;
-      fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, &ws);
+      fgemm_status_t st = ensure_workspace(h, wsrc, (size_t)parts * (size_t)c.M * 4, c.stream, &ws);
       if (st != FGEMM_OK) return st;
       p.ss_partial = static_cast<float*>(ws);
     }
@@ -375,7 +389,8 @@ fgemm_status_t run_classical(fgemm_handle_t h, const fgemm_plan_t& plan, const C
     // fp32 K slices into the workspace, then the epilogue in the finalize pass
     void* ws;
     fgemm_status_t st =
-        ensure_workspace(h, wsrc, (size_t)plan.split_k * (size_t)c.M * (size_t)c.N * 4, &ws);
+        ensure_workspace(h, wsrc, (size_t)plan.split_k * (size_t)c.M * (size_t)c.N * 4, c.stream,
+                         &ws);
     if (st != FGEMM_OK) return st;
     p.C = ws;
     p.ldc = c.N;
@@ -508,7 +523,7 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
   const size_t body = strassen_workspace(c.M, Nb, c.K, plan.depth, plan.variant);
   const size_t need = body + strassen_stats_bytes(c.M, Nb, flags);
   void* ws;
-  fgemm_status_t st = ensure_workspace(h, WsSource{}, need, &ws);
+  fgemm_status_t st = ensure_workspace(h, WsSource{}, need, c.stream, &ws);
   if (st != FGEMM_OK) return st;
   StrassenRun run{};
   run.c = &c;
@@ -683,6 +698,11 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
   if (!h) return FGEMM_ERR_ALLOC;
   h->device = device;
   h->cus = prop.multiProcessorCount;
+  if (hipDeviceGetAttribute(&h->pools, hipDeviceAttributeMemoryPoolsSupported, device) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    h->pools = 0;
+  }
   double ghz = prop.clockRate > 0 ? prop.clockRate / 1e6 : 2.4;
   model_defaults(&h->model, prop.multiProcessorCount, ghz, (double)prop.totalGlobalMem);
   *handle = h;
@@ -693,8 +713,13 @@ fgemm_status_t fgemm_destroy(fgemm_handle_t h) {
   if (!h) return FGEMM_ERR_INVALID_VALUE;
   if (h->own_ws) {
     DeviceGuard guard(h->device);
-    hipDeviceSynchronize();
-    hipFree(h->own_ws);
+    (void)hipDeviceSynchronize();
+    if (h->pools) {
+      (void)hipFreeAsync(h->own_ws, nullptr);
+      (void)hipStreamSynchronize(nullptr);
+    } else {
+      (void)hipFree(h->own_ws);
+    }
   }
   delete h;
   return FGEMM_OK;

@@ -40,6 +40,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "epilogue_ops.h"
@@ -1352,18 +1353,22 @@ static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
   const int splits = EPI == kEpiStore32 && b.k_splits > 1 ? b.k_splits : 1;
   const int64_t items = (int64_t)maxtiles * splits * b.count;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  // workgroups resident per CU, asked of the runtime once per instantiation
-  static int occ = 0;
-  if (occ <= 0) {
-    int o = 0;
+  // workgroups resident per CU, asked of the runtime once per instantiation (the
+  // kernel's resources are the same on every gfx950 device); racing first calls
+  // from several threads ask twice and store the same value
+  static std::atomic<int> occ{0};
+  int o = occ.load(std::memory_order_relaxed);
+  if (o <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &o, gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>, CFG::NT, 0) != hipSuccess ||
-        o < 1)
+        o < 1) {
+      (void)hipGetLastError();
       o = 1;
-    occ = o;
+    }
+    occ.store(o, std::memory_order_relaxed);
   }
   int64_t groups = items;
-  if (b.cus > 0 && (int64_t)b.cus * occ < groups) groups = (int64_t)b.cus * occ;
+  if (b.cus > 0 && (int64_t)b.cus * o < groups) groups = (int64_t)b.cus * o;
   hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), dim3((unsigned)groups),
                      dim3(CFG::NT), 0, s, b);
   return hipGetLastError();

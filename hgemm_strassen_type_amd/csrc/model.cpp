@@ -34,7 +34,8 @@ double overlap(double a, double b) {
 double stream_bw(const fgemm_model_t& md, int64_t blocks) {
   constexpr double kWgBytesPerSec = 50e9;
   const double hbm = md.hbm_gbps * 1e9 * md.eta_hbm;
-  const double wg = (double)blocks * kWgBytesPerSec;
+  // an empty grid (M or N = 0) still gets one workgroup's rate: its time stays finite
+  const double wg = (double)(blocks > 0 ? blocks : 1) * kWgBytesPerSec;
   return wg < hbm ? wg : hbm;
 }
 

@@ -53,9 +53,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build(force=False)
-    lib = ctypes.CDLL(_LIB)
+    # FGEMM_ORACLE_LIB: another build of the same source (the tests' sanitizer build)
+    path = os.environ.get("FGEMM_ORACLE_LIB", "")
+    if not path:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        path = _LIB
+    lib = ctypes.CDLL(path)
     i64, u16p, f64p, i64p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     lib.oracle_decode.restype = ctypes.c_double
     lib.oracle_decode.argtypes = [ctypes.c_uint16, ctypes.c_int]
