@@ -15,6 +15,9 @@ What it computes (see the header of ``oracle.c`` for the passages it follows):
 * ``strassen``   the same product through 1 or 2 levels of the Strassen (1969) or
                  Winograd 2x2 block recursion, in fp64 (identity check).
 * ``decode`` / ``encode``  exact 16-bit <-> fp64 conversions, RNE on encode.
+* ``gemm_f8``    the 8-bit GEMM A B^T on E4M3 / E5M2 values with per-tensor scales
+                 or E8M0 scales per block of 32 along K (MXFP8), same epilogue and
+                 rounding as ``gemm``; ``decode_f8`` / ``decode_e8m0`` the formats.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against hand-worked
 products, exact integer identities, invariants and library routines.
@@ -94,8 +97,21 @@ def _load():
     lib.oracle_naive_f64.argtypes = [i64, i64, i64, f64p, f64p, f64p]
     lib.oracle_s69_products.restype = ctypes.c_int
     lib.oracle_s69_products.argtypes = [i64, f64p, f64p, f64p]
+    lib.oracle_decode_f8.restype = ctypes.c_double
+    lib.oracle_decode_f8.argtypes = [ctypes.c_uint8, ctypes.c_int]
+    lib.oracle_decode_e8m0.restype = ctypes.c_double
+    lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+    u8p = ctypes.c_void_p
+    lib.oracle_gemm_f8.restype = ctypes.c_int
+    lib.oracle_gemm_f8.argtypes = [i64, i64, i64, ctypes.c_double, u8p, i64, ctypes.c_int, u8p,
+                                   i64, ctypes.c_int, ctypes.c_double, ctypes.c_double, u8p, i64,
+                                   u8p, i64, ctypes.c_double, u16p, i64, ctypes.c_int,
+                                   ctypes.c_int, u16p, i64p, i64, f64p, u16p, f64p, ctypes.c_int]
     _lib = lib
     return lib
+
+
+E4M3, E5M2 = 0, 1   # OCP 8-bit float formats (values); E8M0 is the MX block scale
 
 
 def _ptr(a):
@@ -288,3 +304,63 @@ def rel_fro(x, ref) -> float:
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((x - ref).ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("8-bit inputs are passed as their uint8 bit patterns")
+    return a
+
+
+def decode_f8(bits: np.ndarray, fmt: int) -> np.ndarray:
+    """Exact fp64 values of E4M3 or E5M2 bit patterns (OCP encodings)."""
+    bits = _u8(bits)
+    lib = _load()
+    table = np.array([lib.oracle_decode_f8(c, fmt) for c in range(256)], dtype=np.float64)
+    return table[bits]
+
+
+def decode_e8m0(bits: np.ndarray) -> np.ndarray:
+    """Exact fp64 values 2^(e-127) of E8M0 scale bytes (255 is NaN)."""
+    bits = _u8(bits)
+    lib = _load()
+    table = np.array([lib.oracle_decode_e8m0(c) for c in range(256)], dtype=np.float64)
+    return table[bits]
+
+
+def gemm_f8(A, B, *, fmt_a=E4M3, fmt_b=E4M3, scale_a=1.0, scale_b=1.0, mx_a=None, mx_b=None,
+            alpha=1.0, beta=0.0, C=None, dtype=BF16, epi=0, bias=None, rows=None, threads=None):
+    """Reference 8-bit GEMM: A (M x K) and B (N x K), uint8 bit patterns of E4M3 or
+    E5M2, both K-contiguous (the product is A B^T).  Each value counts as s * q
+    with s the per-tensor scale, or, when mx_a / mx_b are given (uint8 E8M0 arrays
+    of shape [rows][K/32]), its block's scale.  Returns (D, Q, ss) for the selected
+    rows as gemm() does; epilogues BIAS and ROWSUMSQ."""
+    A, B = _u8(A), _u8(B)
+    M, K = A.shape
+    N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = rows.size
+    if beta != 0.0:
+        C = _u16(C)
+    else:
+        C = None
+    if bias is not None:
+        bias = _u16(bias)
+    mx_a = None if mx_a is None else _u8(mx_a)
+    mx_b = None if mx_b is None else _u8(mx_b)
+    D = np.empty((nrows, N), dtype=np.float64)
+    Q = np.empty((nrows, N), dtype=np.uint16)
+    ss = np.empty(nrows, dtype=np.float64) if epi & EPI_ROWSUMSQ else None
+    rc = _load().oracle_gemm_f8(M, N, K, float(alpha), _ptr(A), A.shape[1], fmt_a, _ptr(B),
+                                B.shape[1], fmt_b, float(scale_a), float(scale_b), _ptr(mx_a),
+                                0 if mx_a is None else mx_a.shape[1], _ptr(mx_b),
+                                0 if mx_b is None else mx_b.shape[1], float(beta), _ptr(C),
+                                0 if C is None else C.shape[1], dtype, epi, _ptr(bias),
+                                _ptr(rows), nrows, _ptr(D), _ptr(Q), _ptr(ss),
+                                threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_f8 rejected its arguments")
+    return D, Q, ss

@@ -606,3 +606,140 @@ int oracle_s69_products(int64_t n, const double* A, const double* B, double* Mou
     free(L.p); free(R.p); free(tmp.p);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * 8-bit floating point (CS336 Lecture 05 notes, Page 27: FP8 E4M3 = 1 sign, 4
+ * exponent, 3 mantissa bits; E5M2 = 1 sign, 5 exponent, 2 mantissa bits; a value
+ * is stored as q = cast(x / s) and used as s * q; MXFP8 keeps one E8M0 scale per
+ * block of 32 values).  The encodings are the OCP 8-bit formats:
+ *   E4M3: bias 7, subnormals at exponent field 0, no infinities; S.1111.111 is NaN,
+ *         so the largest finite value is 1.75 * 2^8 = 448.
+ *   E5M2: bias 15, IEEE-style: exponent field 31 is infinity (fraction 0) or NaN.
+ *   E8M0: an unsigned power of two, 2^(e - 127); e = 255 is NaN.
+ * ------------------------------------------------------------------------- */
+#define OR_E4M3 0
+#define OR_E5M2 1
+
+double oracle_decode_f8(uint8_t h, int fmt) {
+    int sign = (h >> 7) & 1;
+    int ebits = fmt == OR_E4M3 ? 4 : 5;
+    int fbits = fmt == OR_E4M3 ? 3 : 2;
+    int bias = fmt == OR_E4M3 ? 7 : 15;
+    int emax = (1 << ebits) - 1;
+    int e = (h >> fbits) & emax;
+    int f = h & ((1 << fbits) - 1);
+    double v;
+    if (fmt == OR_E4M3 && e == emax && f == (1 << fbits) - 1) {
+        v = NAN;                                   /* the only E4M3 NaN pattern */
+    } else if (fmt == OR_E5M2 && e == emax) {
+        v = f ? NAN : INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)f, 1 - bias - fbits);    /* subnormal */
+    } else {
+        v = ldexp((double)((1 << fbits) | f), e - bias - fbits);
+    }
+    return sign ? -v : v;
+}
+
+double oracle_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+typedef struct {
+    int64_t K, N;
+    const double* Ad;     /* decoded, scaled rows of A: nrows x K */
+    const double* Bd;     /* decoded, scaled op(B): K x N */
+    double* H;            /* nrows x N */
+    int64_t r0, r1;
+} f8_job_t;
+
+static void* f8_worker(void* p) {
+    f8_job_t* J = (f8_job_t*)p;
+    int64_t K = J->K, N = J->N;
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        const double* arow = J->Ad + r * K;
+        double* hrow = J->H + r * N;
+        for (int64_t j = 0; j < N; ++j) hrow[j] = 0.0;
+        for (int64_t jb = 0; jb < N; jb += OR_JB) {   /* ascending k per element */
+            int64_t je = jb + OR_JB < N ? jb + OR_JB : N;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = arow[k];
+                const double* brow = J->Bd + k * N;
+                for (int64_t j = jb; j < je; ++j) hrow[j] += a * brow[j];
+            }
+        }
+    }
+    return NULL;
+}
+
+/*
+ * oracle_gemm_f8: the 8-bit GEMM, all in fp64 from the exact 8-bit values.
+ *   A is M x K row-major (lda), B is N x K row-major (ldb): op(B) = B^T, both
+ *   operands K-contiguous, as the quantized layouts of the notes' Page 27-28 keep
+ *   them.  Each operand value is used as s * q (Page 27):
+ *     s = the per-tensor scale (scale_a, scale_b) when the block-scale array is
+ *         NULL, else the E8M0 scale of the value's block of 32 along K:
+ *         sA(i,k) = mxA[i * ldmxA + k / 32], sB(j,k) = mxB[j * ldmxB + k / 32].
+ *   D[i][j] = alpha * sum_k sA(i,k) qA[i][k] * sB(j,k) qB[j][k]
+ *             + beta * C_in[i][j] + bias[j]          (k ascending)
+ *   Q = RNE of D to the 16-bit output type; ss[r] = sum_j Q^2 with ROWSUMSQ.
+ *   Outputs for the selected rows as in oracle_gemm.  Returns -1 on bad arguments.
+ */
+int oracle_gemm_f8(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t* A,
+                   int64_t lda, int fmtA, const uint8_t* B, int64_t ldb, int fmtB,
+                   double scale_a, double scale_b, const uint8_t* mxA, int64_t ldmxA,
+                   const uint8_t* mxB, int64_t ldmxB, double beta, const uint16_t* Cin,
+                   int64_t ldc, int dtype, int epi, const uint16_t* bias, const int64_t* rows,
+                   int64_t nrows, double* D, uint16_t* Q, double* ss, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || nrows < 0) return -1;
+    if ((fmtA != OR_E4M3 && fmtA != OR_E5M2) || (fmtB != OR_E4M3 && fmtB != OR_E5M2)) return -1;
+    if ((mxA || mxB) && K % 32) return -1;
+    if (epi & ~(OR_EPI_BIAS | OR_EPI_ROWSUMSQ)) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    double* Ad = (double*)malloc(sizeof(double) * (nrows * K > 0 ? nrows * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (K * N > 0 ? K * N : 1));
+    double* H = (double*)malloc(sizeof(double) * (nrows * N > 0 ? nrows * N : 1));
+    if (!Ad || !Bd || !H) { free(Ad); free(Bd); free(H); return -1; }
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t i = rows[r];
+            const double s = mxA ? oracle_decode_e8m0(mxA[i * ldmxA + k / 32]) : scale_a;
+            Ad[r * K + k] = s * oracle_decode_f8(A[i * lda + k], fmtA);
+        }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) {
+            const double s = mxB ? oracle_decode_e8m0(mxB[j * ldmxB + k / 32]) : scale_b;
+            Bd[k * N + j] = s * oracle_decode_f8(B[j * ldb + k], fmtB);
+        }
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    f8_job_t jobs[256];
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    int launched = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t r0 = t * per, r1 = r0 + per < nrows ? r0 + per : nrows;
+        if (r0 >= r1) break;
+        f8_job_t j = {K, N, Ad, Bd, H, r0, r1};
+        jobs[t] = j;
+        pthread_create(&th[t], NULL, f8_worker, &jobs[t]);
+        ++launched;
+    }
+    for (int t = 0; t < launched; ++t) pthread_join(th[t], NULL);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        double sum_sq = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double d = alpha * H[r * N + j];
+            if (beta != 0.0) d += beta * oracle_decode(Cin[i * ldc + j], dtype);
+            if (epi & OR_EPI_BIAS) d += oracle_decode(bias[j], dtype);
+            D[r * N + j] = d;
+            uint16_t q = oracle_encode(d, dtype);
+            Q[r * N + j] = q;
+            double w = oracle_decode(q, dtype);
+            sum_sq += w * w;
+        }
+        if ((epi & OR_EPI_ROWSUMSQ) && ss) ss[r] = sum_sq;
+    }
+    free(Ad); free(Bd); free(H);
+    return 0;
+}

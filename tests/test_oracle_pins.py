@@ -549,3 +549,104 @@ def test_rms_bwd_closed_forms():
     D, _ = oracle.rms_bwd(Z, B, X, rms_ss=ss, rgrad=rg, rms_n=N, rms_eps=0.0, dtype=BF16)
     c = -(ss / N) ** -1.5 * rg / N
     assert np.allclose(D, c[:, None] * oracle.decode(X, BF16), rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- 8-bit formats (FP8, MXFP8)
+def test_f8_decode_matches_torch_on_every_code():
+    """Both OCP 8-bit formats, all 256 codes, against torch's float8 dtypes (the
+    library's own decoding): E4M3 (no infinities, one NaN pattern per sign, largest
+    finite 448) and E5M2 (IEEE-style infinities and NaNs, largest finite 57344)."""
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes)
+    for fmt, tdt in ((oracle.E4M3, torch.float8_e4m3fn), (oracle.E5M2, torch.float8_e5m2)):
+        ours = oracle.decode_f8(codes, fmt)
+        ref = t.view(tdt).to(torch.float64).numpy()
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(ours), nan), fmt
+        assert np.array_equal(ours[~nan], ref[~nan]), fmt
+    e4 = oracle.decode_f8(codes, oracle.E4M3)
+    assert e4[0x7E] == 448.0 and np.isnan(e4[0x7F]) and np.isnan(e4[0xFF])
+    assert e4[0x01] == 2.0 ** -9 and e4[0x08] == 2.0 ** -6      # smallest subnormal, normal
+    assert np.isnan(e4).sum() == 2
+    e5 = oracle.decode_f8(codes, oracle.E5M2)
+    assert e5[0x7B] == 57344.0 and np.isinf(e5[0x7C]) and np.isinf(e5[0xFC])
+    assert e5[0x01] == 2.0 ** -16 and e5[0x04] == 2.0 ** -14
+    assert np.isnan(e5).sum() == 6
+    # E8M0 block scales: 2^(e-127), e = 255 NaN
+    s = oracle.decode_e8m0(codes)
+    assert np.array_equal(s[:255], np.ldexp(1.0, np.arange(255) - 127)) and np.isnan(s[255])
+    assert s[127] == 1.0
+
+
+def _f8_ints(shape, seed, lo=-4, hi=4, fmt=0):
+    """Integers in [lo, hi] as 8-bit codes (exactly representable in both formats)."""
+    v = np.random.default_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+    tdt = torch.float8_e4m3fn if fmt == oracle.E4M3 else torch.float8_e5m2
+    return torch.from_numpy(v).to(tdt).view(torch.uint8).numpy()
+
+
+def test_f8_gemm_exact_on_integers_and_scales():
+    """Small integers are exact in both 8-bit formats; the product A B^T is then the
+    integer product (numpy int64), scaled exactly by power-of-two per-tensor scales,
+    and rounded exactly to bf16 where it fits (|D| <= 256)."""
+    M, N, K = 24, 40, 64
+    for fa, fb in ((oracle.E4M3, oracle.E4M3), (oracle.E5M2, oracle.E4M3), (oracle.E4M3, oracle.E5M2)):
+        A, B = _f8_ints((M, K), 31, -2, 2, fa), _f8_ints((N, K), 32, -2, 2, fb)
+        Ai = oracle.decode_f8(A, fa).astype(np.int64)
+        Bi = oracle.decode_f8(B, fb).astype(np.int64)
+        D, Q, _ = oracle.gemm_f8(A, B, fmt_a=fa, fmt_b=fb)
+        exact = (Ai @ Bi.T).astype(np.float64)
+        assert np.array_equal(D, exact)
+        assert np.abs(exact).max() <= 256 and np.array_equal(oracle.decode(Q, BF16), exact)
+        D2, _, _ = oracle.gemm_f8(A, B, fmt_a=fa, fmt_b=fb, scale_a=0.25, scale_b=8.0, alpha=0.5)
+        assert np.array_equal(D2, exact)          # 0.25 * 8 * 0.5 = 1
+        D3, _, _ = oracle.gemm_f8(A, B, fmt_a=fa, fmt_b=fb, scale_a=2.0 ** -70, scale_b=2.0 ** 3)
+        assert np.array_equal(D3, exact * 2.0 ** -67)
+
+
+def test_f8_gemm_epilogue_and_rows():
+    """alpha, beta*C and bias in the same order as the 16-bit oracle, the written
+    rows' sums of squares, and row sampling equal to the full result."""
+    M, N, K = 33, 48, 96
+    A = _f8_ints((M, K), 41, -3, 3)
+    B = _f8_ints((N, K), 42, -3, 3)
+    C = inputs.normal((M, N), 43, BF16)
+    bias = inputs.normal((N,), 44, BF16)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    D, Q, ss = oracle.gemm_f8(A, B, alpha=0.75, beta=0.5, C=C, bias=bias, epi=flags)
+    h = oracle.decode_f8(A, 0) @ oracle.decode_f8(B, 0).T
+    ref = 0.75 * h + 0.5 * oracle.decode(C, BF16) + oracle.decode(bias, BF16)[None, :]
+    assert np.array_equal(D, ref)
+    q = oracle.decode(Q, BF16)
+    assert np.array_equal(ss, np.sum(q * q, axis=1))
+    rows = np.array([0, 7, 32])
+    D2, Q2, ss2 = oracle.gemm_f8(A, B, alpha=0.75, beta=0.5, C=C, bias=bias, epi=flags, rows=rows)
+    assert np.array_equal(D2, D[rows]) and np.array_equal(Q2, Q[rows]) and np.array_equal(ss2, ss[rows])
+
+
+def test_mx_block_scales():
+    """MXFP8: one E8M0 scale per 32 values along K.  Scales of 127 (2^0) give the
+    unscaled product; a block scaled by 2^(e-127) contributes exactly that multiple;
+    a brute-force sum over blocks on a tiny case agrees exactly."""
+    M, N, K = 8, 12, 128
+    A = _f8_ints((M, K), 51, -3, 3)
+    B = _f8_ints((N, K), 52, -3, 3)
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    D0, _, _ = oracle.gemm_f8(A, B)
+    D1, _, _ = oracle.gemm_f8(A, B, mx_a=ones_a, mx_b=ones_b)
+    assert np.array_equal(D0, D1)
+    rng = np.random.default_rng(53)
+    sa = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    D, _, _ = oracle.gemm_f8(A, B, mx_a=sa, mx_b=sb)
+    a, b = oracle.decode_f8(A, 0), oracle.decode_f8(B, 0)
+    ref = np.zeros((M, N))
+    for blk in range(K // 32):
+        ks = slice(32 * blk, 32 * blk + 32)
+        ref += (np.ldexp(1.0, sa[:, blk].astype(int) - 127)[:, None] *
+                np.ldexp(1.0, sb[:, blk].astype(int) - 127)[None, :] * (a[:, ks] @ b[:, ks].T))
+    assert np.array_equal(D, ref)
+    # K not a multiple of the block is refused
+    with pytest.raises(ValueError):
+        oracle.gemm_f8(A[:, :40], B[:, :40], mx_a=sa[:, :2], mx_b=sb[:, :2])
