@@ -15,7 +15,8 @@ The same JSON line carries
                 null when the kernel sources changed after those counters;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (a seeded subset of output rows), with the threads it used;
-  workloads     the other shapes: 4096^3 and TN layouts, 8192^3 on fp16 inputs, LLM projection/FFN and
+  workloads     the other shapes: 4096^3 and TN layouts, 8192^3 on fp16 inputs, the 8-bit
+                (FP8 E4M3, per-tensor scales) GEMM at 8192^3 and the LLM shapes, LLM projection/FFN and
                 decode shapes (decode as HBM GB/s), the projection with RoPE and the
                 FFN up projection with bias + GELU, the fused two-GEMM chain (also on
                 the Strassen path), and
@@ -77,6 +78,8 @@ def parse():
     ap.add_argument("--only-decode", action="store_true",
                     help="time the 16x14336x4096 decode shape only and print its kernel's "
                          "algorithmic bytes (for profiler runs of the decode kernel)")
+    ap.add_argument("--only-f8", action="store_true",
+                    help="time the 8-bit (FP8 E4M3) workloads only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (byte-counter calibration)")
     return ap.parse_args()
@@ -155,6 +158,9 @@ def main():
         return
     if args.only_decode:
         print(json.dumps(decode_workload(torch, h, fgemm, timer, normal, args)), flush=True)
+        return
+    if args.only_f8:
+        print(json.dumps(f8_workloads(torch, h, fgemm, timer, max(5, args.steps))), flush=True)
         return
 
     # ---------------------------------------------------------------- headline
@@ -265,6 +271,37 @@ def decode_workload(torch, h, fgemm, timer, normal, args):
             "alg_bytes_per_launch": {name: 2 * (K * N + M * K + M * N)}}
 
 
+F8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+
+
+def f8_workloads(torch, h, fgemm, timer, reps):
+    """fgemm_gemm_f8 on E4M3 activations N(0,1) and weights N(0,0.02), each stored
+    with a per-tensor power-of-two scale, A M x K and B N x K (K-contiguous), bf16
+    output, beta 0: 8192^3 and the 16384-token LLM shapes, against the dense fp8
+    MFMA peak."""
+    gen = torch.Generator(device="cuda")
+    out = {}
+
+    def codes(shape, seed, std):
+        gen.manual_seed(seed)
+        x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std
+        scale = 2.0 ** float(torch.ceil(torch.log2(x.abs().max() / 448.0)))
+        return (x / scale).to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+    for (M, N, K) in [(8192, 8192, 8192), (16384, 4096, 4096), (16384, 14336, 4096)]:
+        A, sa = codes((M, K), 6001, 1.0)
+        B, sb = codes((N, K), 6002, 0.02)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ms = timer.time(lambda: h.gemm_f8(A, B, C, scale_a=sa, scale_b=sb), reps, 3, WARM_MS)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        r = {"ms": round(ms, 5), "tflops": round(tf, 2), "f8_peak_frac": round(tf / F8_PEAK_TFLOPS, 4),
+             "format": "E4M3 x E4M3, per-tensor scales, bf16 out"}
+        out[f"f8_e4m3_{M}x{N}x{K}"] = r
+        log(f"f8_e4m3_{M}x{N}x{K}: {r}")
+        del A, B, C
+    return out
+
+
 def decode_cold(torch, h, normal, M, N, K, reps):
     """The decode shape with the 256 MB Infinity Cache and the L2s evicted before
     every call: a 1 GiB buffer is read (a reduction, so the evicting lines stay
@@ -281,7 +318,7 @@ def decode_cold(torch, h, normal, M, N, K, reps):
     for _ in range(5):
         h.gemm(A, B, C)
     for e0, e1 in ev:
-        torch.sum(scratch, out=sink)
+        torch.sum(scratch, dim=0, out=sink)
         e0.record()
         h.gemm(A, B, C)
         e1.record()
@@ -407,6 +444,9 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
               epilogue=fgemm.make_epilogue(fgemm.FGEMM_EPI_ACT | fgemm.FGEMM_EPI_BIAS,
                                            bias=bias.data_ptr(), act=fgemm.FGEMM_ACT_GELU_TANH))
     del pos, bias
+
+    # 8-bit inputs (FP8 with per-tensor scales): both operands K-contiguous, bf16 out
+    W.update(f8_workloads(torch, h, fgemm, timer, reps))
 
     # fused chain: GEMM1 + row sums of squares, GEMM2 + RMS scale + SwiGLU
     Mc, Hc, Fc = 8192, 4096, 11008

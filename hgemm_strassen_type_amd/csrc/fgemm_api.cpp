@@ -877,4 +877,79 @@ fgemm_status_t fgemm_gemm_noalloc(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb
   return execute(h, slot.plan, c, wsrc);
 }
 
+fgemm_status_t fgemm_gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                             const void* A, int64_t lda, fgemm_f8_format_t a_format,
+                             float scale_a, const void* B, int64_t ldb,
+                             fgemm_f8_format_t b_format, float scale_b, float beta, void* C,
+                             int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
+                             void* stream) {
+  if (!h) return FGEMM_ERR_INVALID_VALUE;
+  if ((a_format != FGEMM_E4M3 && a_format != FGEMM_E5M2) ||
+      (b_format != FGEMM_E4M3 && b_format != FGEMM_E5M2))
+    return FGEMM_ERR_INVALID_VALUE;
+  if (dtype != FGEMM_F16 && dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
+  if (M > INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX) return FGEMM_ERR_NOT_SUPPORTED;
+  const uint32_t flags = epi_flags(epi);
+  if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ | FGEMM_EPI_RMS_SWIGLU |
+                          FGEMM_EPI_ACT | FGEMM_EPI_ROPE | FGEMM_EPI_SWIGLU_BWD |
+                          FGEMM_EPI_RMS_BWD))
+    return FGEMM_ERR_INVALID_VALUE;
+  if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ)) return FGEMM_ERR_NOT_SUPPORTED;
+  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
+    return FGEMM_ERR_INVALID_VALUE;
+  const bool any_out = M > 0 && N > 0;
+  if (any_out && K > 0 && (A == nullptr || B == nullptr)) return FGEMM_ERR_INVALID_VALUE;
+  if (any_out && C == nullptr) return FGEMM_ERR_INVALID_VALUE;
+  if ((flags & FGEMM_EPI_BIAS) && any_out && epi->bias == nullptr) return FGEMM_ERR_INVALID_VALUE;
+  if ((flags & FGEMM_EPI_ROWSUMSQ) && any_out && epi->rowsumsq == nullptr)
+    return FGEMM_ERR_INVALID_VALUE;
+  if (!isfinite(scale_a) || !isfinite(scale_b) || !isfinite(alpha)) return FGEMM_ERR_INVALID_VALUE;
+  // whole 128-deep phases, 16-byte rows and pointers: the kernel has no K tail path
+  if (K % 128 || lda % 16 || ldb % 16 || ldc % 8 || !aligned16(A) || !aligned16(B) ||
+      !aligned16(C))
+    return FGEMM_ERR_NOT_SUPPORTED;
+  // the tensor scales enter through alpha, formed in fp32: it must stay a normal value
+  const double f = (double)alpha * (double)scale_a * (double)scale_b;
+  if (f != 0.0 && (fabs(f) < 1.1754943508222875e-38 || fabs(f) > 3.4028234663852886e38))
+    return FGEMM_ERR_NOT_SUPPORTED;
+  if (!any_out) return FGEMM_OK;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return FGEMM_ERR_HIP;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  GemmBatch b{};
+  b.count = 1;
+  b.cus = h->cus;
+  GemmProblem& p = b.p[0];
+  // byte pairs: the kernel addresses both operands in 16-bit units
+  p.A = A; p.B = B; p.C = C; p.Cin = C;
+  p.lda = lda / 2; p.ldb = ldb / 2; p.ldc = ldc;
+  p.M = (int)M; p.N = (int)N; p.K = (int)(K / 2);
+  p.alpha = (float)f;
+  p.beta = beta;
+  p.flags = beta != 0.f ? kFlagBeta : 0u;
+  if (flags & FGEMM_EPI_BIAS) { p.flags |= kFlagBias; p.bias = epi->bias; }
+  int parts = 0;
+  if (flags & FGEMM_EPI_ROWSUMSQ) {
+    // one partial per (128-column tile, wave column) and row
+    parts = (int)ceil_div(N, 128) * 2;
+    void* ws;
+    fgemm_status_t s = ensure_workspace(h, WsSource{}, (size_t)parts * (size_t)M * 4, st, &ws);
+    if (s != FGEMM_OK) return s;
+    p.flags |= kFlagRowSumSq;
+    p.ss_partial = static_cast<float*>(ws);
+  }
+  KernelKey k{};
+  k.a_kcontig = 1;
+  k.b_kcontig = 1;
+  k.dtype = f8_code((int)a_format, (int)b_format);
+  k.epi = kEpiStore16;
+  k.vec = 1;
+  k.odt = dtype == FGEMM_BF16 ? kBF16 : kF16;
+  if (launch_gemm_f8(k, b, st) != hipSuccess) return FGEMM_ERR_HIP;
+  if (parts && launch_rowsumsq_reduce(p.ss_partial, parts, (int)M, epi->rowsumsq, st) != hipSuccess)
+    return FGEMM_ERR_HIP;
+  return FGEMM_OK;
+}
+
 }  // extern "C"

@@ -52,6 +52,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 // Native vectors, not HIP's uint4/uint2 structs: struct copies are lowered through
 // private memory and lose their place in the schedule.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -184,9 +185,20 @@ __device__ __forceinline__ v4u load8_checked(const uint16_t* p, int n, bool vec)
   return v4u{w[0], w[1], w[2], w[3]};
 }
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+// DT is the MFMA input type: kF16 or kBF16, or an 8-bit pair code f8_code(fa, fb)
+// (operands stored as bytes and addressed here as pairs of bytes, i.e. in 16-bit
+// units: BK = 64 units is 128 8-bit values).  ODT is the 16-bit output type.
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 struct GemmTile {
   static constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
+  // 8-bit inputs: one v_mfma_scale_f32_16x16x128_f8f6f4 per 128 k (64 units), fed
+  // with 32 consecutive bytes of one row per lane, i.e. two 16-byte chunks (FC)
+  static constexpr bool F8 = DT >= kF8Base;
+  static constexpr int FC = F8 ? 2 : 1;
+  static constexpr int STEPS = F8 ? CFG::BK / 64 : CFG::STEPS;
+  static_assert(!F8 || (AK && BKC && CFG::MI == 16 && CFG::BK == 64 && EPI == kEpiStore16),
+                "8-bit inputs: K-contiguous operands, 16x16 MFMA blocks, one k-step a phase, "
+                "the 16-bit store epilogue");
   // gate/up column pairs: the SwiGLU epilogue and its backward
   static constexpr bool SWIGLU = EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd;
   using Acc = typename CFG::AccT;
@@ -386,8 +398,8 @@ struct GemmTile {
 
   // ============================================================ fragments
   struct Frags {
-    v4u a[CFG::FM];
-    v4u b[CFG::FN];
+    v4u a[CFG::FM][FC];
+    v4u b[CFG::FN][FC];
   };
 
   // Per-lane LDS byte offsets of the fragments at MFMA step 0 (stage-relative).
@@ -409,7 +421,8 @@ struct GemmTile {
       constexpr int MI = CFG::MI;
       if (KCONTIG) {
         int r = wbase + f * MI + lane % MI;
-        out[f] = base_off + r * (BK * 2) + (((lane / MI) ^ swz_k<BK>(r)) << 4);
+        const int c = F8 ? 2 * (lane / MI) : lane / MI;  // F8: chunk 2g; 2g+1 is ^16 bytes
+        out[f] = base_off + r * (BK * 2) + ((c ^ swz_k<BK>(r)) << 4);
       } else {
         // 16-lane group g: k slot g / (MI/16), columns 16 * (g % (MI/16)) ..
         int g = lane >> 4, j = lane & 15;
@@ -456,16 +469,32 @@ struct GemmTile {
                                                     int s, Frags& fr) {
 #pragma unroll
     for (int f = 0; f < CFG::FM; ++f)
-      fr.a[f] = read_frag<AK, BM>(stage, step_addr<AK, BM>(fa.a[f], s));
+#pragma unroll
+      for (int p = 0; p < FC; ++p)
+        fr.a[f][p] = read_frag<AK, BM>(stage, step_addr<AK, BM>(fa.a[f], s) ^ (16 * p));
 #pragma unroll
     for (int f = 0; f < CFG::FN; ++f)
-      fr.b[f] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s));
+#pragma unroll
+      for (int p = 0; p < FC; ++p)
+        fr.b[f][p] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s) ^ (16 * p));
   }
 
   // One MFMA: the B fragment first, so that a lane's accumulators are consecutive
   // columns of one output row.
-  __device__ __forceinline__ static Acc mfma(const v4u& b, const v4u& a, const Acc& c) {
-    if constexpr (CFG::MI == 32) {
+  __device__ __forceinline__ static Acc mfma(const v4u (&bf)[FC], const v4u (&af)[FC],
+                                             const Acc& c) {
+    const v4u& b = bf[0];
+    const v4u& a = af[0];
+    if constexpr (F8) {
+      // 16x16x128 on 8-bit codes; unit block scales (E8M0 127 = 2^0): the tensor
+      // scales are applied in the epilogue through alpha
+      constexpr int FA = (DT - kF8Base) >> 1, FB = (DT - kF8Base) & 1;
+      const v8i bv = {(int)bf[0].x, (int)bf[0].y, (int)bf[0].z, (int)bf[0].w,
+                      (int)bf[FC - 1].x, (int)bf[FC - 1].y, (int)bf[FC - 1].z, (int)bf[FC - 1].w};
+      const v8i av = {(int)af[0].x, (int)af[0].y, (int)af[0].z, (int)af[0].w,
+                      (int)af[FC - 1].x, (int)af[FC - 1].y, (int)af[FC - 1].z, (int)af[FC - 1].w};
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, FB, FA, 0, 127, 0, 127);
+    } else if constexpr (CFG::MI == 32) {
       if constexpr (DT == kBF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
                                                        __builtin_bit_cast(bf16x8_t, a), c, 0, 0, 0);
@@ -499,10 +528,10 @@ struct GemmTile {
     }
   }
   static constexpr int kMfmaPerStep = CFG::FM * CFG::FN;
-  static constexpr int kReadsPerStep = CFG::FM * (AK ? 1 : 2) + CFG::FN * (BKC ? 1 : 2);
+  static constexpr int kReadsPerStep = CFG::FM * (AK ? FC : 2) + CFG::FN * (BKC ? FC : 2);
 
   // ---- step 0 with the phase's direct loads slotted between its MFMAs
-  static constexpr int kRA = AK ? 1 : 2, kRB = BKC ? 1 : 2;  // read instructions a fragment
+  static constexpr int kRA = AK ? FC : 2, kRB = BKC ? FC : 2;  // read instructions a fragment
   static constexpr int kLoadsPerPhase = CFG::QAW + CFG::QBW;
 
   // Read instruction r of step s into `next`: A fragments first, then B.
@@ -513,26 +542,26 @@ struct GemmTile {
       constexpr int f = R / kRA, part = R % kRA;
       const int addr = step_addr<AK, BM>(fa.a[f], s);
       if constexpr (AK) {
-        next.a[f] = *reinterpret_cast<const v4u*>(cur + addr);
+        next.a[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (16 * part)));
       } else {
         v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BM * 2)));
         v2u t2 = __builtin_bit_cast(v2u, t);
-        if (part == 0) { next.a[f].x = t2.x; next.a[f].y = t2.y; }
-        else { next.a[f].z = t2.x; next.a[f].w = t2.y; }
+        if (part == 0) { next.a[f][0].x = t2.x; next.a[f][0].y = t2.y; }
+        else { next.a[f][0].z = t2.x; next.a[f][0].w = t2.y; }
       }
     } else {
       constexpr int r = R - CFG::FM * kRA;
       constexpr int f = r / kRB, part = r % kRB;
       const int addr = step_addr<BKC, BN>(fa.b[f], s);
       if constexpr (BKC) {
-        next.b[f] = *reinterpret_cast<const v4u*>(cur + addr);
+        next.b[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (16 * part)));
       } else {
         v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BN * 2)));
         v2u t2 = __builtin_bit_cast(v2u, t);
-        if (part == 0) { next.b[f].x = t2.x; next.b[f].y = t2.y; }
-        else { next.b[f].z = t2.x; next.b[f].w = t2.y; }
+        if (part == 0) { next.b[f][0].x = t2.x; next.b[f][0].y = t2.y; }
+        else { next.b[f][0].z = t2.x; next.b[f][0].w = t2.y; }
       }
     }
   }
@@ -654,12 +683,31 @@ struct GemmTile {
     // phases that still load a later phase, then the last S that do not: two
     // straight loop bodies
     int kt = 0;
-    for (; kt + S < ktiles; ++kt)
-      phase<true>(src, m0, smem, wave, lane, fa, la, kt0, kt, ktiles, st, chain, Pn, nx, f0, f1,
-                  acc);
-    for (; kt < ktiles; ++kt)
-      phase<false>(src, m0, smem, wave, lane, fa, la, kt0, kt, ktiles, st, chain, Pn, nx, f0, f1,
-                   acc);
+#define FGEMM_PHASE(LD, K, X, Y) \
+  phase<LD>(src, m0, smem, wave, lane, fa, la, kt0, K, ktiles, st, chain, Pn, nx, X, Y, acc)
+    if constexpr (STEPS == 1) {
+      // the two fragment sets swap roles every phase: two phases an iteration, and
+      // one copy where a loop leaves an odd phase over (a selection of sets at run
+      // time would put them in private memory)
+      for (; kt + 1 + S < ktiles; kt += 2) {
+        FGEMM_PHASE(true, kt, f0, f1);
+        FGEMM_PHASE(true, kt + 1, f1, f0);
+      }
+      if (kt + S < ktiles) {
+        FGEMM_PHASE(true, kt, f0, f1);
+        ++kt;
+        f0 = f1;
+      }
+      for (; kt + 1 < ktiles; kt += 2) {
+        FGEMM_PHASE(false, kt, f0, f1);
+        FGEMM_PHASE(false, kt + 1, f1, f0);
+      }
+      if (kt < ktiles) FGEMM_PHASE(false, kt, f0, f1);
+    } else {
+      for (; kt + S < ktiles; ++kt) FGEMM_PHASE(true, kt, f0, f1);
+      for (; kt < ktiles; ++kt) FGEMM_PHASE(false, kt, f0, f1);
+    }
+#undef FGEMM_PHASE
     FGEMM_PHASE_FENCE();
   }
 
@@ -680,12 +728,15 @@ struct GemmTile {
     const int kl = kt0 + kt + S;
     const char* ab = LD ? uniform_ptr(a_base(src, m0, kl)) : nullptr;
     const char* bb = LD ? uniform_ptr(b_base(src, kl)) : nullptr;
-    // every step but the last; the last step's fragments end up in f1
-    step(cur, fa, 0, f0, f1, acc);
-    if constexpr (CFG::STEPS == 4) {
+    // every step but the last; the last step's fragments end up in f1 (in f0 for
+    // one-step phases, whose caller swaps the two sets every phase)
+    if constexpr (STEPS >= 2) step(cur, fa, 0, f0, f1, acc);
+    if constexpr (STEPS == 4) {
       step(cur, fa, 1, f1, f0, acc);
       step(cur, fa, 2, f0, f1, acc);
     }
+    Frags& fl = STEPS == 1 ? f0 : f1;  // the last step's fragments
+    Frags& fn = STEPS == 1 ? f1 : f0;  // receives the next phase's first
     // phase kt+1 must have landed; the S-2 phases after it may still fly when
     // they have all been issued
     wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
@@ -700,19 +751,19 @@ struct GemmTile {
       if constexpr (LD) {
         // stage st is free once every wave has passed the barrier: phase kt+S goes
         // there, its loads slotted between the last step's MFMAs
-        emit0<0, true>(nxt, 0, fa, f1, f0, acc, ab, bb, la, wave, lds_addr(cur));
+        emit0<0, true>(nxt, 0, fa, fl, fn, acc, ab, bb, la, wave, lds_addr(cur));
         __builtin_amdgcn_s_setprio(0);
         FGEMM_PHASE_FENCE();
         st = st_next;
         return;
       }
-      read_frags(nxt, fa, 0, f0);
+      read_frags(nxt, fa, 0, fn);
     } else if (chain) {
       LoadAddr ln;  // computed here, where the next fragments are dead
       load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);
       issue_prologue(src_of(Pn), nx.m0, nx.kt0, nx.ktiles, wave, ln, smem);
     }
-    mfma_step(f1, acc);
+    mfma_step(fl, acc);
     interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
     __builtin_amdgcn_s_setprio(0);
     st = st_next;
@@ -737,7 +788,7 @@ struct GemmTile {
       const bool more = kt + 1 < ktiles;
       if (more) load_checked(P, m0, n0, kt0 + kt + 1, wave, lane, ra, rb);
 #pragma unroll
-      for (int s = 0; s < CFG::STEPS; ++s) {
+      for (int s = 0; s < STEPS; ++s) {
         Frags fr;
         read_frags(cur, fa, s, fr);
         mfma_step(fr, acc);
@@ -883,7 +934,7 @@ struct GemmTile {
                 for (int e = 0; e < 8; ++e) cb[e] = e < nv ? Cin[off + e] : 0;
               }
 #pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] += P.beta * to_f32<DT>(cb[e]);
+              for (int e = 0; e < 8; ++e) v[e] += P.beta * to_f32<ODT>(cb[e]);
             }
             if (use_bias) {
               // one 16-byte load where the bias vector is aligned
@@ -891,12 +942,12 @@ struct GemmTile {
                 const v4u b4 = *reinterpret_cast<const v4u*>(bias + col);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                  v[2 * e] += to_f32<DT>(b4[e] & 0xffff);
-                  v[2 * e + 1] += to_f32<DT>(b4[e] >> 16);
+                  v[2 * e] += to_f32<ODT>(b4[e] & 0xffff);
+                  v[2 * e + 1] += to_f32<ODT>(b4[e] >> 16);
                 }
               } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<DT>(bias[col + e]) : 0.f;
+                for (int e = 0; e < 8; ++e) v[e] += e < nv ? to_f32<ODT>(bias[col + e]) : 0.f;
               }
             }
             if constexpr (EPI == kEpiAct) apply_act_run<8>(P.act, v);
@@ -910,9 +961,9 @@ struct GemmTile {
             uint32_t o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              o[e] = from_f32<DT>(v[e]);
+              o[e] = from_f32<ODT>(v[e]);
               if (use_ss) {
-                const float rr = to_f32<DT>(o[e]);
+                const float rr = to_f32<ODT>(o[e]);
                 if (e < nv) ss[t] += rr * rr;
               }
             }
@@ -1008,11 +1059,11 @@ struct GemmTile {
                 for (int s = 0; s < 4; ++s) c[s] = s < nv ? Cin[off + s] : 0;
               }
 #pragma unroll
-              for (int s = 0; s < 4; ++s) v[s] += P.beta * to_f32<DT>(c[s]);
+              for (int s = 0; s < 4; ++s) v[s] += P.beta * to_f32<ODT>(c[s]);
             }
             if (use_bias) {
 #pragma unroll
-              for (int s = 0; s < 4; ++s) v[s] += s < nv ? to_f32<DT>(bias[col + s]) : 0.f;
+              for (int s = 0; s < 4; ++s) v[s] += s < nv ? to_f32<ODT>(bias[col + s]) : 0.f;
             }
             if constexpr (EPI == kEpiAct) apply_act_run<4>(P.act, v);
             if constexpr (EPI == kEpiRope) {
@@ -1024,8 +1075,8 @@ struct GemmTile {
             uint32_t o[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              o[s] = from_f32<DT>(v[s]);
-              float r = to_f32<DT>(o[s]);
+              o[s] = from_f32<ODT>(v[s]);
+              float r = to_f32<ODT>(o[s]);
               if (s < nv) ss += r * r;
             }
             if (VEC && nv >= 4) {
@@ -1073,13 +1124,13 @@ struct GemmTile {
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const float d = to_f32<DT>(dv[s]);
+              const float d = to_f32<ODT>(dv[s]);
               const float g = r * acc[i][j][4 * q + s];
               const float u = r * acc[i][j + HF][4 * q + s];
               const float sg = 1.f / (1.f + __expf(-g));
               const float dsilu = sg * (1.f + g * (1.f - sg));
-              og[s] = from_f32<DT>(d * u * dsilu * r);
-              ou[s] = from_f32<DT>(d * g * sg * r);
+              og[s] = from_f32<ODT>(d * u * dsilu * r);
+              ou[s] = from_f32<ODT>(d * g * sg * r);
               rsum += d * (dsilu * g * u + g * sg * u);
             }
             const int64_t off = (int64_t)row * P.ldc + col;
@@ -1135,7 +1186,7 @@ struct GemmTile {
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-              o[s] = from_f32<DT>(P.alpha * acc[i][j][4 * q + s] + c * to_f32<DT>(xv[s]));
+              o[s] = from_f32<ODT>(P.alpha * acc[i][j][4 * q + s] + c * to_f32<ODT>(xv[s]));
             if (v4) {
               *reinterpret_cast<v2u*>(C + off) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
             } else {
@@ -1170,11 +1221,11 @@ struct GemmTile {
             const int64_t off = (int64_t)row * P.ldc + col;
             if (use_beta) {
 #pragma unroll
-              for (int s = 0; s < 4; ++s) v[s] += s < nv ? P.beta * to_f32<DT>(Cin[off + s]) : 0.f;
+              for (int s = 0; s < 4; ++s) v[s] += s < nv ? P.beta * to_f32<ODT>(Cin[off + s]) : 0.f;
             }
             uint32_t o[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) o[s] = from_f32<DT>(v[s]);
+            for (int s = 0; s < 4; ++s) o[s] = from_f32<ODT>(v[s]);
             if (VEC && nv >= 4) {
               *reinterpret_cast<v2u*>(C + off) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
             } else {
@@ -1253,9 +1304,9 @@ __device__ __forceinline__ bool work_of(const GemmBatch& b, int item, int splits
 // Persistent: gridDim.x workgroups (at most what the device holds at once) take
 // items in rounds of gridDim.x.  A tile that follows a direct-load tile has its
 // first phases loaded during that tile's epilogue.
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch batch) {
-  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC>;
+  using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC, ODT>;
   // the rotary embedding keeps its pair rates in a table after the stages
   __shared__ __attribute__((aligned(1024)))
   uint8_t smem[CFG::SMEM + (EPI == kEpiRope ? kRopeMaxPairs * sizeof(double) : 0)];
@@ -1309,7 +1360,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
         T::loop_fast(P, cur.m0, cur.n0, smem, wave, wm, wn, lane, cur.kt0, cur.ktiles, pre,
                      chain, Pn, nx, acc);
         issued = chain;
-      } else {
+      } else if constexpr (!T::F8) {  // 8-bit calls are whole phases by contract
         T::loop_checked(P, cur.m0, cur.n0, smem, wave, wm, wn, lane, cur.kt0, cur.ktiles, acc);
       }
     }
@@ -1338,8 +1389,11 @@ using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
 using Cfg64n = TileCfg<64, 64, 2, 2, 64, 4>;
+// 8-bit inputs: 8 waves of 64x64 (acc 64 + two sets of 32-byte fragments fit two
+// waves per SIMD), phases of 128 k (48 KB), three stages
+using Cfg256x128f8 = TileCfg<256, 128, 4, 2, 64, 3, 1, 16>;
 
-template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC>
+template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
   GemmBatch b = b0;
   int maxtiles = 0;
@@ -1360,7 +1414,7 @@ static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
   int o = occ.load(std::memory_order_relaxed);
   if (o <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>, CFG::NT, 0) != hipSuccess ||
+            &o, gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC, ODT>, CFG::NT, 0) != hipSuccess ||
         o < 1) {
       (void)hipGetLastError();
       o = 1;
@@ -1369,7 +1423,7 @@ static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {
   }
   int64_t groups = items;
   if (b.cus > 0 && (int64_t)b.cus * o < groups) groups = (int64_t)b.cus * o;
-  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((gemm_mfma_kernel<CFG, DT, AK, BKC, EPI, VEC, ODT>), dim3((unsigned)groups),
                      dim3(CFG::NT), 0, s, b);
   return hipGetLastError();
 }

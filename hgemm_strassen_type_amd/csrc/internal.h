@@ -10,6 +10,10 @@ namespace fgemm {
 
 // Element types of an operand as it sits in memory.
 enum ElemType : int { kF16 = 0, kBF16 = 1 };
+// 8-bit MFMA inputs: one code for the formats of both operands, fa and fb each
+// 0 (E4M3) or 1 (E5M2), the MFMA's own format numbers.
+constexpr int kF8Base = 4;
+constexpr int f8_code(int fa, int fb) { return kF8Base + 2 * fa + fb; }
 
 // Epilogue kinds the kernel template is instantiated for.
 enum EpiKind : int {
@@ -75,6 +79,7 @@ struct KernelKey {
   int dtype;          // ElemType of the MFMA inputs and of 16-bit outputs
   int epi;            // EpiKind
   int vec;            // 1: 16-byte aligned fast path
+  int odt;            // 8-bit inputs only: ElemType of the 16-bit output
 };
 
 // One instantiation unit per (MFMA dtype, A layout, B layout); each is compiled from
@@ -84,6 +89,11 @@ struct KernelKey {
 FGEMM_INST_DECL(0, 0, 0) FGEMM_INST_DECL(0, 0, 1) FGEMM_INST_DECL(0, 1, 0) FGEMM_INST_DECL(0, 1, 1)
 FGEMM_INST_DECL(1, 0, 0) FGEMM_INST_DECL(1, 0, 1) FGEMM_INST_DECL(1, 1, 0) FGEMM_INST_DECL(1, 1, 1)
 #undef FGEMM_INST_DECL
+
+// The 8-bit kernel (K-contiguous A and B, dtype = f8_code, 256x128 tiles): one
+// launch over a batch whose problems are given in 16-bit units (K, lda and ldb
+// halved: the kernel moves byte pairs).
+hipError_t launch_gemm_f8(const KernelKey& k, const GemmBatch& b, hipStream_t s);
 
 int tile_m_of(int tile);
 int tile_n_of(int tile);

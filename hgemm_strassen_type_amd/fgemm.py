@@ -24,11 +24,13 @@ FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD, FGEMM_EPI_RMS_BWD = 8, 16, 
 FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
 FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
+FGEMM_E4M3, FGEMM_E5M2 = 0, 1
 
 # every symbol include/fgemm.h declares
 EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
            "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
-           "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_check_args", "fgemm_tile_count",
+           "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_gemm_f8", "fgemm_check_args",
+           "fgemm_tile_count",
            "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_status_string")
 
 # FGEMM_NOALLOC_SCRATCH_BYTES of fgemm.h
@@ -101,6 +103,8 @@ def lib():
                                  vp, i64, i32, epi_p, vp]),
         "fgemm_gemm_noalloc": (st, [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
                                     i64, i32, epi_p, vp]),
+        "fgemm_gemm_f8": (st, [vp, i64, i64, i64, f32, vp, i64, i32, f32, vp, i64, i32, f32, f32,
+                               vp, i64, i32, epi_p, vp]),
         "fgemm_check_args": (st, [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64, i32,
                                   epi_p]),
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
@@ -205,6 +209,16 @@ def fgemm_gemm_noalloc(handle, transA, transB, M, N, K, alpha, A, lda, B, ldb, b
     return s
 
 
+def fgemm_gemm_f8(handle, M, N, K, alpha, A, lda, a_format, scale_a, B, ldb, b_format, scale_b,
+                  beta, C, ldc, dtype, epilogue=None, stream=0, check=True) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    s = lib().fgemm_gemm_f8(handle, M, N, K, alpha, A, lda, a_format, scale_a, B, ldb, b_format,
+                            scale_b, beta, C, ldc, dtype, e, stream)
+    if check:
+        _check(s, "fgemm_gemm_f8")
+    return s
+
+
 def fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype,
                      epilogue=None) -> int:
     e = ctypes.byref(epilogue) if epilogue is not None else None
@@ -289,6 +303,17 @@ class Handle:
         if plan is None:
             return fgemm_gemm(self.h, *args)
         return fgemm_gemm_plan(self.h, plan, *args)
+
+    def gemm_f8(self, A, B, C, *, a_format=FGEMM_E4M3, b_format=FGEMM_E4M3, scale_a=1.0,
+                scale_b=1.0, alpha=1.0, beta=0.0, epilogue=None, stream=None):
+        """C = alpha * (scale_a*A) (scale_b*B)^T + beta*C on torch device tensors: A
+        (M x K) and B (N x K) hold 8-bit codes (uint8 or a float8 dtype), C is 16-bit."""
+        M, K = A.shape
+        N = B.shape[0]
+        s = current_stream() if stream is None else stream
+        return fgemm_gemm_f8(self.h, M, N, K, float(alpha), A.data_ptr(), _ld(A), a_format,
+                             float(scale_a), B.data_ptr(), _ld(B), b_format, float(scale_b),
+                             float(beta), C.data_ptr(), _ld(C), torch_dtype_code(C), epilogue, s)
 
     def select(self, M, N, K, *, transA=False, transB=False, dtype=FGEMM_BF16, epilogue=None):
         return fgemm_select(self.h, FGEMM_OP_T if transA else FGEMM_OP_N,

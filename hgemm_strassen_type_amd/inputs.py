@@ -66,3 +66,34 @@ def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
     pick = set(rng.choice(M, size=n, replace=False).tolist())
     pick.update({0, M - 1})
     return np.array(sorted(pick), dtype=np.int64)
+
+
+# ---------------------------------------------------------------- 8-bit inputs
+E4M3, E5M2 = 0, 1
+F8_MAX = {E4M3: 448.0, E5M2: 57344.0}   # largest finite values of the two formats
+
+
+def _to_f8_codes(x32: np.ndarray, fmt: int) -> np.ndarray:
+    """fp32 values -> 8-bit codes through torch's float8 conversion (RNE, values
+    already inside the format's range)."""
+    import torch
+    tdt = torch.float8_e4m3fn if fmt == E4M3 else torch.float8_e5m2
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(tdt)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def f8_integers(shape, seed: int, fmt: int, lo: int, hi: int) -> np.ndarray:
+    """Small integers in [lo, hi] as 8-bit codes (exact in both formats for |v| <= 8)."""
+    rng = np.random.default_rng(seed)
+    return _to_f8_codes(rng.integers(lo, hi + 1, size=shape).astype(np.float32), fmt)
+
+
+def f8_normal(shape, seed: int, fmt: int, std=1.0):
+    """N(0, std) values stored per-tensor-scaled as 8-bit codes: the scale is a
+    power of two that puts the largest magnitude just inside the format's range.
+    Returns (codes, scale)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape) * std
+    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    scale = 2.0 ** np.ceil(np.log2(amax / F8_MAX[fmt])) if amax > 0 else 1.0
+    return _to_f8_codes((x / scale).astype(np.float32), fmt), float(scale)

@@ -242,6 +242,33 @@ fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
                                fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
                                void* stream);
 
+/* 8-bit floating-point formats of fgemm_gemm_f8 (the OCP encodings): E4M3 is
+ * 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities, largest finite
+ * 448; E5M2 is 1 sign, 5 exponent (bias 15) and 2 mantissa bits, IEEE-style
+ * infinities and NaNs, largest finite 57344 (CS336 Lecture 05 notes, Page 27). */
+typedef enum { FGEMM_E4M3 = 0, FGEMM_E5M2 = 1 } fgemm_f8_format_t;
+
+/* 8-bit GEMM with per-tensor scales (CS336 Lecture 05 notes, Page 27: a value is
+ * stored as q = cast(x/s) and used as s*q, one fp32 scale per tensor; Page 28:
+ * transposes are quantized separately, so both operands arrive K-contiguous):
+ *   C = alpha * (scale_a * A) * (scale_b * B)^T + beta * C
+ * A is M x K row-major 8-bit codes (lda >= K bytes), B is N x K row-major (ldb >= K
+ * bytes), each in its own format; C is M x N in the 16-bit type `dtype` (ldc >= N).
+ * The products are exact and accumulate in fp32 (v_mfma_scale_f32_16x16x128_f8f6f4
+ * with unit block scales); alpha*scale_a*scale_b is formed once and applied to the
+ * fp32 sums, then beta*C and the epilogue: NONE, BIAS and ROWSUMSQ as in
+ * fgemm_gemm (others FGEMM_ERR_NOT_SUPPORTED).  Needs K % 128 == 0, lda and ldb
+ * multiples of 16, ldc a multiple of 8, 16-byte aligned A, B and C, and
+ * alpha*scale_a*scale_b zero or a normal fp32 value, else FGEMM_ERR_NOT_SUPPORTED.
+ * Pointers, streams, errors and beta = 0 as for fgemm_gemm; ROWSUMSQ partials use
+ * the handle's workspace. */
+fgemm_status_t fgemm_gemm_f8(fgemm_handle_t handle, int64_t M, int64_t N, int64_t K, float alpha,
+                             const void* A, int64_t lda, fgemm_f8_format_t a_format,
+                             float scale_a, const void* B, int64_t ldb,
+                             fgemm_f8_format_t b_format, float scale_b, float beta, void* C,
+                             int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                             void* stream);
+
 /* Size of the fixed per-device scratch array behind fgemm_gemm_noalloc. */
 #define FGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -15,6 +15,10 @@ FGEMM_STUB(0, 0, 0) FGEMM_STUB(0, 0, 1) FGEMM_STUB(0, 1, 0) FGEMM_STUB(0, 1, 1)
 FGEMM_STUB(1, 0, 0) FGEMM_STUB(1, 0, 1) FGEMM_STUB(1, 1, 0) FGEMM_STUB(1, 1, 1)
 #undef FGEMM_STUB
 
+hipError_t launch_gemm_f8(const KernelKey&, const GemmBatch&, hipStream_t) {
+  return hipErrorNoDevice;
+}
+
 hipError_t launch_rowsumsq_reduce(const float*, int, int, float*, hipStream_t) {
   return hipErrorNoDevice;
 }

@@ -18,7 +18,7 @@ OK, INVAL, NOTSUP = fgemm.FGEMM_OK, fgemm.FGEMM_ERR_INVALID_VALUE, fgemm.FGEMM_E
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "fgemm.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fgemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fgemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
