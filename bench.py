@@ -299,6 +299,28 @@ def f8_workloads(torch, h, fgemm, timer, reps):
         out[f"f8_e4m3_{M}x{N}x{K}"] = r
         log(f"f8_e4m3_{M}x{N}x{K}: {r}")
         del A, B, C
+    # MXFP8: one E8M0 scale per 32 values along K (the quantizer's per-block amax)
+    M = N = K = 8192
+
+    def mx_codes(shape, seed, std):
+        gen.manual_seed(seed)
+        x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std
+        blk = x.view(shape[0], K // 32, 32)
+        e = torch.ceil(torch.log2(blk.abs().amax(dim=2).clamp_min(1e-30) / 448.0))
+        q = (blk / torch.exp2(e)[:, :, None]).view(shape).to(torch.float8_e4m3fn)
+        scales = (e + 127).to(torch.uint8).contiguous()
+        return q.view(torch.uint8), scales
+
+    A, sA = mx_codes((M, K), 6003, 1.0)
+    B, sB = mx_codes((N, K), 6004, 0.02)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms = timer.time(lambda: h.gemm_mxf8(A, B, C, sA, sB), reps, 3, WARM_MS)
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    r = {"ms": round(ms, 5), "tflops": round(tf, 2), "f8_peak_frac": round(tf / F8_PEAK_TFLOPS, 4),
+         "format": "MXFP8: E4M3 x E4M3, E8M0 scale per 32 values, bf16 out"}
+    out[f"mxf8_e4m3_{M}x{N}x{K}"] = r
+    log(f"mxf8_e4m3_{M}x{N}x{K}: {r}")
+    del A, B, C, sA, sB
     return out
 
 

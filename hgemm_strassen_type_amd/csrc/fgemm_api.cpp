@@ -877,13 +877,30 @@ fgemm_status_t fgemm_gemm_noalloc(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb
   return execute(h, slot.plan, c, wsrc);
 }
 
-fgemm_status_t fgemm_gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
-                             const void* A, int64_t lda, fgemm_f8_format_t a_format,
-                             float scale_a, const void* B, int64_t ldb,
-                             fgemm_f8_format_t b_format, float scale_b, float beta, void* C,
-                             int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The 8-bit GEMM with per-tensor scales (mx_a == mx_b == null) or E8M0 block scales.
+fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, fgemm_f8_format_t a_format, float scale_a,
+                       const uint8_t* mx_a, int64_t ld_mxa, const void* B, int64_t ldb,
+                       fgemm_f8_format_t b_format, float scale_b, const uint8_t* mx_b,
+                       int64_t ld_mxb, float beta, void* C, int64_t ldc, fgemm_dtype_t dtype,
+                       const fgemm_epilogue_t* epi, void* stream) {
   if (!h) return FGEMM_ERR_INVALID_VALUE;
+  const bool mx = mx_a != nullptr || mx_b != nullptr;
+  if (mx) {
+    // whole 16-byte groups of 16 block scales per row (the kernel loads a group of
+    // 4 phases at a time), 16-byte aligned rows
+    const int64_t groups = (K / 32 + 15) / 16 * 16;
+    if (K > 0 && (mx_a == nullptr || mx_b == nullptr)) return FGEMM_ERR_INVALID_VALUE;
+    if (ld_mxa < (K / 32 > 1 ? K / 32 : 1) || ld_mxb < (K / 32 > 1 ? K / 32 : 1))
+      return FGEMM_ERR_INVALID_VALUE;
+    if (ld_mxa % 16 || ld_mxb % 16 || ld_mxa < groups || ld_mxb < groups || !aligned16(mx_a) ||
+        !aligned16(mx_b))
+      return FGEMM_ERR_NOT_SUPPORTED;
+  }
   if ((a_format != FGEMM_E4M3 && a_format != FGEMM_E5M2) ||
       (b_format != FGEMM_E4M3 && b_format != FGEMM_E5M2))
     return FGEMM_ERR_INVALID_VALUE;
@@ -939,10 +956,14 @@ fgemm_status_t fgemm_gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, 
     p.flags |= kFlagRowSumSq;
     p.ss_partial = static_cast<float*>(ws);
   }
+  if (mx) {
+    p.mx_a = mx_a; p.mx_b = mx_b;
+    p.ld_mxa = ld_mxa; p.ld_mxb = ld_mxb;
+  }
   KernelKey k{};
   k.a_kcontig = 1;
   k.b_kcontig = 1;
-  k.dtype = f8_code((int)a_format, (int)b_format);
+  k.dtype = f8_code((int)a_format, (int)b_format, mx ? 1 : 0);
   k.epi = kEpiStore16;
   k.vec = 1;
   k.odt = dtype == FGEMM_BF16 ? kBF16 : kF16;
@@ -950,6 +971,34 @@ fgemm_status_t fgemm_gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, 
   if (parts && launch_rowsumsq_reduce(p.ss_partial, parts, (int)M, epi->rowsumsq, st) != hipSuccess)
     return FGEMM_ERR_HIP;
   return FGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fgemm_status_t fgemm_gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                             const void* A, int64_t lda, fgemm_f8_format_t a_format,
+                             float scale_a, const void* B, int64_t ldb,
+                             fgemm_f8_format_t b_format, float scale_b, float beta, void* C,
+                             int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
+                             void* stream) {
+  return gemm_f8(h, M, N, K, alpha, A, lda, a_format, scale_a, nullptr, 0, B, ldb, b_format,
+                 scale_b, nullptr, 0, beta, C, ldc, dtype, epi, stream);
+}
+
+fgemm_status_t fgemm_gemm_mxf8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                               const void* A, int64_t lda, fgemm_f8_format_t a_format,
+                               const void* a_scales, int64_t ld_a_scales, const void* B,
+                               int64_t ldb, fgemm_f8_format_t b_format, const void* b_scales,
+                               int64_t ld_b_scales, float beta, void* C, int64_t ldc,
+                               fgemm_dtype_t dtype, const fgemm_epilogue_t* epi, void* stream) {
+  if (K > 0 && (a_scales == nullptr || b_scales == nullptr)) return FGEMM_ERR_INVALID_VALUE;
+  // K = 0 reads no scale (C = beta*C + bias): the unscaled kernel does the same
+  const uint8_t* sa = K > 0 ? static_cast<const uint8_t*>(a_scales) : nullptr;
+  const uint8_t* sb = K > 0 ? static_cast<const uint8_t*>(b_scales) : nullptr;
+  return gemm_f8(h, M, N, K, alpha, A, lda, a_format, 1.f, sa, ld_a_scales, B, ldb, b_format,
+                 1.f, sb, ld_b_scales, beta, C, ldc, dtype, epi, stream);
 }
 
 }  // extern "C"

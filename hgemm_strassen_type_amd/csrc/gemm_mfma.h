@@ -191,14 +191,32 @@ __device__ __forceinline__ v4u load8_checked(const uint16_t* p, int n, bool vec)
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 struct GemmTile {
   static constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
-  // 8-bit inputs: one v_mfma_scale_f32_16x16x128_f8f6f4 per 128 k (64 units), fed
-  // with 32 consecutive bytes of one row per lane, i.e. two 16-byte chunks (FC)
+  // 8-bit inputs: v_mfma_scale_f32_32x32x64_f8f6f4 (64 k a step) or _16x16x128
+  // (128 k), fed with two 16-byte chunks of one row per lane (FC).  The instruction
+  // takes its k as two halves: lane group g (lane / MI) holds k 16g..16g+15 of the
+  // first half in its first chunk and the same k of the second half in its second,
+  // so a lane reads chunks g and g + 2 (32x32) or g and g + 4 (16x16) of the step,
+  // CHUNK2 bytes apart, and the hardware's k order is the memory order (which the MX
+  // block scales need: block b is k 32b..32b+31, its scale in lane group b)
   static constexpr bool F8 = DT >= kF8Base;
+  // MX: one E8M0 scale per 32 values along K for every row of A and B (the 8-bit
+  // code's third bit), fed to the MFMA per lane: the lane's 32 bytes are one block
+  static constexpr bool MX = DT >= kF8Base + 4;
   static constexpr int FC = F8 ? 2 : 1;
-  static constexpr int STEPS = F8 ? CFG::BK / 64 : CFG::STEPS;
-  static_assert(!F8 || (AK && BKC && CFG::MI == 16 && CFG::BK == 64 && EPI == kEpiStore16),
-                "8-bit inputs: K-contiguous operands, 16x16 MFMA blocks, one k-step a phase, "
-                "the 16-bit store epilogue");
+  static constexpr int CHUNK2 = CFG::MI == 32 ? 32 : 64;  // F8: XOR offset of the second chunk
+  // MX scales in LDS after the stages: per group of 4 phases (16 blocks) the tile's
+  // BM + BN rows of 16 scale bytes, two groups (one read while the next arrives)
+  static constexpr int MX_OFF = CFG::SMEM;
+  static constexpr int MX_BUF = (CFG::BM + CFG::BN) * 16;
+  static constexpr int MX_SLOTS_A = CFG::BM / 64, MX_SLOTS_B = CFG::BN / 64;
+  static_assert(!MX || MX_SLOTS_A + MX_SLOTS_B <= CFG::NW, "one scale slot per wave at most");
+  // k per MFMA step in 16-bit units (8-bit: 64 or 128 values) and steps per phase
+  static constexpr int KSTEP = F8 ? (CFG::MI == 32 ? 32 : 64) : CFG::KSTEP;
+  static constexpr int STEPS = CFG::BK / KSTEP;
+  // MX: E8M0 blocks of 32 values a step covers
+  static constexpr int BPS = KSTEP / 16;
+  static_assert(!F8 || (AK && BKC && CFG::BK == 64 && EPI == kEpiStore16),
+                "8-bit inputs: K-contiguous operands, 128 k a phase, the 16-bit store epilogue");
   // gate/up column pairs: the SwiGLU epilogue and its backward
   static constexpr bool SWIGLU = EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd;
   using Acc = typename CFG::AccT;
@@ -222,6 +240,7 @@ struct GemmTile {
   struct LoadAddr {
     uint32_t a[CFG::QAW];
     uint32_t b[CFG::QBW];
+    uint32_t mx;  // MX: this wave's scale slot (row of A or B times its leading dimension)
   };
 
   // Rows and columns beyond M or N (edge tiles) are clamped onto the last valid
@@ -236,6 +255,17 @@ struct GemmTile {
     // hoisted out of the tile loop and held in registers across the main loop
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
+    if constexpr (MX) {
+      // slot w < MX_SLOTS_A: rows 64w.. of A's tile; then rows of B's (clamped)
+      la.mx = 0;
+      if (wave < MX_SLOTS_A) {
+        const int r = m0 + 64 * wave + lane;
+        la.mx = (uint32_t)((int64_t)(r < P.M ? r : P.M - 1) * P.ld_mxa);
+      } else if (wave < MX_SLOTS_A + MX_SLOTS_B) {
+        const int r = n0 + 64 * (wave - MX_SLOTS_A) + lane;
+        la.mx = (uint32_t)((int64_t)(r < P.N ? r : P.N - 1) * P.ld_mxb);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CFG::QAW; ++i) {
       int q = wave + CFG::NW * i, row, c;
@@ -272,6 +302,8 @@ struct GemmTile {
     const char* A;
     const char* B;
     int64_t lda, ldb;
+    const char* mxa;  // MX scale arrays
+    const char* mxb;
   };
   __device__ __forceinline__ static Src src_of(const GemmProblem& P) {
     Src r;
@@ -279,7 +311,21 @@ struct GemmTile {
     r.B = static_cast<const char*>(P.B);
     r.lda = P.lda;
     r.ldb = P.ldb;
+    r.mxa = static_cast<const char*>(P.mx_a);
+    r.mxb = static_cast<const char*>(P.mx_b);
     return r;
+  }
+
+  // MX: scale group g (blocks 16g..16g+15, phases 4g..4g+3) of this wave's slot
+  // into buffer g % 2.
+  __device__ __forceinline__ static void issue_scales(const Src& S, int g, int wave,
+                                                      const LoadAddr& la, uint8_t* smem) {
+    if constexpr (MX) {
+      if (wave < MX_SLOTS_A + MX_SLOTS_B) {
+        const char* base = uniform_ptr((wave < MX_SLOTS_A ? S.mxa : S.mxb) + 16 * g);
+        lds_dma(base, la.mx, lds_addr(smem + MX_OFF + (g & 1) * MX_BUF + wave * 1024));
+      }
+    }
   }
 
   // Uniform byte base of phase kt.
@@ -401,6 +447,11 @@ struct GemmTile {
     v4u a[CFG::FM][FC];
     v4u b[CFG::FN][FC];
   };
+  // MX: the E8M0 scale of the lane's block for every step and fragment of a phase
+  struct Scales {
+    uint32_t a[MX ? STEPS : 1][MX ? CFG::FM : 1];
+    uint32_t b[MX ? STEPS : 1][MX ? CFG::FN : 1];
+  };
 
   // Per-lane LDS byte offsets of the fragments at MFMA step 0 (stage-relative).
   // A lane feeds row (lane % MI) of its fragment with k slot lane / MI (8 k each).
@@ -411,6 +462,7 @@ struct GemmTile {
   struct FragAddr {
     int a[CFG::FM];
     int b[CFG::FN];
+    int sc;  // MX: the lane's scale byte within a group buffer, minus the fragment's rows
   };
 
   template <bool KCONTIG, int R, int F>
@@ -421,7 +473,7 @@ struct GemmTile {
       constexpr int MI = CFG::MI;
       if (KCONTIG) {
         int r = wbase + f * MI + lane % MI;
-        const int c = F8 ? 2 * (lane / MI) : lane / MI;  // F8: chunk 2g; 2g+1 is ^16 bytes
+        const int c = lane / MI;  // F8: chunk g; chunk g + 4 is CHUNK2 bytes away
         out[f] = base_off + r * (BK * 2) + ((c ^ swz_k<BK>(r)) << 4);
       } else {
         // 16-lane group g: k slot g / (MI/16), columns 16 * (g % (MI/16)) ..
@@ -436,6 +488,7 @@ struct GemmTile {
   __device__ __forceinline__ static void frag_addr(int wm, int wn, int lane, FragAddr& fa) {
     frag_base<AK, BM, CFG::FM>(wm * CFG::WM, lane, 0, fa.a);
     frag_base<BKC, BN, CFG::FN>(wn * CFG::WN, lane, CFG::LDS_A, fa.b);
+    fa.sc = (lane % CFG::MI) * 16 + lane / CFG::MI;
   }
 
   // Offset of step s from step 0.  K-contiguous: chunk (KSTEP/8)*s + slot, and the
@@ -447,9 +500,9 @@ struct GemmTile {
       if (s == 0) return base;
       int b = base;  // opaque: the XORed address is formed at its use, not held
       asm volatile("" : "+v"(b));
-      return b ^ (2 * CFG::KSTEP * s);
+      return b ^ (2 * KSTEP * s);
     }
-    return base + s * CFG::KSTEP * (R * 2);
+    return base + s * KSTEP * (R * 2);
   }
 
   template <bool KCONTIG, int R>
@@ -471,29 +524,54 @@ struct GemmTile {
     for (int f = 0; f < CFG::FM; ++f)
 #pragma unroll
       for (int p = 0; p < FC; ++p)
-        fr.a[f][p] = read_frag<AK, BM>(stage, step_addr<AK, BM>(fa.a[f], s) ^ (16 * p));
+        fr.a[f][p] = read_frag<AK, BM>(stage, step_addr<AK, BM>(fa.a[f], s) ^ (CHUNK2 * p));
 #pragma unroll
     for (int f = 0; f < CFG::FN; ++f)
 #pragma unroll
       for (int p = 0; p < FC; ++p)
-        fr.b[f][p] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s) ^ (16 * p));
+        fr.b[f][p] = read_frag<BKC, BN>(stage, step_addr<BKC, BN>(fa.b[f], s) ^ (CHUNK2 * p));
+  }
+
+  // MX: the scales of phase p (kt within the tile) for every step and fragment: the
+  // lane's row and block (phase p's 4 blocks follow each other in the group's 16
+  // bytes, BPS of them a step).
+  __device__ __forceinline__ static void read_scales(const uint8_t* smem, const FragAddr& fa,
+                                                     int wm, int wn, int p, Scales& sc) {
+    if constexpr (MX) {
+      const uint8_t* buf = smem + MX_OFF + ((p >> 2) & 1) * MX_BUF + (p & 3) * 4 + fa.sc;
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+        for (int i = 0; i < CFG::FM; ++i)
+          sc.a[s][i] = *(buf + s * BPS + (wm * CFG::WM + i * CFG::MI) * 16);
+#pragma unroll
+        for (int j = 0; j < CFG::FN; ++j)
+          sc.b[s][j] = *(buf + s * BPS + (CFG::BM + wn * CFG::WN + j * CFG::MI) * 16);
+      }
+    }
   }
 
   // One MFMA: the B fragment first, so that a lane's accumulators are consecutive
   // columns of one output row.
   __device__ __forceinline__ static Acc mfma(const v4u (&bf)[FC], const v4u (&af)[FC],
-                                             const Acc& c) {
+                                             const Acc& c, uint32_t scb = 127,
+                                             uint32_t sca = 127) {
     const v4u& b = bf[0];
     const v4u& a = af[0];
     if constexpr (F8) {
-      // 16x16x128 on 8-bit codes; unit block scales (E8M0 127 = 2^0): the tensor
-      // scales are applied in the epilogue through alpha
-      constexpr int FA = (DT - kF8Base) >> 1, FB = (DT - kF8Base) & 1;
+      // 8-bit codes with E8M0 block scales (127 = 2^0 without MX: the tensor scales
+      // are applied in the epilogue through alpha)
+      constexpr int FA = ((DT - kF8Base) >> 1) & 1, FB = (DT - kF8Base) & 1;
       const v8i bv = {(int)bf[0].x, (int)bf[0].y, (int)bf[0].z, (int)bf[0].w,
                       (int)bf[FC - 1].x, (int)bf[FC - 1].y, (int)bf[FC - 1].z, (int)bf[FC - 1].w};
       const v8i av = {(int)af[0].x, (int)af[0].y, (int)af[0].z, (int)af[0].w,
                       (int)af[FC - 1].x, (int)af[FC - 1].y, (int)af[FC - 1].z, (int)af[FC - 1].w};
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, FB, FA, 0, 127, 0, 127);
+      if constexpr (CFG::MI == 32)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FB, FA, 0, (int)scb, 0,
+                                                              (int)sca);
+      else
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, FB, FA, 0, (int)scb,
+                                                               0, (int)sca);
     } else if constexpr (CFG::MI == 32) {
       if constexpr (DT == kBF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
@@ -511,11 +589,23 @@ struct GemmTile {
     }
   }
 
-  __device__ __forceinline__ static void mfma_step(const Frags& fr, Acc (&acc)[CFG::FM][CFG::FN]) {
+  // MX scales of step s, fragment i of A / j of B (127 = 2^0 otherwise)
+  __device__ __forceinline__ static uint32_t sca_of(const Scales& sc, int s, int i) {
+    if constexpr (MX) return sc.a[s][i];
+    return 127u;
+  }
+  __device__ __forceinline__ static uint32_t scb_of(const Scales& sc, int s, int j) {
+    if constexpr (MX) return sc.b[s][j];
+    return 127u;
+  }
+
+  __device__ __forceinline__ static void mfma_step(const Frags& fr, const Scales& sc, int s,
+                                                   Acc (&acc)[CFG::FM][CFG::FN]) {
 #pragma unroll
     for (int i = 0; i < CFG::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < CFG::FN; ++j) acc[i][j] = mfma(fr.b[j], fr.a[i], acc[i][j]);
+      for (int j = 0; j < CFG::FN; ++j)
+        acc[i][j] = mfma(fr.b[j], fr.a[i], acc[i][j], scb_of(sc, s, j), sca_of(sc, s, i));
   }
 
   // one MFMA, then one instruction of OTHER_MASK, while both last (I counts MFMAs)
@@ -542,7 +632,7 @@ struct GemmTile {
       constexpr int f = R / kRA, part = R % kRA;
       const int addr = step_addr<AK, BM>(fa.a[f], s);
       if constexpr (AK) {
-        next.a[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (16 * part)));
+        next.a[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (CHUNK2 * part)));
       } else {
         v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BM * 2)));
@@ -555,7 +645,7 @@ struct GemmTile {
       constexpr int f = r / kRB, part = r % kRB;
       const int addr = step_addr<BKC, BN>(fa.b[f], s);
       if constexpr (BKC) {
-        next.b[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (16 * part)));
+        next.b[f][part] = *reinterpret_cast<const v4u*>(cur + (addr ^ (CHUNK2 * part)));
       } else {
         v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (v4s FGEMM_LDS*)(cur + addr + part * 4 * (BN * 2)));
@@ -585,18 +675,19 @@ struct GemmTile {
   // the order.  Leftover reads and loads follow the last MFMA.
   template <int M, bool LD>
   __device__ __forceinline__ static void emit0(const uint8_t* rd, int rs, const FragAddr& fa,
-                                               const Frags& now, Frags& next,
+                                               const Frags& now, const Scales& sc, Frags& next,
                                                Acc (&acc)[CFG::FM][CFG::FN],
                                                const char* ab, const char* bb,
                                                const LoadAddr& la, int wave, uint32_t ls) {
     constexpr int NM = kMfmaPerStep, NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
     if constexpr (M < NM) {
       constexpr int i = M / CFG::FN, j = M % CFG::FN;
-      acc[i][j] = mfma(now.b[j], now.a[i], acc[i][j]);
+      acc[i][j] = mfma(now.b[j], now.a[i], acc[i][j], scb_of(sc, STEPS - 1, j),
+                       sca_of(sc, STEPS - 1, i));
       if constexpr (M < NR) read_job<M>(rd, fa, rs, next);
       if constexpr (M < NL) load_job<M>(ab, bb, la, wave, ls);
       __builtin_amdgcn_sched_barrier(0);
-      emit0<M + 1, LD>(rd, rs, fa, now, next, acc, ab, bb, la, wave, ls);
+      emit0<M + 1, LD>(rd, rs, fa, now, sc, next, acc, ab, bb, la, wave, ls);
     } else {
       emit0_rest<NM, LD>(rd, rs, fa, next, ab, bb, la, wave, ls);
     }
@@ -615,10 +706,10 @@ struct GemmTile {
 
   // MFMA step s of the phase in `cur` on fragments `now`, reading step s+1 into `next`.
   __device__ __forceinline__ static void step(const uint8_t* cur, const FragAddr& fa, int s,
-                                              const Frags& now, Frags& next,
+                                              const Frags& now, const Scales& sc, Frags& next,
                                               Acc (&acc)[CFG::FM][CFG::FN]) {
     read_frags(cur, fa, s + 1, next);
-    mfma_step(now, acc);
+    mfma_step(now, sc, s, acc);
     interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
     FGEMM_PHASE_FENCE();
   }
@@ -644,6 +735,7 @@ struct GemmTile {
   __device__ __forceinline__ static void issue_prologue(const Src& S, int m0, int kt0,
                                                         int ktiles, int wave, const LoadAddr& la,
                                                         uint8_t* smem) {
+    if constexpr (MX) issue_scales(S, 0, wave, la, smem);  // phases 0-3 (kt0 is 0)
 #pragma unroll
     for (int t = 0; t < CFG::STAGES - 1; ++t)
       if (t < ktiles) issue_loads(S, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
@@ -679,12 +771,15 @@ struct GemmTile {
       issue_loads(src, m0, kt0 + S - 1, wave, la, smem + (S - 1) * CFG::LDS_STAGE);
     Frags f0, f1;
     read_frags(smem, fa, 0, f0);
+    Scales sc;  // MX: the scales of phase kt (read a phase ahead, with its first fragments)
+    if constexpr (MX) read_scales(smem, fa, wm, wn, 0, sc);
     int st = 0;  // stage of phase kt
     // phases that still load a later phase, then the last S that do not: two
     // straight loop bodies
     int kt = 0;
 #define FGEMM_PHASE(LD, K, X, Y) \
-  phase<LD>(src, m0, smem, wave, lane, fa, la, kt0, K, ktiles, st, chain, Pn, nx, X, Y, acc)
+  phase<LD>(src, m0, smem, wave, wm, wn, lane, fa, la, kt0, K, ktiles, st, chain, Pn, nx, X, Y, \
+            sc, acc)
     if constexpr (STEPS == 1) {
       // the two fragment sets swap roles every phase: two phases an iteration, and
       // one copy where a loop leaves an odd phase over (a selection of sets at run
@@ -717,10 +812,12 @@ struct GemmTile {
   // tile's first loads instead).
   template <bool LD>
   __device__ __forceinline__ static void phase(const Src& src, int m0, uint8_t* smem, int wave,
+                                               int wm, int wn,
                                                int lane, const FragAddr& fa, const LoadAddr& la,
                                                int kt0, int kt, int ktiles, int& st, bool chain,
                                                const GemmProblem& Pn, const Next& nx, Frags& f0,
-                                               Frags& f1, Acc (&acc)[CFG::FM][CFG::FN]) {
+                                               Frags& f1, Scales& sc,
+                                               Acc (&acc)[CFG::FM][CFG::FN]) {
     constexpr int S = CFG::STAGES;
     constexpr int QW = CFG::QAW + CFG::QBW;
     FGEMM_PHASE_FENCE();
@@ -730,10 +827,10 @@ struct GemmTile {
     const char* bb = LD ? uniform_ptr(b_base(src, kl)) : nullptr;
     // every step but the last; the last step's fragments end up in f1 (in f0 for
     // one-step phases, whose caller swaps the two sets every phase)
-    if constexpr (STEPS >= 2) step(cur, fa, 0, f0, f1, acc);
+    if constexpr (STEPS >= 2) step(cur, fa, 0, f0, sc, f1, acc);
     if constexpr (STEPS == 4) {
-      step(cur, fa, 1, f1, f0, acc);
-      step(cur, fa, 2, f0, f1, acc);
+      step(cur, fa, 1, f1, sc, f0, acc);
+      step(cur, fa, 2, f0, sc, f1, acc);
     }
     Frags& fl = STEPS == 1 ? f0 : f1;  // the last step's fragments
     Frags& fn = STEPS == 1 ? f1 : f0;  // receives the next phase's first
@@ -747,12 +844,24 @@ struct GemmTile {
     __builtin_amdgcn_s_setprio(1);
     const int st_next = st + 1 == S ? 0 : st + 1;
     const uint8_t* nxt = smem + st_next * CFG::LDS_STAGE;
+    // MX scale groups of 16 blocks (4 phases) alternate between two buffers.  Group g
+    // is issued at phase 4g-4 after the barrier, has landed by the wait of phase
+    // 4g-3 and is read from the barrier of phase 4g-1 on (phase 4g's scales are read
+    // with its first fragments); its buffer is refilled at phase 4g+4, after the
+    // barrier that follows the last read of it, at phase 4g+2.  The last phase of a
+    // tile reads no scales after its barrier, so the next tile's first group may go
+    // to buffer 0 there.
+    if constexpr (MX)
+      if ((kt & 3) == 0 && kt + 4 < ktiles) issue_scales(src, (kt >> 2) + 1, wave, la, smem);
+    Scales scn;  // MX: phase kt+1's scales
     if (kt + 1 < ktiles) {
+      if constexpr (MX) read_scales(smem, fa, wm, wn, kt + 1, scn);
       if constexpr (LD) {
         // stage st is free once every wave has passed the barrier: phase kt+S goes
         // there, its loads slotted between the last step's MFMAs
-        emit0<0, true>(nxt, 0, fa, fl, fn, acc, ab, bb, la, wave, lds_addr(cur));
+        emit0<0, true>(nxt, 0, fa, fl, sc, fn, acc, ab, bb, la, wave, lds_addr(cur));
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (MX) sc = scn;
         FGEMM_PHASE_FENCE();
         st = st_next;
         return;
@@ -763,9 +872,11 @@ struct GemmTile {
       load_addr(Pn, nx.m0, nx.n0, wave, lane, ln);
       issue_prologue(src_of(Pn), nx.m0, nx.kt0, nx.ktiles, wave, ln, smem);
     }
-    mfma_step(fl, acc);
+    mfma_step(fl, sc, STEPS - 1, acc);
     interleave<0, kMfmaPerStep, 0x100, kReadsPerStep>();
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (MX)
+      if (kt + 1 < ktiles) sc = scn;
     st = st_next;
   }
 
@@ -791,7 +902,7 @@ struct GemmTile {
       for (int s = 0; s < STEPS; ++s) {
         Frags fr;
         read_frags(cur, fa, s, fr);
-        mfma_step(fr, acc);
+        mfma_step(fr, Scales{}, s, acc);  // 16-bit inputs only: no block scales
       }
       if (more) store_checked(nxt, wave, lane, ra, rb);
       __syncthreads();
@@ -1309,7 +1420,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_mfma_kernel(GemmBatch 
   using T = GemmTile<CFG, DT, AK, BKC, EPI, VEC, ODT>;
   // the rotary embedding keeps its pair rates in a table after the stages
   __shared__ __attribute__((aligned(1024)))
-  uint8_t smem[CFG::SMEM + (EPI == kEpiRope ? kRopeMaxPairs * sizeof(double) : 0)];
+  uint8_t smem[CFG::SMEM + (EPI == kEpiRope ? kRopeMaxPairs * sizeof(double) : 0) +
+               (T::MX ? 2 * T::MX_BUF : 0)];
   const int tid = threadIdx.x, lane = tid & 63;
   if constexpr (EPI == kEpiRope) {
     double* ft = reinterpret_cast<double*>(smem + CFG::SMEM);
@@ -1389,9 +1501,10 @@ using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
 using Cfg64n = TileCfg<64, 64, 2, 2, 64, 4>;
-// 8-bit inputs: 8 waves of 64x64 (acc 64 + two sets of 32-byte fragments fit two
-// waves per SIMD), phases of 128 k (48 KB), three stages
-using Cfg256x128f8 = TileCfg<256, 128, 4, 2, 64, 3, 1, 16>;
+// 8-bit inputs: 8 waves of 64x64 in 32x32x64 MFMA blocks (64 accumulators and two
+// 32-register fragment sets: two waves fit a SIMD), phases of 128 k (48 KB), three
+// stages
+using Cfg256x128f8 = TileCfg<256, 128, 4, 2, 64, 3, 1, 32>;
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {

@@ -13,7 +13,7 @@ enum ElemType : int { kF16 = 0, kBF16 = 1 };
 // 8-bit MFMA inputs: one code for the formats of both operands, fa and fb each
 // 0 (E4M3) or 1 (E5M2), the MFMA's own format numbers.
 constexpr int kF8Base = 4;
-constexpr int f8_code(int fa, int fb) { return kF8Base + 2 * fa + fb; }
+constexpr int f8_code(int fa, int fb, int mx = 0) { return kF8Base + 4 * mx + 2 * fa + fb; }
 
 // Epilogue kinds the kernel template is instantiated for.
 enum EpiKind : int {
@@ -57,6 +57,11 @@ struct GemmProblem {
   const float* rms_grad;
   const void* rms_x;
   int64_t ldx;
+  // 8-bit MX inputs: E8M0 scales, one per 32 values along K, [M][ld_mxa] for A and
+  // [N][ld_mxb] for B (bytes; rows hold whole 16-byte groups of 16 blocks)
+  const void* mx_a;
+  const void* mx_b;
+  int64_t ld_mxa, ld_mxb;
 };
 
 // Up to 7 problems of one shape launched together (the Strassen sub-products).

@@ -97,3 +97,37 @@ def f8_normal(shape, seed: int, fmt: int, std=1.0):
     amax = float(np.max(np.abs(x))) if x.size else 1.0
     scale = 2.0 ** np.ceil(np.log2(amax / F8_MAX[fmt])) if amax > 0 else 1.0
     return _to_f8_codes((x / scale).astype(np.float32), fmt), float(scale)
+
+
+def mx_scale_cols(K: int) -> int:
+    """Columns of an E8M0 block-scale array for K values per row: K/32 blocks,
+    rounded up to whole 16-byte groups."""
+    return max(16, (K // 32 + 15) // 16 * 16)
+
+
+def mx_normal(shape, seed: int, fmt: int, std=1.0):
+    """N(0, std) values stored MX-style: every block of 32 values along a row gets
+    the power-of-two scale that puts its largest magnitude just inside the 8-bit
+    format's range, stored as E8M0 (2^(e-127)).  Returns (codes, scales) with
+    scales of shape [rows][mx_scale_cols(K)] (unused tail bytes are 127)."""
+    rows, K = shape
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape) * std
+    blocks = x.reshape(rows, K // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / F8_MAX[fmt])), 0.0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    scales = np.full((rows, mx_scale_cols(K)), 127, dtype=np.uint8)
+    scales[:, :K // 32] = (e + 127).astype(np.uint8)
+    q = (blocks / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K)
+    return _to_f8_codes(q.astype(np.float32), fmt), scales
+
+
+def mx_integers(shape, seed: int, fmt: int, lo: int, hi: int, e_lo=124, e_hi=130):
+    """Small integer codes with random E8M0 block scales in [e_lo, e_hi] (2^-3..2^3)."""
+    rows, K = shape
+    codes = f8_integers(shape, seed, fmt, lo, hi)
+    rng = np.random.default_rng(seed + 1)
+    scales = np.full((rows, mx_scale_cols(K)), 127, dtype=np.uint8)
+    scales[:, :K // 32] = rng.integers(e_lo, e_hi + 1, size=(rows, K // 32)).astype(np.uint8)
+    return codes, scales

@@ -254,7 +254,7 @@ typedef enum { FGEMM_E4M3 = 0, FGEMM_E5M2 = 1 } fgemm_f8_format_t;
  *   C = alpha * (scale_a * A) * (scale_b * B)^T + beta * C
  * A is M x K row-major 8-bit codes (lda >= K bytes), B is N x K row-major (ldb >= K
  * bytes), each in its own format; C is M x N in the 16-bit type `dtype` (ldc >= N).
- * The products are exact and accumulate in fp32 (v_mfma_scale_f32_16x16x128_f8f6f4
+ * The products are exact and accumulate in fp32 (v_mfma_scale_f32_32x32x64_f8f6f4
  * with unit block scales); alpha*scale_a*scale_b is formed once and applied to the
  * fp32 sums, then beta*C and the epilogue: NONE, BIAS and ROWSUMSQ as in
  * fgemm_gemm (others FGEMM_ERR_NOT_SUPPORTED).  Needs K % 128 == 0, lda and ldb
@@ -268,6 +268,28 @@ fgemm_status_t fgemm_gemm_f8(fgemm_handle_t handle, int64_t M, int64_t N, int64_
                              fgemm_f8_format_t b_format, float scale_b, float beta, void* C,
                              int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
                              void* stream);
+
+/* MXFP8 GEMM: the 8-bit GEMM of fgemm_gemm_f8 with one E8M0 scale per block of 32
+ * values along K instead of one scale per tensor (CS336 Lecture 05 notes, Page 27:
+ * MXFP8 keeps an FP8 E8M0 scale, 2^(e-127), for every 32 values):
+ *   C[i][j] = alpha * sum_k sA(i,k) A[i][k] * sB(j,k) B[j][k] + beta * C[i][j]
+ *   sA(i,k) = 2^(a_scales[i*ld_a_scales + k/32] - 127), sB likewise from b_scales.
+ * a_scales is M x (K/32) bytes, b_scales N x (K/32) bytes, row-major device arrays
+ * (a leading dimension below K/32 is FGEMM_ERR_INVALID_VALUE); the leading
+ * dimensions must be multiples of 16 of at least K/32 rounded up to a multiple of
+ * 16 (the kernel reads 16 scales, four phases, per row at a time; the bytes past
+ * K/32 are read and not used) and the arrays 16-byte aligned, else
+ * FGEMM_ERR_NOT_SUPPORTED.  The MFMA applies each lane's block scale
+ * (v_mfma_scale_f32_32x32x64_f8f6f4).  K = 0 reads no scale (the arrays may be
+ * null); everything else is as for fgemm_gemm_f8. */
+fgemm_status_t fgemm_gemm_mxf8(fgemm_handle_t handle, int64_t M, int64_t N, int64_t K,
+                               float alpha, const void* A, int64_t lda,
+                               fgemm_f8_format_t a_format, const void* a_scales,
+                               int64_t ld_a_scales, const void* B, int64_t ldb,
+                               fgemm_f8_format_t b_format, const void* b_scales,
+                               int64_t ld_b_scales, float beta, void* C, int64_t ldc,
+                               fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                               void* stream);
 
 /* Size of the fixed per-device scratch array behind fgemm_gemm_noalloc. */
 #define FGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -136,6 +136,8 @@ int main() {
          FGEMM_ERR_INVALID_VALUE);
   EXPECT(fgemm_gemm_f8(NULL, 8, 8, 128, 1.f, P, 128, FGEMM_E4M3, 1.f, P, 128, FGEMM_E4M3, 1.f, 0.f,
                        P, 8, FGEMM_BF16, NULL, NULL) == FGEMM_ERR_INVALID_VALUE);
+  EXPECT(fgemm_gemm_mxf8(NULL, 8, 8, 128, 1.f, P, 128, FGEMM_E4M3, P, 16, P, 128, FGEMM_E4M3, P, 16,
+                         0.f, P, 8, FGEMM_BF16, NULL, NULL) == FGEMM_ERR_INVALID_VALUE);
   EXPECT(fgemm_create(NULL, 0) == FGEMM_ERR_INVALID_VALUE);
   EXPECT(fgemm_destroy(NULL) == FGEMM_ERR_INVALID_VALUE);
   printf("harness: %ld selects, %ld checks, sum %.6f, %d failures\n", selects, checks, tsum,

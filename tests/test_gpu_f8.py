@@ -151,3 +151,96 @@ def test_refusals():
     assert call(epi=sw) == fgemm.FGEMM_ERR_NOT_SUPPORTED
     torch.cuda.synchronize()
     assert bool((C == 0).all())
+
+
+# ------------------------------------------------------------------ MXFP8 block scales
+def run_mx(A, sA, B, sB, dtype, *, fa=E4, fb=E4, alpha=1.0, beta=0.0, C_bits=None, epilogue=None):
+    import torch
+    M, N = A.shape[0], B.shape[0]
+    Ad, Bd, sAd, sBd = dev8(A), dev8(B), dev8(sA), dev8(sB)
+    if C_bits is None:
+        C_bits = np.full((M, N), 0x7FC0 if dtype == BF16 else 0x7E00, dtype=np.uint16)
+    pad_c = (-N) % 8
+    Cd = to_dev(C_bits, dtype, pad_c)
+    handle().gemm_mxf8(Ad, Bd, Cd, sAd, sBd, a_format=fa, b_format=fb, alpha=alpha, beta=beta,
+                       epilogue=epilogue)
+    torch.cuda.synchronize()
+    return from_dev(Cd)
+
+
+@pytest.mark.parametrize("fa,fb", FORMATS)
+def test_mx_exact_integers_every_group(fa, fb):
+    """Integer codes with random E8M0 block scales in 2^-3..2^3: every product and
+    partial sum is exact in fp32, so the GPU result must equal the oracle's
+    rounding of the exact sum bit for bit.  1 to 9 phases of 128 k cover the first
+    scale group, the switch between the two group buffers and a partial last group."""
+    dtype = BF16
+    for (M, N, K) in [(256, 128, 128), (300, 200, 512), (64, 77, 640), (257, 129, 1024),
+                      (33, 40, 1152)]:
+        say(f"mx exact fa={fa} fb={fb} {M}x{N}x{K}")
+        A, sA = inputs.mx_integers((M, K), 81 + M, fa, -2, 2)
+        B, sB = inputs.mx_integers((N, K), 82 + N, fb, -2, 2)
+        C = inputs.integers((M, N), 83 + K, dtype, -3, 3)
+        _, Q, _ = oracle.gemm_f8(A, B, fmt_a=fa, fmt_b=fb, mx_a=sA, mx_b=sB, alpha=0.5, beta=1.0,
+                                 C=C, dtype=dtype)
+        got = run_mx(A, sA, B, sB, dtype, fa=fa, fb=fb, alpha=0.5, beta=1.0, C_bits=C)
+        assert np.array_equal(got, Q), (M, N, K)
+
+
+def test_mx_persistent_chains_exact():
+    """MX with more tiles than the device holds at once (17 x 34 tiles of 256 x 128):
+    the next tile's first scale group is loaded while other waves finish the last
+    phase, whose group sits in either buffer (4, 5 and 9 phases).  Exact."""
+    dtype = BF16
+    M = N = 4352
+    for K in (512, 640, 1152):
+        say(f"mx chains K={K}")
+        A, sA = inputs.mx_integers((M, K), 171, E4, -1, 1)
+        B, sB = inputs.mx_integers((N, K), 172, E4, -1, 1)
+        A[:, 256:] = 0
+        _, Q, _ = oracle.gemm_f8(A, B, mx_a=sA, mx_b=sB, dtype=dtype)
+        got = run_mx(A, sA, B, sB, dtype)
+        assert np.array_equal(got, Q), K
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_mx_random_block_scaled_with_statistics(dtype):
+    """Block-scaled N(0,1) activations and N(0,0.02) weights (every 32 values their
+    own power-of-two scale), bias and row sums of squares; within 1e-3."""
+    import torch
+    M, N, K = 600, 520, 1024
+    say(f"mx random dtype={dtype}")
+    A, sA = inputs.mx_normal((M, K), 91, E4)
+    B, sB = inputs.mx_normal((N, K), 92, E4, std=0.02)
+    bias = inputs.normal((N,), 94, dtype, std=0.1)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    _, Q, ss = oracle.gemm_f8(A, B, mx_a=sA, mx_b=sB, dtype=dtype, epi=flags, bias=bias)
+    bd = to_dev(bias[None, :], dtype)
+    ssd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ, bias=bd.data_ptr(),
+                              rowsumsq=ssd.data_ptr())
+    got = run_mx(A, sA, B, sB, dtype, epilogue=epi)
+    assert rel_err(got, Q, dtype) <= CLASSICAL_TOL
+    ssg = ssd.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(ssg - ss) / ss) <= STATS_TOL
+
+
+def test_mx_refusals():
+    import torch
+    say("mx refusals")
+    h = handle()
+    A = torch.zeros((64, 512), dtype=torch.uint8, device="cuda")
+    S = torch.full((64, 32), 127, dtype=torch.uint8, device="cuda")
+    C = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    s = fgemm.current_stream()
+
+    def call(K=512, lds=16, sp=S.data_ptr()):
+        return fgemm.fgemm_gemm_mxf8(h.h, 64, 64, K, 1.0, A.data_ptr(), 512, E4, sp, lds,
+                                     A.data_ptr(), 512, E4, sp, lds, 0.0, C.data_ptr(), 64,
+                                     fgemm.FGEMM_BF16, None, s, check=False)
+    assert call() == fgemm.FGEMM_OK
+    assert call(lds=8) == fgemm.FGEMM_ERR_INVALID_VALUE        # fewer than K/32 scales a row
+    assert call(lds=24) == fgemm.FGEMM_ERR_NOT_SUPPORTED       # not whole 16-byte groups
+    assert call(K=384, lds=12) == fgemm.FGEMM_ERR_NOT_SUPPORTED
+    assert call(sp=0) == fgemm.FGEMM_ERR_INVALID_VALUE
+    torch.cuda.synchronize()
