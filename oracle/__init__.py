@@ -18,6 +18,10 @@ What it computes (see the header of ``oracle.c`` for the passages it follows):
 * ``gemm_f8``    the 8-bit GEMM A B^T on E4M3 / E5M2 values with per-tensor scales
                  or E8M0 scales per block of 32 along K (MXFP8), same epilogue and
                  rounding as ``gemm``; ``decode_f8`` / ``decode_e8m0`` the formats.
+* ``gemm_dense`` / ``gemm_f8_dense``  the unrounded product of every row through
+                 one fp64 library matmul (whole-output checks at full size), with
+                 the magnitude |alpha||A||B| + |beta||C| that ``elementwise_bound``
+                 turns into a per-element rounding-error bound.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against hand-worked
 products, exact integer identities, invariants and library routines.
@@ -364,3 +368,104 @@ def gemm_f8(A, B, *, fmt_a=E4M3, fmt_b=E4M3, scale_a=1.0, scale_b=1.0, mx_a=None
     if rc != 0:
         raise ValueError("oracle_gemm_f8 rejected its arguments")
     return D, Q, ss
+
+
+# ------------------------------------------------------------ whole-output references
+def gemm_dense(A, B, *, transA=False, transB=False, alpha=1.0, beta=0.0, C=None, dtype=BF16,
+               bound=True):
+    """The unrounded product D = alpha*op(A)op(B) + beta*C of ``gemm`` for every
+    row, with one fp64 library matmul as the step that forms sum_k a_ik b_kj (its
+    summation order differs from ascending k by fp64 roundings only, about
+    K*2^-53 relative, far below any 16-bit tolerance).  Also returns
+    S = |alpha| |op(A)| |op(B)| + |beta| |C|: every rounding-error bound of a
+    floating-point evaluation of D scales with S element by element (None when
+    bound=False).  Inputs are 16-bit bit patterns as for ``gemm``."""
+    a = decode(_u16(A), dtype)
+    b = decode(_u16(B), dtype)
+    if transA:
+        a = a.T
+    if transB:
+        b = b.T
+    if a.shape[1] != b.shape[0]:
+        raise ValueError(f"inner dimensions differ: {a.shape[1]} vs {b.shape[0]}")
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    D = alpha * (a @ b)
+    S = abs(alpha) * (np.abs(a) @ np.abs(b)) if bound else None
+    if beta != 0.0:
+        c = decode(_u16(C), dtype)[:, :D.shape[1]]
+        D += beta * c
+        if bound:
+            S += abs(beta) * np.abs(c)
+    return D, S
+
+
+def gemm_f8_dense(A, B, *, fmt_a=E4M3, fmt_b=E4M3, scale_a=1.0, scale_b=1.0, mx_a=None,
+                  mx_b=None, alpha=1.0):
+    """``gemm_f8``'s unrounded alpha * sum_k (s q_a)(s q_b) for every row (A M x K, B
+    N x K, K-contiguous) with one fp64 library matmul, and the matching bound
+    magnitude S = |alpha| |A'| |B'|^T of the scaled values A', B'."""
+    M, K = _u8(A).shape
+    a = decode_f8(A, fmt_a)
+    b = decode_f8(B, fmt_b)
+    if mx_a is not None:
+        a = a * np.repeat(decode_e8m0(_u8(mx_a)[:, :K // 32]), 32, axis=1)
+        b = b * np.repeat(decode_e8m0(_u8(mx_b)[:, :K // 32]), 32, axis=1)
+    else:
+        a = a * float(scale_a)
+        b = b * float(scale_b)
+    D = alpha * (a @ b.T)
+    S = abs(alpha) * (np.abs(a) @ np.abs(b).T)
+    return D, S
+
+
+def elementwise_bound(D, S, K, dtype, acc_unit=2.0 ** -23):
+    """Per-element bound on |RNE16(fl32(D)) - D| for a product evaluated with fp32
+    accumulation: |fl32(D) - D| <= g S with g = n u / (1 - n u), n = K + 4 (the K
+    products' sums and the alpha, beta*C steps; u = 2^-23 also covers truncating
+    adds), then one rounding to the 16-bit type, relative unit u16 = 2^-8 (bf16) or
+    2^-11 (fp16), plus half the fp16 subnormal spacing:
+    bound = u16 |D| + (1 + u16) g S (+ 2^-25 for fp16)."""
+    n = float(K + 4)
+    g = n * acc_unit / (1.0 - n * acc_unit)
+    u16 = 2.0 ** -8 if dtype == BF16 else 2.0 ** -11
+    tiny = 0.0 if dtype == BF16 else 2.0 ** -25  # half the fp16 subnormal spacing
+    return u16 * np.abs(D) + (1.0 + u16) * g * S + tiny
+
+
+def rms_swiglu_terms(Y, W2, *, rms_ss, rms_n, rms_eps=1e-6, alpha=1.0, dtype=BF16):
+    """``gemm``'s EPI_RMS_SWIGLU output for every row, unrounded: H = Y W2 through one
+    fp64 library matmul (W2 holds the gate columns, then the up columns), the row
+    scale r_i = 1 / sqrt(rms_ss_i / rms_n + rms_eps), g = alpha r_i H_gate,
+    u = alpha r_i H_up, out = g / (1 + e^-g) * u.  Returns (out, H, d_gate, d_up)
+    with the partial derivatives d out / d H_gate = alpha r silu'(g) u and
+    d out / d H_up = alpha r silu(g): an error dH in the sums moves out by
+    d_gate dH_gate + d_up dH_up to first order."""
+    y = decode(_u16(Y), dtype)
+    w = decode(_u16(W2), dtype)
+    H = y @ w
+    nout = H.shape[1] // 2
+    r = 1.0 / np.sqrt(np.asarray(rms_ss, dtype=np.float64) / rms_n + rms_eps)
+    ar = alpha * r[:, None]
+    g = ar * H[:, :nout]
+    u = ar * H[:, nout:]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    out = g * sig * u
+    d_gate = ar * sig * (1.0 + g * (1.0 - sig)) * u
+    d_up = ar * g * sig
+    return out, H, d_gate, d_up
+
+
+def rms_swiglu_dense(Y, W2, *, rms_ss, rms_n, rms_eps=1e-6, alpha=1.0, dtype=BF16,
+                     bound=False):
+    """The EPI_RMS_SWIGLU output of ``rms_swiglu_terms``.  With bound=True also
+    returns E = |d_gate| S_gate + |d_up| S_up with S = |Y| |W2|: an fp32
+    evaluation whose sums H carry errors <= gamma S moves out by at most gamma E
+    to first order."""
+    out, _, d_gate, d_up = rms_swiglu_terms(Y, W2, rms_ss=rms_ss, rms_n=rms_n,
+                                            rms_eps=rms_eps, alpha=alpha, dtype=dtype)
+    if not bound:
+        return out
+    S = np.abs(decode(_u16(Y), dtype)) @ np.abs(decode(_u16(W2), dtype))
+    nout = out.shape[1]
+    return out, np.abs(d_gate) * S[:, :nout] + np.abs(d_up) * S[:, nout:]

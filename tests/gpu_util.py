@@ -53,6 +53,45 @@ def rel_err(gpu_bits, ref_Q, dtype):
     return oracle.rel_fro(oracle.decode(gpu_bits, dtype), oracle.decode(ref_Q, dtype))
 
 
+def check_full(gpu_bits, D, S, K, dtype, tol=CLASSICAL_TOL):
+    """Whole-output parity of a classical (fp32-accumulated) product: every element
+    inside oracle.elementwise_bound, and the normwise error against the oracle's
+    rounded result within `tol`."""
+    g = oracle.decode(gpu_bits, dtype)
+    bound = oracle.elementwise_bound(D, S, K, dtype)
+    bad = ~(np.abs(g - D) <= bound)
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} elements outside the bound; "
+                           f"first at {tuple(np.argwhere(bad)[0])}")
+    Q = oracle.encode(D, dtype)
+    assert rel_err(gpu_bits, Q, dtype) <= tol
+
+
+# Per-element cap of the Strassen paths: their rounding error is not bounded element
+# by element by |A||B| (the block sums pair k of one half of K with k of the other),
+# so each element is held to ELEM_FACTOR times the normwise tolerance, in units of
+# the output's RMS.  The error of one element sums thousands of independent
+# roundings, so it is near-Gaussian with a deviation of about the normwise error
+# (up to ~1.5x in the quadrants fed by the most products); the largest of 2.7e8
+# such values is about sqrt(2 ln 2.7e8) = 6.2 deviations, inside 10x the tolerance,
+# while a wrong block, sign or tile leaves errors of order |D| = RMS.
+ELEM_FACTOR = 10.0
+
+
+def check_full_strassen(gpu_bits, D, dtype, tol=STRASSEN_TOL):
+    g = oracle.decode(gpu_bits, dtype)
+    rms = float(np.sqrt(np.mean(D * D)))
+    u16 = 2.0 ** -8 if dtype == BF16 else 2.0 ** -11
+    bound = u16 * np.abs(D) + ELEM_FACTOR * tol * rms
+    err = np.abs(g - D)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} elements outside the bound; "
+                           f"worst {float(np.max(err / bound)):.3g}x at "
+                           f"{tuple(np.unravel_index(np.argmax(err / bound), err.shape))}")
+    Q = oracle.encode(D, dtype)
+    assert rel_err(gpu_bits, Q, dtype) <= tol
+    return float(np.max((err - u16 * np.abs(D)) / rms))
+
+
 _handle = None
 
 
@@ -83,3 +122,22 @@ def run(A_bits, B_bits, dtype, *, transA=False, transB=False, alpha=1.0, beta=0.
                   epilogue=epilogue)
     torch.cuda.synchronize()
     return from_dev(C)
+
+
+def check_full_strassen_swiglu(gpu_bits, out, H, d_gate, d_up, dtype, tol=STRASSEN_TOL):
+    """Whole-output parity of RMS + SwiGLU over a Strassen product: the error of
+    each sum in H is held to ELEM_FACTOR * tol * RMS of its half of H (the cap of
+    check_full_strassen) and carried to the output through the exact first-order
+    derivatives; then the 16-bit rounding; and normwise."""
+    nout = out.shape[1]
+    rg = float(np.sqrt(np.mean(H[:, :nout] ** 2)))
+    ru = float(np.sqrt(np.mean(H[:, nout:] ** 2)))
+    u16 = 2.0 ** -8 if dtype == BF16 else 2.0 ** -11
+    bound = u16 * np.abs(out) + ELEM_FACTOR * tol * (np.abs(d_gate) * rg + np.abs(d_up) * ru)
+    o = oracle.decode(gpu_bits, dtype)
+    err = np.abs(o - out)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} elements outside the bound; "
+                           f"worst {float(np.max(err / bound)):.3g}x")
+    assert rel_err(gpu_bits, oracle.encode(out, dtype), dtype) <= tol
+    return float(np.max(err / bound))

@@ -6,7 +6,7 @@ import pytest
 import oracle
 from hgemm_strassen_type_amd import fgemm
 from hgemm_strassen_type_amd import inputs
-from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, from_dev, handle, rel_err, say,
+from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, check_full, from_dev, handle, rel_err, say,
                       to_dev, empty_out)
 
 pytestmark = pytest.mark.gpu
@@ -118,10 +118,30 @@ def test_chain_small_full_check():
 
 
 def test_chain_llm_size():
-    """M=8192, hidden 4096, FFN 11008: X N(0,1), W and W2 N(0,0.02); sampled rows."""
+    """M=8192, hidden 4096, FFN 11008: X N(0,1), W and W2 N(0,0.02).  Sampled rows
+    through the ascending-k oracle, then every element of Y and of the SwiGLU
+    output against the fp64 references within their rounding-error bounds (GEMM2
+    on the Y and statistics it was given), and every row's statistics."""
+    dtype, M, H = BF16, 8192, 4096
     say("chain 8192x4096 -> 2x11008")
-    X, W, W2, Y, ss, O = run_chain(8192, 4096, 11008, 4001)
-    check_chain(X, W, W2, Y, ss, O, inputs.sample_rows(8192, 24, 9), 4096)
+    X, W, W2, Y, ss, O = run_chain(M, H, 11008, 4001)
+    check_chain(X, W, W2, Y, ss, O, inputs.sample_rows(M, 24, 9), H)
+    D1, S1 = oracle.gemm_dense(X, W, dtype=dtype)
+    check_full(Y, D1, S1, H, dtype)
+    y = oracle.decode(Y, dtype)
+    assert np.max(np.abs(ss - np.sum(y * y, axis=1)) / ss) <= STATS_TOL
+    D2, E2 = oracle.rms_swiglu_dense(Y, W2, rms_ss=ss, rms_n=H, rms_eps=1e-6, dtype=dtype,
+                                     bound=True)
+    # fp32 sums (gamma E2 to first order), a few ulps of fp32 in the row scale, the
+    # exponential and the products, then the 16-bit rounding
+    n = H + 4
+    gamma = n * 2.0 ** -23 / (1 - n * 2.0 ** -23)
+    u16 = 2.0 ** -8
+    bound = u16 * np.abs(D2) + (1 + u16) * (gamma * E2 + 8 * 2.0 ** -23 * np.abs(D2))
+    o = oracle.decode(O, dtype)
+    bad = ~(np.abs(o - D2) <= bound)
+    assert not bad.any(), f"{int(bad.sum())} SwiGLU outputs outside the bound"
+    assert rel_err(O, oracle.encode(D2, dtype), dtype) <= CLASSICAL_TOL
 
 
 # ------------------------------------------------------------ activation and RoPE

@@ -11,7 +11,8 @@ import pytest
 import oracle
 from hgemm_strassen_type_amd import fgemm
 from hgemm_strassen_type_amd import inputs
-from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, from_dev, handle, rel_err, say, to_dev)
+from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, check_full, from_dev, handle, rel_err, say,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,18 +113,30 @@ def test_persistent_chains_exact():
         assert np.array_equal(got, Q), K
 
 
-def test_llm_projection_shape_sampled():
+def test_llm_projection_shape_whole_output():
     """16384 tokens x 4096 -> 4096 (the projection shape), E4M3 activations and
-    weights with per-tensor scales; sampled rows against the oracle."""
+    weights with per-tensor scales: every element against the oracle's fp64
+    product within its rounding-error bound, and normwise."""
     dtype = BF16
     M, N, K = 16384, 4096, 4096
     say("f8 16384x4096x4096")
     A, sa = inputs.f8_normal((M, K), 3001, E4)
     B, sb = inputs.f8_normal((N, K), 3002, E4, std=0.02)
     got = run8(A, B, dtype, sa=sa, sb=sb)
-    rows = inputs.sample_rows(M, 32, 8)
-    _, Q, _ = oracle.gemm_f8(A, B, scale_a=sa, scale_b=sb, dtype=dtype, rows=rows)
-    assert rel_err(got[rows], Q, dtype) <= CLASSICAL_TOL
+    D, S = oracle.gemm_f8_dense(A, B, scale_a=sa, scale_b=sb)
+    check_full(got, D, S, K, dtype)
+
+
+def test_mx_llm_projection_shape_whole_output():
+    """The projection shape in MXFP8 (E8M0 scale per 32 values): whole output."""
+    dtype = BF16
+    M, N, K = 16384, 4096, 4096
+    say("mx 16384x4096x4096")
+    A, sA = inputs.mx_normal((M, K), 3003, E4)
+    B, sB = inputs.mx_normal((N, K), 3004, E4, std=0.02)
+    got = run_mx(A, sA, B, sB, dtype)
+    D, S = oracle.gemm_f8_dense(A, B, mx_a=sA, mx_b=sB)
+    check_full(got, D, S, K, dtype)
 
 
 def test_refusals():

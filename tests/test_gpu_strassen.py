@@ -8,8 +8,9 @@ import pytest
 import oracle
 from hgemm_strassen_type_amd import fgemm
 from hgemm_strassen_type_amd import inputs
-from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, STRASSEN_TOL, empty_out, from_dev, handle, rel_err,
-                      run, say, to_dev)
+from gpu_util import (BF16, CLASSICAL_TOL, F16, STATS_TOL, STRASSEN_TOL, check_full_strassen,
+                      check_full_strassen_swiglu, empty_out, from_dev, handle, rel_err, run, say,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,16 +168,20 @@ def test_fp16_256_cube_depth1(variant):
     (BF16, 32768, 8192, 8192, 1, S69),
     (F16, 32768, 8192, 8192, 2, WIN),
 ])
-def test_large_shapes_sampled(dtype, M, N, K, depth, variant):
-    """U[-1,1] seeds 5001/5002, square 16384^3 and 32768 x 8192 x 8192, depth 1 and 2;
-    the oracle checks sampled rows."""
+def test_large_shapes_whole_output(dtype, M, N, K, depth, variant):
+    """U[-1,1] seeds 5001/5002, square 16384^3 and 32768 x 8192 x 8192, depth 1 and 2:
+    every element of the output against the oracle's fp64 product (per-element
+    cap and normwise), plus the ascending-k oracle on sampled rows."""
     say(f"strassen large {M}x{N}x{K} d={depth} v={variant} dtype={dtype}")
     A = inputs.uniform((M, K), 5001, dtype)
     B = inputs.uniform((K, N), 5002, dtype)
     got = run(A, B, dtype, plan=fgemm.strassen_plan(depth, variant))
-    rows = inputs.sample_rows(M, 16, 10)
+    rows = inputs.sample_rows(M, 8, 10)
     _, Q, _ = oracle.gemm(A, B, dtype=dtype, rows=rows)
     assert rel_err(got[rows], Q, dtype) <= STRASSEN_TOL
+    D, _ = oracle.gemm_dense(A, B, dtype=dtype, bound=False)
+    worst = check_full_strassen(got, D, dtype)
+    say(f"  largest element error {worst:.3g} x RMS(D)")
 
 
 # ------------------------------------------------------------ epilogues in the post-add
@@ -282,7 +287,9 @@ def test_fused_chain_llm_size_on_strassen(depth):
     """The fused chain at its configured size, both GEMMs forced onto Winograd: X
     [8192 x 4096] N(0,1), W [4096 x 4096] and W2 [4096 x 2*11008] N(0,0.02); GEMM1
     writes Y and its row sums of squares, GEMM2 applies the RMS scale and SwiGLU.
-    Sampled rows against the oracle, each GEMM on the inputs it was given."""
+    Every element of both outputs against the oracle's fp64 product on the inputs
+    each GEMM was given (per-element cap and normwise), and the ascending-k oracle
+    with its statistics on sampled rows."""
     import torch
     dtype, M, H, F = BF16, 8192, 4096, 11008
     say(f"strassen chain 8192x4096 -> 2x11008 d={depth}")
@@ -315,6 +322,12 @@ def test_fused_chain_llm_size_on_strassen(depth):
                            rms_eps=1e-6)
     print(f"[chain d={depth}] end-to-end rel err vs the oracle's chain: "
           f"{rel_err(O[rows], Oe, dtype):.3e}")
+    D1, _ = oracle.gemm_dense(X, W, dtype=dtype, bound=False)
+    check_full_strassen(Y, D1, dtype)
+    D2, Hs, dg, du = oracle.rms_swiglu_terms(Y, W2, rms_ss=ss, rms_n=H, rms_eps=1e-6,
+                                             dtype=dtype)
+    worst = check_full_strassen_swiglu(O, D2, Hs, dg, du, dtype)
+    say(f"  SwiGLU output: largest error {worst:.3g} of its bound")
 
 
 @pytest.mark.parametrize("dtype", [BF16, F16])

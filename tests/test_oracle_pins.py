@@ -650,3 +650,144 @@ def test_mx_block_scales():
     # K not a multiple of the block is refused
     with pytest.raises(ValueError):
         oracle.gemm_f8(A[:, :40], B[:, :40], mx_a=sa[:, :2], mx_b=sb[:, :2])
+
+
+# ------------------------------------------------------------ whole-output references
+@pytest.mark.parametrize("transA,transB", [(False, False), (True, False), (False, True)])
+def test_dense_exact_on_integers(transA, transB):
+    """Integer inputs: the dense reference is the exact integer product (int64
+    arithmetic), in every layout, and with beta*C."""
+    dtype = BF16
+    M, N, K = 37, 29, 130
+    A = inputs.integers((K, M) if transA else (M, K), 11, dtype, -8, 8)
+    B = inputs.integers((N, K) if transB else (K, N), 12, dtype, -8, 8)
+    C = inputs.integers((M, N), 13, dtype, -8, 8)
+    ai = oracle.decode(A, dtype).astype(np.int64)
+    bi = oracle.decode(B, dtype).astype(np.int64)
+    ci = oracle.decode(C, dtype).astype(np.int64)
+    exact = (ai.T if transA else ai) @ (bi.T if transB else bi)
+    D, S = oracle.gemm_dense(A, B, transA=transA, transB=transB, dtype=dtype)
+    assert np.array_equal(D, exact.astype(np.float64))
+    D2, _ = oracle.gemm_dense(A, B, transA=transA, transB=transB, alpha=2.0, beta=-3.0, C=C,
+                              dtype=dtype)
+    assert np.array_equal(D2, (2 * exact - 3 * ci).astype(np.float64))
+
+
+def test_dense_bound_magnitude():
+    """S = |alpha||A||B| + |beta||C|: for nonnegative A, B and nonpositive C with
+    alpha, beta > 0, S - D = 2 beta |C| exactly (integers)."""
+    dtype = F16
+    A = inputs.integers((20, 48), 21, dtype, 0, 5)
+    B = inputs.integers((48, 30), 22, dtype, 0, 5)
+    C = inputs.integers((20, 30), 23, dtype, -6, 0)
+    D, S = oracle.gemm_dense(A, B, alpha=1.0, beta=0.5, C=C, dtype=dtype)
+    c = oracle.decode(C, dtype)
+    assert np.array_equal(S - D, 2 * 0.5 * np.abs(c))
+    assert np.all(S >= np.abs(D))
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_dense_matches_the_ascending_k_oracle(dtype):
+    """Random inputs, alpha and beta: the library-matmul reference agrees with the
+    plain ascending-k loop of ``gemm`` to fp64 rounding (relative to S)."""
+    for transA, transB in [(False, False), (True, True)]:
+        M, N, K = 70, 90, 300
+        A = inputs.normal((K, M) if transA else (M, K), 31, dtype)
+        B = inputs.normal((N, K) if transB else (K, N), 32, dtype)
+        C = inputs.normal((M, N), 33, dtype)
+        D, S = oracle.gemm_dense(A, B, transA=transA, transB=transB, alpha=0.75, beta=-1.5,
+                                 C=C, dtype=dtype)
+        Dc, _, _ = oracle.gemm(A, B, transA=transA, transB=transB, alpha=0.75, beta=-1.5, C=C,
+                               dtype=dtype)
+        assert np.max(np.abs(D - Dc) / S) <= 1e-13
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_elementwise_bound_holds_for_an_fp32_evaluation(dtype):
+    """An fp32 evaluation of the product (torch float32 matmul on the CPU) rounded
+    once to the 16-bit type stays inside the per-element bound, which is not
+    vacuous: typically a fraction of |D|."""
+    M, N, K = 64, 80, 2048
+    A = inputs.normal((M, K), 41, dtype)
+    B = inputs.normal((K, N), 42, dtype)
+    C = inputs.normal((M, N), 43, dtype)
+    D, S = oracle.gemm_dense(A, B, beta=0.5, C=C, dtype=dtype)
+    a = torch.from_numpy(oracle.decode(A, dtype).astype(np.float32))
+    b = torch.from_numpy(oracle.decode(B, dtype).astype(np.float32))
+    c = torch.from_numpy(oracle.decode(C, dtype).astype(np.float32))
+    x = (a @ b + 0.5 * c).numpy().astype(np.float64)
+    q = oracle.decode(oracle.encode(x, dtype), dtype)
+    bound = oracle.elementwise_bound(D, S, K, dtype)
+    assert np.all(np.abs(q - D) <= bound)
+    assert np.median(bound / np.abs(D)) < 0.2
+    # a planted error of one part in 100 on one element is outside it
+    q[5, 7] = D[5, 7] + 0.01 * max(abs(D[5, 7]), 1.0) + bound[5, 7]
+    assert not np.all(np.abs(q - D) <= bound)
+
+
+def test_f8_dense_matches_the_8bit_oracle():
+    """Per-tensor and MX block scales: the dense 8-bit reference equals the C
+    oracle's unrounded rows to fp64 rounding, and integer codes give the exact
+    integer product."""
+    M, N, K = 40, 36, 256
+    A = inputs.f8_integers((M, K), 51, oracle.E4M3, -4, 4)
+    B = inputs.f8_integers((N, K), 52, oracle.E5M2, -4, 4)
+    ai = oracle.decode_f8(A, oracle.E4M3).astype(np.int64)
+    bi = oracle.decode_f8(B, oracle.E5M2).astype(np.int64)
+    D, S = oracle.gemm_f8_dense(A, B, fmt_a=oracle.E4M3, fmt_b=oracle.E5M2)
+    assert np.array_equal(D, (ai @ bi.T).astype(np.float64))
+    A2, sa = inputs.f8_normal((M, K), 53, oracle.E4M3)
+    B2, sb = inputs.f8_normal((N, K), 54, oracle.E4M3, std=0.02)
+    D2, S2 = oracle.gemm_f8_dense(A2, B2, scale_a=sa, scale_b=sb, alpha=0.5)
+    Dc, _, _ = oracle.gemm_f8(A2, B2, scale_a=sa, scale_b=sb, alpha=0.5)
+    assert np.max(np.abs(D2 - Dc) / S2) <= 1e-13
+    A3, s3 = inputs.mx_normal((M, K), 55, oracle.E4M3)
+    B3, t3 = inputs.mx_normal((N, K), 56, oracle.E4M3, std=0.02)
+    D3, S3 = oracle.gemm_f8_dense(A3, B3, mx_a=s3, mx_b=t3)
+    Dc3, _, _ = oracle.gemm_f8(A3, B3, mx_a=s3, mx_b=t3)
+    assert np.max(np.abs(D3 - Dc3) / S3) <= 1e-13
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_rms_swiglu_dense_matches_the_loop_oracle(dtype):
+    """The whole-output RMS + SwiGLU reference equals the ascending-k oracle's
+    unrounded EPI_RMS_SWIGLU rows to fp64 rounding, alpha included."""
+    M, H, F = 24, 160, 48
+    Y = inputs.normal((M, H), 61, dtype)
+    W2 = inputs.normal((H, 2 * F), 62, dtype, std=0.1)
+    ss = np.sum(oracle.decode(Y, dtype) ** 2, axis=1)
+    for alpha in (1.0, 0.5):
+        D = oracle.rms_swiglu_dense(Y, W2, rms_ss=ss, rms_n=H, alpha=alpha, dtype=dtype)
+        Dc, _, _ = oracle.gemm(Y, W2, dtype=dtype, alpha=alpha, epi=oracle.EPI_RMS_SWIGLU,
+                               rms_ss=ss, rms_n=H, rms_eps=1e-6)
+        assert np.max(np.abs(D - Dc)) <= 1e-12 * np.max(np.abs(Dc))
+
+
+def test_rms_swiglu_derivatives_by_central_differences():
+    """d out / d H from rms_swiglu_terms against central differences, in one gate
+    and one up sum, of the output written out from its definition."""
+    dtype = BF16
+    M, H, F = 3, 32, 4
+    yv = np.zeros((M, H))
+    yv[:, 0] = 1.0
+    yv[:, 1:] = np.random.default_rng(71).integers(-2, 3, size=(M, H - 1))
+    Y = oracle.encode(yv, dtype)
+    W2 = inputs.normal((H, 2 * F), 72, dtype, std=0.3)
+    ss = np.full(M, 64.0)
+    out, Hs, dg, du = oracle.rms_swiglu_terms(Y, W2, rms_ss=ss, rms_n=H, alpha=0.7, dtype=dtype)
+    w = oracle.decode(W2, dtype)
+    y = oracle.decode(Y, dtype)
+    r = 1 / np.sqrt(ss / H + 1e-6)
+
+    def f(Hm):
+        g = 0.7 * r[:, None] * Hm[:, :F]
+        u = 0.7 * r[:, None] * Hm[:, F:]
+        return g / (1 + np.exp(-g)) * u
+    assert np.allclose(f(y @ w), out, rtol=1e-12, atol=1e-14)
+    h = 1e-6
+    for col, d in ((1, dg), (F + 1, du)):
+        Hp, Hm = Hs.copy(), Hs.copy()
+        Hp[:, col] += h
+        Hm[:, col] -= h
+        num = (f(Hp) - f(Hm))[:, col % F] / (2 * h)
+        assert np.allclose(num, d[:, col % F], rtol=1e-6, atol=1e-9)
