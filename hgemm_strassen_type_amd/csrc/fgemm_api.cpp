@@ -78,6 +78,11 @@ struct fgemm_handle_s {
   void* own_ws = nullptr;
   size_t own_ws_bytes = 0;
   int pools = 0;  // the device supports stream-ordered allocation
+  // Second stream of the overlapped Winograd schedule (the operand sums run there
+  // beside the products that need none), with its fork and join events; null when
+  // they could not be created (the schedule then runs on the caller's stream).
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -420,6 +425,11 @@ struct StrassenRun {
   int cus;
   int depth, variant, sub_tile;
   int in_dtype;
+  // Winograd depth 1: P1 = A11 B11 and P2 = A12 B21 read the input blocks
+  // (blocks of `L0`, `R0`) on the caller's stream while the sums run on `aux`
+  bool overlap;
+  hipStream_t aux;
+  hipEvent_t join;
   float* scale_a; float* scale_b;
   // per level l (1-based): the seven left and right product operands (fp16) and
   // the seven products (fp32)
@@ -442,39 +452,80 @@ BlockedOperand temp_op(void* p, int64_t rows, int64_t cols, int trans) {
 // One level of the recursion on the left operand L (Ml x Kl) and the right
 // operand R (Kl x Nl): pre-adds, seven sub-products (batched, or recursed into the
 // next level), post-add into `out32` (inner levels) or the caller's C (top level).
+// Storage address of logical block (bi, bj) of a rows x cols operand split 2 x 2.
+const void* block_of(const BlockedOperand& x, int64_t rows, int64_t cols, int bi, int bj) {
+  const uint16_t* base = static_cast<const uint16_t*>(x.ptr);
+  const int64_t hr = rows / 2, hc = cols / 2;
+  return x.trans ? base + (int64_t)bj * hc * x.ld + bi * hr : base + (int64_t)bi * hr * x.ld + bj * hc;
+}
+
+// The batched sub-products [first, first + count) of one level: fp16 temporaries, or
+// (overlap, products 0 and 1) the input blocks, fp32 results.
+hipError_t launch_products(const StrassenRun& run, int level, const BlockedOperand& L,
+                           const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
+                           int first, int count, bool inputs, int cus) {
+  const int64_t m = Ml / 2, k = Kl / 2, n = Nl / 2;
+  GemmBatch b{};
+  b.count = count;
+  b.cus = cus;
+  for (int j = 0; j < count; ++j) {
+    const int i = first + j;
+    GemmProblem& p = b.p[j];
+    if (inputs) {
+      // Winograd P1 = A11 B11, P2 = A12 B21
+      p.A = block_of(L, Ml, Kl, 0, i);
+      p.B = block_of(R, Kl, Nl, i, 0);
+      p.lda = L.ld;
+      p.ldb = R.ld;
+    } else {
+      BlockedOperand lo = temp_op(run.S[level][i], m, k, L.trans);
+      BlockedOperand ro = temp_op(run.T[level][i], k, n, R.trans);
+      p.A = lo.ptr; p.lda = lo.ld;
+      p.B = ro.ptr; p.ldb = ro.ld;
+    }
+    p.C = run.P[level][i]; p.Cin = nullptr; p.ldc = n;
+    p.M = (int)m; p.N = (int)n; p.K = (int)k;
+    p.alpha = 1.f; p.beta = 0.f;
+  }
+  KernelKey key{};
+  key.tile = run.sub_tile;
+  key.a_kcontig = !L.trans;
+  key.b_kcontig = R.trans;
+  key.dtype = inputs ? L.dtype : kF16;
+  key.epi = kEpiStore32;
+  key.vec = 1;
+  if (inputs) {
+    // the blocks keep the parent's leading dimension: whole 16-byte chunks only
+    for (int j = 0; j < count; ++j)
+      if (!aligned16(b.p[j].A) || !aligned16(b.p[j].B)) key.vec = 0;
+    if (L.ld % 8 || R.ld % 8) key.vec = 0;
+  }
+  return launch_gemm(key, b, run.c->stream);
+}
+
 fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOperand& L,
                               const BlockedOperand& R, int64_t Ml, int64_t Kl, int64_t Nl,
                               float* out32, int64_t ld32) {
   const Call& c = *run.c;
   const int64_t m = Ml / 2, k = Kl / 2, n = Nl / 2;
-  hipError_t e = launch_preadd(L, Ml, Kl, run.variant, 0, run.scale_a, run.S[level], c.stream);
-  if (e != hipSuccess) return FGEMM_ERR_HIP;
-  e = launch_preadd(R, Kl, Nl, run.variant, 1, run.scale_b, run.T[level], c.stream);
-  if (e != hipSuccess) return FGEMM_ERR_HIP;
-  if (level == run.depth) {
-    GemmBatch b{};
-    b.count = 7;
-    b.cus = run.cus;
-    for (int i = 0; i < 7; ++i) {
-      BlockedOperand lo = temp_op(run.S[level][i], m, k, L.trans);
-      BlockedOperand ro = temp_op(run.T[level][i], k, n, R.trans);
-      GemmProblem& p = b.p[i];
-      p.A = lo.ptr; p.lda = lo.ld;
-      p.B = ro.ptr; p.ldb = ro.ld;
-      p.C = run.P[level][i]; p.Cin = nullptr; p.ldc = n;
-      p.M = (int)m; p.N = (int)n; p.K = (int)k;
-      p.alpha = 1.f; p.beta = 0.f;
-    }
-    KernelKey key{};
-    key.tile = run.sub_tile;
-    key.a_kcontig = !L.trans;
-    key.b_kcontig = R.trans;
-    key.dtype = kF16;
-    key.epi = kEpiStore32;
-    key.vec = 1;
-    e = launch_gemm(key, b, c.stream);
+  hipError_t e;
+  if (run.overlap) {
+    // the sums were issued on the second stream before this level: P1 and P2 take
+    // the input blocks on 7/8 of the CUs meanwhile (the sums have the rest), then
+    // the other five follow once the sums are done
+    e = launch_products(run, level, L, R, Ml, Kl, Nl, 0, 2, true, run.cus - run.cus / 8);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c.stream, run.join, 0);
+    if (e == hipSuccess) e = launch_products(run, level, L, R, Ml, Kl, Nl, 2, 5, false, run.cus);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
+  } else if (level == run.depth) {
+    e = launch_preadd(L, Ml, Kl, run.variant, 0, run.scale_a, run.S[level], c.stream);
+    if (e == hipSuccess) e = launch_preadd(R, Kl, Nl, run.variant, 1, run.scale_b, run.T[level], c.stream);
+    if (e == hipSuccess) e = launch_products(run, level, L, R, Ml, Kl, Nl, 0, 7, false, run.cus);
     if (e != hipSuccess) return FGEMM_ERR_HIP;
   } else {
+    e = launch_preadd(L, Ml, Kl, run.variant, 0, run.scale_a, run.S[level], c.stream);
+    if (e == hipSuccess) e = launch_preadd(R, Kl, Nl, run.variant, 1, run.scale_b, run.T[level], c.stream);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
     for (int i = 0; i < 7; ++i) {
       fgemm_status_t st = strassen_level(run, level + 1, temp_op(run.S[level][i], m, k, L.trans),
                                          temp_op(run.T[level][i], k, n, R.trans), m, k, n,
@@ -500,6 +551,7 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
     pa.bias = (flags & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr;
     pa.scale_a = run.scale_a;
     pa.scale_b = run.scale_b;
+    pa.unscaled = run.overlap ? 3 : 0;  // P1, P2 of the input blocks
     if (flags & FGEMM_EPI_ROWSUMSQ) {
       pa.rowsumsq = c.epi->rowsumsq;
       pa.ss_partial = run.ss_partial;
@@ -550,20 +602,48 @@ fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Ca
       off += align256((size_t)(m * n * 4));
     }
   }
+  BlockedOperand L{c.A, c.lda, c.ta == FGEMM_OP_T, run.in_dtype, 0};
+  BlockedOperand R{c.B, c.ldb, c.tb == FGEMM_OP_T, run.in_dtype, 0};
+  // Winograd depth 1 overlapped: P1 and P2 need no operand sums (FalconGEMM page,
+  // group-parallel optimizations: additions overlapped with products), so max|x|,
+  // the scales and the sums of the other five run on the second stream while P1
+  // and P2 run on the caller's; their plain-block temporaries are not written.
+  // (the input blocks feed the 16-byte loads directly: whole 8-element block
+  // offsets, leading dimensions and base addresses)
+  const bool blocks16 = c.M % 16 == 0 && c.K % 16 == 0 && Nb % 16 == 0 && c.lda % 8 == 0 &&
+                        c.ldb % 8 == 0 && aligned16(c.A) && aligned16(c.B);
+  run.overlap = plan.variant == FGEMM_VARIANT_WINOGRAD && plan.depth == 1 && h->aux && blocks16;
+  run.aux = h->aux;
+  run.join = h->join;
+  const hipStream_t as = run.overlap ? h->aux : c.stream;
+  hipError_t e = hipSuccess;
+  if (run.overlap) {
+    e = hipEventRecord(h->fork, c.stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(as, h->fork, 0);
+    if (e != hipSuccess) return FGEMM_ERR_HIP;
+  }
   // power-of-two scales keeping every fp16 sum in range: at most 4^depth terms
   const float target = plan.depth == 1 ? 8192.f : 2048.f;
   int na = 0, nb = 0;
-  hipError_t e =
-      launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
-                    run.in_dtype, part_a, &na, c.stream);
+  e = launch_maxabs(c.A, c.lda, c.ta == FGEMM_OP_T ? c.K : c.M, c.ta == FGEMM_OP_T ? c.M : c.K,
+                    run.in_dtype, part_a, &na, as);
   if (e == hipSuccess)
     e = launch_maxabs(c.B, c.ldb, c.tb == FGEMM_OP_T ? Nb : c.K, c.tb == FGEMM_OP_T ? c.K : Nb,
-                      run.in_dtype, part_b, &nb, c.stream);
-  if (e == hipSuccess) e = launch_scale_from_max(part_a, na, target, run.scale_a, c.stream);
-  if (e == hipSuccess) e = launch_scale_from_max(part_b, nb, target, run.scale_b, c.stream);
+                      run.in_dtype, part_b, &nb, as);
+  if (e == hipSuccess) e = launch_scale_from_max(part_a, na, target, run.scale_a, as);
+  if (e == hipSuccess) e = launch_scale_from_max(part_b, nb, target, run.scale_b, as);
+  if (run.overlap) {
+    void* S[7];
+    void* T[7];
+    for (int q = 0; q < 7; ++q) {
+      S[q] = q < 2 ? nullptr : run.S[1][q];
+      T[q] = q < 2 ? nullptr : run.T[1][q];
+    }
+    if (e == hipSuccess) e = launch_preadd(L, c.M, c.K, run.variant, 0, run.scale_a, S, as);
+    if (e == hipSuccess) e = launch_preadd(R, c.K, Nb, run.variant, 1, run.scale_b, T, as);
+    if (e == hipSuccess) e = hipEventRecord(h->join, as);
+  }
   if (e != hipSuccess) return FGEMM_ERR_HIP;
-  BlockedOperand L{c.A, c.lda, c.ta == FGEMM_OP_T, run.in_dtype, 0};
-  BlockedOperand R{c.B, c.ldb, c.tb == FGEMM_OP_T, run.in_dtype, 0};
   return strassen_level(run, 1, L, R, c.M, c.K, Nb, nullptr, 0);
 }
 
@@ -703,6 +783,21 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
     (void)hipGetLastError();
     h->pools = 0;
   }
+  {
+    // the overlapped Winograd schedule's second stream (default priority) and
+    // events; without them that schedule runs on the caller's stream alone
+    DeviceGuard guard(device);
+    if (!guard.ok || hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      if (h->join) (void)hipEventDestroy(h->join);
+      if (h->fork) (void)hipEventDestroy(h->fork);
+      if (h->aux) (void)hipStreamDestroy(h->aux);
+      h->aux = nullptr;
+      h->fork = h->join = nullptr;
+    }
+  }
   double ghz = prop.clockRate > 0 ? prop.clockRate / 1e6 : 2.4;
   model_defaults(&h->model, prop.multiProcessorCount, ghz, (double)prop.totalGlobalMem);
   *handle = h;
@@ -711,6 +806,13 @@ fgemm_status_t fgemm_create(fgemm_handle_t* handle, int device) {
 
 fgemm_status_t fgemm_destroy(fgemm_handle_t h) {
   if (!h) return FGEMM_ERR_INVALID_VALUE;
+  if (h->aux) {
+    DeviceGuard guard(h->device);
+    (void)hipStreamSynchronize(h->aux);
+    (void)hipEventDestroy(h->join);
+    (void)hipEventDestroy(h->fork);
+    (void)hipStreamDestroy(h->aux);
+  }
   if (h->own_ws) {
     DeviceGuard guard(h->device);
     (void)hipDeviceSynchronize();

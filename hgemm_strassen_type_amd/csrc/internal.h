@@ -171,6 +171,9 @@ struct PostAddArgs {
   // act != 0 or rope_hd != 0: the activation or the rotary embedding before rounding
   int act; int rope_hd;
   const int32_t* rope_pos; int64_t rope_off; double rope_log2_base;
+  // Top level only.  Bit q set: product q was formed from the unscaled inputs, so it
+  // is unscaled by alpha alone (the others by alpha/(sa*sb)), in fp64.
+  int unscaled;
 };
 hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
 // Row-sum partials per output row the post-add writes for sub-block width n.

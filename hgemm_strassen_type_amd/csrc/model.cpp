@@ -163,10 +163,37 @@ size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int varian
   return total;
 }
 
+// Winograd at depth 1 runs overlapped: max|x|, the scales and the sums of P3..P7 on
+// a second stream beside P1 = A11 B11 and P2 = A12 B21 (no sums, the input blocks)
+// on 7/8 of the CUs; then P3..P7 on the whole chip and the post-add.  Measured on
+// the 16384^3 and 32768 x 8192^2 bf16 shapes: the sums reach about a quarter of the
+// chip's HBM rate on their eighth of the CUs, P1/P2 take 13 % longer beside them
+// than their CU share alone gives, and whatever sum traffic is left when P1/P2 end
+// runs at the full rate.
+double winograd_overlapped_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int beta,
+                              int* sub_tile) {
+  constexpr double kAuxBwShare = 0.25, kContention = 1.13, kProductRate = 0.93;
+  const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
+  const double m = (double)(M / 2), k = (double)(K / 2), n = (double)(N / 2);
+  // max passes, then sums: four blocks read and five fp16 operands written a side
+  const double aux = ((double)M * K + (double)K * N) * 2.0 + 9 * m * k * 2 + 9 * k * n * 2;
+  const double post = 7 * m * n * 4 + 4 * m * n * 2.0 + (beta ? 4 * m * n * 2.0 : 0.0);
+  double tp;  // a batch of seven products on the whole chip
+  const int tile = best_tile(md, M / 2, N / 2, K / 2, 0, 7, 2.0, 4.0, 0, &tp, 1);
+  if (sub_tile) *sub_tile = tile;
+  const double one = (tp - md.launch_us) * 1e-6 / kProductRate / 7.0;  // one product, s
+  const double t12 = 2 * one * 8.0 / 7.0 * kContention;
+  const double aux_slow = aux / (bw * kAuxBwShare);
+  const double t_aux = aux_slow <= t12 ? aux_slow : t12 + (aux - t12 * bw * kAuxBwShare) / bw;
+  const double t = (t12 > t_aux ? t12 : t_aux) + 5 * one + post / bw;
+  return t * 1e6 + 9 * md.launch_us;  // 4 max/scale, 2 sums, 2 product batches, post-add
+}
+
 double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int depth,
                         int variant, int beta, int* sub_tile) {
   const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
-  (void)variant;
+  if (variant == FGEMM_VARIANT_WINOGRAD && depth == 1)
+    return winograd_overlapped_us(md, M, N, K, beta, sub_tile);
   const double ns = 7;  // fp16 operands written per side (sums and plain blocks)
   double t = 0, launches = 0;
   // max|A|, max|B| for the fp16 scales

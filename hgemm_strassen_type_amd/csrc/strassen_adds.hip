@@ -131,7 +131,8 @@ __global__ void scale_from_max_kernel(const float* partial, int count, float tar
 // One pass over the four sub-blocks of an operand writes the seven operands of
 // that side's products, in product order, as scaled fp16: the block sums (chained
 // Winograd sums stay in fp32 registers) and the plain blocks, so that every
-// sub-product is a plain fp16 GEMM.
+// sub-product is a plain fp16 GEMM.  A null output is skipped (a product that
+// reads its plain block from the input instead).
 struct PreAddArgs {
   const uint16_t* blk[4];   // X11, X12, X21, X22 (logical blocks) in storage
   int64_t ld;               // source leading dimension
@@ -214,7 +215,8 @@ __global__ void preadd_kernel(PreAddArgs a) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 7; ++q) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
+    for (int q = 0; q < 7; ++q)
+      if (a.out[q]) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
   }
 }
 
@@ -233,13 +235,15 @@ struct PostAddKArgs {
   const float* rms_ss; float rms_inv_n, rms_eps;
   int act; int rope_hd;
   const int32_t* rope_pos; int64_t rope_off; double rope_log2_base;
+  int unscaled;        // bit q: product q was formed from the unscaled inputs
 };
 
-__device__ __forceinline__ void combine(int variant, const float (&p)[7], float* c) {
+template <class F>
+__device__ __forceinline__ void combine(int variant, const F (&p)[7], F* c) {
   if (variant == FGEMM_VARIANT_WINOGRAD) {
-    float u2 = p[0] + p[5];             // U2 = P1 + P6
-    float u3 = u2 + p[6];               // U3 = U2 + P7
-    float u4 = u2 + p[4];               // U4 = U2 + P5
+    F u2 = p[0] + p[5];                 // U2 = P1 + P6
+    F u3 = u2 + p[6];                   // U3 = U2 + P7
+    F u4 = u2 + p[4];                   // U4 = U2 + P5
     c[0] = p[0] + p[1];                 // C11 = P1 + P2
     c[1] = u4 + p[2];                   // C12 = U4 + P3
     c[2] = u3 - p[3];                   // C21 = U3 - P4
@@ -275,6 +279,11 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
   // fp64 and its one rounding is the one to fp32, as in an fp32 product.
   double factor = 1.0;
   if (!a.out32) factor = (double)a.alpha / (double)*a.scale_a / (double)*a.scale_b;
+  // products of unscaled inputs carry alpha alone: every product is brought to the
+  // output's scale in fp64 (exact: powers of two and fp32 values) and the seven are
+  // combined there, one rounding to fp32 at the end
+  const double f_unscaled = (double)a.alpha;
+  const double f_out = a.unscaled ? 1.0 : factor;
   const bool stats = a.ss_partial != nullptr;
   // rotary embedding: the rates of this lane's two pairs in each column block
   // (a lane keeps its columns for every row)
@@ -297,14 +306,27 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
         p[0][q] = v.x; p[1][q] = v.y; p[2][q] = v.z; p[3][q] = v.w;
       }
       float c[4][4];  // [element][block]
+      if (a.unscaled) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) combine(a.variant, p[e], c[e]);
+        for (int e = 0; e < 4; ++e) {
+          double pd[7], cd[4];
+#pragma unroll
+          for (int q = 0; q < 7; ++q)
+            pd[q] = ((a.unscaled >> q) & 1 ? f_unscaled : factor) * (double)p[e][q];
+          combine(a.variant, pd, cd);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) c[e][b] = (float)cd[b];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) combine(a.variant, p[e], c[e]);
+      }
       if (a.swiglu) {
         // blocks 0/1 (rows i) and 2/3 (rows m + i): gate, then up
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int64_t row = h * a.m + i;
-          const double r = (double)rsqrtf(a.rms_ss[row] * a.rms_inv_n + a.rms_eps) * factor;
+          const double r = (double)rsqrtf(a.rms_ss[row] * a.rms_inv_n + a.rms_eps) * f_out;
           const int64_t off = row * a.ldc + j;
           float v[4];
 #pragma unroll
@@ -334,7 +356,7 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
             const int64_t off = row * a.ldc + col;
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (float)(factor * c[e][b]);
+            for (int e = 0; e < 4; ++e) v[e] = (float)(f_out * c[e][b]);
             if (a.beta != 0.f) {
               uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
               v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
@@ -469,6 +491,8 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
   a.rope_pos = in.rope_pos;
   a.rope_off = in.rope_off;
   a.rope_log2_base = in.rope_log2_base;
+  a.unscaled = in.unscaled;
+  if (a.unscaled && a.out32) return hipErrorInvalidValue;
   if ((a.act || a.rope_hd) && (a.out32 || !in.C || a.swiglu)) return hipErrorInvalidValue;
   if (a.n % 4) return hipErrorInvalidValue;
   const bool stats = in.rowsumsq != nullptr;
