@@ -230,10 +230,12 @@ def main():
 
 def adds_workload(torch, h, fgemm, timer, uniform, args):
     """Winograd depth 1 on bf16 16384^3 (U[-1,1], beta 0): one step is one
-    fgemm_gemm call, which launches max|x| twice (A, B), the pre-add twice (A side,
-    B side), the batched sub-products once and the post-add once.  Algorithmic
-    bytes per launch with 8192^2 sub-blocks (m = k = n = 8192), 2-byte inputs and
-    outputs: pre-add 4*m*k*2 read + 7*m*k*2 written; post-add 7*m*n*4 read +
+    fgemm_gemm call.  Overlapped schedule: on a second stream max|x| twice (A, B)
+    and the pre-add twice (A side, B side), beside the batch of P1 and P2 (input
+    blocks) on the caller's stream; then the batch of P3..P7 and the post-add.
+    Algorithmic bytes per launch with 8192^2 sub-blocks (m = k = n = 8192), 2-byte
+    inputs and outputs: pre-add 4*m*k*2 read + 5*m*k*2 written (the operand sums
+    and the two plain blocks P3 and P4 take as fp16); post-add 7*m*n*4 read +
     4*m*n*2 written; max|x| 2*M*K read."""
     n = 16384
     m = n // 2
@@ -247,7 +249,7 @@ def adds_workload(torch, h, fgemm, timer, uniform, args):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "effective_tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 2),
             "launches_per_step": {"preadd_kernel": 2, "postadd_kernel": 1, "maxabs_kernel": 2},
-            "alg_bytes_per_launch": {"preadd_kernel": 4 * m * m * 2 + 7 * m * m * 2,
+            "alg_bytes_per_launch": {"preadd_kernel": 4 * m * m * 2 + 5 * m * m * 2,
                                      "postadd_kernel": 7 * m * m * 4 + 4 * m * m * 2,
                                      "maxabs_kernel": 2 * n * n}}
 

@@ -9,6 +9,8 @@
         "<kernel substring>" <FLOP per launch>
     python -m hgemm_strassen_type_amd.prof_summary adds <kernel_trace.csv> <fetch.csv>
         <write.csv> <bench stdout log> <out.md> "<commands>"
+    python -m hgemm_strassen_type_amd.prof_summary timeline <kernel_trace.csv> <out.md>
+        "<command>" "<first kernel substring>" "<title>" [<its launches per call>]
 
 `stats` keeps the per-kernel call count and average/min/max duration of a
 `--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
@@ -20,7 +22,9 @@ copy that `bench.py --copy-calib` runs in the same process (read 1 GiB, write
 for the decode kernel of `bench.py --only-decode`, whose JSON line has the same keys): per
 kernel, the average duration of the timed dispatches, the algorithmic bytes that
 bench.py states, the GB/s they make against the 8 TB/s HBM peak, and the
-counters' bytes per launch next to the algorithmic ones.
+counters' bytes per launch next to the algorithmic ones.  `timeline` lists the
+kernels of the last call of a trace (start, end, queue, workgroups), which shows
+what runs concurrently on two streams.
 """
 from __future__ import annotations
 
@@ -201,6 +205,43 @@ def clock(pmc_csv: str, out_md: str, command: str, kernel: str, flops: float, cu
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def timeline(trace_csv: str, out_md: str, command: str, first: str, title: str,
+             per_call: int = 1) -> None:
+    """The kernels of the last call in a `--kernel-trace` run, in start order, from
+    the `per_call`-th last dispatch whose name contains `first` (the call's first
+    kernel, which a call launches `per_call` times; kernels
+    of that call already running on another queue are included from the latest
+    start before it that overlaps it): start and end relative to that dispatch,
+    duration, hardware queue and workgroup count."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    marks = [i for i, r in enumerate(rows) if first in r["Kernel_Name"]]
+    if not marks:
+        raise SystemExit(f"no kernel matching {first!r}")
+    i0 = marks[-per_call]
+    t0 = int(rows[i0]["Start_Timestamp"])
+    # launches of the same call issued on another queue just before it, still running at t0
+    lo = i0
+    while lo > 0 and int(rows[lo - 1]["End_Timestamp"]) > t0 and \
+            rows[lo - 1]["Queue_Id"] != rows[i0]["Queue_Id"]:
+        lo -= 1
+    lines = [f"# Timeline of one call: {title} (rocprofv3 --kernel-trace)", "", "Command:", "",
+             "```", command, "```", "",
+             "| start us | end us | us | queue | workgroups | kernel |", "|---|---|---|---|---|---|"]
+    end = 0.0
+    for r in rows[lo:]:
+        s_us = (int(r["Start_Timestamp"]) - t0) / 1e3
+        e_us = (int(r["End_Timestamp"]) - t0) / 1e3
+        end = max(end, e_us)
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        wgs *= int(r.get("Grid_Size_Y") or 1) // max(1, int(r.get("Workgroup_Size_Y") or 1))
+        lines.append(f"| {s_us:.1f} | {e_us:.1f} | {e_us - s_us:.1f} | {r['Queue_Id']} | {wgs} | "
+                     f"`{_short(r['Kernel_Name'], 100)}` |")
+    first_start = (int(rows[lo]["Start_Timestamp"]) - t0) / 1e3
+    lines += ["", f"Call span: {end - first_start:.1f} us from the first start to the last end."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         extra = sys.argv[5:]
@@ -213,5 +254,8 @@ if __name__ == "__main__":
     elif sys.argv[1] == "adds":
         adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
              title=sys.argv[8] if len(sys.argv) > 8 else "the Strassen add kernels")
+    elif sys.argv[1] == "timeline":
+        timeline(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
+                 int(sys.argv[7]) if len(sys.argv) > 7 else 1)
     else:
         raise SystemExit(__doc__)

@@ -103,3 +103,34 @@ def test_clock_summary(tmp_path):
     assert float(cells[5]) == pytest.approx(1.05e12 / (256 * 4096) / 1.5e6, abs=1e-3)
     assert float(cells[6]) == pytest.approx(1050, abs=1)
     assert "| 8 |" not in out.read_text()
+
+
+def test_timeline_of_the_last_call(tmp_path):
+    """Two calls on two queues: the second call's kernels, with the product batch that
+    started on the other queue just before its first kernel, at times relative to
+    that kernel; workgroups from the grid and workgroup sizes."""
+    header = ["Kernel_Name", "Queue_Id", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+              "Workgroup_Size_X", "Grid_Size_Y", "Workgroup_Size_Y"]
+    rows = []
+    for base in (0, 100000):
+        rows += [["gemm_mfma_kernel<P1P2>", 2, base + 9000, base + 40000, 224 * 512, 512, 1, 1],
+                 ["maxabs_kernel(a)", 1, base + 10000, base + 13000, 8 * 256, 256, 4, 1],
+                 ["preadd_kernel(a)", 1, base + 13000, base + 30000, 4 * 256, 256, 8192, 1],
+                 ["gemm_mfma_kernel<P3P7>", 2, base + 41000, base + 90000, 256 * 512, 512, 1, 1],
+                 ["postadd_kernel(c)", 2, base + 90000, base + 95000, 32 * 256, 256, 8192, 1]]
+    write_csv(tmp_path / "t.csv", header, rows)
+    out = tmp_path / "t.md"
+    prof_summary.timeline(str(tmp_path / "t.csv"), str(out), "cmd", "maxabs", "test")
+    text = out.read_text()
+    body = [l for l in text.splitlines() if l.startswith("| ") and not l.startswith("| start")]
+    assert len(body) == 5
+    assert body[0].startswith("| -1.0 | 30.0 | 31.0 | 2 | 224 | `gemm_mfma_kernel<P1P2>`")
+    assert body[1].startswith("| 0.0 | 3.0 | 3.0 | 1 | 32 |")
+    assert body[4].startswith("| 80.0 | 85.0 | 5.0 | 2 | 262144 |")
+    assert "Call span: 86.0 us" in text
+    # a first kernel launched twice per call: the earlier of the last call's two
+    rows2 = [r for r in rows]
+    rows2.insert(2, ["maxabs_kernel(b)", 1, 100000 + 13000, 100000 + 13000, 8 * 256, 256, 4, 1])
+    write_csv(tmp_path / "t2.csv", header, rows2)
+    prof_summary.timeline(str(tmp_path / "t2.csv"), str(out), "cmd", "maxabs", "test", per_call=2)
+    assert "| 0.0 | 3.0 | 3.0 | 1 | 32 |" in out.read_text()
