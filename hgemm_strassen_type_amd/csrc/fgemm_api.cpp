@@ -1050,8 +1050,8 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
   if (flags & FGEMM_EPI_BIAS) { p.flags |= kFlagBias; p.bias = epi->bias; }
   int parts = 0;
   if (flags & FGEMM_EPI_ROWSUMSQ) {
-    // one partial per (128-column tile, wave column) and row
-    parts = (int)ceil_div(N, 128) * 2;
+    // one partial per (tile column, wave column) and row
+    parts = (int)ceil_div(N, kF8TileN) * kF8WavesN;
     void* ws;
     fgemm_status_t s = ensure_workspace(h, WsSource{}, (size_t)parts * (size_t)M * 4, st, &ws);
     if (s != FGEMM_OK) return s;

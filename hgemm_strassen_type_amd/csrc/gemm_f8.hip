@@ -9,8 +9,8 @@ namespace fgemm {
 template <int FA, int FB, int MX>
 static hipError_t by_output(const KernelKey& k, const GemmBatch& b, hipStream_t s) {
   constexpr int DT = f8_code(FA, FB, MX);
-  if (k.odt == kBF16) return launch_t<Cfg256x128f8, DT, true, true, kEpiStore16, true, kBF16>(b, s);
-  if (k.odt == kF16) return launch_t<Cfg256x128f8, DT, true, true, kEpiStore16, true, kF16>(b, s);
+  if (k.odt == kBF16) return launch_t<CfgF8, DT, true, true, kEpiStore16, true, kBF16>(b, s);
+  if (k.odt == kF16) return launch_t<CfgF8, DT, true, true, kEpiStore16, true, kF16>(b, s);
   return hipErrorInvalidValue;
 }
 

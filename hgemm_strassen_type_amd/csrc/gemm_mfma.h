@@ -209,7 +209,8 @@ struct GemmTile {
   static constexpr int MX_OFF = CFG::SMEM;
   static constexpr int MX_BUF = (CFG::BM + CFG::BN) * 16;
   static constexpr int MX_SLOTS_A = CFG::BM / 64, MX_SLOTS_B = CFG::BN / 64;
-  static_assert(!MX || MX_SLOTS_A + MX_SLOTS_B <= CFG::NW, "one scale slot per wave at most");
+  // 1 KB scale slots (64 rows of 16 bytes) a wave loads: slot q = wave + NW*i
+  static constexpr int MX_SW = (MX_SLOTS_A + MX_SLOTS_B + CFG::NW - 1) / CFG::NW;
   // k per MFMA step in 16-bit units (8-bit: 64 or 128 values) and steps per phase
   static constexpr int KSTEP = F8 ? (CFG::MI == 32 ? 32 : 64) : CFG::KSTEP;
   static constexpr int STEPS = CFG::BK / KSTEP;
@@ -240,7 +241,7 @@ struct GemmTile {
   struct LoadAddr {
     uint32_t a[CFG::QAW];
     uint32_t b[CFG::QBW];
-    uint32_t mx;  // MX: this wave's scale slot (row of A or B times its leading dimension)
+    uint32_t mx[MX ? MX_SW : 1];  // MX: the wave's scale slots (row of A or B times its ld)
   };
 
   // Rows and columns beyond M or N (edge tiles) are clamped onto the last valid
@@ -256,14 +257,18 @@ struct GemmTile {
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
     if constexpr (MX) {
-      // slot w < MX_SLOTS_A: rows 64w.. of A's tile; then rows of B's (clamped)
-      la.mx = 0;
-      if (wave < MX_SLOTS_A) {
-        const int r = m0 + 64 * wave + lane;
-        la.mx = (uint32_t)((int64_t)(r < P.M ? r : P.M - 1) * P.ld_mxa);
-      } else if (wave < MX_SLOTS_A + MX_SLOTS_B) {
-        const int r = n0 + 64 * (wave - MX_SLOTS_A) + lane;
-        la.mx = (uint32_t)((int64_t)(r < P.N ? r : P.N - 1) * P.ld_mxb);
+      // slot q < MX_SLOTS_A: rows 64q.. of A's tile; then rows of B's (clamped)
+#pragma unroll
+      for (int i = 0; i < MX_SW; ++i) {
+        const int q = wave + CFG::NW * i;
+        la.mx[i] = 0;
+        if (q < MX_SLOTS_A) {
+          const int r = m0 + 64 * q + lane;
+          la.mx[i] = (uint32_t)((int64_t)(r < P.M ? r : P.M - 1) * P.ld_mxa);
+        } else if (q < MX_SLOTS_A + MX_SLOTS_B) {
+          const int r = n0 + 64 * (q - MX_SLOTS_A) + lane;
+          la.mx[i] = (uint32_t)((int64_t)(r < P.N ? r : P.N - 1) * P.ld_mxb);
+        }
       }
     }
 #pragma unroll
@@ -321,9 +326,12 @@ struct GemmTile {
   __device__ __forceinline__ static void issue_scales(const Src& S, int g, int wave,
                                                       const LoadAddr& la, uint8_t* smem) {
     if constexpr (MX) {
-      if (wave < MX_SLOTS_A + MX_SLOTS_B) {
-        const char* base = uniform_ptr((wave < MX_SLOTS_A ? S.mxa : S.mxb) + 16 * g);
-        lds_dma(base, la.mx, lds_addr(smem + MX_OFF + (g & 1) * MX_BUF + wave * 1024));
+#pragma unroll
+      for (int i = 0; i < MX_SW; ++i) {
+        const int q = wave + CFG::NW * i;
+        if (q >= MX_SLOTS_A + MX_SLOTS_B) break;
+        const char* base = uniform_ptr((q < MX_SLOTS_A ? S.mxa : S.mxb) + 16 * g);
+        lds_dma(base, la.mx[i], lds_addr(smem + MX_OFF + (g & 1) * MX_BUF + q * 1024));
       }
     }
   }
@@ -1501,10 +1509,11 @@ using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using Cfg64 = TileCfg<64, 128, 2, 2, 32, 4>;
 using Cfg32 = TileCfg<32, 128, 1, 4, 64, 4>;
 using Cfg64n = TileCfg<64, 64, 2, 2, 64, 4>;
-// 8-bit inputs: 8 waves of 64x64 in 32x32x64 MFMA blocks (64 accumulators and two
-// 32-register fragment sets: two waves fit a SIMD), phases of 128 k (48 KB), three
-// stages
-using Cfg256x128f8 = TileCfg<256, 128, 4, 2, 64, 3, 1, 32>;
+// 8-bit inputs: 256 x 256 in 4 waves of 128 x 128 (one per SIMD, 256 accumulators in
+// AGPRs) in 32x32x64 MFMA blocks, phases of 128 k (64 KB), two stages.  Per phase a
+// CU reads half the LDS bytes per MFMA of 8 waves of 64 x 64 on 256 x 128 (which read
+// as much LDS as their MFMAs take cycles): 8-13 % faster at 8192^3 and the LLM shapes.
+using CfgF8 = TileCfg<256, kF8TileN, 2, kF8WavesN, 64, 2, 1, 32>;
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {

@@ -13,6 +13,9 @@ enum ElemType : int { kF16 = 0, kBF16 = 1 };
 // 8-bit MFMA inputs: one code for the formats of both operands, fa and fb each
 // 0 (E4M3) or 1 (E5M2), the MFMA's own format numbers.
 constexpr int kF8Base = 4;
+// Column width and wave columns of the 8-bit kernels' tile (row-statistics partials
+// are [ceil(N / kF8TileN) * kF8WavesN][M]).
+constexpr int kF8TileN = 256, kF8WavesN = 2;
 constexpr int f8_code(int fa, int fb, int mx = 0) { return kF8Base + 4 * mx + 2 * fa + fb; }
 
 // Epilogue kinds the kernel template is instantiated for.
