@@ -18,6 +18,9 @@ What it computes (see the header of ``oracle.c`` for the passages it follows):
 * ``gemm_f8``    the 8-bit GEMM A B^T on E4M3 / E5M2 values with per-tensor scales
                  or E8M0 scales per block of 32 along K (MXFP8), same epilogue and
                  rounding as ``gemm``; ``decode_f8`` / ``decode_e8m0`` the formats.
+* ``bilinear``   (oracle/bilinear.py) block schemes as coefficient tables (U, V, W):
+                 Strassen (1969), Winograd's form and the rectangular <2,2,3;11>, their
+                 Brent equations checked exactly, and the product through a scheme.
 * ``gemm_dense`` / ``gemm_f8_dense``  the unrounded product of every row through
                  one fp64 library matmul (whole-output checks at full size), with
                  the magnitude |alpha||A||B| + |beta||C| that ``elementwise_bound``
@@ -33,6 +36,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from . import bilinear  # noqa: E402,F401  (block schemes; pure numpy)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")

@@ -791,3 +791,51 @@ def test_rms_swiglu_derivatives_by_central_differences():
         Hm[:, col] -= h
         num = (f(Hp) - f(Hm))[:, col % F] / (2 * h)
         assert np.allclose(num, d[:, col % F], rtol=1e-6, atol=1e-9)
+
+
+# ------------------------------------------------------------ bilinear block schemes
+@pytest.mark.parametrize("name", ["S69", "WINOGRAD", "R223"])
+def test_scheme_brent_equations_and_every_coefficient_matters(name):
+    """The scheme's tables satisfy every Brent equation exactly; zeroing any one
+    nonzero coefficient, or flipping its sign, breaks at least one."""
+    from oracle import bilinear
+    s = bilinear.SCHEMES[name]
+    assert bilinear.brent_ok(s)
+    for key in ("U", "V", "W"):
+        T = s[key]
+        for idx in zip(*np.nonzero(T)):
+            for new in (0, -T[idx]):
+                t = dict(s)
+                t[key] = T.copy()
+                t[key][idx] = new
+                assert not bilinear.brent_ok(t), (name, key, idx, new)
+
+
+@pytest.mark.parametrize("name,shape", [("S69", (6, 10, 4)), ("WINOGRAD", (8, 4, 12)),
+                                        ("R223", (6, 8, 9)), ("R223", (4, 2, 3))])
+def test_scheme_exact_on_integers(name, shape):
+    """Integer operands: the product through the scheme equals the exact int64 product."""
+    from oracle import bilinear
+    M, K, N = shape
+    rng = np.random.default_rng(M * 100 + N)
+    A = rng.integers(-9, 10, size=(M, K))
+    B = rng.integers(-9, 10, size=(K, N))
+    assert np.array_equal(bilinear.apply(A, B, bilinear.SCHEMES[name]), (A @ B).astype(np.float64))
+
+
+@pytest.mark.parametrize("name,variant", [("S69", oracle.S69), ("WINOGRAD", oracle.WINOGRAD)])
+def test_scheme_tables_match_the_recursion_oracle(name, variant):
+    """The S69 and Winograd tables reproduce the C oracle's depth-1 recursion (written
+    from the block formulas, not from the tables) bit for bit on integer inputs."""
+    from oracle import bilinear
+    A = inputs.integers((16, 24), 81, BF16, -6, 6)
+    B = inputs.integers((24, 20), 82, BF16, -6, 6)
+    ref = oracle.strassen(A, B, depth=1, variant=variant, dtype=BF16)
+    got = bilinear.apply(oracle.decode(A, BF16), oracle.decode(B, BF16), bilinear.SCHEMES[name])
+    assert np.array_equal(got, ref)
+
+
+def test_rectangular_scheme_rejects_shapes_that_do_not_split():
+    from oracle import bilinear
+    with pytest.raises(ValueError):
+        bilinear.apply(np.ones((4, 4)), np.ones((4, 4)), bilinear.R223)  # N = 4 not / 3
