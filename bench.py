@@ -545,8 +545,7 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
                              "effective_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
             code = fgemm.FGEMM_BF16 if dt == torch.bfloat16 else fgemm.FGEMM_F16
             pick = h.select(M, N, K, dtype=code)
-            pname = "classical" if pick.path == 0 else \
-                f"{'winograd' if pick.variant == WIN else 's69'}_d{pick.depth}"
+            pname = plan_name(pick)
             best = min(res, key=lambda k: res[k]["ms"])
             res["model_pick"] = pname
             res["model_pred_us"] = round(pick.t_pred_us, 1)
@@ -571,14 +570,40 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
             ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), 3, 1, WARM_MS)
             res[name] = {"ms": round(ms, 4),
                          "effective_tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 2)}
-        res["model_pick_plan"] = "classical" if pick.path == 0 else \
-            f"{'winograd' if pick.variant == WIN else 's69'}_d{pick.depth}"
+        res["model_pick_plan"] = plan_name(pick)
         key = f"strassen_{dname}_{n}x{n}x{n}_ld+{pad}"
         W[key] = res
         log(f"{key}: {res}")
         del A, B, C
         torch.cuda.empty_cache()
+    # the rectangular <2,2,3;11> scheme on a shape whose N splits in three (and in two)
+    M, N, K = 16384, 24576, 16384
+    A = uniform((M, K), 5001, torch.bfloat16)
+    B = uniform((K, N), 5002, torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    cands = {"classical": fgemm.classical_plan(),
+             "r223_d1": fgemm.strassen_plan(1, fgemm.FGEMM_VARIANT_R223),
+             "s69_d1": fgemm.strassen_plan(1, S69), "winograd_d1": fgemm.strassen_plan(1, WIN)}
+    for name, pl in cands.items():
+        ms = timer.time(lambda: h.gemm(A, B, C, plan=pl), 3, 1, WARM_MS)
+        res[name] = {"ms": round(ms, 4),
+                     "effective_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+    res["model_pick"] = plan_name(h.select(M, N, K, dtype=fgemm.FGEMM_BF16))
+    key = f"scheme_bf16_{M}x{N}x{K}"
+    W[key] = res
+    log(f"{key}: {res}")
+    del A, B, C
+    torch.cuda.empty_cache()
     return W
+
+
+def plan_name(p):
+    """classical, or the scheme and depth of a Strassen-path plan (s69_d1, winograd_d2,
+    r223_d1, ...)."""
+    if p.path == 0:
+        return "classical"
+    return f"{({0: 's69', 1: 'winograd', 2: 'r223'}).get(p.variant, 'scheme')}_d{p.depth}"
 
 
 def cpu_model():

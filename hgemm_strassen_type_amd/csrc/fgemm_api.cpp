@@ -129,6 +129,15 @@ fgemm_status_t check_plan_shape(const fgemm_plan_t& p, int64_t M, int64_t N, int
   }
   if (p.path != FGEMM_PATH_STRASSEN) return FGEMM_ERR_INVALID_VALUE;
   if (p.depth < 1 || p.depth > 2) return FGEMM_ERR_INVALID_VALUE;
+  if (const BlockScheme* s = block_scheme(p.variant)) {
+    // table-driven schemes: one level, 16-element blocks, epilogues NONE and BIAS
+    if (p.depth != 1) return FGEMM_ERR_INVALID_VALUE;
+    if (flags & ~(uint32_t)FGEMM_EPI_BIAS) return FGEMM_ERR_NOT_SUPPORTED;
+    if (M % (16 * s->mb) || K % (16 * s->kb) || N % (16 * s->nb) || M == 0 || N == 0 || K == 0)
+      return FGEMM_ERR_NOT_SUPPORTED;
+    if (!vec) return FGEMM_ERR_NOT_SUPPORTED;
+    return FGEMM_OK;
+  }
   if (p.variant != FGEMM_VARIANT_S69 && p.variant != FGEMM_VARIANT_WINOGRAD)
     return FGEMM_ERR_INVALID_VALUE;
   // the recursion runs on op(B)'s Nb columns (2N with SwiGLU: its top split is the
@@ -200,7 +209,9 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
   p.t_classical_pred_us = tc;
   p.pred_rel_err = predicted_rel_err(dtype, 0, 0);
   for (int depth = 1; depth <= (classical_only ? 0 : 2); ++depth) {
-    for (int variant = FGEMM_VARIANT_S69; variant <= FGEMM_VARIANT_WINOGRAD; ++variant) {
+    for (int variant = FGEMM_VARIANT_S69; variant <= FGEMM_VARIANT_R223; ++variant) {
+      const BlockScheme* bs = block_scheme(variant);
+      if (bs && depth != 1) continue;
       fgemm_plan_t c{};
       c.path = FGEMM_PATH_STRASSEN;
       c.depth = depth;
@@ -217,6 +228,7 @@ fgemm_status_t select_plan(const fgemm_model_t& md, int64_t M, int64_t N, int64_
       // sub-problems below 512 never pay for their additions; keep them classical
       if ((M >> depth) < 512 || ((swiglu ? 2 * N : N) >> depth) < 512 || (K >> depth) < 512)
         continue;
+      if (bs && (M / bs->mb < 512 || N / bs->nb < 512 || K / bs->kb < 512)) continue;
       const int64_t Nb = swiglu ? 2 * N : N;
       const size_t ws = strassen_workspace(M, Nb, K, depth, variant) +
                         strassen_stats_bytes(M, Nb, flags);
@@ -569,7 +581,99 @@ fgemm_status_t strassen_level(const StrassenRun& run, int level, const BlockedOp
   return hip_status(e);
 }
 
+// A table-driven block scheme at depth 1: max|x| and the fp16 scales, one pre-add
+// pass a side writing the R product operands, the products in batches of at most
+// seven, one post-add pass writing C with alpha, beta*C and bias.
+fgemm_status_t run_scheme(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c,
+                          const BlockScheme& s) {
+  const int64_t m = c.M / s.mb, k = c.K / s.kb, n = c.N / s.nb;
+  // the post-add reads the bias four columns (8 bytes) at a time
+  const void* bias = (epi_flags(c.epi) & FGEMM_EPI_BIAS) ? c.epi->bias : nullptr;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 7)) return FGEMM_ERR_NOT_SUPPORTED;
+  const size_t need = strassen_workspace(c.M, c.N, c.K, 1, plan.variant);
+  void* ws;
+  fgemm_status_t st = ensure_workspace(h, WsSource{}, need, c.stream, &ws);
+  if (st != FGEMM_OK) return st;
+  const int in_dtype = c.dtype == FGEMM_BF16 ? kBF16 : kF16;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* scale_a = reinterpret_cast<float*>(base + 64);
+  float* scale_b = reinterpret_cast<float*>(base + 128);
+  float* part_a = reinterpret_cast<float*>(base + 256);
+  float* part_b = part_a + kMaxPartials;
+  void* S[kLinMaxProducts];
+  void* T[kLinMaxProducts];
+  const float* P[kLinMaxProducts];
+  size_t off = kScaleHeaderBytes;
+  for (int r = 0; r < s.R; ++r) { S[r] = base + off; off += align256((size_t)(m * k * 2)); }
+  for (int r = 0; r < s.R; ++r) { T[r] = base + off; off += align256((size_t)(k * n * 2)); }
+  for (int r = 0; r < s.R; ++r) {
+    P[r] = reinterpret_cast<float*>(base + off);
+    off += align256((size_t)(m * n * 4));
+  }
+  const bool ta = c.ta == FGEMM_OP_T, tb = c.tb == FGEMM_OP_T;
+  // power-of-two scales keeping every fp16 sum in range (sums of at most four blocks)
+  int na = 0, nb = 0;
+  hipError_t e = launch_maxabs(c.A, c.lda, ta ? c.K : c.M, ta ? c.M : c.K, in_dtype, part_a, &na,
+                               c.stream);
+  if (e == hipSuccess)
+    e = launch_maxabs(c.B, c.ldb, tb ? c.N : c.K, tb ? c.K : c.N, in_dtype, part_b, &nb, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(part_a, na, 8192.f, scale_a, c.stream);
+  if (e == hipSuccess) e = launch_scale_from_max(part_b, nb, 8192.f, scale_b, c.stream);
+  BlockedOperand L{c.A, c.lda, ta, in_dtype, 0};
+  BlockedOperand R{c.B, c.ldb, tb, in_dtype, 0};
+  if (e == hipSuccess)
+    e = launch_lin_pre(L, c.M, c.K, s.mb, s.kb, s.R, s.U, scale_a, S, c.stream);
+  if (e == hipSuccess)
+    e = launch_lin_pre(R, c.K, c.N, s.kb, s.nb, s.R, s.V, scale_b, T, c.stream);
+  int sub_tile = tile_id(plan.tile_m, plan.tile_n);
+  if (sub_tile != 0 && sub_tile != 1) sub_tile = 0;
+  for (int r0 = 0; e == hipSuccess && r0 < s.R; r0 += 7) {
+    GemmBatch b{};
+    b.count = s.R - r0 < 7 ? s.R - r0 : 7;
+    b.cus = h->cus;
+    for (int j = 0; j < b.count; ++j) {
+      BlockedOperand lo = temp_op(S[r0 + j], m, k, ta);
+      BlockedOperand ro = temp_op(T[r0 + j], k, n, tb);
+      GemmProblem& p = b.p[j];
+      p.A = lo.ptr; p.lda = lo.ld;
+      p.B = ro.ptr; p.ldb = ro.ld;
+      p.C = const_cast<float*>(P[r0 + j]); p.Cin = nullptr; p.ldc = n;
+      p.M = (int)m; p.N = (int)n; p.K = (int)k;
+      p.alpha = 1.f; p.beta = 0.f;
+    }
+    KernelKey key{};
+    key.tile = sub_tile;
+    key.a_kcontig = !ta;
+    key.b_kcontig = tb;
+    key.dtype = kF16;
+    key.epi = kEpiStore32;
+    key.vec = 1;
+    e = launch_gemm(key, b, c.stream);
+  }
+  if (e == hipSuccess) {
+    LinPostArgs pa{};
+    for (int r = 0; r < s.R; ++r) pa.P[r] = P[r];
+    pa.np = s.R;
+    pa.m = m;
+    pa.n = n;
+    pa.mbc = s.mb;
+    pa.nbc = s.nb;
+    pa.coef = s.W;
+    pa.C = c.C;
+    pa.ldc = c.ldc;
+    pa.dtype = in_dtype;
+    pa.alpha = c.alpha;
+    pa.beta = c.beta;
+    pa.bias = bias;
+    pa.scale_a = scale_a;
+    pa.scale_b = scale_b;
+    e = launch_lin_post(pa, c.stream);
+  }
+  return hip_status(e);
+}
+
 fgemm_status_t run_strassen(fgemm_handle_t h, const fgemm_plan_t& plan, const Call& c) {
+  if (const BlockScheme* bs = block_scheme(plan.variant)) return run_scheme(h, plan, c, *bs);
   const uint32_t flags = epi_flags(c.epi);
   const int64_t Nb = (flags & FGEMM_EPI_RMS_SWIGLU) ? 2 * c.N : c.N;  // columns of op(B)
   const size_t body = strassen_workspace(c.M, Nb, c.K, plan.depth, plan.variant);

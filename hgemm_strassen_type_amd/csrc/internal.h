@@ -182,6 +182,30 @@ hipError_t launch_postadd(const PostAddArgs& args, hipStream_t stream);
 // Row-sum partials per output row the post-add writes for sub-block width n.
 int64_t postadd_ss_parts(int64_t n);
 
+// Table-driven block schemes (rectangular and tensor-decomposition LCMAs): at most
+// kLinMaxBlocks blocks per operand or output and kLinMaxProducts products.
+constexpr int kLinMaxBlocks = 6, kLinMaxProducts = 12;
+// One pass over the br x bc logical blocks of a rows x cols operand writes the nout
+// fp16 product operands out[q] = scale * sum_b coef[q*br*bc + b] * block_b (stored in
+// the operand's orientation, leading dimension the stored block width).
+hipError_t launch_lin_pre(const BlockedOperand& src, int64_t rows, int64_t cols, int br, int bc,
+                          int nout, const signed char* coef, const float* scale, void* const* out,
+                          hipStream_t stream);
+// Output block (cb / nbc, cb % nbc) of C = RNE16(alpha/(sa*sb) * sum_r coef[cb*np + r] P_r
+// + beta*C + bias); the products are m x n fp32 (leading dimension n).
+struct LinPostArgs {
+  const float* P[kLinMaxProducts];
+  int np;
+  int64_t m, n;
+  int mbc, nbc;
+  const signed char* coef;
+  void* C; int64_t ldc; int dtype;
+  float alpha, beta;
+  const void* bias;
+  const float* scale_a; const float* scale_b;
+};
+hipError_t launch_lin_post(const LinPostArgs& args, hipStream_t stream);
+
 // Split-K finalize: C = RNE16(alpha * sum_s part[s] + beta*C + bias), part[s] is
 // M x N fp32 (leading dimension N), C is 16-bit with leading dimension ldc.
 hipError_t launch_splitk_finalize(const float* part, int splits, int64_t M, int64_t N,

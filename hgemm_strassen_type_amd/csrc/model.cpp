@@ -81,6 +81,9 @@ void model_defaults(fgemm_model_t* m, int cus, double clock_ghz, double device_b
 double predicted_rel_err(int dtype, int variant, int depth) {
   if (depth <= 0) return 1e-4;  // fp32 accumulation and one rounding (measured <= 6.4e-5)
   const bool bf = dtype == FGEMM_BF16;
+  // <2,2,3;11>: S69's seven products on two thirds of C, fp16-scaled plain blocks on
+  // the last third; measured 5.6-6.7e-4 (bf16) and 5.05e-4 (fp16) at 1024 x 1536 x 1024
+  if (variant == FGEMM_VARIANT_R223) return bf ? 7.3e-4 : 5.5e-4;
   const bool s69 = variant == FGEMM_VARIANT_S69;
   if (depth == 1) return s69 ? (bf ? 8.6e-4 : 6.5e-4) : (bf ? 1.17e-3 : 8.4e-4);
   return s69 ? (bf ? 1.64e-3 : 1.33e-3) : (bf ? 2.6e-3 : 2.26e-3);
@@ -150,8 +153,80 @@ double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int
   return (overlap(t_compute, t_mem) + fin) * 1e6 + 2 * md.launch_us;
 }
 
+// <2,2,3;11>: Strassen (1969) on op(B) and C's first two column blocks, then the four
+// block products of the third (C13 = A11 B13 + A12 B23, C23 = A21 B13 + A22 B23).
+// Blocks of op(A): A11 A12 A21 A22; of op(B): B11 B12 B13 B21 B22 B23; of C: C11 C12
+// C13 C21 C22 C23.
+namespace {
+const signed char kR223U[11 * 4] = {
+    1, 0, 0, 1,    // M1: A11 + A22
+    0, 0, 1, 1,    // M2: A21 + A22
+    1, 0, 0, 0,    // M3: A11
+    0, 0, 0, 1,    // M4: A22
+    1, 1, 0, 0,    // M5: A11 + A12
+    -1, 0, 1, 0,   // M6: A21 - A11
+    0, 1, 0, -1,   // M7: A12 - A22
+    1, 0, 0, 0,    // M8: A11
+    0, 1, 0, 0,    // M9: A12
+    0, 0, 1, 0,    // M10: A21
+    0, 0, 0, 1,    // M11: A22
+};
+const signed char kR223V[11 * 6] = {
+    1, 0, 0, 0, 1, 0,    // M1: B11 + B22
+    1, 0, 0, 0, 0, 0,    // M2: B11
+    0, 1, 0, 0, -1, 0,   // M3: B12 - B22
+    -1, 0, 0, 1, 0, 0,   // M4: B21 - B11
+    0, 0, 0, 0, 1, 0,    // M5: B22
+    1, 1, 0, 0, 0, 0,    // M6: B11 + B12
+    0, 0, 0, 1, 1, 0,    // M7: B21 + B22
+    0, 0, 1, 0, 0, 0,    // M8: B13
+    0, 0, 0, 0, 0, 1,    // M9: B23
+    0, 0, 1, 0, 0, 0,    // M10: B13
+    0, 0, 0, 0, 0, 1,    // M11: B23
+};
+const signed char kR223W[6 * 11] = {
+    1, 0, 0, 1, -1, 0, 1, 0, 0, 0, 0,    // C11 = M1 + M4 - M5 + M7
+    0, 0, 1, 0, 1, 0, 0, 0, 0, 0, 0,     // C12 = M3 + M5
+    0, 0, 0, 0, 0, 0, 0, 1, 1, 0, 0,     // C13 = M8 + M9
+    0, 1, 0, 1, 0, 0, 0, 0, 0, 0, 0,     // C21 = M2 + M4
+    1, -1, 1, 0, 0, 1, 0, 0, 0, 0, 0,    // C22 = M1 - M2 + M3 + M6
+    0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 1,     // C23 = M10 + M11
+};
+const BlockScheme kR223{2, 2, 3, 11, kR223U, kR223V, kR223W};
+}  // namespace
+
+const BlockScheme* block_scheme(int variant) {
+  return variant == FGEMM_VARIANT_R223 ? &kR223 : nullptr;
+}
+
+// Time of a table-driven scheme at depth 1: max|x| passes, one pre-add pass a side
+// (its blocks read, R fp16 operands written), R products of the block size, the
+// post-add (R fp32 products read, C written, beta*C read).
+double scheme_time_us(const fgemm_model_t& md, const BlockScheme& s, int64_t M, int64_t N,
+                      int64_t K, int beta, int* sub_tile) {
+  const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
+  const double m = (double)(M / s.mb), k = (double)(K / s.kb), n = (double)(N / s.nb);
+  const double R = s.R;
+  double bytes = ((double)M * K + (double)K * N) * 2.0;                // max|x|
+  bytes += s.mb * s.kb * m * k * 2 + R * m * k * 2;                     // pre-add, A side
+  bytes += s.kb * s.nb * k * n * 2 + R * k * n * 2;                     // pre-add, B side
+  bytes += R * m * n * 4 + (double)M * N * 2 * (beta ? 2.0 : 1.0);     // post-add
+  double tp;  // a batch of seven products (the batches hold at most seven)
+  const int tile = best_tile(md, M / s.mb, N / s.nb, K / s.kb, 0, 7, 2.0, 4.0, 0, &tp, 1);
+  if (sub_tile) *sub_tile = tile;
+  constexpr double kProductRate = 0.93;  // fp16 operands, fp32 outputs (as for Strassen)
+  const double one = (tp - md.launch_us) * 1e-6 / kProductRate / 7.0;
+  const int launches = 4 + 2 + (s.R + 6) / 7 + 1;
+  return (bytes / bw + R * one) * 1e6 + launches * md.launch_us;
+}
+
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant) {
-  (void)variant;
+  if (const BlockScheme* s = block_scheme(variant)) {
+    if (depth != 1) return 0;
+    const int64_t m = M / s->mb, k = K / s->kb, n = N / s->nb;
+    return kScaleHeaderBytes + (align256((size_t)(m * k * 2)) + align256((size_t)(k * n * 2)) +
+                                align256((size_t)(m * n * 4))) * (size_t)s->R;
+  }
   const int64_t ns = 7;  // the seven fp16 operands of each side's products
   size_t total = kScaleHeaderBytes;
   for (int l = 1; l <= depth; ++l) {
@@ -194,6 +269,7 @@ double strassen_time_us(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K
   const double bw = md.hbm_gbps * 1e9 * md.eta_hbm;
   if (variant == FGEMM_VARIANT_WINOGRAD && depth == 1)
     return winograd_overlapped_us(md, M, N, K, beta, sub_tile);
+  if (const BlockScheme* s = block_scheme(variant)) return scheme_time_us(md, *s, M, N, K, beta, sub_tile);
   const double ns = 7;  // fp16 operands written per side (sums and plain blocks)
   double t = 0, launches = 0;
   // max|A|, max|B| for the fp16 scales
@@ -238,7 +314,9 @@ extern "C" double fgemm_plan_rel_err(fgemm_dtype_t dtype, const fgemm_plan_t* pl
   if (!plan || (dtype != FGEMM_F16 && dtype != FGEMM_BF16)) return -1.0;
   if (plan->path == FGEMM_PATH_CLASSICAL) return predicted_rel_err(dtype, 0, 0);
   if (plan->path != FGEMM_PATH_STRASSEN || plan->depth < 1 || plan->depth > 2 ||
-      (plan->variant != FGEMM_VARIANT_S69 && plan->variant != FGEMM_VARIANT_WINOGRAD))
+      (plan->variant != FGEMM_VARIANT_S69 && plan->variant != FGEMM_VARIANT_WINOGRAD &&
+       plan->variant != FGEMM_VARIANT_R223) ||
+      (plan->variant == FGEMM_VARIANT_R223 && plan->depth != 1))
     return -1.0;
   return predicted_rel_err(dtype, plan->variant, plan->depth);
 }

@@ -41,6 +41,17 @@ int best_tile(const fgemm_model_t& md, int64_t M, int64_t N, int64_t K, int swig
 // Split-K plan of `splits` K slices with an fp32 finalize pass.
 double splitk_time_us(const fgemm_model_t& md, const TileInfo& t, int64_t M, int64_t N,
                       int64_t K, int splits, int beta);
+// Table-driven block schemes: op(A) in mb x kb blocks, op(B) in kb x nb, C in mb x nb;
+// R products P_r = (sum_a U[r*mb*kb + a] A_a)(sum_b V[r*kb*nb + b] B_b) and output
+// blocks C_c = sum_r W[c*R + r] P_r (blocks numbered row by row).  Null for the 2 x 2
+// recursive variants, which have their own chained kernels.
+struct BlockScheme {
+  int mb, kb, nb, R;
+  const signed char* U;
+  const signed char* V;
+  const signed char* W;
+};
+const BlockScheme* block_scheme(int variant);
 size_t strassen_workspace(int64_t M, int64_t N, int64_t K, int depth, int variant);
 // Predicted normwise error against the exactly rounded result (depth 0: classical).
 double predicted_rel_err(int dtype, int variant, int depth);

@@ -401,6 +401,123 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
   }
 }
 
+// ------------------------------------------------------------ table-driven schemes
+// A block scheme given by its coefficient tables (FalconGEMM page, Methodology 1:
+// tensor-decomposition LCMAs; the rectangular <2,2,3;11> among them).  One pass per
+// operand side reads that side's blocks once and writes every product operand
+// sum_b coef[q][b] X_b as scaled fp16; one pass over the products writes every output
+// block sum_r coef[c][r] P_r with the top-level epilogue (alpha, beta*C, bias).
+struct LinPreKArgs {
+  const uint16_t* blk[kLinMaxBlocks];   // logical blocks in storage, block order
+  int nblk;
+  int64_t ld, srows, scols;             // source leading dimension, stored block shape
+  uint16_t* out[kLinMaxProducts];       // fp16 outputs, stored srows x scols
+  int nout;
+  signed char coef[kLinMaxProducts][kLinMaxBlocks];
+  int dt;
+  const float* scale;
+};
+
+__global__ __launch_bounds__(256) void lin_pre_kernel(LinPreKArgs a) {
+  const float s = *a.scale;
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (c >= a.scols) return;
+  for (int64_t r = blockIdx.y; r < a.srows; r += gridDim.y) {
+    const int64_t si = r * a.ld + c;
+    float x[kLinMaxBlocks][8];
+#pragma unroll
+    for (int b = 0; b < kLinMaxBlocks; ++b) {
+      if (b < a.nblk) {
+        unpack8(*reinterpret_cast<const uint4*>(a.blk[b] + si), a.dt, x[b]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[b][e] *= s;
+      }
+    }
+    const int64_t di = r * a.scols + c;
+#pragma unroll
+    for (int q = 0; q < kLinMaxProducts; ++q) {
+      if (q < a.nout) {
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < kLinMaxBlocks; ++b) {
+          const int w = b < a.nblk ? a.coef[q][b] : 0;
+          if (w != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += (float)w * x[b][e];
+          }
+        }
+        *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o);
+      }
+    }
+  }
+}
+
+struct LinPostKArgs {
+  const float* P[kLinMaxProducts];      // products, each m x n (leading dimension n)
+  int np;
+  int64_t m, n;
+  int mbc, nbc;                         // output blocks: mbc x nbc of m x n
+  signed char coef[kLinMaxBlocks][kLinMaxProducts];
+  uint16_t* C; int64_t ldc; int dt;
+  float alpha, beta;
+  const uint16_t* bias;
+  const float* scale_a; const float* scale_b;
+};
+
+__global__ __launch_bounds__(256) void lin_post_kernel(LinPostKArgs a) {
+  const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (j >= a.n) return;
+  // alpha / (sa*sb) in fp64, as in the Strassen post-add (both scales powers of two)
+  const double factor = (double)a.alpha / (double)*a.scale_a / (double)*a.scale_b;
+  for (int64_t i = blockIdx.y; i < a.m; i += gridDim.y) {
+    float p[kLinMaxProducts][4];
+#pragma unroll
+    for (int r = 0; r < kLinMaxProducts; ++r) {
+      if (r < a.np) {
+        const float4 v = *reinterpret_cast<const float4*>(a.P[r] + i * a.n + j);
+        p[r][0] = v.x; p[r][1] = v.y; p[r][2] = v.z; p[r][3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < kLinMaxBlocks; ++cb) {
+      if (cb < a.mbc * a.nbc) {
+        float c4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kLinMaxProducts; ++r) {
+          const int w = r < a.np ? a.coef[cb][r] : 0;
+          if (w != 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c4[e] += (float)w * p[r][e];
+          }
+        }
+        const int64_t row = (int64_t)(cb / a.nbc) * a.m + i;
+        const int64_t col = (int64_t)(cb % a.nbc) * a.n + j;
+        const int64_t off = row * a.ldc + col;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)(factor * c4[e]);
+        if (a.beta != 0.f) {
+          uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+          v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
+          v[1] += a.beta * h2f(cv.x >> 16, a.dt);
+          v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
+          v[3] += a.beta * h2f(cv.y >> 16, a.dt);
+        }
+        if (a.bias) {
+          uint2 bv = *reinterpret_cast<const uint2*>(a.bias + col);
+          v[0] += h2f(bv.x & 0xffffu, a.dt);
+          v[1] += h2f(bv.x >> 16, a.dt);
+          v[2] += h2f(bv.y & 0xffffu, a.dt);
+          v[3] += h2f(bv.y >> 16, a.dt);
+        }
+        *reinterpret_cast<uint2*>(a.C + off) =
+            make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
+                       f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+      }
+    }
+  }
+}
+
 int stream_grid(int64_t work_items) {
   // enough workgroups to cover every CU several times; grid-stride for the rest
   int64_t g = (work_items + 255) / 256;
@@ -508,6 +625,63 @@ hipError_t launch_postadd(const PostAddArgs& in, hipStream_t stream) {
 }
 
 int64_t postadd_ss_parts(int64_t n) { return rows_grid(1, n, 4).x; }
+
+hipError_t launch_lin_pre(const BlockedOperand& src, int64_t rows, int64_t cols, int br, int bc,
+                          int nout, const signed char* coef, const float* scale, void* const* out,
+                          hipStream_t stream) {
+  const int nblk = br * bc;
+  if (nblk < 1 || nblk > kLinMaxBlocks || nout < 1 || nout > kLinMaxProducts || rows % br ||
+      cols % bc)
+    return hipErrorInvalidValue;
+  LinPreKArgs a{};
+  const uint16_t* base = static_cast<const uint16_t*>(src.ptr);
+  const int64_t hr = rows / br, hc = cols / bc;
+  for (int b = 0; b < nblk; ++b) {
+    const int bi = b / bc, bj = b % bc;
+    // logical block (bi, bj) starts at logical (bi*hr, bj*hc)
+    a.blk[b] = src.trans ? base + (int64_t)bj * hc * src.ld + bi * hr
+                         : base + (int64_t)bi * hr * src.ld + bj * hc;
+  }
+  a.nblk = nblk;
+  a.ld = src.ld;
+  a.srows = src.trans ? hc : hr;
+  a.scols = src.trans ? hr : hc;
+  a.nout = nout;
+  for (int q = 0; q < nout; ++q) {
+    a.out[q] = static_cast<uint16_t*>(out[q]);
+    for (int b = 0; b < nblk; ++b) a.coef[q][b] = coef[q * nblk + b];
+  }
+  a.dt = src.dtype;
+  a.scale = scale;
+  if (a.scols % 8 || a.ld % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lin_pre_kernel, rows_grid(a.srows, a.scols, 8), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lin_post(const LinPostArgs& in, hipStream_t stream) {
+  if (in.np < 1 || in.np > kLinMaxProducts || in.mbc * in.nbc < 1 ||
+      in.mbc * in.nbc > kLinMaxBlocks || in.n % 4 || !in.C)
+    return hipErrorInvalidValue;
+  LinPostKArgs a{};
+  for (int r = 0; r < in.np; ++r) a.P[r] = in.P[r];
+  a.np = in.np;
+  a.m = in.m;
+  a.n = in.n;
+  a.mbc = in.mbc;
+  a.nbc = in.nbc;
+  for (int cb = 0; cb < in.mbc * in.nbc; ++cb)
+    for (int r = 0; r < in.np; ++r) a.coef[cb][r] = in.coef[cb * in.np + r];
+  a.C = static_cast<uint16_t*>(in.C);
+  a.ldc = in.ldc;
+  a.dt = in.dtype;
+  a.alpha = in.alpha;
+  a.beta = in.beta;
+  a.bias = static_cast<const uint16_t*>(in.bias);
+  a.scale_a = in.scale_a;
+  a.scale_b = in.scale_b;
+  hipLaunchKernelGGL(lin_post_kernel, rows_grid(a.m, a.n, 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------------ split-K finalize
 namespace {

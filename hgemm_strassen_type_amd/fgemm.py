@@ -23,7 +23,7 @@ FGEMM_EPI_NONE, FGEMM_EPI_BIAS, FGEMM_EPI_ROWSUMSQ, FGEMM_EPI_RMS_SWIGLU = 0, 1,
 FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD, FGEMM_EPI_RMS_BWD = 8, 16, 32, 64
 FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
-FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD = 0, 1
+FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD, FGEMM_VARIANT_R223 = 0, 1, 2
 FGEMM_E4M3, FGEMM_E5M2 = 0, 1
 
 # every symbol include/fgemm.h declares
@@ -84,6 +84,14 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m hgemm_strassen_type_amd.build` (no fallback exists)")
+    # torch first: its HIP runtime and the system one share a soname, and whichever is
+    # loaded first serves the process; handles are used with torch's device memory and
+    # streams, so that must be torch's (loading the library first made fgemm_create
+    # fail once torch initialised the GPU)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     st = ctypes.c_int

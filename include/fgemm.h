@@ -141,8 +141,18 @@ typedef enum {
 } fgemm_path_t;
 
 /* Strassen (1969): 7 products, 18 block additions.
- * Winograd form: 7 products, 15 block additions (8 pre-add outputs instead of 10). */
-typedef enum { FGEMM_VARIANT_S69 = 0, FGEMM_VARIANT_WINOGRAD = 1 } fgemm_variant_t;
+ * Winograd form: 7 products, 15 block additions (8 pre-add outputs instead of 10).
+ * R223: a rectangular block scheme <2,2,3;11> (FalconGEMM summary, Methodology 1:
+ * the catalog's tensor-decomposition schemes): op(A) in 2 x 2 blocks, op(B) and C
+ * in 2 x 3, eleven block products (twelve classically): Strassen (1969) on the
+ * first two column blocks of op(B) and C, the four block products of the third.
+ * Depth 1 only; M and K multiples of 32, N a multiple of 48; epilogues NONE and
+ * BIAS (others FGEMM_ERR_NOT_SUPPORTED). */
+typedef enum {
+    FGEMM_VARIANT_S69 = 0,
+    FGEMM_VARIANT_WINOGRAD = 1,
+    FGEMM_VARIANT_R223 = 2
+} fgemm_variant_t;
 
 /* A plan: what fgemm_select chose (or what a caller forces through fgemm_gemm_plan). */
 typedef struct {

@@ -378,3 +378,20 @@ def test_split_k_respects_the_workspace_cap():
     two = mi355x_model(eta_mfma=0.52, eta_hbm=0.66, max_workspace_bytes=2 * M * N * 4)
     q = select(M, N, K, two)
     assert q.split_k == 2 and q.workspace_bytes <= two.max_workspace_bytes
+
+
+def test_rectangular_scheme_error_figures_and_model_time():
+    """The <2,2,3;11> scheme has an error figure at depth 1 only (below S69's at
+    depth 1: two thirds of C are S69's, one third plain blocks), and the model never
+    prefers it where Strassen's 2 x 2 split applies as well (eleven products of a
+    twelfth of the work against seven of an eighth)."""
+    r1 = fgemm.strassen_plan(1, fgemm.FGEMM_VARIANT_R223)
+    r2 = fgemm.strassen_plan(2, fgemm.FGEMM_VARIANT_R223)
+    s1 = fgemm.strassen_plan(1, fgemm.FGEMM_VARIANT_S69)
+    for dt in (fgemm.FGEMM_BF16, fgemm.FGEMM_F16):
+        assert 0 < fgemm.fgemm_plan_rel_err(dt, r1) < fgemm.fgemm_plan_rel_err(dt, s1)
+        assert fgemm.fgemm_plan_rel_err(dt, r2) < 0
+    m = mi355x_model()
+    for (M, N, K) in [(16384, 24576, 16384), (49152, 49152, 49152), (32768, 49152, 32768)]:
+        p = fgemm.fgemm_select_model(m, 0, 0, M, N, K, fgemm.FGEMM_BF16)
+        assert p.variant != fgemm.FGEMM_VARIANT_R223 or p.path == fgemm.FGEMM_PATH_CLASSICAL
