@@ -357,6 +357,34 @@ def decode_cold(torch, h, normal, M, N, K, reps):
     return r
 
 
+def read_ceiling(torch, fgemm, timer, nbytes, reps):
+    """What a plain streaming read of `nbytes` reaches on this machine (fgemm_read_probe:
+    1024 workgroups, each over one contiguous chunk, 16 loads per lane in flight):
+    warm (back to back, timed like the GEMM workloads) and cold (the same 1 GiB
+    eviction read between calls as decode_cold).  The HBM-bound decode kernels are
+    compared with this rather than only with the nominal 8 TB/s."""
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(fgemm.FGEMM_READ_PROBE_GROUPS, dtype=torch.int32, device="cuda")
+    warm = timer.time(lambda: fgemm.read_probe(buf, out), reps, 3, WARM_MS)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(20, reps))]
+    for e0, e1 in ev:
+        torch.sum(scratch, dim=0, out=sink)
+        e0.record()
+        fgemm.read_probe(buf, out)
+        e1.record()
+    torch.cuda.synchronize()
+    cold = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    r = {"bytes": nbytes, "warm_ms": round(warm, 5), "cold_ms": round(cold, 5),
+         "warm_gbps": round(nbytes / (warm * 1e-3) / 1e9, 1),
+         "cold_gbps": round(nbytes / (cold * 1e-3) / 1e9, 1)}
+    log(f"hbm read ceiling {nbytes} B: {r}")
+    del buf, out, scratch, sink
+    return r
+
+
 def dispatch_overhead(torch, h, fgemm, normal):
     """Host cost of the run-time decision (FalconGEMM summary, Results: the decision
     module costs under half a percent of run time).  Host microseconds per call,
@@ -448,12 +476,21 @@ def run_workloads(torch, h, fgemm, timer, normal, uniform, args):
     for N in (4096, 14336):
         gemm_case(f"bf16_prefill_16384x{N}x4096", 16384, N, 4096, std_b=0.02,
                   seeds=(3001, 3002, 3003))
+    # a plain read of the decode weights' bytes, and a sustained 1 GiB read: the rates
+    # the device reaches for reads of these sizes, beside the nominal 8 TB/s
+    ceil = read_ceiling(torch, fgemm, timer, 2 * 4096 * 14336, reps)
+    W["hbm_read_ceiling_117MB"] = ceil
+    W["hbm_read_ceiling_1GiB"] = read_ceiling(torch, fgemm, timer, 1 << 30, max(5, reps // 4))
     for M in (1, 16, 64):
         K, N = 4096, 14336
-        gemm_case(f"bf16_decode_{M}x{N}x{K}", M, N, K, std_b=0.02, seeds=(3001, 3002, 3003),
+        name = f"bf16_decode_{M}x{N}x{K}"
+        gemm_case(name, M, N, K, std_b=0.02, seeds=(3001, 3002, 3003),
                   bytes_alg=2.0 * (K * N + M * K + M * N))
-        W[f"bf16_decode_{M}x{N}x{K}"]["warm"] = True
-        W[f"bf16_decode_{M}x{N}x{K}_cold"] = decode_cold(torch, h, normal, M, N, K, reps)
+        W[name]["warm"] = True
+        W[name]["read_ceiling_frac"] = round(W[name]["hbm_gbps"] / ceil["warm_gbps"], 4)
+        W[name + "_cold"] = decode_cold(torch, h, normal, M, N, K, reps)
+        W[name + "_cold"]["read_ceiling_frac"] = round(
+            W[name + "_cold"]["hbm_gbps"] / ceil["cold_gbps"], 4)
     W["dispatch"] = dispatch_overhead(torch, h, fgemm, normal)
     # prefill shapes with the transform epilogues: RoPE on the projection (32 heads of
     # 128, four sequences of 4096 positions) and bias + GELU on the FFN up projection

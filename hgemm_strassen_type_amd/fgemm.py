@@ -32,10 +32,11 @@ EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_mo
            "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_gemm_f8", "fgemm_gemm_mxf8",
            "fgemm_check_args",
            "fgemm_tile_count",
-           "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_status_string")
+           "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_read_probe", "fgemm_status_string")
 
-# FGEMM_NOALLOC_SCRATCH_BYTES of fgemm.h
+# FGEMM_NOALLOC_SCRATCH_BYTES and FGEMM_READ_PROBE_GROUPS of fgemm.h
 FGEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
+FGEMM_READ_PROBE_GROUPS = 1024
 
 
 class FgemmError(RuntimeError):
@@ -121,6 +122,7 @@ def lib():
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
         "fgemm_wave_count": (i64, [i64, i64, ctypes.POINTER(ctypes.c_double)]),
         "fgemm_plan_rel_err": (ctypes.c_double, [i32, plan_p]),
+        "fgemm_read_probe": (st, [vp, i64, vp, vp]),
         "fgemm_status_string": (ctypes.c_char_p, [st]),
     }
     for name, (res, args) in sig.items():
@@ -261,6 +263,13 @@ def fgemm_plan_rel_err(dtype, plan) -> float:
     return lib().fgemm_plan_rel_err(dtype, ctypes.byref(plan))
 
 
+def fgemm_read_probe(src, nbytes, out, stream=None, check=True) -> int:
+    s = lib().fgemm_read_probe(src, nbytes, out, stream)
+    if check:
+        _check(s, "fgemm_read_probe")
+    return s
+
+
 # ------------------------------------------------------------ torch conveniences
 def torch_dtype_code(t) -> int:
     import torch
@@ -355,6 +364,20 @@ class Handle:
 
     def model(self) -> fgemm_model_t:
         return fgemm_get_model(self.h)
+
+
+def read_probe(t, out=None, stream=None):
+    """One streaming read of the device tensor `t` (contiguous, a multiple of 16 bytes,
+    16-byte aligned) by fgemm_read_probe; returns the int32 tensor of the
+    FGEMM_READ_PROBE_GROUPS per-workgroup XOR checksums."""
+    import torch
+    if not t.is_contiguous():
+        raise ValueError("read_probe takes a contiguous tensor")
+    if out is None:
+        out = torch.empty(FGEMM_READ_PROBE_GROUPS, dtype=torch.int32, device=t.device)
+    s = current_stream() if stream is None else stream
+    fgemm_read_probe(t.data_ptr(), t.numel() * t.element_size(), out.data_ptr(), s)
+    return out
 
 
 def strassen_plan(depth: int, variant: int, tile: int = 0) -> fgemm_plan_t:

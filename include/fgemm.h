@@ -346,6 +346,21 @@ int64_t fgemm_wave_count(int64_t tiles, int64_t units, double* tail_fraction);
  * dtype, path, depth or variant.  Calibrated on MI355X with i.i.d. inputs; not a
  * worst-case bound. */
 double fgemm_plan_rel_err(fgemm_dtype_t dtype, const fgemm_plan_t* plan);
+
+/* Read-bandwidth reference for the rooflines of the HBM-bound kernels (the decode
+ * shapes, the Strassen additions): one streaming pass over `bytes` of device memory
+ * at `src` with FGEMM_READ_PROBE_GROUPS workgroups of 256 threads, each over one
+ * contiguous chunk with 16 independent 16-byte loads per thread in flight, enqueued
+ * on `stream` (a hipStream_t; null is the default stream).  out[g] (device memory,
+ * FGEMM_READ_PROBE_GROUPS words, written in full) receives the XOR of the 32-bit
+ * words of chunk g, so the XOR of all of out is the XOR of every 32-bit word of src.
+ * FGEMM_ERR_INVALID_VALUE for bytes < 0, bytes not a multiple of 16, a null out, or
+ * (bytes > 0) a null or not 16-byte aligned src; FGEMM_ERR_HIP for a failed launch.
+ * Timed on the same buffer and cache state as a kernel, it gives the rate a plain
+ * read of that size reaches on the device. */
+#define FGEMM_READ_PROBE_GROUPS 1024
+fgemm_status_t fgemm_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream);
+
 const char* fgemm_status_string(fgemm_status_t status);
 
 #ifdef __cplusplus

@@ -395,3 +395,12 @@ def test_rectangular_scheme_error_figures_and_model_time():
     for (M, N, K) in [(16384, 24576, 16384), (49152, 49152, 49152), (32768, 49152, 32768)]:
         p = fgemm.fgemm_select_model(m, 0, 0, M, N, K, fgemm.FGEMM_BF16)
         assert p.variant != fgemm.FGEMM_VARIANT_R223 or p.path == fgemm.FGEMM_PATH_CLASSICAL
+
+
+def test_read_probe_argument_checks():
+    """Every refusal of fgemm_read_probe returns before any device call."""
+    inval = fgemm.FGEMM_ERR_INVALID_VALUE
+    fake = 1 << 20  # a 16-byte aligned address that is never dereferenced
+    for src, nbytes, out in ((fake, -16, fake), (fake, 15, fake), (fake, 24, fake),
+                             (fake, 32, None), (None, 16, fake), (fake + 8, 16, fake)):
+        assert fgemm.fgemm_read_probe(src, nbytes, out, None, check=False) == inval
