@@ -110,6 +110,8 @@ def _load():
     lib.oracle_decode_f8.argtypes = [ctypes.c_uint8, ctypes.c_int]
     lib.oracle_decode_e8m0.restype = ctypes.c_double
     lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_f4.restype = ctypes.c_double
+    lib.oracle_decode_f4.argtypes = [ctypes.c_uint8]
     u8p = ctypes.c_void_p
     lib.oracle_gemm_f8.restype = ctypes.c_int
     lib.oracle_gemm_f8.argtypes = [i64, i64, i64, ctypes.c_double, u8p, i64, ctypes.c_int, u8p,
@@ -121,6 +123,7 @@ def _load():
 
 
 E4M3, E5M2 = 0, 1   # OCP 8-bit float formats (values); E8M0 is the MX block scale
+E2M1 = 2            # OCP 4-bit float (two values a byte, unpack_f4's order)
 
 
 def _ptr(a):
@@ -330,6 +333,30 @@ def decode_f8(bits: np.ndarray, fmt: int) -> np.ndarray:
     return table[bits]
 
 
+def decode_f4(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of E2M1 codes (the low nibble of each uint8)."""
+    codes = _u8(codes) & 15
+    lib = _load()
+    table = np.array([lib.oracle_decode_f4(c) for c in range(16)], dtype=np.float64)
+    return table[codes]
+
+
+def unpack_f4(packed: np.ndarray) -> np.ndarray:
+    """Rows of packed 4-bit values (uint8, two a byte) -> one E2M1 code per value:
+    value 2i is the low nibble of byte i, value 2i + 1 its high nibble."""
+    packed = _u8(packed)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 15
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def pack_f4(codes: np.ndarray) -> np.ndarray:
+    """The inverse of unpack_f4 (an even number of codes a row)."""
+    codes = _u8(codes) & 15
+    return np.ascontiguousarray((codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8))
+
+
 def decode_e8m0(bits: np.ndarray) -> np.ndarray:
     """Exact fp64 values 2^(e-127) of E8M0 scale bytes (255 is NaN)."""
     bits = _u8(bits)
@@ -373,6 +400,51 @@ def gemm_f8(A, B, *, fmt_a=E4M3, fmt_b=E4M3, scale_a=1.0, scale_b=1.0, mx_a=None
     if rc != 0:
         raise ValueError("oracle_gemm_f8 rejected its arguments")
     return D, Q, ss
+
+
+def gemm_mxf4(A, B, mx_a, mx_b, *, alpha=1.0, beta=0.0, C=None, dtype=BF16, epi=0, bias=None,
+              rows=None, threads=None):
+    """Reference MXFP4 GEMM: A (M x K/2) and B (N x K/2) uint8 rows of packed E2M1
+    values (unpack_f4's order), both K-contiguous (the product is A B^T); each value
+    counts as s * q with s the E8M0 scale of its block of 32 along K (mx_a, mx_b:
+    uint8 arrays [rows][>= K/32]).  Returns (D, Q, ss) for the selected rows as
+    gemm_f8 does; epilogues BIAS and ROWSUMSQ."""
+    A, B = _u8(A), _u8(B)
+    M, K = A.shape[0], 2 * A.shape[1]
+    N = B.shape[0]
+    if 2 * B.shape[1] != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {2 * B.shape[1]}")
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = rows.size
+    C = _u16(C) if beta != 0.0 else None
+    if bias is not None:
+        bias = _u16(bias)
+    mx_a, mx_b = _u8(mx_a), _u8(mx_b)
+    D = np.empty((nrows, N), dtype=np.float64)
+    Q = np.empty((nrows, N), dtype=np.uint16)
+    ss = np.empty(nrows, dtype=np.float64) if epi & EPI_ROWSUMSQ else None
+    rc = _load().oracle_gemm_f8(M, N, K, float(alpha), _ptr(A), A.shape[1], E2M1, _ptr(B),
+                                B.shape[1], E2M1, 1.0, 1.0, _ptr(mx_a), mx_a.shape[1], _ptr(mx_b),
+                                mx_b.shape[1], float(beta), _ptr(C),
+                                0 if C is None else C.shape[1], dtype, epi, _ptr(bias),
+                                _ptr(rows), nrows, _ptr(D), _ptr(Q), _ptr(ss),
+                                threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_f8 rejected its arguments")
+    return D, Q, ss
+
+
+def gemm_mxf4_dense(A, B, mx_a, mx_b, *, alpha=1.0):
+    """``gemm_mxf4``'s unrounded alpha * sum_k (s q_a)(s q_b) for every row with one
+    fp64 library matmul, and the bound magnitude S = |alpha| |A'| |B'|^T."""
+    a = decode_f4(unpack_f4(A))
+    b = decode_f4(unpack_f4(B))
+    K = a.shape[1]
+    a = a * np.repeat(decode_e8m0(_u8(mx_a)[:, :K // 32]), 32, axis=1)
+    b = b * np.repeat(decode_e8m0(_u8(mx_b)[:, :K // 32]), 32, axis=1)
+    D = alpha * (a @ b.T)
+    S = abs(alpha) * (np.abs(a) @ np.abs(b).T)
+    return D, S
 
 
 # ------------------------------------------------------------ whole-output references

@@ -619,6 +619,7 @@ int oracle_s69_products(int64_t n, const double* A, const double* B, double* Mou
  * ------------------------------------------------------------------------- */
 #define OR_E4M3 0
 #define OR_E5M2 1
+#define OR_E2M1 2   /* 4-bit values, two per byte (see oracle_gemm_f8) */
 
 double oracle_decode_f8(uint8_t h, int fmt) {
     int sign = (h >> 7) & 1;
@@ -642,6 +643,28 @@ double oracle_decode_f8(uint8_t h, int fmt) {
 }
 
 double oracle_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* 4-bit floating point (CS336 Lecture 05 notes, Page 29, "Frontiers in low
+ * precision - MXFP4": the representable values are 0, +-0.5, +-1, +-1.5, +-2, +-3,
+ * +-4, +-6, used with a block scale).  The code is the OCP E2M1 layout that gives
+ * exactly that set: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa; exponent
+ * field 0 is subnormal (0 or 0.5); no infinities or NaN.  Only the low nibble of
+ * `h` is read. */
+double oracle_decode_f4(uint8_t h) {
+    int sign = (h >> 3) & 1;
+    int e = (h >> 1) & 3;
+    int f = h & 1;
+    double v = e == 0 ? 0.5 * f : ldexp(1.0 + 0.5 * f, e - 1);
+    return sign ? -v : v;
+}
+
+/* Value k of a row that starts at `row`: a byte for the 8-bit formats; for E2M1,
+ * value k sits in byte k/2, in its low nibble when k is even and its high nibble
+ * when k is odd (the OCP packing of two 4-bit values per byte). */
+static double lp_value(const uint8_t* row, int64_t k, int fmt) {
+    if (fmt == OR_E2M1) return oracle_decode_f4((uint8_t)(row[k / 2] >> (4 * (k & 1))));
+    return oracle_decode_f8(row[k], fmt);
+}
 
 typedef struct {
     int64_t K, N;
@@ -671,10 +694,12 @@ static void* f8_worker(void* p) {
 }
 
 /*
- * oracle_gemm_f8: the 8-bit GEMM, all in fp64 from the exact 8-bit values.
+ * oracle_gemm_f8: the 8-bit and 4-bit GEMM, all in fp64 from the exact values.
  *   A is M x K row-major (lda), B is N x K row-major (ldb): op(B) = B^T, both
  *   operands K-contiguous, as the quantized layouts of the notes' Page 27-28 keep
- *   them.  Each operand value is used as s * q (Page 27):
+ *   them.  fmtA / fmtB: OR_E4M3, OR_E5M2 (one byte a value, lda/ldb in values =
+ *   bytes) or OR_E2M1 (two values a byte as lp_value reads them, lda/ldb in bytes,
+ *   K even).  Each operand value is used as s * q (Page 27; Page 29 for 4-bit):
  *     s = the per-tensor scale (scale_a, scale_b) when the block-scale array is
  *         NULL, else the E8M0 scale of the value's block of 32 along K:
  *         sA(i,k) = mxA[i * ldmxA + k / 32], sB(j,k) = mxB[j * ldmxB + k / 32].
@@ -690,7 +715,8 @@ int oracle_gemm_f8(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t*
                    int64_t ldc, int dtype, int epi, const uint16_t* bias, const int64_t* rows,
                    int64_t nrows, double* D, uint16_t* Q, double* ss, int nthreads) {
     if (M < 0 || N < 0 || K < 0 || nrows < 0) return -1;
-    if ((fmtA != OR_E4M3 && fmtA != OR_E5M2) || (fmtB != OR_E4M3 && fmtB != OR_E5M2)) return -1;
+    if (fmtA < OR_E4M3 || fmtA > OR_E2M1 || fmtB < OR_E4M3 || fmtB > OR_E2M1) return -1;
+    if ((fmtA == OR_E2M1 || fmtB == OR_E2M1) && K % 2) return -1;
     if ((mxA || mxB) && K % 32) return -1;
     if (epi & ~(OR_EPI_BIAS | OR_EPI_ROWSUMSQ)) return -1;
     for (int64_t r = 0; r < nrows; ++r)
@@ -703,12 +729,12 @@ int oracle_gemm_f8(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t*
         for (int64_t k = 0; k < K; ++k) {
             const int64_t i = rows[r];
             const double s = mxA ? oracle_decode_e8m0(mxA[i * ldmxA + k / 32]) : scale_a;
-            Ad[r * K + k] = s * oracle_decode_f8(A[i * lda + k], fmtA);
+            Ad[r * K + k] = s * lp_value(A + i * lda, k, fmtA);
         }
     for (int64_t k = 0; k < K; ++k)
         for (int64_t j = 0; j < N; ++j) {
             const double s = mxB ? oracle_decode_e8m0(mxB[j * ldmxB + k / 32]) : scale_b;
-            Bd[k * N + j] = s * oracle_decode_f8(B[j * ldb + k], fmtB);
+            Bd[k * N + j] = s * lp_value(B + j * ldb, k, fmtB);
         }
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

@@ -652,6 +652,92 @@ def test_mx_block_scales():
         oracle.gemm_f8(A[:, :40], B[:, :40], mx_a=sa[:, :2], mx_b=sb[:, :2])
 
 
+# ------------------------------------------------------------ 4-bit values (MXFP4)
+# The values CS336 Lecture 05 notes, Page 29 ("Frontiers in low precision - MXFP4")
+# lists for 4-bit floating point, in increasing order of the positive codes.
+F4_PAGE_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_f4_decode_is_the_pages_value_set():
+    """Codes 0..7 decode to the page's eight magnitudes in increasing order (a wrong
+    bias, a dropped mantissa bit or a missing subnormal would break the list), codes
+    8..15 to their negatives (sign in bit 3); only the low nibble is read."""
+    v = oracle.decode_f4(np.arange(16, dtype=np.uint8))
+    assert list(v[:8]) == F4_PAGE_VALUES
+    assert list(v[8:]) == [-x for x in F4_PAGE_VALUES]
+    assert np.signbit(v[8])                                   # code 8 is -0
+    assert np.array_equal(oracle.decode_f4(np.arange(16, 256, 16, dtype=np.uint8)), np.zeros(15))
+
+
+def test_f4_packing_order():
+    """Two values a byte: value 2i is the low nibble of byte i, value 2i + 1 the high
+    one; pack_f4 inverts unpack_f4."""
+    packed = np.array([[0x21, 0xF3]], dtype=np.uint8)
+    assert oracle.unpack_f4(packed).tolist() == [[0x1, 0x2, 0x3, 0xF]]
+    assert list(oracle.decode_f4(oracle.unpack_f4(packed))[0]) == [0.5, 1.0, 1.5, -6.0]
+    codes = np.random.default_rng(3).integers(0, 16, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_f4(oracle.pack_f4(codes)), codes)
+
+
+def test_mxf4_gemm_brute_force():
+    """A tiny MXFP4 product as a plain Python triple loop over the page's value table
+    and 2^(e-127) block scales (no oracle decoding involved): every value is dyadic,
+    so the fp64 results agree exactly; then alpha, beta*C, bias and row sampling."""
+    M, N, K = 3, 4, 64
+    rng = np.random.default_rng(71)
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sa = rng.integers(118, 137, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(118, 137, size=(N, K // 32)).astype(np.uint8)
+
+    def val(c):
+        return (-1.0 if c & 8 else 1.0) * F4_PAGE_VALUES[c & 7]
+
+    ref = np.zeros((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += (val(int(ca[i, k])) * 2.0 ** (int(sa[i, k // 32]) - 127) *
+                        val(int(cb[j, k])) * 2.0 ** (int(sb[j, k // 32]) - 127))
+            ref[i, j] = acc
+    A, B = oracle.pack_f4(ca), oracle.pack_f4(cb)
+    D, Q, _ = oracle.gemm_mxf4(A, B, sa, sb)
+    assert np.array_equal(D, ref)
+    C = inputs.normal((M, N), 72, BF16)
+    bias = inputs.normal((N,), 73, BF16)
+    D2, _, _ = oracle.gemm_mxf4(A, B, sa, sb, alpha=0.5, beta=2.0, C=C, epi=oracle.EPI_BIAS,
+                                bias=bias, rows=np.array([2, 0]))
+    want = 0.5 * ref + 2.0 * oracle.decode(C, BF16) + oracle.decode(bias, BF16)[None, :]
+    assert np.array_equal(D2, want[[2, 0]])
+    Dd, S = oracle.gemm_mxf4_dense(A, B, sa, sb)
+    assert np.array_equal(Dd, ref) and np.all(S >= np.abs(ref))
+
+
+def test_mxf4_equals_mxf8_on_the_same_values():
+    """Every E2M1 value is exact in E4M3, so re-encoding the operands as E4M3 codes
+    (through torch's float8 conversion) with the same block scales must give the
+    already-pinned MXFP8 product exactly; a K not a multiple of 32 is refused."""
+    M, N, K = 6, 10, 128
+    rng = np.random.default_rng(81)
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sa = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    tbl = np.array([(-1.0 if c & 8 else 1.0) * F4_PAGE_VALUES[c & 7] for c in range(16)])
+
+    def e4m3(codes):
+        return torch.from_numpy(tbl[codes].astype(np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    D4, Q4, _ = oracle.gemm_mxf4(oracle.pack_f4(ca), oracle.pack_f4(cb), sa, sb)
+    D8, Q8, _ = oracle.gemm_f8(e4m3(ca), e4m3(cb), mx_a=sa, mx_b=sb)
+    assert np.array_equal(D4, D8) and np.array_equal(Q4, Q8)
+    with pytest.raises(ValueError):
+        oracle.gemm_mxf4(oracle.pack_f4(ca[:, :40]), oracle.pack_f4(cb[:, :40]), sa[:, :2],
+                         sb[:, :2])
+
+
 # ------------------------------------------------------------ whole-output references
 @pytest.mark.parametrize("transA,transB", [(False, False), (True, False), (False, True)])
 def test_dense_exact_on_integers(transA, transB):
