@@ -274,13 +274,15 @@ def decode_workload(torch, h, fgemm, timer, normal, args):
 
 
 F8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+F4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 (and fp6) MFMA
 
 
 def f8_workloads(torch, h, fgemm, timer, reps):
     """fgemm_gemm_f8 on E4M3 activations N(0,1) and weights N(0,0.02), each stored
     with a per-tensor power-of-two scale, A M x K and B N x K (K-contiguous), bf16
     output, beta 0: 8192^3 and the 16384-token LLM shapes, against the dense fp8
-    MFMA peak."""
+    MFMA peak; MXFP8 at 8192^3; MXFP4 at the same three shapes against the dense
+    fp4 peak."""
     gen = torch.Generator(device="cuda")
     out = {}
 
@@ -323,6 +325,38 @@ def f8_workloads(torch, h, fgemm, timer, reps):
     out[f"mxf8_e4m3_{M}x{N}x{K}"] = r
     log(f"mxf8_e4m3_{M}x{N}x{K}: {r}")
     del A, B, C, sA, sB
+
+    # MXFP4: E2M1 values (two a byte) with one E8M0 scale per 32 values, the block's
+    # amax put at or below 6, each value rounded to the nearest E2M1 magnitude
+    mags = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device="cuda")
+    mids = (mags[1:] + mags[:-1]) / 2
+
+    def f4_codes(shape, seed, std):
+        rows, k = shape
+        gen.manual_seed(seed)
+        x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std
+        blk = x.view(rows, k // 32, 32)
+        e = torch.ceil(torch.log2(blk.abs().amax(dim=2).clamp_min(1e-30) / 6.0))
+        q = (blk / torch.exp2(e)[:, :, None]).view(shape)
+        code = torch.bucketize(q.abs(), mids).to(torch.uint8) | ((q < 0).to(torch.uint8) << 3)
+        packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+        cols = max(16, (k // 32 + 15) // 16 * 16)
+        scales = torch.full((rows, cols), 127, dtype=torch.uint8, device="cuda")
+        scales[:, :k // 32] = (e + 127).to(torch.uint8)
+        return packed, scales
+
+    for (M, N, K) in [(8192, 8192, 8192), (16384, 4096, 4096), (16384, 14336, 4096)]:
+        A, sA = f4_codes((M, K), 6005, 1.0)
+        B, sB = f4_codes((N, K), 6006, 0.02)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ms = timer.time(lambda: h.gemm_mxf4(A, B, C, sA, sB), reps, 3, WARM_MS)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        r = {"ms": round(ms, 5), "tflops": round(tf, 2),
+             "f4_peak_frac": round(tf / F4_PEAK_TFLOPS, 4),
+             "format": "MXFP4: E2M1 x E2M1, E8M0 scale per 32 values, bf16 out"}
+        out[f"mxf4_{M}x{N}x{K}"] = r
+        log(f"mxf4_{M}x{N}x{K}: {r}")
+        del A, B, C, sA, sB
     return out
 
 

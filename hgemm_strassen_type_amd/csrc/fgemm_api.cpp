@@ -1087,13 +1087,15 @@ fgemm_status_t fgemm_gemm_noalloc(fgemm_handle_t h, fgemm_op_t ta, fgemm_op_t tb
 
 namespace {
 
-// The 8-bit GEMM with per-tensor scales (mx_a == mx_b == null) or E8M0 block scales.
+// The 8-bit GEMM with per-tensor scales (mx_a == mx_b == null) or E8M0 block scales;
+// with f4, the MXFP4 GEMM (E2M1 values two a byte, block scales required, formats
+// unused, lda/ldb in bytes).
 fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
                        const void* A, int64_t lda, fgemm_f8_format_t a_format, float scale_a,
                        const uint8_t* mx_a, int64_t ld_mxa, const void* B, int64_t ldb,
                        fgemm_f8_format_t b_format, float scale_b, const uint8_t* mx_b,
                        int64_t ld_mxb, float beta, void* C, int64_t ldc, fgemm_dtype_t dtype,
-                       const fgemm_epilogue_t* epi, void* stream) {
+                       const fgemm_epilogue_t* epi, void* stream, bool f4 = false) {
   if (!h) return FGEMM_ERR_INVALID_VALUE;
   const bool mx = mx_a != nullptr || mx_b != nullptr;
   if (mx) {
@@ -1107,8 +1109,8 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
         !aligned16(mx_b))
       return FGEMM_ERR_NOT_SUPPORTED;
   }
-  if ((a_format != FGEMM_E4M3 && a_format != FGEMM_E5M2) ||
-      (b_format != FGEMM_E4M3 && b_format != FGEMM_E5M2))
+  if (!f4 && ((a_format != FGEMM_E4M3 && a_format != FGEMM_E5M2) ||
+              (b_format != FGEMM_E4M3 && b_format != FGEMM_E5M2)))
     return FGEMM_ERR_INVALID_VALUE;
   if (dtype != FGEMM_F16 && dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return FGEMM_ERR_INVALID_VALUE;
@@ -1119,7 +1121,9 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
                           FGEMM_EPI_RMS_BWD))
     return FGEMM_ERR_INVALID_VALUE;
   if (flags & ~(uint32_t)(FGEMM_EPI_BIAS | FGEMM_EPI_ROWSUMSQ)) return FGEMM_ERR_NOT_SUPPORTED;
-  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
+  const int64_t row_bytes = f4 ? (K + 1) / 2 : K;  // bytes of one operand row
+  if (lda < (row_bytes > 1 ? row_bytes : 1) || ldb < (row_bytes > 1 ? row_bytes : 1) ||
+      ldc < (N > 1 ? N : 1))
     return FGEMM_ERR_INVALID_VALUE;
   const bool any_out = M > 0 && N > 0;
   if (any_out && K > 0 && (A == nullptr || B == nullptr)) return FGEMM_ERR_INVALID_VALUE;
@@ -1128,9 +1132,10 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
   if ((flags & FGEMM_EPI_ROWSUMSQ) && any_out && epi->rowsumsq == nullptr)
     return FGEMM_ERR_INVALID_VALUE;
   if (!isfinite(scale_a) || !isfinite(scale_b) || !isfinite(alpha)) return FGEMM_ERR_INVALID_VALUE;
-  // whole 128-deep phases, 16-byte rows and pointers: the kernel has no K tail path
-  if (K % 128 || lda % 16 || ldb % 16 || ldc % 8 || !aligned16(A) || !aligned16(B) ||
-      !aligned16(C))
+  // whole phases (128 bytes a row: 128 values, 256 at 4 bits), 16-byte rows and
+  // pointers: the kernel has no K tail path
+  if (K % (f4 ? 256 : 128) || lda % 16 || ldb % 16 || ldc % 8 || !aligned16(A) ||
+      !aligned16(B) || !aligned16(C))
     return FGEMM_ERR_NOT_SUPPORTED;
   // the tensor scales enter through alpha, formed in fp32: it must stay a normal value
   const double f = (double)alpha * (double)scale_a * (double)scale_b;
@@ -1144,10 +1149,11 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
   b.count = 1;
   b.cus = h->cus;
   GemmProblem& p = b.p[0];
-  // byte pairs: the kernel addresses both operands in 16-bit units
+  // byte pairs: the kernel addresses both operands in 16-bit units (2 values at 8
+  // bits, 4 at 4 bits)
   p.A = A; p.B = B; p.C = C; p.Cin = C;
   p.lda = lda / 2; p.ldb = ldb / 2; p.ldc = ldc;
-  p.M = (int)M; p.N = (int)N; p.K = (int)(K / 2);
+  p.M = (int)M; p.N = (int)N; p.K = (int)(f4 ? K / 4 : K / 2);
   p.alpha = (float)f;
   p.beta = beta;
   p.flags = beta != 0.f ? kFlagBeta : 0u;
@@ -1169,7 +1175,7 @@ fgemm_status_t gemm_f8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float 
   KernelKey k{};
   k.a_kcontig = 1;
   k.b_kcontig = 1;
-  k.dtype = f8_code((int)a_format, (int)b_format, mx ? 1 : 0);
+  k.dtype = f4 ? kF4MX : f8_code((int)a_format, (int)b_format, mx ? 1 : 0);
   k.epi = kEpiStore16;
   k.vec = 1;
   k.odt = dtype == FGEMM_BF16 ? kBF16 : kF16;
@@ -1205,6 +1211,24 @@ fgemm_status_t fgemm_gemm_mxf8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K
   const uint8_t* sb = K > 0 ? static_cast<const uint8_t*>(b_scales) : nullptr;
   return gemm_f8(h, M, N, K, alpha, A, lda, a_format, 1.f, sa, ld_a_scales, B, ldb, b_format,
                  1.f, sb, ld_b_scales, beta, C, ldc, dtype, epi, stream);
+}
+
+fgemm_status_t fgemm_gemm_mxf4(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                               const void* A, int64_t lda, const void* a_scales,
+                               int64_t ld_a_scales, const void* B, int64_t ldb,
+                               const void* b_scales, int64_t ld_b_scales, float beta, void* C,
+                               int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epi,
+                               void* stream) {
+  if (K > 0 && (a_scales == nullptr || b_scales == nullptr)) return FGEMM_ERR_INVALID_VALUE;
+  if (K == 0) {
+    // no value and no scale is read (C = beta*C + bias): the 8-bit kernel does that
+    return gemm_f8(h, M, N, 0, alpha, A, lda, FGEMM_E4M3, 1.f, nullptr, 0, B, ldb, FGEMM_E4M3,
+                   1.f, nullptr, 0, beta, C, ldc, dtype, epi, stream);
+  }
+  return gemm_f8(h, M, N, K, alpha, A, lda, FGEMM_E4M3, 1.f,
+                 static_cast<const uint8_t*>(a_scales), ld_a_scales, B, ldb, FGEMM_E4M3, 1.f,
+                 static_cast<const uint8_t*>(b_scales), ld_b_scales, beta, C, ldc, dtype, epi,
+                 stream, true);
 }
 
 }  // extern "C"

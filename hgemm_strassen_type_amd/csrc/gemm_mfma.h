@@ -199,10 +199,17 @@ struct GemmTile {
   // CHUNK2 bytes apart, and the hardware's k order is the memory order (which the MX
   // block scales need: block b is k 32b..32b+31, its scale in lane group b)
   static constexpr bool F8 = DT >= kF8Base;
+  // 4-bit inputs (E2M1, two values a byte) through the same instruction: a lane's
+  // operand is 16 bytes, 32 values, and lane group g holds k 32g..32g+31 of the
+  // step, one whole E8M0 block, in memory order.  That is the 16-bit 32x32x16
+  // fragment geometry (lane group g reads the step's 16-byte chunk g), so the
+  // K-contiguous fragment addressing serves unchanged, with 128 bytes (256 values,
+  // 8 blocks, 4 steps) a row a phase.
+  static constexpr bool F4 = DT == kF4MX;
   // MX: one E8M0 scale per 32 values along K for every row of A and B (the 8-bit
   // code's third bit), fed to the MFMA per lane: the lane's 32 bytes are one block
   static constexpr bool MX = DT >= kF8Base + 4;
-  static constexpr int FC = F8 ? 2 : 1;
+  static constexpr int FC = F8 && !F4 ? 2 : 1;
   static constexpr int CHUNK2 = CFG::MI == 32 ? 32 : 64;  // F8: XOR offset of the second chunk
   // MX scales in LDS after the stages: per group of 4 phases (16 blocks) the tile's
   // BM + BN rows of 16 scale bytes, two groups (one read while the next arrives)
@@ -212,12 +219,18 @@ struct GemmTile {
   // 1 KB scale slots (64 rows of 16 bytes) a wave loads: slot q = wave + NW*i
   static constexpr int MX_SW = (MX_SLOTS_A + MX_SLOTS_B + CFG::NW - 1) / CFG::NW;
   // k per MFMA step in 16-bit units (8-bit: 64 or 128 values) and steps per phase
-  static constexpr int KSTEP = F8 ? (CFG::MI == 32 ? 32 : 64) : CFG::KSTEP;
+  static constexpr int KSTEP = F4 ? 16 : F8 ? (CFG::MI == 32 ? 32 : 64) : CFG::KSTEP;
   static constexpr int STEPS = CFG::BK / KSTEP;
-  // MX: E8M0 blocks of 32 values a step covers
-  static constexpr int BPS = KSTEP / 16;
+  // MX: E8M0 blocks of 32 values a step covers (a 16-bit unit is 4 values at 4 bits)
+  static constexpr int BPS = F4 ? KSTEP / 8 : KSTEP / 16;
+  // MX: blocks a phase covers, and phases a 16-block scale group covers
+  static constexpr int BPP = STEPS * BPS;
+  static constexpr int PPG = MX ? 16 / BPP : 1;
   static_assert(!F8 || (AK && BKC && CFG::BK == 64 && EPI == kEpiStore16),
-                "8-bit inputs: K-contiguous operands, 128 k a phase, the 16-bit store epilogue");
+                "8/4-bit inputs: K-contiguous operands, 128 bytes a row a phase, the 16-bit "
+                "store epilogue");
+  static_assert(!MX || BPP * PPG == 16, "whole phases a scale group");
+  static_assert(!F4 || (CFG::MI == 32 && MX), "4-bit inputs: 32x32x64 MFMAs with block scales");
   // gate/up column pairs: the SwiGLU epilogue and its backward
   static constexpr bool SWIGLU = EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd;
   using Acc = typename CFG::AccT;
@@ -321,8 +334,8 @@ struct GemmTile {
     return r;
   }
 
-  // MX: scale group g (blocks 16g..16g+15, phases 4g..4g+3) of this wave's slot
-  // into buffer g % 2.
+  // MX: scale group g (blocks 16g..16g+15, phases PPG*g..PPG*g+PPG-1) of this wave's
+  // slot into buffer g % 2.
   __device__ __forceinline__ static void issue_scales(const Src& S, int g, int wave,
                                                       const LoadAddr& la, uint8_t* smem) {
     if constexpr (MX) {
@@ -455,10 +468,15 @@ struct GemmTile {
     v4u a[CFG::FM][FC];
     v4u b[CFG::FN][FC];
   };
-  // MX: the E8M0 scale of the lane's block for every step and fragment of a phase
+  // MX: the E8M0 scales of the lane's blocks for every pair of steps and fragment of
+  // a phase: steps 2q and 2q+1 use blocks 4q+g and 4q+2+g of the phase (lane group g,
+  // two blocks a step), one aligned dword of the row's scale bytes shifted right by
+  // 8g, so they sit in bytes 0 and 2, which the MFMA's op_sel picks (one VGPR and
+  // one LDS read for two steps)
+  static_assert(!MX || BPS == 2, "block scales: two blocks a step (32x32x64)");
   struct Scales {
-    uint32_t a[MX ? STEPS : 1][MX ? CFG::FM : 1];
-    uint32_t b[MX ? STEPS : 1][MX ? CFG::FN : 1];
+    uint32_t a[MX ? (STEPS + 1) / 2 : 1][MX ? CFG::FM : 1];
+    uint32_t b[MX ? (STEPS + 1) / 2 : 1][MX ? CFG::FN : 1];
   };
 
   // Per-lane LDS byte offsets of the fragments at MFMA step 0 (stage-relative).
@@ -470,7 +488,9 @@ struct GemmTile {
   struct FragAddr {
     int a[CFG::FM];
     int b[CFG::FN];
-    int sc;  // MX: the lane's scale byte within a group buffer, minus the fragment's rows
+    int sc;    // MX: the lane's row's first scale byte within a group buffer, minus the
+               // fragment's rows
+    int scsh;  // MX: 8 * lane group: the shift that brings the lane's block to byte 0
   };
 
   template <bool KCONTIG, int R, int F>
@@ -496,7 +516,8 @@ struct GemmTile {
   __device__ __forceinline__ static void frag_addr(int wm, int wn, int lane, FragAddr& fa) {
     frag_base<AK, BM, CFG::FM>(wm * CFG::WM, lane, 0, fa.a);
     frag_base<BKC, BN, CFG::FN>(wn * CFG::WN, lane, CFG::LDS_A, fa.b);
-    fa.sc = (lane % CFG::MI) * 16 + lane / CFG::MI;
+    fa.sc = (lane % CFG::MI) * 16;
+    fa.scsh = 8 * (lane / CFG::MI);
   }
 
   // Offset of step s from step 0.  K-contiguous: chunk (KSTEP/8)*s + slot, and the
@@ -541,26 +562,30 @@ struct GemmTile {
   }
 
   // MX: the scales of phase p (kt within the tile) for every step and fragment: the
-  // lane's row and block (phase p's 4 blocks follow each other in the group's 16
+  // lane's row and block (phase p's BPP blocks follow each other in the group's 16
   // bytes, BPS of them a step).
   __device__ __forceinline__ static void read_scales(const uint8_t* smem, const FragAddr& fa,
                                                      int wm, int wn, int p, Scales& sc) {
     if constexpr (MX) {
-      const uint8_t* buf = smem + MX_OFF + ((p >> 2) & 1) * MX_BUF + (p & 3) * 4 + fa.sc;
+      const uint8_t* buf = smem + MX_OFF + ((p / PPG) & 1) * MX_BUF + (p % PPG) * BPP + fa.sc;
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
+      for (int q = 0; q < (STEPS + 1) / 2; ++q) {
 #pragma unroll
         for (int i = 0; i < CFG::FM; ++i)
-          sc.a[s][i] = *(buf + s * BPS + (wm * CFG::WM + i * CFG::MI) * 16);
+          sc.a[q][i] = *reinterpret_cast<const uint32_t*>(
+                           buf + 4 * q + (wm * CFG::WM + i * CFG::MI) * 16) >> fa.scsh;
 #pragma unroll
         for (int j = 0; j < CFG::FN; ++j)
-          sc.b[s][j] = *(buf + s * BPS + (CFG::BM + wn * CFG::WN + j * CFG::MI) * 16);
+          sc.b[q][j] = *reinterpret_cast<const uint32_t*>(
+                           buf + 4 * q + (CFG::BM + wn * CFG::WN + j * CFG::MI) * 16) >> fa.scsh;
       }
     }
   }
 
   // One MFMA: the B fragment first, so that a lane's accumulators are consecutive
-  // columns of one output row.
+  // columns of one output row.  OPS: the byte of the scale registers the 8/4-bit
+  // MFMA applies (its op_sel).
+  template <int OPS = 0>
   __device__ __forceinline__ static Acc mfma(const v4u (&bf)[FC], const v4u (&af)[FC],
                                              const Acc& c, uint32_t scb = 127,
                                              uint32_t sca = 127) {
@@ -569,17 +594,23 @@ struct GemmTile {
     if constexpr (F8) {
       // 8-bit codes with E8M0 block scales (127 = 2^0 without MX: the tensor scales
       // are applied in the epilogue through alpha)
-      constexpr int FA = ((DT - kF8Base) >> 1) & 1, FB = (DT - kF8Base) & 1;
-      const v8i bv = {(int)bf[0].x, (int)bf[0].y, (int)bf[0].z, (int)bf[0].w,
-                      (int)bf[FC - 1].x, (int)bf[FC - 1].y, (int)bf[FC - 1].z, (int)bf[FC - 1].w};
-      const v8i av = {(int)af[0].x, (int)af[0].y, (int)af[0].z, (int)af[0].w,
-                      (int)af[FC - 1].x, (int)af[FC - 1].y, (int)af[FC - 1].z, (int)af[FC - 1].w};
+      // format numbers: 0 E4M3, 1 E5M2, 4 E2M1 (whose operand is the low 4 registers)
+      constexpr int FA = F4 ? 4 : ((DT - kF8Base) >> 1) & 1;
+      constexpr int FB = F4 ? 4 : (DT - kF8Base) & 1;
+      const v8i bv = F4 ? v8i{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0}
+                        : v8i{(int)bf[0].x, (int)bf[0].y, (int)bf[0].z, (int)bf[0].w,
+                              (int)bf[FC - 1].x, (int)bf[FC - 1].y, (int)bf[FC - 1].z,
+                              (int)bf[FC - 1].w};
+      const v8i av = F4 ? v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0}
+                        : v8i{(int)af[0].x, (int)af[0].y, (int)af[0].z, (int)af[0].w,
+                              (int)af[FC - 1].x, (int)af[FC - 1].y, (int)af[FC - 1].z,
+                              (int)af[FC - 1].w};
       if constexpr (CFG::MI == 32)
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FB, FA, 0, (int)scb, 0,
-                                                              (int)sca);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FB, FA, OPS, (int)scb,
+                                                              OPS, (int)sca);
       else
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, FB, FA, 0, (int)scb,
-                                                               0, (int)sca);
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, FB, FA, OPS,
+                                                               (int)scb, OPS, (int)sca);
     } else if constexpr (CFG::MI == 32) {
       if constexpr (DT == kBF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
@@ -597,14 +628,17 @@ struct GemmTile {
     }
   }
 
-  // MX scales of step s, fragment i of A / j of B (127 = 2^0 otherwise)
-  __device__ __forceinline__ static uint32_t sca_of(const Scales& sc, int s, int i) {
-    if constexpr (MX) return sc.a[s][i];
-    return 127u;
-  }
-  __device__ __forceinline__ static uint32_t scb_of(const Scales& sc, int s, int j) {
-    if constexpr (MX) return sc.b[s][j];
-    return 127u;
+  // The MFMA of step s on fragments i of A and j of B: with MX, the scale registers
+  // of s's pair of steps and the byte for s (0 or 2; s is a constant at every call,
+  // so the choice folds away); else unit scales (127 = 2^0).
+  __device__ __forceinline__ static Acc mfma_s(const v4u (&bf)[FC], const v4u (&af)[FC],
+                                               const Acc& c, const Scales& sc, int s, int i,
+                                               int j) {
+    if constexpr (MX) {
+      if (s & 1) return mfma<2>(bf, af, c, sc.b[s >> 1][j], sc.a[s >> 1][i]);
+      return mfma<0>(bf, af, c, sc.b[s >> 1][j], sc.a[s >> 1][i]);
+    }
+    return mfma(bf, af, c);
   }
 
   __device__ __forceinline__ static void mfma_step(const Frags& fr, const Scales& sc, int s,
@@ -613,7 +647,7 @@ struct GemmTile {
     for (int i = 0; i < CFG::FM; ++i)
 #pragma unroll
       for (int j = 0; j < CFG::FN; ++j)
-        acc[i][j] = mfma(fr.b[j], fr.a[i], acc[i][j], scb_of(sc, s, j), sca_of(sc, s, i));
+        acc[i][j] = mfma_s(fr.b[j], fr.a[i], acc[i][j], sc, s, i, j);
   }
 
   // one MFMA, then one instruction of OTHER_MASK, while both last (I counts MFMAs)
@@ -690,8 +724,7 @@ struct GemmTile {
     constexpr int NM = kMfmaPerStep, NR = kReadsPerStep, NL = LD ? kLoadsPerPhase : 0;
     if constexpr (M < NM) {
       constexpr int i = M / CFG::FN, j = M % CFG::FN;
-      acc[i][j] = mfma(now.b[j], now.a[i], acc[i][j], scb_of(sc, STEPS - 1, j),
-                       sca_of(sc, STEPS - 1, i));
+      acc[i][j] = mfma_s(now.b[j], now.a[i], acc[i][j], sc, STEPS - 1, i, j);
       if constexpr (M < NR) read_job<M>(rd, fa, rs, next);
       if constexpr (M < NL) load_job<M>(ab, bb, la, wave, ls);
       __builtin_amdgcn_sched_barrier(0);
@@ -743,7 +776,7 @@ struct GemmTile {
   __device__ __forceinline__ static void issue_prologue(const Src& S, int m0, int kt0,
                                                         int ktiles, int wave, const LoadAddr& la,
                                                         uint8_t* smem) {
-    if constexpr (MX) issue_scales(S, 0, wave, la, smem);  // phases 0-3 (kt0 is 0)
+    if constexpr (MX) issue_scales(S, 0, wave, la, smem);  // phases 0..PPG-1 (kt0 is 0)
 #pragma unroll
     for (int t = 0; t < CFG::STAGES - 1; ++t)
       if (t < ktiles) issue_loads(S, m0, kt0 + t, wave, la, smem + t * CFG::LDS_STAGE);
@@ -852,15 +885,17 @@ struct GemmTile {
     __builtin_amdgcn_s_setprio(1);
     const int st_next = st + 1 == S ? 0 : st + 1;
     const uint8_t* nxt = smem + st_next * CFG::LDS_STAGE;
-    // MX scale groups of 16 blocks (4 phases) alternate between two buffers.  Group g
-    // is issued at phase 4g-4 after the barrier, has landed by the wait of phase
-    // 4g-3 and is read from the barrier of phase 4g-1 on (phase 4g's scales are read
-    // with its first fragments); its buffer is refilled at phase 4g+4, after the
-    // barrier that follows the last read of it, at phase 4g+2.  The last phase of a
-    // tile reads no scales after its barrier, so the next tile's first group may go
-    // to buffer 0 there.
+    // MX scale groups of 16 blocks (P = PPG phases: 4 at 8 bits, 2 at 4 bits)
+    // alternate between two buffers.  Group g is issued at phase Pg-P after the
+    // barrier, ahead of that phase's loads of phase Pg-P+S, so it has landed by the
+    // wait of phase Pg-P+S-1 (loads complete in issue order), and it is read from the
+    // barrier of phase Pg-1 on (phase Pg's scales are read with its first fragments):
+    // hence S <= P.  Its buffer is refilled at phase Pg+P, after the barriers that
+    // follow the last read of it, at phase Pg+P-2.  The last phase of a tile reads no
+    // scales after its barrier, so the next tile's first group may go to buffer 0.
+    static_assert(!MX || S <= PPG, "block scales must land before their first read");
     if constexpr (MX)
-      if ((kt & 3) == 0 && kt + 4 < ktiles) issue_scales(src, (kt >> 2) + 1, wave, la, smem);
+      if (kt % PPG == 0 && kt + PPG < ktiles) issue_scales(src, kt / PPG + 1, wave, la, smem);
     Scales scn;  // MX: phase kt+1's scales
     if (kt + 1 < ktiles) {
       if constexpr (MX) read_scales(smem, fa, wm, wn, kt + 1, scn);
@@ -1514,6 +1549,10 @@ using Cfg64n = TileCfg<64, 64, 2, 2, 64, 4>;
 // CU reads half the LDS bytes per MFMA of 8 waves of 64 x 64 on 256 x 128 (which read
 // as much LDS as their MFMAs take cycles): 8-13 % faster at 8192^3 and the LLM shapes.
 using CfgF8 = TileCfg<256, kF8TileN, 2, kF8WavesN, 64, 2, 1, 32>;
+// 4-bit inputs: the same tile and ring (128 bytes a row a phase, now 256 values in
+// 4 MFMA steps; two 64 KB stages).  Measured against 64-byte phases in four stages:
+// those carry half the MFMA work a phase for the same barrier, waits and scale reads.
+using CfgF4 = TileCfg<256, kF8TileN, 2, kF8WavesN, 64, 2, 1, 32>;
 
 template <class CFG, int DT, bool AK, bool BKC, int EPI, bool VEC, int ODT = DT>
 static hipError_t launch_t(const GemmBatch& b0, hipStream_t s) {

@@ -17,6 +17,9 @@ constexpr int kF8Base = 4;
 // are [ceil(N / kF8TileN) * kF8WavesN][M]).
 constexpr int kF8TileN = 256, kF8WavesN = 2;
 constexpr int f8_code(int fa, int fb, int mx = 0) { return kF8Base + 4 * mx + 2 * fa + fb; }
+// MXFP4: both operands E2M1, two values a byte, with E8M0 block scales (the same
+// 8-bit-path kernel, a 4-bit operand mode).
+constexpr int kF4MX = kF8Base + 8;
 
 // Epilogue kinds the kernel template is instantiated for.
 enum EpiKind : int {

@@ -30,6 +30,7 @@ FGEMM_E4M3, FGEMM_E5M2 = 0, 1
 EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
            "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
            "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_gemm_f8", "fgemm_gemm_mxf8",
+           "fgemm_gemm_mxf4",
            "fgemm_check_args",
            "fgemm_tile_count",
            "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_read_probe", "fgemm_status_string")
@@ -117,6 +118,8 @@ def lib():
                                vp, i64, i32, epi_p, vp]),
         "fgemm_gemm_mxf8": (st, [vp, i64, i64, i64, f32, vp, i64, i32, vp, i64, vp, i64, i32, vp,
                                  i64, f32, vp, i64, i32, epi_p, vp]),
+        "fgemm_gemm_mxf4": (st, [vp, i64, i64, i64, f32, vp, i64, vp, i64, vp, i64, vp, i64, f32,
+                                 vp, i64, i32, epi_p, vp]),
         "fgemm_check_args": (st, [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64, i32,
                                   epi_p]),
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
@@ -243,6 +246,17 @@ def fgemm_gemm_mxf8(handle, M, N, K, alpha, A, lda, a_format, a_scales, ld_a_sca
     return s
 
 
+def fgemm_gemm_mxf4(handle, M, N, K, alpha, A, lda, a_scales, ld_a_scales, B, ldb, b_scales,
+                    ld_b_scales, beta, C, ldc, dtype, epilogue=None, stream=0,
+                    check=True) -> int:
+    e = ctypes.byref(epilogue) if epilogue is not None else None
+    s = lib().fgemm_gemm_mxf4(handle, M, N, K, alpha, A, lda, a_scales, ld_a_scales, B, ldb,
+                              b_scales, ld_b_scales, beta, C, ldc, dtype, e, stream)
+    if check:
+        _check(s, "fgemm_gemm_mxf4")
+    return s
+
+
 def fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype,
                      epilogue=None) -> int:
     e = ctypes.byref(epilogue) if epilogue is not None else None
@@ -355,6 +369,19 @@ class Handle:
         s = current_stream() if stream is None else stream
         return fgemm_gemm_mxf8(self.h, M, N, K, float(alpha), A.data_ptr(), _ld(A), a_format,
                                a_scales.data_ptr(), _ld(a_scales), B.data_ptr(), _ld(B), b_format,
+                               b_scales.data_ptr(), _ld(b_scales), float(beta), C.data_ptr(),
+                               _ld(C), torch_dtype_code(C), epilogue, s)
+
+    def gemm_mxf4(self, A, B, C, a_scales, b_scales, *, alpha=1.0, beta=0.0, epilogue=None,
+                  stream=None):
+        """MXFP4: A (M x K/2) and B (N x K/2) uint8 device tensors of packed E2M1 values
+        (two a byte), a_scales (M x >= K/32) and b_scales (N x >= K/32) E8M0 bytes;
+        C = alpha * A' B'^T + beta * C."""
+        M, K = A.shape[0], 2 * A.shape[1]
+        N = B.shape[0]
+        s = current_stream() if stream is None else stream
+        return fgemm_gemm_mxf4(self.h, M, N, K, float(alpha), A.data_ptr(), _ld(A),
+                               a_scales.data_ptr(), _ld(a_scales), B.data_ptr(), _ld(B),
                                b_scales.data_ptr(), _ld(b_scales), float(beta), C.data_ptr(),
                                _ld(C), torch_dtype_code(C), epilogue, s)
 

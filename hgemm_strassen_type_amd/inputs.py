@@ -131,3 +131,49 @@ def mx_integers(shape, seed: int, fmt: int, lo: int, hi: int, e_lo=124, e_hi=130
     scales = np.full((rows, mx_scale_cols(K)), 127, dtype=np.uint8)
     scales[:, :K // 32] = rng.integers(e_lo, e_hi + 1, size=(rows, K // 32)).astype(np.uint8)
     return codes, scales
+
+
+# 4-bit E2M1 codes: bit 3 the sign, bits 2-0 the magnitude index into these values
+# (the OCP E2M1 encoding).  Rows are stored two codes a byte, code 2i in the low
+# nibble of byte i.
+F4_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def pack_f4_codes(codes: np.ndarray) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8) & 15
+    return np.ascontiguousarray((codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8))
+
+
+def mxf4_small(shape, seed: int, max_index=4, e_lo=125, e_hi=129):
+    """Random E2M1 codes of magnitude index <= max_index (4: |v| <= 2) with random
+    signs, packed, and random E8M0 block scales in [e_lo, e_hi] (2^-2..2^2 by
+    default).  Returns (packed [rows][K/2], scales [rows][mx_scale_cols(K)])."""
+    rows, K = shape
+    rng = np.random.default_rng(seed)
+    codes = (rng.integers(0, max_index + 1, size=shape) |
+             (rng.integers(0, 2, size=shape) << 3)).astype(np.uint8)
+    scales = np.full((rows, mx_scale_cols(K)), 127, dtype=np.uint8)
+    scales[:, :K // 32] = rng.integers(e_lo, e_hi + 1, size=(rows, K // 32)).astype(np.uint8)
+    return pack_f4_codes(codes), scales
+
+
+def mxf4_normal(shape, seed: int, std=1.0):
+    """N(0, std) values stored MXFP4-style: every block of 32 values along a row gets
+    the power-of-two scale that puts its largest magnitude at or below 6 (the largest
+    E2M1 value), stored as E8M0, and each scaled value becomes the code of the
+    nearest E2M1 magnitude (the smaller one on a tie).  Returns (packed, scales)."""
+    rows, K = shape
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape) * std
+    blocks = x.reshape(rows, K // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / 6.0)), 0.0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    q = (blocks / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K)
+    # nearest magnitude: count the midpoints between neighbours strictly below |q|
+    mids = (F4_MAGNITUDES[1:] + F4_MAGNITUDES[:-1]) / 2
+    idx = np.searchsorted(mids, np.abs(q), side="left").astype(np.uint8)
+    codes = idx | ((q < 0).astype(np.uint8) << 3)
+    scales = np.full((rows, mx_scale_cols(K)), 127, dtype=np.uint8)
+    scales[:, :K // 32] = (e + 127).astype(np.uint8)
+    return pack_f4_codes(codes), scales

@@ -301,6 +301,29 @@ fgemm_status_t fgemm_gemm_mxf8(fgemm_handle_t handle, int64_t M, int64_t N, int6
                                fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
                                void* stream);
 
+/* MXFP4 GEMM (CS336 Lecture 05 notes, Page 29: 4-bit floating point holds only 0,
+ * +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6 and is usable only with block scales):
+ *   C[i][j] = alpha * sum_k sA(i,k) qA(i,k) * sB(j,k) qB(j,k) + beta * C[i][j]
+ * with q the E2M1 value (1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * exponent field 0 gives 0 and 0.5) and s the E8M0 scale 2^(e-127) of the value's
+ * block of 32 along K.  A is M x K values, B is N x K values, both row-major and
+ * K-contiguous, packed two values a byte: value k of a row is the low nibble of
+ * byte k/2 when k is even, its high nibble when k is odd.  lda and ldb are row
+ * strides in BYTES (>= K/2); a_scales / b_scales, ld_a_scales / ld_b_scales as for
+ * fgemm_gemm_mxf8.  The page's slide groups 16 values under an E4M3 scale; the
+ * gfx950 block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, format E2M1) applies
+ * E8M0 scales to blocks of 32, so the scales here are the OCP MX ones.  Needs
+ * K % 256 == 0, lda and ldb multiples of 16, ldc a multiple of 8 and 16-byte
+ * aligned A, B and C, else FGEMM_ERR_NOT_SUPPORTED; K = 0 reads no value or scale
+ * (C = beta*C + bias).  Output type, epilogues (NONE, BIAS, ROWSUMSQ), pointers,
+ * streams and errors as for fgemm_gemm_f8. */
+fgemm_status_t fgemm_gemm_mxf4(fgemm_handle_t handle, int64_t M, int64_t N, int64_t K,
+                               float alpha, const void* A, int64_t lda, const void* a_scales,
+                               int64_t ld_a_scales, const void* B, int64_t ldb,
+                               const void* b_scales, int64_t ld_b_scales, float beta, void* C,
+                               int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
+                               void* stream);
+
 /* Size of the fixed per-device scratch array behind fgemm_gemm_noalloc. */
 #define FGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
