@@ -112,6 +112,9 @@ def _load():
     lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
     lib.oracle_decode_f4.restype = ctypes.c_double
     lib.oracle_decode_f4.argtypes = [ctypes.c_uint8]
+    lib.oracle_quantize_mx.restype = ctypes.c_int
+    lib.oracle_quantize_mx.argtypes = [u16p, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, i64, ctypes.c_void_p, i64]
     u8p = ctypes.c_void_p
     lib.oracle_gemm_f8.restype = ctypes.c_int
     lib.oracle_gemm_f8.argtypes = [i64, i64, i64, ctypes.c_double, u8p, i64, ctypes.c_int, u8p,
@@ -432,6 +435,31 @@ def gemm_mxf4(A, B, mx_a, mx_b, *, alpha=1.0, beta=0.0, C=None, dtype=BF16, epi=
     if rc != 0:
         raise ValueError("oracle_gemm_f8 rejected its arguments")
     return D, Q, ss
+
+
+def quantize_mx(X, dtype, fmt, *, transpose=False):
+    """MX quantization of a 16-bit matrix X (rows x cols bit patterns): blocks of 32
+    values along each row, or, with transpose, along each column of X, i.e. along
+    the rows of X^T.  Returns (Q, S): Q the codes of the quantized matrix (X or X^T:
+    one byte a value, or E2M1 packed two a byte), S its E8M0 scales [rows][len/32]."""
+    X = _u16(X)
+    rows, cols = X.shape
+    orows, olen = (cols, rows) if transpose else (rows, cols)
+    width = olen // 2 if fmt == E2M1 else olen
+    Q = np.zeros((orows, width), dtype=np.uint8)
+    S = np.zeros((orows, olen // 32), dtype=np.uint8)
+    rc = _load().oracle_quantize_mx(_ptr(X), rows, cols, cols, dtype, fmt, int(bool(transpose)),
+                                    _ptr(Q), width, _ptr(S), max(olen // 32, 1))
+    if rc != 0:
+        raise ValueError("oracle_quantize_mx rejected its arguments")
+    return Q, S
+
+
+def dequantize_mx(Q, S, fmt):
+    """The fp64 values s * q of quantize_mx's output."""
+    codes = unpack_f4(Q) if fmt == E2M1 else _u8(Q)
+    vals = decode_f4(codes) if fmt == E2M1 else decode_f8(codes, fmt)
+    return vals * np.repeat(decode_e8m0(_u8(S)), 32, axis=1)[:, :vals.shape[1]]
 
 
 def gemm_mxf4_dense(A, B, mx_a, mx_b, *, alpha=1.0):

@@ -769,3 +769,96 @@ int oracle_gemm_f8(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t*
     free(Ad); free(Bd); free(H);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * MX quantization (CS336 Lecture 05 notes, Page 27: a value is stored as
+ * q = cast(x / s) and used as s * q, the scale bringing the values into the
+ * format's range; MX keeps one E8M0 scale per block of 32 values; Pages 27-28:
+ * block scales make a transpose nontrivial, so the transposed operand is quantized
+ * on its own, its blocks running along the other dimension).  Readings:
+ *   s = 2^e, e the smallest integer with amax <= maxval * 2^e (maxval the format's
+ *   largest finite value: E4M3 448, E5M2 57344, E2M1 6), clamped to [-127, 127];
+ *   an all-zero block gets e = 0 (scale byte 127);
+ *   q = the format's finite value nearest to x / s, ties to the code with the even
+ *   last bit, the sign of x kept (a negative value that rounds to 0 gives -0).
+ * ------------------------------------------------------------------------- */
+static double lp_code_value(int code, int fmt) {
+    return fmt == OR_E2M1 ? oracle_decode_f4((uint8_t)code) : oracle_decode_f8((uint8_t)code, fmt);
+}
+
+/* The nonnegative finite codes of a format in increasing value order (codes with the
+ * sign bit clear; E4M3's NaN pattern and E5M2's infinities and NaNs left out). */
+static int lp_positive_codes(int fmt, int* codes) {
+    int n = 0, top = fmt == OR_E2M1 ? 8 : 128;
+    for (int c = 0; c < top; ++c) {
+        double v = lp_code_value(c, fmt);
+        if (isfinite(v)) codes[n++] = c;
+    }
+    return n;   /* values increase with the code for sign-magnitude formats */
+}
+
+static int lp_round(double v, int fmt, const int* pos, int npos) {
+    int sign = signbit(v) ? 1 : 0;
+    double a = fabs(v);
+    int lo = 0, hi = npos - 1;              /* largest code with value <= a */
+    if (a >= lp_code_value(pos[hi], fmt)) {
+        lo = hi;
+    } else {
+        while (hi - lo > 1) {
+            int mid = (lo + hi) / 2;
+            if (lp_code_value(pos[mid], fmt) <= a) lo = mid; else hi = mid;
+        }
+    }
+    int c = pos[lo];
+    if (lo + 1 < npos) {
+        double dl = a - lp_code_value(pos[lo], fmt);
+        double dh = lp_code_value(pos[lo + 1], fmt) - a;
+        if (dh < dl || (dh == dl && (pos[lo + 1] & 1) == 0)) c = pos[lo + 1];
+    }
+    int sbit = fmt == OR_E2M1 ? 8 : 128;
+    return sign ? (c | sbit) : c;
+}
+
+int oracle_quantize_mx(const uint16_t* X, int64_t rows, int64_t cols, int64_t ldx, int dtype,
+                       int fmt, int transpose, uint8_t* Q, int64_t ldq, uint8_t* S,
+                       int64_t lds) {
+    if (rows < 0 || cols < 0 || fmt < OR_E4M3 || fmt > OR_E2M1) return -1;
+    const int64_t orows = transpose ? cols : rows;   /* rows of the quantized matrix */
+    const int64_t olen = transpose ? rows : cols;    /* values in each of its rows */
+    if (olen % 32) return -1;
+    const double maxval = fmt == OR_E4M3 ? 448.0 : fmt == OR_E5M2 ? 57344.0 : 6.0;
+    int pos[128];
+    const int npos = lp_positive_codes(fmt, pos);
+    for (int64_t r = 0; r < orows; ++r) {
+        for (int64_t b = 0; b < olen / 32; ++b) {
+            double x[32], amax = 0.0;
+            for (int t = 0; t < 32; ++t) {
+                const int64_t k = 32 * b + t;
+                const uint16_t h = transpose ? X[k * ldx + r] : X[r * ldx + k];
+                x[t] = oracle_decode(h, dtype);
+                if (!isfinite(x[t])) return -1;
+                if (fabs(x[t]) > amax) amax = fabs(x[t]);
+            }
+            int e = 0;
+            if (amax > 0.0) {
+                e = (int)ceil(log2(amax / maxval));
+                while (amax > ldexp(maxval, e)) ++e;          /* exact: smallest such e */
+                while (amax <= ldexp(maxval, e - 1)) --e;
+            }
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            S[r * lds + b] = (uint8_t)(e + 127);
+            for (int t = 0; t < 32; ++t) {
+                const int64_t k = 32 * b + t;
+                const int c = lp_round(ldexp(x[t], -e), fmt, pos, npos);
+                if (fmt == OR_E2M1) {
+                    uint8_t* p = Q + r * ldq + k / 2;
+                    *p = (k & 1) ? (uint8_t)((*p & 0x0F) | (c << 4)) : (uint8_t)((*p & 0xF0) | c);
+                } else {
+                    Q[r * ldq + k] = (uint8_t)c;
+                }
+            }
+        }
+    }
+    return 0;
+}

@@ -738,6 +738,101 @@ def test_mxf4_equals_mxf8_on_the_same_values():
                          sb[:, :2])
 
 
+# ------------------------------------------------------------ MX quantization
+MX_MAXVAL = {oracle.E4M3: 448.0, oracle.E5M2: 57344.0, oracle.E2M1: 6.0}
+
+
+def _smallest_e(amax, maxval):
+    """The definition of the block exponent, by search: the smallest integer e with
+    amax <= maxval * 2^e (0 for an all-zero block), clamped to [-127, 127]."""
+    if amax == 0.0:
+        return 0
+    e = -200
+    while amax > maxval * 2.0 ** e:
+        e += 1
+    return max(-127, min(127, e))
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2, oracle.E2M1])
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_quantize_scales_are_the_smallest_that_fit(fmt, dtype):
+    """Every block's E8M0 scale is the smallest power of two that brings its largest
+    magnitude within the format's largest finite value (blocks of mixed magnitudes,
+    one all-zero block); dequantized values never exceed that value times s."""
+    rng = np.random.default_rng(11 + fmt)
+    x = rng.standard_normal((6, 128)) * np.exp2(rng.integers(-8, 8, size=(6, 1)))  # fp16-finite
+    x[2, 32:64] = 0.0
+    X = inputs.to_bits(x, dtype)
+    Q, S = oracle.quantize_mx(X, dtype, fmt)
+    xv = oracle.decode(X, dtype)
+    for r in range(6):
+        for b in range(4):
+            amax = float(np.max(np.abs(xv[r, 32 * b:32 * b + 32])))
+            assert int(S[r, b]) - 127 == _smallest_e(amax, MX_MAXVAL[fmt]), (r, b)
+    D = oracle.dequantize_mx(Q, S, fmt)
+    s = np.repeat(oracle.decode_e8m0(S), 32, axis=1)
+    assert np.all(np.abs(D) <= MX_MAXVAL[fmt] * s)
+    assert np.all(D[2, 32:64] == 0.0) and S[2, 1] == 127
+
+
+@pytest.mark.parametrize("fmt,tdt", [(oracle.E4M3, torch.float8_e4m3fn),
+                                     (oracle.E5M2, torch.float8_e5m2)])
+def test_quantize_8bit_rounding_is_torchs_cast(fmt, tdt):
+    """With the scale fixed, each 8-bit code is the round-to-nearest-even cast of
+    x / s that torch's float8 types perform (sign of zero kept)."""
+    rng = np.random.default_rng(21 + fmt)
+    x = rng.standard_normal((8, 256)) * 3.0
+    x[0, :4] = [-1e-30, 1e-30, 0.0, -0.0]
+    X = inputs.to_bits(x, BF16)
+    Q, S = oracle.quantize_mx(X, BF16, fmt)
+    xv = oracle.decode(X, BF16)
+    scaled = xv / np.repeat(oracle.decode_e8m0(S), 32, axis=1)
+    ref = torch.from_numpy(scaled.astype(np.float32)).to(tdt).view(torch.uint8).numpy()
+    assert np.array_equal(Q, ref)
+    assert Q[0, 0] == 0x80 and Q[0, 2] == 0x00
+
+
+def test_quantize_4bit_rounding_and_ties():
+    """E2M1 codes: the nearest of the page's values (CS336 Lecture 05 notes, Page 29),
+    a tie going to the even code, by a plain search over the table; worked ties
+    0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0
+    (a block whose largest value is 6, so s = 1)."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 6.0]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -4.0, 6.0]
+    row = np.zeros(32)
+    row[:len(ties)] = ties
+    X = inputs.to_bits(row[None, :], BF16)
+    Q, S = oracle.quantize_mx(X, BF16, oracle.E2M1)
+    assert S[0, 0] == 127
+    got = oracle.decode_f4(oracle.unpack_f4(Q))[0, :len(ties)]
+    assert list(got) == want
+    # random values against the plain search
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((4, 64)) * 2.0
+    X = inputs.to_bits(x, F16)
+    Q, S = oracle.quantize_mx(X, F16, oracle.E2M1)
+    xv = oracle.decode(X, F16)
+    table = F4_PAGE_VALUES
+    for r in range(4):
+        for k in range(64):
+            v = xv[r, k] / 2.0 ** (int(S[r, k // 32]) - 127)
+            best = min(range(8), key=lambda c: (abs(abs(v) - table[c]), c & 1))
+            code = best | (8 if np.signbit(v) else 0)
+            assert oracle.unpack_f4(Q)[r, k] == code, (r, k, v)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E2M1])
+def test_quantize_transpose_is_quantizing_the_transpose(fmt):
+    """The transposed quantization (blocks along the columns of X) equals quantizing
+    the explicitly transposed matrix (Page 28: transposes quantized separately); it
+    differs from the transpose of the row-wise quantization."""
+    X = inputs.normal((64, 96), 41, BF16)
+    Qt, St = oracle.quantize_mx(X, BF16, fmt, transpose=True)
+    Q2, S2 = oracle.quantize_mx(np.ascontiguousarray(X.T), BF16, fmt)
+    assert np.array_equal(Qt, Q2) and np.array_equal(St, S2)
+    assert Qt.shape[0] == 96 and St.shape == (96, 2)
+
+
 # ------------------------------------------------------------ whole-output references
 @pytest.mark.parametrize("transA,transB", [(False, False), (True, False), (False, True)])
 def test_dense_exact_on_integers(transA, transB):
