@@ -282,7 +282,7 @@ def f8_workloads(torch, h, fgemm, timer, reps):
     with a per-tensor power-of-two scale, A M x K and B N x K (K-contiguous), bf16
     output, beta 0: 8192^3 and the 16384-token LLM shapes, against the dense fp8
     MFMA peak; MXFP8 at 8192^3; MXFP4 at the same three shapes against the dense
-    fp4 peak."""
+    fp4 peak; the MX quantizer (row-wise and transposed) against the HBM peak."""
     gen = torch.Generator(device="cuda")
     out = {}
 
@@ -357,6 +357,26 @@ def f8_workloads(torch, h, fgemm, timer, reps):
         out[f"mxf4_{M}x{N}x{K}"] = r
         log(f"mxf4_{M}x{N}x{K}: {r}")
         del A, B, C, sA, sB
+
+    # MX quantization (HBM-bound): the projection's activations row-wise to MXFP8 and
+    # the FFN-up weights W (K x N) transposed to MXFP4; algorithmic bytes = the 16-bit
+    # input read once, the codes and the scale bytes written once
+    for (name, rows, cols, fmt, tr, std) in [
+            ("quantize_mxfp8_16384x4096", 16384, 4096, fgemm.FGEMM_E4M3, False, 1.0),
+            ("quantize_mxfp4_T_4096x14336", 4096, 14336, fgemm.FGEMM_E2M1, True, 0.02)]:
+        gen.manual_seed(6007)
+        X = (torch.randn((rows, cols), generator=gen, device="cuda") * std).to(torch.bfloat16)
+        Q, S = fgemm.quantize_mx(X, fmt, transpose=tr)
+        ms = timer.time(lambda: fgemm.quantize_mx(X, fmt, transpose=tr, Q=Q, scales=S), reps, 3,
+                        WARM_MS)
+        n = rows * cols
+        alg = 2.0 * n + (0.5 if fmt == fgemm.FGEMM_E2M1 else 1.0) * n + n / 32
+        r = {"ms": round(ms, 5), "hbm_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "bytes": alg, "transposed": tr}
+        out[name] = r
+        log(f"{name}: {r}")
+        del X, Q, S
     return out
 
 

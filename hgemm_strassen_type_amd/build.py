@@ -34,7 +34,7 @@ def _units():
             for bk in (0, 1):
                 units.append((os.path.join(CSRC, "gemm_inst.hip"), f"gemm_inst_{dt}_{ak}{bk}.o",
                               [f"-DFG_DT={dt}", f"-DFG_AK={ak}", f"-DFG_BK={bk}"]))
-    for src in ("gemm_f8.hip", "strassen_adds.hip", "noalloc.hip", "read_probe.hip",
+    for src in ("gemm_f8.hip", "strassen_adds.hip", "noalloc.hip", "read_probe.hip", "quantize_mx.hip",
                 "fgemm_api.cpp", "model.cpp"):
         units.append((os.path.join(CSRC, src), src.rsplit(".", 1)[0] + ".o", []))
     return units

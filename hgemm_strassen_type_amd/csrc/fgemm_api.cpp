@@ -1213,6 +1213,33 @@ fgemm_status_t fgemm_gemm_mxf8(fgemm_handle_t h, int64_t M, int64_t N, int64_t K
                  1.f, sb, ld_b_scales, beta, C, ldc, dtype, epi, stream);
 }
 
+fgemm_status_t fgemm_quantize_mx(const void* X, int64_t rows, int64_t cols, int64_t ldx,
+                                 fgemm_dtype_t x_dtype, int transpose, fgemm_f8_format_t format,
+                                 void* Q, int64_t ldq, void* scales, int64_t ld_scales,
+                                 void* stream) {
+  if (rows < 0 || cols < 0 || ldx < (cols > 1 ? cols : 1)) return FGEMM_ERR_INVALID_VALUE;
+  if (x_dtype != FGEMM_F16 && x_dtype != FGEMM_BF16) return FGEMM_ERR_INVALID_VALUE;
+  if (format != FGEMM_E4M3 && format != FGEMM_E5M2 && format != FGEMM_E2M1)
+    return FGEMM_ERR_INVALID_VALUE;
+  const int64_t orows = transpose ? cols : rows, olen = transpose ? rows : cols;
+  if (olen % 32) return FGEMM_ERR_INVALID_VALUE;
+  const int64_t row_bytes = format == FGEMM_E2M1 ? olen / 2 : olen;
+  if (ldq < (row_bytes > 1 ? row_bytes : 1) || ld_scales < (olen / 32 > 1 ? olen / 32 : 1))
+    return FGEMM_ERR_INVALID_VALUE;
+  if (orows == 0 || olen == 0) return FGEMM_OK;
+  if (!X || !Q || !scales) return FGEMM_ERR_INVALID_VALUE;
+  if (!aligned16(X) || !aligned16(Q) || ldx % 8 || ldq % 16) return FGEMM_ERR_NOT_SUPPORTED;
+  // 32-bit grid limits of the two kernels
+  if ((!transpose && rows * (cols / 32) * 4 / 256 >= INT32_MAX) ||
+      (transpose && (rows + 127) / 128 > 65535))
+    return FGEMM_ERR_NOT_SUPPORTED;
+  const hipError_t e = launch_quantize_mx(X, rows, cols, ldx,
+                                          x_dtype == FGEMM_BF16 ? kBF16 : kF16, transpose != 0,
+                                          (int)format, Q, ldq, scales, ld_scales,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FGEMM_OK : FGEMM_ERR_HIP;
+}
+
 fgemm_status_t fgemm_gemm_mxf4(fgemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
                                const void* A, int64_t lda, const void* a_scales,
                                int64_t ld_a_scales, const void* B, int64_t ldb,

@@ -21,6 +21,13 @@ constexpr int f8_code(int fa, int fb, int mx = 0) { return kF8Base + 4 * mx + 2 
 // 8-bit-path kernel, a 4-bit operand mode).
 constexpr int kF4MX = kF8Base + 8;
 
+// MX quantization of a 16-bit matrix (dtype kF16/kBF16) into codes of format `fmt`
+// (fgemm_f8_format_t) and E8M0 block scales, blocks along rows or, with transpose,
+// along columns; arguments checked by the caller.
+hipError_t launch_quantize_mx(const void* X, int64_t rows, int64_t cols, int64_t ldx, int dtype,
+                              bool transpose, int fmt, void* Q, int64_t ldq, void* S, int64_t lds,
+                              hipStream_t s);
+
 // Epilogue kinds the kernel template is instantiated for.
 enum EpiKind : int {
   kEpiStore16 = 0,   // 16-bit output: alpha, beta*C, optional bias, optional row sum of squares

@@ -24,13 +24,13 @@ FGEMM_EPI_ACT, FGEMM_EPI_ROPE, FGEMM_EPI_SWIGLU_BWD, FGEMM_EPI_RMS_BWD = 8, 16, 
 FGEMM_ACT_RELU, FGEMM_ACT_SILU, FGEMM_ACT_GELU_TANH = 1, 2, 3
 FGEMM_PATH_CLASSICAL, FGEMM_PATH_STRASSEN = 0, 1
 FGEMM_VARIANT_S69, FGEMM_VARIANT_WINOGRAD, FGEMM_VARIANT_R223 = 0, 1, 2
-FGEMM_E4M3, FGEMM_E5M2 = 0, 1
+FGEMM_E4M3, FGEMM_E5M2, FGEMM_E2M1 = 0, 1, 2
 
 # every symbol include/fgemm.h declares
 EXPORTS = ("fgemm_create", "fgemm_destroy", "fgemm_set_workspace", "fgemm_get_model",
            "fgemm_set_model", "fgemm_select", "fgemm_select_model", "fgemm_gemm",
            "fgemm_gemm_plan", "fgemm_gemm_noalloc", "fgemm_gemm_f8", "fgemm_gemm_mxf8",
-           "fgemm_gemm_mxf4",
+           "fgemm_gemm_mxf4", "fgemm_quantize_mx",
            "fgemm_check_args",
            "fgemm_tile_count",
            "fgemm_wave_count", "fgemm_plan_rel_err", "fgemm_read_probe", "fgemm_status_string")
@@ -120,6 +120,7 @@ def lib():
                                  i64, f32, vp, i64, i32, epi_p, vp]),
         "fgemm_gemm_mxf4": (st, [vp, i64, i64, i64, f32, vp, i64, vp, i64, vp, i64, vp, i64, f32,
                                  vp, i64, i32, epi_p, vp]),
+        "fgemm_quantize_mx": (st, [vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, i64, vp]),
         "fgemm_check_args": (st, [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64, i32,
                                   epi_p]),
         "fgemm_tile_count": (i64, [i64, i64, i64, i64]),
@@ -255,6 +256,35 @@ def fgemm_gemm_mxf4(handle, M, N, K, alpha, A, lda, a_scales, ld_a_scales, B, ld
     if check:
         _check(s, "fgemm_gemm_mxf4")
     return s
+
+
+def fgemm_quantize_mx(X, rows, cols, ldx, x_dtype, transpose, fmt, Q, ldq, scales, ld_scales,
+                      stream=0, check=True) -> int:
+    s = lib().fgemm_quantize_mx(X, rows, cols, ldx, x_dtype, int(bool(transpose)), fmt, Q, ldq,
+                                scales, ld_scales, stream)
+    if check:
+        _check(s, "fgemm_quantize_mx")
+    return s
+
+
+def quantize_mx(X, fmt, *, transpose=False, Q=None, scales=None, stream=None):
+    """MX quantization of a 2-D fp16/bf16 device tensor by fgemm_quantize_mx: blocks of
+    32 along its rows, or (transpose) along its columns, i.e. of X^T.  Returns (Q,
+    scales): uint8 codes of X or X^T (two E2M1 values a byte) and E8M0 scales whose
+    row stride is rounded up to whole 16-byte groups, as the MX GEMMs take them."""
+    import torch
+    rows, cols = X.shape
+    orows, olen = (cols, rows) if transpose else (rows, cols)
+    width = olen // 2 if fmt == FGEMM_E2M1 else olen
+    if Q is None:
+        Q = torch.empty((orows, width), dtype=torch.uint8, device=X.device)
+    if scales is None:
+        scols = max(16, (olen // 32 + 15) // 16 * 16)
+        scales = torch.full((orows, scols), 127, dtype=torch.uint8, device=X.device)
+    s = current_stream() if stream is None else stream
+    fgemm_quantize_mx(X.data_ptr(), rows, cols, _ld(X), torch_dtype_code(X), transpose, fmt,
+                      Q.data_ptr(), _ld(Q), scales.data_ptr(), _ld(scales), s)
+    return Q, scales
 
 
 def fgemm_check_args(transA, transB, M, N, K, A, lda, B, ldb, beta, C, ldc, dtype,

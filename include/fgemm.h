@@ -256,7 +256,9 @@ fgemm_status_t fgemm_gemm_plan(fgemm_handle_t handle, const fgemm_plan_t* plan,
  * 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities, largest finite
  * 448; E5M2 is 1 sign, 5 exponent (bias 15) and 2 mantissa bits, IEEE-style
  * infinities and NaNs, largest finite 57344 (CS336 Lecture 05 notes, Page 27). */
-typedef enum { FGEMM_E4M3 = 0, FGEMM_E5M2 = 1 } fgemm_f8_format_t;
+typedef enum { FGEMM_E4M3 = 0, FGEMM_E5M2 = 1, FGEMM_E2M1 = 2 } fgemm_f8_format_t;
+/* FGEMM_E2M1 (the 4-bit format of fgemm_gemm_mxf4) is taken by fgemm_quantize_mx
+ * only; fgemm_gemm_f8 and fgemm_gemm_mxf8 refuse it. */
 
 /* 8-bit GEMM with per-tensor scales (CS336 Lecture 05 notes, Page 27: a value is
  * stored as q = cast(x/s) and used as s*q, one fp32 scale per tensor; Page 28:
@@ -323,6 +325,33 @@ fgemm_status_t fgemm_gemm_mxf4(fgemm_handle_t handle, int64_t M, int64_t N, int6
                                const void* b_scales, int64_t ld_b_scales, float beta, void* C,
                                int64_t ldc, fgemm_dtype_t dtype, const fgemm_epilogue_t* epilogue,
                                void* stream);
+
+/* MX quantization for the 8-bit and 4-bit GEMMs (CS336 Lecture 05 notes, Page 27: a
+ * value is stored as q = cast(x/s) and used as s*q, one E8M0 scale per block of 32;
+ * Pages 27-28: block scales make a transpose nontrivial, so the transposed operand
+ * is quantized separately, its blocks running along the other dimension).
+ * X is rows x cols 16-bit values of `x_dtype`, row-major (ldx >= cols elements).
+ *   transpose == 0: quantizes X itself: Q has `rows` rows of `cols` values, blocks of
+ *     32 consecutive values of a row of X (cols % 32 == 0);
+ *   transpose != 0: quantizes X^T: Q has `cols` rows of `rows` values, row j holding
+ *     column j of X, blocks of 32 consecutive rows of X (rows % 32 == 0);
+ * in both cases the K-contiguous layout the GEMMs take (A M x K, B N x K).  For a
+ * block with largest magnitude amax, e is the smallest integer with
+ * amax <= maxval * 2^e (maxval = 448 for E4M3, 57344 for E5M2, 6 for E2M1; clamped
+ * to [-127, 127]; 0 for an all-zero block), scales[r*ld_scales + b] = e + 127, and
+ * each value is coded as the format's value nearest to x * 2^-e, ties to the even
+ * code, its sign kept.  Q holds one byte a value (E4M3, E5M2) or two values a byte
+ * (E2M1, value 2i in the low nibble); ldq is its row stride in BYTES.  ld_scales
+ * (bytes) >= the quantized row length / 32; only those bytes of a scale row are
+ * written.  X, Q, scales are device pointers; work is enqueued on `stream`.  Needs X
+ * and Q 16-byte aligned, ldx % 8 == 0, ldq % 16 == 0, else FGEMM_ERR_NOT_SUPPORTED;
+ * a row length not a multiple of 32, ldq below a quantized row, ld_scales below its
+ * block count, an unknown format or type, or a null pointer with work to do is
+ * FGEMM_ERR_INVALID_VALUE.  Inputs are finite (NaN or Inf give unspecified codes). */
+fgemm_status_t fgemm_quantize_mx(const void* X, int64_t rows, int64_t cols, int64_t ldx,
+                                 fgemm_dtype_t x_dtype, int transpose, fgemm_f8_format_t format,
+                                 void* Q, int64_t ldq, void* scales, int64_t ld_scales,
+                                 void* stream);
 
 /* Size of the fixed per-device scratch array behind fgemm_gemm_noalloc. */
 #define FGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

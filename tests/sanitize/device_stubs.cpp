@@ -40,6 +40,10 @@ hipError_t launch_lin_pre(const BlockedOperand&, int64_t, int64_t, int, int, int
   return hipErrorNoDevice;
 }
 hipError_t launch_lin_post(const LinPostArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_quantize_mx(const void*, int64_t, int64_t, int64_t, int, bool, int, void*,
+                              int64_t, void*, int64_t, hipStream_t) {
+  return hipErrorNoDevice;
+}
 int64_t postadd_ss_parts(int64_t n) {  // as the post-add's grid: 256 lanes of 4 columns
   const int64_t g = (n / 4 + 255) / 256;
   return g > 0 ? g : 1;

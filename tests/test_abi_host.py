@@ -404,3 +404,25 @@ def test_read_probe_argument_checks():
     for src, nbytes, out in ((fake, -16, fake), (fake, 15, fake), (fake, 24, fake),
                              (fake, 32, None), (None, 16, fake), (fake + 8, 16, fake)):
         assert fgemm.fgemm_read_probe(src, nbytes, out, None, check=False) == inval
+
+
+def test_quantize_argument_checks():
+    """fgemm_quantize_mx's refusals return before any device call."""
+    inval, nsup = fgemm.FGEMM_ERR_INVALID_VALUE, fgemm.FGEMM_ERR_NOT_SUPPORTED
+    p = 1 << 20  # 16-byte aligned addresses that are never dereferenced
+
+    def call(rows=64, cols=64, ldx=64, dt=fgemm.FGEMM_BF16, tr=0, fmt=fgemm.FGEMM_E4M3, x=p,
+             q=p, ldq=64, s=p, lds=2):
+        return fgemm.fgemm_quantize_mx(x, rows, cols, ldx, dt, tr, fmt, q, ldq, s, lds, None,
+                                       check=False)
+    assert call(cols=48) == inval                    # row length not a multiple of 32
+    assert call(tr=1, rows=40) == inval              # transposed row length = rows
+    assert call(ldx=32) == inval                     # ldx < cols
+    assert call(ldq=63) == inval                     # a quantized row is 64 bytes
+    assert call(fmt=fgemm.FGEMM_E2M1, ldq=31) == inval   # 4-bit: 32 bytes
+    assert call(lds=1) == inval
+    assert call(fmt=5) == inval and call(dt=3) == inval
+    assert call(x=0) == inval and call(q=0) == inval and call(s=0) == inval
+    assert call(x=p + 4) == nsup and call(q=p + 8) == nsup
+    assert call(ldx=68) == nsup and call(ldq=72) == nsup
+    assert call(rows=0, x=0, q=0, s=0) == fgemm.FGEMM_OK   # nothing to do
