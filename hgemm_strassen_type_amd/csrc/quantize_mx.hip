@@ -19,7 +19,8 @@
 // scale byte a block.  Row-wise blocks are contiguous: four lanes share a block, each
 // moving one 16-byte chunk, so every load and store instruction of a wave is one
 // contiguous run.  Transposed blocks run down columns: a workgroup stages a 128 x 64
-// tile in LDS as fp32 and each wave quantizes one 32-row band of it, a column a lane.
+// tile in LDS as fp32 and each wave quantizes 16 of its columns, four lanes a column
+// (one 32-row block each), so that the four write one output row's 128 (64) bytes.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -132,18 +133,24 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
   }
 }
 
-constexpr int kTR = 128, kTC = 64, kPitch = kTC + 1;  // transposed tile (fp32 in LDS)
+constexpr int kTR = 128, kTC = 64;  // transposed tile (fp32 in LDS, kTC words a row)
+
+// LDS word of tile element (row, col): each 32-row band's columns rotated by 8 words,
+// so that the 32 lanes of a half-wave (8 columns x 4 bands) read 32 distinct banks.
+__device__ __forceinline__ int tile_at(int row, int col) {
+  return row * kTC + ((col + 8 * (row >> 5)) & (kTC - 1));
+}
 
 // Transposed: the tile of source rows r0 .. r0+127, columns c0 .. c0+63 becomes rows
 // c0 .. c0+63 of the quantized X^T, blocks r0/32 .. r0/32+3 of each; wave w takes
-// block w (source rows r0+32w ..), lane l column c0 + l.
+// columns c0 + 16w .., lane l column 16w + l/4 and block l%4 (source rows 32(l%4) ..).
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ X,
                                                             int64_t ldx, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ Q,
                                                             int64_t ldq, uint8_t* __restrict__ S,
                                                             int64_t lds) {
-  __shared__ float tile[kTR * kPitch];
+  __shared__ float tile[kTR * kTC];
   const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
   const int t = threadIdx.x;
 #pragma unroll
@@ -162,18 +169,21 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
     } else if (r0 + rr < rows && c0 + cc < cols) {  // the last columns of a row
       for (int k = 0; c0 + cc + k < cols; ++k) v[k] = load16<DT>(X[(r0 + rr) * ldx + c0 + cc + k]);
     }
+    // 8 consecutive words: the rotation moves whole 8-word chunks, so none wraps
+    float* dst = tile + tile_at(rr, cc);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) tile[rr * kPitch + cc + k] = v[k];
+    for (int k = 0; k < 8; ++k) dst[k] = v[k];
   }
   __syncthreads();
   const int w = t >> 6, l = t & 63;
-  const int64_t col = c0 + l, rb = r0 + 32 * w;      // output row, first source row
+  const int tc = 16 * w + (l >> 2), band = l & 3;    // tile column and 32-row band
+  const int64_t col = c0 + tc, rb = r0 + 32 * band;  // output row, first source row
   if (col >= cols || rb >= rows) return;            // rows % 32 == 0: a block is whole
   float x[32];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    x[i] = tile[(32 * w + i) * kPitch + l];
+    x[i] = tile[tile_at(32 * band + i, tc)];
     amax = fmaxf(amax, fabsf(x[i]));
   }
   const int e = block_exponent<FMT>(amax);
