@@ -77,3 +77,62 @@ def test_graph_replays_match_eager():
         del g
     finally:
         h.close()
+
+
+def test_graph_quantize_then_low_precision_gemms():
+    """The MX quantizer (row-wise and transposed) feeding the MXFP4 and MXFP8 GEMMs,
+    captured in one graph: neither allocates nor synchronises, so every replay
+    reproduces the eager codes, scales and products bit for bit."""
+    import torch
+    say("graph capture: quantize_mx + mxf4 + mxf8 chain")
+    h = fgemm.Handle(0)
+    try:
+        M, N, K = 512, 384, 1024
+        X = to_dev(inputs.normal((M, K), 811, BF16), BF16)
+        W = to_dev(inputs.normal((K, N), 812, BF16, std=0.02), BF16)
+        E4, E2 = fgemm.FGEMM_E4M3, fgemm.FGEMM_E2M1
+        qx4, sx4 = fgemm.quantize_mx(X, E2)
+        qw4, sw4 = fgemm.quantize_mx(W, E2, transpose=True)
+        qx8, sx8 = fgemm.quantize_mx(X, E4)
+        qw8, sw8 = fgemm.quantize_mx(W, E4, transpose=True)
+        C4 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        C8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def calls():
+            fgemm.quantize_mx(X, E2, Q=qx4, scales=sx4)
+            fgemm.quantize_mx(W, E2, transpose=True, Q=qw4, scales=sw4)
+            fgemm.quantize_mx(X, E4, Q=qx8, scales=sx8)
+            fgemm.quantize_mx(W, E4, transpose=True, Q=qw8, scales=sw8)
+            h.gemm_mxf4(qx4, qw4, C4, sx4, sw4)
+            h.gemm_mxf8(qx8, qw8, C8, sx8, sw8)
+
+        calls()
+        torch.cuda.synchronize()
+        outs = (qx4, sx4, qw4, sw4, qx8, sx8, qw8, sw8)
+        ref = [t.cpu().numpy().copy() for t in outs] + [from_dev(C4), from_dev(C8)]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            calls()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            calls()
+        torch.cuda.synchronize()
+        for r in range(3):
+            for t in (qx4, qw4, qx8, qw8):
+                t.fill_(0xAA)
+            for t in (sx4, sw4, sx8, sw8):   # the written scale columns (K/32 a row)
+                t[:, :K // 32].fill_(0xAA)
+            C4.fill_(float("nan"))
+            C8.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = [t.cpu().numpy() for t in outs] + [from_dev(C4), from_dev(C8)]
+            for i, (a, b) in enumerate(zip(got, ref)):
+                assert np.array_equal(a, b), (r, i)
+        del g
+    finally:
+        h.close()
