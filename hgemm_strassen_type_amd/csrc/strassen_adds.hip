@@ -32,6 +32,33 @@ namespace fgemm {
 
 namespace {
 
+// Streaming accesses: every input of these kernels is read once and every output
+// written once, so their lines are non-temporal; kept in L2 they would only evict
+// lines that other work reuses (Winograd/S69 depth 1 at 16384^3: 1.3-1.8 % faster in
+// all).  The nontemporal builtins take native vector types, HIP's uint4 / uint2 /
+// float4 are structs: these route them through.
+typedef unsigned nt_v4u __attribute__((ext_vector_type(4)));
+typedef unsigned nt_v2u __attribute__((ext_vector_type(2)));
+typedef float nt_v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_ld(const uint4* p) {
+  const nt_v4u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 nt_ld(const uint2* p) {
+  const nt_v2u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v2u*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 nt_ld(const float4* p) {
+  const nt_v4f v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4f*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_st(uint4 v, uint4* p) {
+  __builtin_nontemporal_store(nt_v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_v4u*>(p));
+}
+__device__ __forceinline__ void nt_st(uint2 v, uint2* p) {
+  __builtin_nontemporal_store(nt_v2u{v.x, v.y}, reinterpret_cast<nt_v2u*>(p));
+}
+
 __device__ __forceinline__ float h2f(uint32_t h, int dt) {
   return dt == kBF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
@@ -79,7 +106,7 @@ __global__ void maxabs_kernel(const uint16_t* __restrict__ X, int64_t ld, int64_
         uint4 v[kMaxRows];
 #pragma unroll
         for (int u = 0; u < kMaxRows; ++u)
-          v[u] = *reinterpret_cast<const uint4*>(X + (r0 + u) * ld + c);
+          v[u] = nt_ld(reinterpret_cast<const uint4*>(X + (r0 + u) * ld + c));
 #pragma unroll
         for (int u = 0; u < kMaxRows; ++u) {
           float f[8];
@@ -151,10 +178,10 @@ __global__ void preadd_kernel(PreAddArgs a) {
   for (int64_t r = blockIdx.y; r < a.srows; r += gridDim.y) {
     int64_t si = r * a.ld + c;
     float x11[8], x12[8], x21[8], x22[8];
-    unpack8(*reinterpret_cast<const uint4*>(a.blk[0] + si), a.dt, x11);
-    unpack8(*reinterpret_cast<const uint4*>(a.blk[1] + si), a.dt, x12);
-    unpack8(*reinterpret_cast<const uint4*>(a.blk[2] + si), a.dt, x21);
-    unpack8(*reinterpret_cast<const uint4*>(a.blk[3] + si), a.dt, x22);
+    unpack8(nt_ld(reinterpret_cast<const uint4*>(a.blk[0] + si)), a.dt, x11);
+    unpack8(nt_ld(reinterpret_cast<const uint4*>(a.blk[1] + si)), a.dt, x12);
+    unpack8(nt_ld(reinterpret_cast<const uint4*>(a.blk[2] + si)), a.dt, x21);
+    unpack8(nt_ld(reinterpret_cast<const uint4*>(a.blk[3] + si)), a.dt, x22);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x11[e] *= s; x12[e] *= s; x21[e] *= s; x22[e] *= s;
@@ -216,7 +243,7 @@ __global__ void preadd_kernel(PreAddArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < 7; ++q)
-      if (a.out[q]) *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o[q]);
+      if (a.out[q]) nt_st(pack8_f16(o[q]), reinterpret_cast<uint4*>(a.out[q] + di));
   }
 }
 
@@ -302,7 +329,7 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
       float p[4][7];
 #pragma unroll
       for (int q = 0; q < 7; ++q) {
-        float4 v = *reinterpret_cast<const float4*>(a.P[q] + i * a.n + j);
+        float4 v = nt_ld(reinterpret_cast<const float4*>(a.P[q] + i * a.n + j));
         p[0][q] = v.x; p[1][q] = v.y; p[2][q] = v.z; p[3][q] = v.w;
       }
       float c[4][4];  // [element][block]
@@ -335,15 +362,15 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
             v[e] = g / (1.f + __expf(-g)) * u;
           }
           if (a.beta != 0.f) {
-            uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+            uint2 cv = nt_ld(reinterpret_cast<const uint2*>(a.C + off));
             v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
             v[1] += a.beta * h2f(cv.x >> 16, a.dt);
             v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
             v[3] += a.beta * h2f(cv.y >> 16, a.dt);
           }
-          *reinterpret_cast<uint2*>(a.C + off) =
+          nt_st(
               make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
-                         f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+                         f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16)), reinterpret_cast<uint2*>(a.C + off));
         }
       } else {
 #pragma unroll
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (float)(f_out * c[e][b]);
             if (a.beta != 0.f) {
-              uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+              uint2 cv = nt_ld(reinterpret_cast<const uint2*>(a.C + off));
               v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
               v[1] += a.beta * h2f(cv.x >> 16, a.dt);
               v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
@@ -384,7 +411,7 @@ __global__ __launch_bounds__(256) void postadd_kernel(PostAddKArgs a) {
               const float w = h2f(o[e], a.dt);
               ss[b >> 1] += w * w;
             }
-            *reinterpret_cast<uint2*>(a.C + off) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            nt_st(make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16)), reinterpret_cast<uint2*>(a.C + off));
           }
         }
       }
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(256) void lin_pre_kernel(LinPreKArgs a) {
 #pragma unroll
     for (int b = 0; b < kLinMaxBlocks; ++b) {
       if (b < a.nblk) {
-        unpack8(*reinterpret_cast<const uint4*>(a.blk[b] + si), a.dt, x[b]);
+        unpack8(nt_ld(reinterpret_cast<const uint4*>(a.blk[b] + si)), a.dt, x[b]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[b][e] *= s;
       }
@@ -446,7 +473,7 @@ __global__ __launch_bounds__(256) void lin_pre_kernel(LinPreKArgs a) {
             for (int e = 0; e < 8; ++e) o[e] += (float)w * x[b][e];
           }
         }
-        *reinterpret_cast<uint4*>(a.out[q] + di) = pack8_f16(o);
+        nt_st(pack8_f16(o), reinterpret_cast<uint4*>(a.out[q] + di));
       }
     }
   }
@@ -474,7 +501,7 @@ __global__ __launch_bounds__(256) void lin_post_kernel(LinPostKArgs a) {
 #pragma unroll
     for (int r = 0; r < kLinMaxProducts; ++r) {
       if (r < a.np) {
-        const float4 v = *reinterpret_cast<const float4*>(a.P[r] + i * a.n + j);
+        const float4 v = nt_ld(reinterpret_cast<const float4*>(a.P[r] + i * a.n + j));
         p[r][0] = v.x; p[r][1] = v.y; p[r][2] = v.z; p[r][3] = v.w;
       }
     }
@@ -497,7 +524,7 @@ __global__ __launch_bounds__(256) void lin_post_kernel(LinPostKArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (float)(factor * c4[e]);
         if (a.beta != 0.f) {
-          uint2 cv = *reinterpret_cast<const uint2*>(a.C + off);
+          uint2 cv = nt_ld(reinterpret_cast<const uint2*>(a.C + off));
           v[0] += a.beta * h2f(cv.x & 0xffffu, a.dt);
           v[1] += a.beta * h2f(cv.x >> 16, a.dt);
           v[2] += a.beta * h2f(cv.y & 0xffffu, a.dt);
@@ -510,9 +537,9 @@ __global__ __launch_bounds__(256) void lin_post_kernel(LinPostKArgs a) {
           v[2] += h2f(bv.y & 0xffffu, a.dt);
           v[3] += h2f(bv.y >> 16, a.dt);
         }
-        *reinterpret_cast<uint2*>(a.C + off) =
+        nt_st(
             make_uint2(f2h(v[0], a.dt) | (f2h(v[1], a.dt) << 16),
-                       f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16));
+                       f2h(v[2], a.dt) | (f2h(v[3], a.dt) << 16)), reinterpret_cast<uint2*>(a.C + off));
       }
     }
   }
