@@ -11,6 +11,8 @@
         <write.csv> <bench stdout log> <out.md> "<commands>"
     python -m hgemm_strassen_type_amd.prof_summary timeline <kernel_trace.csv> <out.md>
         "<command>" "<first kernel substring>" "<title>" [<its launches per call>]
+    python -m hgemm_strassen_type_amd.prof_summary stalls <pmc1.csv,pmc2.csv,...> <out.md>
+        "<commands joined by ' && '>" "<kernel substring>" <FLOP per launch> [<phases a wave>]
 
 `stats` keeps the per-kernel call count and average/min/max duration of a
 `--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
@@ -24,7 +26,9 @@ kernel, the average duration of the timed dispatches, the algorithmic bytes that
 bench.py states, the GB/s they make against the 8 TB/s HBM peak, and the
 counters' bytes per launch next to the algorithmic ones.  `timeline` lists the
 kernels of the last call of a trace (start, end, queue, workgroups), which shows
-what runs concurrently on two streams.
+what runs concurrently on two streams.  `stalls` splits a GEMM kernel's wave cycles
+into issuing, ready-but-not-issued and waiting, from SQ counters taken in several
+--pmc runs of one command, with LDS occupancy and the instruction mix.
 """
 from __future__ import annotations
 
@@ -205,6 +209,96 @@ def clock(pmc_csv: str, out_md: str, command: str, kernel: str, flops: float, cu
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def _steady_medians(pmc_csv: str, kernel: str) -> dict:
+    """Median over the dispatches of `kernel` in one --pmc run, the first one left
+    out (it starts from an idle chip at a higher clock), of every counter."""
+    per = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no kernel matching {kernel!r} in {pmc_csv}")
+    ids = sorted(per)[1:] or sorted(per)
+    names = set().union(*(per[i] for i in ids))
+    return {n: statistics.median(per[i][n] for i in ids if n in per[i]) for n in names}
+
+
+def stalls(pmc_csvs: list, out_md: str, command: str, kernel: str, flops: float,
+           phases_per_wave: int = 0, cus: int = 256, xcds: int = 8,
+           flop_per_clk_cu: float = 4096.0) -> None:
+    """Where a GEMM kernel's wave cycles go, from --pmc runs of the same command
+    (each run one counter set; every set holds GRBM_GUI_ACTIVE).  The SQ wave
+    counters count quad-cycles summed over all waves: SQ_WAVE_CYCLES is the waves'
+    lifetime, split into SQ_ACTIVE_INST_ANY (issuing), SQ_WAIT_INST_ANY (an
+    instruction ready but not issued, e.g. behind the SIMD's other wave on the MFMA
+    pipe) and SQ_WAIT_ANY (waiting on a counter or the barrier).  A run's wave-cycle
+    counters are scaled to the first run by the ratio of GRBM_GUI_ACTIVE.  MFMA busy
+    is the cycles the MFMA work needs at full rate over the cycles taken, as in
+    `clock`; LDS busy is SQ_LDS_IDX_ACTIVE per CU over the cycles taken."""
+    runs = [_steady_medians(p, kernel) for p in pmc_csvs]
+    base = runs[0]
+    if "SQ_WAVE_CYCLES" not in base:
+        raise SystemExit("the first run must hold SQ_WAVE_CYCLES")
+    c = {}
+    for r in runs:
+        scale = base["GRBM_GUI_ACTIVE"] / r["GRBM_GUI_ACTIVE"]
+        for n, v in r.items():
+            if n != "GRBM_GUI_ACTIVE" and n not in c:
+                c[n] = (v, scale)
+    cyc = base["GRBM_GUI_ACTIVE"] / xcds
+    waves = c["SQ_WAVES"][0] if "SQ_WAVES" in c else None
+    wave_cycles = 4.0 * base["SQ_WAVE_CYCLES"]
+
+    def frac(n):
+        v, s = c[n]
+        return 4.0 * v * s / wave_cycles
+
+    lines = ["# Where the GEMM kernel's wave cycles go (rocprofv3 --pmc)", "",
+             f"Kernel filter: `{kernel}`; medians over each run's dispatches but the first.", "",
+             "Commands (one counter set a run):", "", "```", *command.split(" && "), "```", "",
+             "| counter | median per dispatch |", "|---|---|"]
+    for n in sorted(c):
+        lines.append(f"| {n} | {c[n][0]:.4g} |")
+    need = flops / (cus * flop_per_clk_cu)
+    lines += ["", f"GRBM_GUI_ACTIVE (first run): {base['GRBM_GUI_ACTIVE']:.4g}, {cyc / 1e6:.3f} M "
+              f"cycles per XCD; MFMA work {flops:.4g} FLOP needs {need / 1e6:.3f} M cycles per CU at "
+              f"{flop_per_clk_cu:.0f} FLOP/clock/CU: **MFMA busy {need / cyc:.3f}**.", ""]
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+        lines.append(f"MFMA work counted by SQ_INSTS_VALU_MFMA_MOPS_BF16 × 512: "
+                     f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16'][0] * 512:.4g} FLOP.")
+        lines.append("")
+    lines += ["| share of the waves' cycles | fraction |", "|---|---|"]
+    for n, label in (("SQ_ACTIVE_INST_ANY", "issuing (SQ_ACTIVE_INST_ANY)"),
+                     ("SQ_WAIT_INST_ANY", "ready, not issued (SQ_WAIT_INST_ANY)"),
+                     ("SQ_WAIT_ANY", "waiting on a counter or the barrier (SQ_WAIT_ANY)"),
+                     ("SQ_ACTIVE_INST_LDS", "  of which LDS instructions issuing (SQ_ACTIVE_INST_LDS)"),
+                     ("SQ_WAIT_INST_LDS", "  LDS instruction ready, not issued (SQ_WAIT_INST_LDS)"),
+                     ("SQ_ACTIVE_INST_VALU", "  VALU and MFMA instructions issuing (SQ_ACTIVE_INST_VALU)"),
+                     ("SQ_ACTIVE_INST_SCA", "  scalar instructions issuing (SQ_ACTIVE_INST_SCA)")):
+        if n in c:
+            lines.append(f"| {label} | {frac(n):.3f} |")
+    if waves and "SQ_WAVE_CYCLES" in base:
+        lines += ["", f"Waves: {waves:.0f}; lifetime {wave_cycles / waves / 1e6:.3f} M cycles a wave "
+                  f"against {cyc / 1e6:.3f} M for the launch."]
+    if "SQ_LDS_IDX_ACTIVE" in c:
+        lds = c["SQ_LDS_IDX_ACTIVE"][0] * c["SQ_LDS_IDX_ACTIVE"][1] / cus
+        lines.append(f"LDS busy (SQ_LDS_IDX_ACTIVE per CU over the launch's cycles): {lds / cyc:.3f}; "
+                     f"bank-conflict cycles: {c.get('SQ_LDS_BANK_CONFLICT', (0.0, 1.0))[0]:.4g}.")
+    if waves:
+        per = [("SQ_INSTS_MFMA", "MFMA"), ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_VALU", "VALU (MFMA included)"),
+               ("SQ_INSTS_SALU", "SALU"), ("SQ_INSTS_VMEM", "vector memory")]
+        have = [(n, l) for n, l in per if n in c]
+        if have:
+            unit = f"a wave a phase ({phases_per_wave} phases a wave)" if phases_per_wave else "a wave"
+            lines += ["", f"| instructions | {unit} |", "|---|---|"]
+            for n, l in have:
+                v = c[n][0] / waves / (phases_per_wave or 1)
+                lines.append(f"| {l} | {v:.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def timeline(trace_csv: str, out_md: str, command: str, first: str, title: str,
              per_call: int = 1) -> None:
     """The kernels of the last call in a `--kernel-trace` run, in start order, from
@@ -254,6 +348,9 @@ if __name__ == "__main__":
     elif sys.argv[1] == "adds":
         adds(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
              title=sys.argv[8] if len(sys.argv) > 8 else "the Strassen add kernels")
+    elif sys.argv[1] == "stalls":
+        stalls(sys.argv[2].split(","), sys.argv[3], sys.argv[4], sys.argv[5], float(sys.argv[6]),
+               int(sys.argv[7]) if len(sys.argv) > 7 else 0)
     elif sys.argv[1] == "timeline":
         timeline(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                  int(sys.argv[7]) if len(sys.argv) > 7 else 1)

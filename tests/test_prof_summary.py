@@ -134,3 +134,45 @@ def test_timeline_of_the_last_call(tmp_path):
     write_csv(tmp_path / "t2.csv", header, rows2)
     prof_summary.timeline(str(tmp_path / "t2.csv"), str(out), "cmd", "maxabs", "test", per_call=2)
     assert "| 0.0 | 3.0 | 3.0 | 1 | 32 |" in out.read_text()
+
+
+def test_stall_breakdown(tmp_path):
+    # two --pmc runs of one command; the first dispatch of each is left out.  Run 1:
+    # 2048 waves living 1.0e6 cycles each (SQ_WAVE_CYCLES in quad-cycles), 30 % of
+    # them issuing, 50 % ready but not issued, 20 % waiting; 8 XCDs at 1.5e6 cycles.
+    # Run 2 took 1.2x the cycles, so its wave-cycle counters are scaled by 1/1.2.
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "gemm_mfma_kernel<TileCfg<256, 256,...>"
+    wc = 2048 * 1.0e6 / 4
+    run1 = []
+    for d, f in (("1", 3.0), ("2", 1.0), ("3", 1.0)):      # dispatch 1: a different state
+        run1 += [[d, k, "GRBM_GUI_ACTIVE", 8 * 1.5e6 * f], [d, k, "SQ_WAVE_CYCLES", wc * f],
+                 [d, k, "SQ_ACTIVE_INST_ANY", 0.3 * wc * f], [d, k, "SQ_WAIT_INST_ANY", 0.5 * wc * f],
+                 [d, k, "SQ_WAIT_ANY", 0.2 * wc * f], [d, k, "SQ_INSTS_MFMA", 2048 * 6400.0]]
+    run1.append(["4", "other_kernel", "SQ_WAVE_CYCLES", 1.0])
+    run2 = []
+    for d in ("5", "6"):
+        run2 += [[d, k, "GRBM_GUI_ACTIVE", 1.2 * 8 * 1.5e6], [d, k, "SQ_WAVES", 2048],
+                 [d, k, "SQ_WAIT_INST_LDS", 1.2 * 0.05 * wc], [d, k, "SQ_INSTS_LDS", 2048 * 4000.0],
+                 [d, k, "SQ_LDS_IDX_ACTIVE", 256 * 0.25 * 1.2 * 1.5e6],
+                 [d, k, "SQ_LDS_BANK_CONFLICT", 0]]
+    write_csv(tmp_path / "a.csv", hdr, run1)
+    write_csv(tmp_path / "b.csv", hdr, run2)
+    out = tmp_path / "s.md"
+    flops = 0.7 * 1.5e6 * 256 * 4096
+    prof_summary.stalls([str(tmp_path / "a.csv"), str(tmp_path / "b.csv")], str(out),
+                        "cmd1 && cmd2", "TileCfg<256, 256", flops, phases_per_wave=100)
+    text = out.read_text()
+
+    def row(label):
+        line = [l for l in text.splitlines() if l.startswith(f"| {label}")][0]
+        return float(line.split("|")[-2])
+    assert "**MFMA busy 0.700**" in text
+    assert row("issuing (SQ_ACTIVE_INST_ANY)") == pytest.approx(0.3)
+    assert row("ready, not issued (SQ_WAIT_INST_ANY)") == pytest.approx(0.5)
+    assert row("waiting on a counter or the barrier") == pytest.approx(0.2)
+    assert row("  LDS instruction ready, not issued") == pytest.approx(0.05)
+    assert "LDS busy (SQ_LDS_IDX_ACTIVE per CU over the launch's cycles): 0.250" in text
+    assert row("MFMA |") == pytest.approx(64.0)
+    assert row("LDS |") == pytest.approx(40.0)
+    assert "cmd2" in text
