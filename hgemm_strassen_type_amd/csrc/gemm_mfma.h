@@ -641,6 +641,16 @@ struct GemmTile {
     return mfma(bf, af, c);
   }
 
+  // An empty asm that reads every accumulator block in its AGPRs: the MFMAs that
+  // produce them must issue before it (it is volatile, so it stays in program order
+  // with the barrier that follows it).
+  __device__ __forceinline__ static void pin_acc(Acc (&acc)[CFG::FM][CFG::FN]) {
+#pragma unroll
+    for (int i = 0; i < CFG::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CFG::FN; ++j) asm volatile("" : : "a"(acc[i][j]));
+  }
+
   __device__ __forceinline__ static void mfma_step(const Frags& fr, const Scales& sc, int s,
                                                    Acc (&acc)[CFG::FM][CFG::FN]) {
 #pragma unroll
@@ -875,6 +885,11 @@ struct GemmTile {
     }
     Frags& fl = STEPS == 1 ? f0 : f1;  // the last step's fragments
     Frags& fn = STEPS == 1 ? f1 : f0;  // receives the next phase's first
+    // MX: the accumulators of the steps above, read in place by an empty asm ahead of
+    // the barrier.  The scale-group branch after the barrier otherwise lets the
+    // compiler sink those MFMAs below it, and the phase then runs its fragment reads,
+    // wait and barrier with the MFMA pipe idle.
+    if constexpr (MX && STEPS >= 2) pin_acc(acc);
     // phase kt+1 must have landed; the S-2 phases after it may still fly when
     // they have all been issued
     wait_phase<(S - 2) * QW>(kt + S - 1 < ktiles);
