@@ -12,7 +12,8 @@
     python -m hgemm_strassen_type_amd.prof_summary timeline <kernel_trace.csv> <out.md>
         "<command>" "<first kernel substring>" "<title>" [<its launches per call>]
     python -m hgemm_strassen_type_amd.prof_summary stalls <pmc1.csv,pmc2.csv,...> <out.md>
-        "<commands joined by ' && '>" "<kernel substring>" <FLOP per launch> [<phases a wave>]
+        "<commands joined by ' && '>" "<kernel substring>" <FLOP per launch> [<phases a wave>
+        [<FLOP per clock per CU at the MFMA's full rate: 4096 for 16-bit, 16384 for 4-bit>]]
 
 `stats` keeps the per-kernel call count and average/min/max duration of a
 `--kernel-trace --stats` run.  `traffic` turns two `--pmc FETCH_SIZE` /
@@ -209,15 +210,27 @@ def clock(pmc_csv: str, out_md: str, command: str, kernel: str, flops: float, cu
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def _steady_medians(pmc_csv: str, kernel: str) -> dict:
+def _mops_flops(d: dict):
+    """FLOP of a dispatch from whichever SQ_INSTS_VALU_MFMA_MOPS_* counters it holds
+    (each counts FLOP / 512), or None."""
+    v = [x for n, x in d.items() if n.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
+    return 512.0 * sum(v) if v else None
+
+
+def _steady_medians(pmc_csv: str, kernel: str, flops: float | None = None) -> dict:
     """Median over the dispatches of `kernel` in one --pmc run, the first one left
-    out (it starts from an idle chip at a higher clock), of every counter."""
+    out (it starts from an idle chip at a higher clock), of every counter.  With
+    `flops`, dispatches whose MOPS counters show other MFMA work (another shape of the
+    same kernel) are left out too."""
     per = {}
     for r in csv.DictReader(open(pmc_csv)):
         if kernel not in r["Kernel_Name"]:
             continue
         d = per.setdefault(int(r["Dispatch_Id"]), {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if flops:
+        per = {i: d for i, d in per.items()
+               if _mops_flops(d) is None or abs(_mops_flops(d) - flops) <= 0.01 * flops}
     if not per:
         raise SystemExit(f"no kernel matching {kernel!r} in {pmc_csv}")
     ids = sorted(per)[1:] or sorted(per)
@@ -236,8 +249,10 @@ def stalls(pmc_csvs: list, out_md: str, command: str, kernel: str, flops: float,
     pipe) and SQ_WAIT_ANY (waiting on a counter or the barrier).  A run's wave-cycle
     counters are scaled to the first run by the ratio of GRBM_GUI_ACTIVE.  MFMA busy
     is the cycles the MFMA work needs at full rate over the cycles taken, as in
-    `clock`; LDS busy is SQ_LDS_IDX_ACTIVE per CU over the cycles taken."""
-    runs = [_steady_medians(p, kernel) for p in pmc_csvs]
+    `clock`; LDS busy is SQ_LDS_IDX_ACTIVE per CU over the cycles taken.  Dispatches
+    whose SQ_INSTS_VALU_MFMA_MOPS_* counters show other work than `flops` (another
+    shape of the same kernel in the run) are left out."""
+    runs = [_steady_medians(p, kernel, flops) for p in pmc_csvs]
     base = runs[0]
     if "SQ_WAVE_CYCLES" not in base:
         raise SystemExit("the first run must hold SQ_WAVE_CYCLES")
@@ -265,10 +280,10 @@ def stalls(pmc_csvs: list, out_md: str, command: str, kernel: str, flops: float,
     lines += ["", f"GRBM_GUI_ACTIVE (first run): {base['GRBM_GUI_ACTIVE']:.4g}, {cyc / 1e6:.3f} M "
               f"cycles per XCD; MFMA work {flops:.4g} FLOP needs {need / 1e6:.3f} M cycles per CU at "
               f"{flop_per_clk_cu:.0f} FLOP/clock/CU: **MFMA busy {need / cyc:.3f}**.", ""]
-    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
-        lines.append(f"MFMA work counted by SQ_INSTS_VALU_MFMA_MOPS_BF16 × 512: "
-                     f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16'][0] * 512:.4g} FLOP.")
-        lines.append("")
+    for n in sorted(c):
+        if n.startswith("SQ_INSTS_VALU_MFMA_MOPS_"):
+            lines.append(f"MFMA work counted by {n} × 512: {c[n][0] * 512:.4g} FLOP.")
+            lines.append("")
     lines += ["| share of the waves' cycles | fraction |", "|---|---|"]
     for n, label in (("SQ_ACTIVE_INST_ANY", "issuing (SQ_ACTIVE_INST_ANY)"),
                      ("SQ_WAIT_INST_ANY", "ready, not issued (SQ_WAIT_INST_ANY)"),
@@ -350,7 +365,8 @@ if __name__ == "__main__":
              title=sys.argv[8] if len(sys.argv) > 8 else "the Strassen add kernels")
     elif sys.argv[1] == "stalls":
         stalls(sys.argv[2].split(","), sys.argv[3], sys.argv[4], sys.argv[5], float(sys.argv[6]),
-               int(sys.argv[7]) if len(sys.argv) > 7 else 0)
+               int(sys.argv[7]) if len(sys.argv) > 7 else 0,
+               flop_per_clk_cu=float(sys.argv[8]) if len(sys.argv) > 8 else 4096.0)
     elif sys.argv[1] == "timeline":
         timeline(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                  int(sys.argv[7]) if len(sys.argv) > 7 else 1)

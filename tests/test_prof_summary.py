@@ -176,3 +176,25 @@ def test_stall_breakdown(tmp_path):
     assert row("MFMA |") == pytest.approx(64.0)
     assert row("LDS |") == pytest.approx(40.0)
     assert "cmd2" in text
+
+
+def test_stall_breakdown_picks_one_shape(tmp_path):
+    # one kernel run at two shapes: the MOPS counter tells them apart, so the
+    # medians come from the 1e12-FLOP launches only (the first of them left out)
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "gemm_mfma_kernel<TileCfg<256, 256, 2, 2, 64, 2, 1, 32>, 12, true>"
+    rows = []
+    for d, fl, cyc in (("1", 1e12, 9e6), ("2", 1e12, 8e6), ("3", 1e12, 8e6), ("4", 5e11, 4e6),
+                       ("5", 5e11, 4e6)):
+        rows += [[d, k, "GRBM_GUI_ACTIVE", cyc], [d, k, "SQ_WAVE_CYCLES", cyc / 4],
+                 [d, k, "SQ_WAIT_ANY", 0.25 * cyc / 4], [d, k, "SQ_WAVES", 1024],
+                 [d, k, "SQ_INSTS_VALU_MFMA_MOPS_F6F4", fl / 512]]
+    write_csv(tmp_path / "a.csv", hdr, rows)
+    out = tmp_path / "s.md"
+    prof_summary.stalls([str(tmp_path / "a.csv")], str(out), "cmd", ", 12, true", 1e12,
+                        flop_per_clk_cu=16384.0)
+    text = out.read_text()
+    # 1e12 FLOP at 16384 FLOP/clock on 256 CUs over 1e6 cycles per XCD
+    assert f"**MFMA busy {1e12 / (256 * 16384) / 1e6:.3f}**" in text
+    assert "SQ_INSTS_VALU_MFMA_MOPS_F6F4 × 512: 1e+12 FLOP" in text
+    assert "| waiting on a counter or the barrier (SQ_WAIT_ANY) | 0.250 |" in text
