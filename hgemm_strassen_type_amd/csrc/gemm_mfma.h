@@ -90,6 +90,18 @@ template <int DT>
 __device__ __forceinline__ uint32_t from_f32(float f) {
   return DT == kBF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
 }
+// Two values rounded (RNE) and packed low | high << 16: one v_cvt_pk_{bf16,f16}_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == kBF16) {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, h2));
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, h2));
+  }
+}
 
 // s_waitcnt immediate for "vector memory count <= n", other counters unconstrained
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -968,6 +980,54 @@ struct GemmTile {
   }
 
   // ============================================================ epilogues
+  // One lane's 8 consecutive outputs of a whole block (row < M, 8 columns < N):
+  // alpha is applied already; + beta*C (prefetched), + bias, the activation, one
+  // rounding of each pair into a packed word, the row's sum of squares of the
+  // rounded values, one non-temporal 16-byte store.  Same arithmetic, in the same
+  // order, as the general path of epilogue_rows.
+  __device__ __forceinline__ static void store_whole(const GemmProblem& P, void* Cout, int row,
+                                                     int col, const v4u* cpre, bool use_bias,
+                                                     bool use_ss, v4f lo, v4f hi, float& ss) {
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if (cpre) {
+      const v4u cv = *cpre;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] += P.beta * to_f32<ODT>(cv[e] & 0xffff);
+        v[2 * e + 1] += P.beta * to_f32<ODT>(cv[e] >> 16);
+      }
+    }
+    if (use_bias) {
+      const uint16_t* bias = static_cast<const uint16_t*>(P.bias) + col;
+      if ((reinterpret_cast<uintptr_t>(bias) & 15) == 0) {
+        const v4u b4 = *reinterpret_cast<const v4u*>(bias);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] += to_f32<ODT>(b4[e] & 0xffff);
+          v[2 * e + 1] += to_f32<ODT>(b4[e] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += to_f32<ODT>(bias[e]);
+      }
+    }
+    if constexpr (EPI == kEpiAct) apply_act_run<8>(P.act, v);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack2<ODT>(v[2 * e], v[2 * e + 1]);
+    if (use_ss) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = to_f32<ODT>(w[e] & 0xffff), b = to_f32<ODT>(w[e] >> 16);
+        ss += a * a;
+        ss += b * b;
+      }
+    }
+    uint16_t* C = static_cast<uint16_t*>(Cout);
+    __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]},
+                                reinterpret_cast<v4u*>(C + (int64_t)row * P.ldc + col));
+  }
+
   // Row-contiguous epilogue (16-byte aligned operands): every 32-row, EPI_CW-column
   // block of the wave's results goes to LDS in the MFMA layout and comes back as 8
   // consecutive columns of one row per lane, so that beta*C is read and the result
@@ -1070,6 +1130,9 @@ struct GemmTile {
         }
         const int col = n0 + wn * WO + jc * CW + 8 * oc;
         const int nv = P.N - col;
+        // the wave's 32 rows and CW columns all inside the matrix (wave-uniform): the
+        // passes store whole 16-byte pieces with no per-element tests
+        const bool whole = row_base + 32 <= P.M && P.N - (n0 + wn * WO + jc * CW) >= CW;
 #pragma unroll
         for (int t = 0; t < 32 / RPT; ++t) {
           const int r = t * RPT + orow;
@@ -1077,6 +1140,15 @@ struct GemmTile {
           v4f lo = *reinterpret_cast<const v4f*>(src + (((2 * oc) ^ swz(r)) << 4));
           v4f hi = *reinterpret_cast<const v4f*>(src + (((2 * oc + 1) ^ swz(r)) << 4));
           const int row = row_base + r;
+          // (16-bit inputs only: in the 4-wave 8-bit tiles this path measured 4-8 % slower
+          // and spilled with fp16 outputs)
+          if constexpr (STORE16 && EPI != kEpiRope && !F8) {
+            if (whole) {
+              store_whole(P, Cout, row, col, use_beta ? &cpre[i][jc][t] : nullptr, use_bias,
+                          use_ss, lo, hi, ss[t]);
+              continue;
+            }
+          }
           if (row >= P.M || nv <= 0) continue;
           float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           const int64_t off = (int64_t)row * P.ldc + col;
