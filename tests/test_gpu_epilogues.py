@@ -202,6 +202,39 @@ def test_relu_exact_integers():
 
 
 @pytest.mark.parametrize("dtype", [BF16, F16])
+def test_bias_pointer_off_16_bytes_exact(dtype):
+    """Aligned operands with a bias vector that starts 2 bytes past a 16-byte boundary
+    (the epilogue loads it element by element), beta*C, alpha and the row sums of
+    squares, on tiles whose interior waves take the whole-block store and whose edge
+    waves take the general one: integer values, so the outputs are exact and must
+    match the oracle bit for bit; the statistics within 1e-3."""
+    import torch
+    M, N, K = 300, 520, 192
+    A = inputs.integers((M, K), 741, dtype, -2, 2)
+    B = inputs.integers((K, N), 742, dtype, -2, 2)
+    C = inputs.integers((M, N), 743, dtype, -4, 4)
+    bias = inputs.integers((N + 1,), 744, dtype, -3, 3)
+    flags = oracle.EPI_BIAS | oracle.EPI_ROWSUMSQ
+    _, Q, ss = oracle.gemm(A, B, alpha=0.5, beta=1.5, C=C, dtype=dtype, epi=flags, bias=bias[1:])
+    bd = to_dev(bias[None, :], dtype)
+    assert (bd.data_ptr() + 2) % 16 != 0
+    for tile in TILES:
+        say(f"bias off 16 bytes dtype={dtype} tile={tile}")
+        Ad, Bd, Cd = to_dev(A, dtype), to_dev(B, dtype), to_dev(C, dtype)
+        ssd = dev_f32(M)
+        epi = fgemm.make_epilogue(fgemm.FGEMM_EPI_BIAS | fgemm.FGEMM_EPI_ROWSUMSQ,
+                                  bias=bd.data_ptr() + 2, rowsumsq=ssd.data_ptr())
+        handle().gemm(Ad, Bd, Cd, alpha=0.5, beta=1.5, epilogue=epi,
+                      plan=fgemm.classical_plan(*tile))
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(Cd), Q), tile
+        got = ssd.cpu().numpy().astype(np.float64)
+        nz = ss > 0
+        assert np.max(np.abs(got[nz] - ss[nz]) / ss[nz]) <= STATS_TOL, tile
+        assert np.all(got[~nz] == 0), tile
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("transB", [False, True])
 def test_rope_positions_and_offset(dtype, tile, transB):
